@@ -1,0 +1,199 @@
+"""CPU oracle for row-wise RMSNorm and the fused K-partial + residual form.
+
+TEST INFRASTRUCTURE.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package.  The GPU library
+never calls it; the product path has no CPU fallback.
+
+This module is a thin ctypes wrapper over ``oracle/rmsnorm_oracle.c`` (plain C,
+double accumulation, single-threaded), whose C ABI is declared in
+``include/rmsnorm_oracle.h``.  Arrays are numpy: float32 data for "f32",
+uint16 bit patterns for "f16" and "bf16".
+
+What the oracle computes follows page "RMSNorm kernel" (section 1 Background
+and section 2 "Abstraction") for the plain form and page "Tokenweave
+fused-RMSNorm-AR kernel" (section "Code walkthrough") for the fused form; the
+readings taken where they are silent are listed in the C source header.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "rmsnorm_oracle.c")
+_INCLUDE = os.path.join(os.path.dirname(_HERE), "include")
+LIB_PATH = os.path.join(_HERE, "librmsnorm_oracle.so")
+
+DTYPE_CODE = {"f32": 0, "f16": 1, "bf16": 2}
+KMAX = 16
+
+_ERRORS = {
+    -1: "null pointer",
+    -2: "bad shape",
+    -3: "bad dtype",
+    -4: "bad k",
+    -6: "bad eps",
+    -8: "out of memory",
+}
+
+_default = None
+_lock = threading.Lock()
+
+
+def compile_library(src: str, out: str) -> str:
+    """Compile an oracle source file with the oracle's flags: no FMA
+    contraction, no fast-math, no excess precision (binary32 adds stay
+    binary32)."""
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-Wall", "-Wextra",
+           "-ffp-contract=off", "-fno-fast-math", "-fexcess-precision=standard",
+           "-I", _INCLUDE, "-o", tmp, src, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle library in-tree."""
+    if not force and os.path.exists(LIB_PATH):
+        return LIB_PATH
+    return compile_library(_SRC, LIB_PATH)
+
+
+class Library:
+    """ctypes handle on one build of the oracle (the default build, or a
+    deliberately mutated copy compiled by the oracle's mutation tests)."""
+
+    def __init__(self, path: str):
+        lib = ctypes.CDLL(path)
+        vp, dp, i64 = ctypes.c_void_p, ctypes.POINTER(ctypes.c_double), ctypes.c_int64
+        lib.rmsnorm_oracle.argtypes = [vp, vp, ctypes.POINTER(vp), ctypes.c_int, vp,
+                                       i64, i64, ctypes.c_float, ctypes.c_int, dp]
+        lib.rmsnorm_oracle.restype = ctypes.c_int
+        lib.rmsnorm_oracle_f64.argtypes = [vp, dp, vp, ctypes.POINTER(vp), ctypes.c_int, vp,
+                                           i64, i64, ctypes.c_float, ctypes.c_int, dp]
+        lib.rmsnorm_oracle_f64.restype = ctypes.c_int
+        lib.rmsnorm_oracle_round.argtypes = [vp, dp, i64, ctypes.c_int]
+        lib.rmsnorm_oracle_round.restype = ctypes.c_int
+        lib.rmsnorm_oracle_decode.argtypes = [dp, vp, i64, ctypes.c_int]
+        lib.rmsnorm_oracle_decode.restype = ctypes.c_int
+        self.lib = lib
+        self.path = path
+
+
+def load_library(path: str) -> Library:
+    """Open another build of the oracle (the mutation tests use this)."""
+    return Library(path)
+
+
+def _load(lib: "Library | None" = None):
+    global _default
+    if lib is not None:
+        return lib.lib
+    with _lock:
+        if _default is None:
+            if not os.path.exists(LIB_PATH):
+                build()
+            _default = Library(LIB_PATH)
+        return _default.lib
+
+
+def _storage(dtype: str):
+    return np.float32 if dtype == "f32" else np.uint16
+
+
+def _check(arr: np.ndarray, dtype: str, shape=None) -> np.ndarray:
+    want = _storage(dtype)
+    if arr.dtype != want:
+        raise TypeError(f"oracle expects {np.dtype(want)} storage for {dtype}, got {arr.dtype}")
+    if not arr.flags.c_contiguous:
+        raise ValueError("oracle expects C-contiguous arrays")
+    if shape is not None and arr.shape != tuple(shape):
+        raise ValueError(f"shape {arr.shape} != {tuple(shape)}")
+    return arr
+
+
+def _ptr(a: np.ndarray):
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+def _dptr(a):
+    if a is None:
+        return ctypes.cast(None, ctypes.POINTER(ctypes.c_double))
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def _raise(rc: int):
+    if rc != 0:
+        raise RuntimeError(f"rmsnorm_oracle failed: {rc} ({_ERRORS.get(rc, 'unknown')})")
+
+
+def rmsnorm(x: np.ndarray, gamma: np.ndarray, eps: float, dtype: str, *,
+            want_f64: bool = False, lib: "Library | None" = None):
+    """Plain RMSNorm of x[rows, hidden].  Returns (out, rstd[rows]) and, with
+    ``want_f64``, the unrounded double y as a third item."""
+    rows, hidden = x.shape
+    _check(x, dtype)
+    _check(gamma, dtype, (hidden,))
+    out = np.empty_like(x)
+    rstd = np.empty(rows, dtype=np.float64)
+    y64 = np.empty((rows, hidden), dtype=np.float64) if want_f64 else None
+    parts = (ctypes.c_void_p * 1)(x.ctypes.data)
+    rc = _load(lib).rmsnorm_oracle_f64(_ptr(out), _dptr(y64), None, parts, 1, _ptr(gamma),
+                                       rows, hidden, ctypes.c_float(eps), DTYPE_CODE[dtype],
+                                       _dptr(rstd))
+    _raise(rc)
+    return (out, rstd, y64) if want_f64 else (out, rstd)
+
+
+def add_rmsnorm(partials, residual: np.ndarray, gamma: np.ndarray, eps: float, dtype: str,
+                *, want_f64: bool = False, lib: "Library | None" = None):
+    """Fused form.  ``residual`` is NOT modified; the oracle works on a copy.
+    Returns (out, new_residual, rstd) and, with ``want_f64``, the unrounded y."""
+    rows, hidden = residual.shape
+    _check(residual, dtype)
+    _check(gamma, dtype, (hidden,))
+    parts = [_check(p, dtype, (rows, hidden)) for p in partials]
+    k = len(parts)
+    out = np.empty_like(residual)
+    res = residual.copy()
+    rstd = np.empty(rows, dtype=np.float64)
+    y64 = np.empty((rows, hidden), dtype=np.float64) if want_f64 else None
+    arr = (ctypes.c_void_p * max(k, 1))(*[p.ctypes.data for p in parts])
+    rc = _load(lib).rmsnorm_oracle_f64(_ptr(out), _dptr(y64), _ptr(res), arr, k, _ptr(gamma),
+                                       rows, hidden, ctypes.c_float(eps), DTYPE_CODE[dtype],
+                                       _dptr(rstd))
+    _raise(rc)
+    return (out, res, rstd, y64) if want_f64 else (out, res, rstd)
+
+
+def raw_call(out, residual, partials, gamma, rows, hidden, eps, dtype_code,
+             lib: "Library | None" = None) -> int:
+    """Direct call with arbitrary (possibly invalid) arguments; returns the code."""
+    k = len(partials)
+    arr = (ctypes.c_void_p * max(k, 1))(*[(p.ctypes.data if p is not None else None)
+                                          for p in partials])
+    return _load(lib).rmsnorm_oracle(
+        None if out is None else _ptr(out), None if residual is None else _ptr(residual),
+        arr, k, None if gamma is None else _ptr(gamma), rows, hidden,
+        ctypes.c_float(eps), dtype_code, _dptr(None))
+
+
+def round_to(values: np.ndarray, dtype: str, lib: "Library | None" = None) -> np.ndarray:
+    """Round float64 values to dtype with the oracle's converter."""
+    v = np.ascontiguousarray(values, dtype=np.float64)
+    dst = np.empty(v.shape, dtype=_storage(dtype))
+    _raise(_load(lib).rmsnorm_oracle_round(_ptr(dst), _dptr(v), v.size, DTYPE_CODE[dtype]))
+    return dst
+
+
+def decode(bits: np.ndarray, dtype: str, lib: "Library | None" = None) -> np.ndarray:
+    """Exact float64 values of dtype storage."""
+    b = _check(np.ascontiguousarray(bits), dtype)
+    dst = np.empty(b.shape, dtype=np.float64)
+    _raise(_load(lib).rmsnorm_oracle_decode(_dptr(dst), _ptr(b), b.size, DTYPE_CODE[dtype]))
+    return dst
