@@ -1,0 +1,125 @@
+/*
+ * rmsnorm.h -- C ABI of librmsnorm.so: row-wise RMSNorm and the fused
+ * "K partials + residual -> residual in place -> RMSNorm" form on MI355X
+ * (gfx950) with hand-written HIP kernels.
+ *
+ * The operation (per row i of a contiguous row-major [rows, hidden] tensor):
+ *   RMSNorm (page "RMSNorm kernel", section 1 Background: the PyTorch RMSNorm
+ *   definition over the last dimension; section 2 "Abstraction": per-row sum
+ *   of squares, mean, + eps, square root, then x_j * gamma_j / RMS):
+ *       y_j = x_j * rsqrt(mean_j(x_j^2) + eps) * gamma_j
+ *   Fused form (page "Tokenweave fused-RMSNorm-AR kernel", section "Code
+ *   walkthrough": the reduced rank partials plus the residual are written
+ *   back to the residual in place, and the stored row is normalised):
+ *       acc_j = p0_j + p1_j + ... + p(K-1)_j + r_j   (binary32, this order)
+ *       r_j  <- round_to_dtype(acc_j)                 (in place)
+ *       y_j   = r_j * rsqrt(mean_j(r_j^2) + eps) * gamma_j
+ *
+ * Numerics: values are widened to fp32; the residual sum is a sequence of
+ * binary32 adds seeded with p0, rounded once to the storage dtype (round to
+ * nearest even), so the stored residual is exactly reproducible.  The sum of
+ * squares is accumulated in fp32; y is computed in fp32 as (r * inv) * gamma
+ * and rounded once to the output dtype.  fp32 denormals are preserved.
+ *
+ * Conventions for every entry point:
+ *   - All data pointers are DEVICE pointers to contiguous row-major tensors;
+ *     row i occupies elements [i*hidden, (i+1)*hidden).  gamma is [hidden].
+ *     All tensors share one dtype (RMSN_F32, RMSN_F16, RMSN_BF16).
+ *   - The caller owns every buffer.  The library never allocates, frees or
+ *     synchronises; work is enqueued on `stream` (a hipStream_t; NULL means
+ *     the default stream) and the call returns.  A fault inside a kernel
+ *     surfaces at the caller's next synchronisation.
+ *   - Arguments are validated before anything is launched; on any error
+ *     nothing is launched and a negative RMSN_ERR_* code is returned.
+ *     rmsnorm_last_error() describes the most recent failure of the calling
+ *     thread.  rows == 0 is a no-op that returns RMSN_OK.
+ *   - Any base alignment is accepted.  The 128-bit vector kernels are used
+ *     when every base is 16-byte aligned and hidden*sizeof(dtype) is a
+ *     multiple of 16; otherwise an element-wise kernel of the same numerics.
+ *   - Limits: 1 <= hidden <= RMSN_MAX_HIDDEN, rows >= 0, eps finite and >= 0.
+ */
+#ifndef RMSNORM_H
+#define RMSNORM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { RMSN_F32 = 0, RMSN_F16 = 1, RMSN_BF16 = 2 } rmsn_dtype;
+
+enum {
+  RMSN_OK = 0,
+  RMSN_ERR_NULL = -1,   /* a required pointer is NULL (rows > 0)               */
+  RMSN_ERR_SHAPE = -2,  /* rows < 0, hidden < 1 or hidden > RMSN_MAX_HIDDEN    */
+  RMSN_ERR_DTYPE = -3,  /* unknown dtype code                                  */
+  RMSN_ERR_K = -4,      /* k outside [1, RMSN_KMAX]                            */
+  RMSN_ERR_ALIAS = -5,  /* forbidden overlap between buffers (see below)       */
+  RMSN_ERR_EPS = -6,    /* eps negative, NaN or infinite                       */
+  RMSN_ERR_HIP = -7     /* the HIP runtime reported an error at launch         */
+};
+
+#define RMSN_KMAX 16
+#define RMSN_MAX_HIDDEN (1 << 24)
+
+/*
+ * rmsnorm_fwd -- plain RMSNorm (page "RMSNorm kernel", sections 1 and 2).
+ *   out    [rows, hidden] written.  May be exactly x (in-place); any other
+ *          overlap with x, and any overlap with gamma, is RMSN_ERR_ALIAS.
+ *   x      [rows, hidden] read.
+ *   gamma  [hidden] read.
+ *   eps    added to the mean of squares inside the square root.
+ */
+int rmsnorm_fwd(void* out, const void* x, const void* gamma, int64_t rows, int64_t hidden,
+                float eps, int dtype, void* stream);
+
+/*
+ * add_rmsnorm_fwd -- fused K-partial sum + residual + RMSNorm (page
+ * "Tokenweave fused-RMSNorm-AR kernel", "Code walkthrough"; with every
+ * partial already in local device memory).
+ *   out       [rows, hidden] written.  May be exactly one of the partials.
+ *   residual  [rows, hidden] read, then overwritten with the rounded sum.
+ *   partials  HOST array of k device pointers, each [rows, hidden] read; the
+ *             array is copied at the call and may be freed on return.
+ *             Partials may alias one another.
+ *   k         1..RMSN_KMAX.
+ *   Forbidden overlaps (RMSN_ERR_ALIAS): out with residual or gamma; out
+ *   partially overlapping a partial; residual with any partial or gamma.
+ */
+int add_rmsnorm_fwd(void* out, void* residual, const void* const* partials, int k,
+                    const void* gamma, int64_t rows, int64_t hidden, float eps, int dtype,
+                    void* stream);
+
+/* Static description of an error code (never NULL). */
+const char* rmsnorm_strerror(int code);
+
+/* Description of the calling thread's most recent failed call ("" if none). */
+const char* rmsnorm_last_error(void);
+
+/*
+ * rmsnorm_plan -- which kernel the dispatcher picks for a call with these
+ * sizes (k = 0 means plain RMSNorm; aligned != 0 means every base pointer is
+ * 16-byte aligned).  Writes a NUL-terminated name such as
+ * "vgpr<bf16,tpr=256,npt=2,wg=256,k=1>" into buf and returns RMSN_OK, or an
+ * error code for sizes that a call would reject.  Launches nothing.
+ */
+int rmsnorm_plan(int64_t rows, int64_t hidden, int k, int dtype, int aligned, char* buf,
+                 int buflen);
+
+/*
+ * rmsnorm_variants -- names of every compiled kernel variant for dtype,
+ * newline-separated, into buf.  Returns the number of variants (>= 0) or an
+ * error code.  Any name can be forced for every call by setting the
+ * environment variable RMSNORM_VARIANT to it (a call the variant cannot run
+ * then fails with RMSN_ERR_SHAPE); RMSNORM_GRID_CAP=<n> caps the number of
+ * workgroups per launch (rows are then processed in a grid-stride loop).
+ * Both exist for tuning and testing; unset, the dispatcher decides.
+ */
+int rmsnorm_variants(int dtype, char* buf, int buflen);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RMSNORM_H */

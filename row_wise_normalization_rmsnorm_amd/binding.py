@@ -1,0 +1,149 @@
+"""Python binding of librmsnorm.so (C ABI in include/rmsnorm.h).
+
+Argument marshalling only: torch tensors become device pointers, the current
+HIP stream becomes the stream argument, and every step of the computation runs
+in the library's HIP kernels.  There is no fallback: if the library is not
+built, or a call fails, a ``RmsnormError`` is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional, Sequence
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "librmsnorm.so")
+
+DTYPE_CODE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+DTYPE_NAME = {"f32": 0, "f16": 1, "bf16": 2}
+KMAX = 16
+EXPORTS = ("rmsnorm_fwd", "add_rmsnorm_fwd", "rmsnorm_strerror", "rmsnorm_last_error",
+           "rmsnorm_plan", "rmsnorm_variants")
+
+_lib = None
+_lock = threading.Lock()
+
+
+class RmsnormError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(msg)
+        self.code = code
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (loaded once).  Raises if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RmsnormError(-7, f"{LIB_PATH} is not built; run "
+                                       "`python -m row_wise_normalization_rmsnorm_amd.build`")
+            l = ctypes.CDLL(LIB_PATH)
+            vp, i64, c_int, c_float = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
+            l.rmsnorm_fwd.argtypes = [vp, vp, vp, i64, i64, c_float, c_int, vp]
+            l.rmsnorm_fwd.restype = c_int
+            l.add_rmsnorm_fwd.argtypes = [vp, vp, ctypes.POINTER(vp), c_int, vp, i64, i64,
+                                          c_float, c_int, vp]
+            l.add_rmsnorm_fwd.restype = c_int
+            l.rmsnorm_strerror.argtypes = [c_int]
+            l.rmsnorm_strerror.restype = ctypes.c_char_p
+            l.rmsnorm_last_error.argtypes = []
+            l.rmsnorm_last_error.restype = ctypes.c_char_p
+            l.rmsnorm_plan.argtypes = [i64, i64, c_int, c_int, c_int, ctypes.c_char_p, c_int]
+            l.rmsnorm_plan.restype = c_int
+            l.rmsnorm_variants.argtypes = [c_int, ctypes.c_char_p, c_int]
+            l.rmsnorm_variants.restype = c_int
+            _lib = l
+        return _lib
+
+
+def _check(rc: int) -> None:
+    if rc != 0:
+        l = lib()
+        raise RmsnormError(rc, f"{l.rmsnorm_strerror(rc).decode()} ({rc}): "
+                               f"{l.rmsnorm_last_error().decode()}")
+
+
+def _stream(t: torch.Tensor, stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream(t.device)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dev_ptr(t: torch.Tensor, what: str) -> int:
+    if not t.is_cuda:
+        raise RmsnormError(-1, f"{what} must be a device tensor")
+    if not t.is_contiguous():
+        raise RmsnormError(-2, f"{what} must be contiguous")
+    return t.data_ptr()
+
+
+def _rows_hidden(t: torch.Tensor):
+    hidden = t.shape[-1] if t.dim() > 0 else 1
+    rows = t.numel() // hidden if hidden else 0
+    return rows, hidden
+
+
+def rmsnorm_fwd(out: torch.Tensor, x: torch.Tensor, gamma: torch.Tensor, eps: float,
+                stream=None) -> None:
+    """out[..., H] = RMSNorm(x[..., H]) * gamma[H] (all one dtype, contiguous)."""
+    rows, hidden = _rows_hidden(x)
+    if out.shape != x.shape or gamma.numel() != hidden:
+        raise RmsnormError(-2, f"shape mismatch: out {tuple(out.shape)} x {tuple(x.shape)} "
+                               f"gamma {tuple(gamma.shape)}")
+    if not (out.dtype == x.dtype == gamma.dtype) or x.dtype not in DTYPE_CODE:
+        raise RmsnormError(-3, f"dtypes must match and be f32/f16/bf16")
+    _check(lib().rmsnorm_fwd(_dev_ptr(out, "out"), _dev_ptr(x, "x"), _dev_ptr(gamma, "gamma"),
+                             rows, hidden, float(eps), DTYPE_CODE[x.dtype], _stream(x, stream)))
+
+
+def add_rmsnorm_fwd(out: torch.Tensor, residual: torch.Tensor, partials: Sequence[torch.Tensor],
+                    gamma: torch.Tensor, eps: float, stream=None) -> None:
+    """residual <- round(p0 + ... + p(K-1) + residual) in place;
+    out = RMSNorm(residual) * gamma."""
+    rows, hidden = _rows_hidden(residual)
+    k = len(partials)
+    if out.shape != residual.shape or gamma.numel() != hidden or \
+            any(p.shape != residual.shape for p in partials):
+        raise RmsnormError(-2, "shape mismatch between out, residual, partials and gamma")
+    if any(t.dtype != residual.dtype for t in [out, gamma, *partials]) or \
+            residual.dtype not in DTYPE_CODE:
+        raise RmsnormError(-3, "dtypes must match and be f32/f16/bf16")
+    arr = (ctypes.c_void_p * max(k, 1))(*[_dev_ptr(p, f"partials[{i}]") for i, p in enumerate(partials)])
+    _check(lib().add_rmsnorm_fwd(_dev_ptr(out, "out"), _dev_ptr(residual, "residual"), arr, k,
+                                 _dev_ptr(gamma, "gamma"), rows, hidden, float(eps),
+                                 DTYPE_CODE[residual.dtype], _stream(residual, stream)))
+
+
+def rmsnorm_plan(rows: int, hidden: int, k: int, dtype: str, aligned: bool = True) -> str:
+    """Name of the kernel variant the dispatcher picks (k = 0: plain)."""
+    buf = ctypes.create_string_buffer(128)
+    _check(lib().rmsnorm_plan(rows, hidden, k, DTYPE_NAME[dtype], int(aligned), buf, 128))
+    return buf.value.decode()
+
+
+def rmsnorm_variants(dtype: str) -> list:
+    """Names of every compiled kernel variant for dtype."""
+    buf = ctypes.create_string_buffer(1 << 16)
+    n = lib().rmsnorm_variants(DTYPE_NAME[dtype], buf, 1 << 16)
+    if n < 0:
+        _check(n)
+    return [s for s in buf.value.decode().split("\n") if s]
+
+
+# convenience wrappers ------------------------------------------------------
+
+def rmsnorm(x: torch.Tensor, gamma: torch.Tensor, eps: float = 1e-6) -> torch.Tensor:
+    out = torch.empty_like(x)
+    rmsnorm_fwd(out, x, gamma, eps)
+    return out
+
+
+def add_rmsnorm(partials: Sequence[torch.Tensor], residual: torch.Tensor, gamma: torch.Tensor,
+                eps: float = 1e-6) -> torch.Tensor:
+    out = torch.empty_like(residual)
+    add_rmsnorm_fwd(out, residual, partials, gamma, eps)
+    return out

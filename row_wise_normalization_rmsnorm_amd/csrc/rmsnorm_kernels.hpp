@@ -1,0 +1,500 @@
+// rmsnorm_kernels.hpp -- gfx950 (CDNA4, wave64) kernels for row-wise RMSNorm and
+// the fused "K partials + residual -> residual in place -> RMSNorm" form.
+//
+// Method: page "RMSNorm kernel", section 1 Background and section 2
+// "Abstraction" (per-row sum of squares -> mean -> + eps -> rsqrt; then
+// x * gamma * rsqrt), and page "Tokenweave fused-RMSNorm-AR kernel", "Code
+// walkthrough" (partials + residual summed, residual written back in place,
+// fp32 sum of squares of the stored values, then residual * scale * weight).
+//
+// The path is bound by HBM bandwidth (no contraction, so no MFMA).  Design:
+//   * 128-bit global loads/stores (global_load_dwordx4): 8 bf16/fp16 or 4 fp32
+//     elements per lane per access, a wave covering 1 KiB contiguous.
+//   * row_vgpr: the whole row lives in VGPRs between the two phases, so every
+//     input byte is read from HBM exactly once and the normalised output is
+//     produced from registers.  Threads-per-row (TPR) is a template choice:
+//     TPR < 64 packs several rows into one wave (segmented DPP reduction),
+//     TPR = 64 is a row per wave (no LDS, no barrier), TPR > 64 spreads a row
+//     over several waves of one workgroup (DPP within waves, then LDS).
+//   * row_stream: two passes over a row of any length.  Pass 1 streams the
+//     inputs and stages the rounded row in LDS (or, when it does not fit,
+//     re-reads the thread's own freshly written residual / input in pass 2).
+//   * Reductions: fp32; within a wave by DPP (quad_perm, row_half_mirror,
+//     row_mirror) and ds_swizzle SWAP16, and readlane for the two 32-lane
+//     halves; across waves through a small double-buffered LDS array that
+//     every wave sums in the same fixed order, so all waves agree bitwise.
+//   * Conversions: bf16 widening is a shift; narrowing uses gfx950's
+//     v_cvt_pk_bf16_f32 / v_cvt_pk_f16_f32 (round to nearest even, the
+//     rounding the stored residual must reproduce exactly).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rmsn {
+
+constexpr int kMaxK = 16;
+
+struct PartialPtrs {
+  const void* p[kMaxK];
+};
+
+struct RowArgs {
+  void* out;
+  void* residual;        // nullptr for plain RMSNorm
+  PartialPtrs partials;  // partials.p[0] is x for plain RMSNorm
+  const void* gamma;
+  int64_t rows;
+  int hidden;            // elements per row
+  int chunks;            // vector chunks (16 B) per row, or elements for scalar kernels
+  int k;                 // number of partials (fused), 1 for plain
+  float eps;
+};
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float as_f(uint32_t u) { return __builtin_bit_cast(float, u); }
+__device__ __forceinline__ uint32_t as_u(float f) { return __builtin_bit_cast(uint32_t, f); }
+
+// ---- storage types -------------------------------------------------------
+// Each dtype describes its 16-byte vector chunk (V elements) and its scalar
+// element, with widening to fp32 and narrowing (round to nearest even).
+
+template <typename T>
+struct DT;
+
+template <>
+struct DT<float> {
+  static constexpr int V = 4;
+  using scalar_t = float;
+  __device__ static void unpack(const uint4& r, float (&f)[V]) {
+    f[0] = as_f(r.x); f[1] = as_f(r.y); f[2] = as_f(r.z); f[3] = as_f(r.w);
+  }
+  __device__ static uint4 pack(const float (&f)[V]) {
+    return make_uint4(as_u(f[0]), as_u(f[1]), as_u(f[2]), as_u(f[3]));
+  }
+  __device__ static float widen(scalar_t s) { return s; }
+  __device__ static scalar_t narrow(float f) { return f; }
+};
+
+template <>
+struct DT<__bf16> {
+  static constexpr int V = 8;
+  using scalar_t = uint16_t;
+  __device__ static void unpack2(uint32_t u, float& lo, float& hi) {
+    lo = as_f(u << 16);
+    hi = as_f(u & 0xffff0000u);
+  }
+  __device__ static uint32_t pack2(float lo, float hi) {
+    f32x2 v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+  }
+  __device__ static void unpack(const uint4& r, float (&f)[V]) {
+    unpack2(r.x, f[0], f[1]); unpack2(r.y, f[2], f[3]);
+    unpack2(r.z, f[4], f[5]); unpack2(r.w, f[6], f[7]);
+  }
+  __device__ static uint4 pack(const float (&f)[V]) {
+    return make_uint4(pack2(f[0], f[1]), pack2(f[2], f[3]), pack2(f[4], f[5]), pack2(f[6], f[7]));
+  }
+  __device__ static float widen(scalar_t s) { return as_f((uint32_t)s << 16); }
+  __device__ static scalar_t narrow(float f) { return (scalar_t)(pack2(f, 0.0f) & 0xffffu); }
+};
+
+template <>
+struct DT<_Float16> {
+  static constexpr int V = 8;
+  using scalar_t = uint16_t;
+  __device__ static void unpack2(uint32_t u, float& lo, float& hi) {
+    f32x2 v = __builtin_convertvector(__builtin_bit_cast(f16x2, u), f32x2);
+    lo = v.x;
+    hi = v.y;
+  }
+  __device__ static uint32_t pack2(float lo, float hi) {
+    f32x2 v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+  }
+  __device__ static void unpack(const uint4& r, float (&f)[V]) {
+    unpack2(r.x, f[0], f[1]); unpack2(r.y, f[2], f[3]);
+    unpack2(r.z, f[4], f[5]); unpack2(r.w, f[6], f[7]);
+  }
+  __device__ static uint4 pack(const float (&f)[V]) {
+    return make_uint4(pack2(f[0], f[1]), pack2(f[2], f[3]), pack2(f[4], f[5]), pack2(f[6], f[7]));
+  }
+  __device__ static float widen(scalar_t s) {
+    return (float)__builtin_bit_cast(_Float16, s);
+  }
+  __device__ static scalar_t narrow(float f) {
+    return __builtin_bit_cast(scalar_t, (_Float16)f);
+  }
+};
+
+// A "chunk" is what one lane moves per access: 16 bytes (vector kernels) or
+// one element (scalar kernels, for unaligned bases or rows whose byte length
+// is not a multiple of 16).
+template <typename T, bool VEC>
+struct Chunk;
+
+template <typename T>
+struct Chunk<T, true> {
+  static constexpr int V = DT<T>::V;
+  using raw_t = uint4;
+  __device__ static raw_t load(const void* base, int64_t chunk) {
+    return reinterpret_cast<const uint4*>(base)[chunk];
+  }
+  __device__ static void store(void* base, int64_t chunk, raw_t v) {
+    reinterpret_cast<uint4*>(base)[chunk] = v;
+  }
+  __device__ static void unpack(const raw_t& r, float (&f)[V]) { DT<T>::unpack(r, f); }
+  __device__ static raw_t pack(const float (&f)[V]) { return DT<T>::pack(f); }
+};
+
+template <typename T>
+struct Chunk<T, false> {
+  static constexpr int V = 1;
+  using raw_t = typename DT<T>::scalar_t;
+  __device__ static raw_t load(const void* base, int64_t i) {
+    return reinterpret_cast<const raw_t*>(base)[i];
+  }
+  __device__ static void store(void* base, int64_t i, raw_t v) {
+    reinterpret_cast<raw_t*>(base)[i] = v;
+  }
+  __device__ static void unpack(const raw_t& r, float (&f)[1]) { f[0] = DT<T>::widen(r); }
+  __device__ static raw_t pack(const float (&f)[1]) { return DT<T>::narrow(f[0]); }
+};
+
+// ---- wave64 reductions ----------------------------------------------------
+// DPP controls (GFX9 encoding).
+constexpr int kDppQuadXor1 = 0xB1;     // quad_perm:[1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;     // quad_perm:[2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+constexpr int kSwizzleSwap16 = 0x401F;  // ds_swizzle bit mode: xor 16 within 32 lanes
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_get(float v) {
+  return as_f((uint32_t)__builtin_amdgcn_update_dpp(0, (int)as_u(v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of G lanes (G in {1,2,4,8,16,32}); every lane of the
+// group receives the group's sum.  Each step adds a value and its mirror
+// partner, so partners compute a+b and b+a: all lanes agree bitwise.
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (G >= 2) v += dpp_get<kDppQuadXor1>(v);
+  if constexpr (G >= 4) v += dpp_get<kDppQuadXor2>(v);
+  if constexpr (G >= 8) v += dpp_get<kDppRowHalfMirror>(v);
+  if constexpr (G >= 16) v += dpp_get<kDppRowMirror>(v);
+  if constexpr (G >= 32) v += as_f((uint32_t)__builtin_amdgcn_ds_swizzle((int)as_u(v), kSwizzleSwap16));
+  return v;
+}
+
+// Sum over the full wave, returned as a wave-uniform value.
+__device__ __forceinline__ float wave_sum(float v) {
+  v = group_sum<32>(v);
+  const float lo = as_f((uint32_t)__builtin_amdgcn_readlane((int)as_u(v), 0));
+  const float hi = as_f((uint32_t)__builtin_amdgcn_readlane((int)as_u(v), 32));
+  return lo + hi;
+}
+
+// ---- per-row scale ---------------------------------------------------------
+// inv = rsqrt(sum/hidden + eps): eps inside the root, after the mean.
+__device__ __forceinline__ float row_scale(float ss, int hidden, float eps) {
+  return rsqrtf(ss / (float)hidden + eps);
+}
+
+// ---- kernel 1: the row held in VGPRs ---------------------------------------
+// TPR threads per row, NPT chunks per thread (chunk c of a row belongs to
+// thread c % TPR), WGS threads per workgroup (WGS / TPR rows per workgroup).
+// KC: 0 = plain RMSNorm; >0 = fused with exactly KC partials; -1 = fused with
+// a runtime number of partials (args.k), summed one partial at a time.
+template <typename T, int TPR, int NPT, int WGS, int KC>
+__global__ __launch_bounds__(WGS) void row_vgpr_kernel(RowArgs a) {
+  using CK = Chunk<T, true>;
+  constexpr int V = CK::V;
+  constexpr int RPW = WGS / TPR;                // rows per workgroup
+  constexpr int WPR = TPR > 64 ? TPR / 64 : 1;  // waves per row
+  static_assert(TPR <= WGS && WGS % TPR == 0, "a row must fit in one workgroup");
+  static_assert(TPR < 64 ? (64 % TPR == 0) : (TPR % 64 == 0), "TPR must tile waves");
+  __shared__ float red[2][WPR > 1 ? RPW * WPR : 1];
+
+  const int tid = threadIdx.x;
+  const int tr = tid % TPR;  // thread index within its row
+  const int slot = tid / TPR;
+  const int C = a.chunks;
+  const int64_t rowstride = (int64_t)a.chunks;  // chunks per row
+  int parity = 0;
+
+  // gamma chunks are the same for every row this thread touches
+  float g[NPT][V];
+#pragma unroll
+  for (int i = 0; i < NPT; ++i) {
+    const int c = tr + i * TPR;
+    if (c < C) {
+      CK::unpack(CK::load(a.gamma, c), g[i]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < V; ++e) g[i][e] = 0.0f;
+    }
+  }
+
+  for (int64_t row0 = (int64_t)blockIdx.x * RPW; row0 < a.rows;
+       row0 += (int64_t)gridDim.x * RPW) {
+    const int64_t row = row0 + slot;
+    const bool row_ok = row < a.rows;
+    const int64_t base = row * rowstride;
+    float v[NPT][V];
+
+    if constexpr (KC == 0) {
+      uint4 raw[NPT];
+#pragma unroll
+      for (int i = 0; i < NPT; ++i) {
+        const int c = tr + i * TPR;
+        if (row_ok && c < C) raw[i] = CK::load(a.partials.p[0], base + c);
+      }
+#pragma unroll
+      for (int i = 0; i < NPT; ++i) {
+        const int c = tr + i * TPR;
+        if (row_ok && c < C) {
+          CK::unpack(raw[i], v[i]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < V; ++e) v[i][e] = 0.0f;
+        }
+      }
+    } else {
+      constexpr int NB = KC > 0 ? KC : 1;  // partial buffers loaded up front
+      uint4 raw[NB][NPT];
+      uint4 rres[NPT];
+#pragma unroll
+      for (int i = 0; i < NPT; ++i) {
+        const int c = tr + i * TPR;
+        if (row_ok && c < C) {
+#pragma unroll
+          for (int q = 0; q < NB; ++q) raw[q][i] = CK::load(a.partials.p[q], base + c);
+          rres[i] = CK::load(a.residual, base + c);
+        }
+      }
+      float acc[NPT][V];
+#pragma unroll
+      for (int i = 0; i < NPT; ++i) {
+        const int c = tr + i * TPR;
+        if (row_ok && c < C) {
+          CK::unpack(raw[0][i], acc[i]);  // accumulator seeded with p0
+#pragma unroll
+          for (int q = 1; q < NB; ++q) {
+            float t[V];
+            CK::unpack(raw[q][i], t);
+#pragma unroll
+            for (int e = 0; e < V; ++e) acc[i][e] += t[e];
+          }
+        }
+      }
+      if constexpr (KC < 0) {
+        // runtime K: remaining partials one at a time, in order
+        for (int q = 1; q < a.k; ++q) {
+          uint4 rq[NPT];
+#pragma unroll
+          for (int i = 0; i < NPT; ++i) {
+            const int c = tr + i * TPR;
+            if (row_ok && c < C) rq[i] = CK::load(a.partials.p[q], base + c);
+          }
+#pragma unroll
+          for (int i = 0; i < NPT; ++i) {
+            const int c = tr + i * TPR;
+            if (row_ok && c < C) {
+              float t[V];
+              CK::unpack(rq[i], t);
+#pragma unroll
+              for (int e = 0; e < V; ++e) acc[i][e] += t[e];
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < NPT; ++i) {
+        const int c = tr + i * TPR;
+        if (row_ok && c < C) {
+          float t[V];
+          CK::unpack(rres[i], t);
+#pragma unroll
+          for (int e = 0; e < V; ++e) acc[i][e] += t[e];  // residual added last
+          const uint4 rn = CK::pack(acc[i]);             // round once to dtype
+          CK::store(a.residual, base + c, rn);
+          CK::unpack(rn, v[i]);                          // normalise the stored row
+        } else {
+#pragma unroll
+          for (int e = 0; e < V; ++e) v[i][e] = 0.0f;
+        }
+      }
+    }
+
+    // sum of squares of this thread's elements (fp32)
+    float ss = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NPT; ++i)
+#pragma unroll
+      for (int e = 0; e < V; ++e) ss = __builtin_fmaf(v[i][e], v[i][e], ss);
+
+    float tot;
+    if constexpr (TPR < 64) {
+      tot = group_sum<TPR>(ss);
+    } else if constexpr (WPR == 1) {
+      tot = wave_sum(ss);
+    } else {
+      const float ws = wave_sum(ss);
+      const int w = tr / 64;  // wave index within the row
+      if ((tid & 63) == 0) red[parity][slot * WPR + w] = ws;
+      __syncthreads();
+      tot = 0.0f;
+#pragma unroll
+      for (int j = 0; j < WPR; ++j) tot += red[parity][slot * WPR + j];
+      parity ^= 1;
+    }
+
+    const float inv = row_scale(tot, a.hidden, a.eps);
+#pragma unroll
+    for (int i = 0; i < NPT; ++i) {
+      const int c = tr + i * TPR;
+      if (row_ok && c < C) {
+        float y[V];
+#pragma unroll
+        for (int e = 0; e < V; ++e) y[e] = (v[i][e] * inv) * g[i][e];
+        CK::store(a.out, base + c, CK::pack(y));
+      }
+    }
+  }
+}
+
+// ---- kernel 2: streaming two-pass row (any length) -------------------------
+// One row per workgroup of WGS threads.  Pass 1 reads the inputs chunk by
+// chunk (UNR chunks in flight per thread), writes the residual, accumulates
+// the sum of squares and keeps the rounded row: in LDS when LDS_STAGE, else
+// pass 2 re-reads what this same thread wrote (fused) or read (plain) --
+// a thread only ever touches its own chunks, so no barrier guards the stage.
+template <typename T, bool VEC, int WGS, bool LDS_STAGE, int KC, int UNR>
+__global__ __launch_bounds__(WGS) void row_stream_kernel(RowArgs a) {
+  using CK = Chunk<T, VEC>;
+  using raw_t = typename CK::raw_t;
+  constexpr int V = CK::V;
+  constexpr int NW = WGS / 64;
+  __shared__ float red[2][NW];
+  extern __shared__ __align__(16) unsigned char stage_bytes[];
+  raw_t* stage = reinterpret_cast<raw_t*>(stage_bytes);
+
+  const int tid = threadIdx.x;
+  const int C = a.chunks;
+  const int64_t rowstride = (int64_t)a.chunks;
+  int parity = 0;
+
+  for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x) {
+    const int64_t base = row * rowstride;
+    float ss = 0.0f;
+
+    for (int c0 = tid; c0 < C; c0 += WGS * UNR) {
+      raw_t rv[UNR];
+      if constexpr (KC == 0) {
+#pragma unroll
+        for (int u = 0; u < UNR; ++u) {
+          const int c = c0 + u * WGS;
+          if (c < C) rv[u] = CK::load(a.partials.p[0], base + c);
+        }
+      } else {
+        raw_t r0[UNR], rr[UNR];
+#pragma unroll
+        for (int u = 0; u < UNR; ++u) {
+          const int c = c0 + u * WGS;
+          if (c < C) {
+            r0[u] = CK::load(a.partials.p[0], base + c);
+            rr[u] = CK::load(a.residual, base + c);
+          }
+        }
+        float acc[UNR][V];
+#pragma unroll
+        for (int u = 0; u < UNR; ++u) {
+          const int c = c0 + u * WGS;
+          if (c < C) CK::unpack(r0[u], acc[u]);
+        }
+        const int K = KC > 0 ? KC : a.k;
+        for (int q = 1; q < K; ++q) {
+          raw_t rq[UNR];
+#pragma unroll
+          for (int u = 0; u < UNR; ++u) {
+            const int c = c0 + u * WGS;
+            if (c < C) rq[u] = CK::load(a.partials.p[q], base + c);
+          }
+#pragma unroll
+          for (int u = 0; u < UNR; ++u) {
+            const int c = c0 + u * WGS;
+            if (c < C) {
+              float t[V];
+              CK::unpack(rq[u], t);
+#pragma unroll
+              for (int e = 0; e < V; ++e) acc[u][e] += t[e];
+            }
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < UNR; ++u) {
+          const int c = c0 + u * WGS;
+          if (c < C) {
+            float t[V];
+            CK::unpack(rr[u], t);
+#pragma unroll
+            for (int e = 0; e < V; ++e) acc[u][e] += t[e];
+            rv[u] = CK::pack(acc[u]);
+            CK::store(a.residual, base + c, rv[u]);
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
+        const int c = c0 + u * WGS;
+        if (c < C) {
+          float t[V];
+          CK::unpack(rv[u], t);
+#pragma unroll
+          for (int e = 0; e < V; ++e) ss = __builtin_fmaf(t[e], t[e], ss);
+          if constexpr (LDS_STAGE) stage[c] = rv[u];
+        }
+      }
+    }
+
+    const float ws = wave_sum(ss);
+    if ((tid & 63) == 0) red[parity][tid >> 6] = ws;
+    __syncthreads();
+    float tot = 0.0f;
+#pragma unroll
+    for (int j = 0; j < NW; ++j) tot += red[parity][j];
+    parity ^= 1;
+    const float inv = row_scale(tot, a.hidden, a.eps);
+
+    const void* src = KC == 0 ? a.partials.p[0] : a.residual;
+    for (int c0 = tid; c0 < C; c0 += WGS * UNR) {
+      raw_t rv[UNR], rg[UNR];
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
+        const int c = c0 + u * WGS;
+        if (c < C) {
+          rv[u] = LDS_STAGE ? stage[c] : CK::load(src, base + c);
+          rg[u] = CK::load(a.gamma, c);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
+        const int c = c0 + u * WGS;
+        if (c < C) {
+          float t[V], g[V], y[V];
+          CK::unpack(rv[u], t);
+          CK::unpack(rg[u], g);
+#pragma unroll
+          for (int e = 0; e < V; ++e) y[e] = (t[e] * inv) * g[e];
+          CK::store(a.out, base + c, CK::pack(y));
+        }
+      }
+    }
+  }
+}
+
+}  // namespace rmsn

@@ -1,0 +1,65 @@
+// rmsnorm_table.hpp -- instantiates every kernel variant for one dtype and
+// builds its descriptor table (included once per dtype translation unit).
+#pragma once
+
+#include <stdio.h>
+
+#include <vector>
+
+#include "rmsnorm_kernels.hpp"
+#include "rmsnorm_variants.hpp"
+
+namespace rmsn {
+
+inline void add_variant(std::vector<Variant>& v, int dtype, const char* dname, int kind, int vec,
+                        int tpr, int npt, int wgs, int kc, int lds, int unr, const void* fn) {
+  Variant d{};
+  if (kind == kVgpr)
+    snprintf(d.name, sizeof(d.name), "vgpr<%s,tpr=%d,npt=%d,wg=%d,k=%d>", dname, tpr, npt, wgs, kc);
+  else
+    snprintf(d.name, sizeof(d.name), "stream<%s,%s,wg=%d,%s,k=%d,unr=%d>", dname,
+             vec ? "vec" : "elem", wgs, lds ? "lds" : "reread", kc, unr);
+  d.dtype = dtype;
+  d.kind = kind;
+  d.vec = vec;
+  d.tpr = tpr;
+  d.npt = npt;
+  d.wgs = wgs;
+  d.kc = kc;
+  d.lds_stage = lds;
+  d.unroll = unr;
+  d.fn = fn;
+  v.push_back(d);
+}
+
+template <typename T>
+std::vector<Variant> build_table(int dtype, const char* dname) {
+  std::vector<Variant> v;
+#define RMSN_ADD_VGPR_K(KC, TPR, NPT, WGS)                                            \
+  add_variant(v, dtype, dname, kVgpr, 1, TPR, NPT, WGS, KC, 0, 0,                     \
+              reinterpret_cast<const void*>(&row_vgpr_kernel<T, TPR, NPT, WGS, KC>));
+#define RMSN_ADD_VGPR(TPR, NPT, WGS) RMSN_KCS(RMSN_ADD_VGPR_K, TPR, NPT, WGS)
+  RMSN_VGPR_SHAPES(RMSN_ADD_VGPR)
+#define RMSN_ADD_STREAM_K(KC, VEC, WGS, LDS)                                          \
+  add_variant(v, dtype, dname, kStream, VEC ? 1 : 0, WGS, 0, WGS, KC, LDS ? 1 : 0,    \
+              VEC ? 2 : 4,                                                            \
+              reinterpret_cast<const void*>(                                         \
+                  &row_stream_kernel<T, VEC, WGS, LDS, KC, (VEC ? 2 : 4)>));
+#define RMSN_ADD_STREAM(VEC, WGS, LDS) RMSN_STREAM_KCS(RMSN_ADD_STREAM_K, VEC, WGS, LDS)
+  RMSN_STREAM_SHAPES(RMSN_ADD_STREAM)
+#undef RMSN_ADD_VGPR_K
+#undef RMSN_ADD_VGPR
+#undef RMSN_ADD_STREAM_K
+#undef RMSN_ADD_STREAM
+  return v;
+}
+
+}  // namespace rmsn
+
+#define RMSN_DEFINE_TABLE(T, CODE, DNAME)                                   \
+  const rmsn::Variant* rmsn_table_##DNAME(int* n) {                         \
+    static const std::vector<rmsn::Variant> table =                         \
+        rmsn::build_table<T>(CODE, #DNAME);                                 \
+    *n = (int)table.size();                                                 \
+    return table.data();                                                    \
+  }

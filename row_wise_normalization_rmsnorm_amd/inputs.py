@@ -145,3 +145,12 @@ def from_storage(a: np.ndarray, dtype: str) -> torch.Tensor:
 
 def storage_list(ts: List[torch.Tensor]) -> List[np.ndarray]:
     return [to_storage(t) for t in ts]
+
+
+def case(dtype: str, rows: int, hidden: int, k: int = 0, seed: int = 1, std: float = 1.0,
+         eps: float = 1e-6) -> Workload:
+    """An ad-hoc seeded test case with the workloads' value distributions
+    (k = 0: plain RMSNorm, else k partials plus a residual)."""
+    return Workload(f"case_{dtype}_{rows}x{hidden}_k{k}_s{seed}",
+                    "add_rmsnorm" if k else "rmsnorm", dtype, rows, hidden, k, eps, std,
+                    seed=seed)

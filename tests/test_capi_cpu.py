@@ -1,0 +1,112 @@
+"""The C ABI without a GPU: both libraries load, export every function their
+headers declare, and reject invalid arguments with the documented codes
+before touching the GPU (validation precedes any HIP call)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from row_wise_normalization_rmsnorm_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared(header):
+    text = open(os.path.join(ROOT, "include", header)).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(\w+)\s*\(", text, flags=re.M))
+
+
+def test_gpu_library_exports_every_declared_function():
+    names = declared("rmsnorm.h")
+    assert {"rmsnorm_fwd", "add_rmsnorm_fwd", "rmsnorm_strerror"} <= names
+    lib = B.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(B.EXPORTS) == names
+
+
+def test_oracle_library_exports_every_declared_function():
+    import oracle
+    names = declared("rmsnorm_oracle.h")
+    assert "rmsnorm_oracle" in names
+    lib = oracle._load()
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+FAKE = 0x100000  # never dereferenced: every call below fails validation first
+
+
+def fwd(**kw):
+    a = dict(out=FAKE, x=FAKE + (1 << 24), gamma=FAKE + (1 << 26), rows=4, hidden=64, eps=1e-6,
+             dtype=2)
+    a.update(kw)
+    return B.lib().rmsnorm_fwd(a["out"], a["x"], a["gamma"], a["rows"], a["hidden"], a["eps"],
+                               a["dtype"], None)
+
+
+def add(k=1, parts=None, **kw):
+    a = dict(out=FAKE, residual=FAKE + (1 << 24), gamma=FAKE + (1 << 26), rows=4, hidden=64,
+             eps=1e-6, dtype=2)
+    a.update(kw)
+    parts = parts if parts is not None else [FAKE + (1 << 27) + i * (1 << 20) for i in range(k)]
+    arr = (ctypes.c_void_p * max(1, len(parts)))(*parts)
+    return B.lib().add_rmsnorm_fwd(a["out"], a["residual"], arr, k, a["gamma"], a["rows"],
+                                   a["hidden"], a["eps"], a["dtype"], None)
+
+
+def test_error_codes():
+    assert fwd(dtype=3) == -3
+    assert fwd(hidden=0) == -2
+    assert fwd(hidden=(1 << 24) + 1) == -2
+    assert fwd(rows=-1) == -2
+    assert fwd(eps=-1.0) == -6
+    assert fwd(eps=float("inf")) == -6
+    assert fwd(eps=float("nan")) == -6
+    assert fwd(out=0) == -1
+    assert fwd(gamma=0) == -1
+    assert fwd(rows=0, out=0, x=0, gamma=0) == 0          # rows == 0: no-op
+    assert fwd(out=FAKE + 2, x=FAKE) == -5                 # partial overlap out/x
+    assert fwd(gamma=FAKE + 64) == -5                      # out overlaps gamma
+    assert add(k=0) == -4
+    assert add(k=17) == -4
+    assert add(k=2, parts=[FAKE + (1 << 27), 0]) == -1
+    assert add(residual=FAKE + (1 << 27) + 8, k=1) == -5   # residual overlaps a partial
+    assert add(out=FAKE + (1 << 24)) == -5                 # out overlaps residual
+    assert add(k=1, parts=[FAKE + 16]) == -5               # out partially overlaps a partial
+    assert add(gamma=FAKE + (1 << 24) + 100) == -5         # residual overlaps gamma
+    assert "overlap" in B.lib().rmsnorm_last_error().decode()
+    for code in (0, -1, -2, -3, -4, -5, -6, -7, -99):
+        assert B.lib().rmsnorm_strerror(code)
+
+
+def test_plan_names_follow_the_dispatch_rule():
+    plan = B.rmsnorm_plan
+    assert plan(8192, 4096, 1, "bf16").startswith("vgpr<bf16")
+    assert plan(4096, 8192, 8, "bf16").startswith("vgpr<bf16")
+    assert plan(512, 2048, 0, "f32").startswith("vgpr<f32")
+    assert plan(65536, 16384, 1, "bf16").startswith("stream<bf16,vec")
+    assert "lds" in plan(65536, 16384, 1, "bf16")
+    assert "tpr=8," in plan(1000, 64, 1, "bf16")            # several rows per wave
+    assert "tpr=64," in plan(512, 1592, 0, "bf16")          # one row per wave
+    assert "elem" in plan(10, 1591, 0, "bf16")              # odd row length
+    assert "elem" in plan(10, 4096, 1, "bf16", aligned=False)
+    assert "reread" in plan(10, 100000, 1, "bf16")          # row beyond the LDS stage
+    for k in range(0, 17):
+        assert plan(3, 777 * 8, k, "f16")
+
+
+def test_variant_table_and_forcing(monkeypatch):
+    names = B.rmsnorm_variants("bf16")
+    assert len(names) == len(set(names)) > 50
+    monkeypatch.setenv("RMSNORM_VARIANT", "vgpr<bf16,tpr=64,npt=1,wg=256,k=1>")
+    assert B.rmsnorm_plan(4, 512, 1, "bf16") == "vgpr<bf16,tpr=64,npt=1,wg=256,k=1>"
+    with pytest.raises(B.RmsnormError):
+        B.rmsnorm_plan(4, 1024, 1, "bf16")   # too long for that variant
+    monkeypatch.setenv("RMSNORM_VARIANT", "no-such-kernel")
+    with pytest.raises(B.RmsnormError):
+        B.rmsnorm_plan(4, 512, 1, "bf16")
