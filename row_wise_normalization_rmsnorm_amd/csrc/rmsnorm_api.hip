@@ -47,6 +47,9 @@ constexpr int64_t kLdsStageMax = 64 * 1024;
 constexpr int64_t kGridCapDefault = 1 << 20;
 // Rows up to this many elements are held in registers.
 constexpr int64_t kVgprMaxHidden = 8192;
+// With two or more partials, rows of at least this many bytes use the
+// streaming kernel (fewer registers per thread than holding K+1 chunk sets).
+constexpr int64_t kStreamMinBytesForK = 8192;
 
 const rmsn::Variant* table_for(int dtype, int* n) {
   switch (dtype) {
@@ -57,13 +60,17 @@ const rmsn::Variant* table_for(int dtype, int* n) {
   }
 }
 
-const rmsn::Variant* find(int dtype, int kind, int vec, int tpr, int npt, int wgs, int kc, int lds) {
+// npt: chunks per thread (register kernel) or chunks in flight per step
+// (streaming kernel).
+const rmsn::Variant* find(int dtype, int kind, int vec, int tpr, int npt, int wgs, int kc, int lds,
+                          int nt) {
   int n = 0;
   const rmsn::Variant* t = table_for(dtype, &n);
   for (int i = 0; i < n; ++i) {
     const rmsn::Variant& v = t[i];
     if (v.kind == kind && v.vec == vec && v.tpr == tpr && v.wgs == wgs && v.kc == kc &&
-        (kind == rmsn::kVgpr ? v.npt == npt : v.lds_stage == lds))
+        v.nt == nt &&
+        (kind == rmsn::kVgpr ? v.npt == npt : (v.lds_stage == lds && v.unroll == npt)))
       return &v;
   }
   return nullptr;
@@ -111,22 +118,32 @@ int choose(int dtype, int64_t hidden, int k, bool aligned, Plan* plan) {
     if (!fits(*v, dtype, hidden, k, vec_ok))
       return fail(RMSN_ERR_SHAPE, "RMSNORM_VARIANT=%s cannot run hidden=%lld k=%d", forced,
                   (long long)hidden, k);
-  } else if (vec_ok && hidden <= kVgprMaxHidden) {
+  } else if (vec_ok && hidden <= kVgprMaxHidden && !(k >= 2 && hidden * s >= kStreamMinBytesForK)) {
+    // One 16-byte chunk per thread wherever a workgroup can cover the row:
+    // threads per row = the next power of two >= chunks (several rows per
+    // wave below 64 chunks), up to 1024 threads, then 2 or 4 chunks each.
     const int64_t C = hidden * s / 16;
-    static const int shapes[][3] = {{8, 1, 256},   {16, 1, 256},  {32, 1, 256},
-                                    {64, 1, 256},  {64, 2, 256},  {64, 4, 256},
-                                    {256, 2, 256}, {256, 4, 256}, {512, 4, 512}};
-    for (const auto& sh : shapes) {
-      if ((int64_t)sh[0] * sh[1] >= C) {
-        v = find(dtype, rmsn::kVgpr, 1, sh[0], sh[1], sh[2], vgpr_kc(k), 0);
-        break;
-      }
+    int tpr = 8;
+    while (tpr < C && tpr < 1024) tpr *= 2;
+    int npt = (int)((C + tpr - 1) / tpr);
+    npt = npt <= 1 ? 1 : npt <= 2 ? 2 : 4;
+    int wgs = tpr < 256 ? 256 : tpr;
+    if (npt == 4 && tpr == 1024) {  // 16 waves x 4 chunks exceeds the register budget
+      tpr = 512;
+      wgs = 512;
     }
+    v = find(dtype, rmsn::kVgpr, 1, tpr, npt, wgs, vgpr_kc(k), 0, 1);
   } else {
+    // Streaming two-pass, LDS-staged while the row fits the stage budget.
+    // Fused calls use the runtime-K form, which sums the partials one at a
+    // time with few registers (measured faster than holding all K+1 chunk
+    // sets in registers at K = 8).
     const int64_t C = vec_ok ? hidden * s / 16 : hidden;
     const bool lds = hidden * s <= kLdsStageMax;
-    const int wgs = C <= 1024 ? 256 : C <= 4096 ? 512 : 1024;
-    v = find(dtype, rmsn::kStream, vec_ok ? 1 : 0, wgs, 0, wgs, stream_kc(k), lds ? 1 : 0);
+    const int wgs = C <= 1024 ? (lds && k >= 2 ? 512 : 256) : C <= 2048 ? 512 : 1024;
+    const int unr = vec_ok ? (lds && k < 2 ? 4 : 2) : 4;
+    v = find(dtype, rmsn::kStream, vec_ok ? 1 : 0, wgs, unr, wgs, k == 0 ? 0 : -1, lds ? 1 : 0,
+             lds ? 1 : 0);
   }
   if (!v) return fail(RMSN_ERR_SHAPE, "no kernel variant for hidden=%lld k=%d", (long long)hidden, k);
   plan->v = v;

@@ -52,6 +52,7 @@ struct RowArgs {
 };
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
@@ -136,15 +137,24 @@ struct DT<_Float16> {
 template <typename T, bool VEC>
 struct Chunk;
 
+// NT selects the nontemporal (streaming) cache policy for data that is touched
+// exactly once; gamma, reused by every row, is always loaded normally.
 template <typename T>
 struct Chunk<T, true> {
   static constexpr int V = DT<T>::V;
   using raw_t = uint4;
+  template <bool NT = false>
   __device__ static raw_t load(const void* base, int64_t chunk) {
-    return reinterpret_cast<const uint4*>(base)[chunk];
+    const u32x4* p = reinterpret_cast<const u32x4*>(base) + chunk;
+    u32x4 v;
+    if constexpr (NT) v = __builtin_nontemporal_load(p); else v = *p;
+    return make_uint4(v.x, v.y, v.z, v.w);
   }
+  template <bool NT = false>
   __device__ static void store(void* base, int64_t chunk, raw_t v) {
-    reinterpret_cast<uint4*>(base)[chunk] = v;
+    u32x4* p = reinterpret_cast<u32x4*>(base) + chunk;
+    const u32x4 w = {v.x, v.y, v.z, v.w};
+    if constexpr (NT) __builtin_nontemporal_store(w, p); else *p = w;
   }
   __device__ static void unpack(const raw_t& r, float (&f)[V]) { DT<T>::unpack(r, f); }
   __device__ static raw_t pack(const float (&f)[V]) { return DT<T>::pack(f); }
@@ -154,11 +164,15 @@ template <typename T>
 struct Chunk<T, false> {
   static constexpr int V = 1;
   using raw_t = typename DT<T>::scalar_t;
+  template <bool NT = false>
   __device__ static raw_t load(const void* base, int64_t i) {
-    return reinterpret_cast<const raw_t*>(base)[i];
+    const raw_t* p = reinterpret_cast<const raw_t*>(base) + i;
+    if constexpr (NT) return __builtin_nontemporal_load(p); else return *p;
   }
+  template <bool NT = false>
   __device__ static void store(void* base, int64_t i, raw_t v) {
-    reinterpret_cast<raw_t*>(base)[i] = v;
+    raw_t* p = reinterpret_cast<raw_t*>(base) + i;
+    if constexpr (NT) __builtin_nontemporal_store(v, p); else *p = v;
   }
   __device__ static void unpack(const raw_t& r, float (&f)[1]) { f[0] = DT<T>::widen(r); }
   __device__ static raw_t pack(const float (&f)[1]) { return DT<T>::narrow(f[0]); }
@@ -209,7 +223,8 @@ __device__ __forceinline__ float row_scale(float ss, int hidden, float eps) {
 // thread c % TPR), WGS threads per workgroup (WGS / TPR rows per workgroup).
 // KC: 0 = plain RMSNorm; >0 = fused with exactly KC partials; -1 = fused with
 // a runtime number of partials (args.k), summed one partial at a time.
-template <typename T, int TPR, int NPT, int WGS, int KC>
+// NT: streaming (nontemporal) loads and stores for the row data.
+template <typename T, int TPR, int NPT, int WGS, int KC, bool NT>
 __global__ __launch_bounds__(WGS) void row_vgpr_kernel(RowArgs a) {
   using CK = Chunk<T, true>;
   constexpr int V = CK::V;
@@ -232,7 +247,7 @@ __global__ __launch_bounds__(WGS) void row_vgpr_kernel(RowArgs a) {
   for (int i = 0; i < NPT; ++i) {
     const int c = tr + i * TPR;
     if (c < C) {
-      CK::unpack(CK::load(a.gamma, c), g[i]);
+      CK::unpack(CK::template load<false>(a.gamma, c), g[i]);
     } else {
 #pragma unroll
       for (int e = 0; e < V; ++e) g[i][e] = 0.0f;
@@ -251,7 +266,7 @@ __global__ __launch_bounds__(WGS) void row_vgpr_kernel(RowArgs a) {
 #pragma unroll
       for (int i = 0; i < NPT; ++i) {
         const int c = tr + i * TPR;
-        if (row_ok && c < C) raw[i] = CK::load(a.partials.p[0], base + c);
+        if (row_ok && c < C) raw[i] = CK::template load<NT>(a.partials.p[0], base + c);
       }
 #pragma unroll
       for (int i = 0; i < NPT; ++i) {
@@ -272,8 +287,8 @@ __global__ __launch_bounds__(WGS) void row_vgpr_kernel(RowArgs a) {
         const int c = tr + i * TPR;
         if (row_ok && c < C) {
 #pragma unroll
-          for (int q = 0; q < NB; ++q) raw[q][i] = CK::load(a.partials.p[q], base + c);
-          rres[i] = CK::load(a.residual, base + c);
+          for (int q = 0; q < NB; ++q) raw[q][i] = CK::template load<NT>(a.partials.p[q], base + c);
+          rres[i] = CK::template load<NT>(a.residual, base + c);
         }
       }
       float acc[NPT][V];
@@ -298,7 +313,7 @@ __global__ __launch_bounds__(WGS) void row_vgpr_kernel(RowArgs a) {
 #pragma unroll
           for (int i = 0; i < NPT; ++i) {
             const int c = tr + i * TPR;
-            if (row_ok && c < C) rq[i] = CK::load(a.partials.p[q], base + c);
+            if (row_ok && c < C) rq[i] = CK::template load<NT>(a.partials.p[q], base + c);
           }
 #pragma unroll
           for (int i = 0; i < NPT; ++i) {
@@ -321,7 +336,7 @@ __global__ __launch_bounds__(WGS) void row_vgpr_kernel(RowArgs a) {
 #pragma unroll
           for (int e = 0; e < V; ++e) acc[i][e] += t[e];  // residual added last
           const uint4 rn = CK::pack(acc[i]);             // round once to dtype
-          CK::store(a.residual, base + c, rn);
+          CK::template store<NT>(a.residual, base + c, rn);
           CK::unpack(rn, v[i]);                          // normalise the stored row
         } else {
 #pragma unroll
@@ -361,7 +376,7 @@ __global__ __launch_bounds__(WGS) void row_vgpr_kernel(RowArgs a) {
         float y[V];
 #pragma unroll
         for (int e = 0; e < V; ++e) y[e] = (v[i][e] * inv) * g[i][e];
-        CK::store(a.out, base + c, CK::pack(y));
+        CK::template store<NT>(a.out, base + c, CK::pack(y));
       }
     }
   }
@@ -373,7 +388,9 @@ __global__ __launch_bounds__(WGS) void row_vgpr_kernel(RowArgs a) {
 // the sum of squares and keeps the rounded row: in LDS when LDS_STAGE, else
 // pass 2 re-reads what this same thread wrote (fused) or read (plain) --
 // a thread only ever touches its own chunks, so no barrier guards the stage.
-template <typename T, bool VEC, int WGS, bool LDS_STAGE, int KC, int UNR>
+// NT: streaming loads/stores for data touched once (never for a residual
+// that pass 2 reads back from memory).
+template <typename T, bool VEC, int WGS, bool LDS_STAGE, int KC, int UNR, bool NT>
 __global__ __launch_bounds__(WGS) void row_stream_kernel(RowArgs a) {
   using CK = Chunk<T, VEC>;
   using raw_t = typename CK::raw_t;
@@ -398,7 +415,7 @@ __global__ __launch_bounds__(WGS) void row_stream_kernel(RowArgs a) {
 #pragma unroll
         for (int u = 0; u < UNR; ++u) {
           const int c = c0 + u * WGS;
-          if (c < C) rv[u] = CK::load(a.partials.p[0], base + c);
+          if (c < C) rv[u] = CK::template load<NT>(a.partials.p[0], base + c);
         }
       } else {
         raw_t r0[UNR], rr[UNR];
@@ -406,8 +423,8 @@ __global__ __launch_bounds__(WGS) void row_stream_kernel(RowArgs a) {
         for (int u = 0; u < UNR; ++u) {
           const int c = c0 + u * WGS;
           if (c < C) {
-            r0[u] = CK::load(a.partials.p[0], base + c);
-            rr[u] = CK::load(a.residual, base + c);
+            r0[u] = CK::template load<NT>(a.partials.p[0], base + c);
+            rr[u] = CK::template load<NT>(a.residual, base + c);
           }
         }
         float acc[UNR][V];
@@ -422,7 +439,7 @@ __global__ __launch_bounds__(WGS) void row_stream_kernel(RowArgs a) {
 #pragma unroll
           for (int u = 0; u < UNR; ++u) {
             const int c = c0 + u * WGS;
-            if (c < C) rq[u] = CK::load(a.partials.p[q], base + c);
+            if (c < C) rq[u] = CK::template load<NT>(a.partials.p[q], base + c);
           }
 #pragma unroll
           for (int u = 0; u < UNR; ++u) {
@@ -444,7 +461,7 @@ __global__ __launch_bounds__(WGS) void row_stream_kernel(RowArgs a) {
 #pragma unroll
             for (int e = 0; e < V; ++e) acc[u][e] += t[e];
             rv[u] = CK::pack(acc[u]);
-            CK::store(a.residual, base + c, rv[u]);
+            CK::template store<NT && LDS_STAGE>(a.residual, base + c, rv[u]);
           }
         }
       }
@@ -477,8 +494,8 @@ __global__ __launch_bounds__(WGS) void row_stream_kernel(RowArgs a) {
       for (int u = 0; u < UNR; ++u) {
         const int c = c0 + u * WGS;
         if (c < C) {
-          rv[u] = LDS_STAGE ? stage[c] : CK::load(src, base + c);
-          rg[u] = CK::load(a.gamma, c);
+          rv[u] = LDS_STAGE ? stage[c] : CK::template load<false>(src, base + c);
+          rg[u] = CK::template load<false>(a.gamma, c);
         }
       }
 #pragma unroll
@@ -490,7 +507,7 @@ __global__ __launch_bounds__(WGS) void row_stream_kernel(RowArgs a) {
           CK::unpack(rg[u], g);
 #pragma unroll
           for (int e = 0; e < V; ++e) y[e] = (t[e] * inv) * g[e];
-          CK::store(a.out, base + c, CK::pack(y));
+          CK::template store<NT>(a.out, base + c, CK::pack(y));
         }
       }
     }

@@ -12,13 +12,16 @@
 namespace rmsn {
 
 inline void add_variant(std::vector<Variant>& v, int dtype, const char* dname, int kind, int vec,
-                        int tpr, int npt, int wgs, int kc, int lds, int unr, const void* fn) {
+                        int tpr, int npt, int wgs, int kc, int lds, int unr, int nt,
+                        const void* fn) {
   Variant d{};
   if (kind == kVgpr)
-    snprintf(d.name, sizeof(d.name), "vgpr<%s,tpr=%d,npt=%d,wg=%d,k=%d>", dname, tpr, npt, wgs, kc);
+    snprintf(d.name, sizeof(d.name), "vgpr<%s,tpr=%d,npt=%d,wg=%d,k=%d%s>", dname, tpr, npt, wgs,
+             kc, nt ? ",nt" : "");
   else
-    snprintf(d.name, sizeof(d.name), "stream<%s,%s,wg=%d,%s,k=%d,unr=%d>", dname,
-             vec ? "vec" : "elem", wgs, lds ? "lds" : "reread", kc, unr);
+    snprintf(d.name, sizeof(d.name), "stream<%s,%s,wg=%d,%s,k=%d,unr=%d%s>", dname,
+             vec ? "vec" : "elem", wgs, lds ? "lds" : "reread", kc, unr, nt ? ",nt" : "");
+  d.nt = nt;
   d.dtype = dtype;
   d.kind = kind;
   d.vec = vec;
@@ -35,17 +38,18 @@ inline void add_variant(std::vector<Variant>& v, int dtype, const char* dname, i
 template <typename T>
 std::vector<Variant> build_table(int dtype, const char* dname) {
   std::vector<Variant> v;
-#define RMSN_ADD_VGPR_K(KC, TPR, NPT, WGS)                                            \
-  add_variant(v, dtype, dname, kVgpr, 1, TPR, NPT, WGS, KC, 0, 0,                     \
-              reinterpret_cast<const void*>(&row_vgpr_kernel<T, TPR, NPT, WGS, KC>));
-#define RMSN_ADD_VGPR(TPR, NPT, WGS) RMSN_KCS(RMSN_ADD_VGPR_K, TPR, NPT, WGS)
+#define RMSN_ADD_VGPR_K(KC, TPR, NPT, WGS, NT)                                        \
+  add_variant(v, dtype, dname, kVgpr, 1, TPR, NPT, WGS, KC, 0, 0, NT ? 1 : 0,         \
+              reinterpret_cast<const void*>(&row_vgpr_kernel<T, TPR, NPT, WGS, KC, NT>));
+#define RMSN_ADD_VGPR(TPR, NPT, WGS, NT) RMSN_KCS(RMSN_ADD_VGPR_K, TPR, NPT, WGS, NT)
   RMSN_VGPR_SHAPES(RMSN_ADD_VGPR)
-#define RMSN_ADD_STREAM_K(KC, VEC, WGS, LDS)                                          \
+#define RMSN_ADD_STREAM_K(KC, VEC, WGS, LDS, NT, UNR)                                 \
   add_variant(v, dtype, dname, kStream, VEC ? 1 : 0, WGS, 0, WGS, KC, LDS ? 1 : 0,    \
-              VEC ? 2 : 4,                                                            \
+              UNR, NT ? 1 : 0,                                                        \
               reinterpret_cast<const void*>(                                         \
-                  &row_stream_kernel<T, VEC, WGS, LDS, KC, (VEC ? 2 : 4)>));
-#define RMSN_ADD_STREAM(VEC, WGS, LDS) RMSN_STREAM_KCS(RMSN_ADD_STREAM_K, VEC, WGS, LDS)
+                  &row_stream_kernel<T, VEC, WGS, LDS, KC, UNR, NT>));
+#define RMSN_ADD_STREAM(VEC, WGS, LDS, NT, UNR) \
+  RMSN_STREAM_KCS(RMSN_ADD_STREAM_K, VEC, WGS, LDS, NT, UNR)
   RMSN_STREAM_SHAPES(RMSN_ADD_STREAM)
 #undef RMSN_ADD_VGPR_K
 #undef RMSN_ADD_VGPR

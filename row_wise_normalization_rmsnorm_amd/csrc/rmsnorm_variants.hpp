@@ -23,24 +23,35 @@ struct Variant {
   int kc;         // 0 plain, >0 fixed partial count, -1 runtime partial count
   int lds_stage;  // stream: stage the row in LDS (1) or re-read it (0)
   int unroll;     // stream: chunks in flight per thread per step
+  int nt;         // streaming (nontemporal) loads/stores for row data
   const void* fn; // host stub for hipLaunchKernel
 };
 
-// Shapes of the register-resident kernel: (threads/row, chunks/thread, threads/WG).
-#define RMSN_VGPR_SHAPES(X)                                                  \
-  X(8, 1, 256) X(16, 1, 256) X(32, 1, 256) X(64, 1, 256) X(64, 2, 256)      \
-  X(64, 4, 256) X(128, 2, 256) X(128, 4, 256) X(256, 1, 256) X(256, 2, 256) \
-  X(256, 4, 256) X(512, 1, 512) X(512, 2, 512) X(512, 4, 512)               \
-  X(1024, 1, 1024) X(1024, 2, 1024)
+// Shapes of the register-resident kernel: (threads/row, chunks/thread,
+// threads/WG, nontemporal).  Every shape streams with nontemporal accesses;
+// a few are also built with cached accesses, for comparison.
+#define RMSN_VGPR_SHAPES(X)                                                              \
+  X(8, 1, 256, true) X(16, 1, 256, true) X(32, 1, 256, true) X(64, 1, 256, true)        \
+  X(64, 2, 256, true) X(64, 4, 256, true) X(128, 1, 256, true) X(128, 2, 256, true)     \
+  X(128, 4, 256, true)                                                                  \
+  X(256, 1, 256, true) X(256, 2, 256, true) X(256, 4, 256, true) X(512, 1, 512, true)   \
+  X(512, 2, 512, true) X(512, 4, 512, true) X(1024, 1, 1024, true)                      \
+  X(1024, 2, 1024, true) X(64, 4, 256, false) X(256, 2, 256, false)                     \
+  X(512, 1, 512, false) X(512, 4, 512, false) X(1024, 1, 1024, false)
 
 // Partial counts compiled as constants (others use the runtime-K kernel).
 #define RMSN_KCS(X, ...) X(0, __VA_ARGS__) X(1, __VA_ARGS__) X(8, __VA_ARGS__) X(-1, __VA_ARGS__)
 
-// Shapes of the streaming kernel: (16-byte chunks?, threads/WG, LDS stage?).
-#define RMSN_STREAM_SHAPES(X)                                                          \
-  X(true, 256, true) X(true, 512, true) X(true, 1024, true) X(true, 256, false)        \
-  X(true, 512, false) X(true, 1024, false) X(false, 256, true) X(false, 512, true)     \
-  X(false, 1024, true) X(false, 256, false) X(false, 512, false) X(false, 1024, false)
+// Shapes of the streaming kernel: (16-byte chunks?, threads/WG, LDS stage?,
+// nontemporal, chunks in flight per thread).  LDS-staged variants stream;
+// re-reading ones keep the residual cacheable for the second pass.
+#define RMSN_STREAM_SHAPES(X)                                                                   \
+  X(true, 256, true, true, 2) X(true, 512, true, true, 2) X(true, 1024, true, true, 2)          \
+  X(true, 256, true, true, 4) X(true, 512, true, true, 4) X(true, 1024, true, true, 4)          \
+  X(true, 256, false, false, 2) X(true, 512, false, false, 2) X(true, 1024, false, false, 2)    \
+  X(false, 256, true, true, 4) X(false, 512, true, true, 4) X(false, 1024, true, true, 4)       \
+  X(false, 256, false, false, 4) X(false, 512, false, false, 4) X(false, 1024, false, false, 4) \
+  X(true, 512, true, false, 2)
 
 #define RMSN_STREAM_KCS(X, ...) X(0, __VA_ARGS__) X(1, __VA_ARGS__) X(-1, __VA_ARGS__)
 

@@ -1,0 +1,157 @@
+"""Turn rocprofv3 output into the short summaries kept under profiles/.
+
+Inputs (CSV, from ``rocprofv3 --output-format csv``):
+  * a kernel trace with ``--stats``: ``<dir>/<name>_kernel_stats.csv``;
+  * two counter runs of the same workload, ``--pmc FETCH_SIZE`` and
+    ``--pmc WRITE_SIZE``: ``<dir>/<name>_counter_collection.csv``;
+  * the same two counters over ``bench.py --copy-calibration`` (a plain 1 GiB
+    device copy), which fixes the scale of each counter on this GPU.
+
+Writes ``profiles/<kernel>__<workload>.md`` (average duration, achieved
+bandwidth, HBM bytes per launch, with the commands) and
+``profiles/traffic_<workload>.json`` (read by bench.py, tied to a hash of the
+kernel sources so that a stale figure is never reported).
+
+Usage: python -m row_wise_normalization_rmsnorm_amd.profiling --workload W
+         --trace DIR --fetch DIR --write DIR --copy-fetch DIR --copy-write DIR
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import re
+import statistics
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+COPY_BYTES = 1 << 30
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "row_wise_normalization_rmsnorm_amd", "csrc", "*"))):
+        h.update(open(p, "rb").read())
+    return h.hexdigest()
+
+
+def _one(d: str, suffix: str) -> str:
+    hits = glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True)
+    if not hits:
+        raise FileNotFoundError(f"no *{suffix} under {d}")
+    return hits[0]
+
+
+def kernel_stats(d: str):
+    rows = list(csv.DictReader(open(_one(d, "kernel_stats.csv"))))
+    out = []
+    for r in rows:
+        out.append({"name": r["Name"], "calls": int(r["Calls"]),
+                    "avg_ns": float(r["AverageNs"]), "min_ns": float(r["MinNs"]),
+                    "max_ns": float(r["MaxNs"]), "pct": float(r["Percentage"])})
+    return out
+
+
+def counter(d: str, name: str, kernel_substr: str):
+    rows = list(csv.DictReader(open(_one(d, "counter_collection.csv"))))
+    vals = [float(r["Counter_Value"]) for r in rows
+            if r["Counter_Name"] == name and kernel_substr in r["Kernel_Name"]]
+    if not vals:
+        raise ValueError(f"{name}: no dispatch of a kernel matching {kernel_substr!r} in {d}")
+    return statistics.median(vals), len(vals)
+
+
+def short_name(plan: str) -> str:
+    return re.sub(r"[^A-Za-z0-9]+", "_", plan).strip("_")
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--workload", required=True)
+    ap.add_argument("--plan", required=True, help="kernel variant name (bench.py prints it)")
+    ap.add_argument("--symbol", required=True, help="substring of the kernel's mangled name")
+    ap.add_argument("--trace", required=True)
+    ap.add_argument("--fetch", required=True)
+    ap.add_argument("--write", required=True)
+    ap.add_argument("--copy-fetch", required=True)
+    ap.add_argument("--copy-write", required=True)
+    ap.add_argument("--bench-json", default=None, help="bench.py output line (for the event timing)")
+    a = ap.parse_args()
+
+    import sys
+    sys.path.insert(0, ROOT)
+    from row_wise_normalization_rmsnorm_amd.workloads import WORKLOADS
+    w = WORKLOADS[a.workload]
+    nbytes = w.algorithmic_bytes()
+
+    stats = kernel_stats(a.trace)
+    mine = [s for s in stats if a.symbol in s["name"]]
+    if not mine:
+        raise SystemExit(f"kernel {a.symbol} not in trace")
+    k = mine[0]
+    fetch_kib, nf = counter(a.fetch, "FETCH_SIZE", a.symbol)
+    write_kib, nw = counter(a.write, "WRITE_SIZE", a.symbol)
+    cf_kib, _ = counter(a.copy_fetch, "FETCH_SIZE", "copyBuffer")
+    cw_kib, _ = counter(a.copy_write, "WRITE_SIZE", "copyBuffer")
+    fscale = COPY_BYTES / 1024 / cf_kib
+    wscale = COPY_BYTES / 1024 / cw_kib
+    read_b = fetch_kib * fscale * 1024
+    write_b = write_kib * wscale * 1024
+    traffic = read_b + write_b
+    achieved = nbytes / (k["avg_ns"] * 1e-9) / 1e9
+    event = None
+    if a.bench_json and os.path.exists(a.bench_json):
+        for line in open(a.bench_json):
+            if line.startswith("{"):
+                event = json.loads(line)
+
+    name = short_name(a.plan)
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    md = os.path.join(ROOT, "profiles", f"{name}__{w.name}.md")
+    with open(md, "w") as f:
+        f.write(f"# {a.plan} on {w.name}\n\n")
+        f.write(f"Workload: {w.describe()}; algorithmic bytes per launch {nbytes:,} "
+                f"(each tensor element read or written once, gamma once).\n\n")
+        f.write("## Kernel trace (rocprofv3 --kernel-trace --stats)\n\n")
+        f.write("Command: `rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o run -- "
+                f"python bench.py --workload {w.name} --no-cpu-baseline`\n\n")
+        f.write("| kernel | calls | avg us | min us | max us | % time |\n|---|---|---|---|---|---|\n")
+        for s in stats[:4]:
+            f.write(f"| {s['name'][:90]} | {s['calls']} | {s['avg_ns'] / 1e3:.2f} | "
+                    f"{s['min_ns'] / 1e3:.2f} | {s['max_ns'] / 1e3:.2f} | {s['pct']:.1f} |\n")
+        f.write(f"\nAchieved (algorithmic bytes / average duration): **{achieved:.0f} GB/s**, "
+                f"{100 * achieved / 8000:.1f}% of the 8 TB/s HBM peak.\n")
+        if event:
+            f.write(f"bench.py (HIP events over the timed region, same command without the "
+                    f"profiler): {event['ms_per_step'] * 1e3:.2f} us per launch, "
+                    f"{event['value']:.0f} GB/s.\n")
+        f.write("\n## HBM bytes (rocprofv3 --pmc, one counter per run)\n\n")
+        f.write("Commands: `rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -o run -- python "
+                f"bench.py --workload {w.name} --steps 10 --warmup 2 --no-cpu-baseline`, the same "
+                "with `--pmc WRITE_SIZE`, and both counters over `python bench.py "
+                "--copy-calibration` (1 GiB device copy).\n\n")
+        f.write("| counter | KiB per dispatch (median) | dispatches | copy-calibration KiB for "
+                "1 GiB | scale | bytes per launch |\n|---|---|---|---|---|---|\n")
+        f.write(f"| FETCH_SIZE | {fetch_kib:,.1f} | {nf} | {cf_kib:,.1f} | {fscale:.4f} | "
+                f"{read_b:,.0f} |\n")
+        f.write(f"| WRITE_SIZE | {write_kib:,.1f} | {nw} | {cw_kib:,.1f} | {wscale:.4f} | "
+                f"{write_b:,.0f} |\n")
+        f.write(f"\nHBM traffic per launch {traffic:,.0f} B = {traffic / nbytes:.4f} x the "
+                "algorithmic bytes.\n")
+        f.write(f"\nKernel sources sha256: `{source_hash()}`\n")
+    tj = os.path.join(ROOT, "profiles", f"traffic_{w.name}.json")
+    json.dump({"workload": w.name, "kernel": a.plan, "traffic_bytes_per_launch": round(traffic),
+               "read_bytes": round(read_b), "write_bytes": round(write_b),
+               "algorithmic_bytes": nbytes, "fetch_kib": fetch_kib, "write_kib": write_kib,
+               "copy_fetch_kib_per_gib": cf_kib, "copy_write_kib_per_gib": cw_kib,
+               "avg_kernel_ns": k["avg_ns"], "source_sha256": source_hash()},
+              open(tj, "w"), indent=1)
+    print(md)
+    print(tj)
+    return 0
+
+
+if __name__ == "__main__":
+    raise SystemExit(main())

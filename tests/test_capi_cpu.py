@@ -87,12 +87,13 @@ def test_error_codes():
 def test_plan_names_follow_the_dispatch_rule():
     plan = B.rmsnorm_plan
     assert plan(8192, 4096, 1, "bf16").startswith("vgpr<bf16")
-    assert plan(4096, 8192, 8, "bf16").startswith("vgpr<bf16")
+    assert plan(4096, 8192, 8, "bf16").startswith("stream<bf16,vec")   # K >= 2, long rows
+    assert plan(4096, 1024, 8, "bf16").startswith("vgpr<bf16")
     assert plan(512, 2048, 0, "f32").startswith("vgpr<f32")
     assert plan(65536, 16384, 1, "bf16").startswith("stream<bf16,vec")
     assert "lds" in plan(65536, 16384, 1, "bf16")
     assert "tpr=8," in plan(1000, 64, 1, "bf16")            # several rows per wave
-    assert "tpr=64," in plan(512, 1592, 0, "bf16")          # one row per wave
+    assert "tpr=64," in plan(512, 512, 0, "bf16")           # one row per wave
     assert "elem" in plan(10, 1591, 0, "bf16")              # odd row length
     assert "elem" in plan(10, 4096, 1, "bf16", aligned=False)
     assert "reread" in plan(10, 100000, 1, "bf16")          # row beyond the LDS stage
@@ -103,8 +104,8 @@ def test_plan_names_follow_the_dispatch_rule():
 def test_variant_table_and_forcing(monkeypatch):
     names = B.rmsnorm_variants("bf16")
     assert len(names) == len(set(names)) > 50
-    monkeypatch.setenv("RMSNORM_VARIANT", "vgpr<bf16,tpr=64,npt=1,wg=256,k=1>")
-    assert B.rmsnorm_plan(4, 512, 1, "bf16") == "vgpr<bf16,tpr=64,npt=1,wg=256,k=1>"
+    monkeypatch.setenv("RMSNORM_VARIANT", "vgpr<bf16,tpr=64,npt=1,wg=256,k=1,nt>")
+    assert B.rmsnorm_plan(4, 512, 1, "bf16") == "vgpr<bf16,tpr=64,npt=1,wg=256,k=1,nt>"
     with pytest.raises(B.RmsnormError):
         B.rmsnorm_plan(4, 1024, 1, "bf16")   # too long for that variant
     monkeypatch.setenv("RMSNORM_VARIANT", "no-such-kernel")
