@@ -107,6 +107,61 @@ def cpu_baseline(w, target_cpu_seconds: float = 12.0, max_passes: int = 40) -> d
                        f"({cpu:.1f} CPU-seconds), rows split over {cores} threads")}
 
 
+def stream_ceiling(w, dev: str = "cuda:0", steps: int = 60, rotate_gib: float = 1.0) -> dict:
+    """HBM bandwidth of a plain streaming kernel (libstreamprobe.so) moving the
+    same bytes as one step of the workload: K+1 read streams and 2 write
+    streams for the fused form, 1 and 1 for the plain form, each the size of
+    one [rows, hidden] tensor, with the same buffer rotation."""
+    import ctypes
+    import torch
+    path = os.path.join(ROOT, "row_wise_normalization_rmsnorm_amd", "libstreamprobe.so")
+    lib = ctypes.CDLL(path)
+    lib.stream_probe.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int,
+                                 ctypes.POINTER(ctypes.c_void_p), ctypes.c_int, ctypes.c_int64,
+                                 ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    nr, nw = (w.k + 1, 2) if w.fused else (1, 1)
+    tensor_bytes = w.rows * w.hidden * w.itemsize
+    n16 = tensor_bytes // 16
+    set_bytes = (nr + nw) * tensor_bytes
+    nsets = max(1, int(-(-rotate_gib * (1 << 30) // set_bytes)))
+    bufs = [[torch.empty(n16 * 16, dtype=torch.uint8, device=dev).fill_(j + 1)
+             for j in range(nr + nw)] for _ in range(nsets)]
+    sink = torch.zeros(64, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    best = None
+    for grid in (2048, 4096, 8192):
+        args = []
+        for b in bufs:
+            ra = (ctypes.c_void_p * nr)(*[t.data_ptr() for t in b[:nr]])
+            wa = (ctypes.c_void_p * nw)(*[t.data_ptr() for t in b[nr:]])
+            args.append((ra, wa))
+
+        def launch(i):
+            ra, wa = args[i % nsets]
+            rc = lib.stream_probe(ra, nr, wa, nw, n16, sink.data_ptr(), grid, stream.cuda_stream)
+            if rc != 0:
+                raise RuntimeError(f"stream_probe failed: {rc}")
+
+        for i in range(5):
+            launch(i)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(steps):
+            launch(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / steps * 1e3
+        gbs = (nr + nw) * tensor_bytes / us / 1e3
+        if best is None or gbs > best["value"]:
+            best = {"value": round(gbs, 1), "unit": "GB/s", "us": round(us, 2), "grid": grid}
+    best.update({"reads": nr, "writes": nw, "kind": "plain nontemporal 16-byte streaming kernel",
+                 "frac_of_peak": round(best["value"] / HBM_PEAK_GBS, 4)})
+    del bufs
+    return best
+
+
 def copy_calibration() -> None:
     """A plain device copy of known size (1 GiB), for scaling the HBM byte
     counters read by rocprofv3 --pmc."""
@@ -128,6 +183,8 @@ def main() -> int:
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the streaming-ceiling probe")
     ap.add_argument("--rotate-bytes", type=float, default=1.0,
                     help="GiB of distinct buffers rotated through (cold cache)")
     a = ap.parse_args()
@@ -215,6 +272,14 @@ def main() -> int:
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic},
     }
+    if not a.no_ceiling:
+        del sets
+        torch.cuda.empty_cache()
+        ceil = stream_ceiling(w)
+        ceil["kernel_frac_of_ceiling"] = round(gbs / ceil["value"], 4)
+        result["stream_ceiling"] = ceil
+        print(f"[bench] streaming ceiling for this mix: {ceil['value']:.0f} GB/s; kernel at "
+              f"{100 * ceil['kernel_frac_of_ceiling']:.1f}% of it", file=sys.stderr, flush=True)
     if not a.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(w)
