@@ -154,3 +154,20 @@ def case(dtype: str, rows: int, hidden: int, k: int = 0, seed: int = 1, std: flo
     return Workload(f"case_{dtype}_{rows}x{hidden}_k{k}_s{seed}",
                     "add_rmsnorm" if k else "rmsnorm", dtype, rows, hidden, k, eps, std,
                     seed=seed)
+
+
+def device_tensor(w: Workload, tensor_id: int, device: str) -> torch.Tensor:
+    """A [rows, hidden] tensor drawn directly on the device by torch's own
+    seeded generator (keyed by seed and tensor id): for sizes too large to
+    draw on the host in reasonable time.  Same distributions as above, but
+    not the same numbers as ``tensor_rows``."""
+    g = torch.Generator(device=device)
+    g.manual_seed(w.seed * 1_000_003 + tensor_id)
+    std = 1.0 if tensor_id == RESIDUAL_ID else w.part_std
+    out = torch.empty((w.rows, w.hidden), dtype=TORCH_DTYPE[w.dtype], device=device)
+    step = max(1, (1 << 26) // w.hidden)
+    for r0 in range(0, w.rows, step):
+        a = torch.randn((min(step, w.rows - r0), w.hidden), generator=g, device=device,
+                        dtype=torch.float32)
+        out[r0:r0 + a.shape[0]].copy_(a.mul_(std))
+    return out
