@@ -67,8 +67,15 @@ def _check(rc: int) -> None:
                                f"{l.rmsnorm_last_error().decode()}")
 
 
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream(t: torch.Tensor, stream) -> Optional[int]:
+    """The HIP stream to launch on: the given one, else torch's current
+    stream on the tensor's device."""
     if stream is None:
+        if _raw_stream is not None:
+            return _raw_stream(t.get_device())
         stream = torch.cuda.current_stream(t.device)
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
