@@ -33,9 +33,10 @@
  *     nothing is launched and a negative RMSN_ERR_* code is returned.
  *     rmsnorm_last_error() describes the most recent failure of the calling
  *     thread.  rows == 0 is a no-op that returns RMSN_OK.
- *   - Any base alignment is accepted.  The 128-bit vector kernels are used
- *     when every base is 16-byte aligned and hidden*sizeof(dtype) is a
- *     multiple of 16; otherwise an element-wise kernel of the same numerics.
+ *   - Any base alignment is accepted.  Kernels move 16-byte chunks when every
+ *     base is 16-byte aligned and hidden*sizeof(dtype) is a multiple of 16,
+ *     else the widest of 8 or 4 bytes that both allow, else single elements;
+ *     the numerics are the same for every width.
  *   - Limits: 1 <= hidden <= RMSN_MAX_HIDDEN, rows >= 0, eps finite and >= 0.
  */
 #ifndef RMSNORM_H
@@ -99,12 +100,13 @@ const char* rmsnorm_last_error(void);
 
 /*
  * rmsnorm_plan -- which kernel the dispatcher picks for a call with these
- * sizes (k = 0 means plain RMSNorm; aligned != 0 means every base pointer is
- * 16-byte aligned).  Writes a NUL-terminated name such as
- * "vgpr<bf16,tpr=256,npt=2,wg=256,k=1>" into buf and returns RMSN_OK, or an
- * error code for sizes that a call would reject.  Launches nothing.
+ * sizes (k = 0 means plain RMSNorm; align is the alignment in bytes that
+ * every base pointer shares, 16 or more meaning 16-byte aligned).  Writes a
+ * NUL-terminated name such as "vgpr<bf16,tpr=512,npt=1,wg=512,k=1,nt>" into
+ * buf and returns RMSN_OK, or an error code for sizes that a call would
+ * reject.  Launches nothing.
  */
-int rmsnorm_plan(int64_t rows, int64_t hidden, int k, int dtype, int aligned, char* buf,
+int rmsnorm_plan(int64_t rows, int64_t hidden, int k, int dtype, int align, char* buf,
                  int buflen);
 
 /*

@@ -125,10 +125,11 @@ def add_rmsnorm_fwd(out: torch.Tensor, residual: torch.Tensor, partials: Sequenc
                                  DTYPE_CODE[residual.dtype], _stream(residual, stream)))
 
 
-def rmsnorm_plan(rows: int, hidden: int, k: int, dtype: str, aligned: bool = True) -> str:
-    """Name of the kernel variant the dispatcher picks (k = 0: plain)."""
+def rmsnorm_plan(rows: int, hidden: int, k: int, dtype: str, align: int = 16) -> str:
+    """Name of the kernel variant the dispatcher picks (k = 0: plain; align:
+    the alignment in bytes shared by every base pointer)."""
     buf = ctypes.create_string_buffer(128)
-    _check(lib().rmsnorm_plan(rows, hidden, k, DTYPE_NAME[dtype], int(aligned), buf, 128))
+    _check(lib().rmsnorm_plan(rows, hidden, k, DTYPE_NAME[dtype], int(align), buf, 128))
     return buf.value.decode()
 
 

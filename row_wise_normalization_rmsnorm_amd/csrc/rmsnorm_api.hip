@@ -62,13 +62,13 @@ const rmsn::Variant* table_for(int dtype, int* n) {
 
 // npt: chunks per thread (register kernel) or chunks in flight per step
 // (streaming kernel).
-const rmsn::Variant* find(int dtype, int kind, int vec, int tpr, int npt, int wgs, int kc, int lds,
+const rmsn::Variant* find(int dtype, int kind, int vb, int tpr, int npt, int wgs, int kc, int lds,
                           int nt) {
   int n = 0;
   const rmsn::Variant* t = table_for(dtype, &n);
   for (int i = 0; i < n; ++i) {
     const rmsn::Variant& v = t[i];
-    if (v.kind == kind && v.vec == vec && v.tpr == tpr && v.wgs == wgs && v.kc == kc &&
+    if (v.kind == kind && v.vb == vb && v.tpr == tpr && v.wgs == wgs && v.kc == kc &&
         v.nt == nt &&
         (kind == rmsn::kVgpr ? v.npt == npt : (v.lds_stage == lds && v.unroll == npt)))
       return &v;
@@ -85,15 +85,27 @@ struct Plan {
   size_t lds_bytes;  // dynamic LDS
 };
 
-// Can variant v run a call with these sizes?
-bool fits(const rmsn::Variant& v, int dtype, int64_t hidden, int k, bool vec_ok) {
+// The widest chunk (16, 8 or 4 bytes; 0 = element) that divides both the
+// row's byte length and the alignment every base pointer shares.
+int widest_chunk(int dtype, int64_t hidden, int align) {
+  const int s = dtype_size(dtype);
+  for (int vb = 16; vb > s; vb /= 2)
+    if (align >= vb && (hidden * s) % vb == 0) return vb;
+  return 0;
+}
+
+int64_t chunks_of(const rmsn::Variant& v, int dtype, int64_t hidden) {
+  return v.vb ? hidden * dtype_size(dtype) / v.vb : hidden;
+}
+
+// Can variant v run a call with these sizes and this base alignment?
+bool fits(const rmsn::Variant& v, int dtype, int64_t hidden, int k, int align) {
   const int s = dtype_size(dtype);
   if (v.dtype != dtype) return false;
-  if (v.vec && !vec_ok) return false;
-  const int64_t chunks = v.vec ? hidden * s / 16 : hidden;
+  if (v.vb && (align < v.vb || (hidden * s) % v.vb != 0)) return false;
   if (v.kind == rmsn::kVgpr) {
     if (v.kc != vgpr_kc(k) && !(v.kc == -1 && k > 0)) return false;
-    return chunks <= (int64_t)v.tpr * v.npt;
+    return chunks_of(v, dtype, hidden) <= (int64_t)v.tpr * v.npt;
   }
   if (v.kc != stream_kc(k) && !(v.kc == -1 && k > 0)) return false;
   if (v.lds_stage && hidden * s > kLdsStageMax) return false;
@@ -102,10 +114,12 @@ bool fits(const rmsn::Variant& v, int dtype, int64_t hidden, int k, bool vec_ok)
 
 // The dispatcher.  Register-resident rows up to 8192 elements, packing rows
 // into waves when they are short; streaming two-pass kernels above that
-// (LDS-staged while the row fits the stage budget) and for unaligned data.
-int choose(int dtype, int64_t hidden, int k, bool aligned, Plan* plan) {
+// (LDS-staged while the row fits the stage budget), for K >= 2 on long rows,
+// and whenever 16-byte accesses do not fit the alignment or row length.
+// align: the largest power of two (capped at 16) dividing every base pointer.
+int choose(int dtype, int64_t hidden, int k, int align, Plan* plan) {
   const int s = dtype_size(dtype);
-  const bool vec_ok = aligned && (hidden * s) % 16 == 0;
+  const int vb = widest_chunk(dtype, hidden, align);
   const rmsn::Variant* v = nullptr;
 
   const char* forced = getenv("RMSNORM_VARIANT");
@@ -115,10 +129,11 @@ int choose(int dtype, int64_t hidden, int k, bool aligned, Plan* plan) {
     for (int i = 0; i < n && !v; ++i)
       if (strcmp(t[i].name, forced) == 0) v = &t[i];
     if (!v) return fail(RMSN_ERR_SHAPE, "RMSNORM_VARIANT=%s names no variant of this dtype", forced);
-    if (!fits(*v, dtype, hidden, k, vec_ok))
-      return fail(RMSN_ERR_SHAPE, "RMSNORM_VARIANT=%s cannot run hidden=%lld k=%d", forced,
-                  (long long)hidden, k);
-  } else if (vec_ok && hidden <= kVgprMaxHidden && !(k >= 2 && hidden * s >= kStreamMinBytesForK)) {
+    if (!fits(*v, dtype, hidden, k, align))
+      return fail(RMSN_ERR_SHAPE, "RMSNORM_VARIANT=%s cannot run hidden=%lld k=%d align=%d",
+                  forced, (long long)hidden, k, align);
+  } else if (vb == 16 && hidden <= kVgprMaxHidden &&
+             !(k >= 2 && hidden * s >= kStreamMinBytesForK)) {
     // One 16-byte chunk per thread wherever a workgroup can cover the row:
     // threads per row = the next power of two >= chunks (several rows per
     // wave below 64 chunks), up to 1024 threads, then 2 or 4 chunks each.
@@ -132,22 +147,21 @@ int choose(int dtype, int64_t hidden, int k, bool aligned, Plan* plan) {
       tpr = 512;
       wgs = 512;
     }
-    v = find(dtype, rmsn::kVgpr, 1, tpr, npt, wgs, vgpr_kc(k), 0, 1);
+    v = find(dtype, rmsn::kVgpr, 16, tpr, npt, wgs, vgpr_kc(k), 0, 1);
   } else {
     // Streaming two-pass, LDS-staged while the row fits the stage budget.
     // Fused calls use the runtime-K form, which sums the partials one at a
     // time with few registers (measured faster than holding all K+1 chunk
     // sets in registers at K = 8).
-    const int64_t C = vec_ok ? hidden * s / 16 : hidden;
+    const int64_t C = vb ? hidden * s / vb : hidden;
     const bool lds = hidden * s <= kLdsStageMax;
     const int wgs = C <= 1024 ? (lds && k >= 2 ? 512 : 256) : C <= 2048 ? 512 : 1024;
-    const int unr = vec_ok ? (lds && k < 2 ? 4 : 2) : 4;
-    v = find(dtype, rmsn::kStream, vec_ok ? 1 : 0, wgs, unr, wgs, k == 0 ? 0 : -1, lds ? 1 : 0,
-             lds ? 1 : 0);
+    const int unr = vb == 16 ? (lds && k < 2 ? 4 : 2) : 4;
+    v = find(dtype, rmsn::kStream, vb, wgs, unr, wgs, k == 0 ? 0 : -1, lds ? 1 : 0, lds ? 1 : 0);
   }
   if (!v) return fail(RMSN_ERR_SHAPE, "no kernel variant for hidden=%lld k=%d", (long long)hidden, k);
   plan->v = v;
-  plan->chunks = (int)(v->vec ? hidden * s / 16 : hidden);
+  plan->chunks = (int)chunks_of(*v, dtype, hidden);
   plan->lds_bytes = (v->kind == rmsn::kStream && v->lds_stage) ? (size_t)hidden * s : 0;
   return RMSN_OK;
 }
@@ -157,7 +171,18 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
   return x < y + nb && y < x + na;
 }
 
-bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+// Largest power of two, capped at 16, dividing the address.
+int align_of(const void* p) {
+  const uintptr_t u = (uintptr_t)p;
+  int a = 16;
+  while (a > 1 && (u & (uintptr_t)(a - 1))) a /= 2;
+  return a;
+}
+
+int min_align(int a, const void* p) {
+  const int b = align_of(p);
+  return a < b ? a : b;
+}
 
 int common_checks(int dtype, int64_t rows, int64_t hidden, float eps) {
   if (dtype != RMSN_F32 && dtype != RMSN_F16 && dtype != RMSN_BF16)
@@ -204,7 +229,7 @@ int rmsnorm_fwd(void* out, const void* x, const void* gamma, int64_t rows, int64
     return fail(RMSN_ERR_ALIAS, "out partially overlaps x");
   if (overlap(out, nbytes, gamma, gbytes)) return fail(RMSN_ERR_ALIAS, "out overlaps gamma");
   Plan plan;
-  rc = choose(dtype, hidden, 0, aligned16(out) && aligned16(x) && aligned16(gamma), &plan);
+  rc = choose(dtype, hidden, 0, min_align(min_align(align_of(out), x), gamma), &plan);
   if (rc) return rc;
   rmsn::RowArgs a{};
   a.out = out;
@@ -229,21 +254,21 @@ int add_rmsnorm_fwd(void* out, void* residual, const void* const* partials, int 
     return fail(RMSN_ERR_NULL, "out, residual, partials and gamma must be non-NULL");
   const size_t nbytes = (size_t)rows * (size_t)hidden * dtype_size(dtype);
   const size_t gbytes = (size_t)hidden * dtype_size(dtype);
-  bool aligned = aligned16(out) && aligned16(residual) && aligned16(gamma);
+  int align = min_align(min_align(align_of(out), residual), gamma);
   for (int j = 0; j < k; ++j) {
     if (!partials[j]) return fail(RMSN_ERR_NULL, "partials[%d] is NULL", j);
     if (overlap(residual, nbytes, partials[j], nbytes))
       return fail(RMSN_ERR_ALIAS, "residual overlaps partials[%d]", j);
     if (out != partials[j] && overlap(out, nbytes, partials[j], nbytes))
       return fail(RMSN_ERR_ALIAS, "out partially overlaps partials[%d]", j);
-    aligned = aligned && aligned16(partials[j]);
+    align = min_align(align, partials[j]);
   }
   if (overlap(out, nbytes, residual, nbytes)) return fail(RMSN_ERR_ALIAS, "out overlaps residual");
   if (overlap(out, nbytes, gamma, gbytes)) return fail(RMSN_ERR_ALIAS, "out overlaps gamma");
   if (overlap(residual, nbytes, gamma, gbytes))
     return fail(RMSN_ERR_ALIAS, "residual overlaps gamma");
   Plan plan;
-  rc = choose(dtype, hidden, k, aligned, &plan);
+  rc = choose(dtype, hidden, k, align, &plan);
   if (rc) return rc;
   rmsn::RowArgs a{};
   a.out = out;
@@ -273,14 +298,16 @@ const char* rmsnorm_strerror(int code) {
 
 const char* rmsnorm_last_error(void) { return g_last_error; }
 
-int rmsnorm_plan(int64_t rows, int64_t hidden, int k, int dtype, int aligned, char* buf,
+int rmsnorm_plan(int64_t rows, int64_t hidden, int k, int dtype, int align, char* buf,
                  int buflen) {
   int rc = common_checks(dtype, rows, hidden, 0.0f);
   if (rc) return rc;
   if (k < 0 || k > RMSN_KMAX) return fail(RMSN_ERR_K, "k=%d outside [0, %d]", k, RMSN_KMAX);
   if (!buf || buflen < 1) return fail(RMSN_ERR_NULL, "buf must be non-NULL");
   Plan plan;
-  rc = choose(dtype, hidden, k, aligned != 0, &plan);
+  int a = 1;
+  while (a < 16 && a * 2 <= align) a *= 2;
+  rc = choose(dtype, hidden, k, a, &plan);
   if (rc) return rc;
   snprintf(buf, (size_t)buflen, "%s", plan.v->name);
   return RMSN_OK;

@@ -9,7 +9,9 @@
 //
 // The path is bound by HBM bandwidth (no contraction, so no MFMA).  Design:
 //   * 128-bit global loads/stores (global_load_dwordx4): 8 bf16/fp16 or 4 fp32
-//     elements per lane per access, a wave covering 1 KiB contiguous.
+//     elements per lane per access, a wave covering 1 KiB contiguous.  Rows
+//     whose byte length or base alignment only allows 8- or 4-byte accesses
+//     use those widths; only what no 4-byte access divides goes element-wise.
 //   * row_vgpr: the whole row lives in VGPRs between the two phases, so every
 //     input byte is read from HBM exactly once and the normalised output is
 //     produced from registers.  Threads-per-row (TPR) is a template choice:
@@ -52,7 +54,6 @@ struct RowArgs {
 };
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
@@ -60,108 +61,117 @@ __device__ __forceinline__ float as_f(uint32_t u) { return __builtin_bit_cast(fl
 __device__ __forceinline__ uint32_t as_u(float f) { return __builtin_bit_cast(uint32_t, f); }
 
 // ---- storage types -------------------------------------------------------
-// Each dtype describes its 16-byte vector chunk (V elements) and its scalar
-// element, with widening to fp32 and narrowing (round to nearest even).
+// Each dtype converts one 32-bit word of storage (one fp32, or two packed
+// 16-bit values) to and from fp32, and one scalar element.  Narrowing rounds
+// to nearest even.
 
 template <typename T>
 struct DT;
 
 template <>
 struct DT<float> {
-  static constexpr int V = 4;
+  static constexpr int PER_WORD = 1;
   using scalar_t = float;
-  __device__ static void unpack(const uint4& r, float (&f)[V]) {
-    f[0] = as_f(r.x); f[1] = as_f(r.y); f[2] = as_f(r.z); f[3] = as_f(r.w);
-  }
-  __device__ static uint4 pack(const float (&f)[V]) {
-    return make_uint4(as_u(f[0]), as_u(f[1]), as_u(f[2]), as_u(f[3]));
-  }
+  __device__ static void unpack_word(uint32_t u, float* f) { f[0] = as_f(u); }
+  __device__ static uint32_t pack_word(const float* f) { return as_u(f[0]); }
   __device__ static float widen(scalar_t s) { return s; }
   __device__ static scalar_t narrow(float f) { return f; }
 };
 
 template <>
 struct DT<__bf16> {
-  static constexpr int V = 8;
+  static constexpr int PER_WORD = 2;
   using scalar_t = uint16_t;
-  __device__ static void unpack2(uint32_t u, float& lo, float& hi) {
-    lo = as_f(u << 16);
-    hi = as_f(u & 0xffff0000u);
+  __device__ static void unpack_word(uint32_t u, float* f) {
+    f[0] = as_f(u << 16);
+    f[1] = as_f(u & 0xffff0000u);
   }
-  __device__ static uint32_t pack2(float lo, float hi) {
-    f32x2 v = {lo, hi};
+  __device__ static uint32_t pack_word(const float* f) {
+    f32x2 v = {f[0], f[1]};
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
   }
-  __device__ static void unpack(const uint4& r, float (&f)[V]) {
-    unpack2(r.x, f[0], f[1]); unpack2(r.y, f[2], f[3]);
-    unpack2(r.z, f[4], f[5]); unpack2(r.w, f[6], f[7]);
-  }
-  __device__ static uint4 pack(const float (&f)[V]) {
-    return make_uint4(pack2(f[0], f[1]), pack2(f[2], f[3]), pack2(f[4], f[5]), pack2(f[6], f[7]));
-  }
   __device__ static float widen(scalar_t s) { return as_f((uint32_t)s << 16); }
-  __device__ static scalar_t narrow(float f) { return (scalar_t)(pack2(f, 0.0f) & 0xffffu); }
+  __device__ static scalar_t narrow(float f) {
+    const float two[2] = {f, 0.0f};
+    return (scalar_t)(pack_word(two) & 0xffffu);
+  }
 };
 
 template <>
 struct DT<_Float16> {
-  static constexpr int V = 8;
+  static constexpr int PER_WORD = 2;
   using scalar_t = uint16_t;
-  __device__ static void unpack2(uint32_t u, float& lo, float& hi) {
+  __device__ static void unpack_word(uint32_t u, float* f) {
     f32x2 v = __builtin_convertvector(__builtin_bit_cast(f16x2, u), f32x2);
-    lo = v.x;
-    hi = v.y;
+    f[0] = v.x;
+    f[1] = v.y;
   }
-  __device__ static uint32_t pack2(float lo, float hi) {
-    f32x2 v = {lo, hi};
+  __device__ static uint32_t pack_word(const float* f) {
+    f32x2 v = {f[0], f[1]};
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
   }
-  __device__ static void unpack(const uint4& r, float (&f)[V]) {
-    unpack2(r.x, f[0], f[1]); unpack2(r.y, f[2], f[3]);
-    unpack2(r.z, f[4], f[5]); unpack2(r.w, f[6], f[7]);
-  }
-  __device__ static uint4 pack(const float (&f)[V]) {
-    return make_uint4(pack2(f[0], f[1]), pack2(f[2], f[3]), pack2(f[4], f[5]), pack2(f[6], f[7]));
-  }
-  __device__ static float widen(scalar_t s) {
-    return (float)__builtin_bit_cast(_Float16, s);
-  }
-  __device__ static scalar_t narrow(float f) {
-    return __builtin_bit_cast(scalar_t, (_Float16)f);
-  }
+  __device__ static float widen(scalar_t s) { return (float)__builtin_bit_cast(_Float16, s); }
+  __device__ static scalar_t narrow(float f) { return __builtin_bit_cast(scalar_t, (_Float16)f); }
 };
 
-// A "chunk" is what one lane moves per access: 16 bytes (vector kernels) or
-// one element (scalar kernels, for unaligned bases or rows whose byte length
-// is not a multiple of 16).
-template <typename T, bool VEC>
-struct Chunk;
+// Groups of W 32-bit words moved by one load or store instruction.
+template <int W>
+struct Words;
+template <>
+struct Words<1> {
+  using type = uint32_t;
+  __device__ static uint32_t get(type v, int) { return v; }
+  __device__ static void set(type& v, int, uint32_t x) { v = x; }
+};
+template <>
+struct Words<2> {
+  typedef uint32_t type __attribute__((ext_vector_type(2)));
+  __device__ static uint32_t get(type v, int i) { return v[i]; }
+  __device__ static void set(type& v, int i, uint32_t x) { v[i] = x; }
+};
+template <>
+struct Words<4> {
+  typedef uint32_t type __attribute__((ext_vector_type(4)));
+  __device__ static uint32_t get(type v, int i) { return v[i]; }
+  __device__ static void set(type& v, int i, uint32_t x) { v[i] = x; }
+};
 
+// A "chunk" is what one lane moves per access: VB bytes (16, 8 or 4: a
+// global_load/store_dwordx4, dwordx2 or dword) or, with VB == 0, one element
+// (for bases or row lengths that no wider access divides).
 // NT selects the nontemporal (streaming) cache policy for data that is touched
 // exactly once; gamma, reused by every row, is always loaded normally.
-template <typename T>
-struct Chunk<T, true> {
-  static constexpr int V = DT<T>::V;
-  using raw_t = uint4;
+template <typename T, int VB>
+struct Chunk {
+  static_assert(VB == 4 || VB == 8 || VB == 16, "vector chunks are 4, 8 or 16 bytes");
+  static constexpr int W = VB / 4;
+  static constexpr int V = W * DT<T>::PER_WORD;
+  using WS = Words<W>;
+  using raw_t = typename WS::type;
   template <bool NT = false>
   __device__ static raw_t load(const void* base, int64_t chunk) {
-    const u32x4* p = reinterpret_cast<const u32x4*>(base) + chunk;
-    u32x4 v;
-    if constexpr (NT) v = __builtin_nontemporal_load(p); else v = *p;
-    return make_uint4(v.x, v.y, v.z, v.w);
+    const raw_t* p = reinterpret_cast<const raw_t*>(base) + chunk;
+    if constexpr (NT) return __builtin_nontemporal_load(p); else return *p;
   }
   template <bool NT = false>
   __device__ static void store(void* base, int64_t chunk, raw_t v) {
-    u32x4* p = reinterpret_cast<u32x4*>(base) + chunk;
-    const u32x4 w = {v.x, v.y, v.z, v.w};
-    if constexpr (NT) __builtin_nontemporal_store(w, p); else *p = w;
+    raw_t* p = reinterpret_cast<raw_t*>(base) + chunk;
+    if constexpr (NT) __builtin_nontemporal_store(v, p); else *p = v;
   }
-  __device__ static void unpack(const raw_t& r, float (&f)[V]) { DT<T>::unpack(r, f); }
-  __device__ static raw_t pack(const float (&f)[V]) { return DT<T>::pack(f); }
+  __device__ static void unpack(const raw_t& r, float (&f)[V]) {
+#pragma unroll
+    for (int w = 0; w < W; ++w) DT<T>::unpack_word(WS::get(r, w), f + w * DT<T>::PER_WORD);
+  }
+  __device__ static raw_t pack(const float (&f)[V]) {
+    raw_t r;
+#pragma unroll
+    for (int w = 0; w < W; ++w) WS::set(r, w, DT<T>::pack_word(f + w * DT<T>::PER_WORD));
+    return r;
+  }
 };
 
 template <typename T>
-struct Chunk<T, false> {
+struct Chunk<T, 0> {
   static constexpr int V = 1;
   using raw_t = typename DT<T>::scalar_t;
   template <bool NT = false>
@@ -226,7 +236,8 @@ __device__ __forceinline__ float row_scale(float ss, int hidden, float eps) {
 // NT: streaming (nontemporal) loads and stores for the row data.
 template <typename T, int TPR, int NPT, int WGS, int KC, bool NT>
 __global__ __launch_bounds__(WGS) void row_vgpr_kernel(RowArgs a) {
-  using CK = Chunk<T, true>;
+  using CK = Chunk<T, 16>;
+  using raw_t = typename CK::raw_t;
   constexpr int V = CK::V;
   constexpr int RPW = WGS / TPR;                // rows per workgroup
   constexpr int WPR = TPR > 64 ? TPR / 64 : 1;  // waves per row
@@ -262,7 +273,7 @@ __global__ __launch_bounds__(WGS) void row_vgpr_kernel(RowArgs a) {
     float v[NPT][V];
 
     if constexpr (KC == 0) {
-      uint4 raw[NPT];
+      raw_t raw[NPT];
 #pragma unroll
       for (int i = 0; i < NPT; ++i) {
         const int c = tr + i * TPR;
@@ -280,8 +291,8 @@ __global__ __launch_bounds__(WGS) void row_vgpr_kernel(RowArgs a) {
       }
     } else {
       constexpr int NB = KC > 0 ? KC : 1;  // partial buffers loaded up front
-      uint4 raw[NB][NPT];
-      uint4 rres[NPT];
+      raw_t raw[NB][NPT];
+      raw_t rres[NPT];
 #pragma unroll
       for (int i = 0; i < NPT; ++i) {
         const int c = tr + i * TPR;
@@ -309,7 +320,7 @@ __global__ __launch_bounds__(WGS) void row_vgpr_kernel(RowArgs a) {
       if constexpr (KC < 0) {
         // runtime K: remaining partials one at a time, in order
         for (int q = 1; q < a.k; ++q) {
-          uint4 rq[NPT];
+          raw_t rq[NPT];
 #pragma unroll
           for (int i = 0; i < NPT; ++i) {
             const int c = tr + i * TPR;
@@ -335,7 +346,7 @@ __global__ __launch_bounds__(WGS) void row_vgpr_kernel(RowArgs a) {
           CK::unpack(rres[i], t);
 #pragma unroll
           for (int e = 0; e < V; ++e) acc[i][e] += t[e];  // residual added last
-          const uint4 rn = CK::pack(acc[i]);             // round once to dtype
+          const raw_t rn = CK::pack(acc[i]);             // round once to dtype
           CK::template store<NT>(a.residual, base + c, rn);
           CK::unpack(rn, v[i]);                          // normalise the stored row
         } else {
@@ -383,16 +394,17 @@ __global__ __launch_bounds__(WGS) void row_vgpr_kernel(RowArgs a) {
 }
 
 // ---- kernel 2: streaming two-pass row (any length) -------------------------
-// One row per workgroup of WGS threads.  Pass 1 reads the inputs chunk by
-// chunk (UNR chunks in flight per thread), writes the residual, accumulates
-// the sum of squares and keeps the rounded row: in LDS when LDS_STAGE, else
-// pass 2 re-reads what this same thread wrote (fused) or read (plain) --
-// a thread only ever touches its own chunks, so no barrier guards the stage.
+// One row per workgroup of WGS threads, in VB-byte chunks (0: one element).
+// Pass 1 reads the inputs chunk by chunk (UNR chunks in flight per thread),
+// writes the residual, accumulates the sum of squares and keeps the rounded
+// row: in LDS when LDS_STAGE, else pass 2 re-reads what this same thread
+// wrote (fused) or read (plain) -- a thread only ever touches its own chunks,
+// so no barrier guards the stage.
 // NT: streaming loads/stores for data touched once (never for a residual
 // that pass 2 reads back from memory).
-template <typename T, bool VEC, int WGS, bool LDS_STAGE, int KC, int UNR, bool NT>
+template <typename T, int VB, int WGS, bool LDS_STAGE, int KC, int UNR, bool NT>
 __global__ __launch_bounds__(WGS) void row_stream_kernel(RowArgs a) {
-  using CK = Chunk<T, VEC>;
+  using CK = Chunk<T, VB>;
   using raw_t = typename CK::raw_t;
   constexpr int V = CK::V;
   constexpr int NW = WGS / 64;

@@ -11,7 +11,16 @@
 
 namespace rmsn {
 
-inline void add_variant(std::vector<Variant>& v, int dtype, const char* dname, int kind, int vec,
+inline const char* width_name(int vb) {
+  switch (vb) {
+    case 16: return "vec";
+    case 8: return "v8";
+    case 4: return "v4";
+    default: return "elem";
+  }
+}
+
+inline void add_variant(std::vector<Variant>& v, int dtype, const char* dname, int kind, int vb,
                         int tpr, int npt, int wgs, int kc, int lds, int unr, int nt,
                         const void* fn) {
   Variant d{};
@@ -20,11 +29,11 @@ inline void add_variant(std::vector<Variant>& v, int dtype, const char* dname, i
              kc, nt ? ",nt" : "");
   else
     snprintf(d.name, sizeof(d.name), "stream<%s,%s,wg=%d,%s,k=%d,unr=%d%s>", dname,
-             vec ? "vec" : "elem", wgs, lds ? "lds" : "reread", kc, unr, nt ? ",nt" : "");
+             width_name(vb), wgs, lds ? "lds" : "reread", kc, unr, nt ? ",nt" : "");
   d.nt = nt;
   d.dtype = dtype;
   d.kind = kind;
-  d.vec = vec;
+  d.vb = vb;
   d.tpr = tpr;
   d.npt = npt;
   d.wgs = wgs;
@@ -39,17 +48,18 @@ template <typename T>
 std::vector<Variant> build_table(int dtype, const char* dname) {
   std::vector<Variant> v;
 #define RMSN_ADD_VGPR_K(KC, TPR, NPT, WGS, NT)                                        \
-  add_variant(v, dtype, dname, kVgpr, 1, TPR, NPT, WGS, KC, 0, 0, NT ? 1 : 0,         \
+  add_variant(v, dtype, dname, kVgpr, 16, TPR, NPT, WGS, KC, 0, 0, NT ? 1 : 0,        \
               reinterpret_cast<const void*>(&row_vgpr_kernel<T, TPR, NPT, WGS, KC, NT>));
 #define RMSN_ADD_VGPR(TPR, NPT, WGS, NT) RMSN_KCS(RMSN_ADD_VGPR_K, TPR, NPT, WGS, NT)
   RMSN_VGPR_SHAPES(RMSN_ADD_VGPR)
-#define RMSN_ADD_STREAM_K(KC, VEC, WGS, LDS, NT, UNR)                                 \
-  add_variant(v, dtype, dname, kStream, VEC ? 1 : 0, WGS, 0, WGS, KC, LDS ? 1 : 0,    \
-              UNR, NT ? 1 : 0,                                                        \
-              reinterpret_cast<const void*>(                                         \
-                  &row_stream_kernel<T, VEC, WGS, LDS, KC, UNR, NT>));
-#define RMSN_ADD_STREAM(VEC, WGS, LDS, NT, UNR) \
-  RMSN_STREAM_KCS(RMSN_ADD_STREAM_K, VEC, WGS, LDS, NT, UNR)
+#define RMSN_ADD_STREAM_K(KC, VB, WGS, LDS, NT, UNR)                                  \
+  if constexpr (VB == 0 || VB > (int)sizeof(typename DT<T>::scalar_t))                 \
+    add_variant(v, dtype, dname, kStream, VB, WGS, 0, WGS, KC, LDS ? 1 : 0, UNR,        \
+                NT ? 1 : 0,                                                             \
+                reinterpret_cast<const void*>(                                         \
+                    &row_stream_kernel<T, VB, WGS, LDS, KC, UNR, NT>));
+#define RMSN_ADD_STREAM(VB, WGS, LDS, NT, UNR) \
+  RMSN_STREAM_KCS(RMSN_ADD_STREAM_K, VB, WGS, LDS, NT, UNR)
   RMSN_STREAM_SHAPES(RMSN_ADD_STREAM)
 #undef RMSN_ADD_VGPR_K
 #undef RMSN_ADD_VGPR

@@ -16,7 +16,7 @@ struct Variant {
   char name[96];
   int dtype;      // 0 f32, 1 f16, 2 bf16
   int kind;       // kVgpr or kStream
-  int vec;        // 1: 16-byte chunks, 0: element-wise
+  int vb;         // bytes per chunk: 16, 8 or 4; 0 = one element per chunk
   int tpr;        // threads per row
   int npt;        // chunks per thread held in registers (vgpr)
   int wgs;        // threads per workgroup
@@ -42,16 +42,22 @@ struct Variant {
 // Partial counts compiled as constants (others use the runtime-K kernel).
 #define RMSN_KCS(X, ...) X(0, __VA_ARGS__) X(1, __VA_ARGS__) X(8, __VA_ARGS__) X(-1, __VA_ARGS__)
 
-// Shapes of the streaming kernel: (16-byte chunks?, threads/WG, LDS stage?,
-// nontemporal, chunks in flight per thread).  LDS-staged variants stream;
-// re-reading ones keep the residual cacheable for the second pass.
-#define RMSN_STREAM_SHAPES(X)                                                                   \
-  X(true, 256, true, true, 2) X(true, 512, true, true, 2) X(true, 1024, true, true, 2)          \
-  X(true, 256, true, true, 4) X(true, 512, true, true, 4) X(true, 1024, true, true, 4)          \
-  X(true, 256, false, false, 2) X(true, 512, false, false, 2) X(true, 1024, false, false, 2)    \
-  X(false, 256, true, true, 4) X(false, 512, true, true, 4) X(false, 1024, true, true, 4)       \
-  X(false, 256, false, false, 4) X(false, 512, false, false, 4) X(false, 1024, false, false, 4) \
-  X(true, 512, true, false, 2)
+// Shapes of the streaming kernel: (bytes per chunk (0: one element),
+// threads/WG, LDS stage?, nontemporal, chunks in flight per thread).
+// LDS-staged variants stream; re-reading ones keep the residual cacheable for
+// the second pass.  4-byte chunks are built for 16-bit types only (for fp32
+// they are the element-wise kernel).
+#define RMSN_STREAM_SHAPES(X)                                                             \
+  X(16, 256, true, true, 2) X(16, 512, true, true, 2) X(16, 1024, true, true, 2)          \
+  X(16, 256, true, true, 4) X(16, 512, true, true, 4) X(16, 1024, true, true, 4)          \
+  X(16, 256, false, false, 2) X(16, 512, false, false, 2) X(16, 1024, false, false, 2)    \
+  X(16, 512, true, false, 2)                                                              \
+  X(8, 256, true, true, 4) X(8, 512, true, true, 4) X(8, 1024, true, true, 4)             \
+  X(8, 256, false, false, 4) X(8, 512, false, false, 4) X(8, 1024, false, false, 4)       \
+  X(4, 256, true, true, 4) X(4, 512, true, true, 4) X(4, 1024, true, true, 4)             \
+  X(4, 256, false, false, 4) X(4, 512, false, false, 4) X(4, 1024, false, false, 4)       \
+  X(0, 256, true, true, 4) X(0, 512, true, true, 4) X(0, 1024, true, true, 4)             \
+  X(0, 256, false, false, 4) X(0, 512, false, false, 4) X(0, 1024, false, false, 4)
 
 #define RMSN_STREAM_KCS(X, ...) X(0, __VA_ARGS__) X(1, __VA_ARGS__) X(-1, __VA_ARGS__)
 

@@ -95,7 +95,13 @@ def test_plan_names_follow_the_dispatch_rule():
     assert "tpr=8," in plan(1000, 64, 1, "bf16")            # several rows per wave
     assert "tpr=64," in plan(512, 512, 0, "bf16")           # one row per wave
     assert "elem" in plan(10, 1591, 0, "bf16")              # odd row length
-    assert "elem" in plan(10, 4096, 1, "bf16", aligned=False)
+    assert "elem" in plan(10, 4096, 1, "bf16", align=2)
+    assert ",v4," in plan(10, 4096, 1, "bf16", align=4)        # 4-byte aligned bases
+    assert ",v8," in plan(10, 4096, 1, "bf16", align=8)
+    assert ",v4," in plan(10, 1594, 0, "bf16")                  # 3188-byte rows
+    assert ",v8," in plan(10, 1596, 0, "bf16")                  # 3192-byte rows
+    assert "elem" in plan(10, 1595, 0, "f32")
+    assert ",v8," in plan(10, 1594, 0, "f32")
     assert "reread" in plan(10, 100000, 1, "bf16")          # row beyond the LDS stage
     for k in range(0, 17):
         assert plan(3, 777 * 8, k, "f16")

@@ -169,7 +169,12 @@ def _parse(name):
     return kind, flags, {k: int(v) for k, v in kv.items()}
 
 
+WIDTH_BYTES = {"vec": 16, "v8": 8, "v4": 4, "elem": 0}
+
+
 def _variant_case(dtype, name):
+    """A (hidden, rows, k) the variant can run, chosen so that a narrower
+    chunk width is also the widest its row length allows."""
     kind, flags, kv = _parse(name)
     s = 4 if dtype == "f32" else 2
     V = 16 // s
@@ -181,11 +186,9 @@ def _variant_case(dtype, name):
         hidden = chunks * V
         rows = 2 * (wg // tpr) + 1
     else:
-        vec = "vec" in flags
-        lds = "lds" in flags
-        hidden = 3000 if lds else (40000 if s == 2 else 20000)
-        if not vec:
-            hidden += 1
+        vb = WIDTH_BYTES[next(f for f in flags if f in WIDTH_BYTES)]
+        base = 3000 if "lds" in flags else (40000 if s == 2 else 20000)
+        hidden = base + {16: 0, 8: 8 // s, 4: 4 // s, 0: 1}[vb]
         rows = 5
     return hidden, rows, k
 
@@ -198,7 +201,7 @@ def test_every_variant(dtype, monkeypatch):
         hidden, rows, k = _variant_case(dtype, name)
         w = I.case(dtype, rows, hidden, k, seed=i, std=0.5)
         monkeypatch.setenv("RMSNORM_VARIANT", name)
-        assert B.rmsnorm_plan(rows, hidden, k, dtype, aligned=True) == name
+        assert B.rmsnorm_plan(rows, hidden, k, dtype, align=16) == name
         check(w, I.make_inputs(w), f"variant {name}")
     monkeypatch.delenv("RMSNORM_VARIANT")
 
@@ -214,28 +217,32 @@ def test_grid_stride_loop(monkeypatch):
 
 # ---- alignment, aliasing, special values, determinism ------------------------------
 
-def test_misaligned_pointers_use_elementwise_kernel():
-    w = I.case("bf16", 33, 1592, 1, seed=77)
+@pytest.mark.parametrize("shift,width", [(1, "elem"), (2, "v4"), (4, "v8"), (8, "vec")])
+def test_misaligned_pointers_use_narrower_chunks(shift, width):
+    """Bases offset by `shift` bf16 elements from a 16-byte boundary take the
+    widest chunk the shared alignment allows."""
+    w = I.case("bf16", 33, 1592, 1, seed=77 + shift)
     d = I.make_inputs(w)
-    assert "elem" in B.rmsnorm_plan(33, 1592, 1, "bf16", aligned=False)
     n = 33 * 1592
+    align = min(16, 2 * shift)
+    plan = B.rmsnorm_plan(33, 1592, 1, "bf16", align=align)
+    assert (f",{width}," in plan) or (width == "vec" and plan.startswith("vgpr<")), plan
 
     def shifted(t):
-        buf = torch.empty(n + 8, dtype=t.dtype, device=DEV)
-        v = buf[1:1 + n].view(33, 1592)
+        buf = torch.empty(n + 16, dtype=t.dtype, device=DEV)
+        v = buf[shift:shift + n].view(33, 1592)
         v.copy_(t)
         return v
 
     ps = [shifted(p) for p in d["partials"]]
     r = shifted(d["residual"])
     out = shifted(torch.zeros_like(d["residual"]))
-    g = torch.empty(1600, dtype=torch.bfloat16, device=DEV)[3:3 + 1592]
+    g = torch.empty(1600, dtype=torch.bfloat16, device=DEV)[shift:shift + 1592]
     g.copy_(d["gamma"])
-    assert r.data_ptr() % 16 != 0
     B.add_rmsnorm_fwd(out, r, ps, g, w.eps)
     torch.cuda.synchronize()
     ref = P.run_oracle("bf16", w.eps, partials=d["partials"], residual=d["residual"], gamma=d["gamma"])
-    P.compare("bf16", out.cpu(), ref, r.cpu(), what="misaligned")
+    P.compare("bf16", out.cpu(), ref, r.cpu(), what=f"shift {shift}")
 
 
 def test_out_aliases_input():
