@@ -162,6 +162,52 @@ def stream_ceiling(w, dev: str = "cuda:0", steps: int = 60, rotate_gib: float = 
     return best
 
 
+def sweep(w, step, a, B) -> int:
+    """Time every compatible variant (the dispatcher's choice is marked).
+    With --repeat R the variants are timed round-robin R times and the
+    median is reported, so slow drifts of the clock do not favour one."""
+    import statistics
+    import torch
+    default = B.rmsnorm_plan(w.rows, w.hidden, w.k, w.dtype)
+    names = []
+    for v in B.rmsnorm_variants(w.dtype):
+        if a.variant_filter and a.variant_filter not in v:
+            continue
+        os.environ["RMSNORM_VARIANT"] = v
+        try:
+            B.rmsnorm_plan(w.rows, w.hidden, w.k, w.dtype)
+            names.append(v)
+        except B.RmsnormError:
+            pass
+    times = {v: [] for v in names}
+    try:
+        for rep in range(a.repeat):
+            for v in names:
+                os.environ["RMSNORM_VARIANT"] = v
+                for i in range(a.warmup):
+                    step(i)
+                torch.cuda.synchronize()
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for i in range(a.steps):
+                    step(i)
+                e1.record()
+                torch.cuda.synchronize()
+                us = e0.elapsed_time(e1) / a.steps * 1e3
+                times[v].append(us)
+                print(f"[sweep {rep}] {us:9.2f} us {w.algorithmic_bytes() / us / 1e3:7.0f} GB/s  {v}"
+                      f"{'  <- dispatcher' if v == default else ''}", file=sys.stderr, flush=True)
+    finally:
+        os.environ.pop("RMSNORM_VARIANT", None)
+    rows = sorted((statistics.median(t), v, t) for v, t in times.items())
+    for us, v, t in rows:
+        print(json.dumps({"workload": w.name, "variant": v, "us": round(us, 3),
+                          "gbs": round(w.algorithmic_bytes() / us / 1e3, 1),
+                          "runs_us": [round(x, 2) for x in t], "dispatcher": v == default}))
+    return 0
+
+
 def copy_calibration() -> None:
     """A plain device copy of known size (1 GiB), for scaling the HBM byte
     counters read by rocprofv3 --pmc."""
@@ -183,6 +229,11 @@ def main() -> int:
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--sweep", action="store_true",
+                    help="time every compiled kernel variant that can run the workload "
+                         "(forced through RMSNORM_VARIANT) and print one line per variant")
+    ap.add_argument("--repeat", type=int, default=1, help="sweep rounds (median reported)")
+    ap.add_argument("--variant-filter", default="", help="sweep only variants containing this")
     ap.add_argument("--no-ceiling", action="store_true",
                     help="skip the streaming-ceiling probe")
     ap.add_argument("--rotate-bytes", type=float, default=1.0,
@@ -226,6 +277,9 @@ def main() -> int:
             B.add_rmsnorm_fwd(s["out"], s["residual"], s["partials"], s["gamma"], w.eps)
         else:
             B.rmsnorm_fwd(s["out"], s["x"], s["gamma"], w.eps)
+
+    if a.sweep:
+        return sweep(w, step, a, B)
 
     for i in range(a.warmup):
         step(i)

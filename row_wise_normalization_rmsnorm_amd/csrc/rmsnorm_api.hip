@@ -152,12 +152,18 @@ int choose(int dtype, int64_t hidden, int k, int align, Plan* plan) {
     // Streaming two-pass, LDS-staged while the row fits the stage budget.
     // Fused calls use the runtime-K form, which sums the partials one at a
     // time with few registers (measured faster than holding all K+1 chunk
-    // sets in registers at K = 8).
-    const int64_t C = vb ? hidden * s / vb : hidden;
+    // sets in registers at K = 8).  The LDS-staged form moves 8-byte chunks,
+    // four per thread, with just enough threads to put the whole row in
+    // flight in one step: measured 3% faster than 16-byte chunks at K = 8
+    // and 2% on 16384-wide rows.
     const bool lds = hidden * s <= kLdsStageMax;
-    const int wgs = C <= 1024 ? (lds && k >= 2 ? 512 : 256) : C <= 2048 ? 512 : 1024;
-    const int unr = vb == 16 ? (lds && k < 2 ? 4 : 2) : 4;
-    v = find(dtype, rmsn::kStream, vb, wgs, unr, wgs, k == 0 ? 0 : -1, lds ? 1 : 0, lds ? 1 : 0);
+    const int svb = (lds && vb == 16) ? 8 : vb;
+    const int64_t C = svb ? hidden * s / svb : hidden;
+    const int unr = svb == 16 ? 2 : 4;
+    int wgs = 256;
+    while (wgs < 1024 && (int64_t)wgs * unr < C) wgs *= 2;
+    v = find(dtype, rmsn::kStream, svb, wgs, unr, wgs, k == 0 ? 0 : -1, lds ? 1 : 0,
+             lds ? 1 : 0);
   }
   if (!v) return fail(RMSN_ERR_SHAPE, "no kernel variant for hidden=%lld k=%d", (long long)hidden, k);
   plan->v = v;

@@ -51,7 +51,8 @@ struct Variant {
   X(16, 256, true, true, 2) X(16, 512, true, true, 2) X(16, 1024, true, true, 2)          \
   X(16, 256, true, true, 4) X(16, 512, true, true, 4) X(16, 1024, true, true, 4)          \
   X(16, 256, false, false, 2) X(16, 512, false, false, 2) X(16, 1024, false, false, 2)    \
-  X(16, 512, true, false, 2)                                                              \
+  X(16, 512, true, false, 2) X(16, 256, true, true, 1) X(16, 512, true, true, 1)         \
+  X(8, 256, true, true, 2) X(8, 512, true, true, 2) X(8, 1024, true, true, 2)             \
   X(8, 256, true, true, 4) X(8, 512, true, true, 4) X(8, 1024, true, true, 4)             \
   X(8, 256, false, false, 4) X(8, 512, false, false, 4) X(8, 1024, false, false, 4)       \
   X(4, 256, true, true, 4) X(4, 512, true, true, 4) X(4, 1024, true, true, 4)             \

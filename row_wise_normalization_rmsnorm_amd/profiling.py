@@ -13,7 +13,11 @@ bandwidth, HBM bytes per launch, with the commands) and
 kernel sources so that a stale figure is never reported).
 
 Usage: python -m row_wise_normalization_rmsnorm_amd.profiling --workload W
-         --trace DIR --fetch DIR --write DIR --copy-fetch DIR --copy-write DIR
+         --plan NAME --symbol SUBSTR --trace DIR --fetch DIR --write DIR
+         --copy-fetch DIR --copy-write DIR [--bench-json FILE]
+       python -m row_wise_normalization_rmsnorm_amd.profiling sweep --workload W FILE.jsonl
+       python -m row_wise_normalization_rmsnorm_amd.profiling counters --workload W
+         --plan NAME --symbol SUBSTR DIR
 """
 from __future__ import annotations
 
@@ -67,7 +71,67 @@ def short_name(plan: str) -> str:
     return re.sub(r"[^A-Za-z0-9]+", "_", plan).strip("_")
 
 
+def sweep_summary(argv) -> int:
+    """profiles/sweep__<workload>.md from the JSON lines of
+    ``bench.py --workload W --sweep --repeat R``."""
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--workload", required=True)
+    ap.add_argument("--command", default=None)
+    ap.add_argument("jsonl")
+    a = ap.parse_args(argv)
+    rows = [json.loads(l) for l in open(a.jsonl) if l.startswith("{")]
+    rows.sort(key=lambda r: r["us"])
+    md = os.path.join(ROOT, "profiles", f"sweep__{a.workload}.md")
+    with open(md, "w") as f:
+        f.write(f"# Every compiled variant on {a.workload}\n\n")
+        cmd = a.command or (f"python bench.py --workload {a.workload} --sweep --repeat 3")
+        f.write(f"Command: `{cmd}` (HIP events over the timed launches of each variant, forced "
+                "through RMSNORM_VARIANT; variants timed round-robin, median of the rounds; "
+                "buffers rotated as in the benchmark).\n\n")
+        f.write("| rank | variant | median us | GB/s | rounds (us) | dispatcher |\n|---|---|---|---|---|---|\n")
+        for i, r in enumerate(rows):
+            if i < 15 or r["dispatcher"]:
+                f.write(f"| {i + 1} | `{r['variant']}` | {r['us']:.2f} | {r['gbs']:.0f} | "
+                        f"{', '.join(f'{x:.2f}' for x in r['runs_us'])} | "
+                        f"{'yes' if r['dispatcher'] else ''} |\n")
+        f.write(f"\n{len(rows)} variants can run this workload; the 15 fastest and the "
+                "dispatcher's choice are listed.\n")
+    print(md)
+    return 0
+
+
+def counters_summary(argv) -> int:
+    """profiles/counters_<kernel>__<workload>.md from a rocprofv3 --pmc run of
+    SQ_LDS_BANK_CONFLICT, SQ_INSTS_LDS, SQ_WAVES, SQ_WAVE_CYCLES, SQ_BUSY_CYCLES."""
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--workload", required=True)
+    ap.add_argument("--plan", required=True)
+    ap.add_argument("--symbol", required=True)
+    ap.add_argument("dir")
+    a = ap.parse_args(argv)
+    names = ["SQ_LDS_BANK_CONFLICT", "SQ_INSTS_LDS", "SQ_WAVES", "SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES"]
+    vals = {n: counter(a.dir, n, a.symbol) for n in names}
+    md = os.path.join(ROOT, "profiles", f"counters_{short_name(a.plan)}__{a.workload}.md")
+    with open(md, "w") as f:
+        f.write(f"# LDS and wave counters: {a.plan} on {a.workload}\n\n")
+        f.write("Command: `rocprofv3 --pmc " + " ".join(names) + " --output-format csv -d <dir> -o run "
+                f"-- python bench.py --workload {a.workload} --steps 5 --warmup 1 --no-cpu-baseline "
+                "--no-ceiling`\n\n| counter | per dispatch (median) | dispatches |\n|---|---|---|\n")
+        for n in names:
+            f.write(f"| {n} | {vals[n][0]:,.0f} | {vals[n][1]} |\n")
+        lds, conf, waves = vals["SQ_INSTS_LDS"][0], vals["SQ_LDS_BANK_CONFLICT"][0], vals["SQ_WAVES"][0]
+        f.write(f"\nLDS instructions per wave: {lds / waves:.1f}; bank-conflict cycles per wave: "
+                f"{conf / waves:.1f} ({conf / max(lds, 1):.2f} per LDS instruction).\n")
+    print(md)
+    return 0
+
+
 def main() -> int:
+    import sys
+    if len(sys.argv) > 1 and sys.argv[1] == "sweep":
+        return sweep_summary(sys.argv[2:])
+    if len(sys.argv) > 1 and sys.argv[1] == "counters":
+        return counters_summary(sys.argv[2:])
     ap = argparse.ArgumentParser()
     ap.add_argument("--workload", required=True)
     ap.add_argument("--plan", required=True, help="kernel variant name (bench.py prints it)")

@@ -87,10 +87,10 @@ def test_error_codes():
 def test_plan_names_follow_the_dispatch_rule():
     plan = B.rmsnorm_plan
     assert plan(8192, 4096, 1, "bf16").startswith("vgpr<bf16")
-    assert plan(4096, 8192, 8, "bf16").startswith("stream<bf16,vec")   # K >= 2, long rows
+    assert plan(4096, 8192, 8, "bf16").startswith("stream<bf16,v8")    # K >= 2, long rows
     assert plan(4096, 1024, 8, "bf16").startswith("vgpr<bf16")
     assert plan(512, 2048, 0, "f32").startswith("vgpr<f32")
-    assert plan(65536, 16384, 1, "bf16").startswith("stream<bf16,vec")
+    assert plan(65536, 16384, 1, "bf16").startswith("stream<bf16,v8")
     assert "lds" in plan(65536, 16384, 1, "bf16")
     assert "tpr=8," in plan(1000, 64, 1, "bf16")            # several rows per wave
     assert "tpr=64," in plan(512, 512, 0, "bf16")           # one row per wave

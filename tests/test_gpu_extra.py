@@ -138,3 +138,43 @@ def test_offsets_beyond_4gib():
     del want
     ref = P.run_oracle("bf16", w.eps, partials=[p_s], residual=r_s, gamma=g.cpu())
     P.compare("bf16", out[rows].cpu(), ref, r[rows].cpu(), what=">4 GiB offsets")
+
+
+CANARY = 4096  # elements of guard on each side of every tensor
+
+
+def _guarded(t):
+    """A device copy of t placed between two guard regions filled with a
+    pattern; returns (view, whole buffer)."""
+    n = t.numel()
+    buf = torch.empty(n + 2 * CANARY, dtype=t.dtype, device=DEV)
+    buf.view(torch.int16 if t.element_size() == 2 else torch.int32).fill_(0x5A5A)
+    v = buf[CANARY:CANARY + n].view(t.shape)
+    v.copy_(t)
+    return v, buf
+
+
+@pytest.mark.parametrize("dtype,hidden,k", [("bf16", 4096, 1), ("bf16", 1591, 0), ("f32", 333, 3),
+                                            ("f16", 16384, 1), ("bf16", 70000, 2), ("bf16", 24, 8),
+                                            ("f32", 8192, 0), ("bf16", 1594, 1)])
+def test_no_writes_outside_the_tensors(dtype, hidden, k):
+    """Guard regions around out and the residual stay untouched (tails, odd
+    lengths, every kernel family)."""
+    rows = 13
+    w = I.case(dtype, rows, hidden, k, seed=hidden + k)
+    d = I.make_inputs(w)
+    g = d["gamma"].to(DEV)
+    out, obuf = _guarded(torch.zeros((rows, hidden), dtype=d["gamma"].dtype))
+    guards = []
+    if k:
+        ps = [p.to(DEV) for p in d["partials"]]
+        r, rbuf = _guarded(d["residual"])
+        guards.append(rbuf)
+        B.add_rmsnorm_fwd(out, r, ps, g, w.eps)
+    else:
+        B.rmsnorm_fwd(out, d["x"].to(DEV), g, w.eps)
+    guards.append(obuf)
+    torch.cuda.synchronize()
+    for buf in guards:
+        iv = buf.view(torch.int16 if buf.element_size() == 2 else torch.int32)
+        assert torch.all(iv[:CANARY] == 0x5A5A) and torch.all(iv[-CANARY:] == 0x5A5A)

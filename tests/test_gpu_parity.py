@@ -37,17 +37,19 @@ def say(*a):
 
 
 def run_case(w, d, *, alias_out=False, sync=True):
-    """Run the HIP path on copies of the CPU inputs ``d``; return CPU results."""
+    """Run the HIP path on copies of the CPU inputs ``d``; return CPU results.
+    Outputs start poisoned with NaN, so an element the kernel fails to write
+    shows up as a NaN mismatch."""
     g = d["gamma"].to(DEV)
     if w.fused:
         ps = [p.to(DEV) for p in d["partials"]]
         r = d["residual"].to(DEV)
-        out = ps[0] if alias_out else torch.empty_like(r)
+        out = ps[0] if alias_out else torch.full_like(r, float("nan"))
         B.add_rmsnorm_fwd(out, r, ps, g, w.eps)
         torch.cuda.synchronize()
         return out.cpu(), r.cpu()
     x = d["x"].to(DEV)
-    out = x if alias_out else torch.empty_like(x)
+    out = x if alias_out else torch.full_like(x, float("nan"))
     B.rmsnorm_fwd(out, x, g, w.eps)
     torch.cuda.synchronize()
     return out.cpu(), None

@@ -393,3 +393,51 @@ def test_oracle_nan_propagates():
     g = to_storage_vals(np.ones(3), "bf16")
     out, _ = oracle.rmsnorm(x, g, 1e-6, "bf16")
     assert np.all(np.isnan(ind.decode_np(out, "bf16")))
+
+
+# ---- property-based: the brute force on rows hypothesis chooses -------------
+
+from hypothesis import given, settings, strategies as st  # noqa: E402
+
+
+@settings(max_examples=150, deadline=None)
+@given(dtype=st.sampled_from(DTYPES),
+       vals=st.lists(st.floats(min_value=-1e6, max_value=1e6, allow_nan=False, width=32),
+                     min_size=1, max_size=9),
+       eps=st.sampled_from([1e-6, 1e-5, 0.25]),
+       k=st.integers(min_value=0, max_value=3),
+       seed=st.integers(min_value=0, max_value=2 ** 31))
+def test_brute_force_property(dtype, vals, eps, k, seed):
+    """One row of hypothesis-chosen values (rounded to dtype), plain or with k
+    partials derived from it: the oracle equals exact arithmetic, the
+    residual bit for bit and y up to a value on a rounding tie."""
+    rng = np.random.default_rng(seed)
+    H = len(vals)
+    with np.errstate(over="ignore"):
+        x = np.asarray(vals, dtype=np.float32)
+        if dtype == "f16":
+            x = np.clip(x, -6e4, 6e4)
+        xs = torch.from_numpy(x)
+        store = (lambda t: t.numpy()) if dtype == "f32" else \
+            (lambda t: t.to(TORCH[dtype]).view(torch.int16).numpy().view(np.uint16))
+        g = store(torch.from_numpy(rng.uniform(0.5, 1.5, H).astype(np.float32)))
+        row = store(xs).reshape(1, H)
+    gv = ind.decode_np(g, dtype)
+    if k == 0:
+        out, _ = oracle.rmsnorm(row, g, eps, dtype)
+        v = ind.decode_np(row, dtype)[0]
+    else:
+        ps = [store(torch.from_numpy((rng.standard_normal(H) * 0.3).astype(np.float32))).reshape(1, H)
+              for _ in range(k)]
+        out, rnew, _ = oracle.add_rmsnorm(ps, row, g, eps, dtype)
+        pv = [ind.decode_np(p, dtype)[0] for p in ps]
+        rv = ind.decode_np(row, dtype)[0]
+        v = np.empty(H)
+        for j in range(H):
+            acc = ind.fused_residual_f32([p[j] for p in pv] + [rv[j]])
+            want, _ = ind.round_signed(Fraction(float(acc)), float(acc), dtype)
+            assert int(ind.storage_bits(rnew, dtype)[0, j]) == ind.bits(want, dtype)
+            v[j] = want
+    for j, (want, tie) in enumerate(ind.brute_force_row(v, gv, eps, dtype)):
+        if int(ind.storage_bits(out, dtype)[0, j]) != ind.bits(want, dtype):
+            assert tie < Fraction(1, 10 ** 9)
