@@ -201,31 +201,94 @@ __device__ __forceinline__ float dpp_get(float v) {
   return as_f((uint32_t)__builtin_amdgcn_update_dpp(0, (int)as_u(v), CTRL, 0xF, 0xF, false));
 }
 
-// Sum over aligned groups of G lanes (G in {1,2,4,8,16,32}); every lane of the
-// group receives the group's sum.  Each step adds a value and its mirror
-// partner, so partners compute a+b and b+a: all lanes agree bitwise.
-template <int G>
-__device__ __forceinline__ float group_sum(float v) {
-  if constexpr (G >= 2) v += dpp_get<kDppQuadXor1>(v);
-  if constexpr (G >= 4) v += dpp_get<kDppQuadXor2>(v);
-  if constexpr (G >= 8) v += dpp_get<kDppRowHalfMirror>(v);
-  if constexpr (G >= 16) v += dpp_get<kDppRowMirror>(v);
-  if constexpr (G >= 32) v += as_f((uint32_t)__builtin_amdgcn_ds_swizzle((int)as_u(v), kSwizzleSwap16));
+template <bool MAX>
+__device__ __forceinline__ float combine(float x, float y) {
+  if constexpr (MAX) return fmaxf(x, y); else return x + y;
+}
+
+// Sum (or max) over aligned groups of G lanes (G in {1,2,4,8,16,32}); every
+// lane of the group receives the result.  Each step combines a value with
+// its mirror partner, so partners compute a+b and b+a: all lanes agree
+// bitwise.
+template <int G, bool MAX = false>
+__device__ __forceinline__ float group_reduce(float v) {
+  if constexpr (G >= 2) v = combine<MAX>(v, dpp_get<kDppQuadXor1>(v));
+  if constexpr (G >= 4) v = combine<MAX>(v, dpp_get<kDppQuadXor2>(v));
+  if constexpr (G >= 8) v = combine<MAX>(v, dpp_get<kDppRowHalfMirror>(v));
+  if constexpr (G >= 16) v = combine<MAX>(v, dpp_get<kDppRowMirror>(v));
+  if constexpr (G >= 32)
+    v = combine<MAX>(v, as_f((uint32_t)__builtin_amdgcn_ds_swizzle((int)as_u(v), kSwizzleSwap16)));
   return v;
 }
 
-// Sum over the full wave, returned as a wave-uniform value.
-__device__ __forceinline__ float wave_sum(float v) {
-  v = group_sum<32>(v);
+// Sum (or max) over the full wave, returned as a wave-uniform value.
+template <bool MAX = false>
+__device__ __forceinline__ float wave_reduce(float v) {
+  v = group_reduce<32, MAX>(v);
   const float lo = as_f((uint32_t)__builtin_amdgcn_readlane((int)as_u(v), 0));
   const float hi = as_f((uint32_t)__builtin_amdgcn_readlane((int)as_u(v), 32));
-  return lo + hi;
+  return combine<MAX>(lo, hi);
+}
+
+// Reduction over the TPR threads of a row: within a lane group (TPR < 64),
+// within a wave (TPR == 64), or across the WPR waves of a row through the
+// double-buffered LDS array red[2][RPW * WPR] (one barrier).  Every wave
+// combines the wave results in the same order, so all agree bitwise.  A
+// buffer is rewritten only after a later reduction's barrier, which no wave
+// passes before every wave has read it.
+template <int TPR, int WPR, int N, bool MAX>
+__device__ __forceinline__ float row_reduce(float x, float (&red)[2][N], int& parity, int slot,
+                                            int tr) {
+  if constexpr (TPR < 64) {
+    return group_reduce<TPR, MAX>(x);
+  } else if constexpr (WPR == 1) {
+    return wave_reduce<MAX>(x);
+  } else {
+    const float ws = wave_reduce<MAX>(x);
+    if ((tr & 63) == 0) red[parity][slot * WPR + tr / 64] = ws;
+    __syncthreads();
+    float t = red[parity][slot * WPR];
+#pragma unroll
+    for (int j = 1; j < WPR; ++j) t = combine<MAX>(t, red[parity][slot * WPR + j]);
+    parity ^= 1;
+    return t;
+  }
 }
 
 // ---- per-row scale ---------------------------------------------------------
 // inv = rsqrt(sum/hidden + eps): eps inside the root, after the mean.
 __device__ __forceinline__ float row_scale(float ss, int hidden, float eps) {
   return rsqrtf(ss / (float)hidden + eps);
+}
+
+// The fp32 sum of squares leaves binary32's useful range for rows of huge
+// values (it overflows to +inf) and for rows of tiny values (their squares
+// underflow).  Such a row is rescaled by an exact power of two, 2^-e with
+// 2^e just above its largest magnitude, and normalised as
+//   y = ((x * 2^-e) * rsqrt(sum((x * 2^-e)^2)/hidden + eps * 2^-2e)) * gamma,
+// which is the same quantity.  A row of zeros with eps > 0 is exact as is.
+__device__ __forceinline__ bool needs_rescale(float tot, float eps) {
+  return tot == __builtin_inff() || (tot < 0x1p-60f && (tot > 0.0f || eps == 0.0f));
+}
+
+// Having the row's largest magnitude m and its rescaled sum of squares tot2,
+// return true and the rescaled (inv, shift) if the rescaled form applies; a
+// row holding inf, a row of zeros, or one whose eps * 2^-2e overflows (eps
+// then dominates and the plain form is accurate) keeps the plain form.
+__device__ __forceinline__ bool rescaled_scale(float m, float tot2, int e, int hidden, float eps,
+                                               float& inv, int& shift) {
+  if (!(m > 0.0f) || m == __builtin_inff()) return false;
+  const float eps2 = ldexpf(eps, -2 * e);
+  if (eps2 == __builtin_inff()) return false;
+  inv = rsqrtf(tot2 / (float)hidden + eps2);
+  shift = -e;
+  return true;
+}
+
+__device__ __forceinline__ int exponent_above(float m) {
+  int e = 0;
+  (void)frexpf(m, &e);  // m = f * 2^e, f in [0.5, 1)
+  return e;
 }
 
 // ---- kernel 1: the row held in VGPRs ---------------------------------------
@@ -243,7 +306,8 @@ __global__ __launch_bounds__(WGS) void row_vgpr_kernel(RowArgs a) {
   constexpr int WPR = TPR > 64 ? TPR / 64 : 1;  // waves per row
   static_assert(TPR <= WGS && WGS % TPR == 0, "a row must fit in one workgroup");
   static_assert(TPR < 64 ? (64 % TPR == 0) : (TPR % 64 == 0), "TPR must tile waves");
-  __shared__ float red[2][WPR > 1 ? RPW * WPR : 1];
+  constexpr int kRed = WPR > 1 ? RPW * WPR : 1;
+  __shared__ float red[2][kRed];
 
   const int tid = threadIdx.x;
   const int tr = tid % TPR;  // thread index within its row
@@ -363,30 +427,66 @@ __global__ __launch_bounds__(WGS) void row_vgpr_kernel(RowArgs a) {
 #pragma unroll
       for (int e = 0; e < V; ++e) ss = __builtin_fmaf(v[i][e], v[i][e], ss);
 
-    float tot;
-    if constexpr (TPR < 64) {
-      tot = group_sum<TPR>(ss);
-    } else if constexpr (WPR == 1) {
-      tot = wave_sum(ss);
-    } else {
-      const float ws = wave_sum(ss);
-      const int w = tr / 64;  // wave index within the row
-      if ((tid & 63) == 0) red[parity][slot * WPR + w] = ws;
-      __syncthreads();
-      tot = 0.0f;
+    const float tot = row_reduce<TPR, WPR, kRed, false>(ss, red, parity, slot, tr);
+    float inv = row_scale(tot, a.hidden, a.eps);
+    int shift = 0;
+
+    // Rare: rescale rows whose sum of squares left fp32's range.  The
+    // decision is uniform over everything that takes part in the extra
+    // reductions: a lane group or a wave, or (several waves per row) the
+    // whole workgroup, which then rescales if any of its rows needs it.
+    bool wide = row_ok && needs_rescale(tot, a.eps);
+    bool take = wide;
+    if constexpr (WPR > 1 && RPW > 1) {
+      const int used = parity ^ 1;  // the buffer the sum just went through
+      take = false;
 #pragma unroll
-      for (int j = 0; j < WPR; ++j) tot += red[parity][slot * WPR + j];
-      parity ^= 1;
+      for (int r = 0; r < RPW; ++r) {
+        float t = red[used][r * WPR];
+#pragma unroll
+        for (int j = 1; j < WPR; ++j) t += red[used][r * WPR + j];
+        take = take || (row0 + r < a.rows && needs_rescale(t, a.eps));
+      }
+    }
+    if (take) {
+      float m = 0.0f;
+#pragma unroll
+      for (int i = 0; i < NPT; ++i)
+#pragma unroll
+        for (int e = 0; e < V; ++e) m = fmaxf(m, fabsf(v[i][e]));
+      m = row_reduce<TPR, WPR, kRed, true>(m, red, parity, slot, tr);
+      const int ex = exponent_above(m);
+      float ss2 = 0.0f;
+#pragma unroll
+      for (int i = 0; i < NPT; ++i)
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+          const float t = ldexpf(v[i][e], -ex);
+          ss2 = __builtin_fmaf(t, t, ss2);
+        }
+      const float tot2 = row_reduce<TPR, WPR, kRed, false>(ss2, red, parity, slot, tr);
+      if (wide) {
+        float inv2;
+        int sh2;
+        if (rescaled_scale(m, tot2, ex, a.hidden, a.eps, inv2, sh2)) {
+          inv = inv2;
+          shift = sh2;
+        }
+      }
     }
 
-    const float inv = row_scale(tot, a.hidden, a.eps);
 #pragma unroll
     for (int i = 0; i < NPT; ++i) {
       const int c = tr + i * TPR;
       if (row_ok && c < C) {
         float y[V];
+        if (shift == 0) {
 #pragma unroll
-        for (int e = 0; e < V; ++e) y[e] = (v[i][e] * inv) * g[i][e];
+          for (int e = 0; e < V; ++e) y[e] = (v[i][e] * inv) * g[i][e];
+        } else {
+#pragma unroll
+          for (int e = 0; e < V; ++e) y[e] = (ldexpf(v[i][e], shift) * inv) * g[i][e];
+        }
         CK::template store<NT>(a.out, base + c, CK::pack(y));
       }
     }
@@ -490,23 +590,53 @@ __global__ __launch_bounds__(WGS) void row_stream_kernel(RowArgs a) {
       }
     }
 
-    const float ws = wave_sum(ss);
-    if ((tid & 63) == 0) red[parity][tid >> 6] = ws;
-    __syncthreads();
-    float tot = 0.0f;
-#pragma unroll
-    for (int j = 0; j < NW; ++j) tot += red[parity][j];
-    parity ^= 1;
-    const float inv = row_scale(tot, a.hidden, a.eps);
-
+    const float tot = row_reduce<WGS, NW, NW, false>(ss, red, parity, 0, tid);
+    float inv = row_scale(tot, a.hidden, a.eps);
+    int shift = 0;
     const void* src = KC == 0 ? a.partials.p[0] : a.residual;
+    // this thread's chunk c of the stored row, from the stage or memory
+    auto own = [&](int c) -> raw_t {
+      if constexpr (LDS_STAGE) return stage[c]; else return CK::template load<false>(src, base + c);
+    };
+
+    // Rare: rescale a row whose sum of squares left fp32's range (the whole
+    // workgroup holds one row, so the branch is uniform).
+    if (needs_rescale(tot, a.eps)) {
+      float m = 0.0f;
+      for (int c = tid; c < C; c += WGS) {
+        float t[V];
+        CK::unpack(own(c), t);
+#pragma unroll
+        for (int e = 0; e < V; ++e) m = fmaxf(m, fabsf(t[e]));
+      }
+      m = row_reduce<WGS, NW, NW, true>(m, red, parity, 0, tid);
+      const int ex = exponent_above(m);
+      float ss2 = 0.0f;
+      for (int c = tid; c < C; c += WGS) {
+        float t[V];
+        CK::unpack(own(c), t);
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+          const float q = ldexpf(t[e], -ex);
+          ss2 = __builtin_fmaf(q, q, ss2);
+        }
+      }
+      const float tot2 = row_reduce<WGS, NW, NW, false>(ss2, red, parity, 0, tid);
+      float inv2;
+      int sh2;
+      if (rescaled_scale(m, tot2, ex, a.hidden, a.eps, inv2, sh2)) {
+        inv = inv2;
+        shift = sh2;
+      }
+    }
+
     for (int c0 = tid; c0 < C; c0 += WGS * UNR) {
       raw_t rv[UNR], rg[UNR];
 #pragma unroll
       for (int u = 0; u < UNR; ++u) {
         const int c = c0 + u * WGS;
         if (c < C) {
-          rv[u] = LDS_STAGE ? stage[c] : CK::template load<false>(src, base + c);
+          rv[u] = own(c);
           rg[u] = CK::template load<false>(a.gamma, c);
         }
       }
@@ -517,8 +647,13 @@ __global__ __launch_bounds__(WGS) void row_stream_kernel(RowArgs a) {
           float t[V], g[V], y[V];
           CK::unpack(rv[u], t);
           CK::unpack(rg[u], g);
+          if (shift == 0) {
 #pragma unroll
-          for (int e = 0; e < V; ++e) y[e] = (t[e] * inv) * g[e];
+            for (int e = 0; e < V; ++e) y[e] = (t[e] * inv) * g[e];
+          } else {
+#pragma unroll
+            for (int e = 0; e < V; ++e) y[e] = (ldexpf(t[e], shift) * inv) * g[e];
+          }
           CK::template store<NT>(a.out, base + c, CK::pack(y));
         }
       }

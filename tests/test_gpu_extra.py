@@ -178,3 +178,56 @@ def test_no_writes_outside_the_tensors(dtype, hidden, k):
     for buf in guards:
         iv = buf.view(torch.int16 if buf.element_size() == 2 else torch.int32)
         assert torch.all(iv[:CANARY] == 0x5A5A) and torch.all(iv[-CANARY:] == 0x5A5A)
+
+
+RESCUE_VARIANTS = {
+    "bf16": ["vgpr<bf16,tpr=8,npt=1,wg=256,k=-1,nt>", "vgpr<bf16,tpr=64,npt=2,wg=256,k=-1,nt>",
+             "vgpr<bf16,tpr=128,npt=2,wg=256,k=-1,nt>", "vgpr<bf16,tpr=512,npt=1,wg=512,k=1,nt>",
+             "stream<bf16,v8,wg=512,lds,k=-1,unr=4,nt>", "stream<bf16,vec,wg=256,reread,k=-1,unr=2>",
+             "stream<bf16,elem,wg=256,lds,k=-1,unr=4,nt>", None],
+    "f32": ["vgpr<f32,tpr=16,npt=1,wg=256,k=0,nt>", "vgpr<f32,tpr=256,npt=2,wg=256,k=0,nt>",
+            "stream<f32,v8,wg=256,lds,k=0,unr=4,nt>", "stream<f32,elem,wg=512,reread,k=0,unr=4>", None],
+}
+
+
+def _rescue_case(dtype, hidden, rows, k, eps, seed):
+    """Rows of ordinary, huge (sum of squares past fp32's range) and tiny
+    (squares below it) magnitudes, interleaved so that several rows of one
+    workgroup or wave differ."""
+    w = I.case(dtype, rows, hidden, k, seed=seed, std=0.5, eps=eps)
+    d = I.make_inputs(w)
+    scales = [1.0, 3e25, 1e-30, 1.0, 2e36, 5e-38, 1e-20]
+    tensors = d["partials"] + [d["residual"]] if k else [d["x"]]
+    for t in tensors:
+        f = t.float()
+        for i in range(rows):
+            f[i] *= scales[i % len(scales)]
+        t.copy_(f.to(t.dtype))
+    return w, d
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_rescaled_rows(dtype, monkeypatch):
+    """Rows whose fp32 sum of squares overflows or underflows still match the
+    double oracle, in every kernel family, with eps = 0 and eps > 0."""
+    for i, variant in enumerate(RESCUE_VARIANTS[dtype]):
+        kc = -1 if variant is None else int(variant.split("k=")[1].split(",")[0].rstrip(">"))
+        k = {0: 0, 1: 1, -1: 2}[kc]
+        if variant is None:
+            monkeypatch.delenv("RMSNORM_VARIANT", raising=False)
+            hidden = 4096
+        else:
+            monkeypatch.setenv("RMSNORM_VARIANT", variant)
+            hidden = None
+            for h in (40, 512, 1000, 2048, 4096, 3000, 3001, 40000, 30000, 12000):
+                try:
+                    B.rmsnorm_plan(21, h, k, dtype)
+                    hidden = h
+                    break
+                except B.RmsnormError:
+                    continue
+            assert hidden is not None, variant
+        for eps in (0.0, 1e-6):
+            w, d = _rescue_case(dtype, hidden, 21, k, eps, seed=100 + i)
+            check(w, d, f"rescaled rows {variant} H={hidden} eps={eps}")
+    monkeypatch.delenv("RMSNORM_VARIANT", raising=False)

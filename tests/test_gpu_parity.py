@@ -263,10 +263,9 @@ def _special_inputs(dtype, hidden):
     r[0].zero_()                        # zero row (eps-dominated)
     p[1] = -0.0
     r[1] = -0.0                         # all negative zeros: sum stays -0.0
-    # huge row: as large as an fp32 sum of squares allows (the sum of squares
-    # is accumulated in fp32; rows whose sum overflows binary32 are outside
-    # the supported range)
-    big = {"f32": 1e15, "f16": 3e3, "bf16": 1e15}[dtype]
+    # huge row: its fp32 sum of squares overflows (f32 / bf16), so the
+    # kernels take their rescaled path
+    big = {"f32": 1e30, "f16": 3e3, "bf16": 1e30}[dtype]
     p[2] *= big
     r[2] *= big
     tiny = {"f32": 1e-41, "f16": 1e-7, "bf16": 1e-40}[dtype]
