@@ -24,7 +24,7 @@ import threading
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SRC = os.path.join(_HERE, "rmsnorm_oracle.c")
+_SRCS = [os.path.join(_HERE, "rmsnorm_oracle.c"), os.path.join(_HERE, "block_sum_oracle.c")]
 _INCLUDE = os.path.join(os.path.dirname(_HERE), "include")
 LIB_PATH = os.path.join(_HERE, "librmsnorm_oracle.so")
 
@@ -44,14 +44,15 @@ _default = None
 _lock = threading.Lock()
 
 
-def compile_library(src: str, out: str) -> str:
-    """Compile an oracle source file with the oracle's flags: no FMA
+def compile_library(src, out: str) -> str:
+    """Compile oracle source file(s) with the oracle's flags: no FMA
     contraction, no fast-math, no excess precision (binary32 adds stay
     binary32)."""
+    srcs = [src] if isinstance(src, str) else list(src)
     tmp = out + ".tmp%d" % os.getpid()
     cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-Wall", "-Wextra",
            "-ffp-contract=off", "-fno-fast-math", "-fexcess-precision=standard",
-           "-I", _INCLUDE, "-o", tmp, src, "-lm"]
+           "-I", _INCLUDE, "-o", tmp, *srcs, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, out)
     return out
@@ -61,7 +62,7 @@ def build(force: bool = True) -> str:
     """Compile the oracle library in-tree."""
     if not force and os.path.exists(LIB_PATH):
         return LIB_PATH
-    return compile_library(_SRC, LIB_PATH)
+    return compile_library(_SRCS, LIB_PATH)
 
 
 class Library:
@@ -81,6 +82,12 @@ class Library:
         lib.rmsnorm_oracle_round.restype = ctypes.c_int
         lib.rmsnorm_oracle_decode.argtypes = [dp, vp, i64, ctypes.c_int]
         lib.rmsnorm_oracle_decode.restype = ctypes.c_int
+        if hasattr(lib, "block_sum_oracle"):
+            lib.block_sum_oracle.argtypes = [dp, dp, ctypes.POINTER(ctypes.c_int32), vp, i64,
+                                             ctypes.c_int]
+            lib.block_sum_oracle.restype = ctypes.c_int
+            lib.block_sum_oracle_decode.argtypes = [dp, vp, i64, ctypes.c_int]
+            lib.block_sum_oracle_decode.restype = ctypes.c_int
         self.lib = lib
         self.path = path
 
@@ -196,4 +203,41 @@ def decode(bits: np.ndarray, dtype: str, lib: "Library | None" = None) -> np.nda
     b = _check(np.ascontiguousarray(bits), dtype)
     dst = np.empty(b.shape, dtype=np.float64)
     _raise(_load(lib).rmsnorm_oracle_decode(_dptr(dst), _ptr(b), b.size, DTYPE_CODE[dtype]))
+    return dst
+
+
+# ---- block all-reduce sum family -------------------------------------------
+
+SUM_DTYPE_CODE = {"f32": 0, "f16": 1, "bf16": 2, "fp8_e4m3": 3, "fp8_e5m2": 4, "i8": 5}
+
+
+def _sum_storage(dtype: str):
+    return {"f32": np.float32, "f16": np.uint16, "bf16": np.uint16}.get(
+        dtype, np.int8 if dtype == "i8" else np.uint8)
+
+
+def block_sum(x: np.ndarray, dtype: str, lib: "Library | None" = None):
+    """Sum of all elements of x (numpy storage: float32, uint16 bit patterns,
+    uint8 fp8 codes, or int8).  Floating dtypes: (sum, sum of |x|) as
+    floats; i8: (int32 sum modulo 2^32, exact sum)."""
+    a = np.ascontiguousarray(x)
+    if a.dtype != _sum_storage(dtype):
+        raise TypeError(f"block_sum oracle expects {np.dtype(_sum_storage(dtype))} for {dtype}")
+    s = np.zeros(1, np.float64)
+    ab = np.zeros(1, np.float64)
+    i32 = ctypes.c_int32(0)
+    rc = _load(lib).block_sum_oracle(_dptr(s), _dptr(ab), ctypes.byref(i32),
+                                     ctypes.c_void_p(a.ctypes.data) if a.size else None, a.size,
+                                     SUM_DTYPE_CODE[dtype])
+    _raise(rc)
+    if dtype == "i8":
+        return int(i32.value), float(s[0])
+    return float(s[0]), float(ab[0])
+
+
+def block_sum_decode(x: np.ndarray, dtype: str, lib: "Library | None" = None) -> np.ndarray:
+    a = np.ascontiguousarray(x)
+    dst = np.empty(a.shape, np.float64)
+    _raise(_load(lib).block_sum_oracle_decode(_dptr(dst), ctypes.c_void_p(a.ctypes.data), a.size,
+                                              SUM_DTYPE_CODE[dtype]))
     return dst

@@ -35,7 +35,8 @@ RESIDUAL_ID = 100
 GAMMA_ID = 200
 SPECIAL_ID = 300
 
-TORCH_DTYPE = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+TORCH_DTYPE = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16,
+               "fp8_e4m3": torch.float8_e4m3fn, "fp8_e5m2": torch.float8_e5m2, "i8": torch.int8}
 
 
 def _rng(seed: int, tensor_id: int, block: int) -> np.random.Generator:
@@ -54,6 +55,8 @@ def special_rows(w: Workload):
 def _draw_block(w: Workload, tensor_id: int, block: int, std: float, scaled, zeroed) -> np.ndarray:
     r0 = block * BLOCK_ROWS
     nr = min(BLOCK_ROWS, w.rows - r0)
+    if w.dtype == "i8":  # int8 inputs: uniform over the whole int8 range
+        return _rng(w.seed, tensor_id, block).integers(-128, 128, (nr, w.hidden), dtype=np.int8)
     a = _rng(w.seed, tensor_id, block).standard_normal((nr, w.hidden), dtype=np.float32)
     if std != 1.0:
         a *= np.float32(std)
@@ -66,6 +69,8 @@ def _draw_block(w: Workload, tensor_id: int, block: int, std: float, scaled, zer
 
 
 def _to_dtype(a: np.ndarray, dtype: str) -> torch.Tensor:
+    if dtype == "i8":
+        return torch.from_numpy(a)
     return torch.from_numpy(a).to(TORCH_DTYPE[dtype])
 
 
@@ -128,11 +133,14 @@ def make_inputs(w: Workload, rows: Optional[Sequence[int]] = None, device: str =
 
 
 def to_storage(t: torch.Tensor) -> np.ndarray:
-    """A CPU tensor's storage as numpy: float32 values, or uint16 bit patterns
-    for fp16 / bf16 (the oracle's array convention)."""
+    """A CPU tensor's storage as numpy: float32 values, uint16 bit patterns
+    for fp16 / bf16, uint8 codes for fp8, int8 for int8 (the oracle's array
+    convention)."""
     t = t.detach().to("cpu").contiguous()
-    if t.dtype == torch.float32:
+    if t.dtype == torch.float32 or t.dtype == torch.int8:
         return t.numpy()
+    if t.element_size() == 1:
+        return t.view(torch.uint8).numpy()
     return t.view(torch.int16).numpy().view(np.uint16)
 
 

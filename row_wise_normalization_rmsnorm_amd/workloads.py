@@ -18,8 +18,8 @@ from dataclasses import dataclass
 @dataclass(frozen=True)
 class Workload:
     name: str
-    op: str           # "rmsnorm" or "add_rmsnorm"
-    dtype: str        # "f32", "f16" or "bf16"
+    op: str           # "rmsnorm", "add_rmsnorm" or "block_sum"
+    dtype: str        # "f32", "f16", "bf16" (block_sum also "fp8_e4m3", "fp8_e5m2", "i8")
     rows: int
     hidden: int
     k: int            # partial buffers (0 for plain RMSNorm)
@@ -34,17 +34,22 @@ class Workload:
 
     @property
     def itemsize(self) -> int:
-        return 4 if self.dtype == "f32" else 2
+        return {"f32": 4, "f16": 2, "bf16": 2}.get(self.dtype, 1)
 
     def algorithmic_bytes(self) -> int:
         """Bytes a single pass must move: each tensor element read or written
         once, gamma counted once.  Plain: read x, write out.  Fused: read K
-        partials and the residual, write the residual and out."""
+        partials and the residual, write the residual and out.  Block sum:
+        read x, write one 4-byte result."""
         n = self.rows * self.hidden * self.itemsize
+        if self.op == "block_sum":
+            return n + 4
         per_elem = 2 if not self.fused else self.k + 3
         return n * per_elem + self.hidden * self.itemsize
 
     def describe(self) -> str:
+        if self.op == "block_sum":
+            return f"block_sum {self.dtype} {self.rows}x{self.hidden}"
         return (f"{self.op} {self.dtype} rows={self.rows} hidden={self.hidden}"
                 + (f" K={self.k}" if self.fused else "") + f" eps={self.eps:g}")
 
@@ -65,6 +70,20 @@ WORKLOADS = {
         "add_rmsnorm_bf16_65536x16384_k1", "add_rmsnorm", "bf16", 65536, 16384, 1, 1e-6, 1.0,
         special_frac=0.01),
 }
+
+# Block all-reduce sum of a [S, K] tensor (page "Block All Reduce CUDA代码学习":
+# S = K = 1024 randn, and K = 4096), every input dtype, plus a large bf16
+# tensor for bandwidth.
+for _dt in ("f32", "f16", "bf16", "fp8_e4m3", "fp8_e5m2", "i8"):
+    WORKLOADS[f"block_sum_{_dt}_1024x1024"] = Workload(
+        f"block_sum_{_dt}_1024x1024", "block_sum", _dt, 1024, 1024, 0, 0.0, 1.0)
+WORKLOADS["block_sum_f32_4096x4096"] = Workload(
+    "block_sum_f32_4096x4096", "block_sum", "f32", 4096, 4096, 0, 0.0, 1.0)
+WORKLOADS["block_sum_bf16_16384x16384"] = Workload(
+    "block_sum_bf16_16384x16384", "block_sum", "bf16", 16384, 16384, 0, 0.0, 1.0)
+
+RMSNORM_WORKLOADS = [n for n, w in WORKLOADS.items() if w.op != "block_sum"]
+BLOCK_SUM_WORKLOADS = [n for n, w in WORKLOADS.items() if w.op == "block_sum"]
 
 # The headline workload: fused residual add + RMSNorm, bf16, 8192 x 4096.
 HEADLINE = "add_rmsnorm_bf16_8192x4096_k1"
