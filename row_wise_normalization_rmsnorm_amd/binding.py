@@ -22,6 +22,13 @@ DTYPE_NAME = {"f32": 0, "f16": 1, "bf16": 2}
 KMAX = 16
 EXPORTS = ("rmsnorm_fwd", "add_rmsnorm_fwd", "rmsnorm_strerror", "rmsnorm_last_error",
            "rmsnorm_plan", "rmsnorm_variants")
+BLOCK_SUM_EXPORTS = ("block_all_reduce_sum",)
+
+# block all-reduce sum (include/block_sum.h)
+BRS_DTYPE_CODE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2,
+                  torch.float8_e4m3fn: 3, torch.float8_e5m2: 4, torch.int8: 5}
+BRS_MAX_GROUPS = 2048
+BRS_WORKSPACE_BYTES = 256 + 4 * BRS_MAX_GROUPS
 
 _lib = None
 _lock = threading.Lock()
@@ -56,6 +63,8 @@ def lib() -> ctypes.CDLL:
             l.rmsnorm_plan.restype = c_int
             l.rmsnorm_variants.argtypes = [c_int, ctypes.c_char_p, c_int]
             l.rmsnorm_variants.restype = c_int
+            l.block_all_reduce_sum.argtypes = [vp, vp, i64, c_int, vp, i64, vp]
+            l.block_all_reduce_sum.restype = c_int
             _lib = l
         return _lib
 
@@ -140,6 +149,48 @@ def rmsnorm_variants(dtype: str) -> list:
     if n < 0:
         _check(n)
     return [s for s in buf.value.decode().split("\n") if s]
+
+
+_workspaces = {}
+_ws_lock = threading.Lock()
+
+
+def block_sum_workspace(device=None, stream=None) -> torch.Tensor:
+    """A zeroed workspace for block_all_reduce_sum, one per (device, stream):
+    calls sharing a workspace must be ordered on one stream."""
+    dev = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+    if dev.index is None:
+        dev = torch.device("cuda", torch.cuda.current_device())
+    sid = _stream(torch.empty(0, device=dev), stream)
+    with _ws_lock:
+        ws = _workspaces.get((dev.index, sid))
+        if ws is None:
+            ws = torch.zeros(BRS_WORKSPACE_BYTES, dtype=torch.uint8, device=dev)
+            _workspaces[(dev.index, sid)] = ws
+        return ws
+
+
+def block_all_reduce_sum_fwd(out: torch.Tensor, x: torch.Tensor, workspace: Optional[torch.Tensor] = None,
+                             stream=None) -> None:
+    """out (one float32, or one int32 for int8 x) = sum of every element of x."""
+    if x.dtype not in BRS_DTYPE_CODE:
+        raise RmsnormError(-3, f"unsupported dtype {x.dtype}")
+    want = torch.int32 if x.dtype == torch.int8 else torch.float32
+    if out.dtype != want or out.numel() != 1:
+        raise RmsnormError(-2, f"out must be one {want}")
+    if workspace is None:
+        workspace = block_sum_workspace(x.device, stream)
+    _check(lib().block_all_reduce_sum(_dev_ptr(out, "out"), _dev_ptr(x, "x") if x.numel() else
+                                      x.data_ptr() or None, x.numel(), BRS_DTYPE_CODE[x.dtype],
+                                      _dev_ptr(workspace, "workspace"), workspace.numel(),
+                                      _stream(x, stream)))
+
+
+def block_all_reduce_sum(x: torch.Tensor) -> torch.Tensor:
+    out = torch.empty(1, dtype=torch.int32 if x.dtype == torch.int8 else torch.float32,
+                      device=x.device)
+    block_all_reduce_sum_fwd(out, x)
+    return out
 
 
 # convenience wrappers ------------------------------------------------------

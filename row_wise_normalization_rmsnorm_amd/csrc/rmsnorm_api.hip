@@ -221,6 +221,9 @@ int launch(const Plan& plan, rmsn::RowArgs a, void* stream) {
 
 }  // namespace
 
+// The last-error slot, shared with the other entry points of the library.
+int rmsn_set_error(int code, const char* msg) { return fail(code, "%s", msg); }
+
 extern "C" {
 
 int rmsnorm_fwd(void* out, const void* x, const void* gamma, int64_t rows, int64_t hidden,

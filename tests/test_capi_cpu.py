@@ -29,10 +29,32 @@ def test_gpu_library_exports_every_declared_function():
     assert set(B.EXPORTS) == names
 
 
+def test_block_sum_exports_every_declared_function():
+    names = declared("block_sum.h")
+    assert names == set(B.BLOCK_SUM_EXPORTS)
+    for n in names:
+        assert hasattr(B.lib(), n), n
+
+
+def test_block_sum_error_codes():
+    f = B.lib().block_all_reduce_sum
+    ws = FAKE + (1 << 26)
+    assert f(FAKE, FAKE + (1 << 20), 10, 9, ws, B.BRS_WORKSPACE_BYTES, None) == -3
+    assert f(FAKE, FAKE + (1 << 20), -1, 0, ws, B.BRS_WORKSPACE_BYTES, None) == -2
+    assert f(None, FAKE + (1 << 20), 10, 0, ws, B.BRS_WORKSPACE_BYTES, None) == -1
+    assert f(FAKE, None, 10, 0, ws, B.BRS_WORKSPACE_BYTES, None) == -1
+    assert f(FAKE, FAKE + (1 << 20), 10, 0, None, B.BRS_WORKSPACE_BYTES, None) == -1
+    assert f(FAKE, FAKE + (1 << 20) + 2, 10, 0, ws, B.BRS_WORKSPACE_BYTES, None) == -2  # f32 at 2 mod 4
+    assert f(FAKE, FAKE + (1 << 20), 10, 0, ws, B.BRS_WORKSPACE_BYTES - 4, None) == -2
+    assert f(FAKE, FAKE + (1 << 20), 10, 0, ws + 8, B.BRS_WORKSPACE_BYTES, None) == -2
+    assert f(FAKE + (1 << 20) + 4, FAKE + (1 << 20), 10, 0, ws, B.BRS_WORKSPACE_BYTES, None) == -5
+    assert f(FAKE, FAKE + (1 << 20), 10, 0, FAKE + (1 << 20) + 16, B.BRS_WORKSPACE_BYTES, None) == -5
+
+
 def test_oracle_library_exports_every_declared_function():
     import oracle
-    names = declared("rmsnorm_oracle.h")
-    assert "rmsnorm_oracle" in names
+    names = declared("rmsnorm_oracle.h") | declared("block_sum_oracle.h")
+    assert {"rmsnorm_oracle", "block_sum_oracle"} <= names
     lib = oracle._load()
     for n in names:
         assert hasattr(lib, n), n

@@ -1,0 +1,143 @@
+"""GPU parity of the block all-reduce sum (include/block_sum.h) against the
+CPU oracle.
+
+Bar: int8 sums are exact (modulo 2^32).  fp32 sums of floating inputs are
+within the bound of their summation tree: each element passes through at
+most m + 64 fp32 additions (m = elements one thread adds in sequence), so
+|gpu - exact| <= (m + 64) * 2^-24 * sum|x| (+ the final rounding); NaN and
+inf follow IEEE.
+"""
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from row_wise_normalization_rmsnorm_amd import binding as B
+from row_wise_normalization_rmsnorm_amd import inputs as I
+from row_wise_normalization_rmsnorm_amd.workloads import BLOCK_SUM_WORKLOADS, WORKLOADS, Workload
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+ELEM = {"f32": 4, "f16": 2, "bf16": 2, "fp8_e4m3": 1, "fp8_e5m2": 1, "i8": 1}
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def per_thread_elements(n: int, dtype: str, offset_bytes: int = 0) -> int:
+    s = ELEM[dtype]
+    e = 16 // s
+    head = min(n, ((16 - offset_bytes % 16) % 16) // s)
+    nchunks = (n - head) // e
+    groups = max(1, min(B.BRS_MAX_GROUPS, -(-nchunks // 1024)))
+    iters = -(-nchunks // (groups * 1024)) if nchunks else 0
+    return iters * 4 * e + 2
+
+
+def gpu_sum(x: torch.Tensor) -> float:
+    out = B.block_all_reduce_sum(x)
+    torch.cuda.synchronize()
+    return out.item()
+
+
+def check(x_cpu: torch.Tensor, dtype: str, what: str, offset_bytes: int = 0, x_dev=None):
+    say(f"[gpu] block sum {what}: {dtype} n={x_cpu.numel()} offset={offset_bytes}")
+    st = I.to_storage(x_cpu).reshape(-1)
+    xd = x_dev if x_dev is not None else x_cpu.reshape(-1).to(DEV)
+    got = gpu_sum(xd)
+    if dtype == "i8":
+        want, _ = oracle.block_sum(st, "i8")
+        assert got == want, (what, got, want)
+        return 0.0
+    exact, absum = oracle.block_sum(st, dtype)
+    if math.isnan(exact):
+        assert math.isnan(got), (what, got)
+        return 0.0
+    if math.isinf(exact):
+        assert got == exact, (what, got, exact)
+        return 0.0
+    m = per_thread_elements(x_cpu.numel(), dtype, offset_bytes)
+    bound = (m + 64) * 2.0 ** -24 * absum + abs(exact) * 2.0 ** -24 + 1e-45
+    err = abs(got - exact)
+    assert err <= bound, (what, got, exact, err, bound)
+    return err / bound if bound else 0.0
+
+
+@pytest.mark.parametrize("name", BLOCK_SUM_WORKLOADS)
+def test_workloads(name):
+    w = WORKLOADS[name]
+    x = I.make_inputs(w)["x"]
+    r = check(x, w.dtype, name)
+    say(f"[gpu] {name}: error / bound = {r:.3g}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16", "fp8_e4m3", "fp8_e5m2", "i8"])
+def test_lengths_and_offsets(dtype):
+    """Ragged lengths and every base offset (head, chunks, tail split)."""
+    s = ELEM[dtype]
+    for n in (0, 1, 7, 15, 16, 17, 255, 1024, 4097, 65539, 1 << 20, (1 << 21) + 13):
+        w = Workload("case", "block_sum", dtype, 1, n, 0, 0.0, 1.0, seed=n % 97)
+        x = I.make_inputs(w)["x"].reshape(-1) if n else torch.empty(0, dtype=I.TORCH_DTYPE[dtype])
+        for off in sorted({0, s, 16 - s, 8 if s <= 8 else 0}):
+            buf = torch.zeros(n + 64 // s, dtype=x.dtype, device=DEV)
+            e0 = off // s
+            xd = buf[e0:e0 + n]
+            if n:
+                xd.copy_(x.to(DEV))
+            assert xd.data_ptr() % 16 == off % 16 or n == 0
+            check(x, dtype, f"n={n}", offset_bytes=off, x_dev=xd)
+
+
+def test_deterministic_and_workspace_reset():
+    w = WORKLOADS["block_sum_bf16_16384x16384"]
+    x = I.device_tensor(Workload("d", "block_sum", "f32", 4096, 4096, 0, 0.0, 1.0, seed=3), 0, DEV)
+    ws = torch.zeros(B.BRS_WORKSPACE_BYTES, dtype=torch.uint8, device=DEV)
+    outs = []
+    for _ in range(5):
+        out = torch.empty(1, dtype=torch.float32, device=DEV)
+        B.block_all_reduce_sum_fwd(out, x, ws)
+        outs.append(out)
+    torch.cuda.synchronize()
+    bits = {int(o.view(torch.int32).item()) for o in outs}
+    assert len(bits) == 1
+    assert int(ws[:4].view(torch.int32).item()) == 0  # the completion counter is back at zero
+    del w
+
+
+def test_int8_wraps_like_int32():
+    n = (1 << 25) + 3
+    x = torch.full((n,), 127, dtype=torch.int8)
+    check(x, "i8", "wrap past 2^31")
+    x = torch.full((n,), -128, dtype=torch.int8)
+    check(x, "i8", "wrap below -2^31")
+
+
+def test_special_values():
+    for dtype in ("f32", "bf16", "f16", "fp8_e5m2"):
+        base = torch.ones(5000)
+        a = base.clone()
+        a[1234] = float("nan")
+        check(a.to(I.TORCH_DTYPE[dtype]), dtype, "nan")
+        a = base.clone()
+        a[17] = float("inf")
+        check(a.to(I.TORCH_DTYPE[dtype]), dtype, "+inf")
+        a[4000] = float("-inf")
+        check(a.to(I.TORCH_DTYPE[dtype]), dtype, "+inf -inf")
+    codes = torch.full((3000,), 0x38, dtype=torch.uint8)   # 1.0 in E4M3
+    codes[2999] = 0x7F                                      # NaN
+    check(codes.view(torch.float8_e4m3fn), "fp8_e4m3", "e4m3 nan")
+    sub = torch.tensor([0x01, 0x81, 0x07, 0x08] * 500, dtype=torch.uint8)  # subnormals / min normal
+    check(sub.view(torch.float8_e4m3fn), "fp8_e4m3", "e4m3 subnormals")
+
+
+def test_large_tensor_bf16():
+    """16384 x 16384 bf16 (512 MiB): the whole sum against the oracle."""
+    w = WORKLOADS["block_sum_bf16_16384x16384"]
+    x = I.make_inputs(w)["x"]
+    check(x, "bf16", w.name, x_dev=x.to(DEV).reshape(-1))
