@@ -71,10 +71,16 @@ def cpu_baseline(w, target_cpu_seconds: float = 12.0, max_passes: int = 40) -> d
     from row_wise_normalization_rmsnorm_amd import inputs as I
 
     d = I.make_inputs(w)
-    g = I.to_storage(d["gamma"])
     cores = host_cores()
     bounds = [(i * w.rows // cores, (i + 1) * w.rows // cores) for i in range(cores)]
-    if w.fused:
+    g = I.to_storage(d["gamma"]) if "gamma" in d else None
+    if w.op == "block_sum":
+        xs = I.to_storage(d["x"])
+
+        def job(b):
+            a, z = b
+            return oracle.block_sum(xs[a:z].reshape(-1), w.dtype)
+    elif w.fused:
         ps = I.storage_list(d["partials"])
         r = I.to_storage(d["residual"])
 
@@ -119,7 +125,7 @@ def stream_ceiling(w, dev: str = "cuda:0", steps: int = 60, rotate_gib: float = 
     lib.stream_probe.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int,
                                  ctypes.POINTER(ctypes.c_void_p), ctypes.c_int, ctypes.c_int64,
                                  ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
-    nr, nw = (w.k + 1, 2) if w.fused else (1, 1)
+    nr, nw = (w.k + 1, 2) if w.fused else ((1, 0) if w.op == "block_sum" else (1, 1))
     tensor_bytes = w.rows * w.hidden * w.itemsize
     n16 = tensor_bytes // 16
     set_bytes = (nr + nw) * tensor_bytes
@@ -133,7 +139,7 @@ def stream_ceiling(w, dev: str = "cuda:0", steps: int = 60, rotate_gib: float = 
         args = []
         for b in bufs:
             ra = (ctypes.c_void_p * nr)(*[t.data_ptr() for t in b[:nr]])
-            wa = (ctypes.c_void_p * nw)(*[t.data_ptr() for t in b[nr:]])
+            wa = (ctypes.c_void_p * max(nw, 1))(*[t.data_ptr() for t in b[nr:]])
             args.append((ra, wa))
 
         def launch(i):
@@ -266,14 +272,28 @@ def main() -> int:
     for i in range(nsets):
         s = {k: ([t.clone() for t in v] if isinstance(v, list) else v.clone())
              for k, v in base.items()}
-        s["out"] = torch.empty_like(s["residual"] if w.fused else s["x"])
+        if w.op == "block_sum":
+            s["x"] = s["x"].reshape(-1)
+            s["out"] = torch.empty(1, device=dev,
+                                   dtype=torch.int32 if w.dtype == "i8" else torch.float32)
+        else:
+            s["out"] = torch.empty_like(s["residual"] if w.fused else s["x"])
         sets.append(s)
     del base
-    kernel = B.rmsnorm_plan(w.rows, w.hidden, w.k, w.dtype)
+    if w.op == "block_sum":
+        if a.sweep:
+            print("bench.py: --sweep applies to the RMSNorm kernels only", file=sys.stderr)
+            return 2
+        kernel = f"block_sum<{w.dtype}>"
+        ws = B.block_sum_workspace(dev)
+    else:
+        kernel = B.rmsnorm_plan(w.rows, w.hidden, w.k, w.dtype)
 
     def step(i):
         s = sets[i % nsets]
-        if w.fused:
+        if w.op == "block_sum":
+            B.block_all_reduce_sum_fwd(s["out"], s["x"], ws)
+        elif w.fused:
             B.add_rmsnorm_fwd(s["out"], s["residual"], s["partials"], s["gamma"], w.eps)
         else:
             B.rmsnorm_fwd(s["out"], s["x"], s["gamma"], w.eps)
@@ -304,8 +324,10 @@ def main() -> int:
           f"{nsets} rotating sets, wall {wall:.2f}s", file=sys.stderr, flush=True)
 
     traffic = traffic_for(kernel, w.name)
+    metric = ("achieved HBM GB/s (% of peak) + rows/s, add_rmsnorm bf16 8192x4096"
+              if w.name == HEADLINE else f"achieved HBM GB/s (% of peak) + rows/s, {w.describe()}")
     result = {
-        "metric": "achieved HBM GB/s (% of peak) + rows/s, add_rmsnorm bf16 8192x4096",
+        "metric": metric,
         "value": round(gbs, 1),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -322,6 +344,7 @@ def main() -> int:
                    "algorithmic_bytes_per_step": nbytes},
         "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "rows_per_s": round(rows_per_s, 1),
+        "elements_per_s": round(w.rows * w.hidden / (ms * 1e-3), 1),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic},

@@ -14,8 +14,9 @@
  * partial sums in index order, so the fp32 result is identical from run to
  * run for the same n and the same base address (the split into head, 16-byte
  * chunks and tail depends on the address).  The fp32 result differs from the
- * exact sum by at most about (n / 524288 + 48) * 2^-24 * sum|x| (the depth of
- * its summation tree); the int8 result is exact modulo 2^32.
+ * exact sum by at most (m + 64) * 2^-24 * sum|x| with m = max(33, n*S/2^21 + 1)
+ * * (16/S) elements added by one thread in sequence (S = element bytes): the
+ * depth of its summation tree.  The int8 result is exact modulo 2^32.
  *
  * Conventions (shared with rmsnorm.h, whose RMSN_* codes and
  * rmsnorm_strerror / rmsnorm_last_error apply):
@@ -23,9 +24,10 @@
  *     be aligned to its element size; out receives one float (floating
  *     dtypes) or one int32_t (BRS_I8).
  *   - workspace: a DEVICE buffer of at least BRS_WORKSPACE_BYTES bytes,
- *     16-byte aligned, owned by the caller.  Its first 4 bytes must be zero
- *     before its first use (allocate it zeroed); every call leaves them zero
- *     again.  Calls that share a workspace must be ordered on one stream.
+ *     16-byte aligned, owned by the caller.  Its first BRS_WORKSPACE_HEADER
+ *     bytes (completion counters) must be zero before its first use:
+ *     allocate it zeroed; every call leaves them zero again.  Calls that
+ *     share a workspace must be ordered on one stream.
  *   - The call enqueues one kernel on `stream` (NULL: the default stream),
  *     allocates nothing and does not synchronise.  Arguments are validated
  *     before the launch; on error nothing is launched.
@@ -51,10 +53,11 @@ typedef enum {
   BRS_I8 = 5
 } brs_dtype;
 
-/* Workgroups per launch never exceed this; the workspace holds a 256-byte
- * header (the completion counter) and one 4-byte partial per workgroup. */
+/* Workgroups per launch never exceed BRS_MAX_GROUPS; the workspace holds a
+ * header of completion counters and one 4-byte partial per workgroup. */
 #define BRS_MAX_GROUPS 2048
-#define BRS_WORKSPACE_BYTES (256 + 4 * BRS_MAX_GROUPS)
+#define BRS_WORKSPACE_HEADER 4608
+#define BRS_WORKSPACE_BYTES (BRS_WORKSPACE_HEADER + 4 * BRS_MAX_GROUPS)
 
 /*
  * block_all_reduce_sum -- *out = sum of x[0..n).  Returns RMSN_OK or

@@ -28,7 +28,8 @@ BLOCK_SUM_EXPORTS = ("block_all_reduce_sum",)
 BRS_DTYPE_CODE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2,
                   torch.float8_e4m3fn: 3, torch.float8_e5m2: 4, torch.int8: 5}
 BRS_MAX_GROUPS = 2048
-BRS_WORKSPACE_BYTES = 256 + 4 * BRS_MAX_GROUPS
+BRS_WORKSPACE_HEADER = 4608
+BRS_WORKSPACE_BYTES = BRS_WORKSPACE_HEADER + 4 * BRS_MAX_GROUPS
 
 _lib = None
 _lock = threading.Lock()
