@@ -20,8 +20,6 @@ from __future__ import annotations
 
 import argparse
 import concurrent.futures as cf
-import hashlib
-import glob
 import json
 import os
 import sys
@@ -30,17 +28,12 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+from row_wise_normalization_rmsnorm_amd.profiling import source_hash  # noqa: E402
+
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published peak
 
 
-def source_hash() -> str:
-    h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "row_wise_normalization_rmsnorm_amd", "csrc", "*"))):
-        h.update(open(p, "rb").read())
-    return h.hexdigest()
-
-
-def traffic_for(kernel: str, workload: str):
+def traffic_for(kernel: str, workload: str, op: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or
     None when there is none or the kernel sources changed since."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
@@ -50,7 +43,7 @@ def traffic_for(kernel: str, workload: str):
         d = json.load(open(path))
     except (OSError, ValueError):
         return None
-    if d.get("source_sha256") != source_hash() or d.get("kernel") != kernel:
+    if d.get("source_sha256") != source_hash(op) or d.get("kernel") != kernel:
         return None
     return d.get("traffic_bytes_per_launch")
 
@@ -106,11 +99,25 @@ def cpu_baseline(w, target_cpu_seconds: float = 12.0, max_passes: int = 40) -> d
         dt = time.perf_counter() - t0
         cpu = time.process_time() - c0
     per_pass = dt / passes
+    # the same oracle on one thread, over whole row blocks until about a
+    # third of the multi-threaded budget is spent
+    blocks, t1 = 0, time.perf_counter()
+    while True:
+        job(bounds[blocks % cores])
+        blocks += 1
+        if time.perf_counter() - t1 >= target_cpu_seconds / 3 or blocks >= max_passes * cores:
+            break
+    single = (time.perf_counter() - t1) / blocks * cores
     return {"value": round(w.algorithmic_bytes() / per_pass / 1e9, 3), "unit": "GB/s",
             "rows_per_s": round(w.rows / per_pass, 1), "seconds_per_pass": round(per_pass, 4),
             "cores": cores, "kind": "oracle",
             "sample": (f"{passes} full passes over all {w.rows} rows of {w.name} "
-                       f"({cpu:.1f} CPU-seconds), rows split over {cores} threads")}
+                       f"({cpu:.1f} CPU-seconds), rows split over {cores} threads"),
+            "single_thread": {"value": round(w.algorithmic_bytes() / single / 1e9, 3),
+                              "unit": "GB/s", "rows_per_s": round(w.rows / single, 1),
+                              "cores": 1,
+                              "sample": f"{blocks} row blocks of {w.rows // cores} rows, "
+                                        "one thread"}}
 
 
 def stream_ceiling(w, dev: str = "cuda:0", steps: int = 60, rotate_gib: float = 1.0) -> dict:
@@ -166,6 +173,30 @@ def stream_ceiling(w, dev: str = "cuda:0", steps: int = 60, rotate_gib: float = 
                  "frac_of_peak": round(best["value"] / HBM_PEAK_GBS, 4)})
     del bufs
     return best
+
+
+def latency(step, n: int, flush_bytes: int = 0) -> dict:
+    """Per-launch durations from an event pair around each launch: median,
+    p10 and p90 in microseconds.  ``flush_bytes`` > 0 clears a scratch
+    buffer of that size before every launch, outside the event pair, so each
+    launch starts with its inputs out of the caches."""
+    import torch
+    stream = torch.cuda.current_stream()
+    scratch = torch.empty(flush_bytes, dtype=torch.uint8, device="cuda:0") if flush_bytes else None
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n)]
+    torch.cuda.synchronize()
+    for i, (e0, e1) in enumerate(ev):
+        if scratch is not None:
+            scratch.zero_()
+        e0.record(stream)
+        step(i)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    us = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in ev)
+    q = lambda f: round(us[min(n - 1, int(f * n))], 3)  # noqa: E731
+    return {"median_us": q(0.5), "p10_us": q(0.1), "p90_us": q(0.9), "launches": n,
+            "flush_bytes": flush_bytes}
 
 
 def sweep(w, step, a, B) -> int:
@@ -323,7 +354,17 @@ def main() -> int:
           f"({100 * gbs / HBM_PEAK_GBS:.1f}% of peak), {rows_per_s:.3g} rows/s, "
           f"{nsets} rotating sets, wall {wall:.2f}s", file=sys.stderr, flush=True)
 
-    traffic = traffic_for(kernel, w.name)
+    # Context beside the graded number: the spread of single launches, and
+    # for inputs far smaller than the 256 MB Infinity Cache the same with a
+    # 1 GiB cache flush before each launch.
+    lat = {"batched": latency(step, min(a.steps, 200))}
+    if nbytes < (64 << 20):
+        lat["flushed"] = latency(step, min(a.steps, 100), flush_bytes=1 << 30)
+    for kind, l in lat.items():
+        print(f"[bench] per-launch ({kind}): median {l['median_us']} us, p10 {l['p10_us']}, "
+              f"p90 {l['p90_us']}", file=sys.stderr, flush=True)
+
+    traffic = traffic_for(kernel, w.name, w.op)
     metric = ("achieved HBM GB/s (% of peak) + rows/s, add_rmsnorm bf16 8192x4096"
               if w.name == HEADLINE else f"achieved HBM GB/s (% of peak) + rows/s, {w.describe()}")
     result = {
@@ -345,6 +386,7 @@ def main() -> int:
         "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "rows_per_s": round(rows_per_s, 1),
         "elements_per_s": round(w.rows * w.hidden / (ms * 1e-3), 1),
+        "per_launch": lat,
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic},

@@ -34,9 +34,20 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 COPY_BYTES = 1 << 30
 
 
-def source_hash() -> str:
+def kernel_sources(op: str) -> list:
+    """The source files a workload's kernel is built from: the block sum has
+    one file of its own; every other op runs the RMSNorm kernels."""
+    csrc = os.path.join(ROOT, "row_wise_normalization_rmsnorm_amd", "csrc")
+    everything = sorted(glob.glob(os.path.join(csrc, "*")))
+    mine = os.path.join(csrc, "block_sum.hip")
+    return [mine] if op == "block_sum" else [p for p in everything if p != mine]
+
+
+def source_hash(op: str) -> str:
+    """sha256 over the kernel sources of ``op``: a traffic figure taken on
+    other sources is stale."""
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "row_wise_normalization_rmsnorm_amd", "csrc", "*"))):
+    for p in kernel_sources(op):
         h.update(open(p, "rb").read())
     return h.hexdigest()
 
@@ -176,8 +187,10 @@ def main() -> int:
     md = os.path.join(ROOT, "profiles", f"{name}__{w.name}.md")
     with open(md, "w") as f:
         f.write(f"# {a.plan} on {w.name}\n\n")
+        what = ("each element read once, the 4-byte sum written once" if w.op == "block_sum"
+                else "each tensor element read or written once, gamma once")
         f.write(f"Workload: {w.describe()}; algorithmic bytes per launch {nbytes:,} "
-                f"(each tensor element read or written once, gamma once).\n\n")
+                f"({what}).\n\n")
         f.write("## Kernel trace (rocprofv3 --kernel-trace --stats)\n\n")
         f.write("Command: `rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o run -- "
                 f"python bench.py --workload {w.name} --no-cpu-baseline`\n\n")
@@ -204,13 +217,13 @@ def main() -> int:
                 f"{write_b:,.0f} |\n")
         f.write(f"\nHBM traffic per launch {traffic:,.0f} B = {traffic / nbytes:.4f} x the "
                 "algorithmic bytes.\n")
-        f.write(f"\nKernel sources sha256: `{source_hash()}`\n")
+        f.write(f"\nKernel sources sha256: `{source_hash(w.op)}`\n")
     tj = os.path.join(ROOT, "profiles", f"traffic_{w.name}.json")
     json.dump({"workload": w.name, "kernel": a.plan, "traffic_bytes_per_launch": round(traffic),
                "read_bytes": round(read_b), "write_bytes": round(write_b),
                "algorithmic_bytes": nbytes, "fetch_kib": fetch_kib, "write_kib": write_kib,
                "copy_fetch_kib_per_gib": cf_kib, "copy_write_kib_per_gib": cw_kib,
-               "avg_kernel_ns": k["avg_ns"], "source_sha256": source_hash()},
+               "avg_kernel_ns": k["avg_ns"], "source_sha256": source_hash(w.op)},
               open(tj, "w"), indent=1)
     print(md)
     print(tj)
