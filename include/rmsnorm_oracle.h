@@ -91,6 +91,19 @@ int rmsnorm_oracle_f64(void* out, double* y_f64, void* residual,
                        double* rstd_out);
 
 /*
+ * rmsnorm_oracle_ex -- the general form: the same computation with gamma in
+ * gamma_dtype and out in out_dtype (each one of the three dtype codes; the
+ * data -- partials, residual -- stay in dtype).  gamma is read exactly in
+ * its own dtype; y is rounded once, from double, to out_dtype.  The residual
+ * is computed and stored exactly as above, in dtype.  out may be NULL; it
+ * may alias an input exactly only when out_dtype == dtype.
+ */
+int rmsnorm_oracle_ex(void* out, int out_dtype, double* y_f64, void* residual,
+                      const void* const* partials, int k, int dtype,
+                      const void* gamma, int gamma_dtype, int64_t rows, int64_t hidden,
+                      float eps, double* rstd_out);
+
+/*
  * rmsnorm_oracle_round -- round n doubles to dtype (nearest, ties to even,
  * overflow to +-inf, NaN to quiet NaN) and store them; exposes the oracle's
  * converter so that it can be pinned against independent converters.

@@ -78,6 +78,11 @@ class Library:
         lib.rmsnorm_oracle_f64.argtypes = [vp, dp, vp, ctypes.POINTER(vp), ctypes.c_int, vp,
                                            i64, i64, ctypes.c_float, ctypes.c_int, dp]
         lib.rmsnorm_oracle_f64.restype = ctypes.c_int
+        if hasattr(lib, "rmsnorm_oracle_ex"):
+            ci = ctypes.c_int
+            lib.rmsnorm_oracle_ex.argtypes = [vp, ci, dp, vp, ctypes.POINTER(vp), ci, ci, vp, ci,
+                                              i64, i64, ctypes.c_float, dp]
+            lib.rmsnorm_oracle_ex.restype = ctypes.c_int
         lib.rmsnorm_oracle_round.argtypes = [vp, dp, i64, ctypes.c_int]
         lib.rmsnorm_oracle_round.restype = ctypes.c_int
         lib.rmsnorm_oracle_decode.argtypes = [dp, vp, i64, ctypes.c_int]
@@ -139,42 +144,69 @@ def _raise(rc: int):
         raise RuntimeError(f"rmsnorm_oracle failed: {rc} ({_ERRORS.get(rc, 'unknown')})")
 
 
+def _general(out, y64, res, parts, gamma, rows, hidden, eps, dtype, gamma_dtype, out_dtype,
+             rstd, lib):
+    k = len(parts)
+    arr = (ctypes.c_void_p * max(k, 1))(*[p.ctypes.data for p in parts])
+    rc = _load(lib).rmsnorm_oracle_ex(_ptr(out), DTYPE_CODE[out_dtype], _dptr(y64),
+                                      None if res is None else _ptr(res), arr, k,
+                                      DTYPE_CODE[dtype], _ptr(gamma), DTYPE_CODE[gamma_dtype],
+                                      rows, hidden, ctypes.c_float(eps), _dptr(rstd))
+    _raise(rc)
+
+
 def rmsnorm(x: np.ndarray, gamma: np.ndarray, eps: float, dtype: str, *,
+            gamma_dtype: str = None, out_dtype: str = None,
             want_f64: bool = False, lib: "Library | None" = None):
     """Plain RMSNorm of x[rows, hidden].  Returns (out, rstd[rows]) and, with
-    ``want_f64``, the unrounded double y as a third item."""
+    ``want_f64``, the unrounded double y as a third item.  gamma_dtype and
+    out_dtype default to dtype."""
+    gamma_dtype = gamma_dtype or dtype
+    out_dtype = out_dtype or dtype
     rows, hidden = x.shape
     _check(x, dtype)
-    _check(gamma, dtype, (hidden,))
-    out = np.empty_like(x)
+    _check(gamma, gamma_dtype, (hidden,))
+    out = np.empty((rows, hidden), dtype=_storage(out_dtype))
     rstd = np.empty(rows, dtype=np.float64)
     y64 = np.empty((rows, hidden), dtype=np.float64) if want_f64 else None
-    parts = (ctypes.c_void_p * 1)(x.ctypes.data)
-    rc = _load(lib).rmsnorm_oracle_f64(_ptr(out), _dptr(y64), None, parts, 1, _ptr(gamma),
-                                       rows, hidden, ctypes.c_float(eps), DTYPE_CODE[dtype],
-                                       _dptr(rstd))
-    _raise(rc)
+    if gamma_dtype == dtype and out_dtype == dtype:
+        parts = (ctypes.c_void_p * 1)(x.ctypes.data)
+        rc = _load(lib).rmsnorm_oracle_f64(_ptr(out), _dptr(y64), None, parts, 1, _ptr(gamma),
+                                           rows, hidden, ctypes.c_float(eps), DTYPE_CODE[dtype],
+                                           _dptr(rstd))
+        _raise(rc)
+    else:
+        _general(out, y64, None, [x], gamma, rows, hidden, eps, dtype, gamma_dtype, out_dtype,
+                 rstd, lib)
     return (out, rstd, y64) if want_f64 else (out, rstd)
 
 
 def add_rmsnorm(partials, residual: np.ndarray, gamma: np.ndarray, eps: float, dtype: str,
-                *, want_f64: bool = False, lib: "Library | None" = None):
+                *, gamma_dtype: str = None, out_dtype: str = None,
+                want_f64: bool = False, lib: "Library | None" = None):
     """Fused form.  ``residual`` is NOT modified; the oracle works on a copy.
-    Returns (out, new_residual, rstd) and, with ``want_f64``, the unrounded y."""
+    Returns (out, new_residual, rstd) and, with ``want_f64``, the unrounded y.
+    gamma_dtype and out_dtype default to dtype."""
+    gamma_dtype = gamma_dtype or dtype
+    out_dtype = out_dtype or dtype
     rows, hidden = residual.shape
     _check(residual, dtype)
-    _check(gamma, dtype, (hidden,))
+    _check(gamma, gamma_dtype, (hidden,))
     parts = [_check(p, dtype, (rows, hidden)) for p in partials]
     k = len(parts)
-    out = np.empty_like(residual)
+    out = np.empty((rows, hidden), dtype=_storage(out_dtype))
     res = residual.copy()
     rstd = np.empty(rows, dtype=np.float64)
     y64 = np.empty((rows, hidden), dtype=np.float64) if want_f64 else None
-    arr = (ctypes.c_void_p * max(k, 1))(*[p.ctypes.data for p in parts])
-    rc = _load(lib).rmsnorm_oracle_f64(_ptr(out), _dptr(y64), _ptr(res), arr, k, _ptr(gamma),
-                                       rows, hidden, ctypes.c_float(eps), DTYPE_CODE[dtype],
-                                       _dptr(rstd))
-    _raise(rc)
+    if gamma_dtype == dtype and out_dtype == dtype:
+        arr = (ctypes.c_void_p * max(k, 1))(*[p.ctypes.data for p in parts])
+        rc = _load(lib).rmsnorm_oracle_f64(_ptr(out), _dptr(y64), _ptr(res), arr, k,
+                                           _ptr(gamma), rows, hidden, ctypes.c_float(eps),
+                                           DTYPE_CODE[dtype], _dptr(rstd))
+        _raise(rc)
+    else:
+        _general(out, y64, res, parts, gamma, rows, hidden, eps, dtype, gamma_dtype, out_dtype,
+                 rstd, lib)
     return (out, res, rstd, y64) if want_f64 else (out, res, rstd)
 
 

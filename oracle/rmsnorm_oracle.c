@@ -25,7 +25,11 @@
  *   - everything after the residual is computed in double and y is rounded
  *     once, to nearest with ties to even, to the output dtype;
  *   - eps enters as the float argument widened to double, added after the
- *     mean and inside the square root; the order is (v * inv) * gamma.
+ *     mean and inside the square root; the order is (v * inv) * gamma;
+ *   - in the general form (rmsnorm_oracle_ex) gamma may have its own dtype
+ *     (read exactly) and y is rounded once to its own output dtype; the rows
+ *     are still [..., hidden] with the hidden dimension contiguous, as page
+ *     "RMSNorm kernel" section 2 states the input shape.
  *
  * Build: gcc -O2 -fPIC -shared -ffp-contract=off -fno-fast-math (no FMA
  * contraction, no reassociation, binary32 adds stay binary32 on x86-64 SSE).
@@ -156,11 +160,12 @@ int rmsnorm_oracle_decode(double* dst, const void* src, int64_t n, int dtype) {
     return RMSNORM_ORACLE_OK;
 }
 
-int rmsnorm_oracle_f64(void* out, double* y_f64, void* residual,
-                       const void* const* partials, int k, const void* gamma,
-                       int64_t rows, int64_t hidden, float eps, int dtype,
-                       double* rstd_out) {
-    if (!fmt_of(dtype)) return RMSNORM_ORACLE_ERR_DTYPE;
+int rmsnorm_oracle_ex(void* out, int out_dtype, double* y_f64, void* residual,
+                      const void* const* partials, int k, int dtype,
+                      const void* gamma, int gamma_dtype, int64_t rows, int64_t hidden,
+                      float eps, double* rstd_out) {
+    if (!fmt_of(dtype) || !fmt_of(out_dtype) || !fmt_of(gamma_dtype))
+        return RMSNORM_ORACLE_ERR_DTYPE;
     if (rows < 0 || hidden < 1) return RMSNORM_ORACLE_ERR_SHAPE;
     if (k < 1 || k > RMSNORM_ORACLE_KMAX) return RMSNORM_ORACLE_ERR_K;
     if (!residual && k != 1) return RMSNORM_ORACLE_ERR_K;
@@ -184,7 +189,8 @@ int rmsnorm_oracle_f64(void* out, double* y_f64, void* residual,
                 continue;
             }
             /* binary32 sum in the order p_0, ..., p_{k-1}, r; every dtype
-             * value converts to float exactly. */
+             * value converts to float exactly.  The residual keeps the data
+             * dtype whatever the output dtype is. */
             float acc = (float)load(partials[0], base + j, dtype);
             for (int q = 1; q < k; ++q) acc = acc + (float)load(partials[q], base + j, dtype);
             acc = acc + (float)load(residual, base + j, dtype);
@@ -202,15 +208,24 @@ int rmsnorm_oracle_f64(void* out, double* y_f64, void* residual,
         double inv = 1.0 / sqrt(ms + (double)eps);
         if (rstd_out) rstd_out[i] = inv;
 
-        /* Step 4: y = (v * inv) * gamma, rounded once. */
+        /* Step 4: y = (v * inv) * gamma (gamma read exactly in its own
+         * dtype), rounded once to the output dtype. */
         for (int64_t j = 0; j < hidden; ++j) {
-            double y = (v[j] * inv) * load(gamma, j, dtype);
+            double y = (v[j] * inv) * load(gamma, j, gamma_dtype);
             if (y_f64) y_f64[base + j] = y;
-            if (out) store_rounded(out, base + j, y, dtype);
+            if (out) store_rounded(out, base + j, y, out_dtype);
         }
     }
     free(v);
     return RMSNORM_ORACLE_OK;
+}
+
+int rmsnorm_oracle_f64(void* out, double* y_f64, void* residual,
+                       const void* const* partials, int k, const void* gamma,
+                       int64_t rows, int64_t hidden, float eps, int dtype,
+                       double* rstd_out) {
+    return rmsnorm_oracle_ex(out, dtype, y_f64, residual, partials, k, dtype, gamma, dtype,
+                             rows, hidden, eps, rstd_out);
 }
 
 int rmsnorm_oracle(void* out, void* residual, const void* const* partials, int k,

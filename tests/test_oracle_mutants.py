@@ -45,7 +45,11 @@ MUTANTS = {
     "no_subnormal_binade": [("if (e < f->emin) e = f->emin;", "")],
     "double_rounding_via_float": [("store_exact(base, idx, round_to(v, fmt_of(dtype)), dtype);",
                                    "store_exact(base, idx, round_to((double)(float)v, fmt_of(dtype)), dtype);")],
-    "gamma_off_by_one": [("* load(gamma, j, dtype);", "* load(gamma, (j + 1) % hidden, dtype);")],
+    "gamma_off_by_one": [("* load(gamma, j, gamma_dtype);",
+                          "* load(gamma, (j + 1) % hidden, gamma_dtype);")],
+    "gamma_read_in_data_dtype": [("* load(gamma, j, gamma_dtype);", "* load(gamma, j, dtype);")],
+    "output_rounded_via_data_dtype": [("if (out) store_rounded(out, base + j, y, out_dtype);",
+                                       "if (out) store_rounded(out, base + j, round_to(y, f), out_dtype);")],
     "float_sum_of_squares": [("double ss = 0.0;", "float ss = 0.0f;")],
     "last_element_dropped": [("for (int64_t j = 0; j < hidden; ++j) ss += v[j] * v[j];",
                               "for (int64_t j = 0; j + 1 < hidden; ++j) ss += v[j] * v[j];")],
@@ -55,7 +59,7 @@ MUTANTS = {
 
 # cheap, discriminating pins first
 ORDER = ["special_cases", "torch_rms_norm", "residual", "scale", "gamma_one", "brute_force",
-         "constant_row", "converters"]
+         "constant_row", "converters", "general_dtypes"]
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))

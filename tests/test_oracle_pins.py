@@ -337,6 +337,72 @@ def pin_converters(lib=None):
         assert ok.all() and np.array_equal(np.signbit(got), np.signbit(want))
 
 
+# P9: the general form -- gamma and the output each in their own dtype.  A
+# constant row against the closed form, with gamma values that need fp32's
+# full significand, and the rounded output against exact rational rounding to
+# the output dtype; torch's RMSNorm in float64 with the wider gamma; every
+# output element against an independent converter (numpy for f32 and f16,
+# exact rationals for bf16); the residual, which keeps the data dtype,
+# against numpy's binary32 sequential sum rounded by torch.
+
+GENERAL = [(d, g, o) for d in DTYPES for g in sorted({d, "f32"}) for o in DTYPES
+           if (g, o) != (d, d)]
+
+
+def _round_indep(y: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "f32":
+        return y.astype(np.float32)
+    if dtype == "f16":
+        return y.astype(np.float16).view(np.uint16)
+    out = np.empty(y.shape, np.uint16)
+    for idx, v in np.ndenumerate(y):
+        r, _ = ind.exact_round(Fraction(float(v)), "bf16")
+        out[idx] = ind.storage_of(math.copysign(float(r), v) if r == 0 else float(r), "bf16")
+    return out
+
+
+def pin_general_dtypes(lib=None, combos=GENERAL):
+    rng = np.random.default_rng(9)
+    for dtype, gd, od in combos:
+        H = 97
+        for c0 in (0.3, -3e3):
+            c = float(torch.tensor(c0).to(torch.bfloat16).to(torch.float64))
+            x = to_storage_vals(np.full((2, H), c), dtype)
+            g = rand_storage(rng, (H,), gd)
+            out, rstd, y64 = oracle.rmsnorm(x, g, 1e-6, dtype, gamma_dtype=gd, out_dtype=od,
+                                            want_f64=True, lib=lib)
+            assert out.dtype == (np.float32 if od == "f32" else np.uint16), (dtype, gd, od)
+            gv = ind.decode_np(g, gd)
+            cq = Fraction(c)
+            inv = 1 / ind.sqrt_dec(cq * cq + Fraction(float(np.float32(1e-6))))
+            for j in range(H):
+                exact = ind.dec(cq) * inv * ind.dec(Fraction(float(gv[j])))
+                assert ind.isclose_rel(y64[0, j], float(exact), 2e-15), (dtype, gd, od, c, j)
+                r, tie = ind.exact_round(Fraction(exact), od)
+                if ind.storage_of(r, od) != out[1, j]:
+                    assert tie < Fraction(1, 10 ** 9), (dtype, gd, od, c, j)
+        R, H = 3, 300
+        ps = [rand_storage(rng, (R, H), dtype) for _ in range(2)]
+        r = rand_storage(rng, (R, H), dtype)
+        g = rand_storage(rng, (H,), gd)
+        out, rnew, _, y = oracle.add_rmsnorm(ps, r, g, 1e-5, dtype, gamma_dtype=gd,
+                                             out_dtype=od, want_f64=True, lib=lib)
+        want = torch.nn.functional.rms_norm(torch.from_numpy(ind.decode_np(rnew, dtype)), [H],
+                                            torch.from_numpy(ind.decode_np(g, gd)),
+                                            float(np.float32(1e-5)))
+        np.testing.assert_allclose(y, want.numpy(), rtol=1e-12, atol=0)
+        assert np.array_equal(ind.storage_bits(out, od), ind.storage_bits(_round_indep(y, od), od)), \
+            (dtype, gd, od)
+        acc = ind.decode_np(ps[0], dtype).astype(np.float32) + \
+            ind.decode_np(ps[1], dtype).astype(np.float32)
+        acc = acc + ind.decode_np(r, dtype).astype(np.float32)
+        t = torch.from_numpy(acc)
+        wr = t.numpy() if dtype == "f32" else \
+            t.to(TORCH[dtype]).view(torch.int16).numpy().view(np.uint16)
+        assert np.array_equal(ind.storage_bits(rnew, dtype), ind.storage_bits(wr, dtype)), \
+            (dtype, gd, od)
+
+
 PINS = {
     "constant_row": pin_constant_row,
     "gamma_one": pin_gamma_one_invariant,
@@ -346,6 +412,7 @@ PINS = {
     "torch_rms_norm": pin_torch_rms_norm,
     "residual": pin_residual,
     "converters": pin_converters,
+    "general_dtypes": pin_general_dtypes,
 }
 
 
