@@ -21,7 +21,7 @@
  * squares is accumulated in fp32; y is computed in fp32 as (r * inv) * gamma
  * and rounded once to the output dtype.  fp32 denormals are preserved.
  *
- * Conventions for every entry point:
+ * Conventions for every entry point (the *_ex forms below relax the first):
  *   - All data pointers are DEVICE pointers to contiguous row-major tensors;
  *     row i occupies elements [i*hidden, (i+1)*hidden).  gamma is [hidden].
  *     All tensors share one dtype (RMSN_F32, RMSN_F16, RMSN_BF16).
@@ -92,6 +92,47 @@ int add_rmsnorm_fwd(void* out, void* residual, const void* const* partials, int 
                     const void* gamma, int64_t rows, int64_t hidden, float eps, int dtype,
                     void* stream);
 
+/*
+ * The general interface -- page "RMSNorm kernel", section 2, which states the
+ * input as [..., hidden_dim]: any number of leading dimensions flattened into
+ * rows, the hidden dimension contiguous.  Beyond rmsnorm_fwd /
+ * add_rmsnorm_fwd it allows:
+ *   - a row stride per tensor, in ELEMENTS of that tensor's dtype (row i of
+ *     a tensor starts i * stride elements after its base).  A stride must be
+ *     >= hidden when rows > 1 (RMSN_ERR_SHAPE otherwise); views that skip
+ *     rows or columns of a larger buffer are accepted as they are;
+ *   - gamma in fp32 (gamma_dtype RMSN_F32) with fp16 / bf16 data, or in the
+ *     data dtype (any other gamma dtype is RMSN_ERR_DTYPE);
+ *   - an output dtype of its own (any of the three).  y is computed in fp32
+ *     exactly as above and rounded once to the output dtype.
+ * The data (x, partials, residual) share `dtype`; the residual is stored in
+ * it, bit-exact as above.  Everything else is as for the plain entry points:
+ * device pointers, nothing allocated, asynchronous on `stream`, validation
+ * before launch.  Aliasing: out may be exactly an input (same base, same
+ * stride) only when out_dtype == dtype; any other shared byte between out
+ * and an input, the residual or gamma, or between the residual and a
+ * partial or gamma, is RMSN_ERR_ALIAS (rows of equal stride that interleave
+ * without sharing bytes do not overlap).  With 16-byte chunks of data, each
+ * tensor's base and row pitch must be aligned to its own access width (16
+ * bytes, or E elements of its dtype when narrower); otherwise narrower
+ * chunks are used, with the same numerics.
+ */
+
+/* rmsnorm_fwd_ex -- plain RMSNorm, general layout and dtypes. */
+int rmsnorm_fwd_ex(void* out, int64_t out_stride, int out_dtype, const void* x, int64_t x_stride,
+                   int dtype, const void* gamma, int gamma_dtype, int64_t rows, int64_t hidden,
+                   float eps, void* stream);
+
+/*
+ * add_rmsnorm_fwd_ex -- fused form, general layout and dtypes.
+ * partial_strides is a HOST array of k strides (copied at the call), or NULL
+ * for partials of stride hidden.
+ */
+int add_rmsnorm_fwd_ex(void* out, int64_t out_stride, int out_dtype, void* residual,
+                       int64_t residual_stride, const void* const* partials,
+                       const int64_t* partial_strides, int k, int dtype, const void* gamma,
+                       int gamma_dtype, int64_t rows, int64_t hidden, float eps, void* stream);
+
 /* Static description of an error code (never NULL). */
 const char* rmsnorm_strerror(int code);
 
@@ -119,6 +160,12 @@ int rmsnorm_plan(int64_t rows, int64_t hidden, int k, int dtype, int align, char
  * Both exist for tuning and testing; unset, the dispatcher decides.
  */
 int rmsnorm_variants(int dtype, char* buf, int buflen);
+
+/* rmsnorm_plan_ex / rmsnorm_variants_ex -- the same for the general
+ * interface's dtype combinations (contiguous rows for the plan). */
+int rmsnorm_plan_ex(int64_t rows, int64_t hidden, int k, int dtype, int gamma_dtype,
+                    int out_dtype, int align, char* buf, int buflen);
+int rmsnorm_variants_ex(int dtype, int gamma_dtype, int out_dtype, char* buf, int buflen);
 
 #ifdef __cplusplus
 }

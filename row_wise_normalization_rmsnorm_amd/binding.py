@@ -21,7 +21,8 @@ DTYPE_CODE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 DTYPE_NAME = {"f32": 0, "f16": 1, "bf16": 2}
 KMAX = 16
 EXPORTS = ("rmsnorm_fwd", "add_rmsnorm_fwd", "rmsnorm_strerror", "rmsnorm_last_error",
-           "rmsnorm_plan", "rmsnorm_variants")
+           "rmsnorm_plan", "rmsnorm_variants", "rmsnorm_fwd_ex", "add_rmsnorm_fwd_ex",
+           "rmsnorm_plan_ex", "rmsnorm_variants_ex")
 BLOCK_SUM_EXPORTS = ("block_all_reduce_sum",)
 
 # block all-reduce sum (include/block_sum.h)
@@ -64,6 +65,18 @@ def lib() -> ctypes.CDLL:
             l.rmsnorm_plan.restype = c_int
             l.rmsnorm_variants.argtypes = [c_int, ctypes.c_char_p, c_int]
             l.rmsnorm_variants.restype = c_int
+            l.rmsnorm_fwd_ex.argtypes = [vp, i64, c_int, vp, i64, c_int, vp, c_int, i64, i64,
+                                         c_float, vp]
+            l.rmsnorm_fwd_ex.restype = c_int
+            l.add_rmsnorm_fwd_ex.argtypes = [vp, i64, c_int, vp, i64, ctypes.POINTER(vp),
+                                             ctypes.POINTER(i64), c_int, c_int, vp, c_int, i64, i64,
+                                             c_float, vp]
+            l.add_rmsnorm_fwd_ex.restype = c_int
+            l.rmsnorm_plan_ex.argtypes = [i64, i64, c_int, c_int, c_int, c_int, c_int,
+                                          ctypes.c_char_p, c_int]
+            l.rmsnorm_plan_ex.restype = c_int
+            l.rmsnorm_variants_ex.argtypes = [c_int, c_int, c_int, ctypes.c_char_p, c_int]
+            l.rmsnorm_variants_ex.restype = c_int
             l.block_all_reduce_sum.argtypes = [vp, vp, i64, c_int, vp, i64, vp]
             l.block_all_reduce_sum.restype = c_int
             _lib = l
@@ -135,6 +148,94 @@ def add_rmsnorm_fwd(out: torch.Tensor, residual: torch.Tensor, partials: Sequenc
                                  DTYPE_CODE[residual.dtype], _stream(residual, stream)))
 
 
+def row_view(t: torch.Tensor, what: str):
+    """(rows, hidden, row stride in elements) of a [..., hidden] device tensor
+    whose last dimension is contiguous and whose leading dimensions collapse
+    into one row stride (page "RMSNorm kernel", section 2: inputs are
+    [..., hidden_dim]).  Anything else raises: the binding never copies."""
+    if not t.is_cuda:
+        raise RmsnormError(-1, f"{what} must be a device tensor")
+    if t.dim() == 0:
+        return 1, 1, 1
+    hidden = t.shape[-1]
+    if hidden > 1 and t.stride(-1) != 1:
+        raise RmsnormError(-2, f"{what}: the last dimension must be contiguous")
+    rows = 1
+    for n in t.shape[:-1]:
+        rows *= n
+    lead = [(n, st) for n, st in zip(t.shape[:-1], t.stride()[:-1]) if n != 1]
+    if not lead or rows == 0:
+        return rows, hidden, max(hidden, 1)
+    stride = lead[-1][1]
+    for (n0, s0), (n1, s1) in zip(lead[:-1], lead[1:]):
+        if s0 != s1 * n1:
+            raise RmsnormError(-2, f"{what}: leading dimensions {tuple(t.shape[:-1])} with strides "
+                                   f"{tuple(t.stride()[:-1])} do not form one row stride")
+    return rows, hidden, stride
+
+
+def rmsnorm_fwd_ex(out: torch.Tensor, x: torch.Tensor, gamma: torch.Tensor, eps: float,
+                   stream=None) -> None:
+    """out[..., H] = RMSNorm(x[..., H]) * gamma[H], general form: x and out
+    are any [..., H] views with a contiguous last dimension (each with its
+    own row stride), gamma is float32 or x's dtype, out any of the three
+    dtypes."""
+    rows, hidden, xs = row_view(x, "x")
+    orows, ohidden, os_ = row_view(out, "out")
+    if (orows, ohidden) != (rows, hidden) or gamma.numel() != hidden:
+        raise RmsnormError(-2, f"shape mismatch: out {tuple(out.shape)} x {tuple(x.shape)} "
+                               f"gamma {tuple(gamma.shape)}")
+    for t, n in ((x, "x"), (out, "out"), (gamma, "gamma")):
+        if t.dtype not in DTYPE_CODE:
+            raise RmsnormError(-3, f"{n}: dtype {t.dtype} is not f32/f16/bf16")
+    _check(lib().rmsnorm_fwd_ex(out.data_ptr(), os_, DTYPE_CODE[out.dtype], x.data_ptr(), xs,
+                                DTYPE_CODE[x.dtype], _dev_ptr(gamma, "gamma"),
+                                DTYPE_CODE[gamma.dtype], rows, hidden, float(eps),
+                                _stream(x, stream)))
+
+
+def add_rmsnorm_fwd_ex(out: torch.Tensor, residual: torch.Tensor, partials: Sequence[torch.Tensor],
+                       gamma: torch.Tensor, eps: float, stream=None) -> None:
+    """Fused form, general layout: residual <- round(p0 + ... + residual) in
+    place (in the residual's dtype, which the partials share); out =
+    RMSNorm(residual) * gamma in out's dtype.  Every tensor may be a
+    [..., H] view with its own row stride."""
+    rows, hidden, rs = row_view(residual, "residual")
+    orows, ohidden, os_ = row_view(out, "out")
+    k = len(partials)
+    views = [row_view(p, f"partials[{i}]") for i, p in enumerate(partials)]
+    if (orows, ohidden) != (rows, hidden) or gamma.numel() != hidden or \
+            any(v[:2] != (rows, hidden) for v in views):
+        raise RmsnormError(-2, "shape mismatch between out, residual, partials and gamma")
+    if any(p.dtype != residual.dtype for p in partials) or \
+            any(t.dtype not in DTYPE_CODE for t in (out, residual, gamma)):
+        raise RmsnormError(-3, "partials must share the residual's dtype; dtypes f32/f16/bf16")
+    arr = (ctypes.c_void_p * max(k, 1))(*[p.data_ptr() for p in partials])
+    strides = (ctypes.c_int64 * max(k, 1))(*[v[2] for v in views])
+    _check(lib().add_rmsnorm_fwd_ex(out.data_ptr(), os_, DTYPE_CODE[out.dtype],
+                                    residual.data_ptr(), rs, arr, strides, k,
+                                    DTYPE_CODE[residual.dtype], _dev_ptr(gamma, "gamma"),
+                                    DTYPE_CODE[gamma.dtype], rows, hidden, float(eps),
+                                    _stream(residual, stream)))
+
+
+def rmsnorm_plan_ex(rows: int, hidden: int, k: int, dtype: str, gamma_dtype: str,
+                    out_dtype: str, align: int = 16) -> str:
+    buf = ctypes.create_string_buffer(128)
+    _check(lib().rmsnorm_plan_ex(rows, hidden, k, DTYPE_NAME[dtype], DTYPE_NAME[gamma_dtype],
+                                 DTYPE_NAME[out_dtype], int(align), buf, 128))
+    return buf.value.decode()
+
+
+def rmsnorm_variants_ex(dtype: str, gamma_dtype: str, out_dtype: str) -> list:
+    buf = ctypes.create_string_buffer(1 << 16)
+    n = lib().rmsnorm_variants_ex(DTYPE_NAME[dtype], DTYPE_NAME[gamma_dtype],
+                                  DTYPE_NAME[out_dtype], buf, 1 << 16)
+    if n < 0:
+        _check(n)
+    return [s for s in buf.value.decode().split("\n") if s]
+
+
 def rmsnorm_plan(rows: int, hidden: int, k: int, dtype: str, align: int = 16) -> str:
     """Name of the kernel variant the dispatcher picks (k = 0: plain; align:
     the alignment in bytes shared by every base pointer)."""
@@ -196,14 +297,27 @@ def block_all_reduce_sum(x: torch.Tensor) -> torch.Tensor:
 
 # convenience wrappers ------------------------------------------------------
 
-def rmsnorm(x: torch.Tensor, gamma: torch.Tensor, eps: float = 1e-6) -> torch.Tensor:
-    out = torch.empty_like(x)
-    rmsnorm_fwd(out, x, gamma, eps)
+def rmsnorm(x: torch.Tensor, gamma: torch.Tensor, eps: float = 1e-6,
+            out_dtype: Optional[torch.dtype] = None) -> torch.Tensor:
+    """RMSNorm of a [..., H] tensor into a new contiguous tensor (of
+    out_dtype, default x's)."""
+    out = torch.empty(x.shape, dtype=out_dtype or x.dtype, device=x.device)
+    if x.is_contiguous() and out.dtype == x.dtype == gamma.dtype:
+        rmsnorm_fwd(out, x, gamma, eps)
+    else:
+        rmsnorm_fwd_ex(out, x, gamma, eps)
     return out
 
 
 def add_rmsnorm(partials: Sequence[torch.Tensor], residual: torch.Tensor, gamma: torch.Tensor,
-                eps: float = 1e-6) -> torch.Tensor:
-    out = torch.empty_like(residual)
-    add_rmsnorm_fwd(out, residual, partials, gamma, eps)
+                eps: float = 1e-6, out_dtype: Optional[torch.dtype] = None) -> torch.Tensor:
+    """Fused form; residual is updated in place, the normalised rows are
+    returned in a new contiguous tensor (of out_dtype, default residual's)."""
+    out = torch.empty(residual.shape, dtype=out_dtype or residual.dtype, device=residual.device)
+    simple = residual.is_contiguous() and all(p.is_contiguous() for p in partials) and \
+        out.dtype == residual.dtype == gamma.dtype
+    if simple:
+        add_rmsnorm_fwd(out, residual, partials, gamma, eps)
+    else:
+        add_rmsnorm_fwd_ex(out, residual, partials, gamma, eps)
     return out

@@ -1,4 +1,4 @@
-// kernels_f16.hip -- every kernel variant for f16 storage.
+// kernels_f16.hip -- every kernel variant for fp16 data.
 #include "rmsnorm_table.hpp"
 
-RMSN_DEFINE_TABLE(_Float16, 1, f16)
+RMSN_DEFINE_TABLE(f16, rmsn::add_full<_Float16>(v, rmsn::Types{1, 1, 1}))

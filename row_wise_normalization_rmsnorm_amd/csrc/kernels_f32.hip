@@ -1,4 +1,4 @@
-// kernels_f32.hip -- every kernel variant for f32 storage.
+// kernels_f32.hip -- every kernel variant for fp32 data.
 #include "rmsnorm_table.hpp"
 
-RMSN_DEFINE_TABLE(float, 0, f32)
+RMSN_DEFINE_TABLE(f32, rmsn::add_full<float>(v, rmsn::Types{0, 0, 0}))

@@ -18,6 +18,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
+
 #include "../../include/rmsnorm.h"
 #include "rmsnorm_kernels.hpp"
 #include "rmsnorm_variants.hpp"
@@ -25,6 +27,9 @@
 const rmsn::Variant* rmsn_table_f32(int* n);
 const rmsn::Variant* rmsn_table_f16(int* n);
 const rmsn::Variant* rmsn_table_bf16(int* n);
+const rmsn::Variant* rmsn_table_mixed_f32(int* n);
+const rmsn::Variant* rmsn_table_mixed_f16(int* n);
+const rmsn::Variant* rmsn_table_mixed_bf16(int* n);
 
 namespace {
 
@@ -39,6 +44,7 @@ int fail(int code, const char* fmt, ...) {
 }
 
 int dtype_size(int dtype) { return dtype == RMSN_F32 ? 4 : 2; }
+bool known(int dtype) { return dtype == RMSN_F32 || dtype == RMSN_F16 || dtype == RMSN_BF16; }
 
 // LDS budget for staging one row in the streaming kernel.  64 KiB keeps at
 // least two workgroups resident per CU (160 KiB of LDS per CU on gfx950).
@@ -51,25 +57,50 @@ constexpr int64_t kVgprMaxHidden = 8192;
 // streaming kernel (fewer registers per thread than holding K+1 chunk sets).
 constexpr int64_t kStreamMinBytesForK = 8192;
 
-const rmsn::Variant* table_for(int dtype, int* n) {
-  switch (dtype) {
-    case RMSN_F32: return rmsn_table_f32(n);
-    case RMSN_F16: return rmsn_table_f16(n);
-    case RMSN_BF16: return rmsn_table_bf16(n);
-    default: *n = 0; return nullptr;
+// dtypes of one call: data (partials, residual, x), gamma, output
+struct Types {
+  int d, g, o;
+  bool single() const { return g == d && o == d; }
+};
+
+// Alignment (largest power of two, capped at 16) shared by the base and the
+// row pitch of every tensor in a role: data, gamma, output.
+struct Aligns {
+  int in, g, out;
+};
+
+const rmsn::Variant* table_for(Types t, int* n) {
+  if (t.single()) {
+    switch (t.d) {
+      case RMSN_F32: return rmsn_table_f32(n);
+      case RMSN_F16: return rmsn_table_f16(n);
+      case RMSN_BF16: return rmsn_table_bf16(n);
+    }
+  } else {
+    switch (t.d) {
+      case RMSN_F32: return rmsn_table_mixed_f32(n);
+      case RMSN_F16: return rmsn_table_mixed_f16(n);
+      case RMSN_BF16: return rmsn_table_mixed_bf16(n);
+    }
   }
+  *n = 0;
+  return nullptr;
+}
+
+bool same_types(const rmsn::Variant& v, Types t) {
+  return v.dtype == t.d && v.gdtype == t.g && v.odtype == t.o;
 }
 
 // npt: chunks per thread (register kernel) or chunks in flight per step
 // (streaming kernel).
-const rmsn::Variant* find(int dtype, int kind, int vb, int tpr, int npt, int wgs, int kc, int lds,
+const rmsn::Variant* find(Types t, int kind, int vb, int tpr, int npt, int wgs, int kc, int lds,
                           int nt) {
   int n = 0;
-  const rmsn::Variant* t = table_for(dtype, &n);
+  const rmsn::Variant* tab = table_for(t, &n);
   for (int i = 0; i < n; ++i) {
-    const rmsn::Variant& v = t[i];
-    if (v.kind == kind && v.vb == vb && v.tpr == tpr && v.wgs == wgs && v.kc == kc &&
-        v.nt == nt &&
+    const rmsn::Variant& v = tab[i];
+    if (same_types(v, t) && v.kind == kind && v.vb == vb && v.tpr == tpr && v.wgs == wgs &&
+        v.kc == kc && v.nt == nt &&
         (kind == rmsn::kVgpr ? v.npt == npt : (v.lds_stage == lds && v.unroll == npt)))
       return &v;
   }
@@ -85,27 +116,40 @@ struct Plan {
   size_t lds_bytes;  // dynamic LDS
 };
 
-// The widest chunk (16, 8 or 4 bytes; 0 = element) that divides both the
-// row's byte length and the alignment every base pointer shares.
-int widest_chunk(int dtype, int64_t hidden, int align) {
-  const int s = dtype_size(dtype);
-  for (int vb = 16; vb > s; vb /= 2)
-    if (align >= vb && (hidden * s) % vb == 0) return vb;
+// Elements per chunk of a variant with access width vb over data dtype d.
+int64_t elems_per_chunk(int vb, int d) { return vb ? vb / dtype_size(d) : 1; }
+
+// Can chunks of vb bytes of data (E elements; E elements of gamma and of the
+// output) be used: the row splits into whole chunks, and every tensor's base
+// and row pitch are aligned to its own access width (16 bytes, or the chunk
+// when it is narrower)?
+bool width_ok(int vb, Types t, int64_t hidden, Aligns al) {
+  if (vb == 0) return true;
+  const int64_t e = elems_per_chunk(vb, t.d);
+  if (hidden % e != 0) return false;
+  auto need = [&](int dtype) { return (int)std::min<int64_t>(16, e * dtype_size(dtype)); };
+  return al.in >= vb && al.g >= need(t.g) && al.out >= need(t.o);
+}
+
+// The widest chunk (16, 8 or 4 bytes of data; 0 = element) that fits.
+int widest_chunk(Types t, int64_t hidden, Aligns al) {
+  for (int vb = 16; vb > dtype_size(t.d); vb /= 2)
+    if (width_ok(vb, t, hidden, al)) return vb;
   return 0;
 }
 
-int64_t chunks_of(const rmsn::Variant& v, int dtype, int64_t hidden) {
-  return v.vb ? hidden * dtype_size(dtype) / v.vb : hidden;
+int64_t chunks_of(const rmsn::Variant& v, int64_t hidden) {
+  return hidden / elems_per_chunk(v.vb, v.dtype);
 }
 
-// Can variant v run a call with these sizes and this base alignment?
-bool fits(const rmsn::Variant& v, int dtype, int64_t hidden, int k, int align) {
-  const int s = dtype_size(dtype);
-  if (v.dtype != dtype) return false;
-  if (v.vb && (align < v.vb || (hidden * s) % v.vb != 0)) return false;
+// Can variant v run a call with these sizes, dtypes and alignments?
+bool fits(const rmsn::Variant& v, Types t, int64_t hidden, int k, Aligns al) {
+  const int s = dtype_size(t.d);
+  if (!same_types(v, t)) return false;
+  if (!width_ok(v.vb, t, hidden, al)) return false;
   if (v.kind == rmsn::kVgpr) {
     if (v.kc != vgpr_kc(k) && !(v.kc == -1 && k > 0)) return false;
-    return chunks_of(v, dtype, hidden) <= (int64_t)v.tpr * v.npt;
+    return chunks_of(v, hidden) <= (int64_t)v.tpr * v.npt;
   }
   if (v.kc != stream_kc(k) && !(v.kc == -1 && k > 0)) return false;
   if (v.lds_stage && hidden * s > kLdsStageMax) return false;
@@ -116,22 +160,24 @@ bool fits(const rmsn::Variant& v, int dtype, int64_t hidden, int k, int align) {
 // into waves when they are short; streaming two-pass kernels above that
 // (LDS-staged while the row fits the stage budget), for K >= 2 on long rows,
 // and whenever 16-byte accesses do not fit the alignment or row length.
-// align: the largest power of two (capped at 16) dividing every base pointer.
-int choose(int dtype, int64_t hidden, int k, int align, Plan* plan) {
-  const int s = dtype_size(dtype);
-  const int vb = widest_chunk(dtype, hidden, align);
+// The general interface (other gamma or output dtypes) makes the same
+// choice among the shapes compiled for it, with runtime-K fused kernels.
+int choose(Types t, int64_t hidden, int k, Aligns al, Plan* plan) {
+  const int s = dtype_size(t.d);
+  const int vb = widest_chunk(t, hidden, al);
   const rmsn::Variant* v = nullptr;
 
   const char* forced = getenv("RMSNORM_VARIANT");
   if (forced && *forced) {
     int n = 0;
-    const rmsn::Variant* t = table_for(dtype, &n);
+    const rmsn::Variant* tab = table_for(t, &n);
     for (int i = 0; i < n && !v; ++i)
-      if (strcmp(t[i].name, forced) == 0) v = &t[i];
-    if (!v) return fail(RMSN_ERR_SHAPE, "RMSNORM_VARIANT=%s names no variant of this dtype", forced);
-    if (!fits(*v, dtype, hidden, k, align))
-      return fail(RMSN_ERR_SHAPE, "RMSNORM_VARIANT=%s cannot run hidden=%lld k=%d align=%d",
-                  forced, (long long)hidden, k, align);
+      if (same_types(tab[i], t) && strcmp(tab[i].name, forced) == 0) v = &tab[i];
+    if (!v)
+      return fail(RMSN_ERR_SHAPE, "RMSNORM_VARIANT=%s names no variant of these dtypes", forced);
+    if (!fits(*v, t, hidden, k, al))
+      return fail(RMSN_ERR_SHAPE, "RMSNORM_VARIANT=%s cannot run hidden=%lld k=%d", forced,
+                  (long long)hidden, k);
   } else if (vb == 16 && hidden <= kVgprMaxHidden &&
              !(k >= 2 && hidden * s >= kStreamMinBytesForK)) {
     // One 16-byte chunk per thread wherever a workgroup can cover the row:
@@ -147,7 +193,8 @@ int choose(int dtype, int64_t hidden, int k, int align, Plan* plan) {
       tpr = 512;
       wgs = 512;
     }
-    v = find(dtype, rmsn::kVgpr, 16, tpr, npt, wgs, vgpr_kc(k), 0, 1);
+    v = find(t, rmsn::kVgpr, 16, tpr, npt, wgs, vgpr_kc(k), 0, 1);
+    if (!v && k > 0) v = find(t, rmsn::kVgpr, 16, tpr, npt, wgs, -1, 0, 1);
   } else {
     // Streaming two-pass, LDS-staged while the row fits the stage budget.
     // Fused calls use the runtime-K form, which sums the partials one at a
@@ -158,45 +205,88 @@ int choose(int dtype, int64_t hidden, int k, int align, Plan* plan) {
     // and 2% on 16384-wide rows.
     const bool lds = hidden * s <= kLdsStageMax;
     const int svb = (lds && vb == 16) ? 8 : vb;
-    const int64_t C = svb ? hidden * s / svb : hidden;
+    const int64_t C = hidden / elems_per_chunk(svb, t.d);
     const int unr = svb == 16 ? 2 : 4;
     int wgs = 256;
     while (wgs < 1024 && (int64_t)wgs * unr < C) wgs *= 2;
-    v = find(dtype, rmsn::kStream, svb, wgs, unr, wgs, k == 0 ? 0 : -1, lds ? 1 : 0,
-             lds ? 1 : 0);
+    v = find(t, rmsn::kStream, svb, wgs, unr, wgs, k == 0 ? 0 : -1, lds ? 1 : 0, lds ? 1 : 0);
   }
   if (!v) return fail(RMSN_ERR_SHAPE, "no kernel variant for hidden=%lld k=%d", (long long)hidden, k);
   plan->v = v;
-  plan->chunks = (int)chunks_of(*v, dtype, hidden);
+  plan->chunks = (int)chunks_of(*v, hidden);
   plan->lds_bytes = (v->kind == rmsn::kStream && v->lds_stage) ? (size_t)hidden * s : 0;
   return RMSN_OK;
 }
 
-bool overlap(const void* a, size_t na, const void* b, size_t nb) {
-  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
-  return x < y + nb && y < x + na;
-}
-
-// Largest power of two, capped at 16, dividing the address.
-int align_of(const void* p) {
-  const uintptr_t u = (uintptr_t)p;
+// Largest power of two, capped at 16, dividing the value.
+int align_of_int(uint64_t u) {
   int a = 16;
-  while (a > 1 && (u & (uintptr_t)(a - 1))) a /= 2;
+  while (a > 1 && (u & (uint64_t)(a - 1))) a /= 2;
   return a;
 }
+int align_of(const void* p) { return align_of_int((uintptr_t)p); }
 
-int min_align(int a, const void* p) {
-  const int b = align_of(p);
-  return a < b ? a : b;
+// A tensor as the kernels see it: `rows` rows of `len` bytes, row r at
+// base + r * pitch bytes.
+struct Span {
+  const void* base;
+  int64_t pitch;  // bytes
+  int64_t len;    // bytes per row
+  int64_t rows;
+  int align() const { return std::min(align_of(base), rows > 1 ? align_of_int((uint64_t)pitch) : 16); }
+  int64_t extent() const { return (rows - 1) * pitch + len; }
+};
+
+int64_t floor_div(int64_t a, int64_t b) { return a / b - ((a % b != 0) && ((a < 0) != (b < 0))); }
+int64_t ceil_div(int64_t a, int64_t b) { return -floor_div(-a, b); }
+
+// Do two spans share a byte?  Exact for equal pitches that are at least
+// both row lengths (rows interleave); otherwise the extents are compared.
+bool overlap(const Span& a, const Span& b) {
+  const intptr_t x = (intptr_t)a.base, y = (intptr_t)b.base;
+  if (!(x < y + b.extent() && y < x + a.extent())) return false;
+  if (a.pitch == b.pitch && a.rows > 1 && b.rows > 1 && a.pitch >= a.len && a.pitch >= b.len) {
+    // row i of a is [x + i p, x + i p + la), row j of b is [y + j p, ...);
+    // they meet iff d + t p lies in (-lb, la) for d = y - x, t = j - i.
+    const int64_t p = a.pitch, d = (int64_t)(y - x);
+    int64_t lo = floor_div(-b.len - d, p) + 1, hi = ceil_div(a.len - d, p) - 1;
+    lo = std::max(lo, -(b.rows - 1));
+    hi = std::min(hi, a.rows - 1);
+    return lo <= hi;
+  }
+  return true;
+}
+
+bool same_span(const Span& a, const Span& b) {
+  return a.base == b.base && a.pitch == b.pitch && a.len == b.len;
 }
 
 int common_checks(int dtype, int64_t rows, int64_t hidden, float eps) {
-  if (dtype != RMSN_F32 && dtype != RMSN_F16 && dtype != RMSN_BF16)
-    return fail(RMSN_ERR_DTYPE, "unknown dtype %d", dtype);
+  if (!known(dtype)) return fail(RMSN_ERR_DTYPE, "unknown dtype %d", dtype);
   if (rows < 0 || hidden < 1 || hidden > RMSN_MAX_HIDDEN)
     return fail(RMSN_ERR_SHAPE, "rows=%lld hidden=%lld out of range", (long long)rows,
                 (long long)hidden);
   if (!(eps >= 0.0f) || isinf(eps)) return fail(RMSN_ERR_EPS, "eps=%g must be finite and >= 0", eps);
+  return RMSN_OK;
+}
+
+int type_checks(Types t) {
+  if (!known(t.d) || !known(t.o)) return fail(RMSN_ERR_DTYPE, "unknown dtype %d / %d", t.d, t.o);
+  if (t.g != t.d && t.g != RMSN_F32)
+    return fail(RMSN_ERR_DTYPE, "gamma dtype %d must be the data dtype %d or RMSN_F32", t.g, t.d);
+  return RMSN_OK;
+}
+
+// Row stride (elements) of a tensor: at least hidden when rows > 1, and the
+// last row's end must be addressable.
+int stride_check(const char* what, int64_t stride, int64_t rows, int64_t hidden, int size) {
+  if (rows <= 1) return RMSN_OK;
+  if (stride < hidden)
+    return fail(RMSN_ERR_SHAPE, "%s row stride %lld < hidden %lld", what, (long long)stride,
+                (long long)hidden);
+  if (stride > (INT64_MAX / size - hidden) / (rows - 1))
+    return fail(RMSN_ERR_SHAPE, "%s row stride %lld overflows the address range", what,
+                (long long)stride);
   return RMSN_OK;
 }
 
@@ -219,6 +309,100 @@ int launch(const Plan& plan, rmsn::RowArgs a, void* stream) {
   return RMSN_OK;
 }
 
+// Both forms, every dtype combination and stride: validate, choose, launch.
+// residual == nullptr is plain RMSNorm (k == 1, partials[0] is x).  Strides
+// are in elements of each tensor's own dtype.
+int run(Types t, void* out, int64_t out_stride, void* residual, int64_t res_stride,
+        const void* const* partials, const int64_t* part_strides, int k, const void* gamma,
+        int64_t rows, int64_t hidden, float eps, void* stream) {
+  int rc = common_checks(t.d, rows, hidden, eps);
+  if (rc) return rc;
+  if ((rc = type_checks(t))) return rc;
+  const bool fused = residual != nullptr;
+  if (k < 1 || k > RMSN_KMAX) return fail(RMSN_ERR_K, "k=%d outside [1, %d]", k, RMSN_KMAX);
+  if (rows == 0) return RMSN_OK;
+  if (!out || !gamma || !partials) return fail(RMSN_ERR_NULL, "out, inputs and gamma must be non-NULL");
+  const int sd = dtype_size(t.d), so = dtype_size(t.o), sg = dtype_size(t.g);
+  if ((rc = stride_check("out", out_stride, rows, hidden, so))) return rc;
+  if (fused && (rc = stride_check("residual", res_stride, rows, hidden, sd))) return rc;
+  const Span o{out, out_stride * so, hidden * so, rows};
+  const Span g{gamma, hidden * sg, hidden * sg, 1};
+  const Span r{residual, res_stride * sd, hidden * sd, rows};
+  Aligns al{16, align_of(gamma), o.align()};
+  if (fused) al.in = r.align();
+  rmsn::RowArgs a{};
+  for (int j = 0; j < k; ++j) {
+    char nm[32] = "x";
+    if (fused) snprintf(nm, sizeof(nm), "partials[%d]", j);
+    if (!partials[j]) return fail(RMSN_ERR_NULL, "%s is NULL", nm);
+    const int64_t st = part_strides ? part_strides[j] : hidden;
+    if ((rc = stride_check(nm, st, rows, hidden, sd))) return rc;
+    const Span p{partials[j], st * sd, hidden * sd, rows};
+    if (fused && overlap(r, p)) return fail(RMSN_ERR_ALIAS, "residual overlaps %s", nm);
+    // out may be exactly an input (in place) when it has the input's dtype
+    // and layout; any other overlap would let one thread's store reach
+    // elements another thread has not read yet.
+    if (overlap(o, p) && !(t.o == t.d && same_span(o, p)))
+      return fail(RMSN_ERR_ALIAS, "out partially overlaps %s", nm);
+    al.in = std::min(al.in, p.align());
+    a.partials.p[j] = partials[j];
+    a.partials.s[j] = p.pitch;
+  }
+  if (fused && overlap(o, r)) return fail(RMSN_ERR_ALIAS, "out overlaps residual");
+  if (overlap(o, g)) return fail(RMSN_ERR_ALIAS, "out overlaps gamma");
+  if (fused && overlap(r, g)) return fail(RMSN_ERR_ALIAS, "residual overlaps gamma");
+  Plan plan;
+  rc = choose(t, hidden, fused ? k : 0, al, &plan);
+  if (rc) return rc;
+  a.out = out;
+  a.out_stride = o.pitch;
+  a.residual = residual;
+  a.res_stride = fused ? r.pitch : 0;
+  a.gamma = gamma;
+  a.rows = rows;
+  a.hidden = (int)hidden;
+  a.k = k;
+  a.eps = eps;
+  return launch(plan, a, stream);
+}
+
+int list_variants(Types t, char* buf, int buflen) {
+  if (!buf || buflen < 1) return fail(RMSN_ERR_NULL, "buf must be non-NULL");
+  int n = 0, count = 0;
+  const rmsn::Variant* tab = table_for(t, &n);
+  size_t used = 0;
+  buf[0] = 0;
+  for (int i = 0; i < n; ++i) {
+    if (!same_types(tab[i], t)) continue;
+    const size_t len = strlen(tab[i].name);
+    if (used + len + 2 > (size_t)buflen) return fail(RMSN_ERR_SHAPE, "buffer too small");
+    memcpy(buf + used, tab[i].name, len);
+    used += len;
+    buf[used++] = '\n';
+    buf[used] = 0;
+    ++count;
+  }
+  return count;
+}
+
+int plan_name(Types t, int64_t rows, int64_t hidden, int k, int align, char* buf, int buflen) {
+  int rc = common_checks(t.d, rows, hidden, 0.0f);
+  if (rc) return rc;
+  if ((rc = type_checks(t))) return rc;
+  if (k < 0 || k > RMSN_KMAX) return fail(RMSN_ERR_K, "k=%d outside [0, %d]", k, RMSN_KMAX);
+  if (!buf || buflen < 1) return fail(RMSN_ERR_NULL, "buf must be non-NULL");
+  Plan plan;
+  int a = 1;
+  while (a < 16 && a * 2 <= align) a *= 2;
+  // contiguous rows: each tensor's pitch is hidden elements of its dtype
+  const Aligns al{std::min(a, align_of_int((uint64_t)hidden * dtype_size(t.d))),
+                  a, std::min(a, align_of_int((uint64_t)hidden * dtype_size(t.o)))};
+  rc = choose(t, hidden, k, rows > 1 ? al : Aligns{a, a, a}, &plan);
+  if (rc) return rc;
+  snprintf(buf, (size_t)buflen, "%s", plan.v->name);
+  return RMSN_OK;
+}
+
 }  // namespace
 
 // The last-error slot, shared with the other entry points of the library.
@@ -228,67 +412,48 @@ extern "C" {
 
 int rmsnorm_fwd(void* out, const void* x, const void* gamma, int64_t rows, int64_t hidden,
                 float eps, int dtype, void* stream) {
-  int rc = common_checks(dtype, rows, hidden, eps);
-  if (rc) return rc;
-  if (rows == 0) return RMSN_OK;
-  if (!out || !x || !gamma) return fail(RMSN_ERR_NULL, "out, x and gamma must be non-NULL");
-  const size_t nbytes = (size_t)rows * (size_t)hidden * dtype_size(dtype);
-  const size_t gbytes = (size_t)hidden * dtype_size(dtype);
-  if (out != x && overlap(out, nbytes, x, nbytes))
-    return fail(RMSN_ERR_ALIAS, "out partially overlaps x");
-  if (overlap(out, nbytes, gamma, gbytes)) return fail(RMSN_ERR_ALIAS, "out overlaps gamma");
-  Plan plan;
-  rc = choose(dtype, hidden, 0, min_align(min_align(align_of(out), x), gamma), &plan);
-  if (rc) return rc;
-  rmsn::RowArgs a{};
-  a.out = out;
-  a.residual = nullptr;
-  a.partials.p[0] = x;
-  a.gamma = gamma;
-  a.rows = rows;
-  a.hidden = (int)hidden;
-  a.k = 1;
-  a.eps = eps;
-  return launch(plan, a, stream);
+  const void* parts[1] = {x};
+  return run(Types{dtype, dtype, dtype}, out, hidden, nullptr, 0, parts, nullptr, 1, gamma, rows,
+             hidden, eps, stream);
 }
 
 int add_rmsnorm_fwd(void* out, void* residual, const void* const* partials, int k,
                     const void* gamma, int64_t rows, int64_t hidden, float eps, int dtype,
                     void* stream) {
-  int rc = common_checks(dtype, rows, hidden, eps);
-  if (rc) return rc;
-  if (k < 1 || k > RMSN_KMAX) return fail(RMSN_ERR_K, "k=%d outside [1, %d]", k, RMSN_KMAX);
-  if (rows == 0) return RMSN_OK;
-  if (!out || !residual || !gamma || !partials)
-    return fail(RMSN_ERR_NULL, "out, residual, partials and gamma must be non-NULL");
-  const size_t nbytes = (size_t)rows * (size_t)hidden * dtype_size(dtype);
-  const size_t gbytes = (size_t)hidden * dtype_size(dtype);
-  int align = min_align(min_align(align_of(out), residual), gamma);
-  for (int j = 0; j < k; ++j) {
-    if (!partials[j]) return fail(RMSN_ERR_NULL, "partials[%d] is NULL", j);
-    if (overlap(residual, nbytes, partials[j], nbytes))
-      return fail(RMSN_ERR_ALIAS, "residual overlaps partials[%d]", j);
-    if (out != partials[j] && overlap(out, nbytes, partials[j], nbytes))
-      return fail(RMSN_ERR_ALIAS, "out partially overlaps partials[%d]", j);
-    align = min_align(align, partials[j]);
+  if (!residual) {
+    int rc = common_checks(dtype, rows, hidden, eps);
+    if (rc) return rc;
+    if (k < 1 || k > RMSN_KMAX) return fail(RMSN_ERR_K, "k=%d outside [1, %d]", k, RMSN_KMAX);
+    if (rows == 0) return RMSN_OK;
+    return fail(RMSN_ERR_NULL, "residual must be non-NULL");
   }
-  if (overlap(out, nbytes, residual, nbytes)) return fail(RMSN_ERR_ALIAS, "out overlaps residual");
-  if (overlap(out, nbytes, gamma, gbytes)) return fail(RMSN_ERR_ALIAS, "out overlaps gamma");
-  if (overlap(residual, nbytes, gamma, gbytes))
-    return fail(RMSN_ERR_ALIAS, "residual overlaps gamma");
-  Plan plan;
-  rc = choose(dtype, hidden, k, align, &plan);
-  if (rc) return rc;
-  rmsn::RowArgs a{};
-  a.out = out;
-  a.residual = residual;
-  for (int j = 0; j < k; ++j) a.partials.p[j] = partials[j];
-  a.gamma = gamma;
-  a.rows = rows;
-  a.hidden = (int)hidden;
-  a.k = k;
-  a.eps = eps;
-  return launch(plan, a, stream);
+  return run(Types{dtype, dtype, dtype}, out, hidden, residual, hidden, partials, nullptr, k,
+             gamma, rows, hidden, eps, stream);
+}
+
+int rmsnorm_fwd_ex(void* out, int64_t out_stride, int out_dtype, const void* x, int64_t x_stride,
+                   int dtype, const void* gamma, int gamma_dtype, int64_t rows, int64_t hidden,
+                   float eps, void* stream) {
+  const void* parts[1] = {x};
+  const int64_t strides[1] = {x_stride};
+  return run(Types{dtype, gamma_dtype, out_dtype}, out, out_stride, nullptr, 0, parts, strides, 1,
+             gamma, rows, hidden, eps, stream);
+}
+
+int add_rmsnorm_fwd_ex(void* out, int64_t out_stride, int out_dtype, void* residual,
+                       int64_t residual_stride, const void* const* partials,
+                       const int64_t* partial_strides, int k, int dtype, const void* gamma,
+                       int gamma_dtype, int64_t rows, int64_t hidden, float eps, void* stream) {
+  if (!residual) {
+    int rc = common_checks(dtype, rows, hidden, eps);
+    if (rc) return rc;
+    if ((rc = type_checks(Types{dtype, gamma_dtype, out_dtype}))) return rc;
+    if (k < 1 || k > RMSN_KMAX) return fail(RMSN_ERR_K, "k=%d outside [1, %d]", k, RMSN_KMAX);
+    if (rows == 0) return RMSN_OK;
+    return fail(RMSN_ERR_NULL, "residual must be non-NULL");
+  }
+  return run(Types{dtype, gamma_dtype, out_dtype}, out, out_stride, residual, residual_stride,
+             partials, partial_strides, k, gamma, rows, hidden, eps, stream);
 }
 
 const char* rmsnorm_strerror(int code) {
@@ -309,36 +474,24 @@ const char* rmsnorm_last_error(void) { return g_last_error; }
 
 int rmsnorm_plan(int64_t rows, int64_t hidden, int k, int dtype, int align, char* buf,
                  int buflen) {
-  int rc = common_checks(dtype, rows, hidden, 0.0f);
-  if (rc) return rc;
-  if (k < 0 || k > RMSN_KMAX) return fail(RMSN_ERR_K, "k=%d outside [0, %d]", k, RMSN_KMAX);
-  if (!buf || buflen < 1) return fail(RMSN_ERR_NULL, "buf must be non-NULL");
-  Plan plan;
-  int a = 1;
-  while (a < 16 && a * 2 <= align) a *= 2;
-  rc = choose(dtype, hidden, k, a, &plan);
-  if (rc) return rc;
-  snprintf(buf, (size_t)buflen, "%s", plan.v->name);
-  return RMSN_OK;
+  return plan_name(Types{dtype, dtype, dtype}, rows, hidden, k, align, buf, buflen);
+}
+
+int rmsnorm_plan_ex(int64_t rows, int64_t hidden, int k, int dtype, int gamma_dtype,
+                    int out_dtype, int align, char* buf, int buflen) {
+  return plan_name(Types{dtype, gamma_dtype, out_dtype}, rows, hidden, k, align, buf, buflen);
 }
 
 int rmsnorm_variants(int dtype, char* buf, int buflen) {
-  if (dtype != RMSN_F32 && dtype != RMSN_F16 && dtype != RMSN_BF16)
-    return fail(RMSN_ERR_DTYPE, "unknown dtype %d", dtype);
-  if (!buf || buflen < 1) return fail(RMSN_ERR_NULL, "buf must be non-NULL");
-  int n = 0;
-  const rmsn::Variant* t = table_for(dtype, &n);
-  size_t used = 0;
-  buf[0] = 0;
-  for (int i = 0; i < n; ++i) {
-    const size_t len = strlen(t[i].name);
-    if (used + len + 2 > (size_t)buflen) return fail(RMSN_ERR_SHAPE, "buffer too small");
-    memcpy(buf + used, t[i].name, len);
-    used += len;
-    buf[used++] = '\n';
-    buf[used] = 0;
-  }
-  return n;
+  if (!known(dtype)) return fail(RMSN_ERR_DTYPE, "unknown dtype %d", dtype);
+  return list_variants(Types{dtype, dtype, dtype}, buf, buflen);
+}
+
+int rmsnorm_variants_ex(int dtype, int gamma_dtype, int out_dtype, char* buf, int buflen) {
+  const Types t{dtype, gamma_dtype, out_dtype};
+  const int rc = type_checks(t);
+  if (rc) return rc;
+  return list_variants(t, buf, buflen);
 }
 
 }  // extern "C"

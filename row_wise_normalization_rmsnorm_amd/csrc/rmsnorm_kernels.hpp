@@ -33,25 +33,39 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace rmsn {
 
 constexpr int kMaxK = 16;
 
+// Row-major tensors addressed per row: row r of a tensor starts at
+// base + r * stride bytes, and its hidden elements are contiguous.
 struct PartialPtrs {
   const void* p[kMaxK];
+  int64_t s[kMaxK];      // row strides in bytes
 };
 
 struct RowArgs {
   void* out;
+  int64_t out_stride;    // bytes
   void* residual;        // nullptr for plain RMSNorm
+  int64_t res_stride;    // bytes
   PartialPtrs partials;  // partials.p[0] is x for plain RMSNorm
   const void* gamma;
   int64_t rows;
   int hidden;            // elements per row
-  int chunks;            // vector chunks (16 B) per row, or elements for scalar kernels
+  int chunks;            // chunks per row (E elements each, see Vec)
   int k;                 // number of partials (fused), 1 for plain
   float eps;
 };
+
+__device__ __forceinline__ const char* row_ptr(const void* base, int64_t stride, int64_t row) {
+  return reinterpret_cast<const char*>(base) + row * stride;
+}
+__device__ __forceinline__ char* row_ptr(void* base, int64_t stride, int64_t row) {
+  return reinterpret_cast<char*>(base) + row * stride;
+}
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -136,57 +150,80 @@ struct Words<4> {
   __device__ static void set(type& v, int i, uint32_t x) { v[i] = x; }
 };
 
-// A "chunk" is what one lane moves per access: VB bytes (16, 8 or 4: a
-// global_load/store_dwordx4, dwordx2 or dword) or, with VB == 0, one element
-// (for bases or row lengths that no wider access divides).
-// NT selects the nontemporal (streaming) cache policy for data that is touched
-// exactly once; gamma, reused by every row, is always loaded normally.
-template <typename T, int VB>
-struct Chunk {
-  static_assert(VB == 4 || VB == 8 || VB == 16, "vector chunks are 4, 8 or 16 bytes");
-  static constexpr int W = VB / 4;
-  static constexpr int V = W * DT<T>::PER_WORD;
-  using WS = Words<W>;
-  using raw_t = typename WS::type;
+// A "chunk" is E consecutive elements of a row, moved by one lane.  The
+// kernels pick E from the data dtype and an access width VB (16, 8 or 4
+// bytes: a global_load/store_dwordx4, dwordx2 or dword; 0: one element, for
+// bases or row lengths that no wider access divides).  gamma and the output
+// may have other dtypes: their chunk is then E elements of their own type,
+// e.g. 32 bytes (two 16-byte accesses) of fp32 output for a 16-byte bf16
+// input chunk, or 8 bytes of bf16 output for a 16-byte fp32 chunk.
+// NT selects the nontemporal (streaming) cache policy for data that is
+// touched exactly once; gamma, reused by every row, is loaded normally.
+template <typename T, int E>
+struct Vec {
+  static constexpr int V = E;
+  static constexpr int BYTES = E * (int)sizeof(typename DT<T>::scalar_t);
+  static_assert(BYTES == 2 || BYTES % 4 == 0, "a chunk is one 16-bit element or whole words");
+  static constexpr int W = BYTES / 4;                  // 32-bit words per chunk
+  static constexpr int AW = W >= 4 ? 4 : (W > 0 ? W : 1);  // words per access
+  static constexpr int N = W >= 4 ? W / 4 : 1;         // accesses per chunk
+  static_assert(W <= 4 || W % 4 == 0, "wide chunks are whole 16-byte accesses");
+  static constexpr bool SCALAR = BYTES == 2;
+  using WS = Words<AW>;
+  using acc_t = typename std::conditional<SCALAR, typename DT<T>::scalar_t,
+                                          typename WS::type>::type;
+  struct raw_t {
+    acc_t w[N];
+  };
   template <bool NT = false>
-  __device__ static raw_t load(const void* base, int64_t chunk) {
-    const raw_t* p = reinterpret_cast<const raw_t*>(base) + chunk;
-    if constexpr (NT) return __builtin_nontemporal_load(p); else return *p;
+  __device__ static raw_t load(const void* row, int c) {
+    const acc_t* p = reinterpret_cast<const acc_t*>(row) + (int64_t)c * N;
+    raw_t r;
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+      if constexpr (NT) r.w[n] = __builtin_nontemporal_load(p + n); else r.w[n] = p[n];
+    }
+    return r;
   }
   template <bool NT = false>
-  __device__ static void store(void* base, int64_t chunk, raw_t v) {
-    raw_t* p = reinterpret_cast<raw_t*>(base) + chunk;
-    if constexpr (NT) __builtin_nontemporal_store(v, p); else *p = v;
+  __device__ static void store(void* row, int c, const raw_t& r) {
+    acc_t* p = reinterpret_cast<acc_t*>(row) + (int64_t)c * N;
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+      if constexpr (NT) __builtin_nontemporal_store(r.w[n], p + n); else p[n] = r.w[n];
+    }
   }
   __device__ static void unpack(const raw_t& r, float (&f)[V]) {
+    if constexpr (SCALAR) {
+      f[0] = DT<T>::widen(r.w[0]);
+    } else {
 #pragma unroll
-    for (int w = 0; w < W; ++w) DT<T>::unpack_word(WS::get(r, w), f + w * DT<T>::PER_WORD);
+      for (int n = 0; n < N; ++n)
+#pragma unroll
+        for (int w = 0; w < AW; ++w)
+          DT<T>::unpack_word(WS::get(r.w[n], w), f + (n * AW + w) * DT<T>::PER_WORD);
+    }
   }
   __device__ static raw_t pack(const float (&f)[V]) {
     raw_t r;
+    if constexpr (SCALAR) {
+      r.w[0] = DT<T>::narrow(f[0]);
+    } else {
 #pragma unroll
-    for (int w = 0; w < W; ++w) WS::set(r, w, DT<T>::pack_word(f + w * DT<T>::PER_WORD));
+      for (int n = 0; n < N; ++n)
+#pragma unroll
+        for (int w = 0; w < AW; ++w)
+          WS::set(r.w[n], w, DT<T>::pack_word(f + (n * AW + w) * DT<T>::PER_WORD));
+    }
     return r;
   }
 };
 
-template <typename T>
-struct Chunk<T, 0> {
-  static constexpr int V = 1;
-  using raw_t = typename DT<T>::scalar_t;
-  template <bool NT = false>
-  __device__ static raw_t load(const void* base, int64_t i) {
-    const raw_t* p = reinterpret_cast<const raw_t*>(base) + i;
-    if constexpr (NT) return __builtin_nontemporal_load(p); else return *p;
-  }
-  template <bool NT = false>
-  __device__ static void store(void* base, int64_t i, raw_t v) {
-    raw_t* p = reinterpret_cast<raw_t*>(base) + i;
-    if constexpr (NT) __builtin_nontemporal_store(v, p); else *p = v;
-  }
-  __device__ static void unpack(const raw_t& r, float (&f)[1]) { f[0] = DT<T>::widen(r); }
-  __device__ static raw_t pack(const float (&f)[1]) { return DT<T>::narrow(f[0]); }
-};
+// Elements per chunk for data type T and access width VB (0: one element).
+template <typename T, int VB>
+constexpr int chunk_elems() {
+  return VB == 0 ? 1 : VB / (int)sizeof(typename DT<T>::scalar_t);
+}
 
 // ---- wave64 reductions ----------------------------------------------------
 // DPP controls (GFX9 encoding).
@@ -297,11 +334,13 @@ __device__ __forceinline__ int exponent_above(float m) {
 // KC: 0 = plain RMSNorm; >0 = fused with exactly KC partials; -1 = fused with
 // a runtime number of partials (args.k), summed one partial at a time.
 // NT: streaming (nontemporal) loads and stores for the row data.
-template <typename T, int TPR, int NPT, int WGS, int KC, bool NT>
+template <typename T, typename GT, typename OT, int TPR, int NPT, int WGS, int KC, bool NT>
 __global__ __launch_bounds__(WGS) void row_vgpr_kernel(RowArgs a) {
-  using CK = Chunk<T, 16>;
-  using raw_t = typename CK::raw_t;
-  constexpr int V = CK::V;
+  constexpr int V = chunk_elems<T, 16>();
+  using IV = Vec<T, V>;   // data: partials, residual, x
+  using GV = Vec<GT, V>;  // gamma
+  using OV = Vec<OT, V>;  // output
+  using raw_t = typename IV::raw_t;
   constexpr int RPW = WGS / TPR;                // rows per workgroup
   constexpr int WPR = TPR > 64 ? TPR / 64 : 1;  // waves per row
   static_assert(TPR <= WGS && WGS % TPR == 0, "a row must fit in one workgroup");
@@ -313,7 +352,6 @@ __global__ __launch_bounds__(WGS) void row_vgpr_kernel(RowArgs a) {
   const int tr = tid % TPR;  // thread index within its row
   const int slot = tid / TPR;
   const int C = a.chunks;
-  const int64_t rowstride = (int64_t)a.chunks;  // chunks per row
   int parity = 0;
 
   // gamma chunks are the same for every row this thread touches
@@ -322,7 +360,7 @@ __global__ __launch_bounds__(WGS) void row_vgpr_kernel(RowArgs a) {
   for (int i = 0; i < NPT; ++i) {
     const int c = tr + i * TPR;
     if (c < C) {
-      CK::unpack(CK::template load<false>(a.gamma, c), g[i]);
+      GV::unpack(GV::template load<false>(a.gamma, c), g[i]);
     } else {
 #pragma unroll
       for (int e = 0; e < V; ++e) g[i][e] = 0.0f;
@@ -331,9 +369,11 @@ __global__ __launch_bounds__(WGS) void row_vgpr_kernel(RowArgs a) {
 
   for (int64_t row0 = (int64_t)blockIdx.x * RPW; row0 < a.rows;
        row0 += (int64_t)gridDim.x * RPW) {
-    const int64_t row = row0 + slot;
+    const int64_t row = RPW == 1 ? row0 : row0 + slot;  // uniform when one row per WG
     const bool row_ok = row < a.rows;
-    const int64_t base = row * rowstride;
+    const char* xrow = row_ptr(a.partials.p[0], a.partials.s[0], row);
+    char* rrow = row_ptr(a.residual, a.res_stride, row);
+    char* orow = row_ptr(a.out, a.out_stride, row);
     float v[NPT][V];
 
     if constexpr (KC == 0) {
@@ -341,13 +381,13 @@ __global__ __launch_bounds__(WGS) void row_vgpr_kernel(RowArgs a) {
 #pragma unroll
       for (int i = 0; i < NPT; ++i) {
         const int c = tr + i * TPR;
-        if (row_ok && c < C) raw[i] = CK::template load<NT>(a.partials.p[0], base + c);
+        if (row_ok && c < C) raw[i] = IV::template load<NT>(xrow, c);
       }
 #pragma unroll
       for (int i = 0; i < NPT; ++i) {
         const int c = tr + i * TPR;
         if (row_ok && c < C) {
-          CK::unpack(raw[i], v[i]);
+          IV::unpack(raw[i], v[i]);
         } else {
 #pragma unroll
           for (int e = 0; e < V; ++e) v[i][e] = 0.0f;
@@ -362,8 +402,9 @@ __global__ __launch_bounds__(WGS) void row_vgpr_kernel(RowArgs a) {
         const int c = tr + i * TPR;
         if (row_ok && c < C) {
 #pragma unroll
-          for (int q = 0; q < NB; ++q) raw[q][i] = CK::template load<NT>(a.partials.p[q], base + c);
-          rres[i] = CK::template load<NT>(a.residual, base + c);
+          for (int q = 0; q < NB; ++q)
+            raw[q][i] = IV::template load<NT>(row_ptr(a.partials.p[q], a.partials.s[q], row), c);
+          rres[i] = IV::template load<NT>(rrow, c);
         }
       }
       float acc[NPT][V];
@@ -371,11 +412,11 @@ __global__ __launch_bounds__(WGS) void row_vgpr_kernel(RowArgs a) {
       for (int i = 0; i < NPT; ++i) {
         const int c = tr + i * TPR;
         if (row_ok && c < C) {
-          CK::unpack(raw[0][i], acc[i]);  // accumulator seeded with p0
+          IV::unpack(raw[0][i], acc[i]);  // accumulator seeded with p0
 #pragma unroll
           for (int q = 1; q < NB; ++q) {
             float t[V];
-            CK::unpack(raw[q][i], t);
+            IV::unpack(raw[q][i], t);
 #pragma unroll
             for (int e = 0; e < V; ++e) acc[i][e] += t[e];
           }
@@ -385,17 +426,18 @@ __global__ __launch_bounds__(WGS) void row_vgpr_kernel(RowArgs a) {
         // runtime K: remaining partials one at a time, in order
         for (int q = 1; q < a.k; ++q) {
           raw_t rq[NPT];
+          const char* prow = row_ptr(a.partials.p[q], a.partials.s[q], row);
 #pragma unroll
           for (int i = 0; i < NPT; ++i) {
             const int c = tr + i * TPR;
-            if (row_ok && c < C) rq[i] = CK::template load<NT>(a.partials.p[q], base + c);
+            if (row_ok && c < C) rq[i] = IV::template load<NT>(prow, c);
           }
 #pragma unroll
           for (int i = 0; i < NPT; ++i) {
             const int c = tr + i * TPR;
             if (row_ok && c < C) {
               float t[V];
-              CK::unpack(rq[i], t);
+              IV::unpack(rq[i], t);
 #pragma unroll
               for (int e = 0; e < V; ++e) acc[i][e] += t[e];
             }
@@ -407,12 +449,12 @@ __global__ __launch_bounds__(WGS) void row_vgpr_kernel(RowArgs a) {
         const int c = tr + i * TPR;
         if (row_ok && c < C) {
           float t[V];
-          CK::unpack(rres[i], t);
+          IV::unpack(rres[i], t);
 #pragma unroll
           for (int e = 0; e < V; ++e) acc[i][e] += t[e];  // residual added last
-          const raw_t rn = CK::pack(acc[i]);             // round once to dtype
-          CK::template store<NT>(a.residual, base + c, rn);
-          CK::unpack(rn, v[i]);                          // normalise the stored row
+          const raw_t rn = IV::pack(acc[i]);             // round once to dtype
+          IV::template store<NT>(rrow, c, rn);
+          IV::unpack(rn, v[i]);                          // normalise the stored row
         } else {
 #pragma unroll
           for (int e = 0; e < V; ++e) v[i][e] = 0.0f;
@@ -487,7 +529,7 @@ __global__ __launch_bounds__(WGS) void row_vgpr_kernel(RowArgs a) {
 #pragma unroll
           for (int e = 0; e < V; ++e) y[e] = (ldexpf(v[i][e], shift) * inv) * g[i][e];
         }
-        CK::template store<NT>(a.out, base + c, CK::pack(y));
+        OV::template store<NT>(orow, c, OV::pack(y));
       }
     }
   }
@@ -502,11 +544,14 @@ __global__ __launch_bounds__(WGS) void row_vgpr_kernel(RowArgs a) {
 // so no barrier guards the stage.
 // NT: streaming loads/stores for data touched once (never for a residual
 // that pass 2 reads back from memory).
-template <typename T, int VB, int WGS, bool LDS_STAGE, int KC, int UNR, bool NT>
+template <typename T, typename GT, typename OT, int VB, int WGS, bool LDS_STAGE, int KC, int UNR,
+          bool NT>
 __global__ __launch_bounds__(WGS) void row_stream_kernel(RowArgs a) {
-  using CK = Chunk<T, VB>;
-  using raw_t = typename CK::raw_t;
-  constexpr int V = CK::V;
+  constexpr int V = chunk_elems<T, VB>();
+  using IV = Vec<T, V>;   // data: partials, residual, x
+  using GV = Vec<GT, V>;  // gamma
+  using OV = Vec<OT, V>;  // output
+  using raw_t = typename IV::raw_t;
   constexpr int NW = WGS / 64;
   __shared__ float red[2][NW];
   extern __shared__ __align__(16) unsigned char stage_bytes[];
@@ -514,11 +559,12 @@ __global__ __launch_bounds__(WGS) void row_stream_kernel(RowArgs a) {
 
   const int tid = threadIdx.x;
   const int C = a.chunks;
-  const int64_t rowstride = (int64_t)a.chunks;
   int parity = 0;
 
   for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x) {
-    const int64_t base = row * rowstride;
+    const char* xrow = row_ptr(a.partials.p[0], a.partials.s[0], row);
+    char* rrow = row_ptr(a.residual, a.res_stride, row);
+    char* orow = row_ptr(a.out, a.out_stride, row);
     float ss = 0.0f;
 
     for (int c0 = tid; c0 < C; c0 += WGS * UNR) {
@@ -527,7 +573,7 @@ __global__ __launch_bounds__(WGS) void row_stream_kernel(RowArgs a) {
 #pragma unroll
         for (int u = 0; u < UNR; ++u) {
           const int c = c0 + u * WGS;
-          if (c < C) rv[u] = CK::template load<NT>(a.partials.p[0], base + c);
+          if (c < C) rv[u] = IV::template load<NT>(xrow, c);
         }
       } else {
         raw_t r0[UNR], rr[UNR];
@@ -535,30 +581,31 @@ __global__ __launch_bounds__(WGS) void row_stream_kernel(RowArgs a) {
         for (int u = 0; u < UNR; ++u) {
           const int c = c0 + u * WGS;
           if (c < C) {
-            r0[u] = CK::template load<NT>(a.partials.p[0], base + c);
-            rr[u] = CK::template load<NT>(a.residual, base + c);
+            r0[u] = IV::template load<NT>(xrow, c);
+            rr[u] = IV::template load<NT>(rrow, c);
           }
         }
         float acc[UNR][V];
 #pragma unroll
         for (int u = 0; u < UNR; ++u) {
           const int c = c0 + u * WGS;
-          if (c < C) CK::unpack(r0[u], acc[u]);
+          if (c < C) IV::unpack(r0[u], acc[u]);
         }
         const int K = KC > 0 ? KC : a.k;
         for (int q = 1; q < K; ++q) {
           raw_t rq[UNR];
+          const char* prow = row_ptr(a.partials.p[q], a.partials.s[q], row);
 #pragma unroll
           for (int u = 0; u < UNR; ++u) {
             const int c = c0 + u * WGS;
-            if (c < C) rq[u] = CK::template load<NT>(a.partials.p[q], base + c);
+            if (c < C) rq[u] = IV::template load<NT>(prow, c);
           }
 #pragma unroll
           for (int u = 0; u < UNR; ++u) {
             const int c = c0 + u * WGS;
             if (c < C) {
               float t[V];
-              CK::unpack(rq[u], t);
+              IV::unpack(rq[u], t);
 #pragma unroll
               for (int e = 0; e < V; ++e) acc[u][e] += t[e];
             }
@@ -569,11 +616,11 @@ __global__ __launch_bounds__(WGS) void row_stream_kernel(RowArgs a) {
           const int c = c0 + u * WGS;
           if (c < C) {
             float t[V];
-            CK::unpack(rr[u], t);
+            IV::unpack(rr[u], t);
 #pragma unroll
             for (int e = 0; e < V; ++e) acc[u][e] += t[e];
-            rv[u] = CK::pack(acc[u]);
-            CK::template store<NT && LDS_STAGE>(a.residual, base + c, rv[u]);
+            rv[u] = IV::pack(acc[u]);
+            IV::template store<NT && LDS_STAGE>(rrow, c, rv[u]);
           }
         }
       }
@@ -582,7 +629,7 @@ __global__ __launch_bounds__(WGS) void row_stream_kernel(RowArgs a) {
         const int c = c0 + u * WGS;
         if (c < C) {
           float t[V];
-          CK::unpack(rv[u], t);
+          IV::unpack(rv[u], t);
 #pragma unroll
           for (int e = 0; e < V; ++e) ss = __builtin_fmaf(t[e], t[e], ss);
           if constexpr (LDS_STAGE) stage[c] = rv[u];
@@ -593,10 +640,10 @@ __global__ __launch_bounds__(WGS) void row_stream_kernel(RowArgs a) {
     const float tot = row_reduce<WGS, NW, NW, false>(ss, red, parity, 0, tid);
     float inv = row_scale(tot, a.hidden, a.eps);
     int shift = 0;
-    const void* src = KC == 0 ? a.partials.p[0] : a.residual;
+    const char* src = KC == 0 ? xrow : rrow;
     // this thread's chunk c of the stored row, from the stage or memory
     auto own = [&](int c) -> raw_t {
-      if constexpr (LDS_STAGE) return stage[c]; else return CK::template load<false>(src, base + c);
+      if constexpr (LDS_STAGE) return stage[c]; else return IV::template load<false>(src, c);
     };
 
     // Rare: rescale a row whose sum of squares left fp32's range (the whole
@@ -605,7 +652,7 @@ __global__ __launch_bounds__(WGS) void row_stream_kernel(RowArgs a) {
       float m = 0.0f;
       for (int c = tid; c < C; c += WGS) {
         float t[V];
-        CK::unpack(own(c), t);
+        IV::unpack(own(c), t);
 #pragma unroll
         for (int e = 0; e < V; ++e) m = fmaxf(m, fabsf(t[e]));
       }
@@ -614,7 +661,7 @@ __global__ __launch_bounds__(WGS) void row_stream_kernel(RowArgs a) {
       float ss2 = 0.0f;
       for (int c = tid; c < C; c += WGS) {
         float t[V];
-        CK::unpack(own(c), t);
+        IV::unpack(own(c), t);
 #pragma unroll
         for (int e = 0; e < V; ++e) {
           const float q = ldexpf(t[e], -ex);
@@ -631,13 +678,14 @@ __global__ __launch_bounds__(WGS) void row_stream_kernel(RowArgs a) {
     }
 
     for (int c0 = tid; c0 < C; c0 += WGS * UNR) {
-      raw_t rv[UNR], rg[UNR];
+      raw_t rv[UNR];
+      typename GV::raw_t rg[UNR];
 #pragma unroll
       for (int u = 0; u < UNR; ++u) {
         const int c = c0 + u * WGS;
         if (c < C) {
           rv[u] = own(c);
-          rg[u] = CK::template load<false>(a.gamma, c);
+          rg[u] = GV::template load<false>(a.gamma, c);
         }
       }
 #pragma unroll
@@ -645,8 +693,8 @@ __global__ __launch_bounds__(WGS) void row_stream_kernel(RowArgs a) {
         const int c = c0 + u * WGS;
         if (c < C) {
           float t[V], g[V], y[V];
-          CK::unpack(rv[u], t);
-          CK::unpack(rg[u], g);
+          IV::unpack(rv[u], t);
+          GV::unpack(rg[u], g);
           if (shift == 0) {
 #pragma unroll
             for (int e = 0; e < V; ++e) y[e] = (t[e] * inv) * g[e];
@@ -654,7 +702,7 @@ __global__ __launch_bounds__(WGS) void row_stream_kernel(RowArgs a) {
 #pragma unroll
             for (int e = 0; e < V; ++e) y[e] = (ldexpf(t[e], shift) * inv) * g[e];
           }
-          CK::template store<NT>(a.out, base + c, CK::pack(y));
+          OV::template store<NT>(orow, c, OV::pack(y));
         }
       }
     }

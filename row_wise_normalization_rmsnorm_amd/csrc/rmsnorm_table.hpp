@@ -1,5 +1,6 @@
-// rmsnorm_table.hpp -- instantiates every kernel variant for one dtype and
-// builds its descriptor table (included once per dtype translation unit).
+// rmsnorm_table.hpp -- instantiates the kernel variants for one combination
+// of data, gamma and output dtypes and builds its descriptor table (included
+// by the per-dtype translation units).
 #pragma once
 
 #include <stdio.h>
@@ -20,18 +21,39 @@ inline const char* width_name(int vb) {
   }
 }
 
-inline void add_variant(std::vector<Variant>& v, int dtype, const char* dname, int kind, int vb,
-                        int tpr, int npt, int wgs, int kc, int lds, int unr, int nt,
-                        const void* fn) {
+inline const char* dtype_name(int code) {
+  switch (code) {
+    case 0: return "f32";
+    case 1: return "f16";
+    default: return "bf16";
+  }
+}
+
+struct Types {
+  int d, g, o;  // data, gamma, output dtype codes
+};
+
+inline void add_variant(std::vector<Variant>& v, Types t, int kind, int vb, int tpr, int npt,
+                        int wgs, int kc, int lds, int unr, int nt, const void* fn) {
   Variant d{};
+  // Single-dtype variants are named by the data dtype alone; the general
+  // interface's add gamma's and the output's dtypes.
+  char types[48];
+  if (t.g == t.d && t.o == t.d)
+    snprintf(types, sizeof(types), "%s", dtype_name(t.d));
+  else
+    snprintf(types, sizeof(types), "%s,g=%s,o=%s", dtype_name(t.d), dtype_name(t.g),
+             dtype_name(t.o));
   if (kind == kVgpr)
-    snprintf(d.name, sizeof(d.name), "vgpr<%s,tpr=%d,npt=%d,wg=%d,k=%d%s>", dname, tpr, npt, wgs,
+    snprintf(d.name, sizeof(d.name), "vgpr<%s,tpr=%d,npt=%d,wg=%d,k=%d%s>", types, tpr, npt, wgs,
              kc, nt ? ",nt" : "");
   else
-    snprintf(d.name, sizeof(d.name), "stream<%s,%s,wg=%d,%s,k=%d,unr=%d%s>", dname,
+    snprintf(d.name, sizeof(d.name), "stream<%s,%s,wg=%d,%s,k=%d,unr=%d%s>", types,
              width_name(vb), wgs, lds ? "lds" : "reread", kc, unr, nt ? ",nt" : "");
   d.nt = nt;
-  d.dtype = dtype;
+  d.dtype = t.d;
+  d.gdtype = t.g;
+  d.odtype = t.o;
   d.kind = kind;
   d.vb = vb;
   d.tpr = tpr;
@@ -44,20 +66,20 @@ inline void add_variant(std::vector<Variant>& v, int dtype, const char* dname, i
   v.push_back(d);
 }
 
+// Every variant of the single-dtype interface (full shape lists, for the
+// dispatcher and for sweeps).
 template <typename T>
-std::vector<Variant> build_table(int dtype, const char* dname) {
-  std::vector<Variant> v;
-#define RMSN_ADD_VGPR_K(KC, TPR, NPT, WGS, NT)                                        \
-  add_variant(v, dtype, dname, kVgpr, 16, TPR, NPT, WGS, KC, 0, 0, NT ? 1 : 0,        \
-              reinterpret_cast<const void*>(&row_vgpr_kernel<T, TPR, NPT, WGS, KC, NT>));
+void add_full(std::vector<Variant>& v, Types t) {
+#define RMSN_ADD_VGPR_K(KC, TPR, NPT, WGS, NT)                                          \
+  add_variant(v, t, kVgpr, 16, TPR, NPT, WGS, KC, 0, 0, NT ? 1 : 0,                      \
+              reinterpret_cast<const void*>(&row_vgpr_kernel<T, T, T, TPR, NPT, WGS, KC, NT>));
 #define RMSN_ADD_VGPR(TPR, NPT, WGS, NT) RMSN_KCS(RMSN_ADD_VGPR_K, TPR, NPT, WGS, NT)
   RMSN_VGPR_SHAPES(RMSN_ADD_VGPR)
-#define RMSN_ADD_STREAM_K(KC, VB, WGS, LDS, NT, UNR)                                  \
-  if constexpr (VB == 0 || VB > (int)sizeof(typename DT<T>::scalar_t))                 \
-    add_variant(v, dtype, dname, kStream, VB, WGS, 0, WGS, KC, LDS ? 1 : 0, UNR,        \
-                NT ? 1 : 0,                                                             \
-                reinterpret_cast<const void*>(                                         \
-                    &row_stream_kernel<T, VB, WGS, LDS, KC, UNR, NT>));
+#define RMSN_ADD_STREAM_K(KC, VB, WGS, LDS, NT, UNR)                                    \
+  if constexpr (VB == 0 || VB > (int)sizeof(typename DT<T>::scalar_t))                   \
+    add_variant(v, t, kStream, VB, WGS, 0, WGS, KC, LDS ? 1 : 0, UNR, NT ? 1 : 0,         \
+                reinterpret_cast<const void*>(                                           \
+                    &row_stream_kernel<T, T, T, VB, WGS, LDS, KC, UNR, NT>));
 #define RMSN_ADD_STREAM(VB, WGS, LDS, NT, UNR) \
   RMSN_STREAM_KCS(RMSN_ADD_STREAM_K, VB, WGS, LDS, NT, UNR)
   RMSN_STREAM_SHAPES(RMSN_ADD_STREAM)
@@ -65,15 +87,41 @@ std::vector<Variant> build_table(int dtype, const char* dname) {
 #undef RMSN_ADD_VGPR
 #undef RMSN_ADD_STREAM_K
 #undef RMSN_ADD_STREAM
-  return v;
+}
+
+// The variants of one general combination (data T, gamma GT, output OT).
+template <typename T, typename GT, typename OT>
+void add_mixed(std::vector<Variant>& v, Types t) {
+#define RMSN_ADD_VGPR_K(KC, TPR, NPT, WGS, NT)                                          \
+  add_variant(v, t, kVgpr, 16, TPR, NPT, WGS, KC, 0, 0, NT ? 1 : 0,                      \
+              reinterpret_cast<const void*>(&row_vgpr_kernel<T, GT, OT, TPR, NPT, WGS, KC, NT>));
+#define RMSN_ADD_VGPR(TPR, NPT, WGS, NT) RMSN_MIXED_KCS(RMSN_ADD_VGPR_K, TPR, NPT, WGS, NT)
+  RMSN_MIXED_VGPR_SHAPES(RMSN_ADD_VGPR)
+#define RMSN_ADD_STREAM_K(KC, VB, WGS, LDS, NT, UNR)                                    \
+  if constexpr (VB == 0 || VB > (int)sizeof(typename DT<T>::scalar_t))                   \
+    add_variant(v, t, kStream, VB, WGS, 0, WGS, KC, LDS ? 1 : 0, UNR, NT ? 1 : 0,         \
+                reinterpret_cast<const void*>(                                           \
+                    &row_stream_kernel<T, GT, OT, VB, WGS, LDS, KC, UNR, NT>));
+#define RMSN_ADD_STREAM(VB, WGS, LDS, NT, UNR) \
+  RMSN_MIXED_KCS(RMSN_ADD_STREAM_K, VB, WGS, LDS, NT, UNR)
+  RMSN_MIXED_STREAM_SHAPES(RMSN_ADD_STREAM)
+#undef RMSN_ADD_VGPR_K
+#undef RMSN_ADD_VGPR
+#undef RMSN_ADD_STREAM_K
+#undef RMSN_ADD_STREAM
 }
 
 }  // namespace rmsn
 
-#define RMSN_DEFINE_TABLE(T, CODE, DNAME)                                   \
-  const rmsn::Variant* rmsn_table_##DNAME(int* n) {                         \
-    static const std::vector<rmsn::Variant> table =                         \
-        rmsn::build_table<T>(CODE, #DNAME);                                 \
+// One exported table per translation unit: rmsn_table_<NAME>(&n); the
+// statements after NAME fill the vector v.
+#define RMSN_DEFINE_TABLE(NAME, ...)                                        \
+  const rmsn::Variant* rmsn_table_##NAME(int* n) {                          \
+    static const std::vector<rmsn::Variant> table = [] {                    \
+      std::vector<rmsn::Variant> v;                                         \
+      __VA_ARGS__;                                                          \
+      return v;                                                             \
+    }();                                                                    \
     *n = (int)table.size();                                                 \
     return table.data();                                                    \
   }

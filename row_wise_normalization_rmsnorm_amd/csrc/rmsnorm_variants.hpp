@@ -13,8 +13,10 @@ namespace rmsn {
 enum Kind { kVgpr = 0, kStream = 1 };
 
 struct Variant {
-  char name[96];
-  int dtype;      // 0 f32, 1 f16, 2 bf16
+  char name[112];
+  int dtype;      // data (partials, residual, x): 0 f32, 1 f16, 2 bf16
+  int gdtype;     // gamma
+  int odtype;     // output
   int kind;       // kVgpr or kStream
   int vb;         // bytes per chunk: 16, 8 or 4; 0 = one element per chunk
   int tpr;        // threads per row
@@ -61,5 +63,25 @@ struct Variant {
   X(0, 256, false, false, 4) X(0, 512, false, false, 4) X(0, 1024, false, false, 4)
 
 #define RMSN_STREAM_KCS(X, ...) X(0, __VA_ARGS__) X(1, __VA_ARGS__) X(-1, __VA_ARGS__)
+
+// The general interface -- gamma in fp32 with 16-bit data, or an output dtype
+// other than the data's -- compiles only the shapes the dispatcher picks
+// (one chunk per thread up to 1024 threads, two for 8192-wide fp32 rows; the
+// streaming forms it uses), with plain and runtime-K fused forms.
+#define RMSN_MIXED_VGPR_SHAPES(X)                                                        \
+  X(8, 1, 256, true) X(16, 1, 256, true) X(32, 1, 256, true) X(64, 1, 256, true)        \
+  X(128, 1, 256, true) X(256, 1, 256, true) X(512, 1, 512, true)                        \
+  X(1024, 1, 1024, true) X(1024, 2, 1024, true)
+
+#define RMSN_MIXED_STREAM_SHAPES(X)                                                       \
+  X(16, 256, false, false, 2) X(16, 512, false, false, 2) X(16, 1024, false, false, 2)    \
+  X(8, 256, true, true, 4) X(8, 512, true, true, 4) X(8, 1024, true, true, 4)             \
+  X(8, 256, false, false, 4) X(8, 512, false, false, 4) X(8, 1024, false, false, 4)       \
+  X(4, 256, true, true, 4) X(4, 512, true, true, 4) X(4, 1024, true, true, 4)             \
+  X(4, 256, false, false, 4) X(4, 512, false, false, 4) X(4, 1024, false, false, 4)       \
+  X(0, 256, true, true, 4) X(0, 512, true, true, 4) X(0, 1024, true, true, 4)             \
+  X(0, 256, false, false, 4) X(0, 512, false, false, 4) X(0, 1024, false, false, 4)
+
+#define RMSN_MIXED_KCS(X, ...) X(0, __VA_ARGS__) X(-1, __VA_ARGS__)
 
 }  // namespace rmsn

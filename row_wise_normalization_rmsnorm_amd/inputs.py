@@ -114,9 +114,11 @@ def tensor_rows(w: Workload, tensor_id: int, rows: Optional[Sequence[int]] = Non
     return out
 
 
-def gamma(w: Workload, device: str = "cpu") -> torch.Tensor:
+def gamma(w: Workload, device: str = "cpu", dtype: Optional[str] = None) -> torch.Tensor:
+    """gamma[hidden] ~ U(0.5, 1.5), drawn in float32 and rounded to ``dtype``
+    (default: the workload's dtype; "f32" keeps the full draw)."""
     a = _rng(w.seed, GAMMA_ID, 0).uniform(0.5, 1.5, w.hidden).astype(np.float32)
-    return _to_dtype(a, w.dtype).to(device)
+    return _to_dtype(a, dtype or w.dtype).to(device)
 
 
 def make_inputs(w: Workload, rows: Optional[Sequence[int]] = None, device: str = "cpu") -> Dict:

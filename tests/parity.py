@@ -25,29 +25,37 @@ def storage(t: torch.Tensor) -> np.ndarray:
     return I.to_storage(t)
 
 
-def run_oracle(dtype: str, eps: float, x=None, partials=None, residual=None, gamma=None):
-    """Oracle on CPU copies of torch tensors.  Returns dict with out, y64,
+GAMMA_NAME = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16"}
+
+
+def run_oracle(dtype: str, eps: float, x=None, partials=None, residual=None, gamma=None,
+               out_dtype: str = None):
+    """Oracle on CPU copies of torch tensors (gamma in its own dtype; the
+    output in out_dtype, default dtype).  Returns dict with out, y64,
     (residual)."""
     g = storage(gamma)
+    kw = dict(gamma_dtype=GAMMA_NAME[gamma.dtype], out_dtype=out_dtype or dtype, want_f64=True)
     if partials is None:
-        out, _, y64 = oracle.rmsnorm(storage(x), g, eps, dtype, want_f64=True)
+        out, _, y64 = oracle.rmsnorm(storage(x), g, eps, dtype, **kw)
         return {"out": out, "y64": y64}
     out, rnew, _, y64 = oracle.add_rmsnorm([storage(p) for p in partials], storage(residual), g,
-                                           eps, dtype, want_f64=True)
+                                           eps, dtype, **kw)
     return {"out": out, "y64": y64, "residual": rnew}
 
 
 def compare(dtype: str, gpu_out: torch.Tensor, ref: dict, gpu_residual: torch.Tensor = None,
-            what: str = "") -> dict:
-    """Assert the bar; return error statistics."""
+            what: str = "", res_dtype: str = None) -> dict:
+    """Assert the bar; return error statistics.  dtype is the output's dtype;
+    res_dtype the residual's (default: the same)."""
     go = storage(gpu_out)
     stats = {}
+    res_dtype = res_dtype or dtype
     if gpu_residual is not None:
         gr = storage(gpu_residual)
         same = np.array_equal(gr.view(np.uint8), ref["residual"].view(np.uint8))
         if not same:
-            bad = np.argwhere(gr.view(np.uint32 if dtype == "f32" else np.uint16) !=
-                              ref["residual"].view(np.uint32 if dtype == "f32" else np.uint16))
+            wide = np.uint32 if res_dtype == "f32" else np.uint16
+            bad = np.argwhere(gr.view(wide) != ref["residual"].view(wide))
             raise AssertionError(f"{what}: residual differs at {len(bad)} elements, first {bad[:4].tolist()}")
         stats["residual_bit_exact"] = True
     y64 = ref["y64"]

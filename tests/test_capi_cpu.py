@@ -139,3 +139,81 @@ def test_variant_table_and_forcing(monkeypatch):
     monkeypatch.setenv("RMSNORM_VARIANT", "no-such-kernel")
     with pytest.raises(B.RmsnormError):
         B.rmsnorm_plan(4, 512, 1, "bf16")
+
+
+def fwd_ex(**kw):
+    a = dict(out=FAKE, out_stride=64, out_dtype=0, x=FAKE + (1 << 24), x_stride=64, dtype=2,
+             gamma=FAKE + (1 << 26), gamma_dtype=0, rows=4, hidden=64, eps=1e-6)
+    a.update(kw)
+    return B.lib().rmsnorm_fwd_ex(a["out"], a["out_stride"], a["out_dtype"], a["x"], a["x_stride"],
+                                  a["dtype"], a["gamma"], a["gamma_dtype"], a["rows"], a["hidden"],
+                                  a["eps"], None)
+
+
+def add_ex(k=1, parts=None, strides=None, **kw):
+    a = dict(out=FAKE, out_stride=64, out_dtype=0, residual=FAKE + (1 << 24), res_stride=64,
+             dtype=2, gamma=FAKE + (1 << 26), gamma_dtype=2, rows=4, hidden=64, eps=1e-6)
+    a.update(kw)
+    parts = parts if parts is not None else [FAKE + (1 << 27) + i * (1 << 20) for i in range(k)]
+    arr = (ctypes.c_void_p * max(1, len(parts)))(*parts)
+    st = None if strides is None else (ctypes.c_int64 * max(1, len(strides)))(*strides)
+    return B.lib().add_rmsnorm_fwd_ex(a["out"], a["out_stride"], a["out_dtype"], a["residual"],
+                                      a["res_stride"], arr, st, k, a["dtype"], a["gamma"],
+                                      a["gamma_dtype"], a["rows"], a["hidden"], a["eps"], None)
+
+
+def test_general_interface_error_codes():
+    assert fwd_ex(gamma_dtype=1) == -3                     # fp16 gamma with bf16 data
+    assert fwd_ex(out_dtype=3) == -3
+    assert fwd_ex(dtype=7) == -3
+    assert fwd_ex(x_stride=63) == -2                       # stride below hidden
+    assert fwd_ex(out_stride=-64) == -2
+    assert fwd_ex(x_stride=1 << 62) == -2                  # last row beyond the address range
+    assert fwd_ex(out=0) == -1
+    assert fwd_ex(rows=0, out=0, x=0, gamma=0) == 0
+    assert fwd_ex(rows=1, x_stride=0, out=FAKE, x=FAKE + 2, out_dtype=2) == -5   # one row, shifted
+    # out over x: refused unless same dtype and layout
+    assert fwd_ex(out=FAKE, x=FAKE, out_dtype=0) == -5     # another dtype
+    assert fwd_ex(out=FAKE, x=FAKE, out_dtype=2, out_stride=128, x_stride=64) == -5
+    # equal pitches: rows that interleave share no byte (x at byte 0 of each
+    # 256-byte row, out at byte 128), but a shift into x's bytes is caught
+    assert fwd_ex(out=FAKE + 130, out_dtype=2, out_stride=128, x=FAKE, x_stride=128) == -5
+    assert add_ex(k=2, strides=[64, 32]) == -2             # a partial's stride below hidden
+    assert add_ex(res_stride=10) == -2
+    assert add_ex(residual=0) == -1
+    assert add_ex(k=0) == -4
+    assert add_ex(residual=FAKE + (1 << 27) + 4, k=1) == -5  # residual overlaps the partial
+    assert add_ex(gamma_dtype=1) == -3
+    assert "dtype" in B.lib().rmsnorm_last_error().decode()
+
+
+def test_general_interface_plans():
+    plan = B.rmsnorm_plan_ex
+    assert plan(8192, 4096, 1, "bf16", "f32", "f32") == \
+        "vgpr<bf16,g=f32,o=f32,tpr=512,npt=1,wg=512,k=-1,nt>"
+    assert plan(8192, 4096, 1, "bf16", "bf16", "bf16") == B.rmsnorm_plan(8192, 4096, 1, "bf16")
+    assert plan(512, 2048, 0, "f32", "f32", "bf16").startswith("vgpr<f32,g=f32,o=bf16,tpr=512")
+    assert plan(4096, 8192, 8, "f16", "f32", "f16").startswith("stream<f16,g=f32,o=f16,v8,")
+    assert "lds" in plan(100, 16384, 1, "bf16", "f32", "f32")
+    assert "elem" in plan(10, 1595, 0, "f32", "f32", "f16")
+    # 8-byte aligned bases: 8-byte bf16 chunks would need 16-byte fp32 ones,
+    # so the data moves in 4-byte chunks (8 bytes of fp32 gamma and output)
+    assert ",v4," in plan(10, 4096, 1, "bf16", "f32", "f32", align=8)
+    assert "elem" in plan(10, 4096, 1, "bf16", "f32", "f32", align=4)
+    assert "reread" in plan(10, 100000, 1, "bf16", "bf16", "f32")
+    for k in range(0, 17):
+        assert plan(3, 777 * 8, k, "bf16", "f32", "f16")
+    with pytest.raises(B.RmsnormError):
+        plan(3, 64, 0, "bf16", "f16", "bf16")
+
+
+def test_general_interface_variant_tables():
+    for d, n in (("bf16", 60), ("f16", 60), ("f32", 48)):
+        for g in sorted({d, "f32"}):
+            for o in ("f32", "f16", "bf16"):
+                names = B.rmsnorm_variants_ex(d, g, o)
+                if g == d == o:
+                    assert names == B.rmsnorm_variants(d)
+                    continue
+                assert len(names) == len(set(names)) == n, (d, g, o, len(names))
+                assert all(f"<{d},g={g},o={o}," in v for v in names)
