@@ -120,11 +120,15 @@ def cpu_baseline(w, target_cpu_seconds: float = 12.0, max_passes: int = 40) -> d
                                         "one thread"}}
 
 
-def stream_ceiling(w, dev: str = "cuda:0", steps: int = 60, rotate_gib: float = 1.0) -> dict:
+def stream_ceiling(w, dev: str = "cuda:0", steps: int = 60, rotate_gib: float = 1.0,
+                   inplace: bool = False) -> dict:
     """HBM bandwidth of a plain streaming kernel (libstreamprobe.so) moving the
-    same bytes as one step of the workload: K+1 read streams and 2 write
-    streams for the fused form, 1 and 1 for the plain form, each the size of
-    one [rows, hidden] tensor, with the same buffer rotation."""
+    same bytes as one step of the workload, with the kernel's aliasing: the
+    fused form reads K partials and the residual and writes the residual in
+    place and the output (a separate buffer, or the first partial with
+    ``inplace``); the plain form reads x and writes the output; the block sum
+    only reads.  Each stream is one [rows, hidden] tensor; buffers rotate as
+    in the benchmark."""
     import ctypes
     import torch
     path = os.path.join(ROOT, "row_wise_normalization_rmsnorm_amd", "libstreamprobe.so")
@@ -132,13 +136,22 @@ def stream_ceiling(w, dev: str = "cuda:0", steps: int = 60, rotate_gib: float = 
     lib.stream_probe.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int,
                                  ctypes.POINTER(ctypes.c_void_p), ctypes.c_int, ctypes.c_int64,
                                  ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
-    nr, nw = (w.k + 1, 2) if w.fused else ((1, 0) if w.op == "block_sum" else (1, 1))
+    if w.op == "block_sum":
+        nr, writes = 1, []
+    elif w.fused:
+        nr = w.k + 1                                          # p0..p(K-1), residual
+        writes = [w.k, 0 if inplace else nr]                  # residual in place, output
+    else:
+        nr = 1
+        writes = [0 if inplace else 1]
+    nw = len(writes)
+    nbuf = max([nr] + [j + 1 for j in writes])
     tensor_bytes = w.rows * w.hidden * w.itemsize
     n16 = tensor_bytes // 16
-    set_bytes = (nr + nw) * tensor_bytes
+    set_bytes = nbuf * tensor_bytes
     nsets = max(1, int(-(-rotate_gib * (1 << 30) // set_bytes)))
     bufs = [[torch.empty(n16 * 16, dtype=torch.uint8, device=dev).fill_(j + 1)
-             for j in range(nr + nw)] for _ in range(nsets)]
+             for j in range(nbuf)] for _ in range(nsets)]
     sink = torch.zeros(64, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     best = None
@@ -146,7 +159,7 @@ def stream_ceiling(w, dev: str = "cuda:0", steps: int = 60, rotate_gib: float = 
         args = []
         for b in bufs:
             ra = (ctypes.c_void_p * nr)(*[t.data_ptr() for t in b[:nr]])
-            wa = (ctypes.c_void_p * max(nw, 1))(*[t.data_ptr() for t in b[nr:]])
+            wa = (ctypes.c_void_p * max(nw, 1))(*[b[j].data_ptr() for j in writes])
             args.append((ra, wa))
 
         def launch(i):
@@ -169,7 +182,8 @@ def stream_ceiling(w, dev: str = "cuda:0", steps: int = 60, rotate_gib: float = 
         gbs = (nr + nw) * tensor_bytes / us / 1e3
         if best is None or gbs > best["value"]:
             best = {"value": round(gbs, 1), "unit": "GB/s", "us": round(us, 2), "grid": grid}
-    best.update({"reads": nr, "writes": nw, "kind": "plain nontemporal 16-byte streaming kernel",
+    best.update({"reads": nr, "writes": nw, "writes_in_place": sum(j < nr for j in writes),
+                 "kind": "plain nontemporal 16-byte streaming kernel",
                  "frac_of_peak": round(best["value"] / HBM_PEAK_GBS, 4)})
     del bufs
     return best
@@ -197,6 +211,52 @@ def latency(step, n: int, flush_bytes: int = 0) -> dict:
     q = lambda f: round(us[min(n - 1, int(f * n))], 3)  # noqa: E731
     return {"median_us": q(0.5), "p10_us": q(0.1), "p90_us": q(0.9), "launches": n,
             "flush_bytes": flush_bytes}
+
+
+def sync_latency(step, n: int) -> dict:
+    """"kernel-sync" mode: host wall time of one launch followed by a
+    synchronisation, median over n (context: includes launch overhead)."""
+    import statistics
+    import torch
+    ts = []
+    torch.cuda.synchronize()
+    for i in range(n):
+        t0 = time.perf_counter()
+        step(i)
+        torch.cuda.synchronize()
+        ts.append((time.perf_counter() - t0) * 1e6)
+    return {"median_us": round(statistics.median(ts), 3), "launches": n}
+
+
+def graph_replay(step, n: int, reps: int = 5) -> dict:
+    """n launches captured once in a HIP graph and replayed: the device-side
+    rate with no per-launch host work (context for launch-bound sizes)."""
+    import statistics
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(0)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n):
+            step(i)
+    g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    per = []
+    for _ in range(reps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        per.append(e0.elapsed_time(e1) * 1e3 / n)
+    del g
+    return {"us_per_launch": round(statistics.median(per), 3), "launches": n, "replays": reps}
 
 
 def sweep(w, step, a, B) -> int:
@@ -245,6 +305,75 @@ def sweep(w, step, a, B) -> int:
     return 0
 
 
+# read/write mixes of the ceiling sweep: (name, read streams, write streams
+# given as indices into the buffers -- an index below the read count writes
+# that read stream in place)
+CEILING_PATTERNS = [
+    ("read 1", 1, []), ("read 2", 2, []), ("write 1", 0, [0]), ("write 2", 0, [0, 1]),
+    ("copy 1R1W", 1, [1]), ("2R2W distinct", 2, [2, 3]),
+    ("2R2W, one write in place (fused K=1)", 2, [1, 2]),
+    ("2R2W, both writes in place", 2, [1, 0]),
+    ("9R2W, one write in place (fused K=8)", 9, [8, 9]),
+]
+
+
+def ceiling_sweep(stream_mib: int = 64, steps: int = 40) -> int:
+    """Time libstreamprobe.so over every read/write mix above, every grid,
+    workgroup size and unroll it offers; streams of stream_mib MiB rotated
+    through >= 1 GiB.  One JSON line per configuration."""
+    import ctypes
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "row_wise_normalization_rmsnorm_amd", "libstreamprobe.so"))
+    vp = ctypes.c_void_p
+    lib.stream_probe_shape.argtypes = [ctypes.POINTER(vp), ctypes.c_int, ctypes.POINTER(vp),
+                                       ctypes.c_int, ctypes.c_int64, vp, ctypes.c_int, ctypes.c_int,
+                                       ctypes.c_int, vp]
+    nbytes = stream_mib << 20
+    n16 = nbytes // 16
+    sink = torch.zeros(64, dtype=torch.uint8, device="cuda:0")
+    stream = torch.cuda.current_stream()
+    for name, nr, writes in CEILING_PATTERNS:
+        nbuf = max([nr] + [j + 1 for j in writes])
+        nsets = max(1, -(-(1 << 30) // (nbuf * nbytes)))
+        bufs = [[torch.empty(nbytes, dtype=torch.uint8, device="cuda:0").fill_(j + 1)
+                 for j in range(nbuf)] for _ in range(nsets)]
+        args = [((vp * max(nr, 1))(*[t.data_ptr() for t in b[:nr]]),
+                 (vp * max(len(writes), 1))(*[b[j].data_ptr() for j in writes])) for b in bufs]
+        moved = (nr + len(writes)) * nbytes
+        best = None
+        for grid in (1024, 2048, 4096, 8192, 16384):
+            for block in (256, 512, 1024):
+                for unroll in (1, 2, 4, 8):
+                    def launch(i):
+                        ra, wa = args[i % nsets]
+                        rc = lib.stream_probe_shape(ra, nr, wa, len(writes), n16, sink.data_ptr(),
+                                                    grid, block, unroll, stream.cuda_stream)
+                        if rc != 0:
+                            raise RuntimeError(f"stream_probe_shape failed: {rc}")
+                    for i in range(3):
+                        launch(i)
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    torch.cuda.synchronize()
+                    e0.record(stream)
+                    for i in range(steps):
+                        launch(i)
+                    e1.record(stream)
+                    torch.cuda.synchronize()
+                    us = e0.elapsed_time(e1) * 1e3 / steps
+                    row = {"pattern": name, "reads": nr, "writes": len(writes),
+                           "in_place": sum(j < nr for j in writes), "grid": grid, "block": block,
+                           "unroll": unroll, "us": round(us, 3), "gbs": round(moved / us / 1e3, 1)}
+                    print(json.dumps(row), flush=True)
+                    if best is None or row["gbs"] > best["gbs"]:
+                        best = row
+        print(f"[ceiling] {name}: best {best['gbs']} GB/s (grid {best['grid']}, block "
+              f"{best['block']}, unroll {best['unroll']})", file=sys.stderr, flush=True)
+        del bufs
+        torch.cuda.empty_cache()
+    return 0
+
+
 def copy_calibration() -> None:
     """A plain device copy of known size (1 GiB), for scaling the HBM byte
     counters read by rocprofv3 --pmc."""
@@ -266,6 +395,9 @@ def main() -> int:
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--ceiling-sweep", action="store_true",
+                    help="time the plain streaming probe over read/write mixes and launch "
+                         "shapes (one JSON line each) and exit")
     ap.add_argument("--sweep", action="store_true",
                     help="time every compiled kernel variant that can run the workload "
                          "(forced through RMSNORM_VARIANT) and print one line per variant")
@@ -273,6 +405,8 @@ def main() -> int:
     ap.add_argument("--variant-filter", default="", help="sweep only variants containing this")
     ap.add_argument("--no-ceiling", action="store_true",
                     help="skip the streaming-ceiling probe")
+    ap.add_argument("--inplace", action="store_true",
+                    help="write the output over the first input instead of a separate buffer")
     ap.add_argument("--rotate-bytes", type=float, default=1.0,
                     help="GiB of distinct buffers rotated through (cold cache)")
     a = ap.parse_args()
@@ -291,13 +425,19 @@ def main() -> int:
     if a.copy_calibration:
         copy_calibration()
         return 0
+    if a.ceiling_sweep:
+        return ceiling_sweep()
 
     w = WORKLOADS[a.workload or HEADLINE]
     dev = "cuda:0"
     B.lib()
     print(f"[bench] {w.describe()}: generating inputs", file=sys.stderr, flush=True)
     base = I.make_inputs(w, device=dev)
+    # distinct device bytes of one set of buffers (the output shares the
+    # first input's memory with --inplace)
     set_bytes = w.algorithmic_bytes()
+    if a.inplace and w.op != "block_sum":
+        set_bytes -= w.rows * w.hidden * w.itemsize
     nsets = max(1, int(-(-a.rotate_bytes * (1 << 30) // set_bytes)))
     sets = []
     for i in range(nsets):
@@ -308,7 +448,10 @@ def main() -> int:
             s["out"] = torch.empty(1, device=dev,
                                    dtype=torch.int32 if w.dtype == "i8" else torch.float32)
         else:
-            s["out"] = torch.empty_like(s["residual"] if w.fused else s["x"])
+            if a.inplace:  # the output written over the (first) input, as the fused
+                s["out"] = s["partials"][0] if w.fused else s["x"]  # kernel of the pages does
+            else:
+                s["out"] = torch.empty_like(s["residual"] if w.fused else s["x"])
         sets.append(s)
     del base
     if w.op == "block_sum":
@@ -360,9 +503,10 @@ def main() -> int:
     lat = {"batched": latency(step, min(a.steps, 200))}
     if nbytes < (64 << 20):
         lat["flushed"] = latency(step, min(a.steps, 100), flush_bytes=1 << 30)
+        lat["sync"] = sync_latency(step, min(a.steps, 100))
+        lat["graph"] = graph_replay(step, min(a.steps, 200))
     for kind, l in lat.items():
-        print(f"[bench] per-launch ({kind}): median {l['median_us']} us, p10 {l['p10_us']}, "
-              f"p90 {l['p90_us']}", file=sys.stderr, flush=True)
+        print(f"[bench] per-launch ({kind}): {json.dumps(l)}", file=sys.stderr, flush=True)
 
     traffic = traffic_for(kernel, w.name, w.op)
     metric = ("achieved HBM GB/s (% of peak) + rows/s, add_rmsnorm bf16 8192x4096"
@@ -382,6 +526,7 @@ def main() -> int:
         "data": "synthetic (seeded N(0,1) / U(0.5,1.5) inputs, resident in HBM)",
         "config": {"workload": w.name, "op": w.op, "rows": w.rows, "hidden": w.hidden,
                    "k": w.k, "eps": w.eps, "kernel": kernel, "rotating_sets": nsets,
+                   "out_over_input": bool(a.inplace),
                    "algorithmic_bytes_per_step": nbytes},
         "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "rows_per_s": round(rows_per_s, 1),
@@ -394,7 +539,7 @@ def main() -> int:
     if not a.no_ceiling:
         del sets
         torch.cuda.empty_cache()
-        ceil = stream_ceiling(w)
+        ceil = stream_ceiling(w, inplace=a.inplace)
         ceil["kernel_frac_of_ceiling"] = round(gbs / ceil["value"], 4)
         result["stream_ceiling"] = ceil
         print(f"[bench] streaming ceiling for this mix: {ceil['value']:.0f} GB/s; kernel at "

@@ -4,7 +4,8 @@
 // the RMSNorm library).
 //
 // stream_probe(reads[], nr, writes[], nw, n16, grid, stream): every lane moves
-// 16-byte chunks, 4 per step, with nontemporal loads and stores, over nr read
+// 16-byte chunks, 4 per step (256-lane workgroups; stream_probe_shape picks
+// other shapes), with nontemporal loads and stores, over nr read
 // streams and nw write streams of n16 chunks each.  The written value is the
 // XOR of the read chunks, so the loads cannot be dropped; with nw == 0 the
 // XOR is stored to writes' sink slot only if it equals an impossible value.
@@ -23,41 +24,51 @@ struct Streams {
   u32x4* w[kMaxStreams];
 };
 
-__global__ __launch_bounds__(kBlock) void probe_kernel(Streams s, int nr, int nw, int64_t n,
-                                                       u32x4* sink) {
+template <int BLOCK, int UNROLL>
+__global__ __launch_bounds__(BLOCK) void probe_kernel(Streams s, int nr, int nw, int64_t n,
+                                                      u32x4* sink) {
   u32x4 keep = {0u, 0u, 0u, 0u};
-  const int64_t step = (int64_t)gridDim.x * kBlock * kUnroll;
-  for (int64_t i0 = (int64_t)blockIdx.x * kBlock * kUnroll + threadIdx.x; i0 < n; i0 += step) {
-    u32x4 acc[kUnroll];
+  const int64_t step = (int64_t)gridDim.x * BLOCK * UNROLL;
+  for (int64_t i0 = (int64_t)blockIdx.x * BLOCK * UNROLL + threadIdx.x; i0 < n; i0 += step) {
+    u32x4 acc[UNROLL];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) acc[u] = u32x4{(uint32_t)u, 0u, 0u, 0u};
+    for (int u = 0; u < UNROLL; ++u) acc[u] = u32x4{(uint32_t)u, 0u, 0u, 0u};
     for (int j = 0; j < nr; ++j) {
-      u32x4 v[kUnroll];
+      u32x4 v[UNROLL];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int64_t i = i0 + (int64_t)u * kBlock;
+      for (int u = 0; u < UNROLL; ++u) {
+        const int64_t i = i0 + (int64_t)u * BLOCK;
         v[u] = i < n ? __builtin_nontemporal_load(s.r[j] + i) : u32x4{0u, 0u, 0u, 0u};
       }
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) acc[u] ^= v[u];
+      for (int u = 0; u < UNROLL; ++u) acc[u] ^= v[u];
     }
     for (int j = 0; j < nw; ++j) {
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int64_t i = i0 + (int64_t)u * kBlock;
+      for (int u = 0; u < UNROLL; ++u) {
+        const int64_t i = i0 + (int64_t)u * BLOCK;
         if (i < n) __builtin_nontemporal_store(acc[u], s.w[j] + i);
       }
     }
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) keep ^= acc[u];
+    for (int u = 0; u < UNROLL; ++u) keep ^= acc[u];
   }
   if (nw == 0 && keep.x == 0x9e3779b9u && keep.y == 0x7f4a7c15u) sink[0] = keep;
 }
 
+template <int BLOCK, int UNROLL>
+void launch(Streams s, int nr, int nw, int64_t n16, int grid, void* sink, void* stream) {
+  hipLaunchKernelGGL((probe_kernel<BLOCK, UNROLL>), dim3(grid), dim3(BLOCK), 0,
+                     (hipStream_t)stream, s, nr, nw, n16, static_cast<u32x4*>(sink));
+}
+
 }  // namespace
 
-extern "C" int stream_probe(const void* const* reads, int nr, void* const* writes, int nw,
-                            int64_t n16, void* sink, int grid, void* stream) {
+// stream_probe_shape: the same with a chosen workgroup size (256, 512 or
+// 1024) and chunks in flight per lane and stream (1, 2, 4 or 8).
+extern "C" int stream_probe_shape(const void* const* reads, int nr, void* const* writes, int nw,
+                                  int64_t n16, void* sink, int grid, int block, int unroll,
+                                  void* stream) {
   if (nr < 0 || nw < 0 || nr > kMaxStreams || nw > kMaxStreams || n16 < 0 || grid < 1 || !sink)
     return -1;
   Streams s{};
@@ -69,7 +80,17 @@ extern "C" int stream_probe(const void* const* reads, int nr, void* const* write
     if (!writes[j]) return -1;
     s.w[j] = static_cast<u32x4*>(writes[j]);
   }
-  hipLaunchKernelGGL(probe_kernel, dim3(grid), dim3(kBlock), 0, (hipStream_t)stream, s, nr, nw,
-                     n16, static_cast<u32x4*>(sink));
+#define PROBE_CASE(B, U) \
+  if (block == B && unroll == U) launch<B, U>(s, nr, nw, n16, grid, sink, stream); else
+  PROBE_CASE(256, 1) PROBE_CASE(256, 2) PROBE_CASE(256, 4) PROBE_CASE(256, 8)
+  PROBE_CASE(512, 1) PROBE_CASE(512, 2) PROBE_CASE(512, 4) PROBE_CASE(512, 8)
+  PROBE_CASE(1024, 1) PROBE_CASE(1024, 2) PROBE_CASE(1024, 4) PROBE_CASE(1024, 8)
+  return -1;
+#undef PROBE_CASE
   return hipGetLastError() == hipSuccess ? 0 : -7;
+}
+
+extern "C" int stream_probe(const void* const* reads, int nr, void* const* writes, int nw,
+                            int64_t n16, void* sink, int grid, void* stream) {
+  return stream_probe_shape(reads, nr, writes, nw, n16, sink, grid, kBlock, kUnroll, stream);
 }

@@ -111,6 +111,39 @@ def sweep_summary(argv) -> int:
     return 0
 
 
+def ceiling_summary(argv) -> int:
+    """profiles/hbm_ceiling_sweep.md from the JSON lines of
+    ``bench.py --ceiling-sweep``: the best launch shape of the plain
+    streaming probe for every read/write mix, and the spread over shapes."""
+    ap = argparse.ArgumentParser()
+    ap.add_argument("jsonl")
+    a = ap.parse_args(argv)
+    rows = [json.loads(l) for l in open(a.jsonl) if l.startswith("{")]
+    order = []
+    for r in rows:
+        if r["pattern"] not in order:
+            order.append(r["pattern"])
+    md = os.path.join(ROOT, "profiles", "hbm_ceiling_sweep.md")
+    with open(md, "w") as f:
+        f.write("# HBM ceiling of a plain streaming kernel, by read/write mix\n\n")
+        f.write("Command: `python bench.py --ceiling-sweep` (libstreamprobe.so: 16-byte nontemporal "
+                "loads and stores, every lane `unroll` chunks in flight per stream, grid-stride "
+                "loop; 64 MiB per stream, buffers rotated through >= 1 GiB; HIP events over 40 "
+                "launches per shape).  Swept: grid 1024-16384 workgroups, workgroup 256/512/1024 "
+                "lanes, unroll 1/2/4/8 (60 shapes per mix).\n\n")
+        f.write("| mix | reads | writes (in place) | best GB/s | % of 8 TB/s | best shape "
+                "(grid, block, unroll) | median over shapes GB/s |\n|---|---|---|---|---|---|---|\n")
+        for name in order:
+            rs = [r for r in rows if r["pattern"] == name]
+            b = max(rs, key=lambda r: r["gbs"])
+            med = statistics.median(r["gbs"] for r in rs)
+            f.write(f"| {name} | {b['reads']} | {b['writes']} ({b['in_place']}) | {b['gbs']:.0f} | "
+                    f"{b['gbs'] / 80:.1f} | {b['grid']}, {b['block']}, {b['unroll']} | {med:.0f} |\n")
+        f.write(f"\n{len(rows)} configurations timed.\n")
+    print(md)
+    return 0
+
+
 def counters_summary(argv) -> int:
     """profiles/counters_<kernel>__<workload>.md from a rocprofv3 --pmc run of
     SQ_LDS_BANK_CONFLICT, SQ_INSTS_LDS, SQ_WAVES, SQ_WAVE_CYCLES, SQ_BUSY_CYCLES."""
@@ -143,6 +176,8 @@ def main() -> int:
         return sweep_summary(sys.argv[2:])
     if len(sys.argv) > 1 and sys.argv[1] == "counters":
         return counters_summary(sys.argv[2:])
+    if len(sys.argv) > 1 and sys.argv[1] == "ceiling":
+        return ceiling_summary(sys.argv[2:])
     ap = argparse.ArgumentParser()
     ap.add_argument("--workload", required=True)
     ap.add_argument("--plan", required=True, help="kernel variant name (bench.py prints it)")
