@@ -325,6 +325,8 @@ int run(Types t, void* out, int64_t out_stride, void* residual, int64_t res_stri
   const int sd = dtype_size(t.d), so = dtype_size(t.o), sg = dtype_size(t.g);
   if ((rc = stride_check("out", out_stride, rows, hidden, so))) return rc;
   if (fused && (rc = stride_check("residual", res_stride, rows, hidden, sd))) return rc;
+  // a single row has no stride: whatever was passed is never used
+  if (rows == 1) out_stride = res_stride = hidden;
   const Span o{out, out_stride * so, hidden * so, rows};
   const Span g{gamma, hidden * sg, hidden * sg, 1};
   const Span r{residual, res_stride * sd, hidden * sd, rows};
@@ -335,7 +337,7 @@ int run(Types t, void* out, int64_t out_stride, void* residual, int64_t res_stri
     char nm[32] = "x";
     if (fused) snprintf(nm, sizeof(nm), "partials[%d]", j);
     if (!partials[j]) return fail(RMSN_ERR_NULL, "%s is NULL", nm);
-    const int64_t st = part_strides ? part_strides[j] : hidden;
+    const int64_t st = part_strides && rows > 1 ? part_strides[j] : hidden;
     if ((rc = stride_check(nm, st, rows, hidden, sd))) return rc;
     const Span p{partials[j], st * sd, hidden * sd, rows};
     if (fused && overlap(r, p)) return fail(RMSN_ERR_ALIAS, "residual overlaps %s", nm);
