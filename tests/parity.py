@@ -88,3 +88,38 @@ def compare(dtype: str, gpu_out: torch.Tensor, ref: dict, gpu_residual: torch.Te
         if nz.any():
             stats["max_rel_err"] = float((np.abs(gv[ok][nz] - y64[ok][nz]) / np.abs(y64[ok][nz])).max())
     return stats
+
+
+# ---- kernel variants ----------------------------------------------------------
+
+def parse_variant(name):
+    kind = name.split("<")[0]
+    body = name[name.index("<") + 1:-1].split(",")
+    kv = dict(p.split("=") for p in body if "=" in p)
+    flags = [p for p in body if "=" not in p]
+    return kind, flags, {k: (int(v) if v.lstrip("-").isdigit() else v) for k, v in kv.items()}
+
+
+WIDTH_BYTES = {"vec": 16, "v8": 8, "v4": 4, "elem": 0}
+
+
+def variant_case(dtype, name):
+    """A (hidden, rows, k) that the named variant (over data dtype `dtype`)
+    can run, chosen so that a narrower chunk width is also the widest its row
+    length allows."""
+    kind, flags, kv = parse_variant(name)
+    s = 4 if dtype == "f32" else 2
+    V = 16 // s
+    kc = kv["k"]
+    k = 3 if kc == -1 else kc
+    if kind == "vgpr":
+        tpr, npt, wg = kv["tpr"], kv["npt"], kv["wg"]
+        chunks = max(1, tpr * npt - 3)
+        hidden = chunks * V
+        rows = 2 * (wg // tpr) + 1
+    else:
+        vb = WIDTH_BYTES[next(f for f in flags if f in WIDTH_BYTES)]
+        base = 3000 if "lds" in flags else (40000 if s == 2 else 20000)
+        hidden = base + {16: 0, 8: 8 // s, 4: 4 // s, 0: 1}[vb]
+        rows = 5
+    return hidden, rows, k

@@ -231,3 +231,49 @@ def test_rescaled_rows(dtype, monkeypatch):
             w, d = _rescue_case(dtype, hidden, 21, k, eps, seed=100 + i)
             check(w, d, f"rescaled rows {variant} H={hidden} eps={eps}")
     monkeypatch.delenv("RMSNORM_VARIANT", raising=False)
+
+
+def test_graph_capture_general_interface_and_block_sum():
+    """The general interface (strided view, fp32 gamma, fp32 output) and the
+    block sum (its completion counters reset by the kernel itself) captured
+    in one graph; every replay, with eager work in between, equals the eager
+    result bit for bit."""
+    w = I.case("bf16", 96, 3072, 1, seed=61)
+    d = I.make_inputs(w)
+    big = torch.zeros(96, 3200, dtype=torch.bfloat16, device=DEV)
+    p = big[:, 64:64 + 3072]
+    p.copy_(d["partials"][0].to(DEV))
+    r0 = d["residual"].to(DEV)
+    g = I.gamma(w, DEV, dtype="f32")
+    xs = I.make_inputs(I.case("bf16", 512, 1024, 0, seed=62))["x"].to(DEV).reshape(-1)
+    ws = torch.zeros(B.BRS_WORKSPACE_BYTES, dtype=torch.uint8, device=DEV)
+    r_e = r0.clone()
+    out_e = torch.empty(96, 3072, dtype=torch.float32, device=DEV)
+    B.add_rmsnorm_fwd_ex(out_e, r_e, [p], g, w.eps)
+    s_e = torch.empty(1, dtype=torch.float32, device=DEV)
+    B.block_all_reduce_sum_fwd(s_e, xs, ws)
+    torch.cuda.synchronize()
+    r = torch.empty_like(r0)
+    out = torch.empty_like(out_e)
+    s = torch.empty_like(s_e)
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        r.copy_(r0)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=side):
+            B.add_rmsnorm_fwd_ex(out, r, [p], g, w.eps)
+            B.block_all_reduce_sum_fwd(s, xs, ws)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        r.copy_(r0)
+        out.fill_(float("nan"))
+        s.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(r.view(torch.int16), r_e.view(torch.int16)), rep
+        assert torch.equal(out.view(torch.int32), out_e.view(torch.int32)), rep
+        assert torch.equal(s.view(torch.int32), s_e.view(torch.int32)), rep
+        assert int(ws[:B.BRS_WORKSPACE_HEADER].count_nonzero()) == 0, rep

@@ -165,3 +165,31 @@ def test_convenience_wrappers_pick_the_general_form():
     torch.cuda.synchronize()
     ref = P.run_oracle("bf16", w.eps, x=x.cpu(), gamma=I.gamma(w, dtype="f32"), out_dtype="f32")
     P.compare("f32", y.cpu(), ref, what="wrapper")
+
+
+@pytest.mark.parametrize("d,g,o", [c for c in COMBOS if not (c[0] == c[1] == c[2])])
+def test_every_mixed_variant(d, g, o, monkeypatch):
+    """Every compiled variant of each general combination, forced through
+    RMSNORM_VARIANT on a case it can run (contiguous rows)."""
+    names = B.rmsnorm_variants_ex(d, g, o)
+    assert names
+    say(f"[gpu] {len(names)} variants of {d},g={g},o={o}")
+    for i, name in enumerate(names):
+        hidden, rows, k = P.variant_case(d, name)
+        w = I.case(d, rows, hidden, k, seed=i, std=0.5)
+        monkeypatch.setenv("RMSNORM_VARIANT", name)
+        assert B.rmsnorm_plan_ex(rows, hidden, k, d, g, o) == name
+        inp = I.make_inputs(w)
+        gamma = I.gamma(w, DEV, dtype=g)
+        out = torch.full((rows, hidden), float("nan"), dtype=TD[o], device=DEV)
+        res = None
+        if k:
+            res = inp["residual"].to(DEV)
+            B.add_rmsnorm_fwd_ex(out, res, [p.to(DEV) for p in inp["partials"]], gamma, w.eps)
+        else:
+            B.rmsnorm_fwd_ex(out, inp["x"].to(DEV), gamma, w.eps)
+        torch.cuda.synchronize()
+        ref = P.run_oracle(d, w.eps, x=inp.get("x"), partials=inp.get("partials"),
+                           residual=inp.get("residual"), gamma=gamma.cpu(), out_dtype=o)
+        P.compare(o, out.cpu(), ref, res.cpu() if k else None, what=f"variant {name}", res_dtype=d)
+    monkeypatch.delenv("RMSNORM_VARIANT")

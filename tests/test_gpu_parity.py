@@ -163,44 +163,12 @@ def test_zero_rows_is_noop():
 
 # ---- every compiled variant -----------------------------------------------------
 
-def _parse(name):
-    kind = name.split("<")[0]
-    body = name[name.index("<") + 1:-1].split(",")
-    kv = dict(p.split("=") for p in body if "=" in p)
-    flags = [p for p in body if "=" not in p]
-    return kind, flags, {k: int(v) for k, v in kv.items()}
-
-
-WIDTH_BYTES = {"vec": 16, "v8": 8, "v4": 4, "elem": 0}
-
-
-def _variant_case(dtype, name):
-    """A (hidden, rows, k) the variant can run, chosen so that a narrower
-    chunk width is also the widest its row length allows."""
-    kind, flags, kv = _parse(name)
-    s = 4 if dtype == "f32" else 2
-    V = 16 // s
-    kc = kv["k"]
-    k = 3 if kc == -1 else kc
-    if kind == "vgpr":
-        tpr, npt, wg = kv["tpr"], kv["npt"], kv["wg"]
-        chunks = max(1, tpr * npt - 3)
-        hidden = chunks * V
-        rows = 2 * (wg // tpr) + 1
-    else:
-        vb = WIDTH_BYTES[next(f for f in flags if f in WIDTH_BYTES)]
-        base = 3000 if "lds" in flags else (40000 if s == 2 else 20000)
-        hidden = base + {16: 0, 8: 8 // s, 4: 4 // s, 0: 1}[vb]
-        rows = 5
-    return hidden, rows, k
-
-
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 def test_every_variant(dtype, monkeypatch):
     names = B.rmsnorm_variants(dtype)
     assert names
     for i, name in enumerate(names):
-        hidden, rows, k = _variant_case(dtype, name)
+        hidden, rows, k = P.variant_case(dtype, name)
         w = I.case(dtype, rows, hidden, k, seed=i, std=0.5)
         monkeypatch.setenv("RMSNORM_VARIANT", name)
         assert B.rmsnorm_plan(rows, hidden, k, dtype, align=16) == name
