@@ -2,7 +2,8 @@
 
 One step = one ``add_rmsnorm_fwd`` launch over the whole workload (every step
 of the path: load K partials and the residual, sum, write the residual, sum of
-squares, reduce, scale, normalise, store).  Inputs are seeded synthetic data
+squares, reduce, scale, normalise, store); ``--workload`` selects another
+workload (plain RMSNorm, or the block all-reduce sum).  Inputs are seeded synthetic data
 resident in HBM before timing starts.  Several copies of the buffers are
 rotated so that consecutive steps never find their inputs in the 256 MB
 Infinity Cache.  Timing: W untimed warm-up steps, then exactly K steps
@@ -13,8 +14,14 @@ Prints one JSON line.  ``roofline.achieved`` is the workload's algorithmic
 bytes per launch divided by the average launch duration; ``cpu_baseline``
 times the CPU oracle (row-parallel over the host cores) on the same workload.
 
+``per_launch`` (context) adds single-launch timings, and for small
+workloads a cache-flushed, a launch-and-synchronise and a graph-replay rate;
+``stream_ceiling`` is a plain streaming kernel moving the same bytes.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-       [--no-cpu-baseline] [--copy-calibration]
+       [--no-cpu-baseline] [--no-ceiling] [--inplace] [--rotate-bytes GIB]
+       python bench.py --workload NAME --sweep [--repeat R] [--variant-filter S]
+       python bench.py --ceiling-sweep | --copy-calibration
 """
 from __future__ import annotations
 

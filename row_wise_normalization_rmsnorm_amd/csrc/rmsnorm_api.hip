@@ -1,14 +1,17 @@
 // rmsnorm_api.hip -- the C ABI of librmsnorm.so (include/rmsnorm.h):
 // argument validation, aliasing rules, kernel choice, and the launch on the
-// caller's stream.  Host code only; the kernels live in kernels_<dtype>.hip.
+// caller's stream.  Host code only; the kernels live in kernels_<dtype>.hip
+// (single dtype) and kernels_mixed_<dtype>.hip (the general interface).
 //
 // Argument conventions follow the pages' problem statement: x[rows, hidden]
 // with gamma[hidden] of the same dtype, a float eps and an out-of-place
 // output (page "RMSNorm kernel", section 2, naive kernel signature), and for
 // the fused form an input, a residual updated in place and a weight over
 // num_tokens x hidden_size (page "Tokenweave fused-RMSNorm-AR kernel", "Code
-// walkthrough").  Sizes are validated before any launch, as the torch
-// bindings on page "Block All Reduce CUDA代码学习" check dtype and size before
+// walkthrough").  The *_ex entry points take the same page's [..., hidden_dim]
+// reading further: per-tensor row strides, an fp32 gamma and an output dtype
+// of its own.  Sizes are validated before any launch, as the torch bindings
+// on page "Block All Reduce CUDA代码学习" check dtype and size before
 // dispatching.
 #include <hip/hip_runtime.h>
 #include <math.h>
