@@ -334,7 +334,7 @@ def ceiling_sweep(stream_mib: int = 64, steps: int = 40) -> int:
     vp = ctypes.c_void_p
     lib.stream_probe_shape.argtypes = [ctypes.POINTER(vp), ctypes.c_int, ctypes.POINTER(vp),
                                        ctypes.c_int, ctypes.c_int64, vp, ctypes.c_int, ctypes.c_int,
-                                       ctypes.c_int, vp]
+                                       ctypes.c_int, ctypes.c_int, vp]
     nbytes = stream_mib << 20
     n16 = nbytes // 16
     sink = torch.zeros(64, dtype=torch.uint8, device="cuda:0")
@@ -348,34 +348,36 @@ def ceiling_sweep(stream_mib: int = 64, steps: int = 40) -> int:
                  (vp * max(len(writes), 1))(*[b[j].data_ptr() for j in writes])) for b in bufs]
         moved = (nr + len(writes)) * nbytes
         best = None
-        for grid in (1024, 2048, 4096, 8192, 16384):
-            for block in (256, 512, 1024):
-                for unroll in (1, 2, 4, 8):
-                    def launch(i):
-                        ra, wa = args[i % nsets]
-                        rc = lib.stream_probe_shape(ra, nr, wa, len(writes), n16, sink.data_ptr(),
-                                                    grid, block, unroll, stream.cuda_stream)
-                        if rc != 0:
-                            raise RuntimeError(f"stream_probe_shape failed: {rc}")
-                    for i in range(3):
-                        launch(i)
-                    e0 = torch.cuda.Event(enable_timing=True)
-                    e1 = torch.cuda.Event(enable_timing=True)
-                    torch.cuda.synchronize()
-                    e0.record(stream)
-                    for i in range(steps):
-                        launch(i)
-                    e1.record(stream)
-                    torch.cuda.synchronize()
-                    us = e0.elapsed_time(e1) * 1e3 / steps
-                    row = {"pattern": name, "reads": nr, "writes": len(writes),
-                           "in_place": sum(j < nr for j in writes), "grid": grid, "block": block,
-                           "unroll": unroll, "us": round(us, 3), "gbs": round(moved / us / 1e3, 1)}
-                    print(json.dumps(row), flush=True)
-                    if best is None or row["gbs"] > best["gbs"]:
-                        best = row
+        shapes = [(g, b, u, c) for c in (0, 1) for g in (1024, 2048, 4096, 8192, 16384)
+                  for b in (256, 512, 1024) for u in (1, 2, 4, 8)]
+        for grid, block, unroll, contig in shapes:
+            def launch(i):
+                ra, wa = args[i % nsets]
+                rc = lib.stream_probe_shape(ra, nr, wa, len(writes), n16, sink.data_ptr(),
+                                            grid, block, unroll, contig, stream.cuda_stream)
+                if rc != 0:
+                    raise RuntimeError(f"stream_probe_shape failed: {rc}")
+            for i in range(3):
+                launch(i)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for i in range(steps):
+                launch(i)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / steps
+            row = {"pattern": name, "reads": nr, "writes": len(writes),
+                   "in_place": sum(j < nr for j in writes), "grid": grid, "block": block,
+                   "unroll": unroll, "layout": "contiguous" if contig else "grid-stride",
+                   "us": round(us, 3), "gbs": round(moved / us / 1e3, 1)}
+            print(json.dumps(row), flush=True)
+            if best is None or row["gbs"] > best["gbs"]:
+                best = row
         print(f"[ceiling] {name}: best {best['gbs']} GB/s (grid {best['grid']}, block "
-              f"{best['block']}, unroll {best['unroll']})", file=sys.stderr, flush=True)
+              f"{best['block']}, unroll {best['unroll']}, {best['layout']})", file=sys.stderr,
+              flush=True)
         del bufs
         torch.cuda.empty_cache()
     return 0

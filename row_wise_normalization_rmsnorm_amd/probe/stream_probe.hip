@@ -24,12 +24,26 @@ struct Streams {
   u32x4* w[kMaxStreams];
 };
 
-template <int BLOCK, int UNROLL>
+// CONTIG = false: grid-stride loop (workgroup b takes tiles b, b + grid, ...);
+// CONTIG = true: workgroup b streams one contiguous range of n / grid chunks.
+template <int BLOCK, int UNROLL, bool CONTIG>
 __global__ __launch_bounds__(BLOCK) void probe_kernel(Streams s, int nr, int nw, int64_t n,
                                                       u32x4* sink) {
   u32x4 keep = {0u, 0u, 0u, 0u};
-  const int64_t step = (int64_t)gridDim.x * BLOCK * UNROLL;
-  for (int64_t i0 = (int64_t)blockIdx.x * BLOCK * UNROLL + threadIdx.x; i0 < n; i0 += step) {
+  const int64_t tile = (int64_t)BLOCK * UNROLL;
+  int64_t begin, end, step;
+  if constexpr (CONTIG) {
+    const int64_t tiles = (n + tile - 1) / tile;
+    const int64_t per = (tiles + gridDim.x - 1) / gridDim.x;
+    begin = (int64_t)blockIdx.x * per * tile;
+    end = begin + per * tile < n ? begin + per * tile : n;
+    step = tile;
+  } else {
+    begin = (int64_t)blockIdx.x * tile;
+    end = n;
+    step = (int64_t)gridDim.x * tile;
+  }
+  for (int64_t i0 = begin + threadIdx.x; i0 < end; i0 += step) {
     u32x4 acc[UNROLL];
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) acc[u] = u32x4{(uint32_t)u, 0u, 0u, 0u};
@@ -38,7 +52,7 @@ __global__ __launch_bounds__(BLOCK) void probe_kernel(Streams s, int nr, int nw,
 #pragma unroll
       for (int u = 0; u < UNROLL; ++u) {
         const int64_t i = i0 + (int64_t)u * BLOCK;
-        v[u] = i < n ? __builtin_nontemporal_load(s.r[j] + i) : u32x4{0u, 0u, 0u, 0u};
+        v[u] = i < end ? __builtin_nontemporal_load(s.r[j] + i) : u32x4{0u, 0u, 0u, 0u};
       }
 #pragma unroll
       for (int u = 0; u < UNROLL; ++u) acc[u] ^= v[u];
@@ -47,7 +61,7 @@ __global__ __launch_bounds__(BLOCK) void probe_kernel(Streams s, int nr, int nw,
 #pragma unroll
       for (int u = 0; u < UNROLL; ++u) {
         const int64_t i = i0 + (int64_t)u * BLOCK;
-        if (i < n) __builtin_nontemporal_store(acc[u], s.w[j] + i);
+        if (i < end) __builtin_nontemporal_store(acc[u], s.w[j] + i);
       }
     }
 #pragma unroll
@@ -57,18 +71,24 @@ __global__ __launch_bounds__(BLOCK) void probe_kernel(Streams s, int nr, int nw,
 }
 
 template <int BLOCK, int UNROLL>
-void launch(Streams s, int nr, int nw, int64_t n16, int grid, void* sink, void* stream) {
-  hipLaunchKernelGGL((probe_kernel<BLOCK, UNROLL>), dim3(grid), dim3(BLOCK), 0,
-                     (hipStream_t)stream, s, nr, nw, n16, static_cast<u32x4*>(sink));
+void launch(Streams s, int nr, int nw, int64_t n16, int grid, bool contig, void* sink,
+            void* stream) {
+  if (contig)
+    hipLaunchKernelGGL((probe_kernel<BLOCK, UNROLL, true>), dim3(grid), dim3(BLOCK), 0,
+                       (hipStream_t)stream, s, nr, nw, n16, static_cast<u32x4*>(sink));
+  else
+    hipLaunchKernelGGL((probe_kernel<BLOCK, UNROLL, false>), dim3(grid), dim3(BLOCK), 0,
+                       (hipStream_t)stream, s, nr, nw, n16, static_cast<u32x4*>(sink));
 }
 
 }  // namespace
 
 // stream_probe_shape: the same with a chosen workgroup size (256, 512 or
-// 1024) and chunks in flight per lane and stream (1, 2, 4 or 8).
+// 1024), chunks in flight per lane and stream (1, 2, 4 or 8), and layout
+// (contig != 0: each workgroup streams one contiguous range).
 extern "C" int stream_probe_shape(const void* const* reads, int nr, void* const* writes, int nw,
                                   int64_t n16, void* sink, int grid, int block, int unroll,
-                                  void* stream) {
+                                  int contig, void* stream) {
   if (nr < 0 || nw < 0 || nr > kMaxStreams || nw > kMaxStreams || n16 < 0 || grid < 1 || !sink)
     return -1;
   Streams s{};
@@ -81,7 +101,7 @@ extern "C" int stream_probe_shape(const void* const* reads, int nr, void* const*
     s.w[j] = static_cast<u32x4*>(writes[j]);
   }
 #define PROBE_CASE(B, U) \
-  if (block == B && unroll == U) launch<B, U>(s, nr, nw, n16, grid, sink, stream); else
+  if (block == B && unroll == U) launch<B, U>(s, nr, nw, n16, grid, contig != 0, sink, stream); else
   PROBE_CASE(256, 1) PROBE_CASE(256, 2) PROBE_CASE(256, 4) PROBE_CASE(256, 8)
   PROBE_CASE(512, 1) PROBE_CASE(512, 2) PROBE_CASE(512, 4) PROBE_CASE(512, 8)
   PROBE_CASE(1024, 1) PROBE_CASE(1024, 2) PROBE_CASE(1024, 4) PROBE_CASE(1024, 8)
@@ -92,5 +112,5 @@ extern "C" int stream_probe_shape(const void* const* reads, int nr, void* const*
 
 extern "C" int stream_probe(const void* const* reads, int nr, void* const* writes, int nw,
                             int64_t n16, void* sink, int grid, void* stream) {
-  return stream_probe_shape(reads, nr, writes, nw, n16, sink, grid, kBlock, kUnroll, stream);
+  return stream_probe_shape(reads, nr, writes, nw, n16, sink, grid, kBlock, kUnroll, 0, stream);
 }

@@ -130,15 +130,20 @@ def ceiling_summary(argv) -> int:
                 "loads and stores, every lane `unroll` chunks in flight per stream, grid-stride "
                 "loop; 64 MiB per stream, buffers rotated through >= 1 GiB; HIP events over 40 "
                 "launches per shape).  Swept: grid 1024-16384 workgroups, workgroup 256/512/1024 "
-                "lanes, unroll 1/2/4/8 (60 shapes per mix).\n\n")
+                "lanes, unroll 1/2/4/8, and two layouts -- a grid-stride loop, or each workgroup "
+                "streaming one contiguous range (120 shapes per mix).\n\n")
         f.write("| mix | reads | writes (in place) | best GB/s | % of 8 TB/s | best shape "
-                "(grid, block, unroll) | median over shapes GB/s |\n|---|---|---|---|---|---|---|\n")
+                "(grid, block, unroll, layout) | best contiguous GB/s | median over shapes GB/s |\n"
+                "|---|---|---|---|---|---|---|---|\n")
         for name in order:
             rs = [r for r in rows if r["pattern"] == name]
             b = max(rs, key=lambda r: r["gbs"])
+            cont = [r["gbs"] for r in rs if r.get("layout") == "contiguous"]
             med = statistics.median(r["gbs"] for r in rs)
             f.write(f"| {name} | {b['reads']} | {b['writes']} ({b['in_place']}) | {b['gbs']:.0f} | "
-                    f"{b['gbs'] / 80:.1f} | {b['grid']}, {b['block']}, {b['unroll']} | {med:.0f} |\n")
+                    f"{b['gbs'] / 80:.1f} | {b['grid']}, {b['block']}, {b['unroll']}, "
+                    f"{b.get('layout', 'grid-stride')} | {max(cont) if cont else float('nan'):.0f} | "
+                    f"{med:.0f} |\n")
         f.write(f"\n{len(rows)} configurations timed.\n")
     print(md)
     return 0
