@@ -149,28 +149,46 @@ def ceiling_summary(argv) -> int:
     return 0
 
 
+COUNTERS = ["SQ_LDS_BANK_CONFLICT", "SQ_INSTS_LDS", "SQ_WAVES", "SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES",
+            "TCC_HIT_sum", "TCC_MISS_sum"]
+
+
 def counters_summary(argv) -> int:
-    """profiles/counters_<kernel>__<workload>.md from a rocprofv3 --pmc run of
-    SQ_LDS_BANK_CONFLICT, SQ_INSTS_LDS, SQ_WAVES, SQ_WAVE_CYCLES, SQ_BUSY_CYCLES."""
+    """profiles/counters_<kernel>__<workload>.md from one rocprofv3 --pmc run
+    of COUNTERS (LDS use and bank conflicts, waves, L2 hits and misses)."""
     ap = argparse.ArgumentParser()
     ap.add_argument("--workload", required=True)
     ap.add_argument("--plan", required=True)
     ap.add_argument("--symbol", required=True)
     ap.add_argument("dir")
     a = ap.parse_args(argv)
-    names = ["SQ_LDS_BANK_CONFLICT", "SQ_INSTS_LDS", "SQ_WAVES", "SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES"]
-    vals = {n: counter(a.dir, n, a.symbol) for n in names}
+    vals = {}
+    for n in COUNTERS:
+        try:
+            vals[n] = counter(a.dir, n, a.symbol)
+        except ValueError:
+            pass
     md = os.path.join(ROOT, "profiles", f"counters_{short_name(a.plan)}__{a.workload}.md")
     with open(md, "w") as f:
-        f.write(f"# LDS and wave counters: {a.plan} on {a.workload}\n\n")
-        f.write("Command: `rocprofv3 --pmc " + " ".join(names) + " --output-format csv -d <dir> -o run "
-                f"-- python bench.py --workload {a.workload} --steps 5 --warmup 1 --no-cpu-baseline "
-                "--no-ceiling`\n\n| counter | per dispatch (median) | dispatches |\n|---|---|---|\n")
-        for n in names:
-            f.write(f"| {n} | {vals[n][0]:,.0f} | {vals[n][1]} |\n")
-        lds, conf, waves = vals["SQ_INSTS_LDS"][0], vals["SQ_LDS_BANK_CONFLICT"][0], vals["SQ_WAVES"][0]
-        f.write(f"\nLDS instructions per wave: {lds / waves:.1f}; bank-conflict cycles per wave: "
-                f"{conf / waves:.1f} ({conf / max(lds, 1):.2f} per LDS instruction).\n")
+        f.write(f"# LDS, wave and L2 counters: {a.plan} on {a.workload}\n\n")
+        f.write("Command: `rocprofv3 --pmc " + " ".join(COUNTERS) + " --output-format csv -d <dir> "
+                f"-o run -- python bench.py --workload {a.workload} --steps 5 --warmup 1 "
+                "--no-cpu-baseline --no-ceiling`\n\n| counter | per dispatch (median) | dispatches |\n"
+                "|---|---|---|\n")
+        for n, (v, c) in vals.items():
+            f.write(f"| {n} | {v:,.0f} | {c} |\n")
+        if {"SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT", "SQ_WAVES"} <= set(vals):
+            lds, conf, waves = (vals[n][0] for n in ("SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT",
+                                                     "SQ_WAVES"))
+            f.write(f"\nLDS instructions per wave: {lds / waves:.1f}; bank-conflict cycles per "
+                    f"wave: {conf / waves:.1f} ({conf / max(lds, 1):.2f} per LDS instruction).\n")
+        if {"TCC_HIT_sum", "TCC_MISS_sum"} <= set(vals):
+            hit, miss = vals["TCC_HIT_sum"][0], vals["TCC_MISS_sum"][0]
+            f.write(f"L2 (TCC) requests per dispatch: {hit + miss:,.0f}, hit rate "
+                    f"{hit / max(hit + miss, 1):.3f}.  Hits include gamma, which every "
+                    f"workgroup reads from L2; whether data comes from HBM more than once is "
+                    f"settled by FETCH_SIZE / WRITE_SIZE in the traffic summary.\n")
+        f.write(f"\nKernel sources sha256: `{source_hash('block_sum' if 'block_sum' in a.symbol else 'rmsnorm')}`\n")
     print(md)
     return 0
 
