@@ -193,3 +193,46 @@ def test_every_mixed_variant(d, g, o, monkeypatch):
                            residual=inp.get("residual"), gamma=gamma.cpu(), out_dtype=o)
         P.compare(o, out.cpu(), ref, res.cpu() if k else None, what=f"variant {name}", res_dtype=d)
     monkeypatch.delenv("RMSNORM_VARIANT")
+
+
+def test_random_general_calls():
+    """Seeded random calls of the general interface: dtype triple, shape, K,
+    a pad (row pitch) and a base offset for every tensor independently."""
+    import numpy as np
+    rng = np.random.default_rng(77)
+    for t in range(60):
+        d, g, o = COMBOS[int(rng.integers(len(COMBOS)))]
+        hidden = int(rng.choice([int(rng.integers(1, 200)), int(rng.integers(200, 9000)),
+                                 int(rng.integers(9000, 30000))], p=[0.35, 0.5, 0.15]))
+        if rng.random() < 0.5:
+            hidden = max(8, hidden // 8 * 8)
+        k = int(rng.choice([0, 1, 2, 5]))
+        rows = int(rng.integers(1, 60))
+        rows = max(1, min(rows, (2 << 20) // (hidden * (k + 2))))
+        w = I.case(d, rows, hidden, k, seed=1000 + t, std=float(rng.choice([0.3, 1.0, 20.0])),
+                   eps=float(rng.choice([1e-6, 1e-5])))
+        inp = I.make_inputs(w)
+        gamma = I.gamma(w, DEV, dtype=g)
+
+        def emb(src, dt, fill=None):
+            pad = int(rng.choice([0, int(rng.integers(1, 40)), 8 * int(rng.integers(1, 6))]))
+            off = int(rng.choice([0, 0, int(rng.integers(0, pad + 1))]))
+            return Embedded(src, dt, pad, off, fill=fill)
+
+        out = emb(None, o, fill=(rows, hidden))
+        what = f"random general #{t}: {d},g={g},o={o} rows={rows} H={hidden} k={k}"
+        say(f"[gpu] {what}")
+        if k:
+            parts = [emb(p, d) for p in inp["partials"]]
+            res = emb(inp["residual"], d)
+            B.add_rmsnorm_fwd_ex(out.view, res.view, [p.view for p in parts], gamma, w.eps)
+        else:
+            parts, res = [emb(inp["x"], d)], None
+            B.rmsnorm_fwd_ex(out.view, parts[0].view, gamma, w.eps)
+        torch.cuda.synchronize()
+        ref = P.run_oracle(d, w.eps, x=inp.get("x"), partials=inp.get("partials"),
+                           residual=inp.get("residual"), gamma=gamma.cpu(), out_dtype=o)
+        P.compare(o, out.view.cpu().contiguous(), ref,
+                  res.view.cpu().contiguous() if res else None, what=what, res_dtype=d)
+        assert out.outside_intact() and all(p.outside_intact() for p in parts), what
+        assert res is None or res.outside_intact(), what
