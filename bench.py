@@ -421,8 +421,9 @@ def main() -> int:
     a = ap.parse_args()
 
     if a.gpus != 1:
-        print(f"bench.py: this build measures one GPU; --gpus {a.gpus} is not supported "
-              "(the path shards rows with no communication; see the design notes)",
+        print(f"bench.py measures one GPU; --gpus {a.gpus} is not supported "
+              "(rows are independent: each further GPU would run the same kernel on its own "
+              "share of the rows, with no communication)",
               file=sys.stderr)
         return 2
 

@@ -16,7 +16,7 @@
  *     walkthrough" (per token: reduced partials, + residual, residual stored
  *     back in place, sum of squares of the stored values in fp32, then
  *     rsqrt(variance/hidden + eps) and residual*scale*weight).
- * Readings taken where the pages are silent (each is listed in the design doc):
+ * Readings taken where the pages are silent:
  *   - the partials and the residual are summed in binary32, in the order
  *     p_0, ..., p_{k-1}, r, with the accumulator seeded by p_0 (not by +0.0,
  *     which would turn an all -0.0 sum into +0.0);
