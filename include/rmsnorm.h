@@ -167,6 +167,21 @@ int rmsnorm_plan_ex(int64_t rows, int64_t hidden, int k, int dtype, int gamma_dt
                     int out_dtype, int align, char* buf, int buflen);
 int rmsnorm_variants_ex(int dtype, int gamma_dtype, int out_dtype, char* buf, int buflen);
 
+/*
+ * rmsnorm_plan_call -- validate one call of the general interface exactly
+ * as add_rmsnorm_fwd_ex (residual != NULL) or rmsnorm_fwd_ex (residual ==
+ * NULL: then k == 1 and partials[0] is x) would, with these very pointers,
+ * strides and dtypes, and write the name of the kernel that call would
+ * launch into buf ("none" when rows == 0).  Launches nothing and touches no
+ * device memory: callers can check a call before recording it in a graph.
+ * Returns RMSN_OK or the error code the call would return.
+ */
+int rmsnorm_plan_call(void* out, int64_t out_stride, int out_dtype, void* residual,
+                      int64_t residual_stride, const void* const* partials,
+                      const int64_t* partial_strides, int k, int dtype, const void* gamma,
+                      int gamma_dtype, int64_t rows, int64_t hidden, float eps, char* buf,
+                      int buflen);
+
 #ifdef __cplusplus
 }
 #endif

@@ -22,7 +22,7 @@ DTYPE_NAME = {"f32": 0, "f16": 1, "bf16": 2}
 KMAX = 16
 EXPORTS = ("rmsnorm_fwd", "add_rmsnorm_fwd", "rmsnorm_strerror", "rmsnorm_last_error",
            "rmsnorm_plan", "rmsnorm_variants", "rmsnorm_fwd_ex", "add_rmsnorm_fwd_ex",
-           "rmsnorm_plan_ex", "rmsnorm_variants_ex")
+           "rmsnorm_plan_ex", "rmsnorm_variants_ex", "rmsnorm_plan_call")
 BLOCK_SUM_EXPORTS = ("block_all_reduce_sum",)
 
 # block all-reduce sum (include/block_sum.h)
@@ -77,6 +77,10 @@ def lib() -> ctypes.CDLL:
             l.rmsnorm_plan_ex.restype = c_int
             l.rmsnorm_variants_ex.argtypes = [c_int, c_int, c_int, ctypes.c_char_p, c_int]
             l.rmsnorm_variants_ex.restype = c_int
+            l.rmsnorm_plan_call.argtypes = [vp, i64, c_int, vp, i64, ctypes.POINTER(vp),
+                                            ctypes.POINTER(i64), c_int, c_int, vp, c_int, i64, i64,
+                                            c_float, ctypes.c_char_p, c_int]
+            l.rmsnorm_plan_call.restype = c_int
             l.block_all_reduce_sum.argtypes = [vp, vp, i64, c_int, vp, i64, vp]
             l.block_all_reduce_sum.restype = c_int
             _lib = l
@@ -148,30 +152,35 @@ def add_rmsnorm_fwd(out: torch.Tensor, residual: torch.Tensor, partials: Sequenc
                                  DTYPE_CODE[residual.dtype], _stream(residual, stream)))
 
 
-def row_view(t: torch.Tensor, what: str):
-    """(rows, hidden, row stride in elements) of a [..., hidden] device tensor
-    whose last dimension is contiguous and whose leading dimensions collapse
-    into one row stride (page "RMSNorm kernel", section 2: inputs are
-    [..., hidden_dim]).  Anything else raises: the binding never copies."""
-    if not t.is_cuda:
-        raise RmsnormError(-1, f"{what} must be a device tensor")
-    if t.dim() == 0:
+def collapse_rows(shape, strides, what: str = "tensor"):
+    """(rows, hidden, row stride in elements) of a [..., hidden] layout given
+    by its shape and element strides: the last dimension must be contiguous
+    and the leading dimensions must collapse into one row stride (page
+    "RMSNorm kernel", section 2: inputs are [..., hidden_dim]).  Raises
+    otherwise: the binding never copies."""
+    if len(shape) == 0:
         return 1, 1, 1
-    hidden = t.shape[-1]
-    if hidden > 1 and t.stride(-1) != 1:
+    hidden = shape[-1]
+    if hidden > 1 and strides[-1] != 1:
         raise RmsnormError(-2, f"{what}: the last dimension must be contiguous")
     rows = 1
-    for n in t.shape[:-1]:
+    for n in shape[:-1]:
         rows *= n
-    lead = [(n, st) for n, st in zip(t.shape[:-1], t.stride()[:-1]) if n != 1]
+    lead = [(n, st) for n, st in zip(shape[:-1], strides[:-1]) if n != 1]
     if not lead or rows == 0:
         return rows, hidden, max(hidden, 1)
-    stride = lead[-1][1]
     for (n0, s0), (n1, s1) in zip(lead[:-1], lead[1:]):
         if s0 != s1 * n1:
-            raise RmsnormError(-2, f"{what}: leading dimensions {tuple(t.shape[:-1])} with strides "
-                                   f"{tuple(t.stride()[:-1])} do not form one row stride")
-    return rows, hidden, stride
+            raise RmsnormError(-2, f"{what}: leading dimensions {tuple(shape[:-1])} with strides "
+                                   f"{tuple(strides[:-1])} do not form one row stride")
+    return rows, hidden, lead[-1][1]
+
+
+def row_view(t: torch.Tensor, what: str):
+    """collapse_rows of a device tensor."""
+    if not t.is_cuda:
+        raise RmsnormError(-1, f"{what} must be a device tensor")
+    return collapse_rows(tuple(t.shape), t.stride(), what)
 
 
 def rmsnorm_fwd_ex(out: torch.Tensor, x: torch.Tensor, gamma: torch.Tensor, eps: float,

@@ -314,10 +314,13 @@ int launch(const Plan& plan, rmsn::RowArgs a, void* stream) {
 
 // Both forms, every dtype combination and stride: validate, choose, launch.
 // residual == nullptr is plain RMSNorm (k == 1, partials[0] is x).  Strides
-// are in elements of each tensor's own dtype.
+// are in elements of each tensor's own dtype.  With dry != nullptr nothing is
+// launched: *dry receives the chosen variant (nullptr when rows == 0).
 int run(Types t, void* out, int64_t out_stride, void* residual, int64_t res_stride,
         const void* const* partials, const int64_t* part_strides, int k, const void* gamma,
-        int64_t rows, int64_t hidden, float eps, void* stream) {
+        int64_t rows, int64_t hidden, float eps, void* stream,
+        const rmsn::Variant** dry = nullptr) {
+  if (dry) *dry = nullptr;
   int rc = common_checks(t.d, rows, hidden, eps);
   if (rc) return rc;
   if ((rc = type_checks(t))) return rc;
@@ -359,6 +362,10 @@ int run(Types t, void* out, int64_t out_stride, void* residual, int64_t res_stri
   Plan plan;
   rc = choose(t, hidden, fused ? k : 0, al, &plan);
   if (rc) return rc;
+  if (dry) {
+    *dry = plan.v;
+    return RMSN_OK;
+  }
   a.out = out;
   a.out_stride = o.pitch;
   a.residual = residual;
@@ -485,6 +492,22 @@ int rmsnorm_plan(int64_t rows, int64_t hidden, int k, int dtype, int align, char
 int rmsnorm_plan_ex(int64_t rows, int64_t hidden, int k, int dtype, int gamma_dtype,
                     int out_dtype, int align, char* buf, int buflen) {
   return plan_name(Types{dtype, gamma_dtype, out_dtype}, rows, hidden, k, align, buf, buflen);
+}
+
+int rmsnorm_plan_call(void* out, int64_t out_stride, int out_dtype, void* residual,
+                      int64_t residual_stride, const void* const* partials,
+                      const int64_t* partial_strides, int k, int dtype, const void* gamma,
+                      int gamma_dtype, int64_t rows, int64_t hidden, float eps, char* buf,
+                      int buflen) {
+  if (!buf || buflen < 1) return fail(RMSN_ERR_NULL, "buf must be non-NULL");
+  buf[0] = 0;
+  const rmsn::Variant* v = nullptr;
+  const int rc = run(Types{dtype, gamma_dtype, out_dtype}, out, out_stride, residual,
+                     residual_stride, partials, partial_strides, k, gamma, rows, hidden, eps,
+                     nullptr, &v);
+  if (rc) return rc;
+  snprintf(buf, (size_t)buflen, "%s", v ? v->name : "none");
+  return RMSN_OK;
 }
 
 int rmsnorm_variants(int dtype, char* buf, int buflen) {

@@ -217,3 +217,57 @@ def test_general_interface_variant_tables():
                     continue
                 assert len(names) == len(set(names)) == n, (d, g, o, len(names))
                 assert all(f"<{d},g={g},o={o}," in v for v in names)
+
+
+def plan_call(out=FAKE, out_stride=64, out_dtype=2, residual=None, res_stride=64, parts=None,
+              strides=None, dtype=2, gamma=FAKE + (1 << 26), gamma_dtype=2, rows=4, hidden=64,
+              eps=1e-6):
+    parts = parts if parts is not None else [FAKE + (1 << 24)]
+    arr = (ctypes.c_void_p * len(parts))(*parts)
+    st = None if strides is None else (ctypes.c_int64 * len(strides))(*strides)
+    buf = ctypes.create_string_buffer(128)
+    rc = B.lib().rmsnorm_plan_call(out, out_stride, out_dtype, residual, res_stride, arr, st,
+                                   len(parts), dtype, gamma, gamma_dtype, rows, hidden, eps, buf, 128)
+    return rc, buf.value.decode()
+
+
+def test_plan_call_validates_without_launching():
+    # interleaved rows of one buffer (x in the first half of each 256-byte
+    # row, out in the second half): legal
+    rc, name = plan_call(out=FAKE + 128, out_stride=128, parts=[FAKE], strides=[128])
+    assert rc == 0 and name.startswith("vgpr<bf16,"), (rc, name)
+    assert plan_call(out=FAKE + 126, out_stride=128, parts=[FAKE], strides=[128])[0] == -5
+    # exact in place with the same stride: legal; with another dtype: not
+    assert plan_call(out=FAKE, out_stride=128, parts=[FAKE], strides=[128])[0] == 0
+    assert plan_call(out=FAKE, out_stride=128, out_dtype=1, parts=[FAKE], strides=[128])[0] == -5
+    # row pitches decide the chunk width: 136-byte pitch -> 8-byte chunks,
+    # 132 -> 4-byte, 130 -> elements
+    for pitch_elems, width in ((68, ",v8,"), (66, ",v4,"), (65, "elem")):
+        rc, name = plan_call(parts=[FAKE + (1 << 24)], strides=[pitch_elems])
+        assert rc == 0 and width in name, (pitch_elems, name)
+    # fp32 gamma with bf16 data and an fp32 output: 32-byte output chunks
+    rc, name = plan_call(out_dtype=0, gamma_dtype=0, hidden=4096, out_stride=4096, strides=[4096])
+    assert rc == 0 and name == "vgpr<bf16,g=f32,o=f32,tpr=512,npt=1,wg=512,k=0,nt>", name
+    # ... whose 8-byte aligned base forces 4-byte data chunks (8 bytes of fp32)
+    rc, name = plan_call(out=FAKE + 8, out_dtype=0, gamma_dtype=0, hidden=4096, out_stride=4096,
+                         strides=[4096])
+    assert rc == 0 and ",v4," in name, name
+    # the fused form, and rows == 0
+    rc, name = plan_call(residual=FAKE + (1 << 25), parts=[FAKE + (1 << 24), FAKE + (1 << 23)],
+                         hidden=16384, out_stride=16384, res_stride=16384, strides=[16384, 16384])
+    assert rc == 0 and name.startswith("stream<bf16,v8,") and "lds" in name, name
+    assert plan_call(rows=0, out=0, gamma=0, parts=[0]) == (0, "none")
+
+
+def test_row_collapse_rules():
+    assert B.collapse_rows((8192, 4096), (4096, 1)) == (8192, 4096, 4096)
+    assert B.collapse_rows((8192, 4096), (4224, 1)) == (8192, 4096, 4224)     # padded rows
+    assert B.collapse_rows((3, 4, 1000), (4 * 1016, 1016, 1)) == (12, 1000, 1016)
+    assert B.collapse_rows((1, 5, 1, 7), (99, 7, 7, 1)) == (5, 7, 7)            # size-1 dims ignored
+    assert B.collapse_rows((), ()) == (1, 1, 1)
+    assert B.collapse_rows((0, 16), (16, 1)) == (0, 16, 16)
+    assert B.collapse_rows((6, 1), (3, 5)) == (6, 1, 3)                         # hidden 1: any stride
+    with pytest.raises(B.RmsnormError):
+        B.collapse_rows((4, 6, 1000), (1016, 4 * 1016, 1))                   # transposed leading dims
+    with pytest.raises(B.RmsnormError):
+        B.collapse_rows((16, 64), (1, 16))                                   # column-major
