@@ -35,12 +35,15 @@ COPY_BYTES = 1 << 30
 
 
 def kernel_sources(op: str) -> list:
-    """The source files a workload's kernel is built from: the block sum has
-    one file of its own; every other op runs the RMSNorm kernels."""
+    """The source files a workload's device code is built from: the block
+    sum has one file of its own; every other op runs the RMSNorm kernels
+    (everything in csrc/ but the host-only dispatcher, rmsnorm_api.hip --
+    which kernel the dispatcher picks is checked by name instead)."""
     csrc = os.path.join(ROOT, "row_wise_normalization_rmsnorm_amd", "csrc")
     everything = sorted(glob.glob(os.path.join(csrc, "*")))
     mine = os.path.join(csrc, "block_sum.hip")
-    return [mine] if op == "block_sum" else [p for p in everything if p != mine]
+    host = os.path.join(csrc, "rmsnorm_api.hip")
+    return [mine] if op == "block_sum" else [p for p in everything if p not in (mine, host)]
 
 
 def source_hash(op: str) -> str:
