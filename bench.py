@@ -275,7 +275,7 @@ def sweep(w, step, a, B) -> int:
     default = B.rmsnorm_plan(w.rows, w.hidden, w.k, w.dtype)
     names = []
     for v in B.rmsnorm_variants(w.dtype):
-        if a.variant_filter and a.variant_filter not in v:
+        if a.variant_filter and not any(f in v for f in a.variant_filter.split("|")):
             continue
         os.environ["RMSNORM_VARIANT"] = v
         try:
@@ -411,7 +411,8 @@ def main() -> int:
                     help="time every compiled kernel variant that can run the workload "
                          "(forced through RMSNORM_VARIANT) and print one line per variant")
     ap.add_argument("--repeat", type=int, default=1, help="sweep rounds (median reported)")
-    ap.add_argument("--variant-filter", default="", help="sweep only variants containing this")
+    ap.add_argument("--variant-filter", default="",
+                    help="sweep only variants containing one of these |-separated substrings")
     ap.add_argument("--no-ceiling", action="store_true",
                     help="skip the streaming-ceiling probe")
     ap.add_argument("--inplace", action="store_true",
