@@ -156,6 +156,69 @@ COUNTERS = ["SQ_LDS_BANK_CONFLICT", "SQ_INSTS_LDS", "SQ_WAVES", "SQ_WAVE_CYCLES"
             "TCC_HIT_sum", "TCC_MISS_sum"]
 
 
+def report_summary(argv) -> int:
+    """profiles/per_config_report.md: for every workload, the GPU figures and
+    the oracle's CPU rate (many cores and one) from ``bench.py --workload W``
+    JSON lines, beside the parity statistics the GPU tests print ("[gpu]
+    NAME: {stats}" lines of a ``pytest -s`` log)."""
+    import ast
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--tests-log", required=True)
+    ap.add_argument("bench_json", nargs="+")
+    a = ap.parse_args(argv)
+    stats = {}
+    for line in open(a.tests_log, errors="replace"):
+        m = re.search(r"\[gpu\] (\w+): (\{.*\})\s*$", line)
+        if m:
+            try:
+                stats[m.group(1)] = ast.literal_eval(m.group(2))
+            except (ValueError, SyntaxError):
+                pass
+        m = re.search(r"\[gpu\] (\w+): error / bound = ([0-9.e+-]+)", line)
+        if m:
+            stats[m.group(1)] = {"error_over_bound": float(m.group(2))}
+    rows = []
+    for path in a.bench_json:
+        for line in open(path):
+            if line.startswith("{"):
+                rows.append(json.loads(line))
+    md = os.path.join(ROOT, "profiles", "per_config_report.md")
+    with open(md, "w") as f:
+        f.write("# Per-workload report: GPU kernel, CPU oracle, parity\n\n")
+        f.write("Commands: `python bench.py --workload W --no-ceiling` for every workload (the GPU "
+                "step timed with HIP events; the oracle timed on the host's cores, and on one), and "
+                "`python -m pytest tests/test_gpu_parity.py tests/test_gpu_block_sum.py -m gpu -s -k "
+                "\"workloads\"` for the parity statistics (all rows of the 512-row workloads; 128+ "
+                "sampled rows of the full-size launches, whose residual is also checked whole).\n\n")
+        f.write("| workload | GPU µs/step | GPU GB/s | % of 8 TB/s | GPU rows/s | oracle GB/s "
+                "(cores) | oracle rows/s | oracle GB/s, 1 core | GPU ÷ oracle | parity |\n"
+                "|---|---|---|---|---|---|---|---|---|---|\n")
+        for r in rows:
+            w = r["config"]["workload"]
+            cb = r.get("cpu_baseline", {})
+            st = stats.get(w, {})
+            if "max_ulp" in st:
+                par = (f"max {st['max_ulp']} ulp, rel {st.get('max_rel_err', 0):.2g}"
+                       + (", residual bit-exact" if st.get("residual_bit_exact") else ""))
+            elif "max_rel_err" in st:
+                par = (f"max rel {st['max_rel_err']:.2g}"
+                       + (", residual bit-exact" if st.get("residual_bit_exact") else ""))
+            elif "error_over_bound" in st:
+                par = f"error / bound {st['error_over_bound']:.2g}"
+            else:
+                par = "see tests"
+            one = cb.get("single_thread", {})
+            f.write(f"| {w} | {r['ms_per_step'] * 1e3:.2f} | {r['value']:.0f} | "
+                    f"{r['pct_of_peak']:.1f} | {r['rows_per_s']:.3g} | {cb.get('value', float('nan')):.3g} "
+                    f"({cb.get('cores', '-')}) | {cb.get('rows_per_s', float('nan')):.3g} | "
+                    f"{one.get('value', float('nan')):.3g} | "
+                    f"{r['value'] / cb['value'] if cb.get('value') else float('nan'):.0f} | {par} |\n")
+        f.write("\nThe oracle is the plain double-precision reference (test infrastructure), timed "
+                "as it stands: a baseline, not a target.\n")
+    print(md)
+    return 0
+
+
 def counters_summary(argv) -> int:
     """profiles/counters_<kernel>__<workload>.md from one rocprofv3 --pmc run
     of COUNTERS (LDS use and bank conflicts, waves, L2 hits and misses)."""
@@ -204,6 +267,8 @@ def main() -> int:
         return counters_summary(sys.argv[2:])
     if len(sys.argv) > 1 and sys.argv[1] == "ceiling":
         return ceiling_summary(sys.argv[2:])
+    if len(sys.argv) > 1 and sys.argv[1] == "report":
+        return report_summary(sys.argv[2:])
     ap = argparse.ArgumentParser()
     ap.add_argument("--workload", required=True)
     ap.add_argument("--plan", required=True, help="kernel variant name (bench.py prints it)")
