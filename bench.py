@@ -19,7 +19,7 @@ workloads a cache-flushed, a launch-and-synchronise and a graph-replay rate;
 ``stream_ceiling`` is a plain streaming kernel moving the same bytes.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-       [--no-cpu-baseline] [--no-ceiling] [--inplace] [--rotate-bytes GIB]
+       [--no-cpu-baseline] [--no-ceiling] [--inplace] [--rotate-bytes GIB] [--rows N]
        python bench.py --workload NAME --sweep [--repeat R] [--variant-filter S]
        python bench.py --ceiling-sweep | --copy-calibration
 """
@@ -415,6 +415,8 @@ def main() -> int:
                     help="sweep only variants containing one of these |-separated substrings")
     ap.add_argument("--no-ceiling", action="store_true",
                     help="skip the streaming-ceiling probe")
+    ap.add_argument("--rows", type=int, default=0,
+                    help="run the workload with this many rows instead (not a headline figure)")
     ap.add_argument("--inplace", action="store_true",
                     help="write the output over the first input instead of a separate buffer")
     ap.add_argument("--rotate-bytes", type=float, default=1.0,
@@ -440,6 +442,9 @@ def main() -> int:
         return ceiling_sweep()
 
     w = WORKLOADS[a.workload or HEADLINE]
+    if a.rows:  # the same workload with another row count (footprint studies)
+        import dataclasses
+        w = dataclasses.replace(w, name=f"{w.name}_rows{a.rows}", rows=a.rows)
     dev = "cuda:0"
     B.lib()
     print(f"[bench] {w.describe()}: generating inputs", file=sys.stderr, flush=True)
