@@ -66,12 +66,13 @@ struct Variant {
 
 // The general interface -- gamma in fp32 with 16-bit data, or an output dtype
 // other than the data's -- compiles only the shapes the dispatcher picks
-// (one chunk per thread up to 1024 threads, two for 8192-wide fp32 rows; the
-// streaming forms it uses), with plain and runtime-K fused forms.
+// (one or two chunks per thread up to 1024 threads; the streaming forms it
+// uses), with plain and runtime-K fused forms.
 #define RMSN_MIXED_VGPR_SHAPES(X)                                                        \
   X(8, 1, 256, true) X(16, 1, 256, true) X(32, 1, 256, true) X(64, 1, 256, true)        \
   X(128, 1, 256, true) X(256, 1, 256, true) X(512, 1, 512, true)                        \
-  X(1024, 1, 1024, true) X(1024, 2, 1024, true)
+  X(1024, 1, 1024, true) X(64, 2, 256, true) X(128, 2, 256, true) X(256, 2, 256, true)  \
+  X(512, 2, 512, true) X(1024, 2, 1024, true)
 
 #define RMSN_MIXED_STREAM_SHAPES(X)                                                       \
   X(16, 256, false, false, 2) X(16, 512, false, false, 2) X(16, 1024, false, false, 2)    \

@@ -116,6 +116,10 @@ def test_plan_names_follow_the_dispatch_rule():
     assert "lds" in plan(65536, 16384, 1, "bf16")
     assert "tpr=8," in plan(1000, 64, 1, "bf16")            # several rows per wave
     assert "tpr=64," in plan(512, 512, 0, "bf16")           # one row per wave
+    # large plain launches: two chunks per thread; small ones and the fused form: one
+    assert "tpr=256,npt=2," in plan(8192, 4096, 0, "bf16")
+    assert "tpr=512,npt=1," in plan(512, 4096, 0, "bf16")
+    assert "tpr=512,npt=1," in plan(8192, 4096, 1, "bf16")
     assert "elem" in plan(10, 1591, 0, "bf16")              # odd row length
     assert "elem" in plan(10, 4096, 1, "bf16", align=2)
     assert ",v4," in plan(10, 4096, 1, "bf16", align=4)        # 4-byte aligned bases
@@ -192,7 +196,8 @@ def test_general_interface_plans():
     assert plan(8192, 4096, 1, "bf16", "f32", "f32") == \
         "vgpr<bf16,g=f32,o=f32,tpr=512,npt=1,wg=512,k=-1,nt>"
     assert plan(8192, 4096, 1, "bf16", "bf16", "bf16") == B.rmsnorm_plan(8192, 4096, 1, "bf16")
-    assert plan(512, 2048, 0, "f32", "f32", "bf16").startswith("vgpr<f32,g=f32,o=bf16,tpr=512")
+    assert plan(512, 2048, 0, "f32", "f32", "bf16").startswith("vgpr<f32,g=f32,o=bf16,tpr=512,npt=1")
+    assert plan(8192, 2048, 0, "f32", "f32", "bf16").startswith("vgpr<f32,g=f32,o=bf16,tpr=256,npt=2")
     assert plan(4096, 8192, 8, "f16", "f32", "f16").startswith("stream<f16,g=f32,o=f16,v8,")
     assert "lds" in plan(100, 16384, 1, "bf16", "f32", "f32")
     assert "elem" in plan(10, 1595, 0, "f32", "f32", "f16")
@@ -208,7 +213,7 @@ def test_general_interface_plans():
 
 
 def test_general_interface_variant_tables():
-    for d, n in (("bf16", 60), ("f16", 60), ("f32", 48)):
+    for d, n in (("bf16", 68), ("f16", 68), ("f32", 56)):
         for g in sorted({d, "f32"}):
             for o in ("f32", "f16", "bf16"):
                 names = B.rmsnorm_variants_ex(d, g, o)

@@ -121,6 +121,27 @@ def test_large_workloads_full_size(name):
     say(f"[gpu] {name}: {stats}")
 
 
+@pytest.mark.parametrize("dtype,rows,hidden", [("bf16", 8192, 4096), ("f32", 8192, 2048),
+                                               ("f16", 16384, 1592)])
+def test_large_plain_launches(dtype, rows, hidden):
+    """Large plain launches take the two-chunks-per-thread shape; sampled rows
+    against the oracle."""
+    w = I.case(dtype, rows, hidden, 0, seed=rows + hidden)
+    plan = B.rmsnorm_plan(rows, hidden, 0, dtype)
+    say(f"[gpu] large plain {dtype} {rows}x{hidden}: plan {plan}")
+    assert "npt=2" in plan
+    d = I.make_inputs(w, device=DEV)
+    out = torch.full_like(d["x"], float("nan"))
+    B.rmsnorm_fwd(out, d["x"], d["gamma"], w.eps)
+    torch.cuda.synchronize()
+    rows_s = _sample_rows(w)
+    dc = I.make_inputs(w, rows=rows_s)
+    ref = P.run_oracle(dtype, w.eps, x=dc["x"], gamma=dc["gamma"])
+    idx = torch.tensor(rows_s, device=DEV)
+    P.compare(dtype, out.index_select(0, idx).cpu(), ref, what=f"large plain {dtype}")
+    assert not torch.isnan(out).any()
+
+
 # ---- shapes, tails, partial counts ---------------------------------------------
 
 TAIL_H = [1, 2, 7, 8, 63, 64, 65, 511, 1591, 1592, 2048, 4096, 8191, 8192, 8193, 16384, 20000]
