@@ -71,6 +71,23 @@ def kernel_stats(d: str):
     return out
 
 
+def launch_gaps(d: str, kernel_substr: str):
+    """From the kernel trace: (median duration, median idle gap between one
+    dispatch of the kernel and the next when nothing else ran between them,
+    number of such pairs), in ns."""
+    rows = list(csv.DictReader(open(_one(d, "kernel_trace.csv"))))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    durs, gaps = [], []
+    for a, b in zip(rows, rows[1:]):
+        if kernel_substr in a["Kernel_Name"]:
+            durs.append(int(a["End_Timestamp"]) - int(a["Start_Timestamp"]))
+            if kernel_substr in b["Kernel_Name"]:
+                gaps.append(int(b["Start_Timestamp"]) - int(a["End_Timestamp"]))
+    if not durs:
+        return None
+    return statistics.median(durs), (statistics.median(gaps) if gaps else float("nan")), len(gaps)
+
+
 def counter(d: str, name: str, kernel_substr: str):
     rows = list(csv.DictReader(open(_one(d, "counter_collection.csv"))))
     vals = [float(r["Counter_Value"]) for r in rows
@@ -325,6 +342,12 @@ def main() -> int:
                     f"{s['min_ns'] / 1e3:.2f} | {s['max_ns'] / 1e3:.2f} | {s['pct']:.1f} |\n")
         f.write(f"\nAchieved (algorithmic bytes / average duration): **{achieved:.0f} GB/s**, "
                 f"{100 * achieved / 8000:.1f}% of the 8 TB/s HBM peak.\n")
+        gaps = launch_gaps(a.trace, a.symbol)
+        if gaps:
+            f.write(f"Back-to-back launches in the trace: median duration {gaps[0] / 1e3:.2f} us, "
+                    f"median idle gap to the next launch {gaps[1] / 1e3:.2f} us ({gaps[2]} pairs; "
+                    f"a gap means the host, slowed further by the profiler, issued launches "
+                    f"more slowly than the kernel ran).\n")
         if event:
             f.write(f"bench.py (HIP events over the timed region, same command without the "
                     f"profiler): {event['ms_per_step'] * 1e3:.2f} us per launch, "
