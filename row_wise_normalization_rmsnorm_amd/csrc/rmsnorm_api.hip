@@ -54,8 +54,11 @@ bool known(int dtype) { return dtype == RMSN_F32 || dtype == RMSN_F16 || dtype =
 constexpr int64_t kLdsStageMax = 64 * 1024;
 // Upper bound on workgroups per launch; longer problems loop over rows.
 constexpr int64_t kGridCapDefault = 1 << 20;
-// Rows up to this many elements are held in registers.
-constexpr int64_t kVgprMaxHidden = 8192;
+// Rows up to this many bytes are held in registers.
+constexpr int64_t kVgprMaxBytes = 16384;
+// LDS-staged rows longer than this many bytes stream in eight 8-byte chunks
+// per lane with 256-lane workgroups.
+constexpr int64_t kLongRowBytes = 16384;
 // With two or more partials, rows of at least this many bytes use the
 // streaming kernel (fewer registers per thread than holding K+1 chunk sets).
 constexpr int64_t kStreamMinBytesForK = 8192;
@@ -185,7 +188,7 @@ int choose(Types t, int64_t rows, int64_t hidden, int k, Aligns al, Plan* plan) 
     if (!fits(*v, t, hidden, k, al))
       return fail(RMSN_ERR_SHAPE, "RMSNORM_VARIANT=%s cannot run hidden=%lld k=%d", forced,
                   (long long)hidden, k);
-  } else if (vb == 16 && hidden <= kVgprMaxHidden &&
+  } else if (vb == 16 && hidden * s <= kVgprMaxBytes &&
              !(k >= 2 && hidden * s >= kStreamMinBytesForK)) {
     // One 16-byte chunk per thread wherever a workgroup can cover the row:
     // threads per row = the next power of two >= chunks (several rows per
@@ -219,13 +222,17 @@ int choose(Types t, int64_t rows, int64_t hidden, int k, Aligns al, Plan* plan) 
     // sets in registers at K = 8).  The LDS-staged form moves 8-byte chunks,
     // four per thread, with just enough threads to put the whole row in
     // flight in one step: measured 3% faster than 16-byte chunks at K = 8
-    // and 2% on 16384-wide rows.
+    // and 2% on 16384-wide rows.  Rows over 16 KiB take 256-lane
+    // workgroups with eight chunks in flight per lane instead (several
+    // steps per row): 2-10% faster from 10240- to 32768-wide bf16 rows and
+    // on 8192-wide fp32 ones (65536x16384 bf16: 1439 vs 1499 us).
     const bool lds = hidden * s <= kLdsStageMax;
     const int svb = (lds && vb == 16) ? 8 : vb;
     const int64_t C = hidden / elems_per_chunk(svb, t.d);
-    const int unr = svb == 16 ? 2 : 4;
+    const bool long_row = lds && svb == 8 && hidden * s > kLongRowBytes;
+    const int unr = long_row ? 8 : svb == 16 ? 2 : 4;
     int wgs = 256;
-    while (wgs < 1024 && (int64_t)wgs * unr < C) wgs *= 2;
+    while (!long_row && wgs < 1024 && (int64_t)wgs * unr < C) wgs *= 2;
     v = find(t, rmsn::kStream, svb, wgs, unr, wgs, k == 0 ? 0 : -1, lds ? 1 : 0, lds ? 1 : 0);
   }
   if (!v) return fail(RMSN_ERR_SHAPE, "no kernel variant for hidden=%lld k=%d", (long long)hidden, k);

@@ -57,6 +57,7 @@ struct Variant {
   X(8, 256, true, true, 2) X(8, 512, true, true, 2) X(8, 1024, true, true, 2)             \
   X(8, 256, true, true, 4) X(8, 512, true, true, 4) X(8, 1024, true, true, 4)             \
   X(8, 256, false, false, 4) X(8, 512, false, false, 4) X(8, 1024, false, false, 4)       \
+  X(8, 256, true, true, 8)                                                                \
   X(4, 256, true, true, 4) X(4, 512, true, true, 4) X(4, 1024, true, true, 4)             \
   X(4, 256, false, false, 4) X(4, 512, false, false, 4) X(4, 1024, false, false, 4)       \
   X(0, 256, true, true, 4) X(0, 512, true, true, 4) X(0, 1024, true, true, 4)             \
@@ -78,6 +79,7 @@ struct Variant {
   X(16, 256, false, false, 2) X(16, 512, false, false, 2) X(16, 1024, false, false, 2)    \
   X(8, 256, true, true, 4) X(8, 512, true, true, 4) X(8, 1024, true, true, 4)             \
   X(8, 256, false, false, 4) X(8, 512, false, false, 4) X(8, 1024, false, false, 4)       \
+  X(8, 256, true, true, 8)                                                                \
   X(4, 256, true, true, 4) X(4, 512, true, true, 4) X(4, 1024, true, true, 4)             \
   X(4, 256, false, false, 4) X(4, 512, false, false, 4) X(4, 1024, false, false, 4)       \
   X(0, 256, true, true, 4) X(0, 512, true, true, 4) X(0, 1024, true, true, 4)             \

@@ -114,6 +114,9 @@ def test_plan_names_follow_the_dispatch_rule():
     assert plan(512, 2048, 0, "f32").startswith("vgpr<f32")
     assert plan(65536, 16384, 1, "bf16").startswith("stream<bf16,v8")
     assert "lds" in plan(65536, 16384, 1, "bf16")
+    assert ",wg=256,lds,k=-1,unr=8," in plan(65536, 16384, 1, "bf16")   # rows over 16 KiB
+    assert plan(32768, 8192, 1, "f32").startswith("stream<f32,v8,wg=256,lds")
+    assert plan(4096, 8192, 8, "bf16") == "stream<bf16,v8,wg=512,lds,k=-1,unr=4,nt>"
     assert "tpr=8," in plan(1000, 64, 1, "bf16")            # several rows per wave
     assert "tpr=64," in plan(512, 512, 0, "bf16")           # one row per wave
     # large plain launches: two chunks per thread; small ones and the fused form: one
@@ -213,7 +216,7 @@ def test_general_interface_plans():
 
 
 def test_general_interface_variant_tables():
-    for d, n in (("bf16", 68), ("f16", 68), ("f32", 56)):
+    for d, n in (("bf16", 70), ("f16", 70), ("f32", 58)):
         for g in sorted({d, "f32"}):
             for o in ("f32", "f16", "bf16"):
                 names = B.rmsnorm_variants_ex(d, g, o)
