@@ -156,7 +156,8 @@ def _guarded(t):
 
 @pytest.mark.parametrize("dtype,hidden,k", [("bf16", 4096, 1), ("bf16", 1591, 0), ("f32", 333, 3),
                                             ("f16", 16384, 1), ("bf16", 70000, 2), ("bf16", 24, 8),
-                                            ("f32", 8192, 0), ("bf16", 1594, 1)])
+                                            ("f32", 8192, 0), ("bf16", 1594, 1), ("bf16", 20000, 0),
+                                            ("bf16", 12296, 3)])
 def test_no_writes_outside_the_tensors(dtype, hidden, k):
     """Guard regions around out and the residual stay untouched (tails, odd
     lengths, every kernel family)."""
