@@ -166,10 +166,11 @@ bool fits(const rmsn::Variant& v, Types t, int64_t hidden, int k, Aligns al) {
   return true;
 }
 
-// The dispatcher.  Register-resident rows up to 8192 elements, packing rows
-// into waves when they are short; streaming two-pass kernels above that
-// (LDS-staged while the row fits the stage budget), for K >= 2 on long rows,
-// and whenever 16-byte accesses do not fit the alignment or row length.
+// The dispatcher.  Register-resident rows up to 16 KiB, packing rows into
+// waves when they are short; streaming two-pass kernels above that
+// (LDS-staged while the row fits the stage budget), for K >= 2 on rows of
+// 8 KiB and more, and whenever 16-byte accesses do not fit the alignment or
+// row length.
 // The general interface (other gamma or output dtypes) makes the same
 // choice among the shapes compiled for it, with runtime-K fused kernels.
 int choose(Types t, int64_t rows, int64_t hidden, int k, Aligns al, Plan* plan) {
@@ -190,10 +191,9 @@ int choose(Types t, int64_t rows, int64_t hidden, int k, Aligns al, Plan* plan) 
                   (long long)hidden, k);
   } else if (vb == 16 && hidden * s <= kVgprMaxBytes &&
              !(k >= 2 && hidden * s >= kStreamMinBytesForK)) {
-    // One 16-byte chunk per thread wherever a workgroup can cover the row:
-    // threads per row = the next power of two >= chunks (several rows per
-    // wave below 64 chunks), up to 1024 threads, then 2 or 4 chunks each.
-    // Large plain launches give each thread two chunks from 128 chunks up,
+    // One 16-byte chunk per thread: threads per row = the next power of two
+    // >= chunks (several rows per wave below 64 chunks); a 16 KiB row is
+    // 1024 chunks, one workgroup's worth.  Large plain launches give each thread two chunks from 128 chunks up,
     // so that a thread has two loads in flight as the fused form's x and
     // residual give it, and twice the rows fit on a CU: measured 9-11%
     // faster on 2-16 KiB bf16 rows (e.g. 8192x4096: 23.9 vs 26.3 us), even
@@ -206,13 +206,8 @@ int choose(Types t, int64_t rows, int64_t hidden, int k, Aligns al, Plan* plan) 
     const int per = (k == 0 && C >= 128 && rows * half >= kPlainTwoChunkThreads) ? 2 : 1;
     int tpr = 8;
     while ((int64_t)tpr * per < C && tpr < 1024) tpr *= 2;
-    int npt = (int)((C + tpr - 1) / tpr);
-    npt = npt <= 1 ? 1 : npt <= 2 ? 2 : 4;
-    int wgs = tpr < 256 ? 256 : tpr;
-    if (npt == 4 && tpr == 1024) {  // 16 waves x 4 chunks exceeds the register budget
-      tpr = 512;
-      wgs = 512;
-    }
+    const int npt = C <= tpr ? 1 : 2;
+    const int wgs = tpr < 256 ? 256 : tpr;
     v = find(t, rmsn::kVgpr, 16, tpr, npt, wgs, vgpr_kc(k), 0, 1);
     if (!v && k > 0) v = find(t, rmsn::kVgpr, 16, tpr, npt, wgs, -1, 0, 1);
   } else {

@@ -279,3 +279,23 @@ def test_row_collapse_rules():
         B.collapse_rows((4, 6, 1000), (1016, 4 * 1016, 1))                   # transposed leading dims
     with pytest.raises(B.RmsnormError):
         B.collapse_rows((16, 64), (1, 16))                                   # column-major
+
+
+def test_dispatcher_covers_every_shape():
+    """Every row length, K, alignment and row count finds a compiled kernel,
+    for the single-dtype tables and every general combination."""
+    hs = list(range(1, 70)) + [511, 512, 513, 1023, 1024, 1025, 1591, 1592, 2047, 2048, 4096,
+                               4097, 8191, 8192, 8193, 12288, 16384, 16385, 20000, 32768, 32769,
+                               40000, 65536, 70000]
+    for d in ("bf16", "f16", "f32"):
+        for h in hs:
+            for k in (0, 1, 2, 8, 16):
+                for al in (16, 8, 4, 2):
+                    for rows in (1, 512, 65536):
+                        assert B.rmsnorm_plan(rows, h, k, d, align=al)
+        for g in sorted({d, "f32"}):
+            for o in ("f32", "f16", "bf16"):
+                for h in (1, 7, 64, 1592, 4096, 8192, 16384, 20000, 70000):
+                    for k in (0, 1, 3, 8):
+                        for al in (16, 8, 4, 2):
+                            assert B.rmsnorm_plan_ex(65536, h, k, d, g, o, align=al)
