@@ -3,8 +3,8 @@
 Each ``csrc/*.hip`` file is compiled to an object in ``_build/`` (in
 parallel), the objects are linked into ``librmsnorm.so`` next to this file,
 and the device assembly of every kernel is checked: no packed-fp32 VALU
-instructions (they are disabled by a target-feature flag) and no scratch
-spills in the kernels the dispatcher uses.
+instructions (they are disabled by a target-feature flag) and no kernel that
+spills registers to scratch memory (either fails the build).
 
 Usage: ``python -m row_wise_normalization_rmsnorm_amd.build [-j N] [-v]``.
 """
@@ -98,7 +98,8 @@ def build(jobs: int = 0, verbose: bool = False) -> str:
         for k, (vg, sc) in sorted(usage.items()):
             print(f"{vg:4d} vgpr {sc:5d} scratch  {k}")
     if spills:
-        print(f"warning: {len(spills)} kernel variants use scratch memory", file=sys.stderr)
+        raise RuntimeError("kernel variants spill registers to scratch memory: "
+                           + ", ".join(sorted(spills)))
     os.replace(tmp, LIB)
     return LIB
 

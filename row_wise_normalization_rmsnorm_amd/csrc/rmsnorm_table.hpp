@@ -68,15 +68,26 @@ inline void add_variant(std::vector<Variant>& v, Types t, int kind, int vb, int 
 
 // Every variant of the single-dtype interface (full shape lists, for the
 // dispatcher and for sweeps).
+// Shapes left out because they spill registers to scratch memory: the
+// K = 8 register kernel holding 2048 chunk slots per row (nine chunk sets per
+// thread), and the 16-byte runtime-K streaming kernel with four chunks in
+// flight on 1024 lanes.  The dispatcher never picks them.
+template <int KC, int TPR, int NPT>
+constexpr bool vgpr_spills() { return KC == 8 && TPR * NPT >= 2048; }
+template <int VB, int WGS, int KC, int UNR>
+constexpr bool stream_spills() { return VB == 16 && WGS == 1024 && KC < 0 && UNR >= 4; }
+
 template <typename T>
 void add_full(std::vector<Variant>& v, Types t) {
 #define RMSN_ADD_VGPR_K(KC, TPR, NPT, WGS, NT)                                          \
-  add_variant(v, t, kVgpr, 16, TPR, NPT, WGS, KC, 0, 0, NT ? 1 : 0,                      \
-              reinterpret_cast<const void*>(&row_vgpr_kernel<T, T, T, TPR, NPT, WGS, KC, NT>));
+  if constexpr (!vgpr_spills<KC, TPR, NPT>())                                           \
+    add_variant(v, t, kVgpr, 16, TPR, NPT, WGS, KC, 0, 0, NT ? 1 : 0,                    \
+                reinterpret_cast<const void*>(&row_vgpr_kernel<T, T, T, TPR, NPT, WGS, KC, NT>));
 #define RMSN_ADD_VGPR(TPR, NPT, WGS, NT) RMSN_KCS(RMSN_ADD_VGPR_K, TPR, NPT, WGS, NT)
   RMSN_VGPR_SHAPES(RMSN_ADD_VGPR)
 #define RMSN_ADD_STREAM_K(KC, VB, WGS, LDS, NT, UNR)                                    \
-  if constexpr (VB == 0 || VB > (int)sizeof(typename DT<T>::scalar_t))                   \
+  if constexpr ((VB == 0 || VB > (int)sizeof(typename DT<T>::scalar_t)) &&               \
+                !stream_spills<VB, WGS, KC, UNR>())                                      \
     add_variant(v, t, kStream, VB, WGS, 0, WGS, KC, LDS ? 1 : 0, UNR, NT ? 1 : 0,         \
                 reinterpret_cast<const void*>(                                           \
                     &row_stream_kernel<T, T, T, VB, WGS, LDS, KC, UNR, NT>));
