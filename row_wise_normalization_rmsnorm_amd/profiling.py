@@ -35,22 +35,26 @@ COPY_BYTES = 1 << 30
 
 
 def kernel_sources(op: str) -> list:
-    """The files that fix a workload's kernel code: the kernel templates (the
-    block sum's own file, or the RMSNorm kernels' header) and the build
-    flags.  Which variant runs is checked by its name instead, which spells
-    out every template parameter, so adding other variants or changing the
-    host dispatcher leaves a measured figure valid."""
+    """The source that fixes a workload's kernel code: the block sum's own
+    file, or the RMSNorm kernels' template header.  Which variant runs is
+    checked by its name instead, which spells out every template parameter,
+    so adding other variants or changing the host dispatcher leaves a
+    measured figure valid."""
     pkg = os.path.join(ROOT, "row_wise_normalization_rmsnorm_amd")
-    src = "block_sum.hip" if op == "block_sum" else "rmsnorm_kernels.hpp"
-    return [os.path.join(pkg, "csrc", src), os.path.join(pkg, "build.py")]
+    return [os.path.join(pkg, "csrc", "block_sum.hip" if op == "block_sum" else
+                         "rmsnorm_kernels.hpp")]
 
 
 def source_hash(op: str) -> str:
-    """sha256 over the kernel sources of ``op``: a traffic figure taken on
-    other sources is stale."""
+    """sha256 over the kernel source of ``op`` and the compiler flags it is
+    built with: a traffic figure taken on other code is stale."""
+    import sys
+    sys.path.insert(0, ROOT)
+    from row_wise_normalization_rmsnorm_amd.build import FLAGS
     h = hashlib.sha256()
     for p in kernel_sources(op):
         h.update(open(p, "rb").read())
+    h.update(" ".join(FLAGS).encode())
     return h.hexdigest()
 
 
