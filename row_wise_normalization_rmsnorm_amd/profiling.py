@@ -31,6 +31,7 @@ import re
 import statistics
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+PROFILES = os.path.join(ROOT, "profiles")   # where the summaries are written
 COPY_BYTES = 1 << 30
 
 
@@ -115,7 +116,7 @@ def sweep_summary(argv) -> int:
     a = ap.parse_args(argv)
     rows = [json.loads(l) for l in open(a.jsonl) if l.startswith("{")]
     rows.sort(key=lambda r: r["us"])
-    md = os.path.join(ROOT, "profiles", f"sweep__{a.workload}.md")
+    md = os.path.join(PROFILES, f"sweep__{a.workload}.md")
     with open(md, "w") as f:
         f.write(f"# Every compiled variant on {a.workload}\n\n")
         cmd = a.command or (f"python bench.py --workload {a.workload} --sweep --repeat 3")
@@ -146,7 +147,7 @@ def ceiling_summary(argv) -> int:
     for r in rows:
         if r["pattern"] not in order:
             order.append(r["pattern"])
-    md = os.path.join(ROOT, "profiles", "hbm_ceiling_sweep.md")
+    md = os.path.join(PROFILES, "hbm_ceiling_sweep.md")
     with open(md, "w") as f:
         f.write("# HBM ceiling of a plain streaming kernel, by read/write mix\n\n")
         f.write("Command: `python bench.py --ceiling-sweep` (libstreamprobe.so: 16-byte nontemporal "
@@ -202,7 +203,7 @@ def report_summary(argv) -> int:
         for line in open(path):
             if line.startswith("{"):
                 rows.append(json.loads(line))
-    md = os.path.join(ROOT, "profiles", "per_config_report.md")
+    md = os.path.join(PROFILES, "per_config_report.md")
     with open(md, "w") as f:
         f.write("# Per-workload report: GPU kernel, CPU oracle, parity\n\n")
         f.write("Commands: `python bench.py --workload W --no-ceiling` for every workload (the GPU "
@@ -254,7 +255,7 @@ def counters_summary(argv) -> int:
             vals[n] = counter(a.dir, n, a.symbol)
         except ValueError:
             pass
-    md = os.path.join(ROOT, "profiles", f"counters_{short_name(a.plan)}__{a.workload}.md")
+    md = os.path.join(PROFILES, f"counters_{short_name(a.plan)}__{a.workload}.md")
     with open(md, "w") as f:
         f.write(f"# LDS, wave and L2 counters: {a.plan} on {a.workload}\n\n")
         f.write("Command: `rocprofv3 --pmc " + " ".join(COUNTERS) + " --output-format csv -d <dir> "
@@ -329,8 +330,8 @@ def main() -> int:
                 event = json.loads(line)
 
     name = short_name(a.plan)
-    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
-    md = os.path.join(ROOT, "profiles", f"{name}__{w.name}.md")
+    os.makedirs(PROFILES, exist_ok=True)
+    md = os.path.join(PROFILES, f"{name}__{w.name}.md")
     with open(md, "w") as f:
         f.write(f"# {a.plan} on {w.name}\n\n")
         what = ("each element read once, the 4-byte sum written once" if w.op == "block_sum"
@@ -370,7 +371,7 @@ def main() -> int:
         f.write(f"\nHBM traffic per launch {traffic:,.0f} B = {traffic / nbytes:.4f} x the "
                 "algorithmic bytes.\n")
         f.write(f"\nKernel sources sha256: `{source_hash(w.op)}`\n")
-    tj = os.path.join(ROOT, "profiles", f"traffic_{w.name}.json")
+    tj = os.path.join(PROFILES, f"traffic_{w.name}.json")
     json.dump({"workload": w.name, "kernel": a.plan, "traffic_bytes_per_launch": round(traffic),
                "read_bytes": round(read_b), "write_bytes": round(write_b),
                "algorithmic_bytes": nbytes, "fetch_kib": fetch_kib, "write_kib": write_kib,

@@ -1,0 +1,107 @@
+"""Host logic of the measurement tools, on the CPU: the rocprofv3 CSV
+parsing and summaries in profiling.py, and bench.py's refusal of more than
+one GPU.  Synthetic CSV files stand in for rocprofv3 output."""
+from __future__ import annotations
+
+import csv
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+from row_wise_normalization_rmsnorm_amd import profiling as prof
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _write_csv(path, header, rows):
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(header)
+        w.writerows(rows)
+
+
+def test_launch_gaps_and_kernel_stats(tmp_path):
+    d = tmp_path / "trace"
+    hdr = ["Kind", "Kernel_Name", "Start_Timestamp", "End_Timestamp"]
+    rows = [["KERNEL_DISPATCH", "copyBuffer", 0, 50],
+            ["KERNEL_DISPATCH", "row_vgpr_kernel<...>", 100, 1100],
+            ["KERNEL_DISPATCH", "row_vgpr_kernel<...>", 1150, 2150],
+            ["KERNEL_DISPATCH", "row_vgpr_kernel<...>", 2150, 3170],
+            ["KERNEL_DISPATCH", "other", 3200, 3300],
+            ["KERNEL_DISPATCH", "row_vgpr_kernel<...>", 3400, 4400]]
+    _write_csv(str(d / "run_kernel_trace.csv"), hdr, rows[::-1])   # any order
+    med_dur, med_gap, pairs = prof.launch_gaps(str(d), "row_vgpr_kernel")
+    assert pairs == 2 and med_gap == 25.0     # gaps 50 and 0; the pair across "other" is skipped
+    assert med_dur == 1000.0                  # durations 1000, 1000, 1020 (the last has no successor)
+    _write_csv(str(d / "run_kernel_stats.csv"),
+               ["Name", "Calls", "AverageNs", "MinNs", "MaxNs", "Percentage"],
+               [["row_vgpr_kernel<...>", 4, 1005.0, 1000, 1020, 99.0]])
+    st = prof.kernel_stats(str(d))
+    assert st[0]["avg_ns"] == 1005.0 and st[0]["calls"] == 4
+
+
+def test_counter_median_and_missing_kernel(tmp_path):
+    d = tmp_path / "pmc"
+    _write_csv(str(d / "run_counter_collection.csv"),
+               ["Kernel_Name", "Counter_Name", "Counter_Value"],
+               [["k_a", "FETCH_SIZE", 10.0], ["k_a", "FETCH_SIZE", 30.0], ["k_a", "FETCH_SIZE", 20.0],
+                ["k_b", "FETCH_SIZE", 99.0], ["k_a", "WRITE_SIZE", 5.0]])
+    assert prof.counter(str(d), "FETCH_SIZE", "k_a") == (20.0, 3)
+    with pytest.raises(ValueError):
+        prof.counter(str(d), "FETCH_SIZE", "k_c")
+
+
+def test_traffic_summary_scales_counters_by_the_copy(tmp_path, monkeypatch):
+    """FETCH_SIZE reading half of a copy's bytes gets scale 2; the summary
+    and the JSON report bytes per launch in the algorithmic units."""
+    monkeypatch.setattr(prof, "PROFILES", str(tmp_path / "profiles"))
+    os.makedirs(tmp_path / "profiles")
+    w = "rmsnorm_f32_512x2048"
+    t, fe, wr, cf, cw = (tmp_path / n for n in ("t", "f", "w", "cf", "cw"))
+    _write_csv(str(t / "run_kernel_stats.csv"), ["Name", "Calls", "AverageNs", "MinNs", "MaxNs",
+                                                "Percentage"], [["row_vgpr_kernel<x>", 3, 4000, 3900, 4100, 90]])
+    _write_csv(str(t / "run_kernel_trace.csv"), ["Kind", "Kernel_Name", "Start_Timestamp",
+                                                "End_Timestamp"], [["K", "row_vgpr_kernel<x>", 0, 4000]])
+    algo = 512 * 2048 * 4 * 2 + 2048 * 4
+    _write_csv(str(fe / "run_counter_collection.csv"), ["Kernel_Name", "Counter_Name", "Counter_Value"],
+               [["row_vgpr_kernel<x>", "FETCH_SIZE", 512 * 2048 * 4 / 1024 / 2]])
+    _write_csv(str(wr / "run_counter_collection.csv"), ["Kernel_Name", "Counter_Name", "Counter_Value"],
+               [["row_vgpr_kernel<x>", "WRITE_SIZE", 512 * 2048 * 4 / 1024]])
+    _write_csv(str(cf / "run_counter_collection.csv"), ["Kernel_Name", "Counter_Name", "Counter_Value"],
+               [["__amd_rocclr_copyBuffer", "FETCH_SIZE", (1 << 30) / 1024 / 2]])
+    _write_csv(str(cw / "run_counter_collection.csv"), ["Kernel_Name", "Counter_Name", "Counter_Value"],
+               [["__amd_rocclr_copyBuffer", "WRITE_SIZE", (1 << 30) / 1024]])
+    argv = ["profiling", "--workload", w, "--plan", "vgpr<f32,x>", "--symbol", "row_vgpr_kernel",
+            "--trace", str(t), "--fetch", str(fe), "--write", str(wr), "--copy-fetch", str(cf),
+            "--copy-write", str(cw)]
+    monkeypatch.setattr(sys, "argv", argv)
+    assert prof.main() == 0
+    d = json.load(open(tmp_path / "profiles" / f"traffic_{w}.json"))
+    assert d["read_bytes"] == 512 * 2048 * 4 and d["write_bytes"] == 512 * 2048 * 4
+    assert d["algorithmic_bytes"] == algo
+    md = open(tmp_path / "profiles" / f"vgpr_f32_x__{w}.md").read()
+    assert "4.00" in md and "scale" in md
+
+
+def test_ceiling_summary(tmp_path, monkeypatch):
+    monkeypatch.setattr(prof, "PROFILES", str(tmp_path / "profiles"))
+    os.makedirs(tmp_path / "profiles")
+    lines = [{"pattern": "read 1", "reads": 1, "writes": 0, "in_place": 0, "grid": g, "block": 256,
+              "unroll": 4, "layout": lay, "us": 1.0, "gbs": v}
+             for g, lay, v in ((1024, "grid-stride", 5000.0), (2048, "contiguous", 5100.0),
+                               (4096, "grid-stride", 6000.0))]
+    src = tmp_path / "c.jsonl"
+    src.write_text("\n".join(json.dumps(x) for x in lines) + "\n")
+    assert prof.ceiling_summary([str(src)]) == 0
+    md = open(tmp_path / "profiles" / "hbm_ceiling_sweep.md").read()
+    assert "| read 1 | 1 | 0 (0) | 6000 | 75.0 | 4096, 256, 4, grid-stride | 5100 | 5100 |" in md
+
+
+def test_bench_refuses_more_than_one_gpu():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr
