@@ -143,3 +143,28 @@ def test_large_tensor_bf16():
     w = WORKLOADS["block_sum_bf16_16384x16384"]
     x = I.make_inputs(w)["x"]
     check(x, "bf16", w.name, x_dev=x.to(DEV).reshape(-1))
+
+
+def test_random_block_sums():
+    """Seeded random calls: dtype, length (ragged), base offset and value
+    scale, with an occasional NaN or infinity planted."""
+    rng = np.random.default_rng(4242)
+    for t in range(40):
+        dtype = str(rng.choice(list(ELEM)))
+        s = ELEM[dtype]
+        n = int(rng.choice([int(rng.integers(0, 64)), int(rng.integers(64, 70000)),
+                            int(rng.integers(70000, 3_000_000))], p=[0.2, 0.5, 0.3]))
+        off_e = int(rng.integers(0, 16 // s))
+        if dtype == "i8":
+            x = torch.from_numpy(rng.integers(-128, 128, n, dtype=np.int8))
+        else:
+            scale = float(rng.choice([1e-3, 1.0, 50.0]))
+            a = torch.from_numpy((rng.standard_normal(n) * scale).astype(np.float32))
+            if n and rng.random() < 0.15:
+                a[int(rng.integers(n))] = float(rng.choice([np.nan, np.inf, -np.inf]))
+            x = a.to(I.TORCH_DTYPE[dtype])
+        buf = torch.zeros(n + 64 // s, dtype=x.dtype, device=DEV)
+        xd = buf[off_e:off_e + n]
+        if n:
+            xd.copy_(x.to(DEV))
+        check(x, dtype, f"random #{t}", offset_bytes=off_e * s, x_dev=xd)
