@@ -538,7 +538,10 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": w.dtype,
+        # the arithmetic the path computes in (fp32 adds, FMAs and scale on
+        # 16-bit storage; int32 for the int8 sum); the tensors' dtype beside it
+        "dtype": "i32" if w.dtype == "i8" else "f32",
+        "storage_dtype": w.dtype,
         "data": "synthetic (seeded N(0,1) / U(0.5,1.5) inputs, resident in HBM)",
         "config": {"workload": w.name, "op": w.op, "rows": w.rows, "hidden": w.hidden,
                    "k": w.k, "eps": w.eps, "kernel": kernel, "rotating_sets": nsets,
