@@ -592,7 +592,35 @@ __global__ __launch_bounds__(WGS) void row_stream_kernel(RowArgs a) {
           if (c < C) IV::unpack(r0[u], acc[u]);
         }
         const int K = KC > 0 ? KC : a.k;
-        for (int q = 1; q < K; ++q) {
+        int q = 1;
+        if constexpr (KC == -2) {
+          // two partials per step, still added in order
+          for (; q + 1 < K; q += 2) {
+            raw_t ra[UNR], rb[UNR];
+            const char* pa = row_ptr(a.partials.p[q], a.partials.s[q], row);
+            const char* pb = row_ptr(a.partials.p[q + 1], a.partials.s[q + 1], row);
+#pragma unroll
+            for (int u = 0; u < UNR; ++u) {
+              const int c = c0 + u * WGS;
+              if (c < C) {
+                ra[u] = IV::template load<NT>(pa, c);
+                rb[u] = IV::template load<NT>(pb, c);
+              }
+            }
+#pragma unroll
+            for (int u = 0; u < UNR; ++u) {
+              const int c = c0 + u * WGS;
+              if (c < C) {
+                float t[V], t2[V];
+                IV::unpack(ra[u], t);
+                IV::unpack(rb[u], t2);
+#pragma unroll
+                for (int e = 0; e < V; ++e) acc[u][e] = (acc[u][e] + t[e]) + t2[e];
+              }
+            }
+          }
+        }
+        for (; q < K; ++q) {
           raw_t rq[UNR];
           const char* prow = row_ptr(a.partials.p[q], a.partials.s[q], row);
 #pragma unroll

@@ -87,7 +87,7 @@ void add_full(std::vector<Variant>& v, Types t) {
   RMSN_VGPR_SHAPES(RMSN_ADD_VGPR)
 #define RMSN_ADD_STREAM_K(KC, VB, WGS, LDS, NT, UNR)                                    \
   if constexpr ((VB == 0 || VB > (int)sizeof(typename DT<T>::scalar_t)) &&               \
-                !stream_spills<VB, WGS, KC, UNR>())                                      \
+                !stream_spills<VB, WGS, KC, UNR>() && (KC != -2 || (VB == 8 && LDS)))    \
     add_variant(v, t, kStream, VB, WGS, 0, WGS, KC, LDS ? 1 : 0, UNR, NT ? 1 : 0,         \
                 reinterpret_cast<const void*>(                                           \
                     &row_stream_kernel<T, T, T, VB, WGS, LDS, KC, UNR, NT>));

@@ -23,6 +23,7 @@ struct Variant {
   int npt;        // chunks per thread held in registers (vgpr)
   int wgs;        // threads per workgroup
   int kc;         // 0 plain, >0 fixed partial count, -1 runtime partial count
+                  // (-2: runtime, two partials per step)
   int lds_stage;  // stream: stage the row in LDS (1) or re-read it (0)
   int unroll;     // stream: chunks in flight per thread per step
   int nt;         // streaming (nontemporal) loads/stores for row data
@@ -63,7 +64,9 @@ struct Variant {
   X(0, 256, true, true, 4) X(0, 512, true, true, 4) X(0, 1024, true, true, 4)             \
   X(0, 256, false, false, 4) X(0, 512, false, false, 4) X(0, 1024, false, false, 4)
 
-#define RMSN_STREAM_KCS(X, ...) X(0, __VA_ARGS__) X(1, __VA_ARGS__) X(-1, __VA_ARGS__)
+// -1: runtime K, one partial per step; -2: runtime K, two partials per step
+// (built for the LDS-staged 8-byte shapes only).
+#define RMSN_STREAM_KCS(X, ...) X(0, __VA_ARGS__) X(1, __VA_ARGS__) X(-1, __VA_ARGS__) X(-2, __VA_ARGS__)
 
 // The general interface -- gamma in fp32 with 16-bit data, or an output dtype
 // other than the data's -- compiles only the shapes the dispatcher picks

@@ -111,7 +111,8 @@ def variant_case(dtype, name):
     s = 4 if dtype == "f32" else 2
     V = 16 // s
     kc = kv["k"]
-    k = 3 if kc == -1 else kc
+    # runtime K: 3 partials; two per step: 4 (one pair, then one alone)
+    k = {-1: 3, -2: 4}.get(kc, kc)
     if kind == "vgpr":
         tpr, npt, wg = kv["tpr"], kv["npt"], kv["wg"]
         chunks = max(1, tpr * npt - 3)

@@ -116,7 +116,9 @@ def test_plan_names_follow_the_dispatch_rule():
     assert "lds" in plan(65536, 16384, 1, "bf16")
     assert ",wg=256,lds,k=-1,unr=8," in plan(65536, 16384, 1, "bf16")   # rows over 16 KiB
     assert plan(32768, 8192, 1, "f32").startswith("stream<f32,v8,wg=256,lds")
-    assert plan(4096, 8192, 8, "bf16") == "stream<bf16,v8,wg=512,lds,k=-1,unr=4,nt>"
+    assert plan(4096, 8192, 8, "bf16") == "stream<bf16,v8,wg=512,lds,k=-2,unr=4,nt>"  # pairs at K=8
+    assert plan(4096, 8192, 4, "bf16") == "stream<bf16,v8,wg=512,lds,k=-1,unr=4,nt>"
+    assert "k=-1" in B.rmsnorm_plan_ex(4096, 8192, 8, "bf16", "f32", "f32")      # none compiled
     assert "tpr=8," in plan(1000, 64, 1, "bf16")            # several rows per wave
     assert "tpr=64," in plan(512, 512, 0, "bf16")           # one row per wave
     # large plain launches: two chunks per thread; small ones and the fused form: one
