@@ -542,6 +542,9 @@ __global__ __launch_bounds__(WGS) void row_vgpr_kernel(RowArgs a) {
 // row: in LDS when LDS_STAGE, else pass 2 re-reads what this same thread
 // wrote (fused) or read (plain) -- a thread only ever touches its own chunks,
 // so no barrier guards the stage.
+// KC: 0 = plain; 1 = one partial; -1 = runtime K, the partials after p0
+// loaded and added one at a time; -2 = runtime K, two at a time (both loads
+// in flight together, the adds still in order).
 // NT: streaming loads/stores for data touched once (never for a residual
 // that pass 2 reads back from memory).
 template <typename T, typename GT, typename OT, int VB, int WGS, bool LDS_STAGE, int KC, int UNR,

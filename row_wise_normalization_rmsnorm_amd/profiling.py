@@ -47,16 +47,25 @@ def kernel_sources(op: str) -> list:
 
 
 def source_hash(op: str) -> str:
-    """sha256 over the kernel source of ``op`` and the compiler flags it is
-    built with: a traffic figure taken on other code is stale."""
+    """sha256 over the kernel source of ``op`` (its code, not its comments)
+    and the compiler flags it is built with: a traffic figure taken on other
+    code is stale."""
     import sys
     sys.path.insert(0, ROOT)
     from row_wise_normalization_rmsnorm_amd.build import FLAGS
     h = hashlib.sha256()
     for p in kernel_sources(op):
-        h.update(open(p, "rb").read())
+        h.update(code_only(open(p).read()).encode())
     h.update(" ".join(FLAGS).encode())
     return h.hexdigest()
+
+
+def code_only(src: str) -> str:
+    """C++ source without comments and with whitespace collapsed, so that
+    editing a comment does not change the hash."""
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return " ".join(src.split())
 
 
 def _one(d: str, suffix: str) -> str:

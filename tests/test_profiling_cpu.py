@@ -105,3 +105,13 @@ def test_bench_refuses_more_than_one_gpu():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_source_hash_ignores_comments_not_code():
+    a = "int f(int x) {  // doubles\n  return 2 * x; /* fast */ }\n"
+    b = "/* header */\nint f(int x) {\n  return 2 * x;\n}\n"
+    c = "int f(int x) { return 3 * x; }"
+    assert prof.code_only(a) == prof.code_only(b)
+    assert prof.code_only(a) != prof.code_only(c)
+    assert len(prof.source_hash("rmsnorm")) == 64
+    assert prof.source_hash("rmsnorm") != prof.source_hash("block_sum")
