@@ -24,7 +24,8 @@ import threading
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SRCS = [os.path.join(_HERE, "rmsnorm_oracle.c"), os.path.join(_HERE, "block_sum_oracle.c")]
+_SRCS = [os.path.join(_HERE, "rmsnorm_oracle.c"), os.path.join(_HERE, "block_sum_oracle.c"),
+         os.path.join(_HERE, "gemm_scatter_oracle.c")]
 _INCLUDE = os.path.join(os.path.dirname(_HERE), "include")
 LIB_PATH = os.path.join(_HERE, "librmsnorm_oracle.so")
 
@@ -93,6 +94,14 @@ class Library:
             lib.block_sum_oracle.restype = ctypes.c_int
             lib.block_sum_oracle_decode.argtypes = [dp, vp, i64, ctypes.c_int]
             lib.block_sum_oracle_decode.restype = ctypes.c_int
+        if hasattr(lib, "gemm_scatter_oracle"):
+            lib.gemm_scatter_oracle.argtypes = [ctypes.POINTER(vp), i64, ctypes.c_int, vp, i64,
+                                                vp, i64, vp, i64, ctypes.c_float, ctypes.c_float,
+                                                i64, i64, i64, ctypes.c_int, i64, i64, dp, dp]
+            lib.gemm_scatter_oracle.restype = ctypes.c_int
+            lib.gemm_scatter_oracle_chunk_order.argtypes = [ctypes.c_int, ctypes.c_int,
+                                                            ctypes.POINTER(ctypes.c_int)]
+            lib.gemm_scatter_oracle_chunk_order.restype = ctypes.c_int
         self.lib = lib
         self.path = path
 
@@ -273,3 +282,54 @@ def block_sum_decode(x: np.ndarray, dtype: str, lib: "Library | None" = None) ->
     _raise(_load(lib).block_sum_oracle_decode(_dptr(dst), ctypes.c_void_p(a.ctypes.data), a.size,
                                               SUM_DTYPE_CODE[dtype]))
     return dst
+
+
+# ---- GEMM with a reduce-scatter epilogue ------------------------------------
+
+def gemm_scatter(a: np.ndarray, b: np.ndarray, c, alpha: float, beta: float, world: int,
+                 dtype: str, rows=None, want_f64: bool = False,
+                 lib: "Library | None" = None):
+    """``alpha * a @ b.T + beta * c`` split into ``world`` row chunks.
+
+    a [m, k], b [n, k] and c [m, n] (or None) are uint16 bit patterns of
+    dtype ("f16" or "bf16"); row strides are taken from the arrays, which must
+    have unit element stride.  ``rows`` = (row0, row1) restricts the rows
+    computed (default: all).  Returns the list of ``world`` chunks ([m/world,
+    n] uint16; for a row range only the rows inside it are filled, the others
+    are zero) and, with ``want_f64``, (y, mag) for the computed rows: the
+    unrounded values and the magnitude scale of their rounding error bound.
+    """
+    m, k = a.shape
+    n = b.shape[0]
+    for arr, what in ((a, "a"), (b, "b")) + (((c, "c"),) if c is not None else ()):
+        if arr.dtype != np.uint16 or arr.ndim != 2 or (arr.shape[1] > 1 and arr.strides[1] != 2):
+            raise ValueError(f"{what}: expected a 2-D uint16 array with unit element stride")
+    if b.shape[1] != k or (c is not None and c.shape != (m, n)):
+        raise ValueError("shape mismatch")
+    if world < 1 or m % world:
+        raise ValueError("m must split into world equal chunks")
+    r0, r1 = rows if rows is not None else (0, m)
+    chunks = [np.zeros((m // world, n), np.uint16) for _ in range(world)]
+    ptrs = (ctypes.c_void_p * world)(*[ch.ctypes.data for ch in chunks])
+    y = np.empty((r1 - r0, n), np.float64) if want_f64 else None
+    mag = np.empty((r1 - r0, n), np.float64) if want_f64 else None
+    rc = _load(lib).gemm_scatter_oracle(
+        ptrs, n, world, _ptr(a), _ld(a), _ptr(b), _ld(b),
+        None if c is None else _ptr(c), 0 if c is None else _ld(c),
+        ctypes.c_float(alpha), ctypes.c_float(beta), m, n, k, DTYPE_CODE[dtype], r0, r1,
+        _dptr(y), _dptr(mag))
+    _raise(rc)
+    return (chunks, y, mag) if want_f64 else chunks
+
+
+def _ld(arr: np.ndarray) -> int:
+    """Row stride in elements (at least the row length, also for one row)."""
+    return max(arr.strides[0] // 2, arr.shape[1]) if arr.shape[0] > 1 else arr.shape[1]
+
+
+def gemm_scatter_chunk_order(world: int, rank: int, lib: "Library | None" = None) -> list:
+    """The order in which one rank's chunks are produced: the other ranks'
+    chunks first, the rank's own last."""
+    order = (ctypes.c_int * max(world, 1))()
+    _raise(_load(lib).gemm_scatter_oracle_chunk_order(world, rank, order))
+    return list(order[:world])
