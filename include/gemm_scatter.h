@@ -1,0 +1,98 @@
+/*
+ * gemm_scatter.h -- C ABI of the GEMM whose epilogue stores straight into
+ * reduce-scatter buffers, in librmsnorm.so, on MI355X (gfx950).
+ *
+ * The operation follows page "LLM System: 通信计算融合算子实现 01 - sm80GEMM +
+ * ReduceScatter":
+ *   - section "flux实现：sm80 gemm+rs": the second GEMM of a tensor-parallel
+ *     FFN writes its output tiles into the reduce-scatter buffers in its
+ *     epilogue, so no separate copy is needed;
+ *   - section "cutlass自定义epilogue–sm80": the epilogue computes
+ *     alpha * accumulator + beta * C and scatters each tile to the buffer
+ *     that holds it, raising a per-tile flag once the tile is written;
+ *   - section "gemmrs版本的swizzle如何编排": the output is cut into one chunk
+ *     per rank and the tiles of the other ranks' chunks are computed first,
+ *     the local chunk last.
+ * On one GPU every buffer is local memory; with several GPUs dst[q] would be
+ * rank q's receive buffer (mapped peer memory), and the reduction of the
+ * received chunks with the residual is add_rmsnorm_fwd with k = world.
+ *
+ * What is computed (products accumulate in fp32 on the matrix cores):
+ *     D[i][j] = alpha * sum_p A[i][p] * B[j][p] + beta * C[i][j]
+ * A [m][k], B [n][k] (the weight layout of a linear layer: k contiguous),
+ * C [m][n] (optional); D rounded once to the storage type (round to nearest
+ * even).  The m rows form `world` chunks of m / world rows; row i goes to
+ * chunk q = i / (m / world), stored at dst[q] + (i - q * m / world) * ldd.
+ * The fp32 result differs from the exact value by at most about
+ * k * 2^-24 * (|alpha| * sum_p |A[i][p] * B[j][p]|) + 2^-23 * |beta * C[i][j]|
+ * before the final rounding.
+ *
+ * Conventions (shared with rmsnorm.h, whose RMSN_* codes and
+ * rmsnorm_strerror / rmsnorm_last_error apply):
+ *   - a, b, c, every dst[q] and flags are DEVICE pointers; `dst` itself is a
+ *     HOST array of `world` pointers, read during the call only.  Strides
+ *     (lda, ldb, ldc, ldd) are in elements.
+ *   - dtype: RMSN_F16 or RMSN_BF16 for every tensor.
+ *   - For k > 0, a and b must be 16-byte aligned with lda, ldb and k
+ *     multiples of 8 (whole 16-byte chunks along k); with k == 0 they are
+ *     not read.  c and dst need 2-byte alignment.
+ *   - 1 <= world <= GEMM_SCATTER_WORLD_MAX, 0 <= rank < world, m divisible
+ *     by world; m, n, k below 2^31; 255 * lda + k and 255 * ldb + k below
+ *     2^29 (a tile's operand rows are addressed with 32-bit offsets).
+ *   - flags (nullable): gemm_scatter_tiles(m, n) uint32 slots.  When given,
+ *     the workgroup that computes tile t stores `epoch` to flags[t] after
+ *     the tile's elements are written and made visible at system scope, so a
+ *     consumer that reads flags[t] == epoch sees the whole tile.  Tile t
+ *     covers rows [(t / TN) * GEMM_SCATTER_TILE_M, ...) and columns
+ *     [(t % TN) * GEMM_SCATTER_TILE_N, ...), TN = ceil(n / TILE_N).
+ *   - dst chunks must not overlap each other, a, b, c or flags.
+ *   - The call enqueues one kernel on `stream` (NULL: the default stream),
+ *     allocates nothing and does not synchronise.  Arguments are validated
+ *     before the launch; on error nothing is launched.  m == 0 or n == 0
+ *     launches nothing; k == 0 gives beta * C (or zeros).
+ */
+#ifndef GEMM_SCATTER_H
+#define GEMM_SCATTER_H
+
+#include <stdint.h>
+
+#include "rmsnorm.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GEMM_SCATTER_WORLD_MAX 16
+#define GEMM_SCATTER_TILE_M 256
+#define GEMM_SCATTER_TILE_N 256
+
+/*
+ * gemm_scatter_fwd -- the epilogue-scattered product above.  Returns RMSN_OK,
+ * RMSN_ERR_NULL, RMSN_ERR_SHAPE (sizes, strides, alignment, world, rank),
+ * RMSN_ERR_DTYPE, RMSN_ERR_ALIAS or RMSN_ERR_HIP.
+ */
+int gemm_scatter_fwd(void* const* dst, int64_t ldd, int world, int rank, const void* a,
+                     int64_t lda, const void* b, int64_t ldb, const void* c, int64_t ldc,
+                     float alpha, float beta, int64_t m, int64_t n, int64_t k, int dtype,
+                     uint32_t* flags, uint32_t epoch, void* stream);
+
+/* gemm_scatter_tiles -- number of output tiles (and flag slots) for m x n;
+ * -1 if m or n is negative or too large. */
+int64_t gemm_scatter_tiles(int64_t m, int64_t n);
+
+/*
+ * gemm_scatter_schedule -- the tile schedule of one launch (host only, no
+ * GPU needed).  For workgroup w (launch order), wg_tile[w] is the tile it
+ * computes; pos_tile[s] is the tile at position s of the schedule (the
+ * remote-first chunk order, before workgroups are spread over the GPU's
+ * eight XCDs).  Either array may be NULL; each holds `len` >=
+ * gemm_scatter_tiles(m, n) entries.  Returns RMSN_OK or RMSN_ERR_SHAPE.
+ */
+int gemm_scatter_schedule(int64_t m, int64_t n, int world, int rank, int32_t* wg_tile,
+                          int32_t* pos_tile, int64_t len);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GEMM_SCATTER_H */

@@ -24,6 +24,12 @@ EXPORTS = ("rmsnorm_fwd", "add_rmsnorm_fwd", "rmsnorm_strerror", "rmsnorm_last_e
            "rmsnorm_plan", "rmsnorm_variants", "rmsnorm_fwd_ex", "add_rmsnorm_fwd_ex",
            "rmsnorm_plan_ex", "rmsnorm_variants_ex", "rmsnorm_plan_call")
 BLOCK_SUM_EXPORTS = ("block_all_reduce_sum",)
+GEMM_SCATTER_EXPORTS = ("gemm_scatter_fwd", "gemm_scatter_tiles", "gemm_scatter_schedule")
+
+# GEMM with a reduce-scatter epilogue (include/gemm_scatter.h)
+GEMM_SCATTER_WORLD_MAX = 16
+GEMM_SCATTER_TILE_M = 256
+GEMM_SCATTER_TILE_N = 256
 
 # block all-reduce sum (include/block_sum.h)
 BRS_DTYPE_CODE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2,
@@ -83,6 +89,16 @@ def lib() -> ctypes.CDLL:
             l.rmsnorm_plan_call.restype = c_int
             l.block_all_reduce_sum.argtypes = [vp, vp, i64, c_int, vp, i64, vp]
             l.block_all_reduce_sum.restype = c_int
+            l.gemm_scatter_fwd.argtypes = [ctypes.POINTER(vp), i64, c_int, c_int, vp, i64, vp,
+                                           i64, vp, i64, c_float, c_float, i64, i64, i64, c_int,
+                                           vp, ctypes.c_uint32, vp]
+            l.gemm_scatter_fwd.restype = c_int
+            l.gemm_scatter_tiles.argtypes = [i64, i64]
+            l.gemm_scatter_tiles.restype = i64
+            l.gemm_scatter_schedule.argtypes = [i64, i64, c_int, c_int,
+                                                ctypes.POINTER(ctypes.c_int32),
+                                                ctypes.POINTER(ctypes.c_int32), i64]
+            l.gemm_scatter_schedule.restype = c_int
             _lib = l
         return _lib
 
@@ -302,6 +318,94 @@ def block_all_reduce_sum(x: torch.Tensor) -> torch.Tensor:
                       device=x.device)
     block_all_reduce_sum_fwd(out, x)
     return out
+
+
+# GEMM with a reduce-scatter epilogue -----------------------------------------
+
+def _matrix(t: torch.Tensor, what: str):
+    """(pointer, row stride in elements) of a 2-D device tensor whose
+    elements are contiguous within a row."""
+    if not t.is_cuda:
+        raise RmsnormError(-1, f"{what} must be a device tensor")
+    if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
+        raise RmsnormError(-2, f"{what} must be 2-D with contiguous rows")
+    ld = t.stride(0) if t.shape[0] > 1 else t.shape[1]
+    return t.data_ptr(), max(ld, t.shape[1])
+
+
+def gemm_scatter_tiles(m: int, n: int) -> int:
+    return int(lib().gemm_scatter_tiles(m, n))
+
+
+def gemm_scatter_schedule(m: int, n: int, world: int, rank: int):
+    """(wg_tile, pos_tile): the tile each workgroup computes, and the tile at
+    each position of the remote-first schedule."""
+    t = gemm_scatter_tiles(m, n)
+    if t < 0:
+        _check(-2)
+    wg = (ctypes.c_int32 * max(t, 1))()
+    pos = (ctypes.c_int32 * max(t, 1))()
+    _check(lib().gemm_scatter_schedule(m, n, world, rank, wg, pos, t))
+    return list(wg[:t]), list(pos[:t])
+
+
+def gemm_scatter_fwd(dst: Sequence[torch.Tensor], a: torch.Tensor, b: torch.Tensor,
+                     c: Optional[torch.Tensor] = None, alpha: float = 1.0, beta: float = 0.0,
+                     rank: int = 0, flags: Optional[torch.Tensor] = None, epoch: int = 0,
+                     stream=None) -> None:
+    """dst[q] = rows [q m/W, (q+1) m/W) of alpha * a @ b.T + beta * c, W = len(dst).
+
+    a [m, k], b [n, k], c [m, n] and every dst[q] [m/W, n] share one 16-bit
+    dtype; rows may be strided, elements within a row contiguous.  flags
+    (uint32/int32, gemm_scatter_tiles(m, n) slots) receive ``epoch`` per
+    finished tile."""
+    if a.dtype not in (torch.float16, torch.bfloat16):
+        raise RmsnormError(-3, f"unsupported dtype {a.dtype}")
+    world = len(dst)
+    m, k = a.shape
+    n = b.shape[0]
+    if b.dim() != 2 or b.shape[1] != k or (c is not None and tuple(c.shape) != (m, n)):
+        raise RmsnormError(-2, "shape mismatch between a, b and c")
+    for t, what in ((b, "b"), (c, "c"), *((d, "dst") for d in dst)):
+        if t is not None and t.dtype != a.dtype:
+            raise RmsnormError(-3, f"{what} dtype {t.dtype} differs from a's {a.dtype}")
+    if world < 1 or world > GEMM_SCATTER_WORLD_MAX or m % world:
+        raise RmsnormError(-2, "need 1 <= len(dst) <= 16 dividing m")
+    ldd = None
+    ptrs = []
+    for d in dst:
+        if tuple(d.shape) != (m // world, n):
+            raise RmsnormError(-2, f"every dst chunk must be [{m // world}, {n}]")
+        p, ld = _matrix(d, "dst")
+        if ldd is not None and ld != ldd:
+            raise RmsnormError(-2, "dst chunks must share one row stride")
+        ldd = ld
+        ptrs.append(p)
+    pa, lda = _matrix(a, "a")
+    pb, ldb = _matrix(b, "b")
+    pc, ldc = _matrix(c, "c") if c is not None else (None, 0)
+    pf = None
+    if flags is not None:
+        if flags.dtype not in (torch.int32, torch.uint32) or not flags.is_contiguous() or \
+                flags.numel() < gemm_scatter_tiles(m, n):
+            raise RmsnormError(-2, "flags must be a contiguous int32 tensor with one slot per tile")
+        pf = flags.data_ptr()
+    arr = (ctypes.c_void_p * world)(*ptrs)
+    _check(lib().gemm_scatter_fwd(arr, ldd, world, rank, pa, lda, pb, ldb, pc, ldc,
+                                  ctypes.c_float(alpha), ctypes.c_float(beta), m, n, k,
+                                  DTYPE_CODE[a.dtype], pf, ctypes.c_uint32(epoch & 0xFFFFFFFF),
+                                  _stream(a, stream)))
+
+
+def gemm_scatter(a: torch.Tensor, b: torch.Tensor, world: int, rank: int = 0,
+                 c: Optional[torch.Tensor] = None, alpha: float = 1.0,
+                 beta: float = 0.0) -> list:
+    """Allocating form: returns the ``world`` chunks."""
+    m = a.shape[0]
+    dst = [torch.empty(m // world, b.shape[0], dtype=a.dtype, device=a.device)
+           for _ in range(world)]
+    gemm_scatter_fwd(dst, a, b, c, alpha, beta, rank)
+    return dst
 
 
 # convenience wrappers ------------------------------------------------------

@@ -1,0 +1,487 @@
+// gemm_scatter.hip -- GEMM with a reduce-scatter epilogue on gfx950, and its
+// C ABI (include/gemm_scatter.h).
+//
+// Method: page "LLM System: 通信计算融合算子实现 01 - sm80GEMM +
+// ReduceScatter".  The epilogue of the FFN's second GEMM computes
+// alpha * acc + beta * C and writes each output tile straight into the
+// buffer of the rank whose chunk it belongs to (section
+// "cutlass自定义epilogue–sm80"), raising a per-tile flag after the tile is
+// visible; tiles of the other ranks' chunks are scheduled before the local
+// chunk (section "gemmrs版本的swizzle如何编排").
+//
+// MI355X design:
+//   - 256 x 256 output tile per workgroup of four waves (2 x 2), each wave a
+//     128 x 128 block of 8 x 8 v_mfma_f32_16x16x32 products (fp32 accumulate)
+//     over k steps of 64.
+//   - The matrix-core operands are swapped (the weight rows feed the first
+//     operand, the activation rows the second), so each lane's four
+//     accumulator values are four consecutive output columns of one row and
+//     leave as one 8-byte store.
+//   - A and B tiles pass through LDS, double-buffered (2 x 64 KiB of the
+//     CU's 160 KiB): each thread loads 16-byte chunks of the next k step
+//     into registers while the waves multiply the current one, then writes
+//     them to the other buffer; one barrier per k step.
+//   - LDS rows are 128 bytes (64 elements); the 16-byte chunk c of row r is
+//     stored at chunk position c ^ (r & 7), so the eight lanes of each LDS
+//     access phase, which read the same chunk of eight consecutive rows, hit
+//     eight different bank groups.
+//   - Tile order: tile-rows rotated so that the chunks after the local
+//     rank's come first and the local chunk last, grouped a few tile-rows at
+//     a time (column-major within a group) for cache reuse; consecutive
+//     workgroups land on different XCDs (round-robin dispatch), so each
+//     round of positions is dealt out in contiguous runs per XCD.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+
+#include "../../include/gemm_scatter.h"
+
+int rmsn_set_error(int code, const char* msg);
+
+namespace gsc {
+
+constexpr int BM = GEMM_SCATTER_TILE_M;
+constexpr int BN = GEMM_SCATTER_TILE_N;
+constexpr int BK = 64;                 // k elements per step (128 bytes of a row)
+constexpr int kThreads = 256;          // four waves
+constexpr int kChunksPerRow = BK / 8;  // 16-byte chunks per LDS row
+constexpr int kXcds = 8;
+constexpr int kRoundPerXcd = 32;       // positions each XCD takes per round (one per CU)
+constexpr int kGroupM = 2;             // tile-rows per schedule group
+// Buffer resource word 3 for gfx9-family raw (untyped) buffer access; the
+// offset used for a chunk outside every operand's range.
+constexpr int kRsrcWord3 = 0x00020000;
+constexpr int kOutOfRange = 0x7FFFFFF0;
+static_assert(BM == 256 && BN == 256 && kThreads == 256, "the thread mapping assumes these");
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+template <int DT>
+struct Elem;
+
+template <>
+struct Elem<RMSN_BF16> {
+  __device__ static f32x4 mfma(u32x4 x, u32x4 y, f32x4 acc) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, x),
+                                                   __builtin_bit_cast(bf16x8, y), acc, 0, 0, 0);
+  }
+  __device__ static float decode(uint16_t h) { return __builtin_bit_cast(float, (uint32_t)h << 16); }
+  __device__ static uint32_t pack2(float lo, float hi) {
+    const f32x2 v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+  }
+  __device__ static uint16_t pack1(float v) { return (uint16_t)(pack2(v, 0.0f) & 0xFFFFu); }
+};
+
+template <>
+struct Elem<RMSN_F16> {
+  __device__ static f32x4 mfma(u32x4 x, u32x4 y, f32x4 acc) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, x),
+                                                  __builtin_bit_cast(f16x8, y), acc, 0, 0, 0);
+  }
+  __device__ static float decode(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
+  __device__ static uint32_t pack2(float lo, float hi) {
+    const f32x2 v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+  }
+  __device__ static uint16_t pack1(float v) { return (uint16_t)(pack2(v, 0.0f) & 0xFFFFu); }
+};
+
+// ---- tile schedule (shared by the kernel and the host's plan query) --------
+
+struct Sched {
+  int tiles_m, tiles_n, tiles;
+  int tm_start;  // first tile-row of the rotated order
+  int group_m;   // tile-rows per schedule group (never straddling two chunks)
+};
+
+__host__ __device__ inline Sched make_sched(int m, int n, int world, int rank) {
+  Sched s;
+  s.tiles_m = (m + BM - 1) / BM;
+  s.tiles_n = (n + BN - 1) / BN;
+  s.tiles = s.tiles_m * s.tiles_n;
+  // the first tile-row whose first row lies in chunk rank + 1 or later
+  const int64_t chunk_rows = world > 0 ? (int64_t)m / world : m;
+  const int64_t first_row = (int64_t)(rank + 1) * chunk_rows;
+  int64_t tm = (first_row + BM - 1) / BM;
+  if (tm >= s.tiles_m) tm = 0;
+  s.tm_start = (int)tm;
+  // Chunks that are whole tile-rows (r of them each) take groups of the
+  // largest divisor of r up to kGroupM, so no group mixes two chunks; other
+  // chunk sizes take one tile-row per group.
+  s.group_m = 1;
+  if (chunk_rows > 0 && chunk_rows % BM == 0) {
+    const int64_t r = chunk_rows / BM;
+    for (int g = kGroupM; g > 1; --g)
+      if (r % g == 0) {
+        s.group_m = g;
+        break;
+      }
+  }
+  return s;
+}
+
+// launch order -> schedule position: each round of kXcds * kRoundPerXcd
+// positions is dealt out so that XCD x (which receives workgroups x, x + 8,
+// ...) takes a contiguous run of kRoundPerXcd positions; a final partial
+// round keeps the identity.
+__host__ __device__ inline int position_of_wg(int w, int tiles) {
+  constexpr int round = kXcds * kRoundPerXcd;
+  const int full = tiles / round * round;
+  if (w >= full) return w;
+  const int base = w / round * round;
+  const int within = w - base;
+  return base + (within % kXcds) * kRoundPerXcd + within / kXcds;
+}
+
+// schedule position -> tile: groups of group_m rotated tile-rows,
+// column-major inside a group.
+__host__ __device__ inline int tile_at(int p, const Sched& s) {
+  const int group = s.group_m * s.tiles_n;
+  const int g = p / group;
+  const int idx = p - g * group;
+  const int first = g * s.group_m;
+  const int rows = s.tiles_m - first < s.group_m ? s.tiles_m - first : s.group_m;
+  const int ptm = first + idx % rows;
+  const int tn = idx / rows;
+  const int tm = (ptm + s.tm_start) % s.tiles_m;
+  return tm * s.tiles_n + tn;
+}
+
+struct Params {
+  const uint16_t* a;
+  const uint16_t* b;
+  const uint16_t* c;
+  int64_t lda, ldb, ldc, ldd;
+  uint16_t* dst[GEMM_SCATTER_WORLD_MAX];
+  uint32_t* flags;
+  uint32_t epoch;
+  int m, n, k;
+  int chunk_rows;
+  float alpha, beta;
+  int vec_out;  // every dst row and C row 8-byte aligned for 4-element access
+  Sched sched;
+};
+
+template <int DT>
+__global__ __launch_bounds__(kThreads) void gemm_scatter_kernel(Params p) {
+  using E = Elem<DT>;
+  // [stage][operand: 0 = A rows (m), 1 = B rows (n)][row * 8 + chunk]
+  __shared__ u32x4 lds[2][2][BM * kChunksPerRow];
+
+  const int tile = tile_at(position_of_wg((int)blockIdx.x, p.sched.tiles), p.sched);
+  const int m0 = (tile / p.sched.tiles_n) * BM;
+  const int n0 = (tile % p.sched.tiles_n) * BN;
+  const int tid = (int)threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // global -> LDS: thread t moves logical chunk (t & 7) of rows (t >> 3) + 32 i
+  const int lrow = tid >> 3;
+  const int lchunk = tid & 7;
+
+  f32x4 acc[8][8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s)
+#pragma unroll
+    for (int t = 0; t < 8; ++t) acc[s][t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  u32x4 ra[8], rb[8];
+  const int nk = (p.k + BK - 1) / BK;
+
+  // Operand loads are raw buffer loads over this tile's rows; the resource
+  // ends at the last element of the tile's last existing row.  Rows past m
+  // (n) only feed outputs that are never stored, so they re-read the
+  // thread's last existing row.  Chunks past k must read as zero: they take
+  // an offset beyond every resource, which the range check turns into zeros.
+  // Nothing is selected after a load, so the loads of the next k step stay
+  // in flight while the current one is multiplied.  The whole variable
+  // offset sits in the VGPR offset, which the range check covers.
+  const int a_tile_rows = p.m - m0 < BM ? p.m - m0 : BM;
+  const int b_tile_rows = p.n - n0 < BN ? p.n - n0 : BN;
+  const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.a + (int64_t)m0 * p.lda), (short)0,
+      (int)(((int64_t)(a_tile_rows - 1) * p.lda + p.k) * 2), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.b + (int64_t)n0 * p.ldb), (short)0,
+      (int)(((int64_t)(b_tile_rows - 1) * p.ldb + p.k) * 2), kRsrcWord3);
+  // rows lrow + 32 i exist for i < a_rows (b_rows); the last one of them
+  const int a_rows = a_tile_rows > lrow ? (a_tile_rows - lrow + 31) / 32 : 0;
+  const int b_rows = b_tile_rows > lrow ? (b_tile_rows - lrow + 31) / 32 : 0;
+  const int a_last = a_rows > 0 ? lrow + 32 * (a_rows - 1) : a_tile_rows - 1;
+  const int b_last = b_rows > 0 ? lrow + 32 * (b_rows - 1) : b_tile_rows - 1;
+  const int a_off0 = (lrow * (int)p.lda + lchunk * 8) * 2;
+  const int b_off0 = (lrow * (int)p.ldb + lchunk * 8) * 2;
+  const int a_off_last = (a_last * (int)p.lda + lchunk * 8) * 2;
+  const int b_off_last = (b_last * (int)p.ldb + lchunk * 8) * 2;
+  const int a_row_step = 32 * (int)p.lda * 2, b_row_step = 32 * (int)p.ldb * 2;
+
+  auto gload = [&](int kt) {
+    const bool kin = kt * BK + lchunk * 8 < p.k;
+    const int kb = kt * BK * 2;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int oa = kin ? (i < a_rows ? a_off0 + i * a_row_step : a_off_last) + kb : kOutOfRange;
+      const int ob = kin ? (i < b_rows ? b_off0 + i * b_row_step : b_off_last) + kb : kOutOfRange;
+      ra[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsa, oa, 0, 0));
+      rb[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsb, ob, 0, 0));
+    }
+  };
+  auto lstore = [&](int stage) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = lrow + 32 * i;
+      const int at = r * kChunksPerRow + (lchunk ^ (r & 7));
+      lds[stage][0][at] = ra[i];
+      lds[stage][1][at] = rb[i];
+    }
+  };
+
+  // Fragments of one 32-wide k half: lane l supplies row (l & 15) of each
+  // 16-row block and 16-byte chunk ks*4 + l/16 of the 64-wide k step.
+  auto read_frags = [&](int stage, int ks, u32x4 (&xf)[8], u32x4 (&yf)[8]) {
+    const int sw = (ks * 4 + (lane >> 4)) ^ (lane & 7);
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+      xf[s] = lds[stage][1][(wn * 128 + s * 16 + (lane & 15)) * kChunksPerRow + sw];
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+      yf[t] = lds[stage][0][(wm * 128 + t * 16 + (lane & 15)) * kChunksPerRow + sw];
+  };
+  auto mfmas = [&](const u32x4 (&xf)[8], const u32x4 (&yf)[8]) {
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+#pragma unroll
+      for (int t = 0; t < 8; ++t) acc[s][t] = E::mfma(xf[s], yf[t], acc[s][t]);
+  };
+
+  if (nk > 0) {
+    gload(0);
+    lstore(0);
+  }
+  __syncthreads();
+  u32x4 x0[8], y0[8], x1[8], y1[8];
+  if (nk > 0) read_frags(0, 0, x0, y0);
+
+  // One k step per iteration, with no branch inside: the loads of step
+  // kt + 1 (step kt again on the last iteration: harmless, never read) go
+  // out first; the second half's fragments are read while the first half
+  // multiplies; the staged loads are written to the other LDS buffer while
+  // the second half multiplies; after the barrier the next step's first
+  // half is read.
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    gload(kt + 1 < nk ? kt + 1 : kt);
+    read_frags(cur, 1, x1, y1);
+    mfmas(x0, y0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one global (buffer) load
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // four MFMAs
+    }
+    lstore(cur ^ 1);
+    mfmas(x1, y1);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // one LDS write
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // four MFMAs
+    }
+    __syncthreads();
+    read_frags(cur ^ 1, 0, x0, y0);
+  }
+
+  // epilogue: acc[s][t][r] is D[row m0 + wm*128 + t*16 + (lane & 15)]
+  //                           [col n0 + wn*128 + s*16 + 4*(lane >> 4) + r]
+  const int row0 = m0 + wm * 128 + (lane & 15);
+  const int col0 = n0 + wn * 128 + 4 * (lane >> 4);
+  if (p.vec_out && m0 + BM <= p.m && n0 + BN <= p.n) {
+    // interior tile: every element exists and every access is 8-byte aligned
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int gm = row0 + t * 16;
+      const int q = gm / p.chunk_rows;
+      uint16_t* drow = p.dst[q] + (int64_t)(gm - q * p.chunk_rows) * p.ldd + col0;
+      const uint16_t* crow = p.c ? p.c + (int64_t)gm * p.ldc + col0 : nullptr;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = p.alpha * acc[s][t][r];
+        if (crow) {
+          const u32x2 cv = *reinterpret_cast<const u32x2*>(crow + s * 16);
+          v[0] = __builtin_fmaf(p.beta, E::decode((uint16_t)(cv.x & 0xFFFFu)), v[0]);
+          v[1] = __builtin_fmaf(p.beta, E::decode((uint16_t)(cv.x >> 16)), v[1]);
+          v[2] = __builtin_fmaf(p.beta, E::decode((uint16_t)(cv.y & 0xFFFFu)), v[2]);
+          v[3] = __builtin_fmaf(p.beta, E::decode((uint16_t)(cv.y >> 16)), v[3]);
+        }
+        *reinterpret_cast<u32x2*>(drow + s * 16) = u32x2{E::pack2(v[0], v[1]), E::pack2(v[2], v[3])};
+      }
+    }
+  } else {
+    // edge tile (or unaligned rows): element by element, inside m x n only
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int gm = row0 + t * 16;
+      const bool row_ok = gm < p.m;
+      const int gmc = row_ok ? gm : 0;
+      const int q = gmc / p.chunk_rows;
+      uint16_t* drow = p.dst[q] + (int64_t)(gmc - q * p.chunk_rows) * p.ldd;
+      const uint16_t* crow = p.c ? p.c + (int64_t)gmc * p.ldc : nullptr;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int gn = col0 + s * 16 + r;
+          if (row_ok && gn < p.n) {
+            float v = p.alpha * acc[s][t][r];
+            if (crow) v = __builtin_fmaf(p.beta, E::decode(crow[gn]), v);
+            drow[gn] = E::pack1(v);
+          }
+        }
+      }
+    }
+  }
+
+  if (p.flags) {
+    __threadfence_system();
+    __syncthreads();
+    if (tid == 0)
+      __hip_atomic_store(p.flags + tile, p.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+  }
+}
+
+}  // namespace gsc
+
+namespace {
+
+constexpr int64_t kIntMax = 0x7FFFFFFF;
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t p = (uintptr_t)a, q = (uintptr_t)b;
+  return p < q + nb && q < p + na;
+}
+
+size_t extent(int64_t rows, int64_t cols, int64_t ld, int64_t elem) {
+  if (rows <= 0 || cols <= 0) return 0;
+  return (size_t)(((rows - 1) * ld + cols) * elem);
+}
+
+}  // namespace
+
+extern "C" int64_t gemm_scatter_tiles(int64_t m, int64_t n) {
+  if (m < 0 || n < 0 || m > kIntMax || n > kIntMax) return -1;
+  const int64_t t = ((m + gsc::BM - 1) / gsc::BM) * ((n + gsc::BN - 1) / gsc::BN);
+  return t > kIntMax ? -1 : t;
+}
+
+extern "C" int gemm_scatter_schedule(int64_t m, int64_t n, int world, int rank, int32_t* wg_tile,
+                                     int32_t* pos_tile, int64_t len) {
+  const int64_t tiles = gemm_scatter_tiles(m, n);
+  if (tiles < 0 || world < 1 || world > GEMM_SCATTER_WORLD_MAX || rank < 0 || rank >= world ||
+      m % world != 0 || len < tiles)
+    return rmsn_set_error(RMSN_ERR_SHAPE, "gemm_scatter_schedule: bad sizes, world or rank");
+  const gsc::Sched s = gsc::make_sched((int)m, (int)n, world, rank);
+  for (int w = 0; w < s.tiles; ++w) {
+    if (wg_tile) wg_tile[w] = gsc::tile_at(gsc::position_of_wg(w, s.tiles), s);
+    if (pos_tile) pos_tile[w] = gsc::tile_at(w, s);
+  }
+  return RMSN_OK;
+}
+
+extern "C" int gemm_scatter_fwd(void* const* dst, int64_t ldd, int world, int rank,
+                                const void* a, int64_t lda, const void* b, int64_t ldb,
+                                const void* c, int64_t ldc, float alpha, float beta, int64_t m,
+                                int64_t n, int64_t k, int dtype, uint32_t* flags, uint32_t epoch,
+                                void* stream) {
+  if (dtype != RMSN_F16 && dtype != RMSN_BF16)
+    return rmsn_set_error(RMSN_ERR_DTYPE, "gemm_scatter: dtype must be f16 or bf16");
+  if (m < 0 || n < 0 || k < 0 || m > kIntMax || n > kIntMax || k > kIntMax)
+    return rmsn_set_error(RMSN_ERR_SHAPE, "gemm_scatter: m, n, k must lie in [0, 2^31)");
+  if (world < 1 || world > GEMM_SCATTER_WORLD_MAX || rank < 0 || rank >= world)
+    return rmsn_set_error(RMSN_ERR_SHAPE, "gemm_scatter: world or rank out of range");
+  if (m % world != 0) return rmsn_set_error(RMSN_ERR_SHAPE, "gemm_scatter: m % world != 0");
+  if (!dst) return rmsn_set_error(RMSN_ERR_NULL, "gemm_scatter: dst is NULL");
+  if (m == 0 || n == 0) return RMSN_OK;
+  for (int q = 0; q < world; ++q)
+    if (!dst[q]) return rmsn_set_error(RMSN_ERR_NULL, "gemm_scatter: a dst chunk is NULL");
+  if (k > 0 && (!a || !b)) return rmsn_set_error(RMSN_ERR_NULL, "gemm_scatter: a or b is NULL");
+  if (ldd < n || (c && ldc < n) || lda < k || ldb < k)
+    return rmsn_set_error(RMSN_ERR_SHAPE, "gemm_scatter: a stride is shorter than its row");
+  if (k > 0 && (k % 8 != 0 || lda % 8 != 0 || ldb % 8 != 0 || ((uintptr_t)a & 15u) ||
+                ((uintptr_t)b & 15u)))
+    return rmsn_set_error(RMSN_ERR_SHAPE,
+                          "gemm_scatter: k, lda, ldb must be multiples of 8 and a, b 16-byte aligned");
+  // operand offsets inside one tile's rows are 32-bit byte offsets
+  if (k > 0 && ((int64_t)(gsc::BM - 1) * lda + k >= (int64_t)1 << 29 ||
+                (int64_t)(gsc::BN - 1) * ldb + k >= (int64_t)1 << 29))
+    return rmsn_set_error(RMSN_ERR_SHAPE, "gemm_scatter: lda or ldb too large (255 * ld + k >= 2^29)");
+  bool vec = (ldd % 4 == 0) && (!c || (ldc % 4 == 0 && ((uintptr_t)c & 7u) == 0));
+  for (int q = 0; q < world; ++q) {
+    if ((uintptr_t)dst[q] & 1u) return rmsn_set_error(RMSN_ERR_SHAPE, "gemm_scatter: dst misaligned");
+    if ((uintptr_t)dst[q] & 7u) vec = false;
+  }
+  if ((c && ((uintptr_t)c & 1u)) || (flags && ((uintptr_t)flags & 3u)))
+    return rmsn_set_error(RMSN_ERR_SHAPE, "gemm_scatter: c or flags misaligned");
+
+  const int64_t chunk_rows = m / world;
+  const int64_t tiles = gemm_scatter_tiles(m, n);
+  if (tiles < 0) return rmsn_set_error(RMSN_ERR_SHAPE, "gemm_scatter: too many tiles");
+  const size_t dext = extent(chunk_rows, n, ldd, 2);
+  const size_t aext = k > 0 ? extent(m, k, lda, 2) : 0, bext = k > 0 ? extent(n, k, ldb, 2) : 0;
+  const size_t cext = c ? extent(m, n, ldc, 2) : 0;
+  const size_t fext = flags ? (size_t)tiles * 4 : 0;
+  for (int q = 0; q < world; ++q) {
+    if (overlap(dst[q], dext, a, aext) || overlap(dst[q], dext, b, bext) ||
+        overlap(dst[q], dext, c, cext) || overlap(dst[q], dext, flags, fext))
+      return rmsn_set_error(RMSN_ERR_ALIAS, "gemm_scatter: a dst chunk overlaps an input or flags");
+    for (int r = 0; r < q; ++r)
+      if (overlap(dst[q], dext, dst[r], dext))
+        return rmsn_set_error(RMSN_ERR_ALIAS, "gemm_scatter: dst chunks overlap");
+  }
+
+  gsc::Params p{};
+  p.a = static_cast<const uint16_t*>(a);
+  p.b = static_cast<const uint16_t*>(b);
+  p.c = static_cast<const uint16_t*>(c);
+  p.lda = lda;
+  p.ldb = ldb;
+  p.ldc = c ? ldc : 0;
+  p.ldd = ldd;
+  for (int q = 0; q < world; ++q) p.dst[q] = static_cast<uint16_t*>(dst[q]);
+  p.flags = flags;
+  p.epoch = epoch;
+  p.m = (int)m;
+  p.n = (int)n;
+  p.k = (int)k;
+  p.chunk_rows = (int)chunk_rows;
+  p.alpha = alpha;
+  p.beta = beta;
+  p.vec_out = vec ? 1 : 0;
+  p.sched = gsc::make_sched((int)m, (int)n, world, rank);
+
+  hipStream_t st = (hipStream_t)stream;
+  if (dtype == RMSN_BF16)
+    hipLaunchKernelGGL(gsc::gemm_scatter_kernel<RMSN_BF16>, dim3((unsigned)tiles),
+                       dim3(gsc::kThreads), 0, st, p);
+  else
+    hipLaunchKernelGGL(gsc::gemm_scatter_kernel<RMSN_F16>, dim3((unsigned)tiles),
+                       dim3(gsc::kThreads), 0, st, p);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    char msg[200];
+    snprintf(msg, sizeof(msg), "gemm_scatter launch failed: %s", hipGetErrorString(e));
+    return rmsn_set_error(RMSN_ERR_HIP, msg);
+  }
+  return RMSN_OK;
+}

@@ -18,6 +18,9 @@ numbers and rounds them to the storage dtype.  Recipe:
   (round to nearest, ties to even).
 
 Tensor ids: partial/x j -> j, residual -> 100, gamma -> 200, special rows -> 300.
+
+GEMM workloads draw A [m, k] (std ``a_std``), B [n, k] (std ``b_std``) and C
+[m, n] (std 1) by the same block recipe, with tensor ids 400, 401 and 402.
 """
 from __future__ import annotations
 
@@ -28,12 +31,13 @@ from typing import Dict, List, Optional, Sequence
 import numpy as np
 import torch
 
-from .workloads import Workload
+from .workloads import GemmWorkload, Workload
 
 BLOCK_ROWS = 16
 RESIDUAL_ID = 100
 GAMMA_ID = 200
 SPECIAL_ID = 300
+GEMM_A_ID, GEMM_B_ID, GEMM_C_ID = 400, 401, 402
 
 TORCH_DTYPE = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16,
                "fp8_e4m3": torch.float8_e4m3fn, "fp8_e5m2": torch.float8_e5m2, "i8": torch.int8}
@@ -181,3 +185,18 @@ def device_tensor(w: Workload, tensor_id: int, device: str) -> torch.Tensor:
                         dtype=torch.float32)
         out[r0:r0 + a.shape[0]].copy_(a.mul_(std))
     return out
+
+
+def matrix(seed: int, tensor_id: int, rows: int, cols: int, std: float, dtype: str,
+           row_idx: Optional[Sequence[int]] = None, device: str = "cpu") -> torch.Tensor:
+    """A seeded [rows, cols] matrix by the block recipe (N(0, std^2))."""
+    w = Workload(f"matrix_{tensor_id}", "matrix", dtype, rows, cols, 0, 0.0, std, seed=seed)
+    return tensor_rows(w, tensor_id, row_idx, device)
+
+
+def gemm_inputs(w: GemmWorkload, device: str = "cpu") -> Dict:
+    """{"a": [m, k], "b": [n, k], "c": [m, n] or None} of a GEMM workload."""
+    return {"a": matrix(w.seed, GEMM_A_ID, w.m, w.k, w.a_std, w.dtype, device=device),
+            "b": matrix(w.seed, GEMM_B_ID, w.n, w.k, w.b_std, w.dtype, device=device),
+            "c": matrix(w.seed, GEMM_C_ID, w.m, w.n, 1.0, w.dtype, device=device)
+            if w.with_c else None}

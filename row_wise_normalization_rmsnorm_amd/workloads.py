@@ -87,3 +87,55 @@ BLOCK_SUM_WORKLOADS = [n for n, w in WORKLOADS.items() if w.op == "block_sum"]
 
 # The headline workload: fused residual add + RMSNorm, bf16, 8192 x 4096.
 HEADLINE = "add_rmsnorm_bf16_8192x4096_k1"
+
+
+# GEMM with a reduce-scatter epilogue (page "LLM System: 通信计算融合算子实现
+# 01 - sm80GEMM + ReduceScatter": the FFN's second GEMM, whose output is
+# reduce-scattered over the tensor-parallel ranks).  One rank's share: tokens
+# m, hidden n, and the rank's slice k of the FFN's intermediate dimension.
+@dataclass(frozen=True)
+class GemmWorkload:
+    name: str
+    dtype: str        # "bf16" or "f16"
+    m: int            # tokens (rows of A and of the output)
+    n: int            # hidden size (rows of the weight B)
+    k: int            # intermediate slice (columns of A and B)
+    world: int        # ranks: the output's rows split into this many chunks
+    rank: int = 0
+    alpha: float = 1.0
+    beta: float = 0.0
+    with_c: bool = False
+    seed: int = 0
+    op = "gemm_scatter"
+
+    @property
+    def a_std(self) -> float:
+        return 1.0
+
+    @property
+    def b_std(self) -> float:
+        """Weights scaled so each rank's partial output is N(0, 1/8), the
+        partials' distribution of the K = 8 fused normalisation."""
+        return (8.0 * self.k) ** -0.5
+
+    def flops(self) -> int:
+        return 2 * self.m * self.n * self.k
+
+    def algorithmic_bytes(self) -> int:
+        """A, B (and C) read once, the output written once."""
+        return 2 * (self.m * self.k + self.n * self.k + self.m * self.n * (2 if self.with_c else 1))
+
+    def describe(self) -> str:
+        return (f"gemm_scatter {self.dtype} m={self.m} n={self.n} k={self.k} world={self.world} "
+                f"rank={self.rank}" + (" +C" if self.with_c else ""))
+
+
+GEMM_WORKLOADS = {
+    # Producer of the K = 8 workload's partials: 4096 tokens, hidden 8192, an
+    # FFN intermediate of 28672 split over 8 ranks (3584 per rank).
+    "gemm_scatter_bf16_4096x8192x3584_w8": GemmWorkload(
+        "gemm_scatter_bf16_4096x8192x3584_w8", "bf16", 4096, 8192, 3584, 8),
+    "gemm_scatter_f16_4096x8192x3584_w8": GemmWorkload(
+        "gemm_scatter_f16_4096x8192x3584_w8", "f16", 4096, 8192, 3584, 8),
+}
+GEMM_HEADLINE = "gemm_scatter_bf16_4096x8192x3584_w8"

@@ -53,7 +53,8 @@ def test_block_sum_error_codes():
 
 def test_oracle_library_exports_every_declared_function():
     import oracle
-    names = declared("rmsnorm_oracle.h") | declared("block_sum_oracle.h")
+    names = declared("rmsnorm_oracle.h") | declared("block_sum_oracle.h") | \
+        declared("gemm_scatter_oracle.h")
     assert {"rmsnorm_oracle", "block_sum_oracle"} <= names
     lib = oracle._load()
     for n in names:

@@ -1,0 +1,116 @@
+"""The GEMM + reduce-scatter epilogue's C ABI without a GPU: the library
+exports what include/gemm_scatter.h declares, invalid arguments are rejected
+with the documented codes before any HIP call, and the tile schedule puts the
+other ranks' chunks first and the local chunk last (the order the oracle
+states), spreads each round of tiles over the eight XCDs in contiguous runs,
+and covers every tile exactly once."""
+from __future__ import annotations
+
+import ctypes
+
+import pytest
+
+import oracle
+from row_wise_normalization_rmsnorm_amd import binding as B
+from tests.test_capi_cpu import FAKE, declared
+
+TM, TN = B.GEMM_SCATTER_TILE_M, B.GEMM_SCATTER_TILE_N
+
+
+def test_exports_every_declared_function():
+    names = declared("gemm_scatter.h")
+    assert names == set(B.GEMM_SCATTER_EXPORTS)
+    for n in names:
+        assert hasattr(B.lib(), n), n
+
+
+def test_tile_count():
+    f = B.lib().gemm_scatter_tiles
+    assert f(4096, 8192) == 16 * 32
+    assert f(1, 1) == 1 and f(0, 5) == 0 and f(257, 256) == 2 and f(256, 257) == 2
+    assert f(-1, 4) == -1 and f(4, 1 << 31) == -1
+
+
+def call(**kw):
+    """gemm_scatter_fwd with valid defaults on fake, well-separated device
+    addresses (every call here must fail validation before any launch)."""
+    world = kw.pop("world", 2)
+    d = kw.pop("dst", None)
+    if d is None:
+        d = [FAKE + (q + 1) * (1 << 28) for q in range(world)]
+    args = dict(ldd=64, rank=0, a=FAKE + (1 << 32), lda=64, b=FAKE + (2 << 32), ldb=64, c=None,
+                ldc=0, alpha=1.0, beta=0.0, m=128, n=64, k=64, dtype=2, flags=None, epoch=1)
+    args.update(kw)
+    arr = (ctypes.c_void_p * max(len(d), 1))(*d)
+    return B.lib().gemm_scatter_fwd(arr, args["ldd"], world, args["rank"], args["a"], args["lda"],
+                                    args["b"], args["ldb"], args["c"], args["ldc"],
+                                    ctypes.c_float(args["alpha"]), ctypes.c_float(args["beta"]),
+                                    args["m"], args["n"], args["k"], args["dtype"], args["flags"],
+                                    ctypes.c_uint32(args["epoch"]), None)
+
+
+def test_error_codes():
+    assert call(dtype=0) == -3 and call(dtype=5) == -3
+    assert call(m=-1) == -2 and call(k=1 << 31) == -2
+    assert call(world=0, dst=[FAKE]) == -2 and call(world=17) == -2
+    assert call(rank=2) == -2 and call(rank=-1) == -2
+    assert call(m=129) == -2                                   # m % world
+    assert call(dst=[FAKE, None]) == -1
+    assert call(a=None) == -1 and call(b=None) == -1
+    assert call(ldd=32) == -2 and call(lda=32) == -2
+    assert call(c=FAKE + (3 << 32), ldc=32) == -2
+    assert call(k=60, lda=64, ldb=64) == -2                     # k % 8
+    assert call(lda=68) == -2                                   # lda % 8
+    assert call(a=FAKE + (1 << 32) + 8) == -2                   # a not 16-byte aligned
+    assert call(dst=[FAKE + 1, FAKE + (1 << 28)]) == -2         # dst misaligned
+    assert call(flags=FAKE + (5 << 32) + 2) == -2               # flags misaligned
+    assert call(lda=1 << 22, k=64) == -2                        # 255 * lda + k too large
+    # overlaps: a dst chunk over a, over another chunk, over flags
+    assert call(dst=[FAKE + (1 << 32), FAKE + (1 << 28)]) == -5
+    assert call(dst=[FAKE + (1 << 28), FAKE + (1 << 28) + 64]) == -5
+    assert call(flags=FAKE + (1 << 28) + 16) == -5
+    assert call(c=FAKE + (2 << 28), ldc=64) == -5
+    # nothing to do: valid, and nothing launched
+    assert call(m=0) == 0 and call(n=0) == 0
+
+
+def tile_chunk(tile: int, m: int, n: int, world: int) -> int:
+    tn = -(-n // TN)
+    return ((tile // tn) * TM) // (m // world)
+
+
+@pytest.mark.parametrize("m,n,world", [(4096, 8192, 8), (4096, 8192, 1), (8192, 4096, 8),
+                                       (1024, 1024, 4), (777 * 8, 300, 8), (256, 256, 2),
+                                       (2048, 2560, 16), (24576, 2048, 8)])
+def test_schedule_is_remote_first_and_complete(m, n, world):
+    tiles = B.gemm_scatter_tiles(m, n)
+    for rank in range(world):
+        wg, pos = B.gemm_scatter_schedule(m, n, world, rank)
+        assert sorted(wg) == list(range(tiles)) and sorted(pos) == list(range(tiles))
+        # chunks (of each tile-row's first row) appear in the oracle's order
+        order = oracle.gemm_scatter_chunk_order(world, rank)
+        rank_of = {q: i for i, q in enumerate(order)}
+        seq = [rank_of[tile_chunk(t, m, n, world)] for t in pos]
+        assert seq == sorted(seq), (m, n, world, rank)
+        # the local chunk's tiles come last
+        local = [i for i, t in enumerate(pos) if tile_chunk(t, m, n, world) == rank]
+        assert not local or local == list(range(tiles - len(local), tiles))
+
+
+def test_workgroups_are_dealt_to_xcds_in_contiguous_runs():
+    m, n, world = 4096, 8192, 8
+    wg, pos = B.gemm_scatter_schedule(m, n, world, 3)
+    at = {t: s for s, t in enumerate(pos)}
+    positions = [at[t] for t in wg]
+    rnd = 8 * 32
+    for base in range(0, len(wg) - len(wg) % rnd, rnd):
+        for x in range(8):
+            ps = [positions[w] for w in range(base + x, base + rnd, 8)]
+            assert ps == list(range(base + 32 * x, base + 32 * x + 32))
+
+
+def test_binding_checks_shapes_before_the_library():
+    import torch
+    a = torch.empty(8, 16, dtype=torch.bfloat16)
+    with pytest.raises(B.RmsnormError):
+        B.gemm_scatter_fwd([a[:4], a[4:]], a, a.to(torch.float16))

@@ -1,0 +1,258 @@
+"""GPU parity of the GEMM with a reduce-scatter epilogue (include/gemm_scatter.h)
+against the CPU oracle.
+
+Bar (floating point, derived from the arithmetic): the GPU accumulates k
+exact products in fp32 on the matrix cores, scales by alpha and adds beta * C
+with one fused multiply-add, then rounds once to the 16-bit type.  Against
+the oracle's exact value y (double) each element satisfies
+
+    |gpu - y| <= (k + 2) * 2^-24 * mag + 2^-p * |y| + 2^-p * tiny
+
+with mag = |alpha| * sum |a b| + |beta c| (from the oracle), p = 8 for bf16
+and 11 for fp16 (half an ulp of the stored value) and tiny the smallest
+normal of the type.  Beyond the bound, most elements must equal the oracle's
+rounded value exactly (they differ only where the fp32 error straddles a
+rounding boundary).  NaN positions and infinities match exactly.  Guard
+bands around every output chunk must stay untouched.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from row_wise_normalization_rmsnorm_amd import binding as B
+from row_wise_normalization_rmsnorm_amd import inputs as I
+from row_wise_normalization_rmsnorm_amd.workloads import GEMM_WORKLOADS, GemmWorkload
+from tests import independent as ind
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+TORCH = {"bf16": torch.bfloat16, "f16": torch.float16}
+P_BITS = {"bf16": 8, "f16": 11}
+TINY = {"bf16": 2.0 ** -126, "f16": 2.0 ** -14}
+GUARD = 0x7E5A  # a NaN pattern in both formats: never a computed value here
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def st(t: torch.Tensor) -> np.ndarray:
+    return I.to_storage(t)
+
+
+def run(a, b, c, alpha, beta, world, rank=0, ldd_pad=0, flags=None, epoch=0):
+    """Launch into guarded chunk buffers; returns (assembled [m, n] storage,
+    the raw buffer).  Each chunk sits inside a [rows + 2, n + ldd_pad + 8]
+    block whose first and last rows and extra columns are guards."""
+    m, n = a.shape[0], b.shape[0]
+    rows = m // world
+    width = n + ldd_pad + 8
+    buf = torch.full((world, rows + 2, width), GUARD, dtype=torch.int16, device=DEV)
+    bufv = buf.view(a.dtype)
+    dst = [bufv[q, 1:rows + 1, 4:4 + n] for q in range(world)]
+    B.gemm_scatter_fwd(dst, a, b, c, alpha, beta, rank, flags, epoch)
+    torch.cuda.synchronize()
+    host = buf.cpu()
+    inner = host[:, 1:rows + 1, 4:4 + n]
+    guard = host.clone()
+    guard[:, 1:rows + 1, 4:4 + n] = GUARD
+    assert bool((guard == GUARD).all()), "a write landed outside the output chunks"
+    return inner.reshape(m, n).numpy().view(np.uint16), host
+
+
+def oracle_rows(a, b, c, alpha, beta, world, dtype, rows=None):
+    ac, bc = st(a.cpu()), st(b.cpu())
+    cc = st(c.cpu()) if c is not None else None
+    chunks, y, mag = oracle.gemm_scatter(ac, bc, cc, alpha, beta, world, dtype, rows=rows,
+                                         want_f64=True)
+    full = np.concatenate(chunks, axis=0)
+    r0, r1 = rows if rows is not None else (0, full.shape[0])
+    return full[r0:r1], y, mag
+
+
+def compare(got: np.ndarray, want: np.ndarray, y: np.ndarray, mag: np.ndarray, k: int,
+            dtype: str, what: str, min_exact: float = 0.8):
+    g = ind.decode_np(got, dtype)
+    nan_y = np.isnan(y)
+    assert np.array_equal(np.isnan(g), nan_y), f"{what}: NaN positions differ"
+    inf_y = np.isinf(y)
+    assert np.array_equal(g[inf_y], y[inf_y]), f"{what}: infinities differ"
+    fin = ~nan_y & ~inf_y
+    bound = (k + 2) * 2.0 ** -24 * mag + 2.0 ** -P_BITS[dtype] * (np.abs(y) + TINY[dtype])
+    with np.errstate(invalid="ignore"):
+        err = np.abs(g - y)
+    bad = fin & ~(err <= bound)
+    if bad.any():
+        i = np.argwhere(bad)[0]
+        raise AssertionError(f"{what}: {int(bad.sum())} elements outside the bound, first at "
+                             f"{tuple(i)}: gpu {g[tuple(i)]!r} exact {y[tuple(i)]!r} "
+                             f"bound {bound[tuple(i)]!r}")
+    exact = float((got[fin] == want[fin]).mean()) if fin.any() else 1.0
+    ratio = float((err[fin] / bound[fin]).max()) if fin.any() else 0.0
+    say(f"[gpu] {what}: error / bound max {ratio:.3g}, equal to the oracle's rounding "
+        f"{100 * exact:.2f}%")
+    assert exact >= min_exact, f"{what}: only {exact:.3f} of elements equal the oracle's"
+
+
+def make(dtype, m, n, k, with_c, seed, lda_pad=0, ldb_pad=0, ldc_pad=0):
+    """Seeded operands (A ~ N(0,1), B ~ N(0, 1/(8k)), C ~ N(0,1)), optionally
+    as views into wider buffers (row strides k + pad)."""
+    w = GemmWorkload("case", dtype, m, n, k, 1, seed=seed)
+
+    def padded(t, pad):
+        if not pad:
+            return t.to(DEV)
+        big = torch.zeros(t.shape[0], t.shape[1] + pad, dtype=t.dtype, device=DEV)
+        big[:, :t.shape[1]] = t.to(DEV)
+        return big[:, :t.shape[1]]
+
+    a = I.matrix(seed, I.GEMM_A_ID, m, k, w.a_std, dtype) if k else torch.zeros(m, 0, dtype=TORCH[dtype])
+    b = I.matrix(seed, I.GEMM_B_ID, n, k, w.b_std if k else 1.0, dtype) if k else torch.zeros(n, 0, dtype=TORCH[dtype])
+    c = I.matrix(seed, I.GEMM_C_ID, m, n, 1.0, dtype) if with_c else None
+    return padded(a, lda_pad), padded(b, ldb_pad), (padded(c, ldc_pad) if c is not None else None)
+
+
+SHAPES = [  # m, n, k, world, with_c
+    (512, 768, 256, 8, False),
+    (776, 300, 136, 8, True),      # ragged m, n and k; chunks of 97 rows
+    (256, 256, 64, 1, False),      # one tile
+    (8, 40, 8, 2, True),           # far below one tile
+    (64, 1000, 72, 2, False),
+    (1024, 512, 1024, 4, True),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("shape", SHAPES, ids=[f"{s[0]}x{s[1]}x{s[2]}w{s[3]}{'c' if s[4] else ''}"
+                                               for s in SHAPES])
+def test_parity(dtype, shape):
+    m, n, k, world, with_c = shape
+    say(f"[gpu] gemm_scatter {dtype} m={m} n={n} k={k} world={world} c={with_c}")
+    a, b, c = make(dtype, m, n, k, with_c, seed=m + n + k)
+    alpha, beta = (0.5, -1.25) if with_c else (1.0, 0.0)
+    got, _ = run(a, b, c, alpha, beta, world, rank=world - 1)
+    want, y, mag = oracle_rows(a, b, c, alpha, beta, world, dtype)
+    compare(got, want, y, mag, k, dtype, f"{dtype} {shape}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_strided_operands(dtype):
+    """Row strides wider than the rows for A, B, C and the output (one odd,
+    which takes the element-wise store path)."""
+    m, n, k, world = 384, 264, 200, 4
+    for ldd_pad, ldc_pad in ((8, 3), (3, 8)):
+        say(f"[gpu] strided {dtype} ldd_pad={ldd_pad} ldc_pad={ldc_pad}")
+        a, b, c = make(dtype, m, n, k, True, seed=7, lda_pad=8, ldb_pad=24, ldc_pad=ldc_pad)
+        got, _ = run(a, b, c, 1.5, 0.75, world, rank=1, ldd_pad=ldd_pad)
+        want, y, mag = oracle_rows(a, b, c, 1.5, 0.75, world, "bf16" if dtype == "bf16" else "f16")
+        compare(got, want, y, mag, k, dtype, f"strided {dtype} {ldd_pad}/{ldc_pad}")
+
+
+def test_k_zero_gives_beta_c():
+    a, b, c = make("bf16", 300, 200, 0, True, seed=3)
+    say("[gpu] k = 0")
+    got, _ = run(a.contiguous(), b.contiguous(), c, 1.0, -2.0, 4)
+    want, y, mag = oracle_rows(a, b, c, 1.0, -2.0, 4, "bf16")
+    compare(got, want, y, mag, 0, "bf16", "k = 0", min_exact=1.0)
+
+
+def test_flags_epoch_and_rank_independence():
+    """Every tile's flag gets the epoch (slots past the tiles stay as they
+    were), and the values do not depend on the rank (only the order of the
+    tiles does)."""
+    m, n, k, world = 1024, 768, 192, 8
+    a, b, c = make("bf16", m, n, k, False, seed=11)
+    tiles = B.gemm_scatter_tiles(m, n)
+    flags = torch.full((tiles + 5,), 3, dtype=torch.int32, device=DEV)
+    say("[gpu] flags")
+    ref, _ = run(a, b, None, 1.0, 0.0, world, rank=0, flags=flags, epoch=41)
+    f = flags.cpu()
+    assert bool((f[:tiles] == 41).all()) and bool((f[tiles:] == 3).all())
+    for rank in (3, 7):
+        got, _ = run(a, b, None, 1.0, 0.0, world, rank=rank, flags=flags, epoch=42 + rank)
+        assert np.array_equal(got, ref), rank
+        assert bool((flags.cpu()[:tiles] == 42 + rank).all())
+
+
+@pytest.mark.parametrize("name", list(GEMM_WORKLOADS))
+def test_full_size_sampled(name):
+    """The benchmark's workload at full size, in the benchmark's launch:
+    sampled rows of every chunk against the oracle, and a second launch
+    bitwise equal to the first."""
+    w = GEMM_WORKLOADS[name]
+    say(f"[gpu] full size {w.describe()}")
+    d = I.gemm_inputs(w)
+    a, b = d["a"].to(DEV), d["b"].to(DEV)
+    c = d["c"].to(DEV) if d["c"] is not None else None
+    got, _ = run(a, b, c, w.alpha, w.beta, w.world, rank=w.rank)
+    again, _ = run(a, b, c, w.alpha, w.beta, w.world, rank=w.rank)
+    assert np.array_equal(got, again), "two launches differ"
+    chunk = w.m // w.world
+    rows = sorted({q * chunk + off for q in range(w.world) for off in (0, chunk // 2 + 3)}
+                  | {w.m - 1, 255, 256})
+    ac, bc = st(d["a"]), st(d["b"])
+    for r in rows:
+        chunks, y, mag = oracle.gemm_scatter(ac, bc, None, w.alpha, w.beta, w.world, w.dtype,
+                                             rows=(r, r + 1), want_f64=True)
+        q = r // chunk
+        want = chunks[q][r - q * chunk:r - q * chunk + 1]
+        compare(got[r:r + 1], want, y, mag, w.k, w.dtype, f"{name} row {r}", min_exact=0.7)
+
+
+def test_special_values():
+    """inf in A, NaN in C, and a zero weight row: IEEE results as the oracle
+    gives them."""
+    m, n, k, world = 256, 64, 64, 2
+    a, b, c = make("bf16", m, n, k, True, seed=5)
+    a, b, c = a.clone(), b.clone(), c.clone()
+    a[3, 10] = float("inf")
+    a[7, :] = 0.0
+    b[5, :] = 0.0                 # inf * 0 -> NaN in row 3, column 5
+    c[9, 11] = float("nan")
+    say("[gpu] special values")
+    got, _ = run(a, b, c, 1.0, 1.0, world)
+    want, y, mag = oracle_rows(a, b, c, 1.0, 1.0, world, "bf16")
+    assert np.isnan(y[3, 5]) and np.isinf(y[3, 0]) and np.isnan(y[9, 11])
+    compare(got, want, y, mag, k, "bf16", "special values")
+
+
+def test_reduce_scatter_then_add_rmsnorm():
+    """Eight ranks emulated on one GPU: rank r multiplies its own A_r, B_r and
+    scatters chunk q into rank q's receive buffer (slot r); rank q then sums
+    its eight received chunks with its residual and normalises
+    (add_rmsnorm_fwd, K = 8).  The received chunks match the oracle's GEMM,
+    and rank q's new residual is bit-exact against the oracle's fused
+    normalisation of the same received chunks."""
+    world, m, n, k = 8, 512, 1024, 256
+    chunk = m // world
+    recv = torch.empty(world, world, chunk, n, dtype=torch.bfloat16, device=DEV)  # [q][r]
+    ops = []
+    for r in range(world):
+        a, b, _ = make("bf16", m, n, k, False, seed=100 + r)
+        ops.append((a, b))
+        B.gemm_scatter_fwd([recv[q, r] for q in range(world)], a, b, None, 1.0, 0.0, rank=r)
+    torch.cuda.synchronize()
+    say("[gpu] reduce-scatter emulation: 8 GEMMs done")
+    for r in (0, 5):
+        a, b = ops[r]
+        full = torch.cat([recv[q, r] for q in range(world)]).cpu()
+        want, y, mag = oracle_rows(a, b, None, 1.0, 0.0, world, "bf16")
+        compare(st(full), want, y, mag, k, "bf16", f"rank {r} partial")
+    q = 6
+    res = I.matrix(9, I.RESIDUAL_ID, chunk, n, 1.0, "bf16").to(DEV)
+    gam = I.matrix(9, I.GAMMA_ID, 1, n, 0.25, "bf16").reshape(n).to(DEV) + 1.0
+    parts = [recv[q, r].contiguous() for r in range(world)]
+    res_in = res.clone()
+    out = torch.empty(chunk, n, dtype=torch.bfloat16, device=DEV)
+    B.add_rmsnorm_fwd(out, res, parts, gam, 1e-5)
+    torch.cuda.synchronize()
+    o_out, o_res, _ = oracle.add_rmsnorm([st(p.cpu()) for p in parts], st(res_in.cpu()),
+                                         st(gam.cpu()), 1e-5, "bf16")
+    assert np.array_equal(st(res.cpu()), o_res), "new residual differs from the oracle"
+    d = ind.ulp_distance(st(out.cpu()), o_out, "bf16")
+    assert int(d.max()) <= 2
