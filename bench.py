@@ -3,7 +3,9 @@
 One step = one ``add_rmsnorm_fwd`` launch over the whole workload (every step
 of the path: load K partials and the residual, sum, write the residual, sum of
 squares, reduce, scale, normalise, store); ``--workload`` selects another
-workload (plain RMSNorm, or the block all-reduce sum).  Inputs are seeded synthetic data
+workload (plain RMSNorm, the block all-reduce sum, or the GEMM with a
+reduce-scatter epilogue, which reports TFLOP/s against the matrix-core
+peak).  Inputs are seeded synthetic data
 resident in HBM before timing starts.  Several copies of the buffers are
 rotated so that consecutive steps never find their inputs in the 256 MB
 Infinity Cache.  Timing: W untimed warm-up steps, then exactly K steps
@@ -38,6 +40,7 @@ sys.path.insert(0, ROOT)
 from row_wise_normalization_rmsnorm_amd.profiling import source_hash  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published peak
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0}  # MI355X dense matrix-core peaks
 
 
 def traffic_for(kernel: str, workload: str, op: str):
@@ -125,6 +128,166 @@ def cpu_baseline(w, target_cpu_seconds: float = 12.0, max_passes: int = 40) -> d
                               "cores": 1,
                               "sample": f"{blocks} row blocks of {w.rows // cores} rows, "
                                         "one thread"}}
+
+
+def gemm_cpu_baseline(w, target_cpu_seconds: float = 12.0) -> dict:
+    """The GEMM oracle, unchanged, on a sample of whole output rows spread
+    over the m rows, one row per task over the host's cores, sized to about
+    ``target_cpu_seconds`` of CPU work; then a few rows on one thread."""
+    import oracle
+    from row_wise_normalization_rmsnorm_amd import inputs as I
+
+    d = I.gemm_inputs(w)
+    ac, bc = I.to_storage(d["a"]), I.to_storage(d["b"])
+    cc = I.to_storage(d["c"]) if d["c"] is not None else None
+
+    def job(r):
+        return oracle.gemm_scatter(ac, bc, cc, w.alpha, w.beta, w.world, w.dtype,
+                                   rows=(r, r + 1), scatter=False)
+
+    oracle._load()
+    t0 = time.perf_counter()
+    job(0)
+    per_row = time.perf_counter() - t0
+    cores = host_cores()
+    nrows = max(cores, min(w.m, int(target_cpu_seconds / max(per_row, 1e-6)) // cores * cores))
+    rows = [int(i * w.m // nrows) for i in range(nrows)]
+    c0 = time.process_time()
+    t0 = time.perf_counter()
+    with cf.ThreadPoolExecutor(cores) as ex:
+        list(ex.map(job, rows))
+    dt = time.perf_counter() - t0
+    cpu = time.process_time() - c0
+    row_flops = 2 * w.n * w.k
+    single_rows = max(1, min(8, int(4.0 / max(per_row, 1e-6))))
+    t1 = time.perf_counter()
+    for r in rows[:single_rows]:
+        job(r)
+    single = (time.perf_counter() - t1) / single_rows
+    return {"value": round(nrows * row_flops / dt / 1e12, 6), "unit": "TFLOP/s",
+            "cores": cores, "kind": "oracle",
+            "seconds_for_full_workload": round(dt * w.m / nrows, 1),
+            "sample": (f"{nrows} of the {w.m} output rows of {w.name} (evenly spaced, every "
+                       f"chunk), one row per task over {cores} threads ({cpu:.1f} CPU-seconds)"),
+            "single_thread": {"value": round(row_flops / single / 1e12, 6), "unit": "TFLOP/s",
+                              "cores": 1, "sample": f"{single_rows} rows, one thread"}}
+
+
+def gemm_bench(a, name: str) -> int:
+    """One step = one gemm_scatter_fwd launch over the whole workload."""
+    import torch
+    from row_wise_normalization_rmsnorm_amd import binding as B
+    from row_wise_normalization_rmsnorm_amd import inputs as I
+    from row_wise_normalization_rmsnorm_amd.workloads import GEMM_WORKLOADS
+
+    w = GEMM_WORKLOADS[name]
+    dev = "cuda:0"
+    B.lib()
+    print(f"[bench] {w.describe()}: generating inputs", file=sys.stderr, flush=True)
+    d = I.gemm_inputs(w)
+    nsets = max(1, int(-(-a.rotate_bytes * (1 << 30) // w.algorithmic_bytes())))
+    sets = []
+    for _ in range(nsets):
+        s = {"a": d["a"].to(dev), "b": d["b"].to(dev),
+             "c": d["c"].to(dev) if d["c"] is not None else None}
+        s["dst"] = [torch.empty(w.m // w.world, w.n, dtype=s["a"].dtype, device=dev)
+                    for _ in range(w.world)]
+        sets.append(s)
+    kernel = f"gemm_scatter<{w.dtype},256x256x64,mfma16x16x32>"
+
+    def step(i):
+        s = sets[i % nsets]
+        B.gemm_scatter_fwd(s["dst"], s["a"], s["b"], s["c"], w.alpha, w.beta, w.rank)
+
+    for i in range(a.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(a.steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / a.steps
+    tflops = w.flops() / (ms * 1e-3) / 1e12
+    peak = MFMA_PEAK_TFLOPS[w.dtype]
+    print(f"[bench] {kernel}: {ms * 1e3:.2f} us/launch, {tflops:.1f} TFLOP/s "
+          f"({100 * tflops / peak:.1f}% of peak), {nsets} rotating sets, wall {wall:.2f}s",
+          file=sys.stderr, flush=True)
+    lat = {"batched": latency(step, min(a.steps, 200))}
+
+    def timed(fn, n):
+        for i in range(5):
+            fn(i)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(n):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    # context: the same kernel on one set of operands (they stay in the
+    # 256 MB Infinity Cache), and the vendor library's GEMM (torch.matmul ->
+    # hipBLASLt, plain output) on the same operands, rotated and not
+    nctx = max(10, min(a.steps, 100))
+    hot_ms = timed(lambda i: B.gemm_scatter_fwd(sets[0]["dst"], sets[0]["a"], sets[0]["b"],
+                                                sets[0]["c"], w.alpha, w.beta, w.rank), nctx)
+    lib_ms = timed(lambda i: torch.matmul(sets[i % nsets]["a"], sets[i % nsets]["b"].t()), nctx)
+    lib_hot_ms = timed(lambda i: torch.matmul(sets[0]["a"], sets[0]["b"].t()), nctx)
+
+    def tf(x):
+        return round(w.flops() / (x * 1e-3) / 1e12, 1)
+
+    print(f"[bench] one operand set (cache-resident): {hot_ms * 1e3:.2f} us, {tf(hot_ms)} TFLOP/s; "
+          f"torch.matmul (hipBLASLt) rotated {lib_ms * 1e3:.2f} us ({tf(lib_ms)} TFLOP/s), "
+          f"one set {lib_hot_ms * 1e3:.2f} us ({tf(lib_hot_ms)} TFLOP/s)", file=sys.stderr,
+          flush=True)
+
+    result = {
+        "metric": f"achieved TFLOP/s (% of dense {w.dtype} matrix-core peak), {w.describe()}",
+        "value": round(tflops, 1),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "accumulate_dtype": "f32",
+        "data": "synthetic (seeded N(0,1) activations, N(0,1/(8k)) weights, resident in HBM)",
+        "config": {"workload": w.name, "op": w.op, "m": w.m, "n": w.n, "k": w.k,
+                   "world": w.world, "rank": w.rank, "kernel": kernel, "rotating_sets": nsets,
+                   "flops_per_step": w.flops(),
+                   "algorithmic_bytes_per_step": w.algorithmic_bytes()},
+        "pct_of_peak": round(100 * tflops / peak, 2),
+        "per_launch": lat,
+        "one_operand_set": {"what": "the same kernel on one set of operands, which stay in "
+                                    "the Infinity Cache", "us": round(hot_ms * 1e3, 2),
+                            "tflops": tf(hot_ms)},
+        "library_context": {"what": "torch.matmul(a, b.t()) (hipBLASLt), same operands, "
+                                    "plain output",
+                            "rotated": {"us": round(lib_ms * 1e3, 2), "tflops": tf(lib_ms)},
+                            "one_operand_set": {"us": round(lib_hot_ms * 1e3, 2),
+                                                "tflops": tf(lib_hot_ms)},
+                            "kernel_over_library": round(tflops / tf(lib_ms), 4),
+                            "kernel_over_library_one_set": round(tf(hot_ms) / tf(lib_hot_ms), 4)},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
+                     "traffic": traffic_for(kernel, w.name, w.op)},
+    }
+    if not a.no_cpu_baseline:
+        del sets
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = gemm_cpu_baseline(w)
+    print(json.dumps(result), flush=True)
+    return 0
 
 
 def stream_ceiling(w, dev: str = "cuda:0", steps: int = 60, rotate_gib: float = 1.0,
@@ -441,6 +604,9 @@ def main() -> int:
     if a.ceiling_sweep:
         return ceiling_sweep()
 
+    from row_wise_normalization_rmsnorm_amd.workloads import GEMM_WORKLOADS
+    if a.workload in GEMM_WORKLOADS:
+        return gemm_bench(a, a.workload)
     w = WORKLOADS[a.workload or HEADLINE]
     if a.rows:  # the same workload with another row count (footprint studies)
         import dataclasses

@@ -83,10 +83,14 @@ int64_t gemm_scatter_tiles(int64_t m, int64_t n);
 /*
  * gemm_scatter_schedule -- the tile schedule of one launch (host only, no
  * GPU needed).  For workgroup w (launch order), wg_tile[w] is the tile it
- * computes; pos_tile[s] is the tile at position s of the schedule (the
- * remote-first chunk order, before workgroups are spread over the GPU's
- * eight XCDs).  Either array may be NULL; each holds `len` >=
- * gemm_scatter_tiles(m, n) entries.  Returns RMSN_OK or RMSN_ERR_SHAPE.
+ * computes; pos_tile[s] is the tile at position s of the schedule, before
+ * workgroups are spread over the GPU's eight XCDs.  A tile-row belongs to
+ * the chunk of its first row.  The schedule runs the other ranks' chunks
+ * first, in ring order from rank + 1, in groups of up to eight tile-rows
+ * (a group may hold several chunks), then the local chunk's tile-rows;
+ * within a group the tiles go column-major.  Either array may be NULL; each
+ * holds `len` >= gemm_scatter_tiles(m, n) entries.  Returns RMSN_OK or
+ * RMSN_ERR_SHAPE.
  */
 int gemm_scatter_schedule(int64_t m, int64_t n, int world, int rank, int32_t* wg_tile,
                           int32_t* pos_tile, int64_t len);

@@ -287,7 +287,7 @@ def block_sum_decode(x: np.ndarray, dtype: str, lib: "Library | None" = None) ->
 # ---- GEMM with a reduce-scatter epilogue ------------------------------------
 
 def gemm_scatter(a: np.ndarray, b: np.ndarray, c, alpha: float, beta: float, world: int,
-                 dtype: str, rows=None, want_f64: bool = False,
+                 dtype: str, rows=None, want_f64: bool = False, scatter: bool = True,
                  lib: "Library | None" = None):
     """``alpha * a @ b.T + beta * c`` split into ``world`` row chunks.
 
@@ -298,6 +298,9 @@ def gemm_scatter(a: np.ndarray, b: np.ndarray, c, alpha: float, beta: float, wor
     n] uint16; for a row range only the rows inside it are filled, the others
     are zero) and, with ``want_f64``, (y, mag) for the computed rows: the
     unrounded values and the magnitude scale of their rounding error bound.
+    With ``scatter=False`` nothing is scattered: the first item is instead
+    the computed rows ([row1 - row0, n] uint16), rounded by the oracle's
+    converter.
     """
     m, k = a.shape
     n = b.shape[0]
@@ -309,9 +312,9 @@ def gemm_scatter(a: np.ndarray, b: np.ndarray, c, alpha: float, beta: float, wor
     if world < 1 or m % world:
         raise ValueError("m must split into world equal chunks")
     r0, r1 = rows if rows is not None else (0, m)
-    chunks = [np.zeros((m // world, n), np.uint16) for _ in range(world)]
-    ptrs = (ctypes.c_void_p * world)(*[ch.ctypes.data for ch in chunks])
-    y = np.empty((r1 - r0, n), np.float64) if want_f64 else None
+    chunks = [np.zeros((m // world, n), np.uint16) for _ in range(world)] if scatter else None
+    ptrs = (ctypes.c_void_p * world)(*[ch.ctypes.data for ch in chunks]) if scatter else None
+    y = np.empty((r1 - r0, n), np.float64) if (want_f64 or not scatter) else None
     mag = np.empty((r1 - r0, n), np.float64) if want_f64 else None
     rc = _load(lib).gemm_scatter_oracle(
         ptrs, n, world, _ptr(a), _ld(a), _ptr(b), _ld(b),
@@ -319,7 +322,8 @@ def gemm_scatter(a: np.ndarray, b: np.ndarray, c, alpha: float, beta: float, wor
         ctypes.c_float(alpha), ctypes.c_float(beta), m, n, k, DTYPE_CODE[dtype], r0, r1,
         _dptr(y), _dptr(mag))
     _raise(rc)
-    return (chunks, y, mag) if want_f64 else chunks
+    first = chunks if scatter else round_to(y, dtype, lib=lib)
+    return (first, y, mag) if want_f64 else first
 
 
 def _ld(arr: np.ndarray) -> int:

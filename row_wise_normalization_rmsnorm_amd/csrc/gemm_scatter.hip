@@ -20,16 +20,22 @@
 //   - A and B tiles pass through LDS, double-buffered (2 x 64 KiB of the
 //     CU's 160 KiB): each thread loads 16-byte chunks of the next k step
 //     into registers while the waves multiply the current one, then writes
-//     them to the other buffer; one barrier per k step.
+//     them to the other buffer; one barrier per k step.  (Loading straight
+//     into LDS with gfx950's buffer-load-to-LDS form measured slower, 225 vs
+//     203 us, the compiler then shuffling accumulators between register
+//     files inside the loop.)
 //   - LDS rows are 128 bytes (64 elements); the 16-byte chunk c of row r is
 //     stored at chunk position c ^ (r & 7), so the eight lanes of each LDS
 //     access phase, which read the same chunk of eight consecutive rows, hit
 //     eight different bank groups.
 //   - Tile order: tile-rows rotated so that the chunks after the local
-//     rank's come first and the local chunk last, grouped a few tile-rows at
-//     a time (column-major within a group) for cache reuse; consecutive
-//     workgroups land on different XCDs (round-robin dispatch), so each
-//     round of positions is dealt out in contiguous runs per XCD.
+//     rank's come first, in ring order, and the local chunk's last; each
+//     part in groups of up to eight tile-rows, column-major within a group,
+//     for cache reuse.  Consecutive workgroups land on different XCDs
+//     (round-robin dispatch), so each round of 256 positions is dealt out in
+//     runs of 32 per XCD: an 8 x 4 block of tiles shares its operand rows in
+//     the XCD's L2 (measured 1214 -> 1241 TFLOP/s against groups of two
+//     tile-rows on the 4096 x 8192 x 3584 bf16 product).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdio.h>
@@ -48,7 +54,7 @@ constexpr int kThreads = 256;          // four waves
 constexpr int kChunksPerRow = BK / 8;  // 16-byte chunks per LDS row
 constexpr int kXcds = 8;
 constexpr int kRoundPerXcd = 32;       // positions each XCD takes per round (one per CU)
-constexpr int kGroupM = 2;             // tile-rows per schedule group
+constexpr int kGroupM = 8;             // tile-rows per schedule group
 // Buffer resource word 3 for gfx9-family raw (untyped) buffer access; the
 // offset used for a chunk outside every operand's range.
 constexpr int kRsrcWord3 = 0x00020000;
@@ -99,8 +105,9 @@ struct Elem<RMSN_F16> {
 
 struct Sched {
   int tiles_m, tiles_n, tiles;
-  int tm_start;  // first tile-row of the rotated order
-  int group_m;   // tile-rows per schedule group (never straddling two chunks)
+  int tm_start;      // first tile-row of the rotated order
+  int remote_rows;   // rotated tile-rows before the local chunk's
+  int local_group;   // tile-rows per group among the local chunk's
 };
 
 __host__ __device__ inline Sched make_sched(int m, int n, int world, int rank) {
@@ -108,24 +115,17 @@ __host__ __device__ inline Sched make_sched(int m, int n, int world, int rank) {
   s.tiles_m = (m + BM - 1) / BM;
   s.tiles_n = (n + BN - 1) / BN;
   s.tiles = s.tiles_m * s.tiles_n;
-  // the first tile-row whose first row lies in chunk rank + 1 or later
+  // A tile-row belongs to the chunk of its first row.  Rotated order starts
+  // at the first tile-row of chunk rank + 1 (ring order), so the tile-rows
+  // of the local chunk (rank) come last.
   const int64_t chunk_rows = world > 0 ? (int64_t)m / world : m;
-  const int64_t first_row = (int64_t)(rank + 1) * chunk_rows;
-  int64_t tm = (first_row + BM - 1) / BM;
-  if (tm >= s.tiles_m) tm = 0;
-  s.tm_start = (int)tm;
-  // Chunks that are whole tile-rows (r of them each) take groups of the
-  // largest divisor of r up to kGroupM, so no group mixes two chunks; other
-  // chunk sizes take one tile-row per group.
-  s.group_m = 1;
-  if (chunk_rows > 0 && chunk_rows % BM == 0) {
-    const int64_t r = chunk_rows / BM;
-    for (int g = kGroupM; g > 1; --g)
-      if (r % g == 0) {
-        s.group_m = g;
-        break;
-      }
-  }
+  const int64_t first_local = ((int64_t)rank * chunk_rows + BM - 1) / BM;
+  int64_t end_local = ((int64_t)(rank + 1) * chunk_rows + BM - 1) / BM;
+  if (end_local > s.tiles_m) end_local = s.tiles_m;
+  const int64_t local = end_local > first_local ? end_local - first_local : 0;
+  s.tm_start = (int)(end_local >= s.tiles_m ? 0 : end_local);
+  s.remote_rows = s.tiles_m - (int)local;
+  s.local_group = local < kGroupM ? (local > 0 ? (int)local : 1) : kGroupM;
   return s;
 }
 
@@ -142,15 +142,30 @@ __host__ __device__ inline int position_of_wg(int w, int tiles) {
   return base + (within % kXcds) * kRoundPerXcd + within / kXcds;
 }
 
-// schedule position -> tile: groups of group_m rotated tile-rows,
-// column-major inside a group.
+// schedule position -> tile.  The rotated tile-rows of the other ranks'
+// chunks come first, in groups of kGroupM tile-rows, then the local chunk's
+// tile-rows in groups of local_group; inside a group the tiles go
+// column-major (down the group's tile-rows, then to the next tile-column),
+// so a run of positions covers a compact block of the output.
 __host__ __device__ inline int tile_at(int p, const Sched& s) {
-  const int group = s.group_m * s.tiles_n;
+  const int remote_tiles = s.remote_rows * s.tiles_n;
+  int first_row, region_rows, gsize;
+  if (p < remote_tiles) {
+    first_row = 0;
+    region_rows = s.remote_rows;
+    gsize = kGroupM;
+  } else {
+    p -= remote_tiles;
+    first_row = s.remote_rows;
+    region_rows = s.tiles_m - s.remote_rows;
+    gsize = s.local_group;
+  }
+  const int group = gsize * s.tiles_n;
   const int g = p / group;
   const int idx = p - g * group;
-  const int first = g * s.group_m;
-  const int rows = s.tiles_m - first < s.group_m ? s.tiles_m - first : s.group_m;
-  const int ptm = first + idx % rows;
+  const int gfirst = g * gsize;
+  const int rows = region_rows - gfirst < gsize ? region_rows - gfirst : gsize;
+  const int ptm = first_row + gfirst + idx % rows;
   const int tn = idx / rows;
   const int tm = (ptm + s.tm_start) % s.tiles_m;
   return tm * s.tiles_n + tn;

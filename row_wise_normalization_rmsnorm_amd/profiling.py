@@ -36,14 +36,15 @@ COPY_BYTES = 1 << 30
 
 
 def kernel_sources(op: str) -> list:
-    """The source that fixes a workload's kernel code: the block sum's own
-    file, or the RMSNorm kernels' template header.  Which variant runs is
+    """The source that fixes a workload's kernel code: the block sum's or the
+    GEMM's own file, or the RMSNorm kernels' template header.  Which variant runs is
     checked by its name instead, which spells out every template parameter,
     so adding other variants or changing the host dispatcher leaves a
     measured figure valid."""
     pkg = os.path.join(ROOT, "row_wise_normalization_rmsnorm_amd")
-    return [os.path.join(pkg, "csrc", "block_sum.hip" if op == "block_sum" else
-                         "rmsnorm_kernels.hpp")]
+    src = {"block_sum": "block_sum.hip", "gemm_scatter": "gemm_scatter.hip"}.get(
+        op, "rmsnorm_kernels.hpp")
+    return [os.path.join(pkg, "csrc", src)]
 
 
 def source_hash(op: str) -> str:
@@ -313,8 +314,9 @@ def main() -> int:
 
     import sys
     sys.path.insert(0, ROOT)
-    from row_wise_normalization_rmsnorm_amd.workloads import WORKLOADS
-    w = WORKLOADS[a.workload]
+    from row_wise_normalization_rmsnorm_amd.workloads import GEMM_WORKLOADS, WORKLOADS
+    w = WORKLOADS[a.workload] if a.workload in WORKLOADS else GEMM_WORKLOADS[a.workload]
+    gemm = w.op == "gemm_scatter"
     nbytes = w.algorithmic_bytes()
 
     stats = kernel_stats(a.trace)
@@ -344,6 +346,7 @@ def main() -> int:
     with open(md, "w") as f:
         f.write(f"# {a.plan} on {w.name}\n\n")
         what = ("each element read once, the 4-byte sum written once" if w.op == "block_sum"
+                else "A, B read once, the output written once" if gemm
                 else "each tensor element read or written once, gamma once")
         f.write(f"Workload: {w.describe()}; algorithmic bytes per launch {nbytes:,} "
                 f"({what}).\n\n")
@@ -354,8 +357,14 @@ def main() -> int:
         for s in stats[:4]:
             f.write(f"| {s['name'][:90]} | {s['calls']} | {s['avg_ns'] / 1e3:.2f} | "
                     f"{s['min_ns'] / 1e3:.2f} | {s['max_ns'] / 1e3:.2f} | {s['pct']:.1f} |\n")
-        f.write(f"\nAchieved (algorithmic bytes / average duration): **{achieved:.0f} GB/s**, "
-                f"{100 * achieved / 8000:.1f}% of the 8 TB/s HBM peak.\n")
+        if gemm:
+            tflops = w.flops() / (k["avg_ns"] * 1e-9) / 1e12
+            f.write(f"\nAchieved ({w.flops():,} flop / average duration): **{tflops:.1f} "
+                    f"TFLOP/s**, {100 * tflops / 2500:.1f}% of the 2.5 PFLOP/s dense "
+                    f"{w.dtype} matrix-core peak; {achieved:.0f} GB/s of algorithmic bytes.\n")
+        else:
+            f.write(f"\nAchieved (algorithmic bytes / average duration): **{achieved:.0f} GB/s**, "
+                    f"{100 * achieved / 8000:.1f}% of the 8 TB/s HBM peak.\n")
         gaps = launch_gaps(a.trace, a.symbol)
         if gaps:
             f.write(f"Back-to-back launches in the trace: median duration {gaps[0] / 1e3:.2f} us, "
@@ -365,7 +374,7 @@ def main() -> int:
         if event:
             f.write(f"bench.py (HIP events over the timed region, same command without the "
                     f"profiler): {event['ms_per_step'] * 1e3:.2f} us per launch, "
-                    f"{event['value']:.0f} GB/s.\n")
+                    f"{event['value']:.{1 if gemm else 0}f} {event['unit']}.\n")
         f.write("\n## HBM bytes (rocprofv3 --pmc, one counter per run)\n\n")
         f.write("Commands: `rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -o run -- python "
                 f"bench.py --workload {w.name} --steps 10 --warmup 2 --no-cpu-baseline`, the same "
@@ -378,7 +387,9 @@ def main() -> int:
         f.write(f"| WRITE_SIZE | {write_kib:,.1f} | {nw} | {cw_kib:,.1f} | {wscale:.4f} | "
                 f"{write_b:,.0f} |\n")
         f.write(f"\nHBM traffic per launch {traffic:,.0f} B = {traffic / nbytes:.4f} x the "
-                "algorithmic bytes.\n")
+                "algorithmic bytes" + (" (operand tiles fetched again by other workgroups "
+                                       "once evicted from the L2 / Infinity Cache)" if gemm
+                                       else "") + ".\n")
         f.write(f"\nKernel sources sha256: `{source_hash(w.op)}`\n")
     tj = os.path.join(PROFILES, f"traffic_{w.name}.json")
     json.dump({"workload": w.name, "kernel": a.plan, "traffic_bytes_per_launch": round(traffic),

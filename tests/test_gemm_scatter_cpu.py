@@ -79,22 +79,36 @@ def tile_chunk(tile: int, m: int, n: int, world: int) -> int:
     return ((tile // tn) * TM) // (m // world)
 
 
+GROUP_ROWS = 8  # tile-rows per schedule group
+
+
 @pytest.mark.parametrize("m,n,world", [(4096, 8192, 8), (4096, 8192, 1), (8192, 4096, 8),
                                        (1024, 1024, 4), (777 * 8, 300, 8), (256, 256, 2),
-                                       (2048, 2560, 16), (24576, 2048, 8)])
+                                       (2048, 2560, 16), (24576, 2048, 8), (4096, 8192, 2)])
 def test_schedule_is_remote_first_and_complete(m, n, world):
     tiles = B.gemm_scatter_tiles(m, n)
+    tn = -(-n // TN)
     for rank in range(world):
         wg, pos = B.gemm_scatter_schedule(m, n, world, rank)
         assert sorted(wg) == list(range(tiles)) and sorted(pos) == list(range(tiles))
-        # chunks (of each tile-row's first row) appear in the oracle's order
         order = oracle.gemm_scatter_chunk_order(world, rank)
         rank_of = {q: i for i, q in enumerate(order)}
         seq = [rank_of[tile_chunk(t, m, n, world)] for t in pos]
-        assert seq == sorted(seq), (m, n, world, rank)
         # the local chunk's tiles come last
-        local = [i for i, t in enumerate(pos) if tile_chunk(t, m, n, world) == rank]
-        assert not local or local == list(range(tiles - len(local), tiles))
+        local = [i for i, q in enumerate(seq) if q == world - 1]
+        assert not local or local == list(range(tiles - len(local), tiles)), (m, n, world, rank)
+        # the other chunks in ring order, group by group (a group of up to
+        # eight tile-rows may hold several chunks, never out of order)
+        remote = seq[:tiles - len(local)]
+        step = GROUP_ROWS * tn
+        blocks = [remote[i:i + step] for i in range(0, len(remote), step)]
+        for x, y in zip(blocks, blocks[1:]):
+            assert max(x) <= min(y), (m, n, world, rank)
+        # inside a group, tiles go down the group's tile-rows first
+        for i in range(0, len(remote), step):
+            block = pos[i:min(i + step, len(remote))]
+            cols = [t % tn for t in block]
+            assert cols == sorted(cols)
 
 
 def test_workgroups_are_dealt_to_xcds_in_contiguous_runs():

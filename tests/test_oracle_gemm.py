@@ -206,6 +206,9 @@ def pin_chunks_and_rows(lib=None):
         got = assemble(ch)
         assert np.array_equal(got[r0:r1], ref[r0:r1])
         assert not got[:r0].any() and not got[r1:].any()
+        rows_only = oracle.gemm_scatter(a, b, c, 1.5, 0.25, 4, dtype, rows=(r0, r1),
+                                        scatter=False, lib=lib)
+        assert np.array_equal(rows_only, ref[r0:r1])
 
 
 def pin_specials(lib=None):
