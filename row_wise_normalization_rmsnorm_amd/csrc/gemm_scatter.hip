@@ -182,7 +182,7 @@ struct Params {
   int m, n, k;
   int chunk_rows;
   float alpha, beta;
-  int vec_out;  // every dst row and C row 8-byte aligned for 4-element access
+  int vec_out;  // 2: dst rows 16-byte aligned (and C rows 8); 1: both 8-byte; 0: neither
   Sched sched;
 };
 
@@ -319,7 +319,51 @@ __global__ __launch_bounds__(kThreads) void gemm_scatter_kernel(Params p) {
   //                           [col n0 + wn*128 + s*16 + 4*(lane >> 4) + r]
   const int row0 = m0 + wm * 128 + (lane & 15);
   const int col0 = n0 + wn * 128 + 4 * (lane >> 4);
-  if (p.vec_out && m0 + BM <= p.m && n0 + BN <= p.n) {
+  if (p.vec_out == 2 && m0 + BM <= p.m && n0 + BN <= p.n) {
+    // interior tile, 16-byte aligned output rows: the rounded tile is staged
+    // in the (now free) 128 KiB of LDS, then leaves in 16-byte stores that
+    // cover whole 512-byte row segments.  (After the loop's last barrier a
+    // slower wave may still be reading the next, unused fragments; what it
+    // reads is never used, so the staging writes need no barrier before
+    // them.)  LDS row pitch 512 bytes; the
+    // 16-byte chunk c of row r sits at chunk position c ^ (r & 15), so the
+    // 16 rows one staging write touches land in 16 different bank groups.
+    uint32_t* st = reinterpret_cast<uint32_t*>(&lds[0][0][0]);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int r = wm * 128 + t * 16 + (lane & 15);
+      const uint16_t* crow = p.c ? p.c + (int64_t)(m0 + r) * p.ldc + col0 : nullptr;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        float v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = p.alpha * acc[s][t][q];
+        if (crow) {
+          const u32x2 cv = *reinterpret_cast<const u32x2*>(crow + s * 16);
+          v[0] = __builtin_fmaf(p.beta, E::decode((uint16_t)(cv.x & 0xFFFFu)), v[0]);
+          v[1] = __builtin_fmaf(p.beta, E::decode((uint16_t)(cv.x >> 16)), v[1]);
+          v[2] = __builtin_fmaf(p.beta, E::decode((uint16_t)(cv.y & 0xFFFFu)), v[2]);
+          v[3] = __builtin_fmaf(p.beta, E::decode((uint16_t)(cv.y >> 16)), v[3]);
+        }
+        const int c = wn * 128 + s * 16 + 4 * (lane >> 4);  // column in the tile
+        const int chunk = (c >> 3) ^ (r & 15);
+        *reinterpret_cast<u32x2*>(st + r * 128 + chunk * 4 + ((c >> 2) & 1) * 2) =
+            u32x2{E::pack2(v[0], v[1]), E::pack2(v[2], v[3])};
+      }
+    }
+    __syncthreads();
+    // thread t stores chunk (t & 31) of rows (t >> 5) + 8 i
+#pragma unroll 4
+    for (int i = 0; i < BM / 8; ++i) {
+      const int r = i * 8 + (tid >> 5);
+      const int gm = m0 + r;
+      const int q = gm / p.chunk_rows;
+      uint16_t* drow = p.dst[q] + (int64_t)(gm - q * p.chunk_rows) * p.ldd + n0;
+      const int c = tid & 31;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(st + r * 128 + ((c ^ (r & 15)) * 4));
+      *reinterpret_cast<u32x4*>(drow + c * 8) = v;
+    }
+  } else if (p.vec_out && m0 + BM <= p.m && n0 + BN <= p.n) {
     // interior tile: every element exists and every access is 8-byte aligned
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
@@ -441,10 +485,14 @@ extern "C" int gemm_scatter_fwd(void* const* dst, int64_t ldd, int world, int ra
   if (k > 0 && ((int64_t)(gsc::BM - 1) * lda + k >= (int64_t)1 << 29 ||
                 (int64_t)(gsc::BN - 1) * ldb + k >= (int64_t)1 << 29))
     return rmsn_set_error(RMSN_ERR_SHAPE, "gemm_scatter: lda or ldb too large (255 * ld + k >= 2^29)");
+  // output access width: 2 = 16-byte rows (staged tile stores), 1 = 8-byte
+  // (direct stores), 0 = element by element; C is read 8 bytes at a time
   bool vec = (ldd % 4 == 0) && (!c || (ldc % 4 == 0 && ((uintptr_t)c & 7u) == 0));
+  bool vec16 = vec && ldd % 8 == 0;
   for (int q = 0; q < world; ++q) {
     if ((uintptr_t)dst[q] & 1u) return rmsn_set_error(RMSN_ERR_SHAPE, "gemm_scatter: dst misaligned");
     if ((uintptr_t)dst[q] & 7u) vec = false;
+    if ((uintptr_t)dst[q] & 15u) vec16 = false;
   }
   if ((c && ((uintptr_t)c & 1u)) || (flags && ((uintptr_t)flags & 3u)))
     return rmsn_set_error(RMSN_ERR_SHAPE, "gemm_scatter: c or flags misaligned");
@@ -482,7 +530,7 @@ extern "C" int gemm_scatter_fwd(void* const* dst, int64_t ldd, int world, int ra
   p.chunk_rows = (int)chunk_rows;
   p.alpha = alpha;
   p.beta = beta;
-  p.vec_out = vec ? 1 : 0;
+  p.vec_out = vec16 ? 2 : vec ? 1 : 0;
   p.sched = gsc::make_sched((int)m, (int)n, world, rank);
 
   hipStream_t st = (hipStream_t)stream;

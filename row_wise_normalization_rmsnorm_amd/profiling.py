@@ -285,13 +285,58 @@ def counters_summary(argv) -> int:
                     f"{hit / max(hit + miss, 1):.3f}.  Hits include gamma, which every "
                     f"workgroup reads from L2; whether data comes from HBM more than once is "
                     f"settled by FETCH_SIZE / WRITE_SIZE in the traffic summary.\n")
-        f.write(f"\nKernel sources sha256: `{source_hash('block_sum' if 'block_sum' in a.symbol else 'rmsnorm')}`\n")
+        op = ("block_sum" if "block_sum" in a.symbol else
+              "gemm_scatter" if "gemm_scatter" in a.symbol else "rmsnorm")
+        f.write(f"\nKernel sources sha256: `{source_hash(op)}`\n")
+    print(md)
+    return 0
+
+
+def gemm_counters_summary(argv) -> int:
+    """profiles/counters_<kernel>__<workload>.md for a GEMM workload: the
+    counters of one or more rocprofv3 --pmc runs (each ``counters=dir``) for
+    the kernel and, side by side, for the vendor library's GEMM that bench.py
+    runs on the same operands as context."""
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--workload", required=True)
+    ap.add_argument("--plan", required=True)
+    ap.add_argument("--symbol", required=True)
+    ap.add_argument("--library-symbol", default="Cijk")
+    ap.add_argument("runs", nargs="+", help="COUNTER,COUNTER,...=dir")
+    a = ap.parse_args(argv)
+    rows = []
+    cmds = []
+    for run in a.runs:
+        names, d = run.split("=", 1)
+        names = names.split(",")
+        cmds.append("rocprofv3 --pmc " + " ".join(names) + " --output-format csv -d <dir> -o run "
+                    f"-- python bench.py --workload {a.workload} --steps 10 --warmup 2 "
+                    "--no-cpu-baseline")
+        for n in names:
+            mine = counter(d, n, a.symbol)
+            try:
+                lib = counter(d, n, a.library_symbol)[0]
+            except ValueError:
+                lib = None
+            rows.append((n, mine[0], mine[1], lib))
+    md = os.path.join(PROFILES, f"counters_{short_name(a.plan)}__{a.workload}.md")
+    with open(md, "w") as f:
+        f.write(f"# Matrix-core, LDS and wait counters: {a.plan} on {a.workload}\n\n")
+        f.write("Commands:\n\n" + "".join(f"* `{c}`\n" for c in cmds) + "\n")
+        f.write("The library column is hipBLASLt's GEMM (`Cijk_...`), which bench.py runs on the "
+                "same operands as context.\n\n| counter | kernel, per dispatch (median) | "
+                "dispatches | hipBLASLt, per dispatch (median) |\n|---|---|---|---|\n")
+        for n, v, c, lib in rows:
+            f.write(f"| {n} | {v:,.0f} | {c} | {'' if lib is None else f'{lib:,.0f}'} |\n")
+        f.write(f"\nKernel sources sha256: `{source_hash('gemm_scatter')}`\n")
     print(md)
     return 0
 
 
 def main() -> int:
     import sys
+    if len(sys.argv) > 1 and sys.argv[1] == "gemm-counters":
+        return gemm_counters_summary(sys.argv[2:])
     if len(sys.argv) > 1 and sys.argv[1] == "sweep":
         return sweep_summary(sys.argv[2:])
     if len(sys.argv) > 1 and sys.argv[1] == "counters":
@@ -357,6 +402,9 @@ def main() -> int:
         for s in stats[:4]:
             f.write(f"| {s['name'][:90]} | {s['calls']} | {s['avg_ns'] / 1e3:.2f} | "
                     f"{s['min_ns'] / 1e3:.2f} | {s['max_ns'] / 1e3:.2f} | {s['pct']:.1f} |\n")
+        if gemm:
+            f.write("\nThe `Cijk_...` kernel is hipBLASLt's GEMM, which bench.py runs on the same "
+                    "rotated operands as context; it is not part of the path.\n")
         if gemm:
             tflops = w.flops() / (k["avg_ns"] * 1e-9) / 1e12
             f.write(f"\nAchieved ({w.flops():,} flop / average duration): **{tflops:.1f} "

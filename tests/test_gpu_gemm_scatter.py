@@ -45,22 +45,24 @@ def st(t: torch.Tensor) -> np.ndarray:
     return I.to_storage(t)
 
 
-def run(a, b, c, alpha, beta, world, rank=0, ldd_pad=0, flags=None, epoch=0):
+def run(a, b, c, alpha, beta, world, rank=0, ldd_pad=0, flags=None, epoch=0, col=4):
     """Launch into guarded chunk buffers; returns (assembled [m, n] storage,
-    the raw buffer).  Each chunk sits inside a [rows + 2, n + ldd_pad + 8]
-    block whose first and last rows and extra columns are guards."""
+    the raw buffer).  Each chunk sits at column ``col`` of a [rows + 2,
+    n + ldd_pad + 8 + col] block whose first and last rows and other columns
+    are guards.  col = 8 with a row pitch that is a multiple of 8 elements
+    gives 16-byte aligned rows (the staged tile stores); col = 4, 8-byte."""
     m, n = a.shape[0], b.shape[0]
     rows = m // world
-    width = n + ldd_pad + 8
+    width = n + ldd_pad + 8 + col
     buf = torch.full((world, rows + 2, width), GUARD, dtype=torch.int16, device=DEV)
     bufv = buf.view(a.dtype)
-    dst = [bufv[q, 1:rows + 1, 4:4 + n] for q in range(world)]
+    dst = [bufv[q, 1:rows + 1, col:col + n] for q in range(world)]
     B.gemm_scatter_fwd(dst, a, b, c, alpha, beta, rank, flags, epoch)
     torch.cuda.synchronize()
     host = buf.cpu()
-    inner = host[:, 1:rows + 1, 4:4 + n]
+    inner = host[:, 1:rows + 1, col:col + n]
     guard = host.clone()
-    guard[:, 1:rows + 1, 4:4 + n] = GUARD
+    guard[:, 1:rows + 1, col:col + n] = GUARD
     assert bool((guard == GUARD).all()), "a write landed outside the output chunks"
     return inner.reshape(m, n).numpy().view(np.uint16), host
 
@@ -131,13 +133,16 @@ SHAPES = [  # m, n, k, world, with_c
 @pytest.mark.parametrize("shape", SHAPES, ids=[f"{s[0]}x{s[1]}x{s[2]}w{s[3]}{'c' if s[4] else ''}"
                                                for s in SHAPES])
 def test_parity(dtype, shape):
+    """Each shape with 8-byte and with 16-byte aligned output rows (the
+    interior tiles of the latter take the LDS-staged stores)."""
     m, n, k, world, with_c = shape
-    say(f"[gpu] gemm_scatter {dtype} m={m} n={n} k={k} world={world} c={with_c}")
     a, b, c = make(dtype, m, n, k, with_c, seed=m + n + k)
     alpha, beta = (0.5, -1.25) if with_c else (1.0, 0.0)
-    got, _ = run(a, b, c, alpha, beta, world, rank=world - 1)
     want, y, mag = oracle_rows(a, b, c, alpha, beta, world, dtype)
-    compare(got, want, y, mag, k, dtype, f"{dtype} {shape}")
+    for col, pad in ((4, 0), (8, (-(n + 16)) % 8)):
+        say(f"[gpu] gemm_scatter {dtype} m={m} n={n} k={k} world={world} c={with_c} col={col}")
+        got, _ = run(a, b, c, alpha, beta, world, rank=world - 1, ldd_pad=pad, col=col)
+        compare(got, want, y, mag, k, dtype, f"{dtype} {shape} col {col}")
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
@@ -189,9 +194,11 @@ def test_full_size_sampled(name):
     d = I.gemm_inputs(w)
     a, b = d["a"].to(DEV), d["b"].to(DEV)
     c = d["c"].to(DEV) if d["c"] is not None else None
-    got, _ = run(a, b, c, w.alpha, w.beta, w.world, rank=w.rank)
-    again, _ = run(a, b, c, w.alpha, w.beta, w.world, rank=w.rank)
+    got, _ = run(a, b, c, w.alpha, w.beta, w.world, rank=w.rank, col=8)
+    again, _ = run(a, b, c, w.alpha, w.beta, w.world, rank=w.rank, col=8)
     assert np.array_equal(got, again), "two launches differ"
+    other, _ = run(a, b, c, w.alpha, w.beta, w.world, rank=w.rank, col=4)
+    assert np.array_equal(got, other), "staged and direct stores differ"
     chunk = w.m // w.world
     rows = sorted({q * chunk + off for q in range(w.world) for off in (0, chunk // 2 + 3)}
                   | {w.m - 1, 255, 256})
