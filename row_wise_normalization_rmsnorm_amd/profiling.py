@@ -208,18 +208,20 @@ def report_summary(argv) -> int:
         m = re.search(r"\[gpu\] (\w+): error / bound = ([0-9.e+-]+)", line)
         if m:
             stats[m.group(1)] = {"error_over_bound": float(m.group(2))}
-    rows = []
+    rows, gemm_rows = [], []
     for path in a.bench_json:
         for line in open(path):
             if line.startswith("{"):
-                rows.append(json.loads(line))
+                d = json.loads(line)
+                (gemm_rows if d["config"].get("op") == "gemm_scatter" else rows).append(d)
     md = os.path.join(PROFILES, "per_config_report.md")
     with open(md, "w") as f:
         f.write("# Per-workload report: GPU kernel, CPU oracle, parity\n\n")
         f.write("Commands: `python bench.py --workload W --no-ceiling` for every workload (the GPU "
                 "step timed with HIP events; the oracle timed on the host's cores, and on one), and "
-                "`python -m pytest tests/test_gpu_parity.py tests/test_gpu_block_sum.py -m gpu -s -k "
-                "\"workloads\"` for the parity statistics (all rows of the 512-row workloads; 128+ "
+                "`python -m pytest tests/test_gpu_parity.py tests/test_gpu_block_sum.py "
+                "tests/test_gpu_gemm_scatter.py -m gpu -s -k \"workloads or full_size\"` for the "
+                "parity statistics (all rows of the 512-row workloads; 128+ "
                 "sampled rows of the full-size launches, whose residual is also checked whole).\n\n")
         f.write("| workload | GPU µs/step | GPU GB/s | % of 8 TB/s | GPU rows/s | oracle GB/s "
                 "(cores) | oracle rows/s | oracle GB/s, 1 core | GPU ÷ oracle | parity |\n"
@@ -244,6 +246,29 @@ def report_summary(argv) -> int:
                     f"({cb.get('cores', '-')}) | {cb.get('rows_per_s', float('nan')):.3g} | "
                     f"{one.get('value', float('nan')):.3g} | "
                     f"{r['value'] / cb['value'] if cb.get('value') else float('nan'):.0f} | {par} |\n")
+        if gemm_rows:
+            f.write("\nGEMM with the reduce-scatter epilogue (bound by the matrix cores; the "
+                    "library column is hipBLASLt's plain GEMM on the same rotated operands; parity "
+                    "from `tests/test_gpu_gemm_scatter.py -k full_size`, sampled rows of every "
+                    "chunk):\n\n| workload | GPU µs/step | TFLOP/s | % of 2.5 PFLOP/s | hipBLASLt "
+                    "µs | oracle TFLOP/s (cores) | oracle TFLOP/s, 1 core | GPU ÷ oracle | parity "
+                    "|\n|---|---|---|---|---|---|---|---|---|\n")
+            for r in gemm_rows:
+                w = r["config"]["workload"]
+                cb = r.get("cpu_baseline", {})
+                one = cb.get("single_thread", {})
+                st = stats.get(w, {})
+                par = (f"error / bound max {st['max_error_over_bound']:.2g}, "
+                       f"{100 * st['min_equal_frac']:.1f}%+ equal to the oracle's rounding "
+                       f"({st['rows_checked']} rows)" if "max_error_over_bound" in st
+                       else "see tests")
+                lib = r.get("library_context", {})
+                f.write(f"| {w} | {r['ms_per_step'] * 1e3:.2f} | {r['value']:.1f} | "
+                        f"{r['pct_of_peak']:.1f} | {lib.get('us', float('nan')):.1f} | "
+                        f"{cb.get('value', float('nan')):.3g} ({cb.get('cores', '-')}) | "
+                        f"{one.get('value', float('nan')):.3g} | "
+                        f"{r['value'] / cb['value'] if cb.get('value') else float('nan'):.0f} | "
+                        f"{par} |\n")
         f.write("\nThe oracle is the plain double-precision reference (test infrastructure), timed "
                 "as it stands: a baseline, not a target.\n")
     print(md)

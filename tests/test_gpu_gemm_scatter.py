@@ -99,6 +99,7 @@ def compare(got: np.ndarray, want: np.ndarray, y: np.ndarray, mag: np.ndarray, k
     say(f"[gpu] {what}: error / bound max {ratio:.3g}, equal to the oracle's rounding "
         f"{100 * exact:.2f}%")
     assert exact >= min_exact, f"{what}: only {exact:.3f} of elements equal the oracle's"
+    return ratio, exact
 
 
 def make(dtype, m, n, k, with_c, seed, lda_pad=0, ldb_pad=0, ldc_pad=0):
@@ -203,12 +204,18 @@ def test_full_size_sampled(name):
     rows = sorted({q * chunk + off for q in range(w.world) for off in (0, chunk // 2 + 3)}
                   | {w.m - 1, 255, 256})
     ac, bc = st(d["a"]), st(d["b"])
+    worst, least = 0.0, 1.0
     for r in rows:
         chunks, y, mag = oracle.gemm_scatter(ac, bc, None, w.alpha, w.beta, w.world, w.dtype,
                                              rows=(r, r + 1), want_f64=True)
         q = r // chunk
         want = chunks[q][r - q * chunk:r - q * chunk + 1]
-        compare(got[r:r + 1], want, y, mag, w.k, w.dtype, f"{name} row {r}", min_exact=0.7)
+        ratio, exact = compare(got[r:r + 1], want, y, mag, w.k, w.dtype, f"{name} row {r}",
+                               min_exact=0.7)
+        worst, least = max(worst, ratio), min(least, exact)
+    say(f"[gpu] {name}: " + repr({"max_error_over_bound": float(f"{worst:.3g}"),
+                                  "min_equal_frac": float(f"{least:.4f}"),
+                                  "rows_checked": len(rows)}))
 
 
 def test_special_values():
