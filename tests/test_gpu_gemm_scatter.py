@@ -127,6 +127,7 @@ SHAPES = [  # m, n, k, world, with_c
     (8, 40, 8, 2, True),           # far below one tile
     (64, 1000, 72, 2, False),
     (1024, 512, 1024, 4, True),
+    (768, 520, 8, 16, True),       # the most chunks (16, of 48 rows), one 8-wide k chunk
 ]
 
 
@@ -157,6 +158,20 @@ def test_strided_operands(dtype):
         got, _ = run(a, b, c, 1.5, 0.75, world, rank=1, ldd_pad=ldd_pad)
         want, y, mag = oracle_rows(a, b, c, 1.5, 0.75, world, "bf16" if dtype == "bf16" else "f16")
         compare(got, want, y, mag, k, dtype, f"strided {dtype} {ldd_pad}/{ldc_pad}")
+
+
+def test_empty_products_launch_nothing():
+    """m = 0 or n = 0: nothing to compute, nothing written, no error."""
+    a = torch.zeros(0, 64, dtype=torch.bfloat16, device=DEV)
+    b = torch.zeros(128, 64, dtype=torch.bfloat16, device=DEV)
+    B.gemm_scatter_fwd([torch.empty(0, 128, dtype=torch.bfloat16, device=DEV)] * 2, a, b)
+    a = torch.ones(64, 64, dtype=torch.bfloat16, device=DEV)
+    b = torch.zeros(0, 64, dtype=torch.bfloat16, device=DEV)
+    sentinel = torch.full((64, 8), 7.0, dtype=torch.bfloat16, device=DEV)
+    dst = [sentinel[:32, :0], sentinel[32:, :0]]
+    B.gemm_scatter_fwd(dst, a, b)
+    torch.cuda.synchronize()
+    assert bool((sentinel == 7.0).all())
 
 
 def test_k_zero_gives_beta_c():
