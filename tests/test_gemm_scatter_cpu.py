@@ -128,3 +128,29 @@ def test_binding_checks_shapes_before_the_library():
     a = torch.empty(8, 16, dtype=torch.bfloat16)
     with pytest.raises(B.RmsnormError):
         B.gemm_scatter_fwd([a[:4], a[4:]], a, a.to(torch.float16))
+
+
+def test_schedule_random_shapes():
+    """Seeded random shapes: every schedule is a permutation, the local chunk
+    runs last, and the other chunks keep ring order group by group."""
+    import random
+    rng = random.Random(77)
+    for _ in range(60):
+        world = rng.choice([1, 2, 3, 4, 5, 7, 8, 16])
+        m = world * rng.randint(1, 700)
+        n = rng.randint(1, 3000)
+        rank = rng.randrange(world)
+        tiles = B.gemm_scatter_tiles(m, n)
+        tn = -(-n // TN)
+        wg, pos = B.gemm_scatter_schedule(m, n, world, rank)
+        assert sorted(wg) == list(range(tiles)) == sorted(pos)
+        order = oracle.gemm_scatter_chunk_order(world, rank)
+        rank_of = {q: i for i, q in enumerate(order)}
+        seq = [rank_of[tile_chunk(t, m, n, world)] for t in pos]
+        local = [i for i, q in enumerate(seq) if q == world - 1]
+        assert not local or local == list(range(tiles - len(local), tiles)), (m, n, world, rank)
+        remote = seq[:tiles - len(local)]
+        step = GROUP_ROWS * tn
+        blocks = [remote[i:i + step] for i in range(0, len(remote), step)]
+        for x, y in zip(blocks, blocks[1:]):
+            assert max(x) <= min(y), (m, n, world, rank)

@@ -285,3 +285,31 @@ def test_reduce_scatter_then_add_rmsnorm():
     assert np.array_equal(st(res.cpu()), o_res), "new residual differs from the oracle"
     d = ind.ulp_distance(st(out.cpu()), o_out, "bf16")
     assert int(d.max()) <= 2
+
+
+def test_random_calls():
+    """Seeded random calls: dtype, shape (ragged m, n, k), world and rank,
+    alpha, beta, optional C, padded strides and both output alignments."""
+    rng = np.random.default_rng(2024)
+    for i in range(14):
+        dtype = str(rng.choice(["bf16", "f16"]))
+        world = int(rng.choice([1, 2, 3, 4, 8, 16]))
+        m = world * int(rng.integers(1, 48))
+        n = int(rng.integers(1, 700))
+        k = 8 * int(rng.integers(0, 48))
+        with_c = bool(rng.random() < 0.5)
+        alpha = float(np.float32(rng.choice([1.0, -0.5, 1.75])))
+        beta = float(np.float32(rng.choice([0.0, 1.0, -2.0]))) if with_c else 0.0
+        rank = int(rng.integers(world))
+        pads = [int(8 * rng.integers(0, 3)) for _ in range(2)]
+        a, b, c = make(dtype, m, n, k, with_c, seed=1000 + i, lda_pad=pads[0],
+                       ldb_pad=pads[1], ldc_pad=int(rng.integers(0, 5)))
+        if k == 0:
+            a, b = a.contiguous(), b.contiguous()
+        col = int(rng.choice([4, 8]))
+        pad = (-(n + 8 + col)) % 8 if col == 8 else int(rng.integers(0, 4))
+        say(f"[gpu] random #{i}: {dtype} m={m} n={n} k={k} world={world} rank={rank} "
+            f"c={with_c} col={col}")
+        got, _ = run(a, b, c, alpha, beta, world, rank=rank, ldd_pad=pad, col=col)
+        want, y, mag = oracle_rows(a, b, c, alpha, beta, world, dtype)
+        compare(got, want, y, mag, k, dtype, f"random #{i}", min_exact=0.6)
