@@ -250,6 +250,23 @@ def test_special_values():
     compare(got, want, y, mag, k, "bf16", "special values")
 
 
+def test_fp16_subnormal_operands():
+    """fp16 operands in the subnormal range (and products far below the
+    smallest normal): the result stays within the bound, whose absolute
+    floor is half an ulp at the smallest normal."""
+    m, n, k = 256, 64, 64
+    rng = np.random.default_rng(8)
+    a = torch.from_numpy(rng.integers(1, 1024, (m, k)).astype(np.float32) * 2.0 ** -24).to(torch.float16)
+    b = torch.from_numpy(rng.standard_normal((n, k)).astype(np.float32)).to(torch.float16)
+    # rows 8.. mix normal and subnormal columns; rows 0..7 stay all subnormal,
+    # so their results (about k * 2^-24) would show a flush to zero
+    a[8:, ::2] = torch.from_numpy(rng.standard_normal((m - 8, k // 2)).astype(np.float32)).to(torch.float16)
+    say("[gpu] fp16 subnormal operands")
+    got, _ = run(a.to(DEV), b.to(DEV), None, 1.0, 0.0, 2)
+    want, y, mag = oracle_rows(a, b, None, 1.0, 0.0, 2, "f16")
+    compare(got, want, y, mag, k, "f16", "fp16 subnormal operands")
+
+
 def test_reduce_scatter_then_add_rmsnorm():
     """Eight ranks emulated on one GPU: rank r multiplies its own A_r, B_r and
     scatters chunk q into rank q's receive buffer (slot r); rank q then sums

@@ -250,7 +250,32 @@ def pin_chunk_order(lib=None):
             assert all((order[s + 1] - order[s]) % world == 1 for s in range(world - 1))
 
 
-PINS = {"worked_example": pin_worked_example, "closed_forms": pin_closed_forms,
+def pin_power_of_two_scaling(lib=None):
+    """Scaling A, or alpha, by 2^e scales every unrounded value by exactly
+    2^e (in the normal range both are exact), so the stored values of the
+    scaled product equal those of the product rounded after scaling."""
+    rng = np.random.default_rng(21)
+    for dtype in ("bf16", "f16"):
+        a = value_grid(rng, (8, 40), dtype)
+        b = value_grid(rng, (6, 40), dtype)
+        c = value_grid(rng, (8, 6), dtype)
+        _, y, _ = oracle.gemm_scatter(a, b, c, 0.75, 0.5, 2, dtype, want_f64=True, lib=lib)
+        for e in (-3, 2):
+            a2 = store(ind.decode_np(a, dtype) * 2.0 ** e, dtype)
+            _, ya, _ = oracle.gemm_scatter(a2, b, None, 0.75, 0.0, 2, dtype, want_f64=True,
+                                           lib=lib)
+            _, y0, _ = oracle.gemm_scatter(a, b, None, 0.75, 0.0, 2, dtype, want_f64=True,
+                                           lib=lib)
+            assert np.array_equal(ya, y0 * 2.0 ** e)
+            _, yb, _ = oracle.gemm_scatter(a, b, None, 0.75 * 2.0 ** e, 0.0, 2, dtype,
+                                           want_f64=True, lib=lib)
+            assert np.array_equal(yb, y0 * 2.0 ** e)
+        # C enters once, scaled by beta: y(beta) - y(0) = beta * C exactly here
+        _, yc0, _ = oracle.gemm_scatter(a, b, c, 0.75, 0.0, 2, dtype, want_f64=True, lib=lib)
+        assert np.array_equal(y - yc0, 0.5 * ind.decode_np(c, dtype))
+
+
+PINS = {"worked_example": pin_worked_example, "power_of_two_scaling": pin_power_of_two_scaling, "closed_forms": pin_closed_forms,
         "chunks_and_rows": pin_chunks_and_rows, "specials": pin_specials,
         "chunk_order": pin_chunk_order, "numpy_matmul": pin_numpy_matmul,
         "brute_force": pin_brute_force}
