@@ -10,20 +10,24 @@
 // chunk (section "gemmrs版本的swizzle如何编排").
 //
 // MI355X design:
-//   - 256 x 256 output tile per workgroup of four waves (2 x 2), each wave a
-//     128 x 128 block of 8 x 8 v_mfma_f32_16x16x32 products (fp32 accumulate)
-//     over k steps of 64.
+//   - 256 x 256 output tile per workgroup of eight waves, two per SIMD; each
+//     wave a 128 x 64 block of 8 x 4 v_mfma_f32_16x16x32 products (fp32
+//     accumulate, 128 accumulator registers) over k steps of 64.  With two
+//     waves per SIMD one wave's products run while the other waits on LDS,
+//     memory or the barrier (measured 188.7 us against 204.6 us for four
+//     waves of 128 x 128 blocks on the 4096 x 8192 x 3584 bf16 product, one
+//     set of operands).
 //   - The matrix-core operands are swapped (the weight rows feed the first
 //     operand, the activation rows the second), so each lane's four
-//     accumulator values are four consecutive output columns of one row and
-//     leave as one 8-byte store.
+//     accumulator values are four consecutive output columns of one row.
 //   - A and B tiles pass through LDS, double-buffered (2 x 64 KiB of the
 //     CU's 160 KiB): each thread loads 16-byte chunks of the next k step
 //     into registers while the waves multiply the current one, then writes
-//     them to the other buffer; one barrier per k step.  (Loading straight
-//     into LDS with gfx950's buffer-load-to-LDS form measured slower, 225 vs
-//     203 us, the compiler then shuffling accumulators between register
-//     files inside the loop.)
+//     them to the other buffer; one barrier per k step.  The loads are
+//     spread between the first half's products and the LDS writes between
+//     the second half's.  (Loading straight into LDS with gfx950's
+//     buffer-load-to-LDS form, and deeper pipelines, measured no better with
+//     four waves.)
 //   - LDS rows are 128 bytes (64 elements); the 16-byte chunk c of row r is
 //     stored at chunk position c ^ (r & 7), so the eight lanes of each LDS
 //     access phase, which read the same chunk of eight consecutive rows, hit
@@ -36,6 +40,8 @@
 //     runs of 32 per XCD: an 8 x 4 block of tiles shares its operand rows in
 //     the XCD's L2 (measured 1214 -> 1241 TFLOP/s against groups of two
 //     tile-rows on the 4096 x 8192 x 3584 bf16 product).
+//   - Interior tiles with 16-byte aligned output rows stage the rounded tile
+//     in LDS and write whole 512-byte row segments.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdio.h>
@@ -45,12 +51,13 @@
 
 int rmsn_set_error(int code, const char* msg);
 
+
 namespace gsc {
 
 constexpr int BM = GEMM_SCATTER_TILE_M;
 constexpr int BN = GEMM_SCATTER_TILE_N;
 constexpr int BK = 64;                 // k elements per step (128 bytes of a row)
-constexpr int kThreads = 256;          // four waves
+constexpr int kThreads = 512;          // eight waves, two per SIMD
 constexpr int kChunksPerRow = BK / 8;  // 16-byte chunks per LDS row
 constexpr int kXcds = 8;
 constexpr int kRoundPerXcd = 32;       // positions each XCD takes per round (one per CU)
@@ -59,7 +66,7 @@ constexpr int kGroupM = 8;             // tile-rows per schedule group
 // offset used for a chunk outside every operand's range.
 constexpr int kRsrcWord3 = 0x00020000;
 constexpr int kOutOfRange = 0x7FFFFFF0;
-static_assert(BM == 256 && BN == 256 && kThreads == 256, "the thread mapping assumes these");
+static_assert(BM == 256 && BN == 256 && kThreads == 512, "the thread mapping assumes these");
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -198,19 +205,19 @@ __global__ __launch_bounds__(kThreads) void gemm_scatter_kernel(Params p) {
   const int tid = (int)threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;  // wave block: 128 rows x 64 columns
 
-  // global -> LDS: thread t moves logical chunk (t & 7) of rows (t >> 3) + 32 i
+  // global -> LDS: thread t moves logical chunk (t & 7) of rows (t >> 3) + 64 i
   const int lrow = tid >> 3;
   const int lchunk = tid & 7;
 
-  f32x4 acc[8][8];
+  f32x4 acc[4][8];
 #pragma unroll
-  for (int s = 0; s < 8; ++s)
+  for (int s = 0; s < 4; ++s)
 #pragma unroll
     for (int t = 0; t < 8; ++t) acc[s][t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  u32x4 ra[8], rb[8];
+  u32x4 ra[4], rb[4];
   const int nk = (p.k + BK - 1) / BK;
 
   // Operand loads are raw buffer loads over this tile's rows; the resource
@@ -230,21 +237,21 @@ __global__ __launch_bounds__(kThreads) void gemm_scatter_kernel(Params p) {
       (void*)(p.b + (int64_t)n0 * p.ldb), (short)0,
       (int)(((int64_t)(b_tile_rows - 1) * p.ldb + p.k) * 2), kRsrcWord3);
   // rows lrow + 32 i exist for i < a_rows (b_rows); the last one of them
-  const int a_rows = a_tile_rows > lrow ? (a_tile_rows - lrow + 31) / 32 : 0;
-  const int b_rows = b_tile_rows > lrow ? (b_tile_rows - lrow + 31) / 32 : 0;
-  const int a_last = a_rows > 0 ? lrow + 32 * (a_rows - 1) : a_tile_rows - 1;
-  const int b_last = b_rows > 0 ? lrow + 32 * (b_rows - 1) : b_tile_rows - 1;
+  const int a_rows = a_tile_rows > lrow ? (a_tile_rows - lrow + 63) / 64 : 0;
+  const int b_rows = b_tile_rows > lrow ? (b_tile_rows - lrow + 63) / 64 : 0;
+  const int a_last = a_rows > 0 ? lrow + 64 * (a_rows - 1) : a_tile_rows - 1;
+  const int b_last = b_rows > 0 ? lrow + 64 * (b_rows - 1) : b_tile_rows - 1;
   const int a_off0 = (lrow * (int)p.lda + lchunk * 8) * 2;
   const int b_off0 = (lrow * (int)p.ldb + lchunk * 8) * 2;
   const int a_off_last = (a_last * (int)p.lda + lchunk * 8) * 2;
   const int b_off_last = (b_last * (int)p.ldb + lchunk * 8) * 2;
-  const int a_row_step = 32 * (int)p.lda * 2, b_row_step = 32 * (int)p.ldb * 2;
+  const int a_row_step = 64 * (int)p.lda * 2, b_row_step = 64 * (int)p.ldb * 2;
 
   auto gload = [&](int kt) {
     const bool kin = kt * BK + lchunk * 8 < p.k;
     const int kb = kt * BK * 2;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 4; ++i) {
       const int oa = kin ? (i < a_rows ? a_off0 + i * a_row_step : a_off_last) + kb : kOutOfRange;
       const int ob = kin ? (i < b_rows ? b_off0 + i * b_row_step : b_off_last) + kb : kOutOfRange;
       ra[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsa, oa, 0, 0));
@@ -253,8 +260,8 @@ __global__ __launch_bounds__(kThreads) void gemm_scatter_kernel(Params p) {
   };
   auto lstore = [&](int stage) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = lrow + 32 * i;
+    for (int i = 0; i < 4; ++i) {
+      const int r = lrow + 64 * i;
       const int at = r * kChunksPerRow + (lchunk ^ (r & 7));
       lds[stage][0][at] = ra[i];
       lds[stage][1][at] = rb[i];
@@ -263,18 +270,18 @@ __global__ __launch_bounds__(kThreads) void gemm_scatter_kernel(Params p) {
 
   // Fragments of one 32-wide k half: lane l supplies row (l & 15) of each
   // 16-row block and 16-byte chunk ks*4 + l/16 of the 64-wide k step.
-  auto read_frags = [&](int stage, int ks, u32x4 (&xf)[8], u32x4 (&yf)[8]) {
+  auto read_frags = [&](int stage, int ks, u32x4 (&xf)[4], u32x4 (&yf)[8]) {
     const int sw = (ks * 4 + (lane >> 4)) ^ (lane & 7);
 #pragma unroll
-    for (int s = 0; s < 8; ++s)
-      xf[s] = lds[stage][1][(wn * 128 + s * 16 + (lane & 15)) * kChunksPerRow + sw];
+    for (int s = 0; s < 4; ++s)
+      xf[s] = lds[stage][1][(wn * 64 + s * 16 + (lane & 15)) * kChunksPerRow + sw];
 #pragma unroll
     for (int t = 0; t < 8; ++t)
       yf[t] = lds[stage][0][(wm * 128 + t * 16 + (lane & 15)) * kChunksPerRow + sw];
   };
-  auto mfmas = [&](const u32x4 (&xf)[8], const u32x4 (&yf)[8]) {
+  auto mfmas = [&](const u32x4 (&xf)[4], const u32x4 (&yf)[8]) {
 #pragma unroll
-    for (int s = 0; s < 8; ++s)
+    for (int s = 0; s < 4; ++s)
 #pragma unroll
       for (int t = 0; t < 8; ++t) acc[s][t] = E::mfma(xf[s], yf[t], acc[s][t]);
   };
@@ -284,41 +291,34 @@ __global__ __launch_bounds__(kThreads) void gemm_scatter_kernel(Params p) {
     lstore(0);
   }
   __syncthreads();
-  u32x4 x0[8], y0[8], x1[8], y1[8];
-  if (nk > 0) read_frags(0, 0, x0, y0);
-
-  // One k step per iteration, with no branch inside: the loads of step
-  // kt + 1 (step kt again on the last iteration: harmless, never read) go
-  // out first; the second half's fragments are read while the first half
-  // multiplies; the staged loads are written to the other LDS buffer while
-  // the second half multiplies; after the barrier the next step's first
-  // half is read.
+  u32x4 xf[4], yf[8];
+  // two waves per SIMD: while one waits on LDS or memory the other's
+  // products run, so each wave keeps one fragment set
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
     gload(kt + 1 < nk ? kt + 1 : kt);
-    read_frags(cur, 1, x1, y1);
-    mfmas(x0, y0);
+    read_frags(cur, 0, xf, yf);
+    mfmas(xf, yf);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < 8; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one global (buffer) load
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
       __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // four MFMAs
     }
+    read_frags(cur, 1, xf, yf);
     lstore(cur ^ 1);
-    mfmas(x1, y1);
+    mfmas(xf, yf);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < 8; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // one LDS write
       __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // four MFMAs
     }
     __syncthreads();
-    read_frags(cur ^ 1, 0, x0, y0);
   }
 
   // epilogue: acc[s][t][r] is D[row m0 + wm*128 + t*16 + (lane & 15)]
   //                           [col n0 + wn*128 + s*16 + 4*(lane >> 4) + r]
   const int row0 = m0 + wm * 128 + (lane & 15);
-  const int col0 = n0 + wn * 128 + 4 * (lane >> 4);
+  const int col0 = n0 + wn * 64 + 4 * (lane >> 4);
   if (p.vec_out == 2 && m0 + BM <= p.m && n0 + BN <= p.n) {
     // interior tile, 16-byte aligned output rows: the rounded tile is staged
     // in the (now free) 128 KiB of LDS, then leaves in 16-byte stores that
@@ -334,7 +334,7 @@ __global__ __launch_bounds__(kThreads) void gemm_scatter_kernel(Params p) {
       const int r = wm * 128 + t * 16 + (lane & 15);
       const uint16_t* crow = p.c ? p.c + (int64_t)(m0 + r) * p.ldc + col0 : nullptr;
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
+      for (int s = 0; s < 4; ++s) {
         float v[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) v[q] = p.alpha * acc[s][t][q];
@@ -345,17 +345,17 @@ __global__ __launch_bounds__(kThreads) void gemm_scatter_kernel(Params p) {
           v[2] = __builtin_fmaf(p.beta, E::decode((uint16_t)(cv.y & 0xFFFFu)), v[2]);
           v[3] = __builtin_fmaf(p.beta, E::decode((uint16_t)(cv.y >> 16)), v[3]);
         }
-        const int c = wn * 128 + s * 16 + 4 * (lane >> 4);  // column in the tile
+        const int c = wn * 64 + s * 16 + 4 * (lane >> 4);  // column in the tile
         const int chunk = (c >> 3) ^ (r & 15);
         *reinterpret_cast<u32x2*>(st + r * 128 + chunk * 4 + ((c >> 2) & 1) * 2) =
             u32x2{E::pack2(v[0], v[1]), E::pack2(v[2], v[3])};
       }
     }
     __syncthreads();
-    // thread t stores chunk (t & 31) of rows (t >> 5) + 8 i
+    // thread t stores chunk (t & 31) of rows (t >> 5) + 16 i
 #pragma unroll 4
-    for (int i = 0; i < BM / 8; ++i) {
-      const int r = i * 8 + (tid >> 5);
+    for (int i = 0; i < BM / 16; ++i) {
+      const int r = i * 16 + (tid >> 5);
       const int gm = m0 + r;
       const int q = gm / p.chunk_rows;
       uint16_t* drow = p.dst[q] + (int64_t)(gm - q * p.chunk_rows) * p.ldd + n0;
@@ -372,7 +372,7 @@ __global__ __launch_bounds__(kThreads) void gemm_scatter_kernel(Params p) {
       uint16_t* drow = p.dst[q] + (int64_t)(gm - q * p.chunk_rows) * p.ldd + col0;
       const uint16_t* crow = p.c ? p.c + (int64_t)gm * p.ldc + col0 : nullptr;
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
+      for (int s = 0; s < 4; ++s) {
         float v[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) v[r] = p.alpha * acc[s][t][r];
@@ -397,7 +397,7 @@ __global__ __launch_bounds__(kThreads) void gemm_scatter_kernel(Params p) {
       uint16_t* drow = p.dst[q] + (int64_t)(gmc - q * p.chunk_rows) * p.ldd;
       const uint16_t* crow = p.c ? p.c + (int64_t)gmc * p.ldc : nullptr;
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
+      for (int s = 0; s < 4; ++s) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int gn = col0 + s * 16 + r;
