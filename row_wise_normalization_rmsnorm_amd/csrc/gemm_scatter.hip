@@ -316,18 +316,16 @@ __global__ __launch_bounds__(kThreads) void gemm_scatter_kernel(Params p) {
   }
 
   // epilogue: acc[s][t][r] is D[row m0 + wm*128 + t*16 + (lane & 15)]
-  //                           [col n0 + wn*128 + s*16 + 4*(lane >> 4) + r]
+  //                           [col n0 + wn*64 + s*16 + 4*(lane >> 4) + r]
   const int row0 = m0 + wm * 128 + (lane & 15);
   const int col0 = n0 + wn * 64 + 4 * (lane >> 4);
   if (p.vec_out == 2 && m0 + BM <= p.m && n0 + BN <= p.n) {
     // interior tile, 16-byte aligned output rows: the rounded tile is staged
-    // in the (now free) 128 KiB of LDS, then leaves in 16-byte stores that
-    // cover whole 512-byte row segments.  (After the loop's last barrier a
-    // slower wave may still be reading the next, unused fragments; what it
-    // reads is never used, so the staging writes need no barrier before
-    // them.)  LDS row pitch 512 bytes; the
-    // 16-byte chunk c of row r sits at chunk position c ^ (r & 15), so the
-    // 16 rows one staging write touches land in 16 different bank groups.
+    // in the 128 KiB of LDS, free since the loop's last barrier (no wave
+    // reads LDS after it), then leaves in 16-byte stores that cover whole
+    // 512-byte row segments.  LDS row pitch 512 bytes; the 16-byte chunk c
+    // of row r sits at chunk position c ^ (r & 15), so the 16 rows one
+    // staging write touches land in 16 different bank groups.
     uint32_t* st = reinterpret_cast<uint32_t*>(&lds[0][0][0]);
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
