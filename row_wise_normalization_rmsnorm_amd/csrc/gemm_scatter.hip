@@ -236,7 +236,7 @@ __global__ __launch_bounds__(kThreads) void gemm_scatter_kernel(Params p) {
   const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(p.b + (int64_t)n0 * p.ldb), (short)0,
       (int)(((int64_t)(b_tile_rows - 1) * p.ldb + p.k) * 2), kRsrcWord3);
-  // rows lrow + 32 i exist for i < a_rows (b_rows); the last one of them
+  // rows lrow + 64 i exist for i < a_rows (b_rows); the last one of them
   const int a_rows = a_tile_rows > lrow ? (a_tile_rows - lrow + 63) / 64 : 0;
   const int b_rows = b_tile_rows > lrow ? (b_tile_rows - lrow + 63) / 64 : 0;
   const int a_last = a_rows > 0 ? lrow + 64 * (a_rows - 1) : a_tile_rows - 1;
