@@ -24,7 +24,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
        [--no-cpu-baseline] [--no-ceiling] [--inplace] [--rotate-bytes GIB] [--rows N]
        [--resident-context]
        python bench.py --workload NAME --sweep [--repeat R] [--variant-filter S]
-       python bench.py --ceiling-sweep | --copy-calibration
+       python bench.py --ceiling-sweep | --copy-calibration | --gemm-shapes
 """
 from __future__ import annotations
 
@@ -292,6 +292,62 @@ def gemm_bench(a, name: str) -> int:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         result["cpu_baseline"] = gemm_cpu_baseline(w)
     print(json.dumps(result), flush=True)
+    return 0
+
+
+GEMM_SHAPES = [  # (m tokens, n hidden, k intermediate slice, world)
+    (1024, 8192, 3584, 8), (2048, 8192, 3584, 8), (4096, 8192, 3584, 8), (8192, 8192, 3584, 8),
+    (4096, 4096, 1792, 8), (4096, 8192, 1024, 8), (4096, 8192, 7168, 8), (16384, 8192, 3584, 8),
+]
+
+
+def gemm_shapes(a) -> int:
+    """One JSON line per shape of GEMM_SHAPES (bf16, operands rotated over
+    about 1 GiB): the kernel against torch.matmul (hipBLASLt) on the same
+    operands, both timed with HIP events over back-to-back launches."""
+    import torch
+    from row_wise_normalization_rmsnorm_amd import binding as B
+    from row_wise_normalization_rmsnorm_amd import inputs as I
+    from row_wise_normalization_rmsnorm_amd.workloads import GemmWorkload
+
+    dev = "cuda:0"
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    for (m, n, k, world) in GEMM_SHAPES:
+        w = GemmWorkload(f"gemm_scatter_bf16_{m}x{n}x{k}_w{world}", "bf16", m, n, k, world)
+        d = I.gemm_inputs(w)
+        nsets = max(1, int(-(-(1 << 30) // w.algorithmic_bytes())))
+        sets = []
+        for _ in range(nsets):
+            sa, sb = d["a"].to(dev), d["b"].to(dev)
+            sets.append((sa, sb, [torch.empty(m // world, n, dtype=sa.dtype, device=dev)
+                                  for _ in range(world)]))
+
+        def timed(fn, reps):
+            for i in range(5):
+                fn(i)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for i in range(reps):
+                fn(i)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / reps
+
+        reps = max(20, min(200, int(2e5 / max(w.flops() / 1.2e12, 1.0))))
+        ms = timed(lambda i: B.gemm_scatter_fwd(sets[i % nsets][2], sets[i % nsets][0],
+                                                sets[i % nsets][1]), reps)
+        lib = timed(lambda i: torch.matmul(sets[i % nsets][0], sets[i % nsets][1].t()), reps)
+        tiles = B.gemm_scatter_tiles(m, n)
+        print(json.dumps({"workload": w.name, "m": m, "n": n, "k": k, "world": world,
+                          "tiles": tiles, "us": round(ms * 1e3, 2),
+                          "tflops": round(w.flops() / (ms * 1e-3) / 1e12, 1),
+                          "library_us": round(lib * 1e3, 2),
+                          "library_tflops": round(w.flops() / (lib * 1e-3) / 1e12, 1),
+                          "rotating_sets": nsets, "launches": reps}), flush=True)
+        del sets
+        torch.cuda.empty_cache()
     return 0
 
 
@@ -589,6 +645,9 @@ def main() -> int:
                     help="write the output over the first input instead of a separate buffer")
     ap.add_argument("--rotate-bytes", type=float, default=1.0,
                     help="GiB of distinct buffers rotated through (cold cache)")
+    ap.add_argument("--gemm-shapes", action="store_true",
+                    help="time the GEMM with the scatter epilogue over a list of shapes against "
+                         "torch.matmul (one JSON line each) and exit")
     ap.add_argument("--resident-context", action="store_true",
                     help="GEMM workloads: also time the kernel and the library on one set of "
                          "operands (cache-resident)")
@@ -613,6 +672,8 @@ def main() -> int:
         return ceiling_sweep()
 
     from row_wise_normalization_rmsnorm_amd.workloads import GEMM_WORKLOADS
+    if a.gemm_shapes:
+        return gemm_shapes(a)
     if a.workload in GEMM_WORKLOADS:
         return gemm_bench(a, a.workload)
     w = WORKLOADS[a.workload or HEADLINE]

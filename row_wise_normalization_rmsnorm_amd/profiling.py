@@ -358,8 +358,36 @@ def gemm_counters_summary(argv) -> int:
     return 0
 
 
+def gemm_shapes_summary(argv) -> int:
+    """profiles/gemm_scatter_bf16_shapes.md from ``bench.py --gemm-shapes``."""
+    ap = argparse.ArgumentParser()
+    ap.add_argument("jsonl")
+    a = ap.parse_args(argv)
+    rows = [json.loads(l) for l in open(a.jsonl) if l.startswith("{")]
+    md = os.path.join(PROFILES, "gemm_scatter_bf16_shapes.md")
+    with open(md, "w") as f:
+        f.write("# GEMM with the scatter epilogue across shapes (bf16)\n\n")
+        f.write("Command: `python bench.py --gemm-shapes` (HIP events over back-to-back launches, "
+                "operands rotated over about 1 GiB; the library column is torch.matmul, i.e. "
+                "hipBLASLt's plain GEMM, on the same operands).  256 x 256 output tiles, one "
+                "workgroup each on 256 CUs.\n\n")
+        f.write("| m | n | k | chunks | tiles | kernel µs | TFLOP/s | % of 2.5 PFLOP/s | "
+                "hipBLASLt µs | hipBLASLt TFLOP/s | kernel ÷ hipBLASLt |\n"
+                "|---|---|---|---|---|---|---|---|---|---|---|\n")
+        for r in rows:
+            f.write(f"| {r['m']} | {r['n']} | {r['k']} | {r['world']} | {r['tiles']} | "
+                    f"{r['us']:.1f} | {r['tflops']:.0f} | {100 * r['tflops'] / 2500:.1f} | "
+                    f"{r['library_us']:.1f} | {r['library_tflops']:.0f} | "
+                    f"{r['library_us'] / r['us']:.2f} |\n")
+        f.write(f"\nKernel sources sha256: `{source_hash('gemm_scatter')}`\n")
+    print(md)
+    return 0
+
+
 def main() -> int:
     import sys
+    if len(sys.argv) > 1 and sys.argv[1] == "gemm-shapes":
+        return gemm_shapes_summary(sys.argv[2:])
     if len(sys.argv) > 1 and sys.argv[1] == "gemm-counters":
         return gemm_counters_summary(sys.argv[2:])
     if len(sys.argv) > 1 and sys.argv[1] == "sweep":
