@@ -194,7 +194,8 @@ def gemm_bench(a, name: str) -> int:
         s["dst"] = [torch.empty(w.m // w.world, w.n, dtype=s["a"].dtype, device=dev)
                     for _ in range(w.world)]
         sets.append(s)
-    kernel = f"gemm_scatter<{w.dtype},256x256x64,mfma16x16x32>"
+    tile_n = B.gemm_scatter_tile_n(w.m, w.n)
+    kernel = f"gemm_scatter<{w.dtype},256x{tile_n}x64,mfma16x16x32>"
 
     def step(i):
         s = sets[i % nsets]
@@ -273,7 +274,8 @@ def gemm_bench(a, name: str) -> int:
         "accumulate_dtype": "f32",
         "data": "synthetic (seeded N(0,1) activations, N(0,1/(8k)) weights, resident in HBM)",
         "config": {"workload": w.name, "op": w.op, "m": w.m, "n": w.n, "k": w.k,
-                   "world": w.world, "rank": w.rank, "kernel": kernel, "rotating_sets": nsets,
+                   "world": w.world, "rank": w.rank, "kernel": kernel, "tile_n": tile_n,
+                   "rotating_sets": nsets,
                    "flops_per_step": w.flops(),
                    "algorithmic_bytes_per_step": w.algorithmic_bytes()},
         "pct_of_peak": round(100 * tflops / peak, 2),
@@ -303,8 +305,9 @@ GEMM_SHAPES = [  # (m tokens, n hidden, k intermediate slice, world)
 
 def gemm_shapes(a) -> int:
     """One JSON line per shape of GEMM_SHAPES (bf16, operands rotated over
-    about 1 GiB): the kernel against torch.matmul (hipBLASLt) on the same
-    operands, both timed with HIP events over back-to-back launches."""
+    about 1 GiB): the kernel at each tile width (and which one the automatic
+    choice takes) against torch.matmul (hipBLASLt) on the same operands, all
+    timed with HIP events over back-to-back launches."""
     import torch
     from row_wise_normalization_rmsnorm_amd import binding as B
     from row_wise_normalization_rmsnorm_amd import inputs as I
@@ -336,13 +339,18 @@ def gemm_shapes(a) -> int:
             return e0.elapsed_time(e1) / reps
 
         reps = max(20, min(200, int(2e5 / max(w.flops() / 1.2e12, 1.0))))
-        ms = timed(lambda i: B.gemm_scatter_fwd(sets[i % nsets][2], sets[i % nsets][0],
-                                                sets[i % nsets][1]), reps)
+        by_width = {}
+        for tn in (B.GEMM_SCATTER_TILE_N, B.GEMM_SCATTER_TILE_N_NARROW):
+            t_ms = timed(lambda i: B.gemm_scatter_fwd(sets[i % nsets][2], sets[i % nsets][0],
+                                                      sets[i % nsets][1], tile_n=tn), reps)
+            by_width[tn] = {"tiles": B.gemm_scatter_tiles(m, n, tn), "us": round(t_ms * 1e3, 2),
+                            "tflops": round(w.flops() / (t_ms * 1e-3) / 1e12, 1)}
+        auto = B.gemm_scatter_tile_n(m, n)
         lib = timed(lambda i: torch.matmul(sets[i % nsets][0], sets[i % nsets][1].t()), reps)
-        tiles = B.gemm_scatter_tiles(m, n)
         print(json.dumps({"workload": w.name, "m": m, "n": n, "k": k, "world": world,
-                          "tiles": tiles, "us": round(ms * 1e3, 2),
-                          "tflops": round(w.flops() / (ms * 1e-3) / 1e12, 1),
+                          "tile_n": auto, "tiles": by_width[auto]["tiles"],
+                          "us": by_width[auto]["us"], "tflops": by_width[auto]["tflops"],
+                          "by_tile_n": {str(t): v for t, v in by_width.items()},
                           "library_us": round(lib * 1e3, 2),
                           "library_tflops": round(w.flops() / (lib * 1e-3) / 1e12, 1),
                           "rotating_sets": nsets, "launches": reps}), flush=True)

@@ -39,12 +39,15 @@
  *   - 1 <= world <= GEMM_SCATTER_WORLD_MAX, 0 <= rank < world, m divisible
  *     by world; m, n, k below 2^31; 255 * lda + k and 255 * ldb + k below
  *     2^29 (a tile's operand rows are addressed with 32-bit offsets).
- *   - flags (nullable): gemm_scatter_tiles(m, n) uint32 slots.  When given,
- *     the workgroup that computes tile t stores `epoch` to flags[t] after
- *     the tile's elements are written and made visible at system scope, so a
- *     consumer that reads flags[t] == epoch sees the whole tile.  Tile t
- *     covers rows [(t / TN) * GEMM_SCATTER_TILE_M, ...) and columns
- *     [(t % TN) * GEMM_SCATTER_TILE_N, ...), TN = ceil(n / TILE_N).
+ *   - tile_n: the output tile's width, GEMM_SCATTER_TILE_N (256) or
+ *     GEMM_SCATTER_TILE_N_NARROW (128); 0 takes gemm_scatter_tile_n(m, n).
+ *     Tiles are GEMM_SCATTER_TILE_M (256) rows high either way.
+ *   - flags (nullable): gemm_scatter_tiles(m, n, tile_n) uint32 slots.  When
+ *     given, the workgroup that computes tile t stores `epoch` to flags[t]
+ *     after the tile's elements are written and made visible at system
+ *     scope, so a consumer that reads flags[t] == epoch sees the whole tile.
+ *     Tile t covers rows [(t / T) * GEMM_SCATTER_TILE_M, ...) and columns
+ *     [(t % T) * W, ...), W the tile width used, T = ceil(n / W).
  *   - dst chunks must not overlap each other, a, b, c or flags.
  *   - The call enqueues one kernel on `stream` (NULL: the default stream),
  *     allocates nothing and does not synchronise.  Arguments are validated
@@ -65,20 +68,32 @@ extern "C" {
 #define GEMM_SCATTER_WORLD_MAX 16
 #define GEMM_SCATTER_TILE_M 256
 #define GEMM_SCATTER_TILE_N 256
+#define GEMM_SCATTER_TILE_N_NARROW 128
+/* the automatic width is narrow when 256-wide tiles would number at most
+ * this many: half the compute units of an MI355X, which the narrow tiling
+ * still fills in one round of workgroups */
+#define GEMM_SCATTER_NARROW_MAX_TILES 128
 
 /*
  * gemm_scatter_fwd -- the epilogue-scattered product above.  Returns RMSN_OK,
- * RMSN_ERR_NULL, RMSN_ERR_SHAPE (sizes, strides, alignment, world, rank),
- * RMSN_ERR_DTYPE, RMSN_ERR_ALIAS or RMSN_ERR_HIP.
+ * RMSN_ERR_NULL, RMSN_ERR_SHAPE (sizes, strides, alignment, world, rank,
+ * tile_n), RMSN_ERR_DTYPE, RMSN_ERR_ALIAS or RMSN_ERR_HIP.
  */
 int gemm_scatter_fwd(void* const* dst, int64_t ldd, int world, int rank, const void* a,
                      int64_t lda, const void* b, int64_t ldb, const void* c, int64_t ldc,
                      float alpha, float beta, int64_t m, int64_t n, int64_t k, int dtype,
-                     uint32_t* flags, uint32_t epoch, void* stream);
+                     uint32_t* flags, uint32_t epoch, int tile_n, void* stream);
 
-/* gemm_scatter_tiles -- number of output tiles (and flag slots) for m x n;
- * -1 if m or n is negative or too large. */
-int64_t gemm_scatter_tiles(int64_t m, int64_t n);
+/* gemm_scatter_tile_n -- the tile width tile_n = 0 takes for m x n:
+ * GEMM_SCATTER_TILE_N_NARROW when ceil(m / 256) * ceil(n / 256) is at most
+ * GEMM_SCATTER_NARROW_MAX_TILES, else GEMM_SCATTER_TILE_N; -1 if m or n is
+ * negative or too large. */
+int gemm_scatter_tile_n(int64_t m, int64_t n);
+
+/* gemm_scatter_tiles -- number of output tiles (and flag slots) for m x n at
+ * tile width tile_n (0: automatic); -1 if m or n is negative or too large,
+ * or tile_n is not 0, 128 or 256. */
+int64_t gemm_scatter_tiles(int64_t m, int64_t n, int tile_n);
 
 /*
  * gemm_scatter_schedule -- the tile schedule of one launch (host only, no
@@ -88,12 +103,12 @@ int64_t gemm_scatter_tiles(int64_t m, int64_t n);
  * the chunk of its first row.  The schedule runs the other ranks' chunks
  * first, in ring order from rank + 1, in groups of up to eight tile-rows
  * (a group may hold several chunks), then the local chunk's tile-rows;
- * within a group the tiles go column-major.  Either array may be NULL; each
- * holds `len` >= gemm_scatter_tiles(m, n) entries.  Returns RMSN_OK or
- * RMSN_ERR_SHAPE.
+ * within a group the tiles go column-major.  tile_n as for gemm_scatter_fwd.
+ * Either array may be NULL; each holds `len` >= gemm_scatter_tiles(m, n,
+ * tile_n) entries.  Returns RMSN_OK or RMSN_ERR_SHAPE.
  */
-int gemm_scatter_schedule(int64_t m, int64_t n, int world, int rank, int32_t* wg_tile,
-                          int32_t* pos_tile, int64_t len);
+int gemm_scatter_schedule(int64_t m, int64_t n, int world, int rank, int tile_n,
+                          int32_t* wg_tile, int32_t* pos_tile, int64_t len);
 
 #ifdef __cplusplus
 }

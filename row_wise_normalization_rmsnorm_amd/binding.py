@@ -24,12 +24,15 @@ EXPORTS = ("rmsnorm_fwd", "add_rmsnorm_fwd", "rmsnorm_strerror", "rmsnorm_last_e
            "rmsnorm_plan", "rmsnorm_variants", "rmsnorm_fwd_ex", "add_rmsnorm_fwd_ex",
            "rmsnorm_plan_ex", "rmsnorm_variants_ex", "rmsnorm_plan_call")
 BLOCK_SUM_EXPORTS = ("block_all_reduce_sum",)
-GEMM_SCATTER_EXPORTS = ("gemm_scatter_fwd", "gemm_scatter_tiles", "gemm_scatter_schedule")
+GEMM_SCATTER_EXPORTS = ("gemm_scatter_fwd", "gemm_scatter_tile_n", "gemm_scatter_tiles",
+                        "gemm_scatter_schedule")
 
 # GEMM with a reduce-scatter epilogue (include/gemm_scatter.h)
 GEMM_SCATTER_WORLD_MAX = 16
 GEMM_SCATTER_TILE_M = 256
 GEMM_SCATTER_TILE_N = 256
+GEMM_SCATTER_TILE_N_NARROW = 128
+GEMM_SCATTER_NARROW_MAX_TILES = 128
 
 # block all-reduce sum (include/block_sum.h)
 BRS_DTYPE_CODE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2,
@@ -91,11 +94,13 @@ def lib() -> ctypes.CDLL:
             l.block_all_reduce_sum.restype = c_int
             l.gemm_scatter_fwd.argtypes = [ctypes.POINTER(vp), i64, c_int, c_int, vp, i64, vp,
                                            i64, vp, i64, c_float, c_float, i64, i64, i64, c_int,
-                                           vp, ctypes.c_uint32, vp]
+                                           vp, ctypes.c_uint32, c_int, vp]
             l.gemm_scatter_fwd.restype = c_int
-            l.gemm_scatter_tiles.argtypes = [i64, i64]
+            l.gemm_scatter_tile_n.argtypes = [i64, i64]
+            l.gemm_scatter_tile_n.restype = c_int
+            l.gemm_scatter_tiles.argtypes = [i64, i64, c_int]
             l.gemm_scatter_tiles.restype = i64
-            l.gemm_scatter_schedule.argtypes = [i64, i64, c_int, c_int,
+            l.gemm_scatter_schedule.argtypes = [i64, i64, c_int, c_int, c_int,
                                                 ctypes.POINTER(ctypes.c_int32),
                                                 ctypes.POINTER(ctypes.c_int32), i64]
             l.gemm_scatter_schedule.restype = c_int
@@ -333,32 +338,38 @@ def _matrix(t: torch.Tensor, what: str):
     return t.data_ptr(), max(ld, t.shape[1])
 
 
-def gemm_scatter_tiles(m: int, n: int) -> int:
-    return int(lib().gemm_scatter_tiles(m, n))
+def gemm_scatter_tile_n(m: int, n: int) -> int:
+    """The output tile width the automatic choice (tile_n=0) takes for m x n."""
+    return int(lib().gemm_scatter_tile_n(m, n))
 
 
-def gemm_scatter_schedule(m: int, n: int, world: int, rank: int):
+def gemm_scatter_tiles(m: int, n: int, tile_n: int = 0) -> int:
+    return int(lib().gemm_scatter_tiles(m, n, tile_n))
+
+
+def gemm_scatter_schedule(m: int, n: int, world: int, rank: int, tile_n: int = 0):
     """(wg_tile, pos_tile): the tile each workgroup computes, and the tile at
     each position of the remote-first schedule."""
-    t = gemm_scatter_tiles(m, n)
+    t = gemm_scatter_tiles(m, n, tile_n)
     if t < 0:
         _check(-2)
     wg = (ctypes.c_int32 * max(t, 1))()
     pos = (ctypes.c_int32 * max(t, 1))()
-    _check(lib().gemm_scatter_schedule(m, n, world, rank, wg, pos, t))
+    _check(lib().gemm_scatter_schedule(m, n, world, rank, tile_n, wg, pos, t))
     return list(wg[:t]), list(pos[:t])
 
 
 def gemm_scatter_fwd(dst: Sequence[torch.Tensor], a: torch.Tensor, b: torch.Tensor,
                      c: Optional[torch.Tensor] = None, alpha: float = 1.0, beta: float = 0.0,
                      rank: int = 0, flags: Optional[torch.Tensor] = None, epoch: int = 0,
-                     stream=None) -> None:
+                     stream=None, tile_n: int = 0) -> None:
     """dst[q] = rows [q m/W, (q+1) m/W) of alpha * a @ b.T + beta * c, W = len(dst).
 
     a [m, k], b [n, k], c [m, n] and every dst[q] [m/W, n] share one 16-bit
-    dtype; rows may be strided, elements within a row contiguous.  flags
-    (uint32/int32, gemm_scatter_tiles(m, n) slots) receive ``epoch`` per
-    finished tile."""
+    dtype; rows may be strided, elements within a row contiguous.  tile_n is
+    the output tile width (128 or 256; 0 picks by shape).  flags
+    (uint32/int32, gemm_scatter_tiles(m, n, tile_n) slots) receive ``epoch``
+    per finished tile."""
     if a.dtype not in (torch.float16, torch.bfloat16):
         raise RmsnormError(-3, f"unsupported dtype {a.dtype}")
     world = len(dst)
@@ -387,14 +398,14 @@ def gemm_scatter_fwd(dst: Sequence[torch.Tensor], a: torch.Tensor, b: torch.Tens
     pf = None
     if flags is not None:
         if flags.dtype not in (torch.int32, torch.uint32) or not flags.is_contiguous() or \
-                flags.numel() < gemm_scatter_tiles(m, n):
+                flags.numel() < gemm_scatter_tiles(m, n, tile_n):
             raise RmsnormError(-2, "flags must be a contiguous int32 tensor with one slot per tile")
         pf = flags.data_ptr()
     arr = (ctypes.c_void_p * world)(*ptrs)
     _check(lib().gemm_scatter_fwd(arr, ldd, world, rank, pa, lda, pb, ldb, pc, ldc,
                                   ctypes.c_float(alpha), ctypes.c_float(beta), m, n, k,
                                   DTYPE_CODE[a.dtype], pf, ctypes.c_uint32(epoch & 0xFFFFFFFF),
-                                  _stream(a, stream)))
+                                  tile_n, _stream(a, stream)))
 
 
 def gemm_scatter(a: torch.Tensor, b: torch.Tensor, world: int, rank: int = 0,

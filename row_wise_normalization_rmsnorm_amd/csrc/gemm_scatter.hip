@@ -17,6 +17,10 @@
 //     memory or the barrier (measured 188.7 us against 204.6 us for four
 //     waves of 128 x 128 blocks on the 4096 x 8192 x 3584 bf16 product, one
 //     set of operands).
+//   - Products too small to give every CU a 256 x 256 tile (at most 128 such
+//     tiles) take 256 x 128 tiles instead: twice the workgroups, each wave a
+//     64 x 64 block of 4 x 4 products.  Both widths accumulate every output
+//     in the same k order, so they give bitwise equal results.
 //   - The matrix-core operands are swapped (the weight rows feed the first
 //     operand, the activation rows the second), so each lane's four
 //     accumulator values are four consecutive output columns of one row.
@@ -55,7 +59,8 @@ int rmsn_set_error(int code, const char* msg);
 namespace gsc {
 
 constexpr int BM = GEMM_SCATTER_TILE_M;
-constexpr int BN = GEMM_SCATTER_TILE_N;
+constexpr int BN = GEMM_SCATTER_TILE_N;            // wide tile
+constexpr int BN_NARROW = GEMM_SCATTER_TILE_N_NARROW;
 constexpr int BK = 64;                 // k elements per step (128 bytes of a row)
 constexpr int kThreads = 512;          // eight waves, two per SIMD
 constexpr int kChunksPerRow = BK / 8;  // 16-byte chunks per LDS row
@@ -66,7 +71,8 @@ constexpr int kGroupM = 8;             // tile-rows per schedule group
 // offset used for a chunk outside every operand's range.
 constexpr int kRsrcWord3 = 0x00020000;
 constexpr int kOutOfRange = 0x7FFFFFF0;
-static_assert(BM == 256 && BN == 256 && kThreads == 512, "the thread mapping assumes these");
+static_assert(BM == 256 && BN == 256 && BN_NARROW == 128 && kThreads == 512,
+              "the thread mapping assumes these");
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -117,10 +123,10 @@ struct Sched {
   int local_group;   // tile-rows per group among the local chunk's
 };
 
-__host__ __device__ inline Sched make_sched(int m, int n, int world, int rank) {
+__host__ __device__ inline Sched make_sched(int m, int n, int tn, int world, int rank) {
   Sched s;
   s.tiles_m = (m + BM - 1) / BM;
-  s.tiles_n = (n + BN - 1) / BN;
+  s.tiles_n = (n + tn - 1) / tn;
   s.tiles = s.tiles_m * s.tiles_n;
   // A tile-row belongs to the chunk of its first row.  Rotated order starts
   // at the first tile-row of chunk rank + 1 (ring order), so the tile-rows
@@ -193,31 +199,60 @@ struct Params {
   Sched sched;
 };
 
-template <int DT>
+// Tile shape of one workgroup: 256 rows by TN columns (256 or 128).  The
+// eight waves cover it as WAVES_M x WAVES_N blocks of WR x WC outputs, each
+// NY x NX products of 16 x 16; each thread loads NB 16-byte chunks of B rows
+// per k step (and four of A rows).
+template <int TN>
+struct Shape {
+  static constexpr int WAVES_N = TN == 256 ? 4 : 2;
+  static constexpr int WAVES_M = 8 / WAVES_N;
+  static constexpr int WR = BM / WAVES_M;  // 128 or 64 rows
+  static constexpr int WC = TN / WAVES_N;  // 64 columns
+  static constexpr int NY = WR / 16;
+  static constexpr int NX = WC / 16;
+  static constexpr int NB = TN / 64;       // B chunks per thread per k step
+  static constexpr int NLOAD = 4 + NB;     // global loads (and LDS writes) per thread per k step
+  static constexpr int PER = NX * NY / NLOAD;        // products placed after each load or write
+  static constexpr int REST = NX * NY - PER * NLOAD;  // products left after the last one
+  static constexpr int CPR = TN / 8;       // 16-byte chunks per staged output row
+  static constexpr int RPP = kThreads / CPR;  // staged rows stored per pass
+  static_assert(WC == 64 && NY * 16 == WR && CPR >= 16 && BM % RPP == 0, "tile mapping");
+};
+
+template <int DT, int TN>
 __global__ __launch_bounds__(kThreads) void gemm_scatter_kernel(Params p) {
   using E = Elem<DT>;
-  // [stage][operand: 0 = A rows (m), 1 = B rows (n)][row * 8 + chunk]
-  __shared__ u32x4 lds[2][2][BM * kChunksPerRow];
+  using S = Shape<TN>;
+  constexpr int NX = S::NX, NY = S::NY, NB = S::NB;
+  // per stage, [row * 8 + chunk] of the tile's BM rows of A, then of its TN
+  // rows of B
+  struct Stage {
+    u32x4 a[BM * kChunksPerRow];
+    u32x4 b[TN * kChunksPerRow];
+  };
+  __shared__ Stage lds[2];
 
   const int tile = tile_at(position_of_wg((int)blockIdx.x, p.sched.tiles), p.sched);
   const int m0 = (tile / p.sched.tiles_n) * BM;
-  const int n0 = (tile % p.sched.tiles_n) * BN;
+  const int n0 = (tile % p.sched.tiles_n) * TN;
   const int tid = (int)threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave >> 2, wn = wave & 3;  // wave block: 128 rows x 64 columns
+  // wave block: WR rows x WC columns
+  const int wm = (int)((unsigned)wave / S::WAVES_N), wn = (int)((unsigned)wave % S::WAVES_N);
 
   // global -> LDS: thread t moves logical chunk (t & 7) of rows (t >> 3) + 64 i
   const int lrow = tid >> 3;
   const int lchunk = tid & 7;
 
-  f32x4 acc[4][8];
+  f32x4 acc[NX][NY];
 #pragma unroll
-  for (int s = 0; s < 4; ++s)
+  for (int s = 0; s < NX; ++s)
 #pragma unroll
-    for (int t = 0; t < 8; ++t) acc[s][t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int t = 0; t < NY; ++t) acc[s][t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  u32x4 ra[4], rb[4];
+  u32x4 ra[4], rb[NB];
   const int nk = (p.k + BK - 1) / BK;
 
   // Operand loads are raw buffer loads over this tile's rows; the resource
@@ -229,7 +264,7 @@ __global__ __launch_bounds__(kThreads) void gemm_scatter_kernel(Params p) {
   // in flight while the current one is multiplied.  The whole variable
   // offset sits in the VGPR offset, which the range check covers.
   const int a_tile_rows = p.m - m0 < BM ? p.m - m0 : BM;
-  const int b_tile_rows = p.n - n0 < BN ? p.n - n0 : BN;
+  const int b_tile_rows = p.n - n0 < TN ? p.n - n0 : TN;
   const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(p.a + (int64_t)m0 * p.lda), (short)0,
       (int)(((int64_t)(a_tile_rows - 1) * p.lda + p.k) * 2), kRsrcWord3);
@@ -255,7 +290,8 @@ __global__ __launch_bounds__(kThreads) void gemm_scatter_kernel(Params p) {
       const int oa = kin ? (i < a_rows ? a_off0 + i * a_row_step : a_off_last) + kb : kOutOfRange;
       const int ob = kin ? (i < b_rows ? b_off0 + i * b_row_step : b_off_last) + kb : kOutOfRange;
       ra[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsa, oa, 0, 0));
-      rb[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsb, ob, 0, 0));
+      if (i < NB)
+        rb[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsb, ob, 0, 0));
     }
   };
   auto lstore = [&](int stage) {
@@ -263,76 +299,131 @@ __global__ __launch_bounds__(kThreads) void gemm_scatter_kernel(Params p) {
     for (int i = 0; i < 4; ++i) {
       const int r = lrow + 64 * i;
       const int at = r * kChunksPerRow + (lchunk ^ (r & 7));
-      lds[stage][0][at] = ra[i];
-      lds[stage][1][at] = rb[i];
+      lds[stage].a[at] = ra[i];
+      if (i < NB) lds[stage].b[at] = rb[i];
     }
   };
 
   // Fragments of one 32-wide k half: lane l supplies row (l & 15) of each
   // 16-row block and 16-byte chunk ks*4 + l/16 of the 64-wide k step.
-  auto read_frags = [&](int stage, int ks, u32x4 (&xf)[4], u32x4 (&yf)[8]) {
+  auto read_frags = [&](int stage, int ks, u32x4 (&xf)[NX], u32x4 (&yf)[NY]) {
     const int sw = (ks * 4 + (lane >> 4)) ^ (lane & 7);
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
-      xf[s] = lds[stage][1][(wn * 64 + s * 16 + (lane & 15)) * kChunksPerRow + sw];
+    for (int s = 0; s < NX; ++s)
+      xf[s] = lds[stage].b[(wn * S::WC + s * 16 + (lane & 15)) * kChunksPerRow + sw];
 #pragma unroll
-    for (int t = 0; t < 8; ++t)
-      yf[t] = lds[stage][0][(wm * 128 + t * 16 + (lane & 15)) * kChunksPerRow + sw];
+    for (int t = 0; t < NY; ++t)
+      yf[t] = lds[stage].a[(wm * S::WR + t * 16 + (lane & 15)) * kChunksPerRow + sw];
   };
-  auto mfmas = [&](const u32x4 (&xf)[4], const u32x4 (&yf)[8]) {
+  auto mfmas = [&](const u32x4 (&xf)[NX], const u32x4 (&yf)[NY]) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
+    for (int s = 0; s < NX; ++s)
 #pragma unroll
-      for (int t = 0; t < 8; ++t) acc[s][t] = E::mfma(xf[s], yf[t], acc[s][t]);
+      for (int t = 0; t < NY; ++t) acc[s][t] = E::mfma(xf[s], yf[t], acc[s][t]);
   };
 
-  if (nk > 0) {
-    gload(0);
-    lstore(0);
-  }
-  __syncthreads();
-  u32x4 xf[4], yf[8];
-  // two waves per SIMD: while one waits on LDS or memory the other's
-  // products run, so each wave keeps one fragment set
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    gload(kt + 1 < nk ? kt + 1 : kt);
-    read_frags(cur, 0, xf, yf);
-    mfmas(xf, yf);
+  if constexpr (TN == BN_NARROW) {
+    // A narrow tile has half the products per k step, too few to cover a
+    // load issued at the step's start (measured 98.8 -> 64.8 us on the
+    // 1024 x 8192 x 3584 bf16 product): the loads of step kt + 2 go out as
+    // soon as the LDS writes of step kt + 1 free their registers, a whole k
+    // step before they are needed.  The row offsets are fixed before the
+    // loop so that no load sits under a branch (a branch there makes the
+    // compiler wait for every load in flight).
+    int a_off[4], b_off[NB];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one global (buffer) load
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // four MFMAs
+    for (int i = 0; i < 4; ++i) {
+      a_off[i] = i < a_rows ? a_off0 + i * a_row_step : a_off_last;
+      if (i < NB) b_off[i] = i < b_rows ? b_off0 + i * b_row_step : b_off_last;
     }
-    read_frags(cur, 1, xf, yf);
-    lstore(cur ^ 1);
-    mfmas(xf, yf);
+    auto gload_early = [&](int kt) {
+      const bool kin = kt * BK + lchunk * 8 < p.k;
+      const int kb = kt * BK * 2;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // one LDS write
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // four MFMAs
+      for (int i = 0; i < 4; ++i) {
+        ra[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                              rsa, kin ? a_off[i] + kb : kOutOfRange, 0, 0));
+        if (i < NB)
+          rb[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                rsb, kin ? b_off[i] + kb : kOutOfRange, 0, 0));
+      }
+    };
+    if (nk > 0) {
+      gload_early(0);
+      lstore(0);
+      gload_early(nk > 1 ? 1 : 0);
     }
     __syncthreads();
+    u32x4 xf[NX], yf[NY];
+    for (int kt = 0; kt < nk; ++kt) {
+      const int cur = kt & 1;
+      read_frags(cur, 0, xf, yf);
+      mfmas(xf, yf);
+      read_frags(cur, 1, xf, yf);
+      lstore(cur ^ 1);
+      gload_early(kt + 2 < nk ? kt + 2 : nk - 1);
+      mfmas(xf, yf);
+#pragma unroll
+      for (int i = 0; i < S::NLOAD; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);       // one LDS write
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);       // one global (buffer) load
+        __builtin_amdgcn_sched_group_barrier(0x008, S::PER, 0);  // products
+      }
+      if constexpr (S::REST > 0) __builtin_amdgcn_sched_group_barrier(0x008, S::REST, 0);
+      __syncthreads();
+    }
+  } else {
+    if (nk > 0) {
+      gload(0);
+      lstore(0);
+    }
+    __syncthreads();
+    u32x4 xf[NX], yf[NY];
+    // two waves per SIMD: while one waits on LDS or memory the other's
+    // products run, so each wave keeps one fragment set
+    for (int kt = 0; kt < nk; ++kt) {
+      const int cur = kt & 1;
+      gload(kt + 1 < nk ? kt + 1 : kt);
+      read_frags(cur, 0, xf, yf);
+      mfmas(xf, yf);
+  #pragma unroll
+      for (int i = 0; i < S::NLOAD; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);       // one global (buffer) load
+        __builtin_amdgcn_sched_group_barrier(0x008, S::PER, 0);  // products
+      }
+      if constexpr (S::REST > 0) __builtin_amdgcn_sched_group_barrier(0x008, S::REST, 0);
+      read_frags(cur, 1, xf, yf);
+      lstore(cur ^ 1);
+      mfmas(xf, yf);
+  #pragma unroll
+      for (int i = 0; i < S::NLOAD; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);       // one LDS write
+        __builtin_amdgcn_sched_group_barrier(0x008, S::PER, 0);  // products
+      }
+      if constexpr (S::REST > 0) __builtin_amdgcn_sched_group_barrier(0x008, S::REST, 0);
+      __syncthreads();
+    }
   }
 
-  // epilogue: acc[s][t][r] is D[row m0 + wm*128 + t*16 + (lane & 15)]
-  //                           [col n0 + wn*64 + s*16 + 4*(lane >> 4) + r]
-  const int row0 = m0 + wm * 128 + (lane & 15);
-  const int col0 = n0 + wn * 64 + 4 * (lane >> 4);
-  if (p.vec_out == 2 && m0 + BM <= p.m && n0 + BN <= p.n) {
+  // epilogue: acc[s][t][r] is D[row m0 + wm*WR + t*16 + (lane & 15)]
+  //                           [col n0 + wn*WC + s*16 + 4*(lane >> 4) + r]
+  const int row0 = m0 + wm * S::WR + (lane & 15);
+  const int col0 = n0 + wn * S::WC + 4 * (lane >> 4);
+  if (p.vec_out == 2 && m0 + BM <= p.m && n0 + TN <= p.n) {
     // interior tile, 16-byte aligned output rows: the rounded tile is staged
-    // in the 128 KiB of LDS, free since the loop's last barrier (no wave
-    // reads LDS after it), then leaves in 16-byte stores that cover whole
-    // 512-byte row segments.  LDS row pitch 512 bytes; the 16-byte chunk c
-    // of row r sits at chunk position c ^ (r & 15), so the 16 rows one
-    // staging write touches land in 16 different bank groups.
-    uint32_t* st = reinterpret_cast<uint32_t*>(&lds[0][0][0]);
+    // in LDS, free since the loop's last barrier (no wave reads LDS after
+    // it), then leaves in 16-byte stores that cover whole row segments of
+    // TN * 2 bytes.  The 16-byte chunk c of staged row r sits at chunk
+    // position c ^ (r & 15), so the 16 rows one staging write touches land
+    // in 16 different bank groups.
+    uint32_t* st = reinterpret_cast<uint32_t*>(&lds[0].a[0]);
+    constexpr int pitch = TN / 2;  // staged row pitch in 32-bit words
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const int r = wm * 128 + t * 16 + (lane & 15);
+    for (int t = 0; t < NY; ++t) {
+      const int r = wm * S::WR + t * 16 + (lane & 15);
       const uint16_t* crow = p.c ? p.c + (int64_t)(m0 + r) * p.ldc + col0 : nullptr;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
+      for (int s = 0; s < NX; ++s) {
         float v[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) v[q] = p.alpha * acc[s][t][q];
@@ -343,34 +434,34 @@ __global__ __launch_bounds__(kThreads) void gemm_scatter_kernel(Params p) {
           v[2] = __builtin_fmaf(p.beta, E::decode((uint16_t)(cv.y & 0xFFFFu)), v[2]);
           v[3] = __builtin_fmaf(p.beta, E::decode((uint16_t)(cv.y >> 16)), v[3]);
         }
-        const int c = wn * 64 + s * 16 + 4 * (lane >> 4);  // column in the tile
+        const int c = wn * S::WC + s * 16 + 4 * (lane >> 4);  // column in the tile
         const int chunk = (c >> 3) ^ (r & 15);
-        *reinterpret_cast<u32x2*>(st + r * 128 + chunk * 4 + ((c >> 2) & 1) * 2) =
+        *reinterpret_cast<u32x2*>(st + r * pitch + chunk * 4 + ((c >> 2) & 1) * 2) =
             u32x2{E::pack2(v[0], v[1]), E::pack2(v[2], v[3])};
       }
     }
     __syncthreads();
-    // thread t stores chunk (t & 31) of rows (t >> 5) + 16 i
+    // thread t stores chunk (t % CPR) of rows t / CPR + RPP i
 #pragma unroll 4
-    for (int i = 0; i < BM / 16; ++i) {
-      const int r = i * 16 + (tid >> 5);
+    for (int i = 0; i < BM / S::RPP; ++i) {
+      const int r = i * S::RPP + (int)((unsigned)tid / S::CPR);
       const int gm = m0 + r;
       const int q = gm / p.chunk_rows;
       uint16_t* drow = p.dst[q] + (int64_t)(gm - q * p.chunk_rows) * p.ldd + n0;
-      const int c = tid & 31;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(st + r * 128 + ((c ^ (r & 15)) * 4));
+      const int c = (int)((unsigned)tid % S::CPR);
+      const u32x4 v = *reinterpret_cast<const u32x4*>(st + r * pitch + ((c ^ (r & 15)) * 4));
       *reinterpret_cast<u32x4*>(drow + c * 8) = v;
     }
-  } else if (p.vec_out && m0 + BM <= p.m && n0 + BN <= p.n) {
+  } else if (p.vec_out && m0 + BM <= p.m && n0 + TN <= p.n) {
     // interior tile: every element exists and every access is 8-byte aligned
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
+    for (int t = 0; t < NY; ++t) {
       const int gm = row0 + t * 16;
       const int q = gm / p.chunk_rows;
       uint16_t* drow = p.dst[q] + (int64_t)(gm - q * p.chunk_rows) * p.ldd + col0;
       const uint16_t* crow = p.c ? p.c + (int64_t)gm * p.ldc + col0 : nullptr;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
+      for (int s = 0; s < NX; ++s) {
         float v[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) v[r] = p.alpha * acc[s][t][r];
@@ -387,7 +478,7 @@ __global__ __launch_bounds__(kThreads) void gemm_scatter_kernel(Params p) {
   } else {
     // edge tile (or unaligned rows): element by element, inside m x n only
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
+    for (int t = 0; t < NY; ++t) {
       const int gm = row0 + t * 16;
       const bool row_ok = gm < p.m;
       const int gmc = row_ok ? gm : 0;
@@ -395,7 +486,7 @@ __global__ __launch_bounds__(kThreads) void gemm_scatter_kernel(Params p) {
       uint16_t* drow = p.dst[q] + (int64_t)(gmc - q * p.chunk_rows) * p.ldd;
       const uint16_t* crow = p.c ? p.c + (int64_t)gmc * p.ldc : nullptr;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
+      for (int s = 0; s < NX; ++s) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int gn = col0 + s * 16 + r;
@@ -436,19 +527,40 @@ size_t extent(int64_t rows, int64_t cols, int64_t ld, int64_t elem) {
 
 }  // namespace
 
-extern "C" int64_t gemm_scatter_tiles(int64_t m, int64_t n) {
+namespace {
+
+// tile width a call uses: the requested one, or for 0 the automatic choice;
+// -1 for anything else
+int resolve_tile_n(int64_t m, int64_t n, int tile_n) {
+  if (tile_n == gsc::BN || tile_n == gsc::BN_NARROW) return tile_n;
+  if (tile_n != 0) return -1;
+  const int64_t wide = ((m + gsc::BM - 1) / gsc::BM) * ((n + gsc::BN - 1) / gsc::BN);
+  return wide <= GEMM_SCATTER_NARROW_MAX_TILES ? gsc::BN_NARROW : gsc::BN;
+}
+
+}  // namespace
+
+extern "C" int gemm_scatter_tile_n(int64_t m, int64_t n) {
   if (m < 0 || n < 0 || m > kIntMax || n > kIntMax) return -1;
-  const int64_t t = ((m + gsc::BM - 1) / gsc::BM) * ((n + gsc::BN - 1) / gsc::BN);
+  return resolve_tile_n(m, n, 0);
+}
+
+extern "C" int64_t gemm_scatter_tiles(int64_t m, int64_t n, int tile_n) {
+  if (m < 0 || n < 0 || m > kIntMax || n > kIntMax) return -1;
+  const int tn = resolve_tile_n(m, n, tile_n);
+  if (tn < 0) return -1;
+  const int64_t t = ((m + gsc::BM - 1) / gsc::BM) * ((n + tn - 1) / tn);
   return t > kIntMax ? -1 : t;
 }
 
-extern "C" int gemm_scatter_schedule(int64_t m, int64_t n, int world, int rank, int32_t* wg_tile,
-                                     int32_t* pos_tile, int64_t len) {
-  const int64_t tiles = gemm_scatter_tiles(m, n);
+extern "C" int gemm_scatter_schedule(int64_t m, int64_t n, int world, int rank, int tile_n,
+                                     int32_t* wg_tile, int32_t* pos_tile, int64_t len) {
+  const int64_t tiles = gemm_scatter_tiles(m, n, tile_n);
   if (tiles < 0 || world < 1 || world > GEMM_SCATTER_WORLD_MAX || rank < 0 || rank >= world ||
       m % world != 0 || len < tiles)
-    return rmsn_set_error(RMSN_ERR_SHAPE, "gemm_scatter_schedule: bad sizes, world or rank");
-  const gsc::Sched s = gsc::make_sched((int)m, (int)n, world, rank);
+    return rmsn_set_error(RMSN_ERR_SHAPE, "gemm_scatter_schedule: bad sizes, tile width, world or rank");
+  const gsc::Sched s =
+      gsc::make_sched((int)m, (int)n, resolve_tile_n(m, n, tile_n), world, rank);
   for (int w = 0; w < s.tiles; ++w) {
     if (wg_tile) wg_tile[w] = gsc::tile_at(gsc::position_of_wg(w, s.tiles), s);
     if (pos_tile) pos_tile[w] = gsc::tile_at(w, s);
@@ -460,11 +572,13 @@ extern "C" int gemm_scatter_fwd(void* const* dst, int64_t ldd, int world, int ra
                                 const void* a, int64_t lda, const void* b, int64_t ldb,
                                 const void* c, int64_t ldc, float alpha, float beta, int64_t m,
                                 int64_t n, int64_t k, int dtype, uint32_t* flags, uint32_t epoch,
-                                void* stream) {
+                                int tile_n, void* stream) {
   if (dtype != RMSN_F16 && dtype != RMSN_BF16)
     return rmsn_set_error(RMSN_ERR_DTYPE, "gemm_scatter: dtype must be f16 or bf16");
   if (m < 0 || n < 0 || k < 0 || m > kIntMax || n > kIntMax || k > kIntMax)
     return rmsn_set_error(RMSN_ERR_SHAPE, "gemm_scatter: m, n, k must lie in [0, 2^31)");
+  const int tn = resolve_tile_n(m, n, tile_n);
+  if (tn < 0) return rmsn_set_error(RMSN_ERR_SHAPE, "gemm_scatter: tile_n must be 0, 128 or 256");
   if (world < 1 || world > GEMM_SCATTER_WORLD_MAX || rank < 0 || rank >= world)
     return rmsn_set_error(RMSN_ERR_SHAPE, "gemm_scatter: world or rank out of range");
   if (m % world != 0) return rmsn_set_error(RMSN_ERR_SHAPE, "gemm_scatter: m % world != 0");
@@ -496,7 +610,7 @@ extern "C" int gemm_scatter_fwd(void* const* dst, int64_t ldd, int world, int ra
     return rmsn_set_error(RMSN_ERR_SHAPE, "gemm_scatter: c or flags misaligned");
 
   const int64_t chunk_rows = m / world;
-  const int64_t tiles = gemm_scatter_tiles(m, n);
+  const int64_t tiles = gemm_scatter_tiles(m, n, tn);
   if (tiles < 0) return rmsn_set_error(RMSN_ERR_SHAPE, "gemm_scatter: too many tiles");
   const size_t dext = extent(chunk_rows, n, ldd, 2);
   const size_t aext = k > 0 ? extent(m, k, lda, 2) : 0, bext = k > 0 ? extent(n, k, ldb, 2) : 0;
@@ -529,15 +643,18 @@ extern "C" int gemm_scatter_fwd(void* const* dst, int64_t ldd, int world, int ra
   p.alpha = alpha;
   p.beta = beta;
   p.vec_out = vec16 ? 2 : vec ? 1 : 0;
-  p.sched = gsc::make_sched((int)m, (int)n, world, rank);
+  p.sched = gsc::make_sched((int)m, (int)n, tn, world, rank);
 
   hipStream_t st = (hipStream_t)stream;
-  if (dtype == RMSN_BF16)
-    hipLaunchKernelGGL(gsc::gemm_scatter_kernel<RMSN_BF16>, dim3((unsigned)tiles),
-                       dim3(gsc::kThreads), 0, st, p);
+  const dim3 grid((unsigned)tiles), block(gsc::kThreads);
+  if (dtype == RMSN_BF16 && tn == gsc::BN)
+    hipLaunchKernelGGL((gsc::gemm_scatter_kernel<RMSN_BF16, gsc::BN>), grid, block, 0, st, p);
+  else if (dtype == RMSN_BF16)
+    hipLaunchKernelGGL((gsc::gemm_scatter_kernel<RMSN_BF16, gsc::BN_NARROW>), grid, block, 0, st, p);
+  else if (tn == gsc::BN)
+    hipLaunchKernelGGL((gsc::gemm_scatter_kernel<RMSN_F16, gsc::BN>), grid, block, 0, st, p);
   else
-    hipLaunchKernelGGL(gsc::gemm_scatter_kernel<RMSN_F16>, dim3((unsigned)tiles),
-                       dim3(gsc::kThreads), 0, st, p);
+    hipLaunchKernelGGL((gsc::gemm_scatter_kernel<RMSN_F16, gsc::BN_NARROW>), grid, block, 0, st, p);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
     char msg[200];

@@ -369,14 +369,20 @@ def gemm_shapes_summary(argv) -> int:
         f.write("# GEMM with the scatter epilogue across shapes (bf16)\n\n")
         f.write("Command: `python bench.py --gemm-shapes` (HIP events over back-to-back launches, "
                 "operands rotated over about 1 GiB; the library column is torch.matmul, i.e. "
-                "hipBLASLt's plain GEMM, on the same operands).  256 x 256 output tiles, one "
-                "workgroup each on 256 CUs.\n\n")
-        f.write("| m | n | k | chunks | tiles | kernel µs | TFLOP/s | % of 2.5 PFLOP/s | "
-                "hipBLASLt µs | hipBLASLt TFLOP/s | kernel ÷ hipBLASLt |\n"
-                "|---|---|---|---|---|---|---|---|---|---|---|\n")
+                "hipBLASLt's plain GEMM, on the same operands).  Output tiles of 256 rows by "
+                "256 or 128 columns, one workgroup each on 256 CUs; the automatic width is 128 "
+                "when 256-wide tiles would number at most 128.\n\n")
+        f.write("| m | n | k | chunks | automatic width | tiles | kernel µs | TFLOP/s | "
+                "% of 2.5 PFLOP/s | 256-wide µs | 128-wide µs | hipBLASLt µs | "
+                "hipBLASLt TFLOP/s | kernel ÷ hipBLASLt |\n"
+                "|---|---|---|---|---|---|---|---|---|---|---|---|---|---|\n")
         for r in rows:
-            f.write(f"| {r['m']} | {r['n']} | {r['k']} | {r['world']} | {r['tiles']} | "
-                    f"{r['us']:.1f} | {r['tflops']:.0f} | {100 * r['tflops'] / 2500:.1f} | "
+            bw = r.get("by_tile_n", {})
+            wide = f"{bw['256']['us']:.1f}" if "256" in bw else "–"
+            narrow = f"{bw['128']['us']:.1f}" if "128" in bw else "–"
+            f.write(f"| {r['m']} | {r['n']} | {r['k']} | {r['world']} | {r.get('tile_n', 256)} | "
+                    f"{r['tiles']} | {r['us']:.1f} | {r['tflops']:.0f} | "
+                    f"{100 * r['tflops'] / 2500:.1f} | {wide} | {narrow} | "
                     f"{r['library_us']:.1f} | {r['library_tflops']:.0f} | "
                     f"{r['library_us'] / r['us']:.2f} |\n")
         f.write(f"\nKernel sources sha256: `{source_hash('gemm_scatter')}`\n")

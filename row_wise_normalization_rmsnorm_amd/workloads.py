@@ -137,5 +137,9 @@ GEMM_WORKLOADS = {
         "gemm_scatter_bf16_4096x8192x3584_w8", "bf16", 4096, 8192, 3584, 8),
     "gemm_scatter_f16_4096x8192x3584_w8": GemmWorkload(
         "gemm_scatter_f16_4096x8192x3584_w8", "f16", 4096, 8192, 3584, 8),
+    # The same layer at 1024 tokens: 128 tiles of 256 x 256 would leave half
+    # of the 256 CUs idle, so this size takes the 128-wide tiles.
+    "gemm_scatter_bf16_1024x8192x3584_w8": GemmWorkload(
+        "gemm_scatter_bf16_1024x8192x3584_w8", "bf16", 1024, 8192, 3584, 8),
 }
 GEMM_HEADLINE = "gemm_scatter_bf16_4096x8192x3584_w8"

@@ -3,7 +3,7 @@ exports what include/gemm_scatter.h declares, invalid arguments are rejected
 with the documented codes before any HIP call, and the tile schedule puts the
 other ranks' chunks first and the local chunk last (the order the oracle
 states), spreads each round of tiles over the eight XCDs in contiguous runs,
-and covers every tile exactly once."""
+and covers every tile exactly once, at either tile width."""
 from __future__ import annotations
 
 import ctypes
@@ -14,7 +14,8 @@ import oracle
 from row_wise_normalization_rmsnorm_amd import binding as B
 from tests.test_capi_cpu import FAKE, declared
 
-TM, TN = B.GEMM_SCATTER_TILE_M, B.GEMM_SCATTER_TILE_N
+TM = B.GEMM_SCATTER_TILE_M
+WIDTHS = (B.GEMM_SCATTER_TILE_N, B.GEMM_SCATTER_TILE_N_NARROW)
 
 
 def test_exports_every_declared_function():
@@ -26,9 +27,27 @@ def test_exports_every_declared_function():
 
 def test_tile_count():
     f = B.lib().gemm_scatter_tiles
-    assert f(4096, 8192) == 16 * 32
-    assert f(1, 1) == 1 and f(0, 5) == 0 and f(257, 256) == 2 and f(256, 257) == 2
-    assert f(-1, 4) == -1 and f(4, 1 << 31) == -1
+    assert f(4096, 8192, 256) == 16 * 32 and f(4096, 8192, 128) == 16 * 64
+    assert f(4096, 8192, 0) == 16 * 32                  # 512 wide tiles: stays wide
+    assert f(1, 1, 256) == 1 and f(0, 5, 256) == 0 and f(257, 256, 256) == 2
+    assert f(256, 257, 256) == 2 and f(256, 257, 128) == 3 and f(256, 129, 128) == 2
+    assert f(-1, 4, 0) == -1 and f(4, 1 << 31, 0) == -1
+    assert f(256, 256, 64) == -1 and f(256, 256, -1) == -1 and f(256, 256, 512) == -1
+
+
+def test_automatic_tile_width():
+    """Narrow tiles exactly when 256-wide ones would number at most
+    GEMM_SCATTER_NARROW_MAX_TILES (128, half of MI355X's 256 CUs)."""
+    w = B.gemm_scatter_tile_n
+    assert B.GEMM_SCATTER_NARROW_MAX_TILES == 128
+    assert w(1024, 8192) == 128          # 4 x 32 = 128 wide tiles
+    assert w(2048, 8192) == 256          # 256 wide tiles fill the GPU
+    assert w(1024, 8193) == 256          # 4 x 33 = 132
+    assert w(256 * 128, 256) == 128 and w(256 * 129, 256) == 256
+    assert w(1, 1) == 128 and w(0, 0) == 128
+    assert w(-1, 5) == -1 and w(5, 1 << 31) == -1
+    for m, n in [(1024, 8192), (4096, 8192), (300, 77), (8 * 700, 2900)]:
+        assert B.gemm_scatter_tiles(m, n) == B.gemm_scatter_tiles(m, n, w(m, n))
 
 
 def call(**kw):
@@ -39,14 +58,15 @@ def call(**kw):
     if d is None:
         d = [FAKE + (q + 1) * (1 << 28) for q in range(world)]
     args = dict(ldd=64, rank=0, a=FAKE + (1 << 32), lda=64, b=FAKE + (2 << 32), ldb=64, c=None,
-                ldc=0, alpha=1.0, beta=0.0, m=128, n=64, k=64, dtype=2, flags=None, epoch=1)
+                ldc=0, alpha=1.0, beta=0.0, m=128, n=64, k=64, dtype=2, flags=None, epoch=1,
+                tile_n=0)
     args.update(kw)
     arr = (ctypes.c_void_p * max(len(d), 1))(*d)
     return B.lib().gemm_scatter_fwd(arr, args["ldd"], world, args["rank"], args["a"], args["lda"],
                                     args["b"], args["ldb"], args["c"], args["ldc"],
                                     ctypes.c_float(args["alpha"]), ctypes.c_float(args["beta"]),
                                     args["m"], args["n"], args["k"], args["dtype"], args["flags"],
-                                    ctypes.c_uint32(args["epoch"]), None)
+                                    ctypes.c_uint32(args["epoch"]), args["tile_n"], None)
 
 
 def test_error_codes():
@@ -65,6 +85,7 @@ def test_error_codes():
     assert call(dst=[FAKE + 1, FAKE + (1 << 28)]) == -2         # dst misaligned
     assert call(flags=FAKE + (5 << 32) + 2) == -2               # flags misaligned
     assert call(lda=1 << 22, k=64) == -2                        # 255 * lda + k too large
+    assert call(tile_n=64) == -2 and call(tile_n=-1) == -2      # width not 0, 128 or 256
     # overlaps: a dst chunk over a, over another chunk, over flags
     assert call(dst=[FAKE + (1 << 32), FAKE + (1 << 28)]) == -5
     assert call(dst=[FAKE + (1 << 28), FAKE + (1 << 28) + 64]) == -5
@@ -72,28 +93,31 @@ def test_error_codes():
     assert call(c=FAKE + (2 << 28), ldc=64) == -5
     # nothing to do: valid, and nothing launched
     assert call(m=0) == 0 and call(n=0) == 0
+    assert call(m=0, tile_n=128) == 0 and call(n=0, tile_n=256) == 0
 
 
-def tile_chunk(tile: int, m: int, n: int, world: int) -> int:
-    tn = -(-n // TN)
+def tile_chunk(tile: int, m: int, n: int, world: int, width: int) -> int:
+    tn = -(-n // width)
     return ((tile // tn) * TM) // (m // world)
 
 
 GROUP_ROWS = 8  # tile-rows per schedule group
 
 
+@pytest.mark.parametrize("width", WIDTHS)
 @pytest.mark.parametrize("m,n,world", [(4096, 8192, 8), (4096, 8192, 1), (8192, 4096, 8),
                                        (1024, 1024, 4), (777 * 8, 300, 8), (256, 256, 2),
-                                       (2048, 2560, 16), (24576, 2048, 8), (4096, 8192, 2)])
-def test_schedule_is_remote_first_and_complete(m, n, world):
-    tiles = B.gemm_scatter_tiles(m, n)
-    tn = -(-n // TN)
+                                       (2048, 2560, 16), (24576, 2048, 8), (4096, 8192, 2),
+                                       (1024, 8192, 8)])
+def test_schedule_is_remote_first_and_complete(m, n, world, width):
+    tiles = B.gemm_scatter_tiles(m, n, width)
+    tn = -(-n // width)
     for rank in range(world):
-        wg, pos = B.gemm_scatter_schedule(m, n, world, rank)
+        wg, pos = B.gemm_scatter_schedule(m, n, world, rank, width)
         assert sorted(wg) == list(range(tiles)) and sorted(pos) == list(range(tiles))
         order = oracle.gemm_scatter_chunk_order(world, rank)
         rank_of = {q: i for i, q in enumerate(order)}
-        seq = [rank_of[tile_chunk(t, m, n, world)] for t in pos]
+        seq = [rank_of[tile_chunk(t, m, n, world, width)] for t in pos]
         # the local chunk's tiles come last
         local = [i for i, q in enumerate(seq) if q == world - 1]
         assert not local or local == list(range(tiles - len(local), tiles)), (m, n, world, rank)
@@ -111,9 +135,10 @@ def test_schedule_is_remote_first_and_complete(m, n, world):
             assert cols == sorted(cols)
 
 
-def test_workgroups_are_dealt_to_xcds_in_contiguous_runs():
+@pytest.mark.parametrize("width", WIDTHS)
+def test_workgroups_are_dealt_to_xcds_in_contiguous_runs(width):
     m, n, world = 4096, 8192, 8
-    wg, pos = B.gemm_scatter_schedule(m, n, world, 3)
+    wg, pos = B.gemm_scatter_schedule(m, n, world, 3, width)
     at = {t: s for s, t in enumerate(pos)}
     positions = [at[t] for t in wg]
     rnd = 8 * 32
@@ -140,13 +165,15 @@ def test_schedule_random_shapes():
         m = world * rng.randint(1, 700)
         n = rng.randint(1, 3000)
         rank = rng.randrange(world)
-        tiles = B.gemm_scatter_tiles(m, n)
-        tn = -(-n // TN)
-        wg, pos = B.gemm_scatter_schedule(m, n, world, rank)
+        width = rng.choice((0,) + WIDTHS)
+        tiles = B.gemm_scatter_tiles(m, n, width)
+        used = width or B.gemm_scatter_tile_n(m, n)
+        tn = -(-n // used)
+        wg, pos = B.gemm_scatter_schedule(m, n, world, rank, width)
         assert sorted(wg) == list(range(tiles)) == sorted(pos)
         order = oracle.gemm_scatter_chunk_order(world, rank)
         rank_of = {q: i for i, q in enumerate(order)}
-        seq = [rank_of[tile_chunk(t, m, n, world)] for t in pos]
+        seq = [rank_of[tile_chunk(t, m, n, world, used)] for t in pos]
         local = [i for i, q in enumerate(seq) if q == world - 1]
         assert not local or local == list(range(tiles - len(local), tiles)), (m, n, world, rank)
         remote = seq[:tiles - len(local)]

@@ -13,7 +13,9 @@ and 11 for fp16 (half an ulp of the stored value) and tiny the smallest
 normal of the type.  Beyond the bound, most elements must equal the oracle's
 rounded value exactly (they differ only where the fp32 error straddles a
 rounding boundary).  NaN positions and infinities match exactly.  Guard
-bands around every output chunk must stay untouched.
+bands around every output chunk must stay untouched.  Both tile widths (256
+and 128 columns) run the same products in the same k order, so their
+outputs must be bitwise equal.
 """
 from __future__ import annotations
 
@@ -35,6 +37,7 @@ TORCH = {"bf16": torch.bfloat16, "f16": torch.float16}
 P_BITS = {"bf16": 8, "f16": 11}
 TINY = {"bf16": 2.0 ** -126, "f16": 2.0 ** -14}
 GUARD = 0x7E5A  # a NaN pattern in both formats: never a computed value here
+WIDTHS = (B.GEMM_SCATTER_TILE_N, B.GEMM_SCATTER_TILE_N_NARROW)
 
 
 def say(*a):
@@ -45,7 +48,7 @@ def st(t: torch.Tensor) -> np.ndarray:
     return I.to_storage(t)
 
 
-def run(a, b, c, alpha, beta, world, rank=0, ldd_pad=0, flags=None, epoch=0, col=4):
+def run(a, b, c, alpha, beta, world, rank=0, ldd_pad=0, flags=None, epoch=0, col=4, tile_n=0):
     """Launch into guarded chunk buffers; returns (assembled [m, n] storage,
     the raw buffer).  Each chunk sits at column ``col`` of a [rows + 2,
     n + ldd_pad + 8 + col] block whose first and last rows and other columns
@@ -57,7 +60,7 @@ def run(a, b, c, alpha, beta, world, rank=0, ldd_pad=0, flags=None, epoch=0, col
     buf = torch.full((world, rows + 2, width), GUARD, dtype=torch.int16, device=DEV)
     bufv = buf.view(a.dtype)
     dst = [bufv[q, 1:rows + 1, col:col + n] for q in range(world)]
-    B.gemm_scatter_fwd(dst, a, b, c, alpha, beta, rank, flags, epoch)
+    B.gemm_scatter_fwd(dst, a, b, c, alpha, beta, rank, flags, epoch, tile_n=tile_n)
     torch.cuda.synchronize()
     host = buf.cpu()
     inner = host[:, 1:rows + 1, col:col + n]
@@ -135,16 +138,24 @@ SHAPES = [  # m, n, k, world, with_c
 @pytest.mark.parametrize("shape", SHAPES, ids=[f"{s[0]}x{s[1]}x{s[2]}w{s[3]}{'c' if s[4] else ''}"
                                                for s in SHAPES])
 def test_parity(dtype, shape):
-    """Each shape with 8-byte and with 16-byte aligned output rows (the
-    interior tiles of the latter take the LDS-staged stores)."""
+    """Each shape at both tile widths, with 8-byte and with 16-byte aligned
+    output rows (the interior tiles of the latter take the LDS-staged
+    stores)."""
     m, n, k, world, with_c = shape
     a, b, c = make(dtype, m, n, k, with_c, seed=m + n + k)
     alpha, beta = (0.5, -1.25) if with_c else (1.0, 0.0)
     want, y, mag = oracle_rows(a, b, c, alpha, beta, world, dtype)
-    for col, pad in ((4, 0), (8, (-(n + 16)) % 8)):
-        say(f"[gpu] gemm_scatter {dtype} m={m} n={n} k={k} world={world} c={with_c} col={col}")
-        got, _ = run(a, b, c, alpha, beta, world, rank=world - 1, ldd_pad=pad, col=col)
-        compare(got, want, y, mag, k, dtype, f"{dtype} {shape} col {col}")
+    first = None
+    for tile_n in WIDTHS:
+        for col, pad in ((4, 0), (8, (-(n + 16)) % 8)):
+            say(f"[gpu] gemm_scatter {dtype} m={m} n={n} k={k} world={world} c={with_c} "
+                f"col={col} tile_n={tile_n}")
+            got, _ = run(a, b, c, alpha, beta, world, rank=world - 1, ldd_pad=pad, col=col,
+                         tile_n=tile_n)
+            compare(got, want, y, mag, k, dtype, f"{dtype} {shape} col {col} tile_n {tile_n}")
+            if first is None:
+                first = got
+            assert np.array_equal(got, first), "tile widths or store paths differ"
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
@@ -152,10 +163,10 @@ def test_strided_operands(dtype):
     """Row strides wider than the rows for A, B, C and the output (one odd,
     which takes the element-wise store path)."""
     m, n, k, world = 384, 264, 200, 4
-    for ldd_pad, ldc_pad in ((8, 3), (3, 8)):
-        say(f"[gpu] strided {dtype} ldd_pad={ldd_pad} ldc_pad={ldc_pad}")
+    for (ldd_pad, ldc_pad), tile_n in zip(((8, 3), (3, 8), (8, 8), (3, 3)), WIDTHS * 2):
+        say(f"[gpu] strided {dtype} ldd_pad={ldd_pad} ldc_pad={ldc_pad} tile_n={tile_n}")
         a, b, c = make(dtype, m, n, k, True, seed=7, lda_pad=8, ldb_pad=24, ldc_pad=ldc_pad)
-        got, _ = run(a, b, c, 1.5, 0.75, world, rank=1, ldd_pad=ldd_pad)
+        got, _ = run(a, b, c, 1.5, 0.75, world, rank=1, ldd_pad=ldd_pad, tile_n=tile_n)
         want, y, mag = oracle_rows(a, b, c, 1.5, 0.75, world, "bf16" if dtype == "bf16" else "f16")
         compare(got, want, y, mag, k, dtype, f"strided {dtype} {ldd_pad}/{ldc_pad}")
 
@@ -182,20 +193,22 @@ def test_k_zero_gives_beta_c():
     compare(got, want, y, mag, 0, "bf16", "k = 0", min_exact=1.0)
 
 
-def test_flags_epoch_and_rank_independence():
+@pytest.mark.parametrize("tile_n", (0,) + WIDTHS)
+def test_flags_epoch_and_rank_independence(tile_n):
     """Every tile's flag gets the epoch (slots past the tiles stay as they
     were), and the values do not depend on the rank (only the order of the
     tiles does)."""
     m, n, k, world = 1024, 768, 192, 8
     a, b, c = make("bf16", m, n, k, False, seed=11)
-    tiles = B.gemm_scatter_tiles(m, n)
+    tiles = B.gemm_scatter_tiles(m, n, tile_n)
     flags = torch.full((tiles + 5,), 3, dtype=torch.int32, device=DEV)
-    say("[gpu] flags")
-    ref, _ = run(a, b, None, 1.0, 0.0, world, rank=0, flags=flags, epoch=41)
+    say(f"[gpu] flags tile_n={tile_n} tiles={tiles}")
+    ref, _ = run(a, b, None, 1.0, 0.0, world, rank=0, flags=flags, epoch=41, tile_n=tile_n)
     f = flags.cpu()
     assert bool((f[:tiles] == 41).all()) and bool((f[tiles:] == 3).all())
     for rank in (3, 7):
-        got, _ = run(a, b, None, 1.0, 0.0, world, rank=rank, flags=flags, epoch=42 + rank)
+        got, _ = run(a, b, None, 1.0, 0.0, world, rank=rank, flags=flags, epoch=42 + rank,
+                     tile_n=tile_n)
         assert np.array_equal(got, ref), rank
         assert bool((flags.cpu()[:tiles] == 42 + rank).all())
 
@@ -206,7 +219,7 @@ def test_full_size_sampled(name):
     sampled rows of every chunk against the oracle, and a second launch
     bitwise equal to the first."""
     w = GEMM_WORKLOADS[name]
-    say(f"[gpu] full size {w.describe()}")
+    say(f"[gpu] full size {w.describe()} (tile width {B.gemm_scatter_tile_n(w.m, w.n)})")
     d = I.gemm_inputs(w)
     a, b = d["a"].to(DEV), d["b"].to(DEV)
     c = d["c"].to(DEV) if d["c"] is not None else None
@@ -215,6 +228,9 @@ def test_full_size_sampled(name):
     assert np.array_equal(got, again), "two launches differ"
     other, _ = run(a, b, c, w.alpha, w.beta, w.world, rank=w.rank, col=4)
     assert np.array_equal(got, other), "staged and direct stores differ"
+    for tile_n in WIDTHS:
+        wide, _ = run(a, b, c, w.alpha, w.beta, w.world, rank=w.rank, col=8, tile_n=tile_n)
+        assert np.array_equal(got, wide), f"tile width {tile_n} differs"
     chunk = w.m // w.world
     rows = sorted({q * chunk + off for q in range(w.world) for off in (0, chunk // 2 + 3)}
                   | {w.m - 1, 255, 256})
@@ -325,8 +341,9 @@ def test_random_calls():
             a, b = a.contiguous(), b.contiguous()
         col = int(rng.choice([4, 8]))
         pad = (-(n + 8 + col)) % 8 if col == 8 else int(rng.integers(0, 4))
+        tile_n = int(rng.choice((0,) + WIDTHS))
         say(f"[gpu] random #{i}: {dtype} m={m} n={n} k={k} world={world} rank={rank} "
-            f"c={with_c} col={col}")
-        got, _ = run(a, b, c, alpha, beta, world, rank=rank, ldd_pad=pad, col=col)
+            f"c={with_c} col={col} tile_n={tile_n}")
+        got, _ = run(a, b, c, alpha, beta, world, rank=rank, ldd_pad=pad, col=col, tile_n=tile_n)
         want, y, mag = oracle_rows(a, b, c, alpha, beta, world, dtype)
         compare(got, want, y, mag, k, dtype, f"random #{i}", min_exact=0.6)
