@@ -259,7 +259,7 @@ def report_summary(argv) -> int:
                 one = cb.get("single_thread", {})
                 st = stats.get(w, {})
                 par = (f"error / bound max {st['max_error_over_bound']:.2g}, "
-                       f"{100 * st['min_equal_frac']:.1f}%+ equal to the oracle's rounding "
+                       f"{100 * st['min_equal_frac']:.2f}%+ equal to the oracle's rounding "
                        f"({st['rows_checked']} rows)" if "max_error_over_bound" in st
                        else "see tests")
                 lib = r.get("library_context", {})
