@@ -298,7 +298,8 @@ def gemm_bench(a, name: str) -> int:
 
 
 GEMM_SHAPES = [  # (m tokens, n hidden, k intermediate slice, world)
-    (1024, 8192, 3584, 8), (2048, 8192, 3584, 8), (4096, 8192, 3584, 8), (8192, 8192, 3584, 8),
+    (1024, 8192, 3584, 8), (1536, 8192, 3584, 8), (2048, 8192, 3584, 8), (2560, 8192, 3584, 8),
+    (3072, 8192, 3584, 8), (4096, 8192, 3584, 8), (5120, 8192, 3584, 8), (8192, 8192, 3584, 8),
     (4096, 4096, 1792, 8), (4096, 8192, 1024, 8), (4096, 8192, 7168, 8), (16384, 8192, 3584, 8),
 ]
 

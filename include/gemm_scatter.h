@@ -69,10 +69,12 @@ extern "C" {
 #define GEMM_SCATTER_TILE_M 256
 #define GEMM_SCATTER_TILE_N 256
 #define GEMM_SCATTER_TILE_N_NARROW 128
-/* the automatic width is narrow when 256-wide tiles would number at most
- * this many: half the compute units of an MI355X, which the narrow tiling
- * still fills in one round of workgroups */
-#define GEMM_SCATTER_NARROW_MAX_TILES 128
+/* The automatic width counts whole rounds of workgroups over the compute
+ * units of an MI355X: a round of 256 x 128 tiles takes about 0.55 of the time
+ * of a round of 256 x 256 tiles, so the narrow width is taken when
+ * 11 * ceil(T128 / CUS) < 20 * ceil(T256 / CUS), T the tile count at each
+ * width. */
+#define GEMM_SCATTER_CUS 256
 
 /*
  * gemm_scatter_fwd -- the epilogue-scattered product above.  Returns RMSN_OK,
@@ -84,10 +86,8 @@ int gemm_scatter_fwd(void* const* dst, int64_t ldd, int world, int rank, const v
                      float alpha, float beta, int64_t m, int64_t n, int64_t k, int dtype,
                      uint32_t* flags, uint32_t epoch, int tile_n, void* stream);
 
-/* gemm_scatter_tile_n -- the tile width tile_n = 0 takes for m x n:
- * GEMM_SCATTER_TILE_N_NARROW when ceil(m / 256) * ceil(n / 256) is at most
- * GEMM_SCATTER_NARROW_MAX_TILES, else GEMM_SCATTER_TILE_N; -1 if m or n is
- * negative or too large. */
+/* gemm_scatter_tile_n -- the tile width tile_n = 0 takes for m x n, by the
+ * rule beside GEMM_SCATTER_CUS; -1 if m or n is negative or too large. */
 int gemm_scatter_tile_n(int64_t m, int64_t n);
 
 /* gemm_scatter_tiles -- number of output tiles (and flag slots) for m x n at

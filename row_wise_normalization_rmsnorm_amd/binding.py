@@ -32,7 +32,7 @@ GEMM_SCATTER_WORLD_MAX = 16
 GEMM_SCATTER_TILE_M = 256
 GEMM_SCATTER_TILE_N = 256
 GEMM_SCATTER_TILE_N_NARROW = 128
-GEMM_SCATTER_NARROW_MAX_TILES = 128
+GEMM_SCATTER_CUS = 256
 
 # block all-reduce sum (include/block_sum.h)
 BRS_DTYPE_CODE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2,

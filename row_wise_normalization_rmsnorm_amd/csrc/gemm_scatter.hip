@@ -17,10 +17,11 @@
 //     memory or the barrier (measured 188.7 us against 204.6 us for four
 //     waves of 128 x 128 blocks on the 4096 x 8192 x 3584 bf16 product, one
 //     set of operands).
-//   - Products too small to give every CU a 256 x 256 tile (at most 128 such
-//     tiles) take 256 x 128 tiles instead: twice the workgroups, each wave a
-//     64 x 64 block of 4 x 4 products.  Both widths accumulate every output
-//     in the same k order, so they give bitwise equal results.
+//   - 256 x 128 tiles, twice the workgroups with each wave a 64 x 64 block
+//     of 4 x 4 products, for products whose 256 x 256 tiles would leave much
+//     of the last round of workgroups idle (1024 tokens: 128 tiles on 256
+//     CUs).  Both widths accumulate every output in the same k order, so
+//     they give bitwise equal results.
 //   - The matrix-core operands are swapped (the weight rows feed the first
 //     operand, the activation rows the second), so each lane's four
 //     accumulator values are four consecutive output columns of one row.
@@ -534,8 +535,11 @@ namespace {
 int resolve_tile_n(int64_t m, int64_t n, int tile_n) {
   if (tile_n == gsc::BN || tile_n == gsc::BN_NARROW) return tile_n;
   if (tile_n != 0) return -1;
-  const int64_t wide = ((m + gsc::BM - 1) / gsc::BM) * ((n + gsc::BN - 1) / gsc::BN);
-  return wide <= GEMM_SCATTER_NARROW_MAX_TILES ? gsc::BN_NARROW : gsc::BN;
+  const int64_t tiles_m = (m + gsc::BM - 1) / gsc::BM;
+  const int64_t wide = tiles_m * ((n + gsc::BN - 1) / gsc::BN);
+  const int64_t narrow = tiles_m * ((n + gsc::BN_NARROW - 1) / gsc::BN_NARROW);
+  const int64_t cus = GEMM_SCATTER_CUS;
+  return 11 * ((narrow + cus - 1) / cus) < 20 * ((wide + cus - 1) / cus) ? gsc::BN_NARROW : gsc::BN;
 }
 
 }  // namespace

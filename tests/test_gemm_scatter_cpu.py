@@ -36,17 +36,30 @@ def test_tile_count():
 
 
 def test_automatic_tile_width():
-    """Narrow tiles exactly when 256-wide ones would number at most
-    GEMM_SCATTER_NARROW_MAX_TILES (128, half of MI355X's 256 CUs)."""
+    """The automatic width counts rounds of workgroups over 256 CUs: narrow
+    exactly when 11 * ceil(T128 / 256) < 20 * ceil(T256 / 256).  The cases are
+    the measured bf16 shapes (n = 8192, k = 3584) and edges of the rule."""
     w = B.gemm_scatter_tile_n
-    assert B.GEMM_SCATTER_NARROW_MAX_TILES == 128
-    assert w(1024, 8192) == 128          # 4 x 32 = 128 wide tiles
-    assert w(2048, 8192) == 256          # 256 wide tiles fill the GPU
-    assert w(1024, 8193) == 256          # 4 x 33 = 132
+    assert B.GEMM_SCATTER_CUS == 256
+    measured = {1024: 128, 1536: 256, 2048: 256, 2560: 128, 3072: 128, 4096: 256,
+                5120: 128, 8192: 256, 16384: 256}
+    for m, width in measured.items():
+        assert w(m, 8192) == width, m
+    assert w(1024, 8193) == 256          # 4 x 33 = 132 wide tiles, 4 x 65 = 260 narrow
     assert w(256 * 128, 256) == 128 and w(256 * 129, 256) == 256
-    assert w(1, 1) == 128 and w(0, 0) == 128
+    assert w(1, 1) == 128 and w(0, 0) == 256      # nothing to launch: no round either way
     assert w(-1, 5) == -1 and w(5, 1 << 31) == -1
-    for m, n in [(1024, 8192), (4096, 8192), (300, 77), (8 * 700, 2900)]:
+
+    def rule(m, n):
+        tm = -(-m // 256)
+        wide, narrow = tm * -(-n // 256), tm * -(-n // 128)
+        return 128 if 11 * -(-narrow // 256) < 20 * -(-wide // 256) else 256
+
+    import random
+    rng = random.Random(5)
+    for _ in range(300):
+        m, n = rng.randint(0, 40000), rng.randint(0, 20000)
+        assert w(m, n) == rule(m, n), (m, n)
         assert B.gemm_scatter_tiles(m, n) == B.gemm_scatter_tiles(m, n, w(m, n))
 
 
