@@ -347,3 +347,68 @@ def test_random_calls():
         got, _ = run(a, b, c, alpha, beta, world, rank=rank, ldd_pad=pad, col=col, tile_n=tile_n)
         want, y, mag = oracle_rows(a, b, c, alpha, beta, world, dtype)
         compare(got, want, y, mag, k, dtype, f"random #{i}", min_exact=0.6)
+
+
+def test_graph_capture_gemm_then_add_rmsnorm():
+    """The reduce-scatter pipeline captured in one HIP graph: four emulated
+    ranks' GEMMs (both tile widths, one with tile flags) scatter into receive
+    buffers, then every receiving rank sums its four chunks with its residual
+    and normalises (add_rmsnorm_fwd, K = 4).  Each replay, with eager resets
+    and poisoning in between, equals the eager run bit for bit, flags
+    included."""
+    world, m, n, k = 4, 512, 1024, 256
+    chunk = m // world
+    ops = [make("bf16", m, n, k, False, seed=300 + r)[:2] for r in range(world)]
+    widths = [0, 256, 128, 0]
+    res0 = I.matrix(31, I.RESIDUAL_ID, m, n, 1.0, "bf16").to(DEV)
+    gam = I.matrix(31, I.GAMMA_ID, 1, n, 0.25, "bf16").reshape(n).to(DEV) + 1.0
+    tiles = B.gemm_scatter_tiles(m, n, widths[1])
+
+    def step(recv, res, out, flags):
+        for r, ((a, b), tn) in enumerate(zip(ops, widths)):
+            B.gemm_scatter_fwd([recv[q, r] for q in range(world)], a, b, rank=r, tile_n=tn,
+                               flags=flags if r == 1 else None, epoch=77)
+        for q in range(world):
+            B.add_rmsnorm_fwd(out[q], res[q], [recv[q, r] for r in range(world)], gam, 1e-5)
+
+    def buffers():
+        return (torch.empty(world, world, chunk, n, dtype=torch.bfloat16, device=DEV),
+                torch.empty(world, chunk, n, dtype=torch.bfloat16, device=DEV),
+                torch.empty(world, chunk, n, dtype=torch.bfloat16, device=DEV),
+                torch.zeros(tiles, dtype=torch.int32, device=DEV))
+
+    recv_e, res_e, out_e, flags_e = buffers()
+    res_e.copy_(res0.view(world, chunk, n))
+    step(recv_e, res_e, out_e, flags_e)
+    torch.cuda.synchronize()
+    assert bool((flags_e == 77).all())
+    recv, res, out, flags = buffers()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        res.copy_(res0.view(world, chunk, n))
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=side):
+            step(recv, res, out, flags)
+    torch.cuda.synchronize()
+    say("[gpu] graph: 4 GEMMs + 4 add_rmsnorm captured")
+    for rep in range(4):
+        res.copy_(res0.view(world, chunk, n))     # eager work between replays
+        recv.fill_(float("nan"))
+        out.fill_(float("nan"))
+        flags.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(recv.view(torch.int16), recv_e.view(torch.int16)), rep
+        assert torch.equal(res.view(torch.int16), res_e.view(torch.int16)), rep
+        assert torch.equal(out.view(torch.int16), out_e.view(torch.int16)), rep
+        assert torch.equal(flags, flags_e), rep
+    # the eager run itself against the oracle for one receiving rank
+    q = 2
+    parts = [st(recv_e[q, r].cpu()) for r in range(world)]
+    o_out, o_res, _ = oracle.add_rmsnorm(parts, st(res0.view(world, chunk, n)[q].cpu()),
+                                         st(gam.cpu()), 1e-5, "bf16")
+    assert np.array_equal(st(res_e[q].cpu()), o_res)
+    assert int(ind.ulp_distance(st(out_e[q].cpu()), o_out, "bf16").max()) <= 2
