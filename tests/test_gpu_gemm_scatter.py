@@ -412,3 +412,34 @@ def test_graph_capture_gemm_then_add_rmsnorm():
                                          st(gam.cpu()), 1e-5, "bf16")
     assert np.array_equal(st(res_e[q].cpu()), o_res)
     assert int(ind.ulp_distance(st(out_e[q].cpu()), o_out, "bf16").max()) <= 2
+
+
+def test_operand_offsets_past_4gib():
+    """A of 65536 x 33280 bf16 (4.36 GB, drawn on the device): rows whose
+    byte offset passes 2^31 and 2^32, in every chunk, against the oracle row
+    by row (each row's values do not depend on the chunk split), at both tile
+    widths, which must agree bit for bit."""
+    m, n, k, world = 65536, 264, 33280, 8
+    chunk = m // world
+    w = I.case("bf16", m, k, 1, seed=71, std=1.0)
+    a = I.device_tensor(w, I.GEMM_A_ID, DEV)
+    b = I.matrix(71, I.GEMM_B_ID, n, k, (8.0 * k) ** -0.5, "bf16").to(DEV)
+    assert a.numel() * 2 > 1 << 32
+    say(f"[gpu] offsets past 4 GiB: A {tuple(a.shape)}, {a.numel() * 2 / 2**30:.2f} GiB")
+    got = None
+    for tile_n in WIDTHS:
+        g, _ = run(a, b, None, 1.0, 0.0, world, rank=3, col=8, tile_n=tile_n)
+        if got is None:
+            got = g
+        assert np.array_equal(g, got), f"tile width {tile_n} differs"
+    row_bytes = k * 2
+    rows = sorted({0, chunk - 1, chunk, (1 << 31) // row_bytes, (1 << 31) // row_bytes + 1,
+                   (1 << 32) // row_bytes + 1, m - 2, m - 1})
+    bc = st(b.cpu())
+    for r in rows:
+        ar = st(a[r:r + 1].cpu())
+        chunks, y, mag = oracle.gemm_scatter(ar, bc, None, 1.0, 0.0, 1, "bf16", want_f64=True)
+        compare(got[r:r + 1], chunks[0], y, mag, k, "bf16", f"row {r} (byte offset {r * row_bytes:#x})",
+                min_exact=0.7)
+    del a
+    torch.cuda.empty_cache()
