@@ -168,3 +168,22 @@ def test_random_block_sums():
         if n:
             xd.copy_(x.to(DEV))
         check(x, dtype, f"random #{t}", offset_bytes=off_e * s, x_dev=xd)
+
+
+def test_more_than_2_31_elements():
+    """2^31 + 77 int8 elements (2 GiB) from an odd base offset: element and
+    chunk indices past the int32 range, the head and the ragged tail; the
+    wrapped int32 sum must equal the oracle's exactly."""
+    n = (1 << 31) + 77
+    g = torch.Generator().manual_seed(91)
+    block = torch.randint(-128, 128, (1 << 20,), generator=g, dtype=torch.int8)
+    x = torch.empty(n + 16, dtype=torch.int8)
+    body = x[5:5 + n]
+    reps = n >> 20
+    body[:reps << 20].view(reps, 1 << 20).copy_(block.expand(reps, 1 << 20))
+    body[reps << 20:] = block[:n - (reps << 20)]
+    xd = torch.empty(n + 16, dtype=torch.int8, device=DEV)
+    xd.copy_(x)
+    check(body, "i8", "past 2^31 elements", offset_bytes=5, x_dev=xd[5:5 + n])
+    del xd
+    torch.cuda.empty_cache()
