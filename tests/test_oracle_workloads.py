@@ -103,6 +103,16 @@ def _fingerprint(w):
     return h.hexdigest()
 
 
+def _gemm_fingerprint(w):
+    """rows 0..47 and the last row of a GEMM workload's A and B (and C)."""
+    h = hashlib.sha256()
+    for tid, rows, cols, std in ((I.GEMM_A_ID, w.m, w.k, w.a_std), (I.GEMM_B_ID, w.n, w.k, w.b_std)) + \
+            (((I.GEMM_C_ID, w.m, w.n, 1.0),) if w.with_c else ()):
+        idx = list(range(min(rows, 48))) + [rows - 1]
+        h.update(I.to_storage(I.matrix(w.seed, tid, rows, cols, std, w.dtype, row_idx=idx)).tobytes())
+    return h.hexdigest()
+
+
 def test_input_generator_fingerprint():
     """The seeded inputs are the recorded ones (tests/golden/input_fingerprints.json,
     written by tests/golden/make_input_fingerprints.py)."""
@@ -110,6 +120,16 @@ def test_input_generator_fingerprint():
         want = json.load(f)["fingerprints"]
     for name, w in WORKLOADS.items():
         assert _fingerprint(w) == want[name], name
+
+
+def test_gemm_input_generator_fingerprint():
+    """The GEMM workloads' seeded operands are the recorded ones (same file)."""
+    from row_wise_normalization_rmsnorm_amd.workloads import GEMM_WORKLOADS
+    with open(os.path.join(GOLDEN, "input_fingerprints.json")) as f:
+        want = json.load(f)["gemm_fingerprints"]
+    assert set(want) == set(GEMM_WORKLOADS)
+    for name, w in GEMM_WORKLOADS.items():
+        assert _gemm_fingerprint(w) == want[name], name
 
 
 def test_generator_rows_subset_equals_full():
