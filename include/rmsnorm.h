@@ -62,6 +62,7 @@ enum {
 };
 
 #define RMSN_KMAX 16
+#define RMSN_GATHER_MAX 16
 #define RMSN_MAX_HIDDEN (1 << 24)
 
 /*
@@ -91,6 +92,29 @@ int rmsnorm_fwd(void* out, const void* x, const void* gamma, int64_t rows, int64
 int add_rmsnorm_fwd(void* out, void* residual, const void* const* partials, int k,
                     const void* gamma, int64_t rows, int64_t hidden, float eps, int dtype,
                     void* stream);
+
+/*
+ * add_rmsnorm_ag_fwd -- add_rmsnorm_fwd with an all-gather epilogue: every
+ * normalised row is stored into each of the nout gather buffers, in one pass
+ * (page "Tokenweave fused-RMSNorm-AR kernel", "Code walkthrough": one rank
+ * reduces its share of the tokens over the ranks' partials, adds its
+ * residual, normalises, and broadcasts the normalised rows to every rank by
+ * stores; here every buffer is local device memory -- with several GPUs,
+ * outs[j] would be rank j's gather buffer at this rank's rows, and partials
+ * the ranks' partial buffers at the same rows).
+ *   outs      HOST array of nout device pointers, each [rows, hidden]
+ *             written with the same values (add_rmsnorm_fwd's out); the
+ *             array is copied at the call.
+ *   nout      1..RMSN_GATHER_MAX (RMSN_ERR_SHAPE otherwise).
+ *   residual, partials, k, gamma: as for add_rmsnorm_fwd.
+ *   Forbidden overlaps (RMSN_ERR_ALIAS): as for add_rmsnorm_fwd, and any
+ *   output buffer with another one, with residual, gamma or any partial
+ *   (exact aliasing included).  Returns RMSN_ERR_NULL for a NULL outs,
+ *   outs[j], residual, partials or gamma (rows > 0).
+ */
+int add_rmsnorm_ag_fwd(void* const* outs, int nout, void* residual, const void* const* partials,
+                       int k, const void* gamma, int64_t rows, int64_t hidden, float eps,
+                       int dtype, void* stream);
 
 /*
  * The general interface -- page "RMSNorm kernel", section 2, which states the
@@ -160,6 +184,12 @@ int rmsnorm_plan(int64_t rows, int64_t hidden, int k, int dtype, int align, char
  * Both exist for tuning and testing; unset, the dispatcher decides.
  */
 int rmsnorm_variants(int dtype, char* buf, int buflen);
+
+/* rmsnorm_plan_ag / rmsnorm_variants_ag -- the same for add_rmsnorm_ag_fwd
+ * (k >= 1; names end in ",ag>"; RMSNORM_VARIANT forces them the same way). */
+int rmsnorm_plan_ag(int64_t rows, int64_t hidden, int k, int dtype, int align, char* buf,
+                    int buflen);
+int rmsnorm_variants_ag(int dtype, char* buf, int buflen);
 
 /* rmsnorm_plan_ex / rmsnorm_variants_ex -- the same for the general
  * interface's dtype combinations (contiguous rows for the plan). */

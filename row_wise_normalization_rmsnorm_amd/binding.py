@@ -22,7 +22,9 @@ DTYPE_NAME = {"f32": 0, "f16": 1, "bf16": 2}
 KMAX = 16
 EXPORTS = ("rmsnorm_fwd", "add_rmsnorm_fwd", "rmsnorm_strerror", "rmsnorm_last_error",
            "rmsnorm_plan", "rmsnorm_variants", "rmsnorm_fwd_ex", "add_rmsnorm_fwd_ex",
-           "rmsnorm_plan_ex", "rmsnorm_variants_ex", "rmsnorm_plan_call")
+           "rmsnorm_plan_ex", "rmsnorm_variants_ex", "rmsnorm_plan_call", "add_rmsnorm_ag_fwd",
+           "rmsnorm_plan_ag", "rmsnorm_variants_ag")
+GATHER_MAX = 16
 BLOCK_SUM_EXPORTS = ("block_all_reduce_sum",)
 GEMM_SCATTER_EXPORTS = ("gemm_scatter_fwd", "gemm_scatter_tile_n", "gemm_scatter_tiles",
                         "gemm_scatter_schedule")
@@ -90,6 +92,13 @@ def lib() -> ctypes.CDLL:
                                             ctypes.POINTER(i64), c_int, c_int, vp, c_int, i64, i64,
                                             c_float, ctypes.c_char_p, c_int]
             l.rmsnorm_plan_call.restype = c_int
+            l.add_rmsnorm_ag_fwd.argtypes = [ctypes.POINTER(vp), c_int, vp, ctypes.POINTER(vp),
+                                             c_int, vp, i64, i64, c_float, c_int, vp]
+            l.add_rmsnorm_ag_fwd.restype = c_int
+            l.rmsnorm_plan_ag.argtypes = [i64, i64, c_int, c_int, c_int, ctypes.c_char_p, c_int]
+            l.rmsnorm_plan_ag.restype = c_int
+            l.rmsnorm_variants_ag.argtypes = [c_int, ctypes.c_char_p, c_int]
+            l.rmsnorm_variants_ag.restype = c_int
             l.block_all_reduce_sum.argtypes = [vp, vp, i64, c_int, vp, i64, vp]
             l.block_all_reduce_sum.restype = c_int
             l.gemm_scatter_fwd.argtypes = [ctypes.POINTER(vp), i64, c_int, c_int, vp, i64, vp,
@@ -171,6 +180,43 @@ def add_rmsnorm_fwd(out: torch.Tensor, residual: torch.Tensor, partials: Sequenc
     _check(lib().add_rmsnorm_fwd(_dev_ptr(out, "out"), _dev_ptr(residual, "residual"), arr, k,
                                  _dev_ptr(gamma, "gamma"), rows, hidden, float(eps),
                                  DTYPE_CODE[residual.dtype], _stream(residual, stream)))
+
+
+def add_rmsnorm_ag_fwd(outs: Sequence[torch.Tensor], residual: torch.Tensor,
+                       partials: Sequence[torch.Tensor], gamma: torch.Tensor, eps: float,
+                       stream=None) -> None:
+    """add_rmsnorm_fwd whose normalised rows go to every tensor of ``outs``
+    (the all-gather epilogue): residual <- round(p0 + ... + residual) in
+    place; outs[j] = RMSNorm(residual) * gamma for every j."""
+    rows, hidden = _rows_hidden(residual)
+    k, nout = len(partials), len(outs)
+    if gamma.numel() != hidden or any(p.shape != residual.shape for p in partials) or \
+            any(o.shape != residual.shape for o in outs):
+        raise RmsnormError(-2, "shape mismatch between outs, residual, partials and gamma")
+    if any(t.dtype != residual.dtype for t in [gamma, *outs, *partials]) or \
+            residual.dtype not in DTYPE_CODE:
+        raise RmsnormError(-3, "dtypes must match and be f32/f16/bf16")
+    arr = (ctypes.c_void_p * max(k, 1))(*[_dev_ptr(p, f"partials[{i}]") for i, p in enumerate(partials)])
+    oarr = (ctypes.c_void_p * max(nout, 1))(*[_dev_ptr(o, f"outs[{i}]") for i, o in enumerate(outs)])
+    _check(lib().add_rmsnorm_ag_fwd(oarr, nout, _dev_ptr(residual, "residual"), arr, k,
+                                    _dev_ptr(gamma, "gamma"), rows, hidden, float(eps),
+                                    DTYPE_CODE[residual.dtype], _stream(residual, stream)))
+
+
+def rmsnorm_plan_ag(rows: int, hidden: int, k: int, dtype: str, align: int = 16) -> str:
+    """Name of the variant add_rmsnorm_ag_fwd would launch (k >= 1)."""
+    buf = ctypes.create_string_buffer(128)
+    _check(lib().rmsnorm_plan_ag(rows, hidden, k, DTYPE_NAME[dtype], int(align), buf, 128))
+    return buf.value.decode()
+
+
+def rmsnorm_variants_ag(dtype: str) -> list:
+    """Names of every compiled all-gather variant for dtype."""
+    buf = ctypes.create_string_buffer(1 << 16)
+    n = lib().rmsnorm_variants_ag(DTYPE_NAME[dtype], buf, 1 << 16)
+    if n < 0:
+        _check(n)
+    return [s for s in buf.value.decode().split("\n") if s]
 
 
 def collapse_rows(shape, strides, what: str = "tensor"):

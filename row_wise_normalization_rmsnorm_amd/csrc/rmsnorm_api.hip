@@ -33,6 +33,9 @@ const rmsn::Variant* rmsn_table_bf16(int* n);
 const rmsn::Variant* rmsn_table_mixed_f32(int* n);
 const rmsn::Variant* rmsn_table_mixed_f16(int* n);
 const rmsn::Variant* rmsn_table_mixed_bf16(int* n);
+const rmsn::Variant* rmsn_table_ag_f32(int* n);
+const rmsn::Variant* rmsn_table_ag_f16(int* n);
+const rmsn::Variant* rmsn_table_ag_bf16(int* n);
 
 namespace {
 
@@ -79,7 +82,19 @@ struct Aligns {
   int in, g, out;
 };
 
-const rmsn::Variant* table_for(Types t, int* n) {
+// ag: the all-gather variants (single dtype only).
+const rmsn::Variant* table_for(Types t, int* n, bool ag = false) {
+  if (ag) {
+    if (t.single()) {
+      switch (t.d) {
+        case RMSN_F32: return rmsn_table_ag_f32(n);
+        case RMSN_F16: return rmsn_table_ag_f16(n);
+        case RMSN_BF16: return rmsn_table_ag_bf16(n);
+      }
+    }
+    *n = 0;
+    return nullptr;
+  }
   if (t.single()) {
     switch (t.d) {
       case RMSN_F32: return rmsn_table_f32(n);
@@ -104,9 +119,9 @@ bool same_types(const rmsn::Variant& v, Types t) {
 // npt: chunks per thread (register kernel) or chunks in flight per step
 // (streaming kernel).
 const rmsn::Variant* find(Types t, int kind, int vb, int tpr, int npt, int wgs, int kc, int lds,
-                          int nt) {
+                          int nt, bool ag) {
   int n = 0;
-  const rmsn::Variant* tab = table_for(t, &n);
+  const rmsn::Variant* tab = table_for(t, &n, ag);
   for (int i = 0; i < n; ++i) {
     const rmsn::Variant& v = tab[i];
     if (same_types(v, t) && v.kind == kind && v.vb == vb && v.tpr == tpr && v.wgs == wgs &&
@@ -173,7 +188,8 @@ bool fits(const rmsn::Variant& v, Types t, int64_t hidden, int k, Aligns al) {
 // row length.
 // The general interface (other gamma or output dtypes) makes the same
 // choice among the shapes compiled for it, with runtime-K fused kernels.
-int choose(Types t, int64_t rows, int64_t hidden, int k, Aligns al, Plan* plan) {
+// ag: the same choice among the all-gather variants.
+int choose(Types t, int64_t rows, int64_t hidden, int k, Aligns al, Plan* plan, bool ag = false) {
   const int s = dtype_size(t.d);
   const int vb = widest_chunk(t, hidden, al);
   const rmsn::Variant* v = nullptr;
@@ -181,7 +197,7 @@ int choose(Types t, int64_t rows, int64_t hidden, int k, Aligns al, Plan* plan) 
   const char* forced = getenv("RMSNORM_VARIANT");
   if (forced && *forced) {
     int n = 0;
-    const rmsn::Variant* tab = table_for(t, &n);
+    const rmsn::Variant* tab = table_for(t, &n, ag);
     for (int i = 0; i < n && !v; ++i)
       if (same_types(tab[i], t) && strcmp(tab[i].name, forced) == 0) v = &tab[i];
     if (!v)
@@ -208,8 +224,8 @@ int choose(Types t, int64_t rows, int64_t hidden, int k, Aligns al, Plan* plan) 
     while ((int64_t)tpr * per < C && tpr < 1024) tpr *= 2;
     const int npt = C <= tpr ? 1 : 2;
     const int wgs = tpr < 256 ? 256 : tpr;
-    v = find(t, rmsn::kVgpr, 16, tpr, npt, wgs, vgpr_kc(k), 0, 1);
-    if (!v && k > 0) v = find(t, rmsn::kVgpr, 16, tpr, npt, wgs, -1, 0, 1);
+    v = find(t, rmsn::kVgpr, 16, tpr, npt, wgs, vgpr_kc(k), 0, 1, ag);
+    if (!v && k > 0) v = find(t, rmsn::kVgpr, 16, tpr, npt, wgs, -1, 0, 1, ag);
   } else {
     // Streaming two-pass, LDS-staged while the row fits the stage budget.
     // Fused calls use the runtime-K form, which sums the partials one at a
@@ -232,8 +248,9 @@ int choose(Types t, int64_t rows, int64_t hidden, int k, Aligns al, Plan* plan) 
     // (4096x8192 bf16: 114.6 vs 116.1 us; 8192x16384: 477 vs 483 us), and
     // 1-2% slower at K = 2, 3, 4 and 16, which keep one per step.
     const int kc = k == 0 ? 0 : k == 8 ? -2 : -1;
-    v = find(t, rmsn::kStream, svb, wgs, unr, wgs, kc, lds ? 1 : 0, lds ? 1 : 0);
-    if (!v && kc == -2) v = find(t, rmsn::kStream, svb, wgs, unr, wgs, -1, lds ? 1 : 0, lds ? 1 : 0);
+    v = find(t, rmsn::kStream, svb, wgs, unr, wgs, kc, lds ? 1 : 0, lds ? 1 : 0, ag);
+    if (!v && kc == -2)
+      v = find(t, rmsn::kStream, svb, wgs, unr, wgs, -1, lds ? 1 : 0, lds ? 1 : 0, ag);
   }
   if (!v) return fail(RMSN_ERR_SHAPE, "no kernel variant for hidden=%lld k=%d", (long long)hidden, k);
   plan->v = v;
@@ -314,7 +331,8 @@ int stride_check(const char* what, int64_t stride, int64_t rows, int64_t hidden,
   return RMSN_OK;
 }
 
-int launch(const Plan& plan, rmsn::RowArgs a, void* stream) {
+template <typename Args>
+int launch(const Plan& plan, Args a, void* stream) {
   const rmsn::Variant& v = *plan.v;
   a.chunks = plan.chunks;
   const int64_t rows_per_wg = v.kind == rmsn::kVgpr ? v.wgs / v.tpr : 1;
@@ -337,10 +355,12 @@ int launch(const Plan& plan, rmsn::RowArgs a, void* stream) {
 // residual == nullptr is plain RMSNorm (k == 1, partials[0] is x).  Strides
 // are in elements of each tensor's own dtype.  With dry != nullptr nothing is
 // launched: *dry receives the chosen variant (nullptr when rows == 0).
+// gather (fused, single dtype only): ngather buffers that each receive the
+// output rows instead of out (the all-gather epilogue); out is then unused.
 int run(Types t, void* out, int64_t out_stride, void* residual, int64_t res_stride,
         const void* const* partials, const int64_t* part_strides, int k, const void* gamma,
         int64_t rows, int64_t hidden, float eps, void* stream,
-        const rmsn::Variant** dry = nullptr) {
+        const rmsn::Variant** dry = nullptr, void* const* gather = nullptr, int ngather = 0) {
   if (dry) *dry = nullptr;
   int rc = common_checks(t.d, rows, hidden, eps);
   if (rc) return rc;
@@ -380,8 +400,28 @@ int run(Types t, void* out, int64_t out_stride, void* residual, int64_t res_stri
   if (fused && overlap(o, r)) return fail(RMSN_ERR_ALIAS, "out overlaps residual");
   if (overlap(o, g)) return fail(RMSN_ERR_ALIAS, "out overlaps gamma");
   if (fused && overlap(r, g)) return fail(RMSN_ERR_ALIAS, "residual overlaps gamma");
+  rmsn::GatherPtrs gp{};
+  if (gather) {
+    // out is gather[0]; every gather buffer is checked like out, and none
+    // may touch an input, gamma, the residual or another gather buffer (not
+    // even exactly: a later copy would overwrite an input already read).
+    gp.n = ngather;
+    for (int j = 0; j < ngather; ++j) {
+      const Span oj{gather[j], o.pitch, o.len, rows};
+      for (int q = 0; q < k; ++q)
+        if (overlap(oj, Span{partials[q], a.partials.s[q], hidden * sd, rows}))
+          return fail(RMSN_ERR_ALIAS, "gather[%d] overlaps partials[%d]", j, q);
+      if (overlap(oj, r)) return fail(RMSN_ERR_ALIAS, "gather[%d] overlaps residual", j);
+      if (overlap(oj, g)) return fail(RMSN_ERR_ALIAS, "gather[%d] overlaps gamma", j);
+      for (int q = 0; q < j; ++q)
+        if (overlap(oj, Span{gather[q], o.pitch, o.len, rows}))
+          return fail(RMSN_ERR_ALIAS, "gather[%d] overlaps gather[%d]", j, q);
+      al.out = std::min(al.out, oj.align());
+      gp.p[j] = gather[j];
+    }
+  }
   Plan plan;
-  rc = choose(t, rows, hidden, fused ? k : 0, al, &plan);
+  rc = choose(t, rows, hidden, fused ? k : 0, al, &plan, gather != nullptr);
   if (rc) return rc;
   if (dry) {
     *dry = plan.v;
@@ -396,13 +436,19 @@ int run(Types t, void* out, int64_t out_stride, void* residual, int64_t res_stri
   a.hidden = (int)hidden;
   a.k = k;
   a.eps = eps;
+  if (gather) {
+    rmsn::RowArgsAG ag{};
+    static_cast<rmsn::RowArgs&>(ag) = a;
+    ag.gather = gp;
+    return launch(plan, ag, stream);
+  }
   return launch(plan, a, stream);
 }
 
-int list_variants(Types t, char* buf, int buflen) {
+int list_variants(Types t, char* buf, int buflen, bool ag = false) {
   if (!buf || buflen < 1) return fail(RMSN_ERR_NULL, "buf must be non-NULL");
   int n = 0, count = 0;
-  const rmsn::Variant* tab = table_for(t, &n);
+  const rmsn::Variant* tab = table_for(t, &n, ag);
   size_t used = 0;
   buf[0] = 0;
   for (int i = 0; i < n; ++i) {
@@ -418,7 +464,8 @@ int list_variants(Types t, char* buf, int buflen) {
   return count;
 }
 
-int plan_name(Types t, int64_t rows, int64_t hidden, int k, int align, char* buf, int buflen) {
+int plan_name(Types t, int64_t rows, int64_t hidden, int k, int align, char* buf, int buflen,
+              bool ag = false) {
   int rc = common_checks(t.d, rows, hidden, 0.0f);
   if (rc) return rc;
   if ((rc = type_checks(t))) return rc;
@@ -430,7 +477,7 @@ int plan_name(Types t, int64_t rows, int64_t hidden, int k, int align, char* buf
   // contiguous rows: each tensor's pitch is hidden elements of its dtype
   const Aligns al{std::min(a, align_of_int((uint64_t)hidden * dtype_size(t.d))),
                   a, std::min(a, align_of_int((uint64_t)hidden * dtype_size(t.o)))};
-  rc = choose(t, rows, hidden, k, rows > 1 ? al : Aligns{a, a, a}, &plan);
+  rc = choose(t, rows, hidden, k, rows > 1 ? al : Aligns{a, a, a}, &plan, ag);
   if (rc) return rc;
   snprintf(buf, (size_t)buflen, "%s", plan.v->name);
   return RMSN_OK;
@@ -462,6 +509,23 @@ int add_rmsnorm_fwd(void* out, void* residual, const void* const* partials, int 
   }
   return run(Types{dtype, dtype, dtype}, out, hidden, residual, hidden, partials, nullptr, k,
              gamma, rows, hidden, eps, stream);
+}
+
+int add_rmsnorm_ag_fwd(void* const* outs, int nout, void* residual, const void* const* partials,
+                       int k, const void* gamma, int64_t rows, int64_t hidden, float eps,
+                       int dtype, void* stream) {
+  int rc = common_checks(dtype, rows, hidden, eps);
+  if (rc) return rc;
+  if (k < 1 || k > RMSN_KMAX) return fail(RMSN_ERR_K, "k=%d outside [1, %d]", k, RMSN_KMAX);
+  if (nout < 1 || nout > RMSN_GATHER_MAX)
+    return fail(RMSN_ERR_SHAPE, "nout=%d outside [1, %d]", nout, RMSN_GATHER_MAX);
+  if (rows == 0) return RMSN_OK;
+  if (!outs) return fail(RMSN_ERR_NULL, "outs must be non-NULL");
+  for (int j = 0; j < nout; ++j)
+    if (!outs[j]) return fail(RMSN_ERR_NULL, "outs[%d] is NULL", j);
+  if (!residual) return fail(RMSN_ERR_NULL, "residual must be non-NULL");
+  return run(Types{dtype, dtype, dtype}, outs[0], hidden, residual, hidden, partials, nullptr, k,
+             gamma, rows, hidden, eps, stream, nullptr, outs, nout);
 }
 
 int rmsnorm_fwd_ex(void* out, int64_t out_stride, int out_dtype, const void* x, int64_t x_stride,
@@ -510,6 +574,12 @@ int rmsnorm_plan(int64_t rows, int64_t hidden, int k, int dtype, int align, char
   return plan_name(Types{dtype, dtype, dtype}, rows, hidden, k, align, buf, buflen);
 }
 
+int rmsnorm_plan_ag(int64_t rows, int64_t hidden, int k, int dtype, int align, char* buf,
+                    int buflen) {
+  if (k < 1 || k > RMSN_KMAX) return fail(RMSN_ERR_K, "k=%d outside [1, %d]", k, RMSN_KMAX);
+  return plan_name(Types{dtype, dtype, dtype}, rows, hidden, k, align, buf, buflen, true);
+}
+
 int rmsnorm_plan_ex(int64_t rows, int64_t hidden, int k, int dtype, int gamma_dtype,
                     int out_dtype, int align, char* buf, int buflen) {
   return plan_name(Types{dtype, gamma_dtype, out_dtype}, rows, hidden, k, align, buf, buflen);
@@ -534,6 +604,11 @@ int rmsnorm_plan_call(void* out, int64_t out_stride, int out_dtype, void* residu
 int rmsnorm_variants(int dtype, char* buf, int buflen) {
   if (!known(dtype)) return fail(RMSN_ERR_DTYPE, "unknown dtype %d", dtype);
   return list_variants(Types{dtype, dtype, dtype}, buf, buflen);
+}
+
+int rmsnorm_variants_ag(int dtype, char* buf, int buflen) {
+  if (!known(dtype)) return fail(RMSN_ERR_DTYPE, "unknown dtype %d", dtype);
+  return list_variants(Types{dtype, dtype, dtype}, buf, buflen, true);
 }
 
 int rmsnorm_variants_ex(int dtype, int gamma_dtype, int out_dtype, char* buf, int buflen) {

@@ -60,6 +60,19 @@ struct RowArgs {
   float eps;
 };
 
+// The fused form with an all-gather epilogue (AG kernels): every normalised
+// row is stored at the same row of each of the n gather buffers, with out's
+// row pitch, instead of into out.
+struct GatherPtrs {
+  void* p[kMaxK];
+  int n;
+};
+struct RowArgsAG : RowArgs {
+  GatherPtrs gather;
+};
+template <bool AG>
+using ArgsOf = typename std::conditional<AG, RowArgsAG, RowArgs>::type;
+
 __device__ __forceinline__ const char* row_ptr(const void* base, int64_t stride, int64_t row) {
   return reinterpret_cast<const char*>(base) + row * stride;
 }
@@ -334,8 +347,11 @@ __device__ __forceinline__ int exponent_above(float m) {
 // KC: 0 = plain RMSNorm; >0 = fused with exactly KC partials; -1 = fused with
 // a runtime number of partials (args.k), summed one partial at a time.
 // NT: streaming (nontemporal) loads and stores for the row data.
-template <typename T, typename GT, typename OT, int TPR, int NPT, int WGS, int KC, bool NT>
-__global__ __launch_bounds__(WGS) void row_vgpr_kernel(RowArgs a) {
+// AG: store each output row into every gather buffer (RowArgsAG) instead of
+// out.
+template <typename T, typename GT, typename OT, int TPR, int NPT, int WGS, int KC, bool NT,
+          bool AG = false>
+__global__ __launch_bounds__(WGS) void row_vgpr_kernel(ArgsOf<AG> a) {
   constexpr int V = chunk_elems<T, 16>();
   using IV = Vec<T, V>;   // data: partials, residual, x
   using GV = Vec<GT, V>;  // gamma
@@ -529,7 +545,13 @@ __global__ __launch_bounds__(WGS) void row_vgpr_kernel(RowArgs a) {
 #pragma unroll
           for (int e = 0; e < V; ++e) y[e] = (ldexpf(v[i][e], shift) * inv) * g[i][e];
         }
-        OV::template store<NT>(orow, c, OV::pack(y));
+        if constexpr (AG) {
+          const auto packed = OV::pack(y);
+          for (int j = 0; j < a.gather.n; ++j)
+            OV::template store<NT>(row_ptr(a.gather.p[j], a.out_stride, row), c, packed);
+        } else {
+          OV::template store<NT>(orow, c, OV::pack(y));
+        }
       }
     }
   }
@@ -547,9 +569,10 @@ __global__ __launch_bounds__(WGS) void row_vgpr_kernel(RowArgs a) {
 // in flight together, the adds still in order).
 // NT: streaming loads/stores for data touched once (never for a residual
 // that pass 2 reads back from memory).
+// AG: as for the register kernel.
 template <typename T, typename GT, typename OT, int VB, int WGS, bool LDS_STAGE, int KC, int UNR,
-          bool NT>
-__global__ __launch_bounds__(WGS) void row_stream_kernel(RowArgs a) {
+          bool NT, bool AG = false>
+__global__ __launch_bounds__(WGS) void row_stream_kernel(ArgsOf<AG> a) {
   constexpr int V = chunk_elems<T, VB>();
   using IV = Vec<T, V>;   // data: partials, residual, x
   using GV = Vec<GT, V>;  // gamma
@@ -733,7 +756,13 @@ __global__ __launch_bounds__(WGS) void row_stream_kernel(RowArgs a) {
 #pragma unroll
             for (int e = 0; e < V; ++e) y[e] = (ldexpf(t[e], shift) * inv) * g[e];
           }
-          OV::template store<NT>(orow, c, OV::pack(y));
+          if constexpr (AG) {
+            const auto packed = OV::pack(y);
+            for (int j = 0; j < a.gather.n; ++j)
+              OV::template store<NT>(row_ptr(a.gather.p[j], a.out_stride, row), c, packed);
+          } else {
+            OV::template store<NT>(orow, c, OV::pack(y));
+          }
         }
       }
     }

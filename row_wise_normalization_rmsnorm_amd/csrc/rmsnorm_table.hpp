@@ -34,7 +34,7 @@ struct Types {
 };
 
 inline void add_variant(std::vector<Variant>& v, Types t, int kind, int vb, int tpr, int npt,
-                        int wgs, int kc, int lds, int unr, int nt, const void* fn) {
+                        int wgs, int kc, int lds, int unr, int nt, const void* fn, int ag = 0) {
   Variant d{};
   // Single-dtype variants are named by the data dtype alone; the general
   // interface's add gamma's and the output's dtypes.
@@ -45,12 +45,14 @@ inline void add_variant(std::vector<Variant>& v, Types t, int kind, int vb, int 
     snprintf(types, sizeof(types), "%s,g=%s,o=%s", dtype_name(t.d), dtype_name(t.g),
              dtype_name(t.o));
   if (kind == kVgpr)
-    snprintf(d.name, sizeof(d.name), "vgpr<%s,tpr=%d,npt=%d,wg=%d,k=%d%s>", types, tpr, npt, wgs,
-             kc, nt ? ",nt" : "");
+    snprintf(d.name, sizeof(d.name), "vgpr<%s,tpr=%d,npt=%d,wg=%d,k=%d%s%s>", types, tpr, npt,
+             wgs, kc, nt ? ",nt" : "", ag ? ",ag" : "");
   else
-    snprintf(d.name, sizeof(d.name), "stream<%s,%s,wg=%d,%s,k=%d,unr=%d%s>", types,
-             width_name(vb), wgs, lds ? "lds" : "reread", kc, unr, nt ? ",nt" : "");
+    snprintf(d.name, sizeof(d.name), "stream<%s,%s,wg=%d,%s,k=%d,unr=%d%s%s>", types,
+             width_name(vb), wgs, lds ? "lds" : "reread", kc, unr, nt ? ",nt" : "",
+             ag ? ",ag" : "");
   d.nt = nt;
+  d.ag = ag;
   d.dtype = t.d;
   d.gdtype = t.g;
   d.odtype = t.o;
@@ -115,6 +117,29 @@ void add_mixed(std::vector<Variant>& v, Types t) {
                     &row_stream_kernel<T, GT, OT, VB, WGS, LDS, KC, UNR, NT>));
 #define RMSN_ADD_STREAM(VB, WGS, LDS, NT, UNR) \
   RMSN_MIXED_KCS(RMSN_ADD_STREAM_K, VB, WGS, LDS, NT, UNR)
+  RMSN_MIXED_STREAM_SHAPES(RMSN_ADD_STREAM)
+#undef RMSN_ADD_VGPR_K
+#undef RMSN_ADD_VGPR
+#undef RMSN_ADD_STREAM_K
+#undef RMSN_ADD_STREAM
+}
+
+// The all-gather variants of one dtype (add_rmsnorm_ag_fwd).
+template <typename T>
+void add_ag(std::vector<Variant>& v, Types t) {
+#define RMSN_ADD_VGPR_K(KC, TPR, NPT, WGS, NT)                                          \
+  add_variant(v, t, kVgpr, 16, TPR, NPT, WGS, KC, 0, 0, NT ? 1 : 0,                      \
+              reinterpret_cast<const void*>(&row_vgpr_kernel<T, T, T, TPR, NPT, WGS, KC, NT, true>), 1);
+#define RMSN_ADD_VGPR(TPR, NPT, WGS, NT) RMSN_AG_VGPR_KCS(RMSN_ADD_VGPR_K, TPR, NPT, WGS, NT)
+  RMSN_AG_VGPR_SHAPES(RMSN_ADD_VGPR)
+#define RMSN_ADD_STREAM_K(KC, VB, WGS, LDS, NT, UNR)                                    \
+  if constexpr ((VB == 0 || VB > (int)sizeof(typename DT<T>::scalar_t)) &&               \
+                (KC != -2 || (VB == 8 && LDS)))                                          \
+    add_variant(v, t, kStream, VB, WGS, 0, WGS, KC, LDS ? 1 : 0, UNR, NT ? 1 : 0,         \
+                reinterpret_cast<const void*>(                                           \
+                    &row_stream_kernel<T, T, T, VB, WGS, LDS, KC, UNR, NT, true>), 1);
+#define RMSN_ADD_STREAM(VB, WGS, LDS, NT, UNR) \
+  RMSN_AG_STREAM_KCS(RMSN_ADD_STREAM_K, VB, WGS, LDS, NT, UNR)
   RMSN_MIXED_STREAM_SHAPES(RMSN_ADD_STREAM)
 #undef RMSN_ADD_VGPR_K
 #undef RMSN_ADD_VGPR

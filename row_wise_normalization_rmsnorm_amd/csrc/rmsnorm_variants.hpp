@@ -27,6 +27,7 @@ struct Variant {
   int lds_stage;  // stream: stage the row in LDS (1) or re-read it (0)
   int unroll;     // stream: chunks in flight per thread per step
   int nt;         // streaming (nontemporal) loads/stores for row data
+  int ag;         // all-gather epilogue: takes RowArgsAG, stores into every gather buffer
   const void* fn; // host stub for hipLaunchKernel
 };
 
@@ -89,5 +90,17 @@ struct Variant {
   X(0, 256, false, false, 4) X(0, 512, false, false, 4) X(0, 1024, false, false, 4)
 
 #define RMSN_MIXED_KCS(X, ...) X(0, __VA_ARGS__) X(-1, __VA_ARGS__)
+
+// The fused form with an all-gather epilogue (add_rmsnorm_ag_fwd, one dtype)
+// compiles the shapes the dispatcher picks for fused calls: the register
+// kernel with one chunk per thread, with K = 1, 8 or any, and the streaming
+// shapes of the general interface with runtime K (one partial per step, or
+// two for the LDS-staged 8-byte shapes).
+#define RMSN_AG_VGPR_SHAPES(X)                                                          \
+  X(8, 1, 256, true) X(16, 1, 256, true) X(32, 1, 256, true) X(64, 1, 256, true)        \
+  X(128, 1, 256, true) X(256, 1, 256, true) X(512, 1, 512, true) X(1024, 1, 1024, true)
+
+#define RMSN_AG_VGPR_KCS(X, ...) X(1, __VA_ARGS__) X(8, __VA_ARGS__) X(-1, __VA_ARGS__)
+#define RMSN_AG_STREAM_KCS(X, ...) X(-1, __VA_ARGS__) X(-2, __VA_ARGS__)
 
 }  // namespace rmsn

@@ -302,3 +302,60 @@ def test_dispatcher_covers_every_shape():
                     for k in (0, 1, 3, 8):
                         for al in (16, 8, 4, 2):
                             assert B.rmsnorm_plan_ex(65536, h, k, d, g, o, align=al)
+
+
+# ---- the all-gather epilogue (add_rmsnorm_ag_fwd) ---------------------------
+
+def add_ag(k=1, parts=None, outs=None, nout=None, **kw):
+    a = dict(residual=FAKE + (1 << 24), gamma=FAKE + (1 << 26), rows=4, hidden=64, eps=1e-6,
+             dtype=2)
+    a.update(kw)
+    parts = parts if parts is not None else [FAKE + (1 << 27) + i * (1 << 20) for i in range(k)]
+    outs = outs if outs is not None else [FAKE + (1 << 29) + j * (1 << 20) for j in range(3)]
+    arr = (ctypes.c_void_p * max(1, len(parts)))(*parts)
+    oarr = (ctypes.c_void_p * max(1, len(outs)))(*outs)
+    return B.lib().add_rmsnorm_ag_fwd(oarr, len(outs) if nout is None else nout, a["residual"],
+                                      arr, k, a["gamma"], a["rows"], a["hidden"], a["eps"],
+                                      a["dtype"], None)
+
+
+def test_ag_error_codes():
+    """add_rmsnorm_ag_fwd validates like add_rmsnorm_fwd, plus the output
+    count and every output buffer (none may touch an input, gamma, the
+    residual or another output, exact aliasing included)."""
+    o = FAKE + (1 << 29)
+    assert add_ag(nout=0) == -2 and add_ag(nout=17) == -2
+    assert add_ag(k=0) == -4 and add_ag(k=17) == -4
+    assert add_ag(dtype=3) == -3 and add_ag(hidden=0) == -2 and add_ag(eps=-1.0) == -6
+    assert add_ag(outs=[o, 0]) == -1
+    assert add_ag(residual=0) == -1 and add_ag(gamma=0) == -1
+    assert add_ag(k=2, parts=[FAKE + (1 << 27), 0]) == -1
+    assert add_ag(outs=[o, o + 256]) == -5                     # two outputs overlap
+    assert add_ag(outs=[o, o]) == -5                           # ... even exactly
+    assert add_ag(outs=[o, FAKE + (1 << 27)]) == -5            # an output is a partial
+    assert add_ag(outs=[FAKE + (1 << 24) + 64]) == -5          # an output overlaps the residual
+    assert add_ag(outs=[o, FAKE + (1 << 26) - 100]) == -5      # an output overlaps gamma
+    assert add_ag(residual=FAKE + (1 << 27) + 8) == -5         # residual overlaps a partial
+    assert "overlap" in B.lib().rmsnorm_last_error().decode()
+    assert add_ag(rows=0, outs=[0], residual=0, gamma=0) == 0  # rows == 0: no-op
+    with pytest.raises(B.RmsnormError):
+        B.rmsnorm_plan_ag(4, 64, 0, "bf16")                    # the fused form only
+
+
+def test_ag_plans_mirror_the_fused_dispatcher():
+    """For every fused call the all-gather dispatcher takes the same shape as
+    add_rmsnorm_fwd's, compiled with the all-gather epilogue."""
+    import random
+    rng = random.Random(3)
+    cases = [(8192, 4096, 1, "bf16", 16), (4096, 8192, 8, "bf16", 16), (512, 8192, 8, "bf16", 16),
+             (65536, 16384, 1, "bf16", 16), (100, 100000, 3, "f16", 16), (7, 17, 16, "bf16", 2)]
+    for _ in range(300):
+        cases.append((rng.randint(1, 5000), rng.randint(1, 70000), rng.randint(1, 16),
+                      rng.choice(["bf16", "f16", "f32"]), rng.choice([1, 2, 4, 8, 16])))
+    for rows, hidden, k, dtype, align in cases:
+        plain = B.rmsnorm_plan(rows, hidden, k, dtype, align=align)
+        assert B.rmsnorm_plan_ag(rows, hidden, k, dtype, align=align) == plain[:-1] + ",ag>", \
+            (rows, hidden, k, dtype, align)
+    for dtype in ("bf16", "f16", "f32"):
+        names = B.rmsnorm_variants_ag(dtype)
+        assert len(names) == len(set(names)) > 40 and all(n.endswith(",ag>") for n in names)
