@@ -123,7 +123,10 @@ def cpu_baseline(w, target_cpu_seconds: float = 12.0, max_passes: int = 40) -> d
             "rows_per_s": round(w.rows / per_pass, 1), "seconds_per_pass": round(per_pass, 4),
             "cores": cores, "kind": "oracle",
             "sample": (f"{passes} full passes over all {w.rows} rows of {w.name} "
-                       f"({cpu:.1f} CPU-seconds), rows split over {cores} threads"),
+                       f"({cpu:.1f} CPU-seconds), rows split over {cores} threads"
+                       + (f"; the oracle computes each output row once (the {w.gather} "
+                          "gather copies are no arithmetic), the rate counts the workload's "
+                          "algorithmic bytes" if w.gather else "")),
             "single_thread": {"value": round(w.algorithmic_bytes() / single / 1e9, 3),
                               "unit": "GB/s", "rows_per_s": round(w.rows / single, 1),
                               "cores": 1,
@@ -378,6 +381,9 @@ def stream_ceiling(w, dev: str = "cuda:0", steps: int = 60, rotate_gib: float = 
                                  ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
     if w.op == "block_sum":
         nr, writes = 1, []
+    elif w.gather:
+        nr = w.k + 1                                          # p0..p(K-1), residual
+        writes = [w.k] + [nr + j for j in range(w.gather)]    # residual in place, each output
     elif w.fused:
         nr = w.k + 1                                          # p0..p(K-1), residual
         writes = [w.k, 0 if inplace else nr]                  # residual in place, output
@@ -505,14 +511,15 @@ def sweep(w, step, a, B) -> int:
     median is reported, so slow drifts of the clock do not favour one."""
     import statistics
     import torch
-    default = B.rmsnorm_plan(w.rows, w.hidden, w.k, w.dtype)
+    plan = B.rmsnorm_plan_ag if w.gather else B.rmsnorm_plan
+    default = plan(w.rows, w.hidden, w.k, w.dtype)
     names = []
-    for v in B.rmsnorm_variants(w.dtype):
+    for v in (B.rmsnorm_variants_ag if w.gather else B.rmsnorm_variants)(w.dtype):
         if a.variant_filter and not any(f in v for f in a.variant_filter.split("|")):
             continue
         os.environ["RMSNORM_VARIANT"] = v
         try:
-            B.rmsnorm_plan(w.rows, w.hidden, w.k, w.dtype)
+            plan(w.rows, w.hidden, w.k, w.dtype)
             names.append(v)
         except B.RmsnormError:
             pass
@@ -686,6 +693,10 @@ def main() -> int:
     if a.workload in GEMM_WORKLOADS:
         return gemm_bench(a, a.workload)
     w = WORKLOADS[a.workload or HEADLINE]
+    if a.inplace and w.gather:
+        print("bench.py: --inplace does not apply to the all-gather form (its outputs are "
+              "separate buffers by definition)", file=sys.stderr)
+        return 2
     if a.rows:  # the same workload with another row count (footprint studies)
         import dataclasses
         w = dataclasses.replace(w, name=f"{w.name}_rows{a.rows}", rows=a.rows)
@@ -707,6 +718,8 @@ def main() -> int:
             s["x"] = s["x"].reshape(-1)
             s["out"] = torch.empty(1, device=dev,
                                    dtype=torch.int32 if w.dtype == "i8" else torch.float32)
+        elif w.gather:
+            s["outs"] = [torch.empty_like(s["residual"]) for _ in range(w.gather)]
         else:
             if a.inplace:  # the output written over the (first) input, as the fused
                 s["out"] = s["partials"][0] if w.fused else s["x"]  # kernel of the pages does
@@ -720,6 +733,8 @@ def main() -> int:
             return 2
         kernel = f"block_sum<{w.dtype}>"
         ws = B.block_sum_workspace(dev)
+    elif w.gather:
+        kernel = B.rmsnorm_plan_ag(w.rows, w.hidden, w.k, w.dtype)
     else:
         kernel = B.rmsnorm_plan(w.rows, w.hidden, w.k, w.dtype)
 
@@ -727,6 +742,8 @@ def main() -> int:
         s = sets[i % nsets]
         if w.op == "block_sum":
             B.block_all_reduce_sum_fwd(s["out"], s["x"], ws)
+        elif w.gather:
+            B.add_rmsnorm_ag_fwd(s["outs"], s["residual"], s["partials"], s["gamma"], w.eps)
         elif w.fused:
             B.add_rmsnorm_fwd(s["out"], s["residual"], s["partials"], s["gamma"], w.eps)
         else:

@@ -18,7 +18,7 @@ from dataclasses import dataclass
 @dataclass(frozen=True)
 class Workload:
     name: str
-    op: str           # "rmsnorm", "add_rmsnorm" or "block_sum"
+    op: str           # "rmsnorm", "add_rmsnorm", "add_rmsnorm_ag" or "block_sum"
     dtype: str        # "f32", "f16", "bf16" (block_sum also "fp8_e4m3", "fp8_e5m2", "i8")
     rows: int
     hidden: int
@@ -27,10 +27,11 @@ class Workload:
     part_std: float   # std of x / each partial
     special_frac: float = 0.0  # fraction of rows scaled by 1e3, and (disjoint) all-zero
     seed: int = 0
+    gather: int = 0   # add_rmsnorm_ag: output buffers that each receive the rows
 
     @property
     def fused(self) -> bool:
-        return self.op == "add_rmsnorm"
+        return self.op in ("add_rmsnorm", "add_rmsnorm_ag")
 
     @property
     def itemsize(self) -> int:
@@ -39,19 +40,21 @@ class Workload:
     def algorithmic_bytes(self) -> int:
         """Bytes a single pass must move: each tensor element read or written
         once, gamma counted once.  Plain: read x, write out.  Fused: read K
-        partials and the residual, write the residual and out.  Block sum:
+        partials and the residual, write the residual and out (with the
+        all-gather epilogue, every one of the gather outputs).  Block sum:
         read x, write one 4-byte result."""
         n = self.rows * self.hidden * self.itemsize
         if self.op == "block_sum":
             return n + 4
-        per_elem = 2 if not self.fused else self.k + 3
+        per_elem = 2 if not self.fused else self.k + 2 + max(1, self.gather)
         return n * per_elem + self.hidden * self.itemsize
 
     def describe(self) -> str:
         if self.op == "block_sum":
             return f"block_sum {self.dtype} {self.rows}x{self.hidden}"
         return (f"{self.op} {self.dtype} rows={self.rows} hidden={self.hidden}"
-                + (f" K={self.k}" if self.fused else "") + f" eps={self.eps:g}")
+                + (f" K={self.k}" if self.fused else "")
+                + (f" outputs={self.gather}" if self.gather else "") + f" eps={self.eps:g}")
 
 
 WORKLOADS = {
@@ -69,6 +72,12 @@ WORKLOADS = {
     "add_rmsnorm_bf16_65536x16384_k1": Workload(
         "add_rmsnorm_bf16_65536x16384_k1", "add_rmsnorm", "bf16", 65536, 16384, 1, 1e-6, 1.0,
         special_frac=0.01),
+    # One rank's share of the K = 8 workload over 8 ranks with the all-gather
+    # epilogue: 4096 / 8 rows reduced over the 8 ranks' partials, normalised,
+    # and stored into the 8 ranks' gather buffers.
+    "add_rmsnorm_ag_bf16_512x8192_k8_w8": Workload(
+        "add_rmsnorm_ag_bf16_512x8192_k8_w8", "add_rmsnorm_ag", "bf16", 512, 8192, 8, 1e-5,
+        0.125 ** 0.5, gather=8),
 }
 
 # Block all-reduce sum of a [S, K] tensor (page "Block All Reduce CUDA代码学习":

@@ -12,6 +12,7 @@ import torch
 
 from row_wise_normalization_rmsnorm_amd import binding as B
 from row_wise_normalization_rmsnorm_amd import inputs as I
+from row_wise_normalization_rmsnorm_amd.workloads import WORKLOADS
 from tests import parity as P
 from tests.test_gpu_parity import DEV, say
 
@@ -129,11 +130,12 @@ def test_every_ag_variant(dtype, monkeypatch):
 
 
 def test_rank_share_full_size():
-    """One rank's share of the 4096 x 8192 K = 8 workload over 8 ranks: 512
-    rows reduced over 8 partials, gathered into 8 buffers."""
-    w = I.case("bf16", 512, 8192, 8, seed=4242, std=8 ** -0.5)
-    stats = check_ag(w, I.make_inputs(w), 8, "rank share 512x8192 k=8 w=8")
-    say(f"[gpu] ag_rank_share: {stats}")
+    """The benchmark's workload: one rank's share of the 4096 x 8192 K = 8
+    workload over 8 ranks (512 rows reduced over 8 partials, gathered into 8
+    buffers), every row against the oracle."""
+    w = WORKLOADS["add_rmsnorm_ag_bf16_512x8192_k8_w8"]
+    stats = check_ag(w, I.make_inputs(w), w.gather, w.name)
+    say(f"[gpu] {w.name}: {stats}")
 
 
 def test_graph_replay():
