@@ -219,7 +219,7 @@ def report_summary(argv) -> int:
         f.write("# Per-workload report: GPU kernel, CPU oracle, parity\n\n")
         f.write("Commands: `python bench.py --workload W --no-ceiling` for every workload (the GPU "
                 "step timed with HIP events; the oracle timed on the host's cores, and on one), and "
-                "`python -m pytest tests/test_gpu_parity.py tests/test_gpu_block_sum.py "
+                "`python -m pytest tests/test_gpu_parity.py tests/test_gpu_allgather.py tests/test_gpu_block_sum.py "
                 "tests/test_gpu_gemm_scatter.py -m gpu -s -k \"workloads or full_size\"` for the "
                 "parity statistics (all rows of the 512-row workloads; 128+ "
                 "sampled rows of the full-size launches, whose residual is also checked whole).\n\n")
