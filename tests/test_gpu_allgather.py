@@ -171,3 +171,52 @@ def test_graph_replay():
         assert torch.equal(r.view(torch.int16), r_e.view(torch.int16)), rep
         for o, oe in zip(outs, outs_e):
             assert torch.equal(o.view(torch.int16), oe.view(torch.int16)), rep
+
+
+def test_tensor_parallel_layer_tail_emulation():
+    """The tail of a tensor-parallel layer on one GPU, W = 4 ranks emulated:
+    rank r's GEMM scatters its partial product's row chunks into the ranks'
+    receive buffers (gemm_scatter_fwd); rank q then reduces its W received
+    chunks with its residual, normalises, and stores the normalised chunk
+    into every rank's gather buffer (add_rmsnorm_ag_fwd).  Every rank ends
+    with the same full output; each received chunk matches the oracle's
+    GEMM within its bound, and rank q's residual and output match the fused
+    oracle on the chunks it received."""
+    import numpy as np
+
+    import oracle
+    from tests import test_gpu_gemm_scatter as G
+
+    world, m, n, k = 4, 256, 2048, 512
+    chunk = m // world
+    recv = torch.empty(world, world, chunk, n, dtype=torch.bfloat16, device=DEV)   # [q][r]
+    gathered = torch.full((world, m, n), float("nan"), dtype=torch.bfloat16, device=DEV)
+    ops = [G.make("bf16", m, n, k, False, seed=700 + r)[:2] for r in range(world)]
+    for r, (a, b) in enumerate(ops):
+        B.gemm_scatter_fwd([recv[q, r] for q in range(world)], a, b, rank=r)
+    res0 = I.matrix(77, I.RESIDUAL_ID, m, n, 1.0, "bf16").to(DEV)
+    res = res0.clone()
+    gam = I.matrix(77, I.GAMMA_ID, 1, n, 0.25, "bf16").reshape(n).to(DEV) + 1.0
+    for q in range(world):
+        rows = slice(q * chunk, (q + 1) * chunk)
+        B.add_rmsnorm_ag_fwd([gathered[j, rows] for j in range(world)], res[rows],
+                             [recv[q, r] for r in range(world)], gam, 1e-5)
+    torch.cuda.synchronize()
+    say("[gpu] tensor-parallel tail: 4 GEMMs + 4 add_rmsnorm_ag done")
+    g16 = gathered.view(torch.int16)
+    for j in range(1, world):
+        assert torch.equal(g16[j], g16[0]), f"rank {j}'s gathered output differs from rank 0's"
+    for r in (0, 3):
+        a, b = ops[r]
+        full = torch.cat([recv[q, r] for q in range(world)]).cpu()
+        want, y, mag = G.oracle_rows(a, b, None, 1.0, 0.0, world, "bf16")
+        G.compare(G.st(full), want, y, mag, k, "bf16", f"rank {r} partial")
+    for q in range(world):
+        rows = slice(q * chunk, (q + 1) * chunk)
+        parts = [I.to_storage(recv[q, r].cpu()) for r in range(world)]
+        o_out, o_res, _ = oracle.add_rmsnorm(parts, I.to_storage(res0[rows].cpu()),
+                                             I.to_storage(gam.cpu()), 1e-5, "bf16")
+        assert np.array_equal(I.to_storage(res[rows].cpu()), o_res), f"rank {q} residual"
+        got = I.to_storage(gathered[0, rows].cpu())
+        from tests import independent as ind
+        assert int(ind.ulp_distance(got, o_out, "bf16").max()) <= 2, f"rank {q} output"
