@@ -785,6 +785,30 @@ def main() -> int:
     for kind, l in lat.items():
         print(f"[bench] per-launch ({kind}): {json.dumps(l)}", file=sys.stderr, flush=True)
 
+    # the all-gather form against the same work unfused: add_rmsnorm_fwd into
+    # the first output, then device copies of it into the others
+    unfused = None
+    if w.gather:
+        def unfused_step(i):
+            s = sets[i % nsets]
+            B.add_rmsnorm_fwd(s["outs"][0], s["residual"], s["partials"], s["gamma"], w.eps)
+            for o in s["outs"][1:]:
+                o.copy_(s["outs"][0])
+
+        for i in range(5):
+            unfused_step(i)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(a.steps):
+            unfused_step(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ums = e0.elapsed_time(e1) / a.steps
+        unfused = {"what": f"add_rmsnorm_fwd, then {w.gather - 1} device copies of its output",
+                   "us": round(ums * 1e3, 2), "fused_speedup": round(ums / ms, 3)}
+        print(f"[bench] unfused (add_rmsnorm_fwd + {w.gather - 1} copies): {ums * 1e3:.2f} us, "
+              f"fused {ms * 1e3:.2f} us", file=sys.stderr, flush=True)
+
     traffic = traffic_for(kernel, w.name, w.op)
     metric = ("achieved HBM GB/s (% of peak) + rows/s, add_rmsnorm bf16 8192x4096"
               if w.name == HEADLINE else f"achieved HBM GB/s (% of peak) + rows/s, {w.describe()}")
@@ -816,6 +840,8 @@ def main() -> int:
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic},
     }
+    if unfused:
+        result["unfused_context"] = unfused
     if not a.no_ceiling:
         del sets
         torch.cuda.empty_cache()
