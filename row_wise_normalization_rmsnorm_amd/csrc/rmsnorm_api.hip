@@ -403,8 +403,9 @@ int run(Types t, void* out, int64_t out_stride, void* residual, int64_t res_stri
   rmsn::GatherPtrs gp{};
   if (gather) {
     // out is gather[0]; every gather buffer is checked like out, and none
-    // may touch an input, gamma, the residual or another gather buffer (not
-    // even exactly: a later copy would overwrite an input already read).
+    // may touch an input, gamma, the residual or another gather buffer, not
+    // even exactly: the buffers stand for distinct ranks' gather buffers, so
+    // the in-place exception of the single-output form is not carried over.
     gp.n = ngather;
     for (int j = 0; j < ngather; ++j) {
       const Span oj{gather[j], o.pitch, o.len, rows};
