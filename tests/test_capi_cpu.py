@@ -359,3 +359,17 @@ def test_ag_plans_mirror_the_fused_dispatcher():
     for dtype in ("bf16", "f16", "f32"):
         names = B.rmsnorm_variants_ag(dtype)
         assert len(names) == len(set(names)) > 40 and all(n.endswith(",ag>") for n in names)
+
+
+def test_ag_binding_checks_before_the_library():
+    """The Python binding rejects host tensors and mismatched shapes or
+    dtypes of the all-gather form before any library call."""
+    import torch
+    r = torch.zeros(4, 64, dtype=torch.bfloat16)
+    g = torch.ones(64, dtype=torch.bfloat16)
+    with pytest.raises(B.RmsnormError):
+        B.add_rmsnorm_ag_fwd([torch.empty_like(r)], r, [r.clone()], g, 1e-6)       # host tensors
+    with pytest.raises(B.RmsnormError):
+        B.add_rmsnorm_ag_fwd([torch.empty(4, 32, dtype=torch.bfloat16)], r, [r], g, 1e-6)
+    with pytest.raises(B.RmsnormError):
+        B.add_rmsnorm_ag_fwd([torch.empty_like(r, dtype=torch.float16)], r, [r], g, 1e-6)
