@@ -564,22 +564,38 @@ CEILING_PATTERNS = [
 ]
 
 
-def ceiling_sweep(stream_mib: int = 64, steps: int = 40) -> int:
-    """Time libstreamprobe.so over every read/write mix above, every grid,
-    workgroup size and unroll it offers; streams of stream_mib MiB rotated
-    through >= 1 GiB.  One JSON line per configuration."""
+CEILING_GRIDS = (256, 384, 512, 768, 1024, 2048, 4096, 8192, 16384)
+CEILING_POLICIES = 8  # libstreamprobe.so's cache policies (stream_probe_policy)
+
+
+def ceiling_sweep(stream_mib: int = 64, steps: int = 40, patterns: str = "",
+                  policies: str = "") -> int:
+    """Time libstreamprobe.so over every read/write mix above (or those whose
+    name contains one of the |-separated ``patterns``), every grid, workgroup
+    size, unroll, layout and cache policy it offers; streams of stream_mib MiB
+    rotated through >= 1 GiB.  One JSON line per configuration."""
     import ctypes
     import torch
     lib = ctypes.CDLL(os.path.join(ROOT, "row_wise_normalization_rmsnorm_amd", "libstreamprobe.so"))
     vp = ctypes.c_void_p
-    lib.stream_probe_shape.argtypes = [ctypes.POINTER(vp), ctypes.c_int, ctypes.POINTER(vp),
-                                       ctypes.c_int, ctypes.c_int64, vp, ctypes.c_int, ctypes.c_int,
-                                       ctypes.c_int, ctypes.c_int, vp]
+    lib.stream_probe_pol.argtypes = [ctypes.POINTER(vp), ctypes.c_int, ctypes.POINTER(vp),
+                                     ctypes.c_int, ctypes.c_int64, vp, ctypes.c_int, ctypes.c_int,
+                                     ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]
+    cpol = {}
+    for pol in range(CEILING_POLICIES):
+        lb, sb = ctypes.c_int(), ctypes.c_int()
+        if lib.stream_probe_policy(pol, ctypes.byref(lb), ctypes.byref(sb)) != 0:
+            raise RuntimeError(f"stream_probe_policy({pol}) failed")
+        cpol[pol] = (("global " if pol == 0 else "buffer ") + cpol_name(lb.value),
+                     ("global " if pol == 0 else "buffer ") + cpol_name(sb.value))
+    pols = [int(x) for x in policies.split(",")] if policies else list(range(CEILING_POLICIES))
     nbytes = stream_mib << 20
     n16 = nbytes // 16
     sink = torch.zeros(64, dtype=torch.uint8, device="cuda:0")
     stream = torch.cuda.current_stream()
     for name, nr, writes in CEILING_PATTERNS:
+        if patterns and not any(f in name for f in patterns.split("|")):
+            continue
         nbuf = max([nr] + [j + 1 for j in writes])
         nsets = max(1, -(-(1 << 30) // (nbuf * nbytes)))
         bufs = [[torch.empty(nbytes, dtype=torch.uint8, device="cuda:0").fill_(j + 1)
@@ -588,15 +604,15 @@ def ceiling_sweep(stream_mib: int = 64, steps: int = 40) -> int:
                  (vp * max(len(writes), 1))(*[b[j].data_ptr() for j in writes])) for b in bufs]
         moved = (nr + len(writes)) * nbytes
         best = None
-        shapes = [(g, b, u, c) for c in (0, 1) for g in (1024, 2048, 4096, 8192, 16384)
+        shapes = [(g, b, u, c, p) for p in pols for c in (0, 1) for g in CEILING_GRIDS
                   for b in (256, 512, 1024) for u in (1, 2, 4, 8)]
-        for grid, block, unroll, contig in shapes:
+        for grid, block, unroll, contig, pol in shapes:
             def launch(i):
                 ra, wa = args[i % nsets]
-                rc = lib.stream_probe_shape(ra, nr, wa, len(writes), n16, sink.data_ptr(),
-                                            grid, block, unroll, contig, stream.cuda_stream)
+                rc = lib.stream_probe_pol(ra, nr, wa, len(writes), n16, sink.data_ptr(),
+                                          grid, block, unroll, contig, pol, stream.cuda_stream)
                 if rc != 0:
-                    raise RuntimeError(f"stream_probe_shape failed: {rc}")
+                    raise RuntimeError(f"stream_probe_pol failed: {rc}")
             for i in range(3):
                 launch(i)
             e0 = torch.cuda.Event(enable_timing=True)
@@ -611,16 +627,25 @@ def ceiling_sweep(stream_mib: int = 64, steps: int = 40) -> int:
             row = {"pattern": name, "reads": nr, "writes": len(writes),
                    "in_place": sum(j < nr for j in writes), "grid": grid, "block": block,
                    "unroll": unroll, "layout": "contiguous" if contig else "grid-stride",
+                   "policy": pol, "load_policy": cpol[pol][0], "store_policy": cpol[pol][1],
                    "us": round(us, 3), "gbs": round(moved / us / 1e3, 1)}
             print(json.dumps(row), flush=True)
             if best is None or row["gbs"] > best["gbs"]:
                 best = row
         print(f"[ceiling] {name}: best {best['gbs']} GB/s (grid {best['grid']}, block "
-              f"{best['block']}, unroll {best['unroll']}, {best['layout']})", file=sys.stderr,
+              f"{best['block']}, unroll {best['unroll']}, {best['layout']}, loads "
+              f"{best['load_policy']}, stores {best['store_policy']})", file=sys.stderr,
               flush=True)
         del bufs
         torch.cuda.empty_cache()
     return 0
+
+
+def cpol_name(bits: int) -> str:
+    """The cache-policy bits of a vector memory instruction, as the assembler
+    spells them (bit 0 sc0, bit 1 nt, bit 4 sc1); "default" for none."""
+    names = [n for b, n in ((1, "sc0"), (16, "sc1"), (2, "nt")) if bits & b]
+    return " ".join(names) if names else "default"
 
 
 def copy_calibration() -> None:
@@ -647,6 +672,11 @@ def main() -> int:
     ap.add_argument("--ceiling-sweep", action="store_true",
                     help="time the plain streaming probe over read/write mixes and launch "
                          "shapes (one JSON line each) and exit")
+    ap.add_argument("--ceiling-patterns", default="",
+                    help="ceiling sweep: only the mixes whose name contains one of these "
+                         "|-separated substrings")
+    ap.add_argument("--ceiling-policies", default="",
+                    help="ceiling sweep: comma-separated cache policies (default: all)")
     ap.add_argument("--sweep", action="store_true",
                     help="time every compiled kernel variant that can run the workload "
                          "(forced through RMSNORM_VARIANT) and print one line per variant")
@@ -685,7 +715,7 @@ def main() -> int:
         copy_calibration()
         return 0
     if a.ceiling_sweep:
-        return ceiling_sweep()
+        return ceiling_sweep(patterns=a.ceiling_patterns, policies=a.ceiling_policies)
 
     from row_wise_normalization_rmsnorm_amd.workloads import GEMM_WORKLOADS
     if a.gemm_shapes:

@@ -148,36 +148,64 @@ def sweep_summary(argv) -> int:
 def ceiling_summary(argv) -> int:
     """profiles/hbm_ceiling_sweep.md from the JSON lines of
     ``bench.py --ceiling-sweep``: the best launch shape of the plain
-    streaming probe for every read/write mix, and the spread over shapes."""
+    streaming probe for every read/write mix, the best per grid size and per
+    cache policy, and the spread over shapes."""
     ap = argparse.ArgumentParser()
     ap.add_argument("jsonl")
+    ap.add_argument("--command", default="python bench.py --ceiling-sweep")
     a = ap.parse_args(argv)
     rows = [json.loads(l) for l in open(a.jsonl) if l.startswith("{")]
     order = []
     for r in rows:
         if r["pattern"] not in order:
             order.append(r["pattern"])
+    grids = sorted({r["grid"] for r in rows})
+    pols = sorted({(r.get("policy", 0), r.get("load_policy", "global nt"),
+                    r.get("store_policy", "global nt")) for r in rows})
     md = os.path.join(PROFILES, "hbm_ceiling_sweep.md")
     with open(md, "w") as f:
         f.write("# HBM ceiling of a plain streaming kernel, by read/write mix\n\n")
-        f.write("Command: `python bench.py --ceiling-sweep` (libstreamprobe.so: 16-byte nontemporal "
-                "loads and stores, every lane `unroll` chunks in flight per stream, grid-stride "
-                "loop; 64 MiB per stream, buffers rotated through >= 1 GiB; HIP events over 40 "
-                "launches per shape).  Swept: grid 1024-16384 workgroups, workgroup 256/512/1024 "
-                "lanes, unroll 1/2/4/8, and two layouts -- a grid-stride loop, or each workgroup "
-                "streaming one contiguous range (120 shapes per mix).\n\n")
+        f.write(f"Command: `{a.command}` (libstreamprobe.so: 16-byte loads and stores, every lane "
+                "`unroll` chunks in flight per stream; 64 MiB per stream, buffers rotated through "
+                ">= 1 GiB; HIP events over 40 launches per shape).  Swept: grid "
+                f"{grids[0]}-{grids[-1]} workgroups ({', '.join(map(str, grids))}), workgroup "
+                "256/512/1024 lanes, unroll 1/2/4/8, two layouts -- a grid-stride loop, or each "
+                "workgroup streaming one contiguous range -- and the cache policies below "
+                f"({len(rows) // max(1, len(order))} shapes per mix).  Policy 0 is the "
+                "global_load/store_dwordx4 pair with the nontemporal bit, as the RMSNorm kernels "
+                "issue them; the others are buffer_load/store_dwordx4 with the named "
+                "cache-policy bits.\n\n")
         f.write("| mix | reads | writes (in place) | best GB/s | % of 8 TB/s | best shape "
-                "(grid, block, unroll, layout) | best contiguous GB/s | median over shapes GB/s |\n"
-                "|---|---|---|---|---|---|---|---|\n")
+                "(grid, block, unroll, layout) | best policy (loads / stores) | best with policy 0 "
+                "GB/s | median over shapes GB/s |\n|---|---|---|---|---|---|---|---|---|\n")
         for name in order:
             rs = [r for r in rows if r["pattern"] == name]
             b = max(rs, key=lambda r: r["gbs"])
-            cont = [r["gbs"] for r in rs if r.get("layout") == "contiguous"]
+            p0 = [r["gbs"] for r in rs if r.get("policy", 0) == 0]
             med = statistics.median(r["gbs"] for r in rs)
             f.write(f"| {name} | {b['reads']} | {b['writes']} ({b['in_place']}) | {b['gbs']:.0f} | "
                     f"{b['gbs'] / 80:.1f} | {b['grid']}, {b['block']}, {b['unroll']}, "
-                    f"{b.get('layout', 'grid-stride')} | {max(cont) if cont else float('nan'):.0f} | "
+                    f"{b.get('layout', 'grid-stride')} | {b.get('load_policy', 'global nt')} / "
+                    f"{b.get('store_policy', 'global nt')} | {max(p0) if p0 else float('nan'):.0f} | "
                     f"{med:.0f} |\n")
+        f.write("\n## Best GB/s per grid size (over workgroup size, unroll, layout and policy)\n\n")
+        f.write("| mix | " + " | ".join(str(g) for g in grids) + " |\n|---|"
+                + "---|" * len(grids) + "\n")
+        for name in order:
+            cells = []
+            for g in grids:
+                v = [r["gbs"] for r in rows if r["pattern"] == name and r["grid"] == g]
+                cells.append(f"{max(v):.0f}" if v else "")
+            f.write(f"| {name} | " + " | ".join(cells) + " |\n")
+        f.write("\n## Best GB/s per cache policy (over every launch shape)\n\n")
+        f.write("| mix | " + " | ".join(f"{p}: {l} / {s_}" for p, l, s_ in pols) + " |\n|---|"
+                + "---|" * len(pols) + "\n")
+        for name in order:
+            cells = []
+            for p, _, _ in pols:
+                v = [r["gbs"] for r in rows if r["pattern"] == name and r.get("policy", 0) == p]
+                cells.append(f"{max(v):.0f}" if v else "")
+            f.write(f"| {name} | " + " | ".join(cells) + " |\n")
         f.write(f"\n{len(rows)} configurations timed.\n")
     print(md)
     return 0

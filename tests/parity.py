@@ -10,6 +10,9 @@ The bar (written here once, used by every GPU parity test):
 """
 from __future__ import annotations
 
+import concurrent.futures as cf
+import os
+
 import numpy as np
 import torch
 
@@ -21,8 +24,9 @@ F32_REL_TOL = 1e-5
 HALF_ULP_TOL = 2
 
 
-def storage(t: torch.Tensor) -> np.ndarray:
-    return I.to_storage(t)
+def storage(t) -> np.ndarray:
+    """dtype storage of a torch tensor (numpy arrays pass through)."""
+    return t if isinstance(t, np.ndarray) else I.to_storage(t)
 
 
 GAMMA_NAME = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16"}
@@ -88,6 +92,60 @@ def compare(dtype: str, gpu_out: torch.Tensor, ref: dict, gpu_residual: torch.Te
         if nz.any():
             stats["max_rel_err"] = float((np.abs(gv[ok][nz] - y64[ok][nz]) / np.abs(y64[ok][nz])).max())
     return stats
+
+
+def host_threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def compare_whole(dtype: str, eps: float, gpu_out: np.ndarray, gpu_res, gamma: np.ndarray,
+                  *, x: np.ndarray = None, partials=None, residual: np.ndarray = None,
+                  what: str = "", block_elems: int = 1 << 22, threads: int = 0) -> dict:
+    """Every row of a full-size result against the oracle.  All arrays are
+    host storage (numpy) of the same [rows, hidden] shape: the GPU's output
+    and residual (gpu_res None for the plain form), and the inputs as they
+    were before the launch.  The oracle runs over blocks of about
+    ``block_elems`` elements, one block per task on the host's threads, and
+    each block is compared with ``compare`` as soon as it is computed, so the
+    oracle's double-precision output never exists for the whole tensor.
+    Returns the statistics over all rows."""
+    rows, hidden = gpu_out.shape
+    br = max(1, block_elems // hidden)
+    blocks = [(a, min(rows, a + br)) for a in range(0, rows, br)]
+
+    def job(b):
+        a, z = b
+        if partials is None:
+            o, _, y64 = oracle.rmsnorm(x[a:z], gamma, eps, dtype, want_f64=True)
+            ref = {"out": o, "y64": y64}
+            st = compare(dtype, gpu_out[a:z], ref, what=f"{what} rows [{a}, {z})")
+        else:
+            o, rn, _, y64 = oracle.add_rmsnorm([p[a:z] for p in partials], residual[a:z], gamma,
+                                               eps, dtype, want_f64=True)
+            ref = {"out": o, "y64": y64, "residual": rn}
+            st = compare(dtype, gpu_out[a:z], ref, gpu_res[a:z], what=f"{what} rows [{a}, {z})")
+        st["elements"] = (z - a) * hidden
+        return st
+
+    with cf.ThreadPoolExecutor(threads or host_threads()) as ex:
+        stats = list(ex.map(job, blocks))
+    n = sum(s["elements"] for s in stats)
+    out = {"rows_checked": rows, "elements_checked": n}
+    if gpu_res is not None:
+        out["residual_bit_exact"] = all(s.get("residual_bit_exact") for s in stats)
+    if dtype == "f32":
+        out["max_rel_err"] = max(s["max_rel_err"] for s in stats)
+    else:
+        out["max_ulp"] = max(s["max_ulp"] for s in stats)
+        out["frac_not_equal"] = sum(s["frac_not_equal"] * s["elements"] for s in stats) / n
+        rel = [s["max_rel_err"] for s in stats if "max_rel_err" in s]
+        if rel:
+            out["max_rel_err"] = max(rel)
+    return out
 
 
 # ---- kernel variants ----------------------------------------------------------
