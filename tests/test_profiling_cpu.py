@@ -91,14 +91,24 @@ def test_ceiling_summary(tmp_path, monkeypatch):
     monkeypatch.setattr(prof, "PROFILES", str(tmp_path / "profiles"))
     os.makedirs(tmp_path / "profiles")
     lines = [{"pattern": "read 1", "reads": 1, "writes": 0, "in_place": 0, "grid": g, "block": 256,
-              "unroll": 4, "layout": lay, "us": 1.0, "gbs": v}
-             for g, lay, v in ((1024, "grid-stride", 5000.0), (2048, "contiguous", 5100.0),
-                               (4096, "grid-stride", 6000.0))]
+              "unroll": 4, "layout": lay, "us": 1.0, "gbs": v, "policy": pol,
+              "load_policy": lp, "store_policy": sp}
+             for g, lay, v, pol, lp, sp in (
+                 (1024, "grid-stride", 5000.0, 0, "global nt", "global nt"),
+                 (2048, "contiguous", 5100.0, 0, "global nt", "global nt"),
+                 (4096, "grid-stride", 6000.0, 0, "global nt", "global nt"),
+                 (512, "grid-stride", 6100.0, 5, "buffer sc0 sc1 nt", "buffer sc0 sc1 nt"))]
     src = tmp_path / "c.jsonl"
     src.write_text("\n".join(json.dumps(x) for x in lines) + "\n")
     assert prof.ceiling_summary([str(src)]) == 0
     md = open(tmp_path / "profiles" / "hbm_ceiling_sweep.md").read()
-    assert "| read 1 | 1 | 0 (0) | 6000 | 75.0 | 4096, 256, 4, grid-stride | 5100 | 5100 |" in md
+    # best overall (policy 5 at grid 512), best with policy 0, median of the four
+    assert ("| read 1 | 1 | 0 (0) | 6100 | 76.2 | 512, 256, 4, grid-stride | buffer sc0 sc1 nt / "
+            "buffer sc0 sc1 nt | 6000 | 5550 |") in md
+    # per grid, in grid order
+    assert "| read 1 | 6100 | 5000 | 5100 | 6000 |" in md
+    # per policy
+    assert "| read 1 | 6000 | 6100 |" in md
 
 
 def test_bench_refuses_more_than_one_gpu():
