@@ -517,17 +517,16 @@ def sweep(w, step, a, B) -> int:
     for v in (B.rmsnorm_variants_ag if w.gather else B.rmsnorm_variants)(w.dtype):
         if a.variant_filter and not any(f in v for f in a.variant_filter.split("|")):
             continue
-        os.environ["RMSNORM_VARIANT"] = v
-        try:
-            plan(w.rows, w.hidden, w.k, w.dtype)
-            names.append(v)
-        except B.RmsnormError:
-            pass
+        with B.forced(v):
+            try:
+                plan(w.rows, w.hidden, w.k, w.dtype)
+                names.append(v)
+            except B.RmsnormError:
+                pass
     times = {v: [] for v in names}
-    try:
-        for rep in range(a.repeat):
-            for v in names:
-                os.environ["RMSNORM_VARIANT"] = v
+    for rep in range(a.repeat):
+        for v in names:
+            with B.forced(v):
                 for i in range(a.warmup):
                     step(i)
                 torch.cuda.synchronize()
@@ -538,12 +537,10 @@ def sweep(w, step, a, B) -> int:
                     step(i)
                 e1.record()
                 torch.cuda.synchronize()
-                us = e0.elapsed_time(e1) / a.steps * 1e3
-                times[v].append(us)
-                print(f"[sweep {rep}] {us:9.2f} us {w.algorithmic_bytes() / us / 1e3:7.0f} GB/s  {v}"
-                      f"{'  <- dispatcher' if v == default else ''}", file=sys.stderr, flush=True)
-    finally:
-        os.environ.pop("RMSNORM_VARIANT", None)
+            us = e0.elapsed_time(e1) / a.steps * 1e3
+            times[v].append(us)
+            print(f"[sweep {rep}] {us:9.2f} us {w.algorithmic_bytes() / us / 1e3:7.0f} GB/s  {v}"
+                  f"{'  <- dispatcher' if v == default else ''}", file=sys.stderr, flush=True)
     rows = sorted((statistics.median(t), v, t) for v, t in times.items())
     for us, v, t in rows:
         print(json.dumps({"workload": w.name, "variant": v, "us": round(us, 3),
@@ -679,7 +676,7 @@ def main() -> int:
                     help="ceiling sweep: comma-separated cache policies (default: all)")
     ap.add_argument("--sweep", action="store_true",
                     help="time every compiled kernel variant that can run the workload "
-                         "(forced through RMSNORM_VARIANT) and print one line per variant")
+                         "(forced through rmsnorm_tune) and print one line per variant")
     ap.add_argument("--repeat", type=int, default=1, help="sweep rounds (median reported)")
     ap.add_argument("--variant-filter", default="",
                     help="sweep only variants containing one of these |-separated substrings")

@@ -177,16 +177,27 @@ int rmsnorm_plan(int64_t rows, int64_t hidden, int k, int dtype, int align, char
 /*
  * rmsnorm_variants -- names of every compiled kernel variant for dtype,
  * newline-separated, into buf.  Returns the number of variants (>= 0) or an
- * error code.  Any name can be forced for every call by setting the
- * environment variable RMSNORM_VARIANT to it (a call the variant cannot run
- * then fails with RMSN_ERR_SHAPE); RMSNORM_GRID_CAP=<n> caps the number of
- * workgroups per launch (rows are then processed in a grid-stride loop).
- * Both exist for tuning and testing; unset, the dispatcher decides.
+ * error code.  Any name can be forced with rmsnorm_tune.
  */
 int rmsnorm_variants(int dtype, char* buf, int buflen);
 
+/*
+ * rmsnorm_tune -- for tuning and testing only.  From now on every call of
+ * this process (every entry point of this header, and the plan queries)
+ * uses the kernel variant named `variant` (a name from rmsnorm_variants,
+ * rmsnorm_variants_ag or rmsnorm_variants_ex; a call the variant cannot run
+ * then fails with RMSN_ERR_SHAPE), and launches at most grid_cap workgroups
+ * (rows beyond are processed in a grid-stride loop).  variant NULL or ""
+ * restores the dispatcher's choice; grid_cap <= 0 restores the default
+ * grid.  Nothing else (no environment variable) changes the choice.  Set it
+ * before the calls it should affect: it is not synchronised with calls
+ * running on other threads.  Returns RMSN_OK, or RMSN_ERR_SHAPE for a name
+ * longer than 127 bytes (nothing is changed then).
+ */
+int rmsnorm_tune(const char* variant, int64_t grid_cap);
+
 /* rmsnorm_plan_ag / rmsnorm_variants_ag -- the same for add_rmsnorm_ag_fwd
- * (k >= 1; names end in ",ag>"; RMSNORM_VARIANT forces them the same way). */
+ * (k >= 1; names end in ",ag>"; rmsnorm_tune forces them the same way). */
 int rmsnorm_plan_ag(int64_t rows, int64_t hidden, int k, int dtype, int align, char* buf,
                     int buflen);
 int rmsnorm_variants_ag(int dtype, char* buf, int buflen);

@@ -7,6 +7,7 @@ built, or a call fails, a ``RmsnormError`` is raised.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 import threading
@@ -23,7 +24,7 @@ KMAX = 16
 EXPORTS = ("rmsnorm_fwd", "add_rmsnorm_fwd", "rmsnorm_strerror", "rmsnorm_last_error",
            "rmsnorm_plan", "rmsnorm_variants", "rmsnorm_fwd_ex", "add_rmsnorm_fwd_ex",
            "rmsnorm_plan_ex", "rmsnorm_variants_ex", "rmsnorm_plan_call", "add_rmsnorm_ag_fwd",
-           "rmsnorm_plan_ag", "rmsnorm_variants_ag")
+           "rmsnorm_plan_ag", "rmsnorm_variants_ag", "rmsnorm_tune")
 GATHER_MAX = 16
 BLOCK_SUM_EXPORTS = ("block_all_reduce_sum",)
 GEMM_SCATTER_EXPORTS = ("gemm_scatter_fwd", "gemm_scatter_tile_n", "gemm_scatter_tiles",
@@ -99,6 +100,8 @@ def lib() -> ctypes.CDLL:
             l.rmsnorm_plan_ag.restype = c_int
             l.rmsnorm_variants_ag.argtypes = [c_int, ctypes.c_char_p, c_int]
             l.rmsnorm_variants_ag.restype = c_int
+            l.rmsnorm_tune.argtypes = [ctypes.c_char_p, i64]
+            l.rmsnorm_tune.restype = c_int
             l.block_all_reduce_sum.argtypes = [vp, vp, i64, c_int, vp, i64, vp]
             l.block_all_reduce_sum.restype = c_int
             l.gemm_scatter_fwd.argtypes = [ctypes.POINTER(vp), i64, c_int, c_int, vp, i64, vp,
@@ -327,6 +330,24 @@ def rmsnorm_variants(dtype: str) -> list:
     if n < 0:
         _check(n)
     return [s for s in buf.value.decode().split("\n") if s]
+
+
+def tune(variant: Optional[str] = None, grid_cap: int = 0) -> None:
+    """Tuning and tests only: force a kernel variant for every later call
+    (None: the dispatcher decides) and cap the workgroups per launch
+    (0: the default grid).  See rmsnorm_tune in include/rmsnorm.h."""
+    _check(lib().rmsnorm_tune(variant.encode() if variant else None, int(grid_cap)))
+
+
+@contextlib.contextmanager
+def forced(variant: Optional[str] = None, grid_cap: int = 0):
+    """``with forced(name):`` runs the block with a forced variant and grid
+    cap, and restores the dispatcher's choice afterwards."""
+    tune(variant, grid_cap)
+    try:
+        yield
+    finally:
+        tune(None, 0)
 
 
 _workspaces = {}

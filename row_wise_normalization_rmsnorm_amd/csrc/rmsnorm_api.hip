@@ -22,9 +22,12 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 
 #include "../../include/rmsnorm.h"
 #include "rmsnorm_kernels.hpp"
+#include "rmsnorm_span.hpp"
 #include "rmsnorm_variants.hpp"
 
 const rmsn::Variant* rmsn_table_f32(int* n);
@@ -39,7 +42,22 @@ const rmsn::Variant* rmsn_table_ag_bf16(int* n);
 
 namespace {
 
+using rmsn_host::align_of;
+using rmsn_host::align_of_int;
+using rmsn_host::overlap;
+using rmsn_host::same_span;
+using rmsn_host::Span;
+
 thread_local char g_last_error[512] = "";
+
+// Process-wide tuning overrides, set only through rmsnorm_tune (never from
+// the environment): a forced variant name and a cap on workgroups per
+// launch.  A call reads them once, without a lock; rmsnorm_tune is meant to
+// run before the calls it should affect, not concurrently with them.
+std::mutex g_tune_mutex;
+char g_forced[128] = "";
+std::atomic<bool> g_forced_on{false};
+std::atomic<int64_t> g_grid_cap{0};
 
 int fail(int code, const char* fmt, ...) {
   va_list ap;
@@ -194,16 +212,16 @@ int choose(Types t, int64_t rows, int64_t hidden, int k, Aligns al, Plan* plan, 
   const int vb = widest_chunk(t, hidden, al);
   const rmsn::Variant* v = nullptr;
 
-  const char* forced = getenv("RMSNORM_VARIANT");
-  if (forced && *forced) {
+  const char* forced = g_forced_on.load(std::memory_order_acquire) ? g_forced : nullptr;
+  if (forced) {
     int n = 0;
     const rmsn::Variant* tab = table_for(t, &n, ag);
     for (int i = 0; i < n && !v; ++i)
       if (same_types(tab[i], t) && strcmp(tab[i].name, forced) == 0) v = &tab[i];
     if (!v)
-      return fail(RMSN_ERR_SHAPE, "RMSNORM_VARIANT=%s names no variant of these dtypes", forced);
+      return fail(RMSN_ERR_SHAPE, "forced variant %s names no variant of these dtypes", forced);
     if (!fits(*v, t, hidden, k, al))
-      return fail(RMSN_ERR_SHAPE, "RMSNORM_VARIANT=%s cannot run hidden=%lld k=%d", forced,
+      return fail(RMSN_ERR_SHAPE, "forced variant %s cannot run hidden=%lld k=%d", forced,
                   (long long)hidden, k);
   } else if (vb == 16 && hidden * s <= kVgprMaxBytes &&
              !(k >= 2 && hidden * s >= kStreamMinBytesForK)) {
@@ -259,49 +277,6 @@ int choose(Types t, int64_t rows, int64_t hidden, int k, Aligns al, Plan* plan, 
   return RMSN_OK;
 }
 
-// Largest power of two, capped at 16, dividing the value.
-int align_of_int(uint64_t u) {
-  int a = 16;
-  while (a > 1 && (u & (uint64_t)(a - 1))) a /= 2;
-  return a;
-}
-int align_of(const void* p) { return align_of_int((uintptr_t)p); }
-
-// A tensor as the kernels see it: `rows` rows of `len` bytes, row r at
-// base + r * pitch bytes.
-struct Span {
-  const void* base;
-  int64_t pitch;  // bytes
-  int64_t len;    // bytes per row
-  int64_t rows;
-  int align() const { return std::min(align_of(base), rows > 1 ? align_of_int((uint64_t)pitch) : 16); }
-  int64_t extent() const { return (rows - 1) * pitch + len; }
-};
-
-int64_t floor_div(int64_t a, int64_t b) { return a / b - ((a % b != 0) && ((a < 0) != (b < 0))); }
-int64_t ceil_div(int64_t a, int64_t b) { return -floor_div(-a, b); }
-
-// Do two spans share a byte?  Exact for equal pitches that are at least
-// both row lengths (rows interleave); otherwise the extents are compared.
-bool overlap(const Span& a, const Span& b) {
-  const intptr_t x = (intptr_t)a.base, y = (intptr_t)b.base;
-  if (!(x < y + b.extent() && y < x + a.extent())) return false;
-  if (a.pitch == b.pitch && a.rows > 1 && b.rows > 1 && a.pitch >= a.len && a.pitch >= b.len) {
-    // row i of a is [x + i p, x + i p + la), row j of b is [y + j p, ...);
-    // they meet iff d + t p lies in (-lb, la) for d = y - x, t = j - i.
-    const int64_t p = a.pitch, d = (int64_t)(y - x);
-    int64_t lo = floor_div(-b.len - d, p) + 1, hi = ceil_div(a.len - d, p) - 1;
-    lo = std::max(lo, -(b.rows - 1));
-    hi = std::min(hi, a.rows - 1);
-    return lo <= hi;
-  }
-  return true;
-}
-
-bool same_span(const Span& a, const Span& b) {
-  return a.base == b.base && a.pitch == b.pitch && a.len == b.len;
-}
-
 int common_checks(int dtype, int64_t rows, int64_t hidden, float eps) {
   if (!known(dtype)) return fail(RMSN_ERR_DTYPE, "unknown dtype %d", dtype);
   if (rows < 0 || hidden < 1 || hidden > RMSN_MAX_HIDDEN)
@@ -337,11 +312,8 @@ int launch(const Plan& plan, Args a, void* stream) {
   a.chunks = plan.chunks;
   const int64_t rows_per_wg = v.kind == rmsn::kVgpr ? v.wgs / v.tpr : 1;
   int64_t groups = (a.rows + rows_per_wg - 1) / rows_per_wg;
-  int64_t cap = kGridCapDefault;
-  if (const char* e = getenv("RMSNORM_GRID_CAP")) {
-    const long long c = atoll(e);
-    if (c > 0) cap = c;
-  }
+  const int64_t tuned = g_grid_cap.load(std::memory_order_relaxed);
+  const int64_t cap = tuned > 0 ? tuned : kGridCapDefault;
   const unsigned grid = (unsigned)(groups < cap ? groups : cap);
   void* args[] = {&a};
   hipError_t err = hipLaunchKernel(v.fn, dim3(grid), dim3(v.wgs), args, plan.lds_bytes,
@@ -569,6 +541,19 @@ const char* rmsnorm_strerror(int code) {
 }
 
 const char* rmsnorm_last_error(void) { return g_last_error; }
+
+int rmsnorm_tune(const char* variant, int64_t grid_cap) {
+  if (variant && strlen(variant) >= sizeof(g_forced))
+    return fail(RMSN_ERR_SHAPE, "variant name longer than %d bytes", (int)sizeof(g_forced) - 1);
+  std::lock_guard<std::mutex> lock(g_tune_mutex);
+  g_forced_on.store(false, std::memory_order_release);
+  if (variant && *variant) {
+    snprintf(g_forced, sizeof(g_forced), "%s", variant);
+    g_forced_on.store(true, std::memory_order_release);
+  }
+  g_grid_cap.store(grid_cap > 0 ? grid_cap : 0, std::memory_order_relaxed);
+  return RMSN_OK;
+}
 
 int rmsnorm_plan(int64_t rows, int64_t hidden, int k, int dtype, int align, char* buf,
                  int buflen) {

@@ -131,7 +131,7 @@ def sweep_summary(argv) -> int:
         f.write(f"# Every compiled variant on {a.workload}\n\n")
         cmd = a.command or (f"python bench.py --workload {a.workload} --sweep --repeat 3")
         f.write(f"Command: `{cmd}` (HIP events over the timed launches of each variant, forced "
-                "through RMSNORM_VARIANT; variants timed round-robin, median of the rounds; "
+                "through rmsnorm_tune; variants timed round-robin, median of the rounds; "
                 "buffers rotated as in the benchmark).\n\n")
         f.write("| rank | variant | median us | GB/s | rounds (us) | dispatcher |\n|---|---|---|---|---|---|\n")
         for i, r in enumerate(rows):

@@ -6,6 +6,7 @@ from __future__ import annotations
 import ctypes
 import os
 import re
+import subprocess
 
 import pytest
 
@@ -142,13 +143,30 @@ def test_plan_names_follow_the_dispatch_rule():
 def test_variant_table_and_forcing(monkeypatch):
     names = B.rmsnorm_variants("bf16")
     assert len(names) == len(set(names)) > 50
+    with B.forced("vgpr<bf16,tpr=64,npt=1,wg=256,k=1,nt>"):
+        assert B.rmsnorm_plan(4, 512, 1, "bf16") == "vgpr<bf16,tpr=64,npt=1,wg=256,k=1,nt>"
+        with pytest.raises(B.RmsnormError):
+            B.rmsnorm_plan(4, 1024, 1, "bf16")   # too long for that variant
+    assert B.rmsnorm_plan(4, 1024, 1, "bf16")    # the dispatcher decides again
+    with B.forced("no-such-kernel"):
+        with pytest.raises(B.RmsnormError):
+            B.rmsnorm_plan(4, 512, 1, "bf16")
+    with pytest.raises(B.RmsnormError):
+        B.tune("x" * 128)                        # longer than the name slot
+
+
+def test_environment_does_not_change_calls(monkeypatch):
+    """The library reads no environment variable: variables that once forced
+    a variant or capped the grid, set after load, change neither the plan of
+    a call nor the check of a call's arguments."""
+    base = B.rmsnorm_plan(8192, 4096, 1, "bf16")
+    ex = plan_call(rows=8192, hidden=4096)
     monkeypatch.setenv("RMSNORM_VARIANT", "vgpr<bf16,tpr=64,npt=1,wg=256,k=1,nt>")
-    assert B.rmsnorm_plan(4, 512, 1, "bf16") == "vgpr<bf16,tpr=64,npt=1,wg=256,k=1,nt>"
-    with pytest.raises(B.RmsnormError):
-        B.rmsnorm_plan(4, 1024, 1, "bf16")   # too long for that variant
+    monkeypatch.setenv("RMSNORM_GRID_CAP", "7")
+    assert B.rmsnorm_plan(8192, 4096, 1, "bf16") == base
+    assert plan_call(rows=8192, hidden=4096) == ex
     monkeypatch.setenv("RMSNORM_VARIANT", "no-such-kernel")
-    with pytest.raises(B.RmsnormError):
-        B.rmsnorm_plan(4, 512, 1, "bf16")
+    assert B.rmsnorm_plan(8192, 4096, 1, "bf16") == base
 
 
 def fwd_ex(**kw):
@@ -373,3 +391,18 @@ def test_ag_binding_checks_before_the_library():
         B.add_rmsnorm_ag_fwd([torch.empty(4, 32, dtype=torch.bfloat16)], r, [r], g, 1e-6)
     with pytest.raises(B.RmsnormError):
         B.add_rmsnorm_ag_fwd([torch.empty_like(r, dtype=torch.float16)], r, [r], g, 1e-6)
+
+
+def test_overlap_brute_force(tmp_path):
+    """The aliasing test (rmsn_host::overlap in csrc/rmsnorm_span.hpp),
+    compiled on the host, against brute force over the bytes of random
+    row-strided spans, unequal row counts included: it never misses a shared
+    byte, and is exact for interleaving rows of one pitch."""
+    src = os.path.join(ROOT, "tests", "span_bruteforce.cpp")
+    inc = os.path.join(ROOT, "row_wise_normalization_rmsnorm_amd", "csrc")
+    exe = str(tmp_path / "span_bruteforce")
+    subprocess.run(["g++", "-O2", "-std=c++17", "-Wall", "-I", inc, "-o", exe, src], check=True)
+    r = subprocess.run([exe, "300000"], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0 and r.stdout.startswith("ok "), r.stdout + r.stderr
+    cases, exact = map(int, r.stdout.split()[1:3])
+    assert cases == 300000 and exact > 10000

@@ -116,7 +116,7 @@ def test_every_ag_variant(dtype, monkeypatch):
     for i, name in enumerate(names):
         hidden, rows, k = P.variant_case(dtype, name)
         w = I.case(dtype, rows, hidden, k, seed=500 + i, std=0.5)
-        monkeypatch.setenv("RMSNORM_VARIANT", name)
+        B.tune(name)
         assert B.rmsnorm_plan_ag(rows, hidden, k, dtype, align=16) == name
         d = I.make_inputs(w)
         say(f"[gpu] ag variant {name}: {w.describe()}")
@@ -126,7 +126,7 @@ def test_every_ag_variant(dtype, monkeypatch):
         P.compare(dtype, outs[0], ref, res, what=name)
         iv = INT[I.TORCH_DTYPE[dtype]]
         assert torch.equal(outs[0].view(iv), outs[1].view(iv)), name
-    monkeypatch.delenv("RMSNORM_VARIANT")
+    B.tune(None)
 
 
 def test_rank_share_full_size():
@@ -136,6 +136,30 @@ def test_rank_share_full_size():
     w = WORKLOADS["add_rmsnorm_ag_bf16_512x8192_k8_w8"]
     stats = check_ag(w, I.make_inputs(w), w.gather, w.name)
     say(f"[gpu] {w.name}: {stats}")
+
+
+def test_rows_past_2gib():
+    """Two outputs over 70000 x 16384 bf16 (each tensor 2.29 GB, so the last
+    rows of every buffer, the gather buffers included, lie past 2^31 bytes):
+    every row of both outputs and of the residual against the oracle, in row
+    blocks."""
+    w = I.case("bf16", 70000, 16384, 1, seed=71)
+    say(f"[gpu] ag past 2 GiB: {w.describe()}: generating inputs on the device")
+    d = I.make_inputs(w, device=DEV)
+    host_p, host_r = I.to_storage(d["partials"][0]), I.to_storage(d["residual"])
+    outs = [torch.empty_like(d["residual"]) for _ in range(2)]
+    say(f"[gpu] ag past 2 GiB: plan {B.rmsnorm_plan_ag(w.rows, w.hidden, 1, 'bf16')}")
+    B.add_rmsnorm_ag_fwd(outs, d["residual"], d["partials"], d["gamma"], w.eps)
+    torch.cuda.synchronize()
+    iv = torch.int16
+    assert torch.equal(outs[0].view(iv), outs[1].view(iv)), "the two gather buffers differ"
+    gpu_out, gpu_res = I.to_storage(outs[0]), I.to_storage(d["residual"])
+    g = I.to_storage(d["gamma"])
+    del outs, d
+    stats = P.compare_whole("bf16", w.eps, gpu_out, gpu_res, g, partials=[host_p],
+                            residual=host_r, what="ag past 2 GiB")
+    assert stats["rows_checked"] == 70000 and stats["residual_bit_exact"]
+    say(f"[gpu] ag past 2 GiB: whole tensor {stats}")
 
 
 def test_graph_replay():

@@ -215,10 +215,10 @@ def test_rescaled_rows(dtype, monkeypatch):
         kc = -1 if variant is None else int(variant.split("k=")[1].split(",")[0].rstrip(">"))
         k = {0: 0, 1: 1, -1: 2}[kc]
         if variant is None:
-            monkeypatch.delenv("RMSNORM_VARIANT", raising=False)
+            B.tune(None)
             hidden = 4096
         else:
-            monkeypatch.setenv("RMSNORM_VARIANT", variant)
+            B.tune(variant)
             hidden = None
             for h in (40, 512, 1000, 2048, 4096, 3000, 3001, 40000, 30000, 12000):
                 try:
@@ -231,7 +231,7 @@ def test_rescaled_rows(dtype, monkeypatch):
         for eps in (0.0, 1e-6):
             w, d = _rescue_case(dtype, hidden, 21, k, eps, seed=100 + i)
             check(w, d, f"rescaled rows {variant} H={hidden} eps={eps}")
-    monkeypatch.delenv("RMSNORM_VARIANT", raising=False)
+    B.tune(None)
 
 
 def test_graph_capture_general_interface_and_block_sum():

@@ -170,14 +170,14 @@ def test_convenience_wrappers_pick_the_general_form():
 @pytest.mark.parametrize("d,g,o", [c for c in COMBOS if not (c[0] == c[1] == c[2])])
 def test_every_mixed_variant(d, g, o, monkeypatch):
     """Every compiled variant of each general combination, forced through
-    RMSNORM_VARIANT on a case it can run (contiguous rows)."""
+    rmsnorm_tune on a case it can run (contiguous rows)."""
     names = B.rmsnorm_variants_ex(d, g, o)
     assert names
     say(f"[gpu] {len(names)} variants of {d},g={g},o={o}")
     for i, name in enumerate(names):
         hidden, rows, k = P.variant_case(d, name)
         w = I.case(d, rows, hidden, k, seed=i, std=0.5)
-        monkeypatch.setenv("RMSNORM_VARIANT", name)
+        B.tune(name)
         assert B.rmsnorm_plan_ex(rows, hidden, k, d, g, o) == name
         inp = I.make_inputs(w)
         gamma = I.gamma(w, DEV, dtype=g)
@@ -192,7 +192,7 @@ def test_every_mixed_variant(d, g, o, monkeypatch):
         ref = P.run_oracle(d, w.eps, x=inp.get("x"), partials=inp.get("partials"),
                            residual=inp.get("residual"), gamma=gamma.cpu(), out_dtype=o)
         P.compare(o, out.cpu(), ref, res.cpu() if k else None, what=f"variant {name}", res_dtype=d)
-    monkeypatch.delenv("RMSNORM_VARIANT")
+    B.tune(None)
 
 
 def test_random_general_calls():

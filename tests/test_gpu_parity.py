@@ -158,6 +158,18 @@ def test_tail_sweep(dtype, hidden):
         check(w, I.make_inputs(w), f"tail {dtype} H={hidden} k={k}")
 
 
+@pytest.mark.parametrize("dtype,hidden", [("bf16", 32768), ("f16", 32768), ("f32", 16384),
+                                          ("bf16", 32760), ("f32", 16383)])
+def test_lds_stage_limit(dtype, hidden):
+    """Rows at the LDS stage budget (64 KiB of row: the largest the staged
+    streaming kernel takes) and just below it, plain and fused."""
+    for k in (0, 1):
+        w = I.case(dtype, 7, hidden, k, seed=hidden + k)
+        plan = B.rmsnorm_plan(7, hidden, k, dtype)
+        say(f"[gpu] lds stage limit {dtype} H={hidden} k={k}: {plan}")
+        check(w, I.make_inputs(w), f"lds stage limit {dtype} H={hidden} k={k}")
+
+
 @pytest.mark.parametrize("k", [2, 4, 5, 15, 16])
 def test_partial_counts(k):
     for dtype, hidden in (("bf16", 4096), ("f16", 1592), ("f32", 300), ("bf16", 12000)):
@@ -193,15 +205,15 @@ def test_every_variant(dtype, monkeypatch):
     for i, name in enumerate(names):
         hidden, rows, k = P.variant_case(dtype, name)
         w = I.case(dtype, rows, hidden, k, seed=i, std=0.5)
-        monkeypatch.setenv("RMSNORM_VARIANT", name)
+        B.tune(name)
         assert B.rmsnorm_plan(rows, hidden, k, dtype, align=16) == name
         check(w, I.make_inputs(w), f"variant {name}")
-    monkeypatch.delenv("RMSNORM_VARIANT")
+    B.tune(None)
 
 
 def test_grid_stride_loop(monkeypatch):
     """A capped grid makes every workgroup loop over several rows."""
-    monkeypatch.setenv("RMSNORM_GRID_CAP", "7")
+    B.tune(None, grid_cap=7)
     for dtype, hidden, k in (("bf16", 4096, 1), ("bf16", 1592, 0), ("bf16", 128, 1),
                              ("bf16", 16384, 1), ("f32", 333, 2), ("bf16", 4096, 8)):
         w = I.case(dtype, 203, hidden, k, seed=hidden)
