@@ -206,6 +206,35 @@ struct Vec {
       if constexpr (NT) __builtin_nontemporal_store(r.w[n], p + n); else p[n] = r.w[n];
     }
   }
+  // The same chunk through a buffer resource `rs` that covers one row of one
+  // tensor from a wave-uniform base (chunk c at byte offset c * BYTES), with
+  // the cache-policy bits CPOL on the instruction.  Chunks of whole 32-bit
+  // words only.
+  static constexpr bool BUFFERABLE = !SCALAR;
+  template <int CPOL>
+  __device__ static raw_t load_buf(__amdgpu_buffer_rsrc_t rs, int c) {
+    static_assert(BUFFERABLE, "buffer access moves whole words");
+    raw_t r;
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+      const int off = c * BYTES + n * AW * 4;
+      if constexpr (AW == 4) r.w[n] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, CPOL);
+      else if constexpr (AW == 2) r.w[n] = __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, CPOL);
+      else r.w[n] = __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, CPOL);
+    }
+    return r;
+  }
+  template <int CPOL>
+  __device__ static void store_buf(__amdgpu_buffer_rsrc_t rs, int c, const raw_t& r) {
+    static_assert(BUFFERABLE, "buffer access moves whole words");
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+      const int off = c * BYTES + n * AW * 4;
+      if constexpr (AW == 4) __builtin_amdgcn_raw_buffer_store_b128(r.w[n], rs, off, 0, CPOL);
+      else if constexpr (AW == 2) __builtin_amdgcn_raw_buffer_store_b64(r.w[n], rs, off, 0, CPOL);
+      else __builtin_amdgcn_raw_buffer_store_b32(r.w[n], rs, off, 0, CPOL);
+    }
+  }
   __device__ static void unpack(const raw_t& r, float (&f)[V]) {
     if constexpr (SCALAR) {
       f[0] = DT<T>::widen(r.w[0]);
@@ -236,6 +265,31 @@ struct Vec {
 template <typename T, int VB>
 constexpr int chunk_elems() {
   return VB == 0 ? 1 : VB / (int)sizeof(typename DT<T>::scalar_t);
+}
+
+// ---- streaming row access through buffer resources ------------------------
+// Rows of data touched exactly once are moved with buffer_load/store_dwordx4
+// (dwordx2, dword for narrower chunks) from a wave-uniform row base held in
+// scalar registers, with explicit cache-policy bits.  Loads are nontemporal
+// (nt).  The register kernel stores nontemporal at system scope (sc0 sc1
+// nt: written through to memory, no dirty lines left in L2) and writes the
+// residual back after the row reduction, next to the output: 667 vs 683 us
+// for 131072 x 4096 bf16 rows (K = 1) against global nt accesses with the
+// residual stored first, and equal on 8192 rows.  The streaming kernel
+// keeps plain nontemporal stores and its residual store in pass 1: at K = 8
+// (4096 x 8192) system-scope stores or a residual stored in pass 2 measured
+// 117.6-119.5 us against 113.7, and 1455-1471 against 1415 us on 65536 x
+// 16384.  No other combination of the sc0 / sc1 / nt bits did better once
+// the footprint exceeded the 256 MB Infinity Cache.
+constexpr int kCpolLoadStream = 2;        // nt
+constexpr int kCpolStoreStream = 2;       // nt
+constexpr int kCpolStoreWriteThrough = 19;  // sc0 | nt | sc1
+
+// A buffer resource over `bytes` bytes from `base` (which must be uniform
+// across the wave): raw 32-bit words, stride 0; accesses at or beyond
+// `bytes` would read zeros and drop stores (every access here is in range).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
 }
 
 // ---- wave64 reductions ----------------------------------------------------
@@ -362,6 +416,9 @@ __global__ __launch_bounds__(WGS) void row_vgpr_kernel(ArgsOf<AG> a) {
   static_assert(TPR <= WGS && WGS % TPR == 0, "a row must fit in one workgroup");
   static_assert(TPR < 64 ? (64 % TPR == 0) : (TPR % 64 == 0), "TPR must tile waves");
   constexpr int kRed = WPR > 1 ? RPW * WPR : 1;
+  // streaming rows whose base is uniform over a wave go through buffer
+  // resources (rows packed several to a wave keep global accesses)
+  constexpr bool BUF = NT && TPR >= 64;
   __shared__ float red[2][kRed];
 
   const int tid = threadIdx.x;
@@ -385,19 +442,28 @@ __global__ __launch_bounds__(WGS) void row_vgpr_kernel(ArgsOf<AG> a) {
 
   for (int64_t row0 = (int64_t)blockIdx.x * RPW; row0 < a.rows;
        row0 += (int64_t)gridDim.x * RPW) {
-    const int64_t row = RPW == 1 ? row0 : row0 + slot;  // uniform when one row per WG
+    // uniform when one row per workgroup, and made explicitly wave-uniform
+    // when a row spans whole waves (the buffer path needs a scalar base)
+    const int64_t row = RPW == 1 ? row0 : row0 + (BUF ? __builtin_amdgcn_readfirstlane(slot) : slot);
     const bool row_ok = row < a.rows;
     const char* xrow = row_ptr(a.partials.p[0], a.partials.s[0], row);
     char* rrow = row_ptr(a.residual, a.res_stride, row);
     char* orow = row_ptr(a.out, a.out_stride, row);
+    // chunk c of a data row: nontemporal, through a buffer resource when
+    // the row base is wave-uniform
+    auto load_in = [&](const char* rowp, int c) -> raw_t {
+      if constexpr (BUF) return IV::template load_buf<kCpolLoadStream>(row_rsrc(rowp, C * IV::BYTES), c);
+      else return IV::template load<NT>(rowp, c);
+    };
     float v[NPT][V];
+    raw_t rnew[NPT];  // the rounded residual chunks, stored after the reduction
 
     if constexpr (KC == 0) {
       raw_t raw[NPT];
 #pragma unroll
       for (int i = 0; i < NPT; ++i) {
         const int c = tr + i * TPR;
-        if (row_ok && c < C) raw[i] = IV::template load<NT>(xrow, c);
+        if (row_ok && c < C) raw[i] = load_in(xrow, c);
       }
 #pragma unroll
       for (int i = 0; i < NPT; ++i) {
@@ -419,8 +485,8 @@ __global__ __launch_bounds__(WGS) void row_vgpr_kernel(ArgsOf<AG> a) {
         if (row_ok && c < C) {
 #pragma unroll
           for (int q = 0; q < NB; ++q)
-            raw[q][i] = IV::template load<NT>(row_ptr(a.partials.p[q], a.partials.s[q], row), c);
-          rres[i] = IV::template load<NT>(rrow, c);
+            raw[q][i] = load_in(row_ptr(a.partials.p[q], a.partials.s[q], row), c);
+          rres[i] = load_in(rrow, c);
         }
       }
       float acc[NPT][V];
@@ -446,7 +512,7 @@ __global__ __launch_bounds__(WGS) void row_vgpr_kernel(ArgsOf<AG> a) {
 #pragma unroll
           for (int i = 0; i < NPT; ++i) {
             const int c = tr + i * TPR;
-            if (row_ok && c < C) rq[i] = IV::template load<NT>(prow, c);
+            if (row_ok && c < C) rq[i] = load_in(prow, c);
           }
 #pragma unroll
           for (int i = 0; i < NPT; ++i) {
@@ -468,9 +534,8 @@ __global__ __launch_bounds__(WGS) void row_vgpr_kernel(ArgsOf<AG> a) {
           IV::unpack(rres[i], t);
 #pragma unroll
           for (int e = 0; e < V; ++e) acc[i][e] += t[e];  // residual added last
-          const raw_t rn = IV::pack(acc[i]);             // round once to dtype
-          IV::template store<NT>(rrow, c, rn);
-          IV::unpack(rn, v[i]);                          // normalise the stored row
+          rnew[i] = IV::pack(acc[i]);                    // round once to dtype
+          IV::unpack(rnew[i], v[i]);                     // normalise the stored row
         } else {
 #pragma unroll
           for (int e = 0; e < V; ++e) v[i][e] = 0.0f;
@@ -533,6 +598,22 @@ __global__ __launch_bounds__(WGS) void row_vgpr_kernel(ArgsOf<AG> a) {
       }
     }
 
+    // The residual is written back here, after the reduction, next to the
+    // output: each workgroup's loads, then its stores (measured 1.7% faster
+    // than storing it before the reduction on a 4 GiB footprint, equal on
+    // 256 MiB).
+    if constexpr (KC != 0) {
+#pragma unroll
+      for (int i = 0; i < NPT; ++i) {
+        const int c = tr + i * TPR;
+        if (row_ok && c < C) {
+          if constexpr (BUF)
+            IV::template store_buf<kCpolStoreWriteThrough>(row_rsrc(rrow, C * IV::BYTES), c, rnew[i]);
+          else
+            IV::template store<NT>(rrow, c, rnew[i]);
+        }
+      }
+    }
 #pragma unroll
     for (int i = 0; i < NPT; ++i) {
       const int c = tr + i * TPR;
@@ -545,12 +626,20 @@ __global__ __launch_bounds__(WGS) void row_vgpr_kernel(ArgsOf<AG> a) {
 #pragma unroll
           for (int e = 0; e < V; ++e) y[e] = (ldexpf(v[i][e], shift) * inv) * g[i][e];
         }
+        const auto packed = OV::pack(y);
         if constexpr (AG) {
-          const auto packed = OV::pack(y);
-          for (int j = 0; j < a.gather.n; ++j)
-            OV::template store<NT>(row_ptr(a.gather.p[j], a.out_stride, row), c, packed);
+          for (int j = 0; j < a.gather.n; ++j) {
+            char* grow = row_ptr(a.gather.p[j], a.out_stride, row);
+            if constexpr (BUF)
+              OV::template store_buf<kCpolStoreWriteThrough>(row_rsrc(grow, C * OV::BYTES), c, packed);
+            else
+              OV::template store<NT>(grow, c, packed);
+          }
         } else {
-          OV::template store<NT>(orow, c, OV::pack(y));
+          if constexpr (BUF)
+            OV::template store_buf<kCpolStoreWriteThrough>(row_rsrc(orow, C * OV::BYTES), c, packed);
+          else
+            OV::template store<NT>(orow, c, packed);
         }
       }
     }
@@ -568,7 +657,8 @@ __global__ __launch_bounds__(WGS) void row_vgpr_kernel(ArgsOf<AG> a) {
 // loaded and added one at a time; -2 = runtime K, two at a time (both loads
 // in flight together, the adds still in order).
 // NT: streaming loads/stores for data touched once (never for a residual
-// that pass 2 reads back from memory).
+// that pass 2 reads back from memory), through buffer resources for chunks
+// of whole words.
 // AG: as for the register kernel.
 template <typename T, typename GT, typename OT, int VB, int WGS, bool LDS_STAGE, int KC, int UNR,
           bool NT, bool AG = false>
@@ -579,6 +669,7 @@ __global__ __launch_bounds__(WGS) void row_stream_kernel(ArgsOf<AG> a) {
   using OV = Vec<OT, V>;  // output
   using raw_t = typename IV::raw_t;
   constexpr int NW = WGS / 64;
+  constexpr bool BUF = NT && IV::BUFFERABLE && OV::BUFFERABLE;
   __shared__ float red[2][NW];
   extern __shared__ __align__(16) unsigned char stage_bytes[];
   raw_t* stage = reinterpret_cast<raw_t*>(stage_bytes);
@@ -592,6 +683,10 @@ __global__ __launch_bounds__(WGS) void row_stream_kernel(ArgsOf<AG> a) {
     char* rrow = row_ptr(a.residual, a.res_stride, row);
     char* orow = row_ptr(a.out, a.out_stride, row);
     float ss = 0.0f;
+    auto load_in = [&](const char* rowp, int c) -> raw_t {
+      if constexpr (BUF) return IV::template load_buf<kCpolLoadStream>(row_rsrc(rowp, C * IV::BYTES), c);
+      else return IV::template load<NT>(rowp, c);
+    };
 
     for (int c0 = tid; c0 < C; c0 += WGS * UNR) {
       raw_t rv[UNR];
@@ -599,7 +694,7 @@ __global__ __launch_bounds__(WGS) void row_stream_kernel(ArgsOf<AG> a) {
 #pragma unroll
         for (int u = 0; u < UNR; ++u) {
           const int c = c0 + u * WGS;
-          if (c < C) rv[u] = IV::template load<NT>(xrow, c);
+          if (c < C) rv[u] = load_in(xrow, c);
         }
       } else {
         raw_t r0[UNR], rr[UNR];
@@ -607,8 +702,8 @@ __global__ __launch_bounds__(WGS) void row_stream_kernel(ArgsOf<AG> a) {
         for (int u = 0; u < UNR; ++u) {
           const int c = c0 + u * WGS;
           if (c < C) {
-            r0[u] = IV::template load<NT>(xrow, c);
-            rr[u] = IV::template load<NT>(rrow, c);
+            r0[u] = load_in(xrow, c);
+            rr[u] = load_in(rrow, c);
           }
         }
         float acc[UNR][V];
@@ -629,8 +724,8 @@ __global__ __launch_bounds__(WGS) void row_stream_kernel(ArgsOf<AG> a) {
             for (int u = 0; u < UNR; ++u) {
               const int c = c0 + u * WGS;
               if (c < C) {
-                ra[u] = IV::template load<NT>(pa, c);
-                rb[u] = IV::template load<NT>(pb, c);
+                ra[u] = load_in(pa, c);
+                rb[u] = load_in(pb, c);
               }
             }
 #pragma unroll
@@ -652,7 +747,7 @@ __global__ __launch_bounds__(WGS) void row_stream_kernel(ArgsOf<AG> a) {
 #pragma unroll
           for (int u = 0; u < UNR; ++u) {
             const int c = c0 + u * WGS;
-            if (c < C) rq[u] = IV::template load<NT>(prow, c);
+            if (c < C) rq[u] = load_in(prow, c);
           }
 #pragma unroll
           for (int u = 0; u < UNR; ++u) {
@@ -756,12 +851,20 @@ __global__ __launch_bounds__(WGS) void row_stream_kernel(ArgsOf<AG> a) {
 #pragma unroll
             for (int e = 0; e < V; ++e) y[e] = (ldexpf(t[e], shift) * inv) * g[e];
           }
+          const auto packed = OV::pack(y);
           if constexpr (AG) {
-            const auto packed = OV::pack(y);
-            for (int j = 0; j < a.gather.n; ++j)
-              OV::template store<NT>(row_ptr(a.gather.p[j], a.out_stride, row), c, packed);
+            for (int j = 0; j < a.gather.n; ++j) {
+              char* grow = row_ptr(a.gather.p[j], a.out_stride, row);
+              if constexpr (BUF)
+                OV::template store_buf<kCpolStoreStream>(row_rsrc(grow, C * OV::BYTES), c, packed);
+              else
+                OV::template store<NT>(grow, c, packed);
+            }
           } else {
-            OV::template store<NT>(orow, c, OV::pack(y));
+            if constexpr (BUF)
+              OV::template store_buf<kCpolStoreStream>(row_rsrc(orow, C * OV::BYTES), c, packed);
+            else
+              OV::template store<NT>(orow, c, packed);
           }
         }
       }
