@@ -69,6 +69,13 @@ typedef enum {
 int block_all_reduce_sum(void* out, const void* x, int64_t n, int dtype, void* workspace,
                          int64_t workspace_bytes, void* stream);
 
+/*
+ * block_sum_tune -- for tuning and testing only: every later sum of this
+ * process launches exactly `groups` workgroups (1..BRS_MAX_GROUPS); 0
+ * restores the size rule.  Returns RMSN_OK or RMSN_ERR_SHAPE.
+ */
+int block_sum_tune(int groups);
+
 #ifdef __cplusplus
 }
 #endif

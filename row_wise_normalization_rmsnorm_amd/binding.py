@@ -26,7 +26,7 @@ EXPORTS = ("rmsnorm_fwd", "add_rmsnorm_fwd", "rmsnorm_strerror", "rmsnorm_last_e
            "rmsnorm_plan_ex", "rmsnorm_variants_ex", "rmsnorm_plan_call", "add_rmsnorm_ag_fwd",
            "rmsnorm_plan_ag", "rmsnorm_variants_ag", "rmsnorm_tune")
 GATHER_MAX = 16
-BLOCK_SUM_EXPORTS = ("block_all_reduce_sum",)
+BLOCK_SUM_EXPORTS = ("block_all_reduce_sum", "block_sum_tune")
 GEMM_SCATTER_EXPORTS = ("gemm_scatter_fwd", "gemm_scatter_tile_n", "gemm_scatter_tiles",
                         "gemm_scatter_schedule")
 
@@ -104,6 +104,8 @@ def lib() -> ctypes.CDLL:
             l.rmsnorm_tune.restype = c_int
             l.block_all_reduce_sum.argtypes = [vp, vp, i64, c_int, vp, i64, vp]
             l.block_all_reduce_sum.restype = c_int
+            l.block_sum_tune.argtypes = [c_int]
+            l.block_sum_tune.restype = c_int
             l.gemm_scatter_fwd.argtypes = [ctypes.POINTER(vp), i64, c_int, c_int, vp, i64, vp,
                                            i64, vp, i64, c_float, c_float, i64, i64, i64, c_int,
                                            vp, ctypes.c_uint32, c_int, vp]
@@ -383,6 +385,12 @@ def block_all_reduce_sum_fwd(out: torch.Tensor, x: torch.Tensor, workspace: Opti
                                       x.data_ptr() or None, x.numel(), BRS_DTYPE_CODE[x.dtype],
                                       _dev_ptr(workspace, "workspace"), workspace.numel(),
                                       _stream(x, stream)))
+
+
+def block_sum_tune(groups: int = 0) -> None:
+    """Tuning and tests only: launch exactly ``groups`` workgroups per sum (0:
+    the size rule)."""
+    _check(lib().block_sum_tune(int(groups)))
 
 
 def block_all_reduce_sum(x: torch.Tensor) -> torch.Tensor:

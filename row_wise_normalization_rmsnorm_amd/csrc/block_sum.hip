@@ -24,6 +24,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "../../include/block_sum.h"
 
 namespace brs {
@@ -314,6 +316,9 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
   return p < q + nb && q < p + na;
 }
 
+// Tuning override of the grid (block_sum_tune); 0: the size rule below.
+std::atomic<int> g_groups_override{0};
+
 template <int DT>
 hipError_t launch(const unsigned char* x, int64_t n, void* out, void* ws, hipStream_t stream) {
   constexpr int S = brs::In<DT>::S;
@@ -329,16 +334,20 @@ hipError_t launch(const unsigned char* x, int64_t n, void* out, void* ws, hipStr
   if (groups > brs::kGridCap) groups = brs::kGridCap;
   const int64_t busy = (nchunks + brs::kThreads - 1) / brs::kThreads;  // groups with any chunk
   if (groups > busy) groups = busy < 1 ? 1 : busy;
-  if (const char* e = getenv("RMSNORM_SUM_GROUPS")) {  // tuning override
-    const long long g = atoll(e);
-    if (g >= 1 && g <= brs::kMaxGroups) groups = g;
-  }
+  if (const int g = g_groups_override.load(std::memory_order_relaxed)) groups = g;
   hipLaunchKernelGGL(brs::block_sum_kernel<DT>, dim3((unsigned)groups), dim3(brs::kThreads), 0,
                      stream, x, n, head, nchunks, out, static_cast<unsigned char*>(ws));
   return hipGetLastError();
 }
 
 }  // namespace
+
+extern "C" int block_sum_tune(int groups) {
+  if (groups < 0 || groups > BRS_MAX_GROUPS)
+    return rmsn_set_error(RMSN_ERR_SHAPE, "groups outside [0, BRS_MAX_GROUPS]");
+  g_groups_override.store(groups, std::memory_order_relaxed);
+  return RMSN_OK;
+}
 
 extern "C" int block_all_reduce_sum(void* out, const void* x, int64_t n, int dtype,
                                     void* workspace, int64_t workspace_bytes, void* stream) {
@@ -374,3 +383,4 @@ extern "C" int block_all_reduce_sum(void* out, const void* x, int64_t n, int dty
   }
   return RMSN_OK;
 }
+

@@ -406,3 +406,14 @@ def test_overlap_brute_force(tmp_path):
     assert r.returncode == 0 and r.stdout.startswith("ok "), r.stdout + r.stderr
     cases, exact = map(int, r.stdout.split()[1:3])
     assert cases == 300000 and exact > 10000
+
+
+def test_block_sum_tune_range():
+    """The block sum's grid override is an explicit call with a checked range
+    (no environment variable is read)."""
+    with pytest.raises(B.RmsnormError):
+        B.block_sum_tune(-1)
+    with pytest.raises(B.RmsnormError):
+        B.block_sum_tune(B.BRS_MAX_GROUPS + 1)
+    B.block_sum_tune(B.BRS_MAX_GROUPS)
+    B.block_sum_tune(0)
