@@ -70,6 +70,26 @@ int block_all_reduce_sum(void* out, const void* x, int64_t n, int dtype, void* w
                          int64_t workspace_bytes, void* stream);
 
 /*
+ * block_all_reduce_sum_noalloc -- block_all_reduce_sum with no workspace
+ * argument, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * The counters and per-workgroup partials live in a device array of
+ * BRS_WORKSPACE_BYTES bytes inside the library, one copy per GPU (each GPU
+ * the library runs on holds its copy until the process ends); the call
+ * allocates and frees nothing.  Limit: none on n beyond the workspace
+ * form's -- a launch uses at most BRS_MAX_GROUPS partials, which the array
+ * holds.  The first call on a GPU also enqueues, ahead of the sum, a small
+ * kernel that zeroes the array's counters; every sum leaves them zero again.
+ * All calls on one GPU share that GPU's array: calls that may run at the
+ * same time on one GPU (on different streams, or from threads without
+ * ordering between them) race and give wrong sums; order them on one
+ * stream.  out, x, n, dtype, stream and the return codes are as for
+ * block_all_reduce_sum (RMSN_ERR_HIP also when the array's address cannot
+ * be obtained).
+ */
+int block_all_reduce_sum_noalloc(void* out, const void* x, int64_t n, int dtype, void* stream);
+
+/*
  * block_sum_tune -- for tuning and testing only: every later sum of this
  * process launches exactly `groups` workgroups (1..BRS_MAX_GROUPS); 0
  * restores the size rule.  Returns RMSN_OK or RMSN_ERR_SHAPE.

@@ -26,7 +26,7 @@ EXPORTS = ("rmsnorm_fwd", "add_rmsnorm_fwd", "rmsnorm_strerror", "rmsnorm_last_e
            "rmsnorm_plan_ex", "rmsnorm_variants_ex", "rmsnorm_plan_call", "add_rmsnorm_ag_fwd",
            "rmsnorm_plan_ag", "rmsnorm_variants_ag", "rmsnorm_tune")
 GATHER_MAX = 16
-BLOCK_SUM_EXPORTS = ("block_all_reduce_sum", "block_sum_tune")
+BLOCK_SUM_EXPORTS = ("block_all_reduce_sum", "block_all_reduce_sum_noalloc", "block_sum_tune")
 GEMM_SCATTER_EXPORTS = ("gemm_scatter_fwd", "gemm_scatter_tile_n", "gemm_scatter_tiles",
                         "gemm_scatter_schedule")
 
@@ -104,6 +104,8 @@ def lib() -> ctypes.CDLL:
             l.rmsnorm_tune.restype = c_int
             l.block_all_reduce_sum.argtypes = [vp, vp, i64, c_int, vp, i64, vp]
             l.block_all_reduce_sum.restype = c_int
+            l.block_all_reduce_sum_noalloc.argtypes = [vp, vp, i64, c_int, vp]
+            l.block_all_reduce_sum_noalloc.restype = c_int
             l.block_sum_tune.argtypes = [c_int]
             l.block_sum_tune.restype = c_int
             l.gemm_scatter_fwd.argtypes = [ctypes.POINTER(vp), i64, c_int, c_int, vp, i64, vp,
@@ -385,6 +387,19 @@ def block_all_reduce_sum_fwd(out: torch.Tensor, x: torch.Tensor, workspace: Opti
                                       x.data_ptr() or None, x.numel(), BRS_DTYPE_CODE[x.dtype],
                                       _dev_ptr(workspace, "workspace"), workspace.numel(),
                                       _stream(x, stream)))
+
+
+def block_all_reduce_sum_noalloc_fwd(out: torch.Tensor, x: torch.Tensor, stream=None) -> None:
+    """block_all_reduce_sum_fwd with the library's own per-GPU scratch instead
+    of a workspace (no device allocation anywhere in the call)."""
+    if x.dtype not in BRS_DTYPE_CODE:
+        raise RmsnormError(-3, f"unsupported dtype {x.dtype}")
+    want = torch.int32 if x.dtype == torch.int8 else torch.float32
+    if out.dtype != want or out.numel() != 1:
+        raise RmsnormError(-2, f"out must be one {want}")
+    _check(lib().block_all_reduce_sum_noalloc(_dev_ptr(out, "out"), _dev_ptr(x, "x") if x.numel()
+                                              else x.data_ptr() or None, x.numel(),
+                                              BRS_DTYPE_CODE[x.dtype], _stream(x, stream)))
 
 
 def block_sum_tune(groups: int = 0) -> None:

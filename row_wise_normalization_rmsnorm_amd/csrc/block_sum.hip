@@ -25,6 +25,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "../../include/block_sum.h"
 
@@ -342,6 +343,75 @@ hipError_t launch(const unsigned char* x, int64_t n, void* out, void* ws, hipStr
 
 }  // namespace
 
+// The device-side scratch of block_all_reduce_sum_noalloc: the same layout as
+// a caller's workspace (completion counters, then one partial per
+// workgroup), one copy per GPU the library runs on, held until the process
+// ends.  Host code never passes `scratch` itself to a kernel (on the host it
+// names a stand-in, not device memory): it passes the device address that
+// hipGetSymbolAddress returns for the current GPU.
+static __device__ __align__(256) unsigned char scratch[BRS_WORKSPACE_BYTES];
+
+namespace {
+
+// Zeroes the counter header of a workspace (a kernel, so that it is ordered
+// on the caller's stream and may be captured into a graph).
+__global__ void clear_header_kernel(uint32_t* ws) {
+  for (int i = threadIdx.x; i < BRS_WORKSPACE_HEADER / 4; i += blockDim.x) ws[i] = 0u;
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch[kMaxDevices];          // device address of `scratch` on each GPU
+bool g_scratch_cleared[kMaxDevices];   // its header zeroed on a stream already
+
+// The device address of this GPU's `scratch`, looked up once per device with
+// that device current; on the first call for a device the counter header is
+// zeroed by a small kernel on `stream`, ahead of the sum.  Returns nullptr
+// (and sets the last error) on failure.
+void* scratch_for(int dev, hipStream_t stream) {
+  if (dev < 0 || dev >= kMaxDevices) {
+    rmsn_set_error(RMSN_ERR_HIP, "device index outside the scratch table");
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch[dev]) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) {
+      rmsn_set_error(RMSN_ERR_HIP, "hipGetDevice failed");
+      return nullptr;
+    }
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) {
+      rmsn_set_error(RMSN_ERR_HIP, "hipSetDevice failed");
+      return nullptr;
+    }
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) (void)hipSetDevice(cur);
+    if (e != hipSuccess || !p) {
+      char msg[200];
+      snprintf(msg, sizeof(msg), "hipGetSymbolAddress(scratch) failed: %s", hipGetErrorString(e));
+      rmsn_set_error(RMSN_ERR_HIP, msg);
+      return nullptr;
+    }
+    g_scratch[dev] = p;
+  }
+  if (!g_scratch_cleared[dev]) {
+    hipLaunchKernelGGL(clear_header_kernel, dim3(1), dim3(256), 0, stream,
+                       static_cast<uint32_t*>(g_scratch[dev]));
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) {
+      char msg[200];
+      snprintf(msg, sizeof(msg), "clearing the scratch counters failed: %s", hipGetErrorString(e));
+      rmsn_set_error(RMSN_ERR_HIP, msg);
+      return nullptr;
+    }
+    g_scratch_cleared[dev] = true;
+  }
+  return g_scratch[dev];
+}
+
+}  // namespace
+
 extern "C" int block_sum_tune(int groups) {
   if (groups < 0 || groups > BRS_MAX_GROUPS)
     return rmsn_set_error(RMSN_ERR_SHAPE, "groups outside [0, BRS_MAX_GROUPS]");
@@ -384,3 +454,24 @@ extern "C" int block_all_reduce_sum(void* out, const void* x, int64_t n, int dty
   return RMSN_OK;
 }
 
+extern "C" int block_all_reduce_sum_noalloc(void* out, const void* x, int64_t n, int dtype,
+                                            void* stream) {
+  // arguments first, exactly as the workspace form checks them (nothing is
+  // set up or launched for a call that would be rejected)
+  if (dtype < BRS_F32 || dtype > BRS_I8) return rmsn_set_error(RMSN_ERR_DTYPE, "unknown sum dtype");
+  if (n < 0) return rmsn_set_error(RMSN_ERR_SHAPE, "n < 0");
+  if (!out || (n > 0 && !x)) return rmsn_set_error(RMSN_ERR_NULL, "out and x must be non-NULL");
+  if (n > INT64_MAX / 4) return rmsn_set_error(RMSN_ERR_SHAPE, "n too large");
+  int dev = -1;
+  hipError_t e = stream ? hipStreamGetDevice((hipStream_t)stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    char msg[200];
+    snprintf(msg, sizeof(msg), "cannot tell the stream's device: %s", hipGetErrorString(e));
+    return rmsn_set_error(RMSN_ERR_HIP, msg);
+  }
+  void* ws = scratch_for(dev, (hipStream_t)stream);
+  if (!ws) return RMSN_ERR_HIP;
+  // The launch never uses more than BRS_MAX_GROUPS partials, which the
+  // scratch holds, so every n fits; the workspace form's checks do the rest.
+  return block_all_reduce_sum(out, x, n, dtype, ws, (int64_t)sizeof(scratch), stream);
+}
