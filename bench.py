@@ -8,7 +8,10 @@ reduce-scatter epilogue, which reports TFLOP/s against the matrix-core
 peak).  Inputs are seeded synthetic data
 resident in HBM before timing starts.  Several copies of the buffers are
 rotated so that consecutive steps never find their inputs in the 256 MB
-Infinity Cache.  Timing: W untimed warm-up steps, then exactly K steps
+Infinity Cache (by default at least 2 GiB of distinct buffers, 8x its
+size: with fewer, stores that allocate in the caches have measured faster
+only because a later step overwrote their lines before they were written
+back).  Timing: W untimed warm-up steps, then exactly K steps
 bracketed by ``torch.cuda.synchronize()`` and HIP events recorded on the
 stream the kernels run on.
 
@@ -363,7 +366,7 @@ def gemm_shapes(a) -> int:
     return 0
 
 
-def stream_ceiling(w, dev: str = "cuda:0", steps: int = 60, rotate_gib: float = 1.0,
+def stream_ceiling(w, dev: str = "cuda:0", steps: int = 60, rotate_gib: float = 2.0,
                    inplace: bool = False) -> dict:
     """HBM bandwidth of a plain streaming kernel (libstreamprobe.so) moving the
     same bytes as one step of the workload, with the kernel's aliasing: the
@@ -562,11 +565,11 @@ CEILING_PATTERNS = [
 
 
 CEILING_GRIDS = (256, 384, 512, 768, 1024, 2048, 4096, 8192, 16384)
-CEILING_POLICIES = 8  # libstreamprobe.so's cache policies (stream_probe_policy)
+CEILING_POLICIES = 9  # libstreamprobe.so's cache policies (stream_probe_policy)
 
 
 def ceiling_sweep(stream_mib: int = 64, steps: int = 40, patterns: str = "",
-                  policies: str = "") -> int:
+                  policies: str = "", rotate_gib: float = 1.0) -> int:
     """Time libstreamprobe.so over every read/write mix above (or those whose
     name contains one of the |-separated ``patterns``), every grid, workgroup
     size, unroll, layout and cache policy it offers; streams of stream_mib MiB
@@ -594,7 +597,7 @@ def ceiling_sweep(stream_mib: int = 64, steps: int = 40, patterns: str = "",
         if patterns and not any(f in name for f in patterns.split("|")):
             continue
         nbuf = max([nr] + [j + 1 for j in writes])
-        nsets = max(1, -(-(1 << 30) // (nbuf * nbytes)))
+        nsets = max(1, int(-(-rotate_gib * (1 << 30) // (nbuf * nbytes))))
         bufs = [[torch.empty(nbytes, dtype=torch.uint8, device="cuda:0").fill_(j + 1)
                  for j in range(nbuf)] for _ in range(nsets)]
         args = [((vp * max(nr, 1))(*[t.data_ptr() for t in b[:nr]]),
@@ -621,7 +624,7 @@ def ceiling_sweep(stream_mib: int = 64, steps: int = 40, patterns: str = "",
             e1.record(stream)
             torch.cuda.synchronize()
             us = e0.elapsed_time(e1) * 1e3 / steps
-            row = {"pattern": name, "reads": nr, "writes": len(writes),
+            row = {"pattern": name, "reads": nr, "writes": len(writes), "rotating_sets": nsets,
                    "in_place": sum(j < nr for j in writes), "grid": grid, "block": block,
                    "unroll": unroll, "layout": "contiguous" if contig else "grid-stride",
                    "policy": pol, "load_policy": cpol[pol][0], "store_policy": cpol[pol][1],
@@ -643,6 +646,114 @@ def cpol_name(bits: int) -> str:
     spells them (bit 0 sc0, bit 1 nt, bit 4 sc1); "default" for none."""
     names = [n for b, n in ((1, "sc0"), (16, "sc1"), (2, "nt")) if bits & b]
     return " ".join(names) if names else "default"
+
+
+DESIGN_NAMES = {0: "one row per workgroup, residual stored before the reduction",
+                1: "one row per workgroup, residual stored after the reduction",
+                2: "one row per workgroup, rows in contiguous eighths per XCD",
+                3: "persistent, next row's loads issued before this row's work",
+                4: "two rows per 1024-lane workgroup"}
+
+
+def design_sweep(a) -> int:
+    """Time the row-kernel designs of librowprobe.so (4096-wide bf16 rows, one
+    partial) beside the library's kernel on the same rotating buffers: every
+    design and cache-policy pair it is built with, the persistent design at
+    several grids.  Each is first checked against the library's kernel on one
+    set (residual bit for bit, output within 2 ulp).  Designs are timed
+    round-robin over ``--repeat`` rounds; the median is reported, one JSON
+    line each."""
+    import ctypes
+    import statistics
+    import torch
+    from row_wise_normalization_rmsnorm_amd import binding as B
+    from row_wise_normalization_rmsnorm_amd.workloads import WORKLOADS
+    w = WORKLOADS["add_rmsnorm_bf16_8192x4096_k1"]
+    rows = a.rows or w.rows
+    lib = ctypes.CDLL(os.path.join(ROOT, "row_wise_normalization_rmsnorm_amd", "librowprobe.so"))
+    vp = ctypes.c_void_p
+    lib.row_probe.argtypes = [ctypes.c_int] * 4 + [vp] * 4 + [ctypes.c_int64, ctypes.c_float, vp]
+    lp, sp = (ctypes.c_int * 16)(), (ctypes.c_int * 16)()
+    npol = lib.row_probe_policies(lp, sp, 16)
+    pols = [(lp[i], sp[i]) for i in range(npol)]
+    dev = "cuda:0"
+    H = w.hidden
+    g = (torch.rand(H, device=dev) + 0.5).to(torch.bfloat16)
+    tb = rows * H * 2
+    nsets = max(1, int(-(-a.rotate_bytes * (1 << 30) // (3 * tb))))
+    gen = torch.Generator(device=dev).manual_seed(0)
+    sets = [(torch.randn(rows, H, device=dev, generator=gen).to(torch.bfloat16),
+             torch.randn(rows, H, device=dev, generator=gen).to(torch.bfloat16),
+             torch.empty(rows, H, device=dev, dtype=torch.bfloat16)) for _ in range(nsets)]
+    stream = torch.cuda.current_stream()
+    sid = stream.cuda_stream
+
+    def probe(design, l, s_, grid):
+        def step(i):
+            x, r, o = sets[i % nsets]
+            rc = lib.row_probe(design, l, s_, grid, x.data_ptr(), r.data_ptr(), o.data_ptr(),
+                               g.data_ptr(), rows, w.eps, sid)
+            if rc != 0:
+                raise RuntimeError(f"row_probe({design}, {l}, {s_}, {grid}) failed: {rc}")
+        return step
+
+    def library(i):
+        x, r, o = sets[i % nsets]
+        B.add_rmsnorm_fwd(o, r, [x], g, w.eps)
+
+    variants = {("library", B.rmsnorm_plan(rows, H, 1, "bf16"), "", 0): library}
+    for d in (0, 1, 2, 4):
+        for l, s_ in pols:
+            grid = rows // 2 if d == 4 else rows
+            variants[(d, DESIGN_NAMES[d], f"{l}/{s_}", grid)] = probe(d, l, s_, grid)
+    for grid in (256, 512, 1024, 2048):
+        for l, s_ in pols:
+            if s_ in (2, 19):
+                variants[(3, DESIGN_NAMES[3], f"{l}/{s_}", grid)] = probe(3, l, s_, grid)
+
+    def ulps(t):
+        i = t.view(torch.int16).int()
+        return torch.where(i < 0, -(i & 0x7FFF), i)
+
+    x0, r0, _ = sets[0]
+    r_init = r0.clone()
+    ref_r, ref_o = r0.clone(), torch.empty_like(r0)
+    B.add_rmsnorm_fwd(ref_o, ref_r, [x0], g, w.eps)
+    for key, f in variants.items():
+        sets[0][1].copy_(r_init)
+        f(0)
+        torch.cuda.synchronize()
+        same_r = torch.equal(sets[0][1].view(torch.int16), ref_r.view(torch.int16))
+        d_ulp = int((ulps(sets[0][2]) - ulps(ref_o)).abs().max())
+        if not same_r or d_ulp > 2:
+            raise RuntimeError(f"design {key} differs from the library: residual exact "
+                               f"{same_r}, output {d_ulp} ulp")
+    print(f"[design] {len(variants)} variants agree with the library's kernel; timing "
+          f"({nsets} rotating sets of {3 * tb / 2**20:.0f} MiB)", file=sys.stderr, flush=True)
+    times = {k: [] for k in variants}
+    for rep in range(a.repeat):
+        for key, f in variants.items():
+            for i in range(2 * nsets):
+                f(i)
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(a.steps):
+                f(i)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times[key].append(e0.elapsed_time(e1) / a.steps * 1e3)
+        print(f"[design] round {rep} done", file=sys.stderr, flush=True)
+    nbytes = rows * H * 2 * 4 + H * 2
+    for key, t in times.items():
+        us = statistics.median(t)
+        print(json.dumps({"workload": f"{w.name}" if rows == w.rows else f"{w.name}_rows{rows}",
+                          "rows": rows, "design": key[0], "what": key[1], "cpol": key[2],
+                          "grid": key[3], "us": round(us, 3),
+                          "gbs": round(nbytes / us / 1e3, 1), "rotating_sets": nsets,
+                          "runs_us": [round(x, 2) for x in t]}), flush=True)
+    return 0
 
 
 def copy_calibration() -> None:
@@ -674,6 +785,9 @@ def main() -> int:
                          "|-separated substrings")
     ap.add_argument("--ceiling-policies", default="",
                     help="ceiling sweep: comma-separated cache policies (default: all)")
+    ap.add_argument("--design-sweep", action="store_true",
+                    help="time the alternative row-kernel designs of librowprobe.so beside the "
+                         "library's kernel (4096-wide bf16 rows, one partial) and exit")
     ap.add_argument("--sweep", action="store_true",
                     help="time every compiled kernel variant that can run the workload "
                          "(forced through rmsnorm_tune) and print one line per variant")
@@ -686,7 +800,7 @@ def main() -> int:
                     help="run the workload with this many rows instead (not a headline figure)")
     ap.add_argument("--inplace", action="store_true",
                     help="write the output over the first input instead of a separate buffer")
-    ap.add_argument("--rotate-bytes", type=float, default=1.0,
+    ap.add_argument("--rotate-bytes", type=float, default=2.0,
                     help="GiB of distinct buffers rotated through (cold cache)")
     ap.add_argument("--gemm-shapes", action="store_true",
                     help="time the GEMM with the scatter epilogue over a list of shapes against "
@@ -712,7 +826,10 @@ def main() -> int:
         copy_calibration()
         return 0
     if a.ceiling_sweep:
-        return ceiling_sweep(patterns=a.ceiling_patterns, policies=a.ceiling_policies)
+        return ceiling_sweep(patterns=a.ceiling_patterns, policies=a.ceiling_policies,
+                             rotate_gib=a.rotate_bytes)
+    if a.design_sweep:
+        return design_sweep(a)
 
     from row_wise_normalization_rmsnorm_amd.workloads import GEMM_WORKLOADS
     if a.gemm_shapes:
@@ -731,11 +848,16 @@ def main() -> int:
     B.lib()
     print(f"[bench] {w.describe()}: generating inputs", file=sys.stderr, flush=True)
     base = I.make_inputs(w, device=dev)
-    # distinct device bytes of one set of buffers (the output shares the
-    # first input's memory with --inplace)
-    set_bytes = w.algorithmic_bytes()
-    if a.inplace and w.op != "block_sum":
-        set_bytes -= w.rows * w.hidden * w.itemsize
+    # distinct device bytes of one set of buffers: every input tensor, the
+    # residual (read and written in place, counted once) and each output
+    # (the output shares the first input's memory with --inplace)
+    tensor = w.rows * w.hidden * w.itemsize
+    if w.op == "block_sum":
+        set_bytes = tensor
+    elif w.fused:
+        set_bytes = (w.k + 1 + (w.gather or (0 if a.inplace else 1))) * tensor
+    else:
+        set_bytes = (1 if a.inplace else 2) * tensor
     nsets = max(1, int(-(-a.rotate_bytes * (1 << 30) // set_bytes)))
     sets = []
     for i in range(nsets):
@@ -872,7 +994,7 @@ def main() -> int:
     if not a.no_ceiling:
         del sets
         torch.cuda.empty_cache()
-        ceil = stream_ceiling(w, inplace=a.inplace)
+        ceil = stream_ceiling(w, inplace=a.inplace, rotate_gib=a.rotate_bytes)
         ceil["kernel_frac_of_ceiling"] = round(gbs / ceil["value"], 4)
         result["stream_ceiling"] = ceil
         print(f"[bench] streaming ceiling for this mix: {ceil['value']:.0f} GB/s; kernel at "

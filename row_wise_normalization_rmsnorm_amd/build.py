@@ -25,6 +25,8 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "librmsnorm.so")
 PROBE_SRC = os.path.join(HERE, "probe", "stream_probe.hip")
 PROBE_LIB = os.path.join(HERE, "libstreamprobe.so")
+ROW_PROBE_SRC = os.path.join(HERE, "probe", "row_probe.hip")
+ROW_PROBE_LIB = os.path.join(HERE, "librowprobe.so")
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -84,14 +86,16 @@ def build(jobs: int = 0, verbose: bool = False) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
-    # the bandwidth-ceiling probe used by bench.py (a separate library)
-    ptmp = PROBE_LIB + ".tmp%d" % os.getpid()
-    pcmd = [HIPCC, f"--offload-arch={ARCH}", "-O3", "-fPIC", "-shared", "-std=c++17",
-            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-o", ptmp, PROBE_SRC]
-    r = subprocess.run(pcmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError("probe build failed:\n" + r.stdout + r.stderr)
-    os.replace(ptmp, PROBE_LIB)
+    # the measurement aids used by bench.py (separate libraries): the
+    # bandwidth-ceiling probe and the row-kernel design probe
+    for src, lib in ((PROBE_SRC, PROBE_LIB), (ROW_PROBE_SRC, ROW_PROBE_LIB)):
+        ptmp = lib + ".tmp%d" % os.getpid()
+        pcmd = [HIPCC, f"--offload-arch={ARCH}", "-O3", "-fPIC", "-shared", "-std=c++17",
+                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-o", ptmp, src]
+        r = subprocess.run(pcmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"probe build failed for {src}:\n" + r.stdout + r.stderr)
+        os.replace(ptmp, lib)
     usage = check_assembly()
     spills = {k: v for k, v in usage.items() if v[1] > 0}
     if verbose:

@@ -30,14 +30,14 @@ struct Streams {
 // chunks with buffer_load/store_dwordx4, whose cache-policy bits are set per
 // instruction: bit 0 = sc0, bit 1 = nt, bit 4 = sc1 (the CDNA3/CDNA4 scope
 // and streaming controls).  {load bits, store bits}.
-constexpr int kPolicies = 8;
+constexpr int kPolicies = 9;
 __host__ __device__ constexpr int load_bits(int pol) {
   return pol == 1 ? 0 : pol == 2 ? 2 : pol == 3 ? 2 : pol == 4 ? 0 : pol == 5 ? 19
-       : pol == 6 ? 17 : pol == 7 ? 2 : 2;
+       : pol == 6 ? 17 : pol == 7 ? 2 : pol == 8 ? 0 : 2;
 }
 __host__ __device__ constexpr int store_bits(int pol) {
   return pol == 1 ? 0 : pol == 2 ? 2 : pol == 3 ? 0 : pol == 4 ? 2 : pol == 5 ? 19
-       : pol == 6 ? 17 : pol == 7 ? 19 : 2;
+       : pol == 6 ? 17 : pol == 7 ? 19 : pol == 8 ? 19 : 2;
 }
 
 // A buffer resource over [base, base + bytes): raw (stride 0) 32-bit words,
@@ -153,7 +153,7 @@ extern "C" int stream_probe_policy(int policy, int* load_cpol, int* store_cpol) 
 
 // stream_probe_pol: a chosen workgroup size (256, 512 or 1024), chunks in
 // flight per lane and stream (1, 2, 4 or 8), layout (contig != 0: each
-// workgroup streams one contiguous range) and cache policy (0..7).
+// workgroup streams one contiguous range) and cache policy (0..8).
 extern "C" int stream_probe_pol(const void* const* reads, int nr, void* const* writes, int nw,
                                 int64_t n16, void* sink, int grid, int block, int unroll,
                                 int contig, int policy, void* stream) {
@@ -180,6 +180,7 @@ extern "C" int stream_probe_pol(const void* const* reads, int nr, void* const* w
     case 5: ok = launch_pol<5>(s, nr, nw, n16, grid, block, unroll, c, sink, stream); break;
     case 6: ok = launch_pol<6>(s, nr, nw, n16, grid, block, unroll, c, sink, stream); break;
     case 7: ok = launch_pol<7>(s, nr, nw, n16, grid, block, unroll, c, sink, stream); break;
+    case 8: ok = launch_pol<8>(s, nr, nw, n16, grid, block, unroll, c, sink, stream); break;
   }
   if (!ok) return -1;
   return hipGetLastError() == hipSuccess ? 0 : -7;

@@ -153,6 +153,7 @@ def ceiling_summary(argv) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("jsonl")
     ap.add_argument("--command", default="python bench.py --ceiling-sweep")
+    ap.add_argument("--name", default="hbm_ceiling_sweep")
     a = ap.parse_args(argv)
     rows = [json.loads(l) for l in open(a.jsonl) if l.startswith("{")]
     order = []
@@ -162,12 +163,13 @@ def ceiling_summary(argv) -> int:
     grids = sorted({r["grid"] for r in rows})
     pols = sorted({(r.get("policy", 0), r.get("load_policy", "global nt"),
                     r.get("store_policy", "global nt")) for r in rows})
-    md = os.path.join(PROFILES, "hbm_ceiling_sweep.md")
+    md = os.path.join(PROFILES, a.name + ".md")
+    nsets = sorted({r.get("rotating_sets", 0) for r in rows})
     with open(md, "w") as f:
         f.write("# HBM ceiling of a plain streaming kernel, by read/write mix\n\n")
         f.write(f"Command: `{a.command}` (libstreamprobe.so: 16-byte loads and stores, every lane "
                 "`unroll` chunks in flight per stream; 64 MiB per stream, buffers rotated through "
-                ">= 1 GiB; HIP events over 40 launches per shape).  Swept: grid "
+                f"{'/'.join(map(str, nsets))} sets; HIP events over 40 launches per shape).  Swept: grid "
                 f"{grids[0]}-{grids[-1]} workgroups ({', '.join(map(str, grids))}), workgroup "
                 "256/512/1024 lanes, unroll 1/2/4/8, two layouts -- a grid-stride loop, or each "
                 "workgroup streaming one contiguous range -- and the cache policies below "
@@ -207,6 +209,38 @@ def ceiling_summary(argv) -> int:
                 cells.append(f"{max(v):.0f}" if v else "")
             f.write(f"| {name} | " + " | ".join(cells) + " |\n")
         f.write(f"\n{len(rows)} configurations timed.\n")
+    print(md)
+    return 0
+
+
+def design_summary(argv) -> int:
+    """profiles/design_sweep__<workload>.md from the JSON lines of
+    ``bench.py --design-sweep``: every row-kernel design and cache policy
+    beside the library's kernel, fastest first."""
+    ap = argparse.ArgumentParser()
+    ap.add_argument("jsonl")
+    ap.add_argument("--command", default="python bench.py --design-sweep --repeat 3 --steps 100")
+    a = ap.parse_args(argv)
+    rows = [json.loads(l) for l in open(a.jsonl) if l.startswith("{")]
+    lib = next(r for r in rows if r["design"] == "library")
+    wl = lib["workload"]
+    md = os.path.join(PROFILES, f"design_sweep__{wl}.md")
+    with open(md, "w") as f:
+        f.write(f"# Row-kernel designs on {wl}\n\n")
+        f.write(f"Command: `{a.command}` (librowprobe.so's designs for 4096-wide bf16 rows with "
+                "one partial, each checked against the library's kernel first -- residual bit "
+                "for bit, output within 2 ulp -- then timed round-robin with HIP events over "
+                f"the launches, median of the rounds; {lib['rotating_sets']} rotating buffer "
+                "sets).  cpol = cache-policy bits of the loads / stores (1 sc0, 2 nt, 16 sc1).  "
+                "% of peak counts the algorithmic bytes against 8 TB/s.\n\n")
+        f.write("| rank | design | cpol (loads / stores) | grid | median us | GB/s | % of 8 TB/s "
+                "| vs the library's kernel |\n|---|---|---|---|---|---|---|---|\n")
+        for i, r in enumerate(sorted(rows, key=lambda r: r["us"])):
+            what = (f"**library: `{r['what']}`**" if r["design"] == "library"
+                    else f"{r['design']}: {r['what']}")
+            f.write(f"| {i + 1} | {what} | {r['cpol']} | {r['grid']} | {r['us']:.2f} | "
+                    f"{r['gbs']:.0f} | {r['gbs'] / 80:.1f} | {lib['us'] / r['us']:.3f}x |\n")
+        f.write(f"\n{len(rows)} kernels timed.\n")
     print(md)
     return 0
 
@@ -431,6 +465,8 @@ def main() -> int:
         return counters_summary(sys.argv[2:])
     if len(sys.argv) > 1 and sys.argv[1] == "ceiling":
         return ceiling_summary(sys.argv[2:])
+    if len(sys.argv) > 1 and sys.argv[1] == "design":
+        return design_summary(sys.argv[2:])
     if len(sys.argv) > 1 and sys.argv[1] == "report":
         return report_summary(sys.argv[2:])
     ap = argparse.ArgumentParser()
