@@ -549,7 +549,8 @@ def main() -> int:
                     f"{event['value']:.{1 if gemm else 0}f} {event['unit']}.\n")
         f.write("\n## HBM bytes (rocprofv3 --pmc, one counter per run)\n\n")
         f.write("Commands: `rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -o run -- python "
-                f"bench.py --workload {w.name} --steps 10 --warmup 2 --no-cpu-baseline`, the same "
+                f"bench.py --workload {w.name} --steps 10 --warmup 2 --no-cpu-baseline --no-ceiling`, "
+                "the same "
                 "with `--pmc WRITE_SIZE`, and both counters over `python bench.py "
                 "--copy-calibration` (1 GiB device copy).\n\n")
         f.write("| counter | KiB per dispatch (median) | dispatches | copy-calibration KiB for "
