@@ -45,6 +45,7 @@ BRS_WORKSPACE_HEADER = 4608
 BRS_WORKSPACE_BYTES = BRS_WORKSPACE_HEADER + 4 * BRS_MAX_GROUPS
 
 _lib = None
+_fast = None   # the CPython marshalling module for the per-step calls, when built
 _lock = threading.Lock()
 
 
@@ -121,6 +122,13 @@ def lib() -> ctypes.CDLL:
                                                 ctypes.POINTER(ctypes.c_int32), i64]
             l.gemm_scatter_schedule.restype = c_int
             _lib = l
+            global _fast
+            try:
+                from . import _fastcall
+                _fastcall.open(LIB_PATH)
+                _fast = _fastcall
+            except ImportError:
+                _fast = None
         return _lib
 
 
@@ -165,10 +173,13 @@ def rmsnorm_fwd(out: torch.Tensor, x: torch.Tensor, gamma: torch.Tensor, eps: fl
     if out.shape != x.shape or gamma.numel() != hidden:
         raise RmsnormError(-2, f"shape mismatch: out {tuple(out.shape)} x {tuple(x.shape)} "
                                f"gamma {tuple(gamma.shape)}")
-    if not (out.dtype == x.dtype == gamma.dtype) or x.dtype not in DTYPE_CODE:
+    code = DTYPE_CODE.get(x.dtype)
+    if code is None or out.dtype != x.dtype or gamma.dtype != x.dtype:
         raise RmsnormError(-3, f"dtypes must match and be f32/f16/bf16")
-    _check(lib().rmsnorm_fwd(_dev_ptr(out, "out"), _dev_ptr(x, "x"), _dev_ptr(gamma, "gamma"),
-                             rows, hidden, float(eps), DTYPE_CODE[x.dtype], _stream(x, stream)))
+    args = (_dev_ptr(out, "out"), _dev_ptr(x, "x"), _dev_ptr(gamma, "gamma"), rows, hidden,
+            float(eps), code, _stream(x, stream))
+    l = _lib or lib()
+    _check(_fast.rmsnorm_fwd(*args) if _fast else l.rmsnorm_fwd(*args))
 
 
 def add_rmsnorm_fwd(out: torch.Tensor, residual: torch.Tensor, partials: Sequence[torch.Tensor],
@@ -177,16 +188,21 @@ def add_rmsnorm_fwd(out: torch.Tensor, residual: torch.Tensor, partials: Sequenc
     out = RMSNorm(residual) * gamma."""
     rows, hidden = _rows_hidden(residual)
     k = len(partials)
-    if out.shape != residual.shape or gamma.numel() != hidden or \
-            any(p.shape != residual.shape for p in partials):
+    shape, dt = residual.shape, residual.dtype
+    if out.shape != shape or gamma.numel() != hidden or any(p.shape != shape for p in partials):
         raise RmsnormError(-2, "shape mismatch between out, residual, partials and gamma")
-    if any(t.dtype != residual.dtype for t in [out, gamma, *partials]) or \
-            residual.dtype not in DTYPE_CODE:
+    code = DTYPE_CODE.get(dt)
+    if code is None or out.dtype != dt or gamma.dtype != dt or any(p.dtype != dt for p in partials):
         raise RmsnormError(-3, "dtypes must match and be f32/f16/bf16")
-    arr = (ctypes.c_void_p * max(k, 1))(*[_dev_ptr(p, f"partials[{i}]") for i, p in enumerate(partials)])
-    _check(lib().add_rmsnorm_fwd(_dev_ptr(out, "out"), _dev_ptr(residual, "residual"), arr, k,
-                                 _dev_ptr(gamma, "gamma"), rows, hidden, float(eps),
-                                 DTYPE_CODE[residual.dtype], _stream(residual, stream)))
+    ptrs = [_dev_ptr(p, f"partials[{i}]") for i, p in enumerate(partials)]
+    o, r, g = _dev_ptr(out, "out"), _dev_ptr(residual, "residual"), _dev_ptr(gamma, "gamma")
+    st = _stream(residual, stream)
+    l = _lib or lib()
+    if _fast:
+        _check(_fast.add_rmsnorm_fwd(o, r, ptrs, g, rows, hidden, float(eps), code, st))
+    else:
+        arr = (ctypes.c_void_p * max(k, 1))(*ptrs)
+        _check(l.add_rmsnorm_fwd(o, r, arr, k, g, rows, hidden, float(eps), code, st))
 
 
 def add_rmsnorm_ag_fwd(outs: Sequence[torch.Tensor], residual: torch.Tensor,

@@ -27,6 +27,8 @@ PROBE_SRC = os.path.join(HERE, "probe", "stream_probe.hip")
 PROBE_LIB = os.path.join(HERE, "libstreamprobe.so")
 ROW_PROBE_SRC = os.path.join(HERE, "probe", "row_probe.hip")
 ROW_PROBE_LIB = os.path.join(HERE, "librowprobe.so")
+FASTCALL_SRC = os.path.join(HERE, "pyext", "fastcall.c")
+FASTCALL_LIB = os.path.join(HERE, "_fastcall.so")
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -96,6 +98,15 @@ def build(jobs: int = 0, verbose: bool = False) -> str:
         if r.returncode != 0:
             raise RuntimeError(f"probe build failed for {src}:\n" + r.stdout + r.stderr)
         os.replace(ptmp, lib)
+    # the binding's argument marshalling for the per-step calls (host C)
+    import sysconfig
+    ftmp = FASTCALL_LIB + ".tmp%d" % os.getpid()
+    fcmd = ["gcc", "-O2", "-shared", "-fPIC", "-Wall", "-Wextra", "-Wno-cast-function-type",
+            "-I", sysconfig.get_paths()["include"], "-o", ftmp, FASTCALL_SRC, "-ldl"]
+    r = subprocess.run(fcmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("fastcall build failed:\n" + r.stdout + r.stderr)
+    os.replace(ftmp, FASTCALL_LIB)
     usage = check_assembly()
     spills = {k: v for k, v in usage.items() if v[1] > 0}
     if verbose:

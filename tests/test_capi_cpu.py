@@ -417,3 +417,32 @@ def test_block_sum_tune_range():
         B.block_sum_tune(B.BRS_MAX_GROUPS + 1)
     B.block_sum_tune(B.BRS_MAX_GROUPS)
     B.block_sum_tune(0)
+
+
+def test_fastcall_marshalling_matches_ctypes():
+    """The binding's CPython marshalling module for the per-step calls passes
+    arguments through unchanged: on calls the library rejects before any
+    launch, it returns the very codes the ctypes calls return."""
+    from row_wise_normalization_rmsnorm_amd import _fastcall as F
+    l = B.lib()
+    assert B._fast is F
+    P, G = FAKE, FAKE + (1 << 26)
+    cases = [(P, P + (1 << 24), G, -1, 64, 1e-6, 2, None),       # rows < 0
+             (P, P + (1 << 24), G, 4, 0, 1e-6, 2, None),         # hidden 0
+             (P, P + (1 << 24), G, 4, 64, float("nan"), 2, None),  # eps NaN
+             (None, P + (1 << 24), G, 4, 64, 1e-6, 2, None),     # out NULL
+             (P, P + (1 << 24), G, 4, 64, 1e-6, 9, None),        # dtype
+             (P + 2, P, G, 4, 64, 1e-6, 2, None),                # partial overlap
+             (P, P + (1 << 24), G, 0, 64, 1e-6, 2, None)]        # rows 0: no-op
+    for c in cases:
+        rc = F.rmsnorm_fwd(*c)
+        assert rc == l.rmsnorm_fwd(*c) and (rc != 0 or c[3] == 0), c
+    arr = lambda ps: (ctypes.c_void_p * max(len(ps), 1))(*ps)  # noqa: E731
+    R = FAKE + (1 << 25)
+    # every call below is rejected before a launch, or has rows == 0 (a
+    # no-op): the fake addresses are never dereferenced
+    for ps, k, rows in (([P + (1 << 24)], 1, 0), ([], 0, 4), ([P + (1 << 24)] * 17, 17, 4),
+                        ([R + 8], 1, 4), ([None], 1, 4), ([P + (1 << 24)], 1, -3)):
+        want = l.add_rmsnorm_fwd(P, R, arr(ps), k, G, rows, 64, 1e-6, 2, None)
+        got = F.add_rmsnorm_fwd(P, R, ps, G, rows, 64, 1e-6, 2, None)
+        assert got == want and (got != 0 or rows == 0), (k, rows, got, want)
