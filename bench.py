@@ -28,6 +28,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
        [--resident-context]
        python bench.py --workload NAME --sweep [--repeat R] [--variant-filter S]
        python bench.py --ceiling-sweep | --copy-calibration | --gemm-shapes
+       python bench.py --design-sweep | --gemm-design-sweep [--repeat R] [--steps K]
 """
 from __future__ import annotations
 
@@ -756,6 +757,141 @@ def design_sweep(a) -> int:
     return 0
 
 
+GEMM_DESIGNS = {0: "4 waves, 64-wide k stages in 2 LDS buffers, LDS reads and loads spread "
+                    "between the products",
+                 1: "4 waves, 64-wide k stages in 2 LDS buffers, LDS reads and loads in one "
+                    "block before the products",
+                 2: "4 waves, 32-wide k stages in {nbuf} LDS buffers (loads {nbuf} stages ahead), "
+                    "spread",
+                 3: "design 2 persistent: one workgroup per CU, pipeline across tiles, "
+                    "results stored from registers"}
+GEMM_MODES = {0: "the product", 1: "operands always in L2 (every workgroup computes tile 0)",
+              2: "no loads in the loop", 3: "products only (no loads, no LDS reads in the loop)",
+              4: "loads, no LDS reads in the loop"}
+
+
+def gemm_design_sweep(a) -> int:
+    """Time the 4-wave GEMM designs of libgemmprobe.so beside the library's
+    kernel and torch.matmul (hipBLASLt) on the same rotating operands of a
+    GEMM workload (default the 4096 x 8192 x 3584 bf16 one).  Every design is
+    first checked bit for bit against the library's 256 x 256 kernel on the
+    workload and on a ragged shape.  Design 2's timing modes (which skip
+    work, so their results are not checked) and the library and hipBLASLt are
+    also timed with k doubled, which takes each time apart into a part that
+    grows with k and a fixed part.  Timed round-robin over --repeat rounds;
+    one JSON line per variant with the median."""
+    import ctypes
+    import statistics
+    import torch
+    from row_wise_normalization_rmsnorm_amd import binding as B
+    from row_wise_normalization_rmsnorm_amd import inputs as I
+    from row_wise_normalization_rmsnorm_amd.workloads import GEMM_WORKLOADS, GEMM_HEADLINE, GemmWorkload
+
+    w0 = GEMM_WORKLOADS[a.workload or GEMM_HEADLINE]
+    dev = "cuda:0"
+    dt = {"bf16": 2, "f16": 1}[w0.dtype]
+    lib = ctypes.CDLL(os.path.join(ROOT, "row_wise_normalization_rmsnorm_amd", "libgemmprobe.so"))
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    lib.gemm_probe.argtypes = [ctypes.c_int] * 3 + [vp, i64, ctypes.c_int, vp, i64, vp, i64,
+                                                    i64, i64, i64, ctypes.c_int, vp]
+    sid = torch.cuda.current_stream().cuda_stream
+
+    def probe(design, mode, nbuf, dst, x, y):
+        ptrs = (ctypes.c_void_p * len(dst))(*[t.data_ptr() for t in dst])
+        rc = lib.gemm_probe(design, mode, nbuf, ptrs, dst[0].stride(0), len(dst), x.data_ptr(),
+                            x.stride(0), y.data_ptr(), y.stride(0), x.shape[0], y.shape[0],
+                            x.shape[1], dt, sid)
+        if rc != 0:
+            raise RuntimeError(f"gemm_probe({design}, {mode}, {nbuf}) failed: {rc}")
+
+    designs = [(0, 0, 0), (1, 0, 0), (2, 0, 4), (2, 0, 5), (3, 0, 4), (3, 0, 5)]
+    # correctness: the workload's operands, and a ragged shape (partial tiles,
+    # k not a multiple of 64, chunks not a multiple of the tile)
+    d = I.gemm_inputs(w0)
+    gen = torch.Generator().manual_seed(5)
+    tdt = d["a"].dtype
+    checks = [(w0.world, d["a"].to(dev), d["b"].to(dev)),
+              (8, torch.randn(520, 3576, generator=gen).to(tdt).to(dev),
+               torch.randn(768, 3576, generator=gen).to(tdt).to(dev))]
+    for world, x, y in checks:
+        m, n = x.shape[0], y.shape[0]
+        ref = [torch.empty(m // world, n, dtype=tdt, device=dev) for _ in range(world)]
+        B.gemm_scatter_fwd(ref, x, y, tile_n=B.GEMM_SCATTER_TILE_N)
+        for design, mode, nbuf in designs:
+            out = [torch.full((m // world, n), float("nan"), dtype=tdt, device=dev)
+                   for _ in range(world)]
+            probe(design, mode, nbuf, out, x, y)
+            torch.cuda.synchronize()
+            if not torch.equal(torch.cat(out).view(torch.int16), torch.cat(ref).view(torch.int16)):
+                raise RuntimeError(f"design {design} (nbuf {nbuf}) differs from the library on "
+                                   f"{m}x{n}x{x.shape[1]}")
+    del checks
+    print(f"[gemm-design] {len(designs)} designs agree with the library bit for bit",
+          file=sys.stderr, flush=True)
+
+    variants = {}
+    groups = []
+    for kmul in (1, 2):
+        w = GemmWorkload(w0.name if kmul == 1 else f"{w0.name}_k{w0.k * kmul}", w0.dtype, w0.m,
+                         w0.n, w0.k * kmul, w0.world)
+        dk = d if kmul == 1 else I.gemm_inputs(w)
+        nsets = max(1, int(-(-a.rotate_bytes * (1 << 30) // w.algorithmic_bytes())))
+        sets = [(dk["a"].to(dev), dk["b"].to(dev),
+                 [torch.empty(w.m // w.world, w.n, dtype=tdt, device=dev) for _ in range(w.world)])
+                for _ in range(nsets)]
+        groups.append((w, sets))
+
+        def lib_step(i, sets=sets, nsets=nsets):
+            x, y, o = sets[i % nsets]
+            B.gemm_scatter_fwd(o, x, y)
+
+        def blas_step(i, sets=sets, nsets=nsets):
+            x, y, _ = sets[i % nsets]
+            torch.matmul(x, y.t())
+
+        def pstep(design, mode, nbuf, sets=sets, nsets=nsets):
+            def f(i):
+                x, y, o = sets[i % nsets]
+                probe(design, mode, nbuf, o, x, y)
+            return f
+
+        tn = B.gemm_scatter_tile_n(w.m, w.n)
+        variants[(w.k, "library", f"gemm_scatter 8 waves, 256x{tn} tiles", -1, 0)] = (w, lib_step)
+        variants[(w.k, "hipBLASLt", "torch.matmul(a, b.t())", -1, 0)] = (w, blas_step)
+        for mode in range(5):
+            variants[(w.k, 2, GEMM_DESIGNS[2].format(nbuf=4), mode, 4)] = (w, pstep(2, mode, 4))
+        if kmul == 1:
+            for design, mode, nbuf in designs:
+                if design != 2 or nbuf != 4:
+                    variants[(w.k, design, GEMM_DESIGNS[design].format(nbuf=nbuf), mode, nbuf)] = \
+                        (w, pstep(design, mode, nbuf))
+    stream = torch.cuda.current_stream()
+    times = {key: [] for key in variants}
+    for rep in range(a.repeat):
+        for key, (w, f) in variants.items():
+            for i in range(10):
+                f(i)
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(a.steps):
+                f(i)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times[key].append(e0.elapsed_time(e1) / a.steps * 1e3)
+        print(f"[gemm-design] round {rep} done", file=sys.stderr, flush=True)
+    for key, t in times.items():
+        w = variants[key][0]
+        us = statistics.median(t)
+        print(json.dumps({"workload": w0.name, "k": key[0], "design": key[1], "what": key[2],
+                          "mode": key[3], "mode_what": GEMM_MODES.get(key[3], ""),
+                          "nbuf": key[4], "us": round(us, 2),
+                          "tflops": round(w.flops() / (us * 1e-6) / 1e12, 1),
+                          "runs_us": [round(x, 2) for x in t]}), flush=True)
+    return 0
+
+
 def copy_calibration() -> None:
     """A plain device copy of known size (1 GiB), for scaling the HBM byte
     counters read by rocprofv3 --pmc."""
@@ -802,6 +938,9 @@ def main() -> int:
                     help="write the output over the first input instead of a separate buffer")
     ap.add_argument("--rotate-bytes", type=float, default=2.0,
                     help="GiB of distinct buffers rotated through (cold cache)")
+    ap.add_argument("--gemm-design-sweep", action="store_true",
+                    help="time the 4-wave GEMM designs of libgemmprobe.so beside the library's "
+                         "kernel and hipBLASLt (one JSON line each)")
     ap.add_argument("--gemm-shapes", action="store_true",
                     help="time the GEMM with the scatter epilogue over a list of shapes against "
                          "torch.matmul (one JSON line each) and exit")
@@ -832,6 +971,8 @@ def main() -> int:
         return design_sweep(a)
 
     from row_wise_normalization_rmsnorm_amd.workloads import GEMM_WORKLOADS
+    if a.gemm_design_sweep:
+        return gemm_design_sweep(a)
     if a.gemm_shapes:
         return gemm_shapes(a)
     if a.workload in GEMM_WORKLOADS:

@@ -27,6 +27,8 @@ PROBE_SRC = os.path.join(HERE, "probe", "stream_probe.hip")
 PROBE_LIB = os.path.join(HERE, "libstreamprobe.so")
 ROW_PROBE_SRC = os.path.join(HERE, "probe", "row_probe.hip")
 ROW_PROBE_LIB = os.path.join(HERE, "librowprobe.so")
+GEMM_PROBE_SRC = os.path.join(HERE, "probe", "gemm_probe.hip")
+GEMM_PROBE_LIB = os.path.join(HERE, "libgemmprobe.so")
 FASTCALL_SRC = os.path.join(HERE, "pyext", "fastcall.c")
 FASTCALL_LIB = os.path.join(HERE, "_fastcall.so")
 ARCH = "gfx950"
@@ -89,8 +91,9 @@ def build(jobs: int = 0, verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
     # the measurement aids used by bench.py (separate libraries): the
-    # bandwidth-ceiling probe and the row-kernel design probe
-    for src, lib in ((PROBE_SRC, PROBE_LIB), (ROW_PROBE_SRC, ROW_PROBE_LIB)):
+    # bandwidth-ceiling probe and the row-kernel and GEMM design probes
+    for src, lib in ((PROBE_SRC, PROBE_LIB), (ROW_PROBE_SRC, ROW_PROBE_LIB),
+                     (GEMM_PROBE_SRC, GEMM_PROBE_LIB)):
         ptmp = lib + ".tmp%d" % os.getpid()
         pcmd = [HIPCC, f"--offload-arch={ARCH}", "-O3", "-fPIC", "-shared", "-std=c++17",
                 "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-o", ptmp, src]

@@ -46,159 +46,25 @@
 //     the XCD's L2 (measured 1214 -> 1241 TFLOP/s against groups of two
 //     tile-rows on the 4096 x 8192 x 3584 bf16 product).
 //   - Interior tiles with 16-byte aligned output rows stage the rounded tile
-//     in LDS and write whole 512-byte row segments.
+//     in LDS and write whole 512-byte row segments, with nontemporal stores:
+//     the output (64 MiB for the 4096 x 8192 product) then does not push the
+//     operand rows out of the XCDs' L2 (measured 2-4% faster at 1024, 4096
+//     and 8192 tokens, 8192 x 3584 weights).
+//   - Designs with four waves of 128 x 128 blocks (one per SIMD) fed by
+//     gfx950's buffer-load-to-LDS form were measured beside this one with
+//     probe/gemm_probe.hip; none was faster (bench.py --gemm-design-sweep).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdio.h>
 #include <stdlib.h>
 
 #include "../../include/gemm_scatter.h"
+#include "gemm_scatter_kernels.hpp"
 
 int rmsn_set_error(int code, const char* msg);
 
 
 namespace gsc {
-
-constexpr int BM = GEMM_SCATTER_TILE_M;
-constexpr int BN = GEMM_SCATTER_TILE_N;            // wide tile
-constexpr int BN_NARROW = GEMM_SCATTER_TILE_N_NARROW;
-constexpr int BK = 64;                 // k elements per step (128 bytes of a row)
-constexpr int kThreads = 512;          // eight waves, two per SIMD
-constexpr int kChunksPerRow = BK / 8;  // 16-byte chunks per LDS row
-constexpr int kXcds = 8;
-constexpr int kRoundPerXcd = 32;       // positions each XCD takes per round (one per CU)
-constexpr int kGroupM = 8;             // tile-rows per schedule group
-// Buffer resource word 3 for gfx9-family raw (untyped) buffer access; the
-// offset used for a chunk outside every operand's range.
-constexpr int kRsrcWord3 = 0x00020000;
-constexpr int kOutOfRange = 0x7FFFFFF0;
-static_assert(BM == 256 && BN == 256 && BN_NARROW == 128 && kThreads == 512,
-              "the thread mapping assumes these");
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-
-template <int DT>
-struct Elem;
-
-template <>
-struct Elem<RMSN_BF16> {
-  __device__ static f32x4 mfma(u32x4 x, u32x4 y, f32x4 acc) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, x),
-                                                   __builtin_bit_cast(bf16x8, y), acc, 0, 0, 0);
-  }
-  __device__ static float decode(uint16_t h) { return __builtin_bit_cast(float, (uint32_t)h << 16); }
-  __device__ static uint32_t pack2(float lo, float hi) {
-    const f32x2 v = {lo, hi};
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
-  }
-  __device__ static uint16_t pack1(float v) { return (uint16_t)(pack2(v, 0.0f) & 0xFFFFu); }
-};
-
-template <>
-struct Elem<RMSN_F16> {
-  __device__ static f32x4 mfma(u32x4 x, u32x4 y, f32x4 acc) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, x),
-                                                  __builtin_bit_cast(f16x8, y), acc, 0, 0, 0);
-  }
-  __device__ static float decode(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
-  __device__ static uint32_t pack2(float lo, float hi) {
-    const f32x2 v = {lo, hi};
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
-  }
-  __device__ static uint16_t pack1(float v) { return (uint16_t)(pack2(v, 0.0f) & 0xFFFFu); }
-};
-
-// ---- tile schedule (shared by the kernel and the host's plan query) --------
-
-struct Sched {
-  int tiles_m, tiles_n, tiles;
-  int tm_start;      // first tile-row of the rotated order
-  int remote_rows;   // rotated tile-rows before the local chunk's
-  int local_group;   // tile-rows per group among the local chunk's
-};
-
-__host__ __device__ inline Sched make_sched(int m, int n, int tn, int world, int rank) {
-  Sched s;
-  s.tiles_m = (m + BM - 1) / BM;
-  s.tiles_n = (n + tn - 1) / tn;
-  s.tiles = s.tiles_m * s.tiles_n;
-  // A tile-row belongs to the chunk of its first row.  Rotated order starts
-  // at the first tile-row of chunk rank + 1 (ring order), so the tile-rows
-  // of the local chunk (rank) come last.
-  const int64_t chunk_rows = world > 0 ? (int64_t)m / world : m;
-  const int64_t first_local = ((int64_t)rank * chunk_rows + BM - 1) / BM;
-  int64_t end_local = ((int64_t)(rank + 1) * chunk_rows + BM - 1) / BM;
-  if (end_local > s.tiles_m) end_local = s.tiles_m;
-  const int64_t local = end_local > first_local ? end_local - first_local : 0;
-  s.tm_start = (int)(end_local >= s.tiles_m ? 0 : end_local);
-  s.remote_rows = s.tiles_m - (int)local;
-  s.local_group = local < kGroupM ? (local > 0 ? (int)local : 1) : kGroupM;
-  return s;
-}
-
-// launch order -> schedule position: each round of kXcds * kRoundPerXcd
-// positions is dealt out so that XCD x (which receives workgroups x, x + 8,
-// ...) takes a contiguous run of kRoundPerXcd positions; a final partial
-// round keeps the identity.
-__host__ __device__ inline int position_of_wg(int w, int tiles) {
-  constexpr int round = kXcds * kRoundPerXcd;
-  const int full = tiles / round * round;
-  if (w >= full) return w;
-  const int base = w / round * round;
-  const int within = w - base;
-  return base + (within % kXcds) * kRoundPerXcd + within / kXcds;
-}
-
-// schedule position -> tile.  The rotated tile-rows of the other ranks'
-// chunks come first, in groups of kGroupM tile-rows, then the local chunk's
-// tile-rows in groups of local_group; inside a group the tiles go
-// column-major (down the group's tile-rows, then to the next tile-column),
-// so a run of positions covers a compact block of the output.
-__host__ __device__ inline int tile_at(int p, const Sched& s) {
-  const int remote_tiles = s.remote_rows * s.tiles_n;
-  int first_row, region_rows, gsize;
-  if (p < remote_tiles) {
-    first_row = 0;
-    region_rows = s.remote_rows;
-    gsize = kGroupM;
-  } else {
-    p -= remote_tiles;
-    first_row = s.remote_rows;
-    region_rows = s.tiles_m - s.remote_rows;
-    gsize = s.local_group;
-  }
-  const int group = gsize * s.tiles_n;
-  const int g = p / group;
-  const int idx = p - g * group;
-  const int gfirst = g * gsize;
-  const int rows = region_rows - gfirst < gsize ? region_rows - gfirst : gsize;
-  const int ptm = first_row + gfirst + idx % rows;
-  const int tn = idx / rows;
-  const int tm = (ptm + s.tm_start) % s.tiles_m;
-  return tm * s.tiles_n + tn;
-}
-
-struct Params {
-  const uint16_t* a;
-  const uint16_t* b;
-  const uint16_t* c;
-  int64_t lda, ldb, ldc, ldd;
-  uint16_t* dst[GEMM_SCATTER_WORLD_MAX];
-  uint32_t* flags;
-  uint32_t epoch;
-  int m, n, k;
-  int chunk_rows;
-  float alpha, beta;
-  int vec_out;  // 2: dst rows 16-byte aligned (and C rows 8); 1: both 8-byte; 0: neither
-  Sched sched;
-};
 
 // Tile shape of one workgroup: 256 rows by TN columns (256 or 128).  The
 // eight waves cover it as WAVES_M x WAVES_N blocks of WR x WC outputs, each
@@ -414,9 +280,9 @@ __global__ __launch_bounds__(kThreads) void gemm_scatter_kernel(Params p) {
     // interior tile, 16-byte aligned output rows: the rounded tile is staged
     // in LDS, free since the loop's last barrier (no wave reads LDS after
     // it), then leaves in 16-byte stores that cover whole row segments of
-    // TN * 2 bytes.  The 16-byte chunk c of staged row r sits at chunk
-    // position c ^ (r & 15), so the 16 rows one staging write touches land
-    // in 16 different bank groups.
+    // TN * 2 bytes (nontemporal: the output is not read back here).  The
+    // 16-byte chunk c of staged row r sits at chunk position c ^ (r & 15), so
+    // the 16 rows one staging write touches land in 16 different bank groups.
     uint32_t* st = reinterpret_cast<uint32_t*>(&lds[0].a[0]);
     constexpr int pitch = TN / 2;  // staged row pitch in 32-bit words
 #pragma unroll
@@ -451,7 +317,7 @@ __global__ __launch_bounds__(kThreads) void gemm_scatter_kernel(Params p) {
       uint16_t* drow = p.dst[q] + (int64_t)(gm - q * p.chunk_rows) * p.ldd + n0;
       const int c = (int)((unsigned)tid % S::CPR);
       const u32x4 v = *reinterpret_cast<const u32x4*>(st + r * pitch + ((c ^ (r & 15)) * 4));
-      *reinterpret_cast<u32x4*>(drow + c * 8) = v;
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(drow + c * 8));
     }
   } else if (p.vec_out && m0 + BM <= p.m && n0 + TN <= p.n) {
     // interior tile: every element exists and every access is 8-byte aligned

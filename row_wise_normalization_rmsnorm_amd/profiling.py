@@ -249,6 +249,64 @@ COUNTERS = ["SQ_LDS_BANK_CONFLICT", "SQ_INSTS_LDS", "SQ_WAVES", "SQ_WAVE_CYCLES"
             "TCC_HIT_sum", "TCC_MISS_sum"]
 
 
+def gemm_design_summary(argv) -> int:
+    """profiles/gemm_design_sweep__<workload>.md from the JSON lines of
+    ``bench.py --gemm-design-sweep``: the 4-wave designs beside the library's
+    kernel and hipBLASLt, and the time taken apart by design 2's modes at k
+    and 2k (the part that grows with k, and the fixed rest)."""
+    ap = argparse.ArgumentParser()
+    ap.add_argument("jsonl")
+    ap.add_argument("--command", default="python bench.py --gemm-design-sweep --repeat 3 --steps 50")
+    a = ap.parse_args(argv)
+    rows = [json.loads(l) for l in open(a.jsonl) if l.startswith("{")]
+    wl = rows[0]["workload"]
+    k1 = min(r["k"] for r in rows)
+    k2 = max(r["k"] for r in rows)
+    md = os.path.join(PROFILES, f"gemm_design_sweep__{wl}.md")
+    lib = next(r for r in rows if r["design"] == "library" and r["k"] == k1)
+    with open(md, "w") as f:
+        f.write(f"# GEMM designs on {wl}\n\n")
+        f.write(f"Command: `{a.command}` (libgemmprobe.so's designs; each checked bit for bit "
+                "against the library's 256 x 256 kernel on the workload and on a ragged "
+                "520 x 768 x 3576 product before timing; timed round-robin with HIP events over "
+                "back-to-back launches on rotating operand sets, median of the rounds).  "
+                "TFLOP/s counts 2 m n k; the dense bf16 matrix-core peak is 2500.\n\n")
+        f.write(f"## Designs at k = {k1}\n\n| rank | kernel | median us | TFLOP/s | vs the library |\n"
+                "|---|---|---|---|---|\n")
+        first = [r for r in rows if r["k"] == k1 and r["mode"] in (0, -1)]
+        for i, r in enumerate(sorted(first, key=lambda r: r["us"])):
+            if r["design"] == "library":
+                name = f"**library: {r['what']}**"
+            elif r["design"] == "hipBLASLt":
+                name = f"hipBLASLt: {r['what']}"
+            else:
+                bufs = f" ({r['nbuf']} LDS buffers)" if r["design"] == 3 else ""
+                name = f"design {r['design']}{bufs}: {r['what']}"
+            f.write(f"| {i + 1} | {name} | {r['us']:.1f} | {r['tflops']:.0f} | "
+                    f"{lib['us'] / r['us']:.3f}x |\n")
+        f.write(f"\n## Where the time goes: design 2 (4 buffers) by mode, at k = {k1} and {k2}\n\n"
+                f"The part that grows with k is t({k2}) - t({k1}), for {k2 - k1} more k; the "
+                f"fixed part is the rest of t({k1}).  Modes 1-4 skip work and give wrong "
+                "results; they only take the time apart.\n\n"
+                f"| kernel | mode | us at k = {k1} | us at k = {k2} | growing part, us per "
+                f"{k2 - k1} k | fixed part, us |\n|---|---|---|---|---|---|\n")
+        keyed = {}
+        for r in rows:
+            keyed.setdefault((r["design"], r["mode"], r["nbuf"]), {})[r["k"]] = r
+        order = [("library", -1, 0), ("hipBLASLt", -1, 0)] + [(2, m, 4) for m in range(5)]
+        for key in order:
+            if key not in keyed or k1 not in keyed[key] or k2 not in keyed[key]:
+                continue
+            r1, r2 = keyed[key][k1], keyed[key][k2]
+            slope = r2["us"] - r1["us"]
+            name = key[0] if isinstance(key[0], str) else f"design {key[0]}"
+            f.write(f"| {name} | {r1['mode_what'] or '-'} | {r1['us']:.1f} | {r2['us']:.1f} | "
+                    f"{slope:.1f} | {r1['us'] - slope * k1 / (k2 - k1):.1f} |\n")
+        f.write(f"\n{len(rows)} kernels timed.\n")
+    print(md)
+    return 0
+
+
 def report_summary(argv) -> int:
     """profiles/per_config_report.md: for every workload, the GPU figures and
     the oracle's CPU rate (many cores and one) from ``bench.py --workload W``
@@ -467,6 +525,8 @@ def main() -> int:
         return ceiling_summary(sys.argv[2:])
     if len(sys.argv) > 1 and sys.argv[1] == "design":
         return design_summary(sys.argv[2:])
+    if len(sys.argv) > 1 and sys.argv[1] == "gemm-design":
+        return gemm_design_summary(sys.argv[2:])
     if len(sys.argv) > 1 and sys.argv[1] == "report":
         return report_summary(sys.argv[2:])
     ap = argparse.ArgumentParser()

@@ -111,6 +111,33 @@ def test_ceiling_summary(tmp_path, monkeypatch):
     assert "| read 1 | 6000 | 6100 |" in md
 
 
+def test_gemm_design_summary(tmp_path, monkeypatch):
+    monkeypatch.setattr(prof, "PROFILES", str(tmp_path / "profiles"))
+    os.makedirs(tmp_path / "profiles")
+    wl = "gemm_scatter_bf16_4096x8192x3584_w8"
+
+    def row(k, design, mode, nbuf, us):
+        return {"workload": wl, "k": k, "design": design, "what": f"w{design}", "mode": mode,
+                "mode_what": "m" if mode > 0 else "", "nbuf": nbuf, "us": us,
+                "tflops": 1.0, "runs_us": [us]}
+    lines = [row(3584, "library", -1, 0, 200.0), row(7168, "library", -1, 0, 380.0),
+             row(3584, "hipBLASLt", -1, 0, 160.0), row(7168, "hipBLASLt", -1, 0, 305.0),
+             row(3584, 2, 0, 4, 190.0), row(7168, 2, 0, 4, 360.0),
+             row(3584, 2, 3, 4, 130.0), row(7168, 2, 3, 4, 235.0),
+             row(3584, 3, 0, 5, 250.0)]
+    src = tmp_path / "g.jsonl"
+    src.write_text("\n".join(json.dumps(x) for x in lines) + "\n")
+    assert prof.gemm_design_summary([str(src)]) == 0
+    md = open(tmp_path / "profiles" / f"gemm_design_sweep__{wl}.md").read()
+    # ranking at the smaller k: timing modes left out, library marked
+    assert "| 1 | hipBLASLt: w" in md and "| 2 | design 2: w2 | 190.0" in md
+    assert "| 3 | **library: wlibrary** | 200.0 | 1 | 1.000x |" in md
+    assert "| 4 | design 3 (5 LDS buffers): w3 | 250.0 | 1 | 0.800x |" in md
+    # growing part t(2k) - t(k) and fixed part t(k) - growing part
+    assert "| library | - | 200.0 | 380.0 | 180.0 | 20.0 |" in md
+    assert "| design 2 | m | 130.0 | 235.0 | 105.0 | 25.0 |" in md
+
+
 def test_bench_refuses_more_than_one_gpu():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)
