@@ -37,6 +37,7 @@ constexpr int kUnroll = 4;
 constexpr int kMaxGroups = BRS_MAX_GROUPS;
 constexpr int kMinGroups = 256;        // one per CU
 constexpr int kGridCap = 512;          // two per CU: measured best for large inputs
+static_assert(kMinGroups <= kGridCap && kGridCap <= kMaxGroups, "grid bounds");
 constexpr int kChunksPerThread = 32;   // target share of a thread
 // Workspace: completion counters, each on its own 128-byte line -- the top
 // counter at line 0 and kSub first-level counters at lines 1..kSub -- then
@@ -413,7 +414,7 @@ void* scratch_for(int dev, hipStream_t stream) {
 }  // namespace
 
 extern "C" int block_sum_tune(int groups) {
-  if (groups < 0 || groups > BRS_MAX_GROUPS)
+  if (groups < 0 || groups > brs::kMaxGroups)
     return rmsn_set_error(RMSN_ERR_SHAPE, "groups outside [0, BRS_MAX_GROUPS]");
   g_groups_override.store(groups, std::memory_order_relaxed);
   return RMSN_OK;

@@ -58,6 +58,8 @@
 #include <stdio.h>
 #include <stdlib.h>
 
+#include <type_traits>
+
 #include "../../include/gemm_scatter.h"
 #include "gemm_scatter_kernels.hpp"
 
@@ -65,6 +67,120 @@ int rmsn_set_error(int code, const char* msg);
 
 
 namespace gsc {
+
+// The results of one tile, alpha * D + beta * C, into the destination
+// chunks, then the tile's flag.  acc[s][t][r] is D[row m0 + wm*WR + t*16 +
+// (lane & 15)][col n0 + wn*WC + s*16 + 4*(lane >> 4) + r] for the THREADS / 64
+// waves' WR x WC blocks of a 256 x TN tile; staging: BM * TN * 2 bytes of LDS
+// that no wave reads any more.
+template <int DT, int TN, int WR, int WC, int THREADS, typename AccT>
+__device__ __forceinline__ void store_tile(const AccT& acc, const Params& p, int tile, int m0, int n0,
+                                           int wm, int wn, int tid, uint32_t* staging) {
+  using E = Elem<DT>;
+  constexpr int NX = WC / 16, NY = WR / 16;
+  constexpr int CPR = TN / 8;          // 16-byte chunks per staged output row
+  constexpr int RPP = THREADS / CPR;   // staged rows stored per pass
+  static_assert(CPR >= 16 && BM % RPP == 0, "staging layout");
+  const int lane = tid & 63;
+  const int row0 = m0 + wm * WR + (lane & 15);
+  const int col0 = n0 + wn * WC + 4 * (lane >> 4);
+  if (p.vec_out == 2 && m0 + BM <= p.m && n0 + TN <= p.n) {
+    // interior tile, 16-byte aligned output rows: the rounded tile is staged
+    // in LDS, then leaves in 16-byte stores that cover whole row segments of
+    // TN * 2 bytes (nontemporal: the output is not read back here).  The
+    // 16-byte chunk c of staged row r sits at chunk position c ^ (r & 15), so
+    // the 16 rows one staging write touches land in 16 different bank groups.
+    uint32_t* st = staging;
+    constexpr int pitch = TN / 2;  // staged row pitch in 32-bit words
+#pragma unroll
+    for (int t = 0; t < NY; ++t) {
+      const int r = wm * WR + t * 16 + (lane & 15);
+      const uint16_t* crow = p.c ? p.c + (int64_t)(m0 + r) * p.ldc + col0 : nullptr;
+#pragma unroll
+      for (int s = 0; s < NX; ++s) {
+        float v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = p.alpha * acc[s][t][q];
+        if (crow) {
+          const u32x2 cv = *reinterpret_cast<const u32x2*>(crow + s * 16);
+          v[0] = __builtin_fmaf(p.beta, E::decode((uint16_t)(cv.x & 0xFFFFu)), v[0]);
+          v[1] = __builtin_fmaf(p.beta, E::decode((uint16_t)(cv.x >> 16)), v[1]);
+          v[2] = __builtin_fmaf(p.beta, E::decode((uint16_t)(cv.y & 0xFFFFu)), v[2]);
+          v[3] = __builtin_fmaf(p.beta, E::decode((uint16_t)(cv.y >> 16)), v[3]);
+        }
+        const int c = wn * WC + s * 16 + 4 * (lane >> 4);  // column in the tile
+        const int chunk = (c >> 3) ^ (r & 15);
+        *reinterpret_cast<u32x2*>(st + r * pitch + chunk * 4 + ((c >> 2) & 1) * 2) =
+            u32x2{E::pack2(v[0], v[1]), E::pack2(v[2], v[3])};
+      }
+    }
+    __syncthreads();
+    // thread t stores chunk (t % CPR) of rows t / CPR + RPP i
+#pragma unroll 4
+    for (int i = 0; i < BM / RPP; ++i) {
+      const int r = i * RPP + (int)((unsigned)tid / CPR);
+      const int gm = m0 + r;
+      const int q = gm / p.chunk_rows;
+      uint16_t* drow = p.dst[q] + (int64_t)(gm - q * p.chunk_rows) * p.ldd + n0;
+      const int c = (int)((unsigned)tid % CPR);
+      const u32x4 v = *reinterpret_cast<const u32x4*>(st + r * pitch + ((c ^ (r & 15)) * 4));
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(drow + c * 8));
+    }
+  } else if (p.vec_out && m0 + BM <= p.m && n0 + TN <= p.n) {
+    // interior tile: every element exists and every access is 8-byte aligned
+#pragma unroll
+    for (int t = 0; t < NY; ++t) {
+      const int gm = row0 + t * 16;
+      const int q = gm / p.chunk_rows;
+      uint16_t* drow = p.dst[q] + (int64_t)(gm - q * p.chunk_rows) * p.ldd + col0;
+      const uint16_t* crow = p.c ? p.c + (int64_t)gm * p.ldc + col0 : nullptr;
+#pragma unroll
+      for (int s = 0; s < NX; ++s) {
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = p.alpha * acc[s][t][r];
+        if (crow) {
+          const u32x2 cv = *reinterpret_cast<const u32x2*>(crow + s * 16);
+          v[0] = __builtin_fmaf(p.beta, E::decode((uint16_t)(cv.x & 0xFFFFu)), v[0]);
+          v[1] = __builtin_fmaf(p.beta, E::decode((uint16_t)(cv.x >> 16)), v[1]);
+          v[2] = __builtin_fmaf(p.beta, E::decode((uint16_t)(cv.y & 0xFFFFu)), v[2]);
+          v[3] = __builtin_fmaf(p.beta, E::decode((uint16_t)(cv.y >> 16)), v[3]);
+        }
+        *reinterpret_cast<u32x2*>(drow + s * 16) = u32x2{E::pack2(v[0], v[1]), E::pack2(v[2], v[3])};
+      }
+    }
+  } else {
+    // edge tile (or unaligned rows): element by element, inside m x n only
+#pragma unroll
+    for (int t = 0; t < NY; ++t) {
+      const int gm = row0 + t * 16;
+      const bool row_ok = gm < p.m;
+      const int gmc = row_ok ? gm : 0;
+      const int q = gmc / p.chunk_rows;
+      uint16_t* drow = p.dst[q] + (int64_t)(gmc - q * p.chunk_rows) * p.ldd;
+      const uint16_t* crow = p.c ? p.c + (int64_t)gmc * p.ldc : nullptr;
+#pragma unroll
+      for (int s = 0; s < NX; ++s) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int gn = col0 + s * 16 + r;
+          if (row_ok && gn < p.n) {
+            float v = p.alpha * acc[s][t][r];
+            if (crow) v = __builtin_fmaf(p.beta, E::decode(crow[gn]), v);
+            drow[gn] = E::pack1(v);
+          }
+        }
+      }
+    }
+  }
+
+  if (p.flags) {
+    __threadfence_system();
+    __syncthreads();
+    if (tid == 0)
+      __hip_atomic_store(p.flags + tile, p.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+  }
+}
 
 // Tile shape of one workgroup: 256 rows by TN columns (256 or 128).  The
 // eight waves cover it as WAVES_M x WAVES_N blocks of WR x WC outputs, each
@@ -87,9 +203,10 @@ struct Shape {
   static_assert(WC == 64 && NY * 16 == WR && CPR >= 16 && BM % RPP == 0, "tile mapping");
 };
 
-template <int DT, int TN>
-__global__ __launch_bounds__(kThreads) void gemm_scatter_kernel(Params p) {
+template <int DT>
+__global__ __launch_bounds__(kThreads) void gemm_narrow_kernel(Params p) {
   using E = Elem<DT>;
+  constexpr int TN = BN_NARROW;
   using S = Shape<TN>;
   constexpr int NX = S::NX, NY = S::NY, NB = S::NB;
   // per stage, [row * 8 + chunk] of the tile's BM rows of A, then of its TN
@@ -149,18 +266,6 @@ __global__ __launch_bounds__(kThreads) void gemm_scatter_kernel(Params p) {
   const int b_off_last = (b_last * (int)p.ldb + lchunk * 8) * 2;
   const int a_row_step = 64 * (int)p.lda * 2, b_row_step = 64 * (int)p.ldb * 2;
 
-  auto gload = [&](int kt) {
-    const bool kin = kt * BK + lchunk * 8 < p.k;
-    const int kb = kt * BK * 2;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int oa = kin ? (i < a_rows ? a_off0 + i * a_row_step : a_off_last) + kb : kOutOfRange;
-      const int ob = kin ? (i < b_rows ? b_off0 + i * b_row_step : b_off_last) + kb : kOutOfRange;
-      ra[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsa, oa, 0, 0));
-      if (i < NB)
-        rb[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsb, ob, 0, 0));
-    }
-  };
   auto lstore = [&](int stage) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -189,190 +294,185 @@ __global__ __launch_bounds__(kThreads) void gemm_scatter_kernel(Params p) {
       for (int t = 0; t < NY; ++t) acc[s][t] = E::mfma(xf[s], yf[t], acc[s][t]);
   };
 
-  if constexpr (TN == BN_NARROW) {
-    // A narrow tile has half the products per k step, too few to cover a
-    // load issued at the step's start (measured 98.8 -> 64.8 us on the
-    // 1024 x 8192 x 3584 bf16 product): the loads of step kt + 2 go out as
-    // soon as the LDS writes of step kt + 1 free their registers, a whole k
-    // step before they are needed.  The row offsets are fixed before the
-    // loop so that no load sits under a branch (a branch there makes the
-    // compiler wait for every load in flight).
-    int a_off[4], b_off[NB];
+  // A narrow tile has half the products per k step, too few to cover a
+  // load issued at the step's start (measured 98.8 -> 64.8 us on the
+  // 1024 x 8192 x 3584 bf16 product): the loads of step kt + 2 go out as
+  // soon as the LDS writes of step kt + 1 free their registers, a whole k
+  // step before they are needed.  The row offsets are fixed before the
+  // loop so that no load sits under a branch (a branch there makes the
+  // compiler wait for every load in flight).
+  int a_off[4], b_off[NB];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    a_off[i] = i < a_rows ? a_off0 + i * a_row_step : a_off_last;
+    if (i < NB) b_off[i] = i < b_rows ? b_off0 + i * b_row_step : b_off_last;
+  }
+  auto gload_early = [&](int kt) {
+    const bool kin = kt * BK + lchunk * 8 < p.k;
+    const int kb = kt * BK * 2;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      a_off[i] = i < a_rows ? a_off0 + i * a_row_step : a_off_last;
-      if (i < NB) b_off[i] = i < b_rows ? b_off0 + i * b_row_step : b_off_last;
+      ra[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            rsa, kin ? a_off[i] + kb : kOutOfRange, 0, 0));
+      if (i < NB)
+        rb[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                              rsb, kin ? b_off[i] + kb : kOutOfRange, 0, 0));
     }
-    auto gload_early = [&](int kt) {
-      const bool kin = kt * BK + lchunk * 8 < p.k;
-      const int kb = kt * BK * 2;
+  };
+  if (nk > 0) {
+    gload_early(0);
+    lstore(0);
+    gload_early(nk > 1 ? 1 : 0);
+  }
+  __syncthreads();
+  u32x4 xf[NX], yf[NY];
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    read_frags(cur, 0, xf, yf);
+    mfmas(xf, yf);
+    read_frags(cur, 1, xf, yf);
+    lstore(cur ^ 1);
+    gload_early(kt + 2 < nk ? kt + 2 : nk - 1);
+    mfmas(xf, yf);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        ra[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                              rsa, kin ? a_off[i] + kb : kOutOfRange, 0, 0));
-        if (i < NB)
-          rb[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                rsb, kin ? b_off[i] + kb : kOutOfRange, 0, 0));
-      }
-    };
-    if (nk > 0) {
-      gload_early(0);
-      lstore(0);
-      gload_early(nk > 1 ? 1 : 0);
+    for (int i = 0; i < S::NLOAD; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);       // one LDS write
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);       // one global (buffer) load
+      __builtin_amdgcn_sched_group_barrier(0x008, S::PER, 0);  // products
     }
+    if constexpr (S::REST > 0) __builtin_amdgcn_sched_group_barrier(0x008, S::REST, 0);
     __syncthreads();
-    u32x4 xf[NX], yf[NY];
-    for (int kt = 0; kt < nk; ++kt) {
-      const int cur = kt & 1;
-      read_frags(cur, 0, xf, yf);
-      mfmas(xf, yf);
-      read_frags(cur, 1, xf, yf);
-      lstore(cur ^ 1);
-      gload_early(kt + 2 < nk ? kt + 2 : nk - 1);
-      mfmas(xf, yf);
-#pragma unroll
-      for (int i = 0; i < S::NLOAD; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);       // one LDS write
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);       // one global (buffer) load
-        __builtin_amdgcn_sched_group_barrier(0x008, S::PER, 0);  // products
-      }
-      if constexpr (S::REST > 0) __builtin_amdgcn_sched_group_barrier(0x008, S::REST, 0);
-      __syncthreads();
-    }
-  } else {
-    if (nk > 0) {
-      gload(0);
-      lstore(0);
-    }
-    __syncthreads();
-    u32x4 xf[NX], yf[NY];
-    // two waves per SIMD: while one waits on LDS or memory the other's
-    // products run, so each wave keeps one fragment set
-    for (int kt = 0; kt < nk; ++kt) {
-      const int cur = kt & 1;
-      gload(kt + 1 < nk ? kt + 1 : kt);
-      read_frags(cur, 0, xf, yf);
-      mfmas(xf, yf);
-  #pragma unroll
-      for (int i = 0; i < S::NLOAD; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);       // one global (buffer) load
-        __builtin_amdgcn_sched_group_barrier(0x008, S::PER, 0);  // products
-      }
-      if constexpr (S::REST > 0) __builtin_amdgcn_sched_group_barrier(0x008, S::REST, 0);
-      read_frags(cur, 1, xf, yf);
-      lstore(cur ^ 1);
-      mfmas(xf, yf);
-  #pragma unroll
-      for (int i = 0; i < S::NLOAD; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);       // one LDS write
-        __builtin_amdgcn_sched_group_barrier(0x008, S::PER, 0);  // products
-      }
-      if constexpr (S::REST > 0) __builtin_amdgcn_sched_group_barrier(0x008, S::REST, 0);
-      __syncthreads();
-    }
   }
 
-  // epilogue: acc[s][t][r] is D[row m0 + wm*WR + t*16 + (lane & 15)]
-  //                           [col n0 + wn*WC + s*16 + 4*(lane >> 4) + r]
-  const int row0 = m0 + wm * S::WR + (lane & 15);
-  const int col0 = n0 + wn * S::WC + 4 * (lane >> 4);
-  if (p.vec_out == 2 && m0 + BM <= p.m && n0 + TN <= p.n) {
-    // interior tile, 16-byte aligned output rows: the rounded tile is staged
-    // in LDS, free since the loop's last barrier (no wave reads LDS after
-    // it), then leaves in 16-byte stores that cover whole row segments of
-    // TN * 2 bytes (nontemporal: the output is not read back here).  The
-    // 16-byte chunk c of staged row r sits at chunk position c ^ (r & 15), so
-    // the 16 rows one staging write touches land in 16 different bank groups.
-    uint32_t* st = reinterpret_cast<uint32_t*>(&lds[0].a[0]);
-    constexpr int pitch = TN / 2;  // staged row pitch in 32-bit words
-#pragma unroll
-    for (int t = 0; t < NY; ++t) {
-      const int r = wm * S::WR + t * 16 + (lane & 15);
-      const uint16_t* crow = p.c ? p.c + (int64_t)(m0 + r) * p.ldc + col0 : nullptr;
-#pragma unroll
-      for (int s = 0; s < NX; ++s) {
-        float v[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) v[q] = p.alpha * acc[s][t][q];
-        if (crow) {
-          const u32x2 cv = *reinterpret_cast<const u32x2*>(crow + s * 16);
-          v[0] = __builtin_fmaf(p.beta, E::decode((uint16_t)(cv.x & 0xFFFFu)), v[0]);
-          v[1] = __builtin_fmaf(p.beta, E::decode((uint16_t)(cv.x >> 16)), v[1]);
-          v[2] = __builtin_fmaf(p.beta, E::decode((uint16_t)(cv.y & 0xFFFFu)), v[2]);
-          v[3] = __builtin_fmaf(p.beta, E::decode((uint16_t)(cv.y >> 16)), v[3]);
-        }
-        const int c = wn * S::WC + s * 16 + 4 * (lane >> 4);  // column in the tile
-        const int chunk = (c >> 3) ^ (r & 15);
-        *reinterpret_cast<u32x2*>(st + r * pitch + chunk * 4 + ((c >> 2) & 1) * 2) =
-            u32x2{E::pack2(v[0], v[1]), E::pack2(v[2], v[3])};
-      }
-    }
-    __syncthreads();
-    // thread t stores chunk (t % CPR) of rows t / CPR + RPP i
-#pragma unroll 4
-    for (int i = 0; i < BM / S::RPP; ++i) {
-      const int r = i * S::RPP + (int)((unsigned)tid / S::CPR);
-      const int gm = m0 + r;
-      const int q = gm / p.chunk_rows;
-      uint16_t* drow = p.dst[q] + (int64_t)(gm - q * p.chunk_rows) * p.ldd + n0;
-      const int c = (int)((unsigned)tid % S::CPR);
-      const u32x4 v = *reinterpret_cast<const u32x4*>(st + r * pitch + ((c ^ (r & 15)) * 4));
-      __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(drow + c * 8));
-    }
-  } else if (p.vec_out && m0 + BM <= p.m && n0 + TN <= p.n) {
-    // interior tile: every element exists and every access is 8-byte aligned
-#pragma unroll
-    for (int t = 0; t < NY; ++t) {
-      const int gm = row0 + t * 16;
-      const int q = gm / p.chunk_rows;
-      uint16_t* drow = p.dst[q] + (int64_t)(gm - q * p.chunk_rows) * p.ldd + col0;
-      const uint16_t* crow = p.c ? p.c + (int64_t)gm * p.ldc + col0 : nullptr;
-#pragma unroll
-      for (int s = 0; s < NX; ++s) {
-        float v[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = p.alpha * acc[s][t][r];
-        if (crow) {
-          const u32x2 cv = *reinterpret_cast<const u32x2*>(crow + s * 16);
-          v[0] = __builtin_fmaf(p.beta, E::decode((uint16_t)(cv.x & 0xFFFFu)), v[0]);
-          v[1] = __builtin_fmaf(p.beta, E::decode((uint16_t)(cv.x >> 16)), v[1]);
-          v[2] = __builtin_fmaf(p.beta, E::decode((uint16_t)(cv.y & 0xFFFFu)), v[2]);
-          v[3] = __builtin_fmaf(p.beta, E::decode((uint16_t)(cv.y >> 16)), v[3]);
-        }
-        *reinterpret_cast<u32x2*>(drow + s * 16) = u32x2{E::pack2(v[0], v[1]), E::pack2(v[2], v[3])};
-      }
-    }
-  } else {
-    // edge tile (or unaligned rows): element by element, inside m x n only
-#pragma unroll
-    for (int t = 0; t < NY; ++t) {
-      const int gm = row0 + t * 16;
-      const bool row_ok = gm < p.m;
-      const int gmc = row_ok ? gm : 0;
-      const int q = gmc / p.chunk_rows;
-      uint16_t* drow = p.dst[q] + (int64_t)(gmc - q * p.chunk_rows) * p.ldd;
-      const uint16_t* crow = p.c ? p.c + (int64_t)gmc * p.ldc : nullptr;
-#pragma unroll
-      for (int s = 0; s < NX; ++s) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int gn = col0 + s * 16 + r;
-          if (row_ok && gn < p.n) {
-            float v = p.alpha * acc[s][t][r];
-            if (crow) v = __builtin_fmaf(p.beta, E::decode(crow[gn]), v);
-            drow[gn] = E::pack1(v);
-          }
-        }
-      }
-    }
-  }
+  store_tile<DT, TN, S::WR, S::WC, kThreads>(acc, p, tile, m0, n0, wm, wn, tid,
+                                            reinterpret_cast<uint32_t*>(&lds[0].a[0]));
+}
 
-  if (p.flags) {
-    __threadfence_system();
-    __syncthreads();
-    if (tid == 0)
-      __hip_atomic_store(p.flags + tile, p.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+
+// The 256 x 256 tile: four waves, one per SIMD, each a 128 x 128 block of
+// 8 x 8 products whose 256 fp32 accumulators stay in AGPRs.  Operand tiles
+// go straight from memory into LDS (gfx950's 16-byte buffer-load-to-LDS
+// form: no VGPR round trip, no LDS write instructions), k steps of 64 in two
+// 64 KiB buffers.  With one wave per SIMD nothing hides a stall, so each
+// 32-wide half step's 64 products carry, one every four, the 16 LDS reads of
+// the fragments the next half step multiplies, and the first half also the
+// next step's 16 loads: no wave holds the LDS queue or the memory pipe for
+// long, and the products keep issuing.
+constexpr int kWideThreads = 256;
+constexpr int kRowBytes = BK * 2;                 // LDS bytes per operand row (128)
+constexpr int kPartBytes = BM * kRowBytes;        // one operand of one k step: 32 KiB
+constexpr int kStepBytes = 2 * kPartBytes;        // 64 KiB
+static_assert(BN == BM, "the wide tile is square");
+
+template <int DT>
+__global__ __launch_bounds__(kWideThreads) void gemm_wide_kernel(Params p) {
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * kStepBytes];
+  const int tile = tile_at(position_of_wg((int)blockIdx.x, p.sched.tiles), p.sched);
+  const int m0 = (tile / p.sched.tiles_n) * BM;
+  const int n0 = (tile % p.sched.tiles_n) * BN;
+  const int tid = (int)threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;   // wave block: rows wm * 128, columns wn * 128
+  const int nk = (p.k + BK - 1) / BK;
+  const int a_tile_rows = p.m - m0 < BM ? p.m - m0 : BM;
+  const int b_tile_rows = p.n - n0 < BN ? p.n - n0 : BN;
+  // buffer resources end at the last element of the tile's last existing
+  // row; rows past m (n) re-read the last existing row (their outputs are
+  // never stored) and chunks past k take an offset outside every resource,
+  // which reads as zeros
+  const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.a + (int64_t)m0 * p.lda), (short)0,
+      (int)(((int64_t)(a_tile_rows - 1) * p.lda + p.k) * 2), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.b + (int64_t)n0 * p.ldb), (short)0,
+      (int)(((int64_t)(b_tile_rows - 1) * p.ldb + p.k) * 2), kRsrcWord3);
+  // load j (0..7 A, 8..15 B) of this wave moves tile rows 64 wave + 8 (j % 8)
+  // + lane / 8; the 64 lanes fill 1 KiB of LDS in order, so LDS chunk
+  // position lane % 8 of a row holds global chunk (lane % 8) ^ (row % 8)
+  const int lr = lane >> 3, gchunk = (lane & 7) ^ lr;
+  int a_off[8], b_off[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int r = 64 * wave + 8 * j + lr;
+    a_off[j] = ((r < a_tile_rows ? r : a_tile_rows - 1) * (int)p.lda + gchunk * 8) * 2;
+    b_off[j] = ((r < b_tile_rows ? r : b_tile_rows - 1) * (int)p.ldb + gchunk * 8) * 2;
   }
+  auto load1 = [&](int kt, int j) __attribute__((always_inline)) {
+    const bool kin = kt * BK + gchunk * 8 < p.k;
+    unsigned char* base = lds + (kt & 1) * kStepBytes + (64 * wave) * kRowBytes;
+    if (j < 8)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_ptr_t)(base + j * 1024), 16,
+                                               kin ? a_off[j] + kt * BK * 2 : kOutOfRange, 0, 0, 0);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_ptr_t)(base + kPartBytes + (j - 8) * 1024), 16,
+                                               kin ? b_off[j - 8] + kt * BK * 2 : kOutOfRange, 0, 0, 0);
+  };
+  // fragment f (0..15) of half `half` of step kt, in the order the products
+  // use them (x 0, y 0..7, x 1..7): lane l supplies row (l & 15) of a 16-row
+  // block and 16-byte chunk half * 4 + l / 16 of the step
+  auto read1 = [&](int kt, int half, int f, u32x4 (&xf)[8], u32x4 (&yf)[8]) __attribute__((always_inline)) {
+    const unsigned char* b = lds + (kt & 1) * kStepBytes;
+    const int c = half * 4 + (lane >> 4);
+    if (f >= 1 && f <= 8) {
+      const int r = wm * 128 + (f - 1) * 16 + (lane & 15);
+      yf[f - 1] = *reinterpret_cast<const u32x4*>(b + r * kRowBytes + ((c ^ (r & 7)) * 16));
+    } else {
+      const int s = f == 0 ? 0 : f - 8;
+      const int r = wn * 128 + s * 16 + (lane & 15);
+      xf[s] = *reinterpret_cast<const u32x4*>(b + kPartBytes + r * kRowBytes + ((c ^ (r & 7)) * 16));
+    }
+  };
+  f32x4 acc[8][8];
+  // one half step: the 64 products of (xc, yc) (x: B rows, y: A rows, so
+  // each lane's four results are four consecutive output columns), the 16
+  // reads of half `half` of step kt into (xn, yn) and, with LOAD, the 16
+  // loads of step lkt
+  auto half_step = [&](auto first, auto load, const u32x4 (&xc)[8], const u32x4 (&yc)[8],
+                       u32x4 (&xn)[8], u32x4 (&yn)[8], int kt, int half, int lkt)
+                       __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 64; ++i) {
+      mma_agpr<DT, decltype(first)::value>(acc[i / 8][i % 8], xc[i / 8], yc[i % 8]);
+      if (i % 4 == 0) read1(kt, half, i / 4, xn, yn);
+      if (decltype(load)::value && i % 4 == 2) load1(lkt, i / 4);
+    }
+  };
+  using Yes = std::true_type;
+  using No = std::false_type;
+  u32x4 xa[8], ya[8], xb[8], yb[8];
+  if (nk > 0) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) load1(0, j);
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+    __builtin_amdgcn_s_barrier();
+#pragma unroll
+    for (int f = 0; f < 16; ++f) read1(0, 0, f, xa, ya);
+    // step 0: its first half's products (from zero) carry the second half's
+    // reads and step 1's loads
+    half_step(Yes{}, Yes{}, xa, ya, xb, yb, 0, 1, 1);
+    for (int kt = 1; kt < nk; ++kt) {
+      // step kt has landed for every wave, and every wave is done reading
+      // step kt - 1, whose buffer step kt + 1 loads into (past k: zeros)
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+      __builtin_amdgcn_s_barrier();
+      half_step(No{}, Yes{}, xb, yb, xa, ya, kt, 0, kt + 1);   // step kt - 1, second half
+      half_step(No{}, No{}, xa, ya, xb, yb, kt, 1, 0);         // step kt, first half
+    }
+#pragma unroll
+    for (int i = 0; i < 64; ++i) mma_agpr<DT, false>(acc[i / 8][i % 8], xb[i / 8], yb[i % 8]);
+    settle_agprs(acc);
+  } else {
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+#pragma unroll
+      for (int t = 0; t < 8; ++t) acc[s][t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+  // the last loads (zeros past k) may still be landing in the LDS the
+  // results are staged in
+  __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+  __builtin_amdgcn_s_barrier();
+  store_tile<DT, BN, 128, 128, kWideThreads>(acc, p, tile, m0, n0, wm, wn, tid,
+                                             reinterpret_cast<uint32_t*>(lds));
 }
 
 }  // namespace gsc
@@ -516,15 +616,20 @@ extern "C" int gemm_scatter_fwd(void* const* dst, int64_t ldd, int world, int ra
   p.sched = gsc::make_sched((int)m, (int)n, tn, world, rank);
 
   hipStream_t st = (hipStream_t)stream;
-  const dim3 grid((unsigned)tiles), block(gsc::kThreads);
-  if (dtype == RMSN_BF16 && tn == gsc::BN)
-    hipLaunchKernelGGL((gsc::gemm_scatter_kernel<RMSN_BF16, gsc::BN>), grid, block, 0, st, p);
-  else if (dtype == RMSN_BF16)
-    hipLaunchKernelGGL((gsc::gemm_scatter_kernel<RMSN_BF16, gsc::BN_NARROW>), grid, block, 0, st, p);
-  else if (tn == gsc::BN)
-    hipLaunchKernelGGL((gsc::gemm_scatter_kernel<RMSN_F16, gsc::BN>), grid, block, 0, st, p);
-  else
-    hipLaunchKernelGGL((gsc::gemm_scatter_kernel<RMSN_F16, gsc::BN_NARROW>), grid, block, 0, st, p);
+  const dim3 grid((unsigned)tiles);
+  if (tn == gsc::BN) {
+    const dim3 block(gsc::kWideThreads);
+    if (dtype == RMSN_BF16)
+      hipLaunchKernelGGL((gsc::gemm_wide_kernel<RMSN_BF16>), grid, block, 0, st, p);
+    else
+      hipLaunchKernelGGL((gsc::gemm_wide_kernel<RMSN_F16>), grid, block, 0, st, p);
+  } else {
+    const dim3 block(gsc::kThreads);
+    if (dtype == RMSN_BF16)
+      hipLaunchKernelGGL((gsc::gemm_narrow_kernel<RMSN_BF16>), grid, block, 0, st, p);
+    else
+      hipLaunchKernelGGL((gsc::gemm_narrow_kernel<RMSN_F16>), grid, block, 0, st, p);
+  }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
     char msg[200];

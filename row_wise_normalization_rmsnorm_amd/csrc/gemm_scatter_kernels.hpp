@@ -153,4 +153,58 @@ struct Params {
   Sched sched;
 };
 
+// ---- matrix-core products with the accumulators in AGPRs --------------------
+
+// One 16 x 16 x 32 product, acc (AGPRs) += x . y, through inline assembly so
+// that the 256 accumulators of a 128 x 128 wave block stay pinned in the
+// AGPRs.  FIRST: the accumulator starts from zero (so nothing else writes
+// the AGPRs before a tile's first product).
+template <int DT, bool FIRST>
+__device__ __forceinline__ void mma_agpr(f32x4& acc, const u32x4& x, const u32x4& y) {
+  if constexpr (FIRST) {
+    if constexpr (DT == RMSN_BF16)
+      asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=a"(acc) : "v"(x), "v"(y));
+    else
+      asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, 0" : "=a"(acc) : "v"(x), "v"(y));
+  } else {
+    if constexpr (DT == RMSN_BF16)
+      asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(x), "v"(y));
+    else
+      asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(x), "v"(y));
+  }
+}
+
+// The last products' results must be written before the AGPRs are read:
+// the hardware leaves those wait states to software, and inline assembly
+// hides the products from the compiler's hazard tracking.  24 wait states
+// cover the longest (16-pass) product; the empty statements keep every
+// accumulator behind the wait.
+__device__ __forceinline__ void settle_agprs(f32x4 (&acc)[8][8]) {
+#define GSC_PIN(I) "+a"(acc[I / 8][I % 8])
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+               : GSC_PIN(0), GSC_PIN(1), GSC_PIN(2), GSC_PIN(3), GSC_PIN(4), GSC_PIN(5), GSC_PIN(6),
+                 GSC_PIN(7), GSC_PIN(8), GSC_PIN(9), GSC_PIN(10), GSC_PIN(11), GSC_PIN(12), GSC_PIN(13),
+                 GSC_PIN(14), GSC_PIN(15));
+  asm volatile(""
+               : GSC_PIN(16), GSC_PIN(17), GSC_PIN(18), GSC_PIN(19), GSC_PIN(20), GSC_PIN(21), GSC_PIN(22),
+                 GSC_PIN(23), GSC_PIN(24), GSC_PIN(25), GSC_PIN(26), GSC_PIN(27), GSC_PIN(28), GSC_PIN(29),
+                 GSC_PIN(30), GSC_PIN(31));
+  asm volatile(""
+               : GSC_PIN(32), GSC_PIN(33), GSC_PIN(34), GSC_PIN(35), GSC_PIN(36), GSC_PIN(37), GSC_PIN(38),
+                 GSC_PIN(39), GSC_PIN(40), GSC_PIN(41), GSC_PIN(42), GSC_PIN(43), GSC_PIN(44), GSC_PIN(45),
+                 GSC_PIN(46), GSC_PIN(47));
+  asm volatile(""
+               : GSC_PIN(48), GSC_PIN(49), GSC_PIN(50), GSC_PIN(51), GSC_PIN(52), GSC_PIN(53), GSC_PIN(54),
+                 GSC_PIN(55), GSC_PIN(56), GSC_PIN(57), GSC_PIN(58), GSC_PIN(59), GSC_PIN(60), GSC_PIN(61),
+                 GSC_PIN(62), GSC_PIN(63));
+#undef GSC_PIN
+}
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
+// 6:4, lgkmcnt 11:8), handed to the compiler's own wait tracking
+constexpr int wait_vmcnt(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+constexpr int kWaitLgkm0 = 0xC07F;
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
 }  // namespace gsc

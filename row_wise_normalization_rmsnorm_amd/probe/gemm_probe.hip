@@ -38,53 +38,15 @@ namespace {
 using namespace gsc;
 
 constexpr int kThreads4 = 256;           // four waves, one per SIMD
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
-// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
-// 6:4, lgkmcnt 11:8) handed to the compiler's own wait tracking
-constexpr int wait_vm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
-constexpr int kWaitLgkm0 = 0xC07F;
-constexpr int kWaitVm0 = wait_vm(0);
-
-// One 16 x 16 x 32 product with the accumulator in AGPRs.  FIRST: it starts
-// from zero, so nothing else writes the AGPRs before the first product.
-template <int DT, bool FIRST>
-__device__ __forceinline__ void mma(f32x4& acc, const u32x4& x, const u32x4& y) {
-  if constexpr (FIRST) {
-    if constexpr (DT == RMSN_BF16)
-      asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=a"(acc) : "v"(x), "v"(y));
-    else
-      asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, 0" : "=a"(acc) : "v"(x), "v"(y));
-  } else {
-    if constexpr (DT == RMSN_BF16)
-      asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(x), "v"(y));
-    else
-      asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(x), "v"(y));
-  }
-}
-
+constexpr int kWaitVm0 = wait_vmcnt(0);
 using Acc = f32x4[8][8];
 
-// The products' results must be written before the AGPRs are read: the
-// hardware leaves those wait states to software, and inline assembly hides
-// the products from the compiler's hazard tracking.  The empty statements
-// keep every accumulator behind the wait.
-__device__ __forceinline__ void settle(Acc& acc) {
-#define GP_PIN(I) "+a"(acc[I / 8][I % 8])
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
-               : GP_PIN(0), GP_PIN(1), GP_PIN(2), GP_PIN(3), GP_PIN(4), GP_PIN(5), GP_PIN(6), GP_PIN(7),
-                 GP_PIN(8), GP_PIN(9), GP_PIN(10), GP_PIN(11), GP_PIN(12), GP_PIN(13), GP_PIN(14), GP_PIN(15));
-  asm volatile(""
-               : GP_PIN(16), GP_PIN(17), GP_PIN(18), GP_PIN(19), GP_PIN(20), GP_PIN(21), GP_PIN(22), GP_PIN(23),
-                 GP_PIN(24), GP_PIN(25), GP_PIN(26), GP_PIN(27), GP_PIN(28), GP_PIN(29), GP_PIN(30), GP_PIN(31));
-  asm volatile(""
-               : GP_PIN(32), GP_PIN(33), GP_PIN(34), GP_PIN(35), GP_PIN(36), GP_PIN(37), GP_PIN(38), GP_PIN(39),
-                 GP_PIN(40), GP_PIN(41), GP_PIN(42), GP_PIN(43), GP_PIN(44), GP_PIN(45), GP_PIN(46), GP_PIN(47));
-  asm volatile(""
-               : GP_PIN(48), GP_PIN(49), GP_PIN(50), GP_PIN(51), GP_PIN(52), GP_PIN(53), GP_PIN(54), GP_PIN(55),
-                 GP_PIN(56), GP_PIN(57), GP_PIN(58), GP_PIN(59), GP_PIN(60), GP_PIN(61), GP_PIN(62), GP_PIN(63));
-#undef GP_PIN
+template <int DT, bool FIRST>
+__device__ __forceinline__ void mma(f32x4& acc, const u32x4& x, const u32x4& y) {
+  mma_agpr<DT, FIRST>(acc, x, y);
 }
+__device__ __forceinline__ void settle(Acc& acc) { settle_agprs(acc); }
+constexpr int wait_vm(int n) { return wait_vmcnt(n); }
 
 // A buffer resource over a tile's operand rows, ending at the last element
 // of its last existing row (loads past it read zeros).

@@ -36,15 +36,17 @@ COPY_BYTES = 1 << 30
 
 
 def kernel_sources(op: str) -> list:
-    """The source that fixes a workload's kernel code: the block sum's or the
-    GEMM's own file, or the RMSNorm kernels' template header.  Which variant runs is
+    """The sources that fix a workload's kernel code: the block sum's file,
+    the GEMM's file and its shared header, or the RMSNorm kernels' template
+    header.  Which variant runs is
     checked by its name instead, which spells out every template parameter,
     so adding other variants or changing the host dispatcher leaves a
     measured figure valid."""
     pkg = os.path.join(ROOT, "row_wise_normalization_rmsnorm_amd")
-    src = {"block_sum": "block_sum.hip", "gemm_scatter": "gemm_scatter.hip"}.get(
-        op, "rmsnorm_kernels.hpp")
-    return [os.path.join(pkg, "csrc", src)]
+    src = {"block_sum": ["block_sum.hip"],
+           "gemm_scatter": ["gemm_scatter.hip", "gemm_scatter_kernels.hpp"]}.get(
+        op, ["rmsnorm_kernels.hpp"])
+    return [os.path.join(pkg, "csrc", f) for f in src]
 
 
 def source_hash(op: str) -> str:
