@@ -307,42 +307,69 @@ __global__ __launch_bounds__(kThreads) void gemm_narrow_kernel(Params p) {
     a_off[i] = i < a_rows ? a_off0 + i * a_row_step : a_off_last;
     if (i < NB) b_off[i] = i < b_rows ? b_off0 + i * b_row_step : b_off_last;
   }
-  auto gload_early = [&](int kt) {
-    const bool kin = kt * BK + lchunk * 8 < p.k;
+  // Steps whose every chunk lies inside k load with plain global loads
+  // (measured 3-5% faster than buffer loads at 1024, 2560 and 3072 tokens);
+  // the partial last step takes the buffer form, whose range check reads
+  // zeros past k.  Rows past m (n) re-read the last existing row.
+  const int nk_full = p.k / BK;
+  const unsigned char* a_tile = reinterpret_cast<const unsigned char*>(p.a + (int64_t)m0 * p.lda);
+  const unsigned char* b_tile = reinterpret_cast<const unsigned char*>(p.b + (int64_t)n0 * p.ldb);
+  auto gload_early = [&](auto global, int kt) __attribute__((always_inline)) {
     const int kb = kt * BK * 2;
+    if constexpr (decltype(global)::value) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      ra[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                            rsa, kin ? a_off[i] + kb : kOutOfRange, 0, 0));
-      if (i < NB)
-        rb[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                              rsb, kin ? b_off[i] + kb : kOutOfRange, 0, 0));
+      for (int i = 0; i < 4; ++i) {
+        ra[i] = *reinterpret_cast<const u32x4*>(a_tile + a_off[i] + kb);
+        if (i < NB) rb[i] = *reinterpret_cast<const u32x4*>(b_tile + b_off[i] + kb);
+      }
+    } else {
+      const bool kin = kt * BK + lchunk * 8 < p.k;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        ra[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                              rsa, kin ? a_off[i] + kb : kOutOfRange, 0, 0));
+        if (i < NB)
+          rb[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                rsb, kin ? b_off[i] + kb : kOutOfRange, 0, 0));
+      }
     }
   };
+  auto gload_step = [&](int kt) __attribute__((always_inline)) {
+    if (kt < nk_full)
+      gload_early(std::true_type{}, kt);
+    else
+      gload_early(std::false_type{}, kt);
+  };
   if (nk > 0) {
-    gload_early(0);
+    gload_step(0);
     lstore(0);
-    gload_early(nk > 1 ? 1 : 0);
+    gload_step(nk > 1 ? 1 : 0);
   }
   __syncthreads();
   u32x4 xf[NX], yf[NY];
-  for (int kt = 0; kt < nk; ++kt) {
+  // step kt multiplies while step min(kt + 2, nk - 1) loads; two loops
+  // rather than a branch per step, which would split the registers'
+  // assignment between two copies of the step
+  auto step = [&](auto global, int kt) __attribute__((always_inline)) {
     const int cur = kt & 1;
     read_frags(cur, 0, xf, yf);
     mfmas(xf, yf);
     read_frags(cur, 1, xf, yf);
     lstore(cur ^ 1);
-    gload_early(kt + 2 < nk ? kt + 2 : nk - 1);
+    gload_early(global, kt + 2 < nk ? kt + 2 : nk - 1);
     mfmas(xf, yf);
 #pragma unroll
     for (int i = 0; i < S::NLOAD; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);       // one LDS write
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);       // one global (buffer) load
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);       // one global load
       __builtin_amdgcn_sched_group_barrier(0x008, S::PER, 0);  // products
     }
     if constexpr (S::REST > 0) __builtin_amdgcn_sched_group_barrier(0x008, S::REST, 0);
     __syncthreads();
-  }
+  };
+  int kt = 0;
+  for (; kt + 2 < nk_full; ++kt) step(std::true_type{}, kt);
+  for (; kt < nk; ++kt) step(std::false_type{}, kt);
 
   store_tile<DT, TN, S::WR, S::WC, kThreads>(acc, p, tile, m0, n0, wm, wn, tid,
                                             reinterpret_cast<uint32_t*>(&lds[0].a[0]));
