@@ -493,7 +493,7 @@ def gemm_shapes_summary(argv) -> int:
                 "operands rotated over about 1 GiB; the library column is torch.matmul, i.e. "
                 "hipBLASLt's plain GEMM, on the same operands).  Output tiles of 256 rows by "
                 "256 or 128 columns, one workgroup each on 256 CUs; the automatic width counts "
-                "whole rounds of workgroups, a round of 128-wide tiles costing about 0.55 of a "
+                "whole rounds of workgroups, a round of 128-wide tiles costing about 0.63 of a "
                 "round of 256-wide ones (include/gemm_scatter.h).\n\n")
         f.write("| m | n | k | chunks | automatic width | tiles | kernel µs | TFLOP/s | "
                 "% of 2.5 PFLOP/s | 256-wide µs | 128-wide µs | hipBLASLt µs | "
