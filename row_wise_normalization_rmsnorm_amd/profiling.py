@@ -321,7 +321,7 @@ def report_summary(argv) -> int:
     a = ap.parse_args(argv)
     stats = {}
     for line in open(a.tests_log, errors="replace"):
-        m = re.search(r"\[gpu\] (\w+): (\{.*\})\s*$", line)
+        m = re.search(r"\[gpu\] (\w+): (?:whole tensor )?(\{.*\})\s*$", line)
         if m:
             try:
                 stats[m.group(1)] = ast.literal_eval(m.group(2))
@@ -343,8 +343,8 @@ def report_summary(argv) -> int:
                 "step timed with HIP events; the oracle timed on the host's cores, and on one), and "
                 "`python -m pytest tests/test_gpu_parity.py tests/test_gpu_allgather.py tests/test_gpu_block_sum.py "
                 "tests/test_gpu_gemm_scatter.py -m gpu -s -k \"workloads or full_size\"` for the "
-                "parity statistics (all rows of the 512-row workloads; 128+ "
-                "sampled rows of the full-size launches, whose residual is also checked whole).\n\n")
+                "parity statistics (every row of every RMSNorm workload against the oracle, the "
+                "full-size ones in row blocks; the elements checked are counted in the column).\n\n")
         f.write("| workload | GPU µs/step | GPU GB/s | % of 8 TB/s | GPU rows/s | oracle GB/s "
                 "(cores) | oracle rows/s | oracle GB/s, 1 core | GPU ÷ oracle | parity |\n"
                 "|---|---|---|---|---|---|---|---|---|---|\n")
@@ -354,7 +354,8 @@ def report_summary(argv) -> int:
             st = stats.get(w, {})
             if "max_ulp" in st:
                 par = (f"max {st['max_ulp']} ulp, rel {st.get('max_rel_err', 0):.2g}"
-                       + (", residual bit-exact" if st.get("residual_bit_exact") else ""))
+                       + (", residual bit-exact" if st.get("residual_bit_exact") else "")
+                       + (f" ({st['elements_checked']:,} elements)" if "elements_checked" in st else ""))
             elif "max_rel_err" in st:
                 par = (f"max rel {st['max_rel_err']:.2g}"
                        + (", residual bit-exact" if st.get("residual_bit_exact") else ""))
