@@ -10,29 +10,26 @@
 // chunk (section "gemmrs版本的swizzle如何编排").
 //
 // MI355X design:
-//   - 256 x 256 output tile per workgroup of eight waves, two per SIMD; each
-//     wave a 128 x 64 block of 8 x 4 v_mfma_f32_16x16x32 products (fp32
-//     accumulate, 128 accumulator registers) over k steps of 64.  With two
-//     waves per SIMD one wave's products run while the other waits on LDS,
-//     memory or the barrier (measured 188.7 us against 204.6 us for four
-//     waves of 128 x 128 blocks on the 4096 x 8192 x 3584 bf16 product, one
-//     set of operands).
-//   - 256 x 128 tiles, twice the workgroups with each wave a 64 x 64 block
-//     of 4 x 4 products, for products whose 256 x 256 tiles would leave much
-//     of the last round of workgroups idle (1024 tokens: 128 tiles on 256
-//     CUs).  Both widths accumulate every output in the same k order, so
-//     they give bitwise equal results.
+//   - 256 x 256 output tiles (gemm_wide_kernel): four waves, one per SIMD,
+//     each a 128 x 128 block of 8 x 8 v_mfma_f32_16x16x32 products whose 256
+//     fp32 accumulators stay in AGPRs (inline-assembly products tied to
+//     them).  Operand tiles go straight from memory into LDS with gfx950's
+//     16-byte load-to-LDS forms, k steps of 64 in two 64 KiB buffers; each
+//     32-wide half step's products carry, one every four, the LDS reads of
+//     the next half's fragments and the next step's loads.  Measured on the
+//     4096 x 8192 x 3584 bf16 product against the eight-wave kernel it
+//     replaced (two waves per SIMD, 128 x 64 blocks, loads staged through
+//     registers): 194.4 against 209.1 us in the same process; the
+//     alternatives are in probe/gemm_probe.hip (bench.py --gemm-design-sweep).
+//   - 256 x 128 tiles (gemm_narrow_kernel) for products whose 256 x 256
+//     tiles would leave much of the last round of workgroups idle (1024
+//     tokens: 128 tiles on 256 CUs): eight waves, two per SIMD, each a
+//     64 x 64 block of 4 x 4 products, loads through registers a whole k
+//     step ahead.  Both widths accumulate every output in the same k order,
+//     so they give bitwise equal results.
 //   - The matrix-core operands are swapped (the weight rows feed the first
 //     operand, the activation rows the second), so each lane's four
 //     accumulator values are four consecutive output columns of one row.
-//   - A and B tiles pass through LDS, double-buffered (2 x 64 KiB of the
-//     CU's 160 KiB): each thread loads 16-byte chunks of the next k step
-//     into registers while the waves multiply the current one, then writes
-//     them to the other buffer; one barrier per k step.  The loads are
-//     spread between the first half's products and the LDS writes between
-//     the second half's.  (Loading straight into LDS with gfx950's
-//     buffer-load-to-LDS form, and deeper pipelines, measured no better with
-//     four waves.)
 //   - LDS rows are 128 bytes (64 elements); the 16-byte chunk c of row r is
 //     stored at chunk position c ^ (r & 7), so the eight lanes of each LDS
 //     access phase, which read the same chunk of eight consecutive rows, hit
@@ -50,9 +47,6 @@
 //     the output (64 MiB for the 4096 x 8192 product) then does not push the
 //     operand rows out of the XCDs' L2 (measured 2-4% faster at 1024, 4096
 //     and 8192 tokens, 8192 x 3584 weights).
-//   - Designs with four waves of 128 x 128 blocks (one per SIMD) fed by
-//     gfx950's buffer-load-to-LDS form were measured beside this one with
-//     probe/gemm_probe.hip; none was faster (bench.py --gemm-design-sweep).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdio.h>
@@ -182,10 +176,10 @@ __device__ __forceinline__ void store_tile(const AccT& acc, const Params& p, int
   }
 }
 
-// Tile shape of one workgroup: 256 rows by TN columns (256 or 128).  The
-// eight waves cover it as WAVES_M x WAVES_N blocks of WR x WC outputs, each
-// NY x NX products of 16 x 16; each thread loads NB 16-byte chunks of B rows
-// per k step (and four of A rows).
+// Tile shape of an eight-wave workgroup: 256 rows by TN columns (the
+// narrow kernel's 128).  The waves cover it as WAVES_M x WAVES_N blocks of
+// WR x WC outputs, each NY x NX products of 16 x 16; each thread loads NB
+// 16-byte chunks of B rows per k step (and four of A rows).
 template <int TN>
 struct Shape {
   static constexpr int WAVES_N = TN == 256 ? 4 : 2;
