@@ -159,6 +159,29 @@ def test_parity(dtype, shape):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_k_around_whole_steps(dtype):
+    """k around multiples of the 64-wide k step.  Both kernels load the k
+    steps that lie wholly inside k with global loads and the last, partial
+    step (and the steps past the end, which must read as zeros) with
+    range-checked buffer loads, in two loops; the boundary moves with k.
+    Ragged and whole tiles, both widths against the oracle and bitwise
+    equal to each other."""
+    for m, n, world in ((264, 520, 2), (512, 512, 4)):
+        for k in (8, 56, 64, 72, 120, 128, 136, 184, 192, 200, 320):
+            a, b, c = make(dtype, m, n, k, False, seed=k + m)
+            want, y, mag = oracle_rows(a, b, c, 1.0, 0.0, world, dtype)
+            first = None
+            for tile_n in WIDTHS:
+                say(f"[gpu] k steps {dtype} m={m} n={n} k={k} tile_n={tile_n}")
+                got, _ = run(a, b, c, 1.0, 0.0, world, ldd_pad=(-(n + 16)) % 8, col=8,
+                             tile_n=tile_n)
+                compare(got, want, y, mag, k, dtype, f"{dtype} {m}x{n}x{k} tile_n {tile_n}")
+                if first is None:
+                    first = got
+                assert np.array_equal(got, first), f"tile widths differ at k = {k}"
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
 def test_strided_operands(dtype):
     """Row strides wider than the rows for A, B, C and the output (one odd,
     which takes the element-wise store path)."""
