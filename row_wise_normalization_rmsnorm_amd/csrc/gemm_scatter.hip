@@ -475,6 +475,8 @@ __global__ __launch_bounds__(kWideThreads) void gemm_wide_kernel(Params p) {
   using No = std::false_type;
   u32x4 xa[8], ya[8], xb[8], yb[8];
   if (nk > 0) {
+    // steps 0 and 1 load at once, so that step 1 has all of step 0 to land
+    // before the loop's first barrier waits for it
     if (nk_full > 0) {
 #pragma unroll
       for (int j = 0; j < 16; ++j) load1(Yes{}, 0, j);
@@ -482,16 +484,20 @@ __global__ __launch_bounds__(kWideThreads) void gemm_wide_kernel(Params p) {
 #pragma unroll
       for (int j = 0; j < 16; ++j) load1(No{}, 0, j);
     }
-    __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+    if (nk_full > 1) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) load1(Yes{}, 1, j);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) load1(No{}, 1, j);
+    }
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt(16));   // step 0 landed (loads complete in order)
     __builtin_amdgcn_s_barrier();
 #pragma unroll
     for (int f = 0; f < 16; ++f) read1(0, 0, f, xa, ya);
     // step 0: its first half's products (from zero) carry the second half's
-    // reads and step 1's loads
-    if (nk_full > 1)
-      half_step(Yes{}, Yes{}, Yes{}, xa, ya, xb, yb, 0, 1, 1);
-    else
-      half_step(Yes{}, Yes{}, No{}, xa, ya, xb, yb, 0, 1, 1);
+    // reads
+    half_step(Yes{}, No{}, No{}, xa, ya, xb, yb, 0, 1, 0);
     auto step = [&](auto global, int kt) __attribute__((always_inline)) {
       // step kt has landed for every wave, and every wave is done reading
       // step kt - 1, whose buffer step kt + 1 loads into (past k: zeros)
