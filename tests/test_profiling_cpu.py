@@ -138,6 +138,43 @@ def test_gemm_design_summary(tmp_path, monkeypatch):
     assert "| design 2 | m | 130.0 | 235.0 | 105.0 | 25.0 |" in md
 
 
+def test_report_reads_whole_tensor_statistics(tmp_path, monkeypatch):
+    """The per-workload report takes each workload's parity statistics from
+    the GPU tests' log, including the whole-tensor lines of the full-size
+    workloads, and leaves "see tests" where the log has none."""
+    monkeypatch.setattr(prof, "PROFILES", str(tmp_path / "profiles"))
+    os.makedirs(tmp_path / "profiles")
+    log = tmp_path / "tests.log"
+    log.write_text(
+        "[gpu] add_rmsnorm_bf16_8192x4096_k1: every row against the oracle\n"
+        "[gpu] add_rmsnorm_bf16_8192x4096_k1: whole tensor {'rows_checked': 8192, "
+        "'elements_checked': 33554432, 'residual_bit_exact': True, 'max_ulp': 1, "
+        "'max_rel_err': 0.0039}\n"
+        "[gpu] rmsnorm_f32_512x2048: {'max_rel_err': 2.2e-07}\n"
+        "[gpu] block_sum_f32_1024x1024: error / bound = 1.5e-05\n")
+
+    def line(name, op="add_rmsnorm"):
+        return json.dumps({"config": {"workload": name, "op": op}, "ms_per_step": 0.05,
+                           "value": 6000.0, "pct_of_peak": 75.0, "rows_per_s": 1.8e8,
+                           "cpu_baseline": {"value": 2.0, "cores": 16, "rows_per_s": 6e4,
+                                            "single_thread": {"value": 0.15}}})
+    paths = []
+    for i, (name, op) in enumerate((("add_rmsnorm_bf16_8192x4096_k1", "add_rmsnorm"),
+                                    ("rmsnorm_f32_512x2048", "rmsnorm"),
+                                    ("block_sum_f32_1024x1024", "block_sum"),
+                                    ("add_rmsnorm_bf16_4096x8192_k8", "add_rmsnorm"))):
+        f = tmp_path / f"b{i}.json"
+        f.write_text(line(name, op) + "\n")
+        paths.append(str(f))
+    assert prof.report_summary(["--tests-log", str(log)] + paths) == 0
+    md = open(tmp_path / "profiles" / "per_config_report.md").read()
+    assert ("| add_rmsnorm_bf16_8192x4096_k1 |" in md and
+            "max 1 ulp, rel 0.0039, residual bit-exact (33,554,432 elements) |" in md)
+    assert "| max rel 2.2e-07 |" in md
+    assert "| error / bound 1.5e-05 |" in md
+    assert md.count("| see tests |") == 1
+
+
 def test_bench_refuses_more_than_one_gpu():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)
