@@ -14,13 +14,15 @@
 //     each a 128 x 128 block of 8 x 8 v_mfma_f32_16x16x32 products whose 256
 //     fp32 accumulators stay in AGPRs (inline-assembly products tied to
 //     them).  Operand tiles go straight from memory into LDS with gfx950's
-//     16-byte load-to-LDS forms, k steps of 64 in two 64 KiB buffers; each
+//     16-byte load-to-LDS forms, k steps of 64 in a ring of five 32 KiB
+//     operand slots, so every load has one and a half steps to land; each
 //     32-wide half step's products carry, one every four, the LDS reads of
-//     the next half's fragments and the next step's loads.  Measured on the
-//     4096 x 8192 x 3584 bf16 product against the eight-wave kernel it
-//     replaced (two waves per SIMD, 128 x 64 blocks, loads staged through
-//     registers): 194.4 against 209.1 us in the same process; the
-//     alternatives are in probe/gemm_probe.hip (bench.py --gemm-design-sweep).
+//     the next half's fragments and, one every eight, a load.  Measured on
+//     the 4096 x 8192 x 3584 bf16 product in one process: 179.0 us, against
+//     190.8 with two 64 KiB step buffers (loads one step ahead) and 209.1
+//     for the earlier eight-wave kernel (two waves per SIMD, 128 x 64
+//     blocks, loads staged through registers); the alternatives are in
+//     probe/gemm_probe.hip (bench.py --gemm-design-sweep).
 //   - 256 x 128 tiles (gemm_narrow_kernel) for products whose 256 x 256
 //     tiles would leave much of the last round of workgroups idle (1024
 //     tokens: 128 tiles on 256 CUs): eight waves, two per SIMD, each a
@@ -372,26 +374,39 @@ __global__ __launch_bounds__(kThreads) void gemm_narrow_kernel(Params p) {
 
 // The 256 x 256 tile: four waves, one per SIMD, each a 128 x 128 block of
 // 8 x 8 products whose 256 fp32 accumulators stay in AGPRs.  Operand tiles
-// go straight from memory into LDS (gfx950's 16-byte load-to-LDS forms: no
-// VGPR round trip, no LDS write instructions), k steps of 64 in two 64 KiB
-// buffers.  With one wave per SIMD nothing hides a stall, so each
-// 32-wide half step's 64 products carry, one every four, the 16 LDS reads of
-// the fragments the next half step multiplies, and the first half also the
-// next step's 16 loads: no wave holds the LDS queue or the memory pipe for
-// long, and the products keep issuing.
+// go straight from memory into LDS (gfx950's 16-byte load-to-LDS buffer
+// form: no VGPR round trip, no LDS write instructions), k steps of 64.  The
+// LDS is a ring of five 32 KiB slots, one operand of one step each: A of
+// step t is part 2t and B part 2t + 1, in slot part % 5.  While step kt is
+// read, A of step kt + 1 has landed or is landing, and step kt issues B of
+// step kt + 1 and A of step kt + 2 into the two slots step kt - 1 freed:
+// every load has at least one and a half steps to land, against one with
+// two 64 KiB step buffers.  With one wave per SIMD nothing hides a stall,
+// so each 32-wide half step's 64 products carry, one every four, the 16 LDS
+// reads of the fragments the next half step multiplies, and one every eight
+// a load (B of the next step in the first half, A of the step after in the
+// second), in that order (a scheduling barrier after each product keeps the
+// compiler from bunching them): no wave holds the LDS queue or the memory
+// pipe for long, and the products keep issuing.  The loop carries almost no
+// address arithmetic: the slot is a scalar, each lane's four LDS read bases
+// are fixed for the kernel (fragments sit at immediate offsets), and a load
+// of a whole step takes its lane's row offset, fixed too, plus the step's
+// byte offset in a scalar register.
 constexpr int kWideThreads = 256;
 constexpr int kRowBytes = BK * 2;                 // LDS bytes per operand row (128)
 constexpr int kPartBytes = BM * kRowBytes;        // one operand of one k step: 32 KiB
-constexpr int kStepBytes = 2 * kPartBytes;        // 64 KiB
+constexpr int kSlots = 5;                         // 160 KiB, the whole LDS
 static_assert(BN == BM, "the wide tile is square");
+static_assert(kSlots * kPartBytes <= 160 * 1024, "gfx950 LDS per workgroup");
 
 template <int DT>
 __global__ __launch_bounds__(kWideThreads) void gemm_wide_kernel(Params p) {
-  __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * kStepBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[kSlots * kPartBytes];
   const int tile = tile_at(position_of_wg((int)blockIdx.x, p.sched.tiles), p.sched);
   const int m0 = (tile / p.sched.tiles_n) * BM;
   const int n0 = (tile % p.sched.tiles_n) * BN;
-  const int tid = (int)threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = (int)threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;   // wave block: rows wm * 128, columns wn * 128
   const int nk = (p.k + BK - 1) / BK;
   const int a_tile_rows = p.m - m0 < BM ? p.m - m0 : BM;
@@ -406,9 +421,9 @@ __global__ __launch_bounds__(kWideThreads) void gemm_wide_kernel(Params p) {
   const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(p.b + (int64_t)n0 * p.ldb), (short)0,
       (int)(((int64_t)(b_tile_rows - 1) * p.ldb + p.k) * 2), kRsrcWord3);
-  // load j (0..7 A, 8..15 B) of this wave moves tile rows 64 wave + 8 (j % 8)
-  // + lane / 8; the 64 lanes fill 1 KiB of LDS in order, so LDS chunk
-  // position lane % 8 of a row holds global chunk (lane % 8) ^ (row % 8)
+  // load j (0..7) of a part moves this wave's tile rows 64 wave + 8 j +
+  // lane / 8; the 64 lanes fill 1 KiB of LDS in order, so LDS chunk position
+  // lane % 8 of a row holds global chunk (lane % 8) ^ (row % 8)
   const int lr = lane >> 3, gchunk = (lane & 7) ^ lr;
   int a_off[8], b_off[8];
 #pragma unroll
@@ -417,101 +432,113 @@ __global__ __launch_bounds__(kWideThreads) void gemm_wide_kernel(Params p) {
     a_off[j] = ((r < a_tile_rows ? r : a_tile_rows - 1) * (int)p.lda + gchunk * 8) * 2;
     b_off[j] = ((r < b_tile_rows ? r : b_tile_rows - 1) * (int)p.ldb + gchunk * 8) * 2;
   }
-  // Steps whose every chunk lies inside k load with the global form
-  // (measured 196.0 against 203.0 us for the buffer form on the 4096 x 8192
-  // x 3584 bf16 product, same results); the last, partial step and the steps
-  // past it take the buffer form, whose range check reads zeros past k.
+  // Steps whose every chunk lies inside k pass the step's byte offset as
+  // the scalar offset, so the loop adds nothing per lane (measured 170.2
+  // against 173.2 us for 64-bit global addresses, bf16 4096 x 8192 x 3584).
+  // The last, partial step and the steps past it put each chunk past k at
+  // an offset outside the resource, which reads as zeros.
   const int nk_full = p.k / BK;
-  const unsigned char* a_tile = reinterpret_cast<const unsigned char*>(p.a + (int64_t)m0 * p.lda);
-  const unsigned char* b_tile = reinterpret_cast<const unsigned char*>(p.b + (int64_t)n0 * p.ldb);
-  auto load1 = [&](auto global, int kt, int j) __attribute__((always_inline)) {
-    unsigned char* base = lds + (kt & 1) * kStepBytes + (64 * wave) * kRowBytes;
-    unsigned char* dst = base + (j < 8 ? 0 : kPartBytes) + (j & 7) * 1024;
-    if constexpr (decltype(global)::value) {
-      const unsigned char* src = (j < 8 ? a_tile + a_off[j] : b_tile + b_off[j & 7]) + kt * BK * 2;
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src, (lds_ptr_t)dst,
-                                       16, 0, 0);
+  auto load1 = [&](auto whole, int q, int slot, int j) __attribute__((always_inline)) {
+    const int kt = q >> 1;
+    unsigned char* dst = lds + slot * kPartBytes + (64 * wave) * kRowBytes + j * 1024;
+    if constexpr (decltype(whole)::value) {
+      if ((q & 1) == 0)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_ptr_t)dst, 16, a_off[j], kt * BK * 2, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_ptr_t)dst, 16, b_off[j], kt * BK * 2, 0, 0);
     } else {
       const bool kin = kt * BK + gchunk * 8 < p.k;
-      if (j < 8)
+      if ((q & 1) == 0)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_ptr_t)dst, 16,
                                                  kin ? a_off[j] + kt * BK * 2 : kOutOfRange, 0, 0, 0);
       else
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_ptr_t)dst, 16,
-                                                 kin ? b_off[j & 7] + kt * BK * 2 : kOutOfRange, 0, 0, 0);
+                                                 kin ? b_off[j] + kt * BK * 2 : kOutOfRange, 0, 0, 0);
     }
   };
-  // fragment f (0..15) of half `half` of step kt, in the order the products
-  // use them (x 0, y 0..7, x 1..7): lane l supplies row (l & 15) of a 16-row
-  // block and 16-byte chunk half * 4 + l / 16 of the step
-  auto read1 = [&](int kt, int half, int f, u32x4 (&xf)[8], u32x4 (&yf)[8]) __attribute__((always_inline)) {
-    const unsigned char* b = lds + (kt & 1) * kStepBytes;
-    const int c = half * 4 + (lane >> 4);
+  // Fragment reads: lane l supplies row (l & 15) of a 16-row block and
+  // 16-byte chunk half * 4 + l / 16 of the step.  rd_a[h] and rd_b[h] are
+  // the lane's byte offsets, inside a slot, of the first fragment of half h;
+  // fragment s lies 16 rows (2 KiB) further.
+  uint32_t rd_a[2], rd_b[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int c = h * 4 + (lane >> 4);
+    const int ra = wm * 128 + (lane & 15), rb = wn * 128 + (lane & 15);
+    rd_a[h] = (uint32_t)(ra * kRowBytes + ((c ^ (ra & 7)) * 16));
+    rd_b[h] = (uint32_t)(rb * kRowBytes + ((c ^ (rb & 7)) * 16));
+  }
+  // fragment f (0..15) of half `half` of the step whose A is in slot sa and
+  // B in slot sb, in the order the products use them (x 0, y 0..7, x 1..7)
+  auto read1 = [&](int sa, int sb, int half, int f, u32x4 (&xf)[8], u32x4 (&yf)[8])
+                   __attribute__((always_inline)) {
     if (f >= 1 && f <= 8) {
-      const int r = wm * 128 + (f - 1) * 16 + (lane & 15);
-      yf[f - 1] = *reinterpret_cast<const u32x4*>(b + r * kRowBytes + ((c ^ (r & 7)) * 16));
+      const unsigned char* a = lds + sa * kPartBytes + rd_a[half];
+      yf[f - 1] = *reinterpret_cast<const u32x4*>(a + (f - 1) * 16 * kRowBytes);
     } else {
       const int s = f == 0 ? 0 : f - 8;
-      const int r = wn * 128 + s * 16 + (lane & 15);
-      xf[s] = *reinterpret_cast<const u32x4*>(b + kPartBytes + r * kRowBytes + ((c ^ (r & 7)) * 16));
+      const unsigned char* b = lds + sb * kPartBytes + rd_b[half];
+      xf[s] = *reinterpret_cast<const u32x4*>(b + s * 16 * kRowBytes);
     }
   };
   f32x4 acc[8][8];
   // one half step: the 64 products of (xc, yc) (x: B rows, y: A rows, so
   // each lane's four results are four consecutive output columns), the 16
-  // reads of half `half` of step kt into (xn, yn) and, with LOAD, the 16
-  // loads of step lkt
-  auto half_step = [&](auto first, auto load, auto global, const u32x4 (&xc)[8], const u32x4 (&yc)[8],
-                       u32x4 (&xn)[8], u32x4 (&yn)[8], int kt, int half, int lkt)
+  // reads of half `half` of the step in slots (sa, sb) into (xn, yn) and,
+  // with LOAD, the eight loads of part lq into slot lslot
+  auto half_step = [&](auto first, auto load, auto whole, const u32x4 (&xc)[8], const u32x4 (&yc)[8],
+                       u32x4 (&xn)[8], u32x4 (&yn)[8], int sa, int sb, int half, int lq, int lslot)
                        __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < 64; ++i) {
       mma_agpr<DT, decltype(first)::value>(acc[i / 8][i % 8], xc[i / 8], yc[i % 8]);
-      if (i % 4 == 0) read1(kt, half, i / 4, xn, yn);
-      if (decltype(load)::value && i % 4 == 2) load1(global, lkt, i / 4);
+      if (i % 4 == 0) read1(sa, sb, half, i / 4, xn, yn);
+      if (decltype(load)::value && i % 8 == 2) load1(whole, lq, lslot, i / 8);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
   using Yes = std::true_type;
   using No = std::false_type;
+  auto wrap = [](int s) __attribute__((always_inline)) { return s >= kSlots ? s - kSlots : s; };
   u32x4 xa[8], ya[8], xb[8], yb[8];
   if (nk > 0) {
-    // steps 0 and 1 load at once, so that step 1 has all of step 0 to land
-    // before the loop's first barrier waits for it
-    if (nk_full > 0) {
+    // parts 0..4 (A0 B0 A1 B1 A2) at once, into slots 0..4; the first
+    // barrier waits for A0 and B0 only
 #pragma unroll
-      for (int j = 0; j < 16; ++j) load1(Yes{}, 0, j);
-    } else {
+    for (int q = 0; q < kSlots; ++q) {
+      if ((q >> 1) < nk_full) {
 #pragma unroll
-      for (int j = 0; j < 16; ++j) load1(No{}, 0, j);
+        for (int j = 0; j < 8; ++j) load1(Yes{}, q, q, j);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) load1(No{}, q, q, j);
+      }
     }
-    if (nk_full > 1) {
-#pragma unroll
-      for (int j = 0; j < 16; ++j) load1(Yes{}, 1, j);
-    } else {
-#pragma unroll
-      for (int j = 0; j < 16; ++j) load1(No{}, 1, j);
-    }
-    __builtin_amdgcn_s_waitcnt(wait_vmcnt(16));   // step 0 landed (loads complete in order)
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt(24));   // loads complete in order
     __builtin_amdgcn_s_barrier();
 #pragma unroll
-    for (int f = 0; f < 16; ++f) read1(0, 0, f, xa, ya);
+    for (int f = 0; f < 16; ++f) read1(0, 1, 0, f, xa, ya);
     // step 0: its first half's products (from zero) carry the second half's
     // reads
-    half_step(Yes{}, No{}, No{}, xa, ya, xb, yb, 0, 1, 0);
-    auto step = [&](auto global, int kt) __attribute__((always_inline)) {
-      // step kt has landed for every wave, and every wave is done reading
-      // step kt - 1, whose buffer step kt + 1 loads into (past k: zeros)
+    half_step(Yes{}, No{}, No{}, xa, ya, xb, yb, 0, 1, 1, 0, 0);
+    // step kt: A in slot sa (2 kt mod 5), B in sa + 1; B of step kt + 1 goes
+    // to sa + 3 and A of step kt + 2 to sa + 4 (mod 5), the slots of step
+    // kt - 1
+    auto step = [&](auto whole, int kt, int sa) __attribute__((always_inline)) {
+      // A and B of step kt have landed for every wave (A of step kt + 1 may
+      // still be landing), and every wave is done reading step kt - 1
       __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-      __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+      __builtin_amdgcn_s_waitcnt(wait_vmcnt(8));
       __builtin_amdgcn_s_barrier();
-      half_step(No{}, Yes{}, global, xb, yb, xa, ya, kt, 0, kt + 1);   // step kt - 1, second half
-      half_step(No{}, No{}, No{}, xa, ya, xb, yb, kt, 1, 0);           // step kt, first half
+      const int sb = wrap(sa + 1);
+      half_step(No{}, Yes{}, whole, xb, yb, xa, ya, sa, sb, 0, 2 * kt + 3, wrap(sa + 3));  // kt - 1, 2nd half
+      half_step(No{}, Yes{}, whole, xa, ya, xb, yb, sa, sb, 1, 2 * kt + 4, wrap(sa + 4));  // kt, 1st half
     };
     // two loops rather than a branch per step, which would split the
     // registers' assignment between two copies of the products
-    int kt = 1;
-    for (; kt + 1 < nk_full; ++kt) step(Yes{}, kt);   // loads of whole steps
-    for (; kt < nk; ++kt) step(No{}, kt);             // the partial step and past it
+    int kt = 1, sa = 2;
+    for (; kt + 2 < nk_full; ++kt, sa = wrap(sa + 2)) step(Yes{}, kt, sa);   // loads of whole steps
+    for (; kt < nk; ++kt, sa = wrap(sa + 2)) step(No{}, kt, sa);             // the partial step, past it
 #pragma unroll
     for (int i = 0; i < 64; ++i) mma_agpr<DT, false>(acc[i / 8][i % 8], xb[i / 8], yb[i % 8]);
     settle_agprs(acc);

@@ -164,10 +164,12 @@ def test_k_around_whole_steps(dtype):
     steps that lie wholly inside k with global loads and the last, partial
     step (and the steps past the end, which must read as zeros) with
     range-checked buffer loads, in two loops; the boundary moves with k.
-    Ragged and whole tiles, both widths against the oracle and bitwise
-    equal to each other."""
+    The wide kernel loads up to two steps ahead into a ring of five operand
+    slots, so k from one step to seven whole steps (and one past) covers
+    every way the ring's prologue and its two loops split.  Ragged and whole
+    tiles, both widths against the oracle and bitwise equal to each other."""
     for m, n, world in ((264, 520, 2), (512, 512, 4)):
-        for k in (8, 56, 64, 72, 120, 128, 136, 184, 192, 200, 320):
+        for k in (8, 56, 64, 72, 120, 128, 136, 184, 192, 200, 256, 264, 320, 384, 448, 456):
             a, b, c = make(dtype, m, n, k, False, seed=k + m)
             want, y, mag = oracle_rows(a, b, c, 1.0, 0.0, world, dtype)
             first = None
