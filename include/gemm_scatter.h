@@ -69,12 +69,15 @@ extern "C" {
 #define GEMM_SCATTER_TILE_M 256
 #define GEMM_SCATTER_TILE_N 256
 #define GEMM_SCATTER_TILE_N_NARROW 128
-/* The automatic width counts whole rounds of workgroups over the compute
- * units of an MI355X: a round of 256 x 128 tiles takes about 0.63 of the time
- * of a round of 256 x 256 tiles (64 against 102 us on the 8192 x 3584 bf16
- * weights), so the narrow width is taken when
- * 63 * ceil(T128 / CUS) < 100 * ceil(T256 / CUS), T the tile count at each
- * width. */
+/* The automatic width counts rounds of workgroups (one tile each) over the
+ * compute units of an MI355X.  A full round of 256 x 128 tiles takes about
+ * 0.63 of the time of a full round of 256 x 256 tiles (63 against 101 us on
+ * the 8192 x 3584 bf16 weights), but a round the 256-wide tiles fill only in
+ * part costs less than a full one (2560 tokens: 156 us in two 256-wide
+ * rounds of 256 and 64 tiles, 163 us in three 128-wide rounds), so the
+ * narrow width is taken only when it needs no more rounds than the wide
+ * one: ceil(T128 / CUS) <= ceil(T256 / CUS), T the tile count at each width
+ * (T > 0). */
 #define GEMM_SCATTER_CUS 256
 
 /*

@@ -586,7 +586,7 @@ int resolve_tile_n(int64_t m, int64_t n, int tile_n) {
   const int64_t wide = tiles_m * ((n + gsc::BN - 1) / gsc::BN);
   const int64_t narrow = tiles_m * ((n + gsc::BN_NARROW - 1) / gsc::BN_NARROW);
   const int64_t cus = GEMM_SCATTER_CUS;
-  return 63 * ((narrow + cus - 1) / cus) < 100 * ((wide + cus - 1) / cus) ? gsc::BN_NARROW : gsc::BN;
+  return wide > 0 && (narrow + cus - 1) / cus <= (wide + cus - 1) / cus ? gsc::BN_NARROW : gsc::BN;
 }
 
 }  // namespace

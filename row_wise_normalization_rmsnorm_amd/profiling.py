@@ -493,9 +493,9 @@ def gemm_shapes_summary(argv) -> int:
         f.write("Command: `python bench.py --gemm-shapes` (HIP events over back-to-back launches, "
                 "operands rotated over about 1 GiB; the library column is torch.matmul, i.e. "
                 "hipBLASLt's plain GEMM, on the same operands).  Output tiles of 256 rows by "
-                "256 or 128 columns, one workgroup each on 256 CUs; the automatic width counts "
-                "whole rounds of workgroups, a round of 128-wide tiles costing about 0.63 of a "
-                "round of 256-wide ones (include/gemm_scatter.h).\n\n")
+                "256 or 128 columns, one workgroup each on 256 CUs; the automatic width takes "
+                "128-wide tiles only where they need no more rounds of 256 workgroups than "
+                "256-wide ones (include/gemm_scatter.h).\n\n")
         f.write("| m | n | k | chunks | automatic width | tiles | kernel µs | TFLOP/s | "
                 "% of 2.5 PFLOP/s | 256-wide µs | 128-wide µs | hipBLASLt µs | "
                 "hipBLASLt TFLOP/s | kernel ÷ hipBLASLt |\n"
