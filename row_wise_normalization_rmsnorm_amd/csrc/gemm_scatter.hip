@@ -80,6 +80,11 @@ __device__ __forceinline__ void store_tile(const AccT& acc, const Params& p, int
   const int lane = tid & 63;
   const int row0 = m0 + wm * WR + (lane & 15);
   const int col0 = n0 + wn * WC + 4 * (lane >> 4);
+  // interior tiles whose BM rows all belong to chunk q0 address every row
+  // from that chunk's row m0
+  const int q0 = m0 / p.chunk_rows;
+  const bool one_chunk = (m0 + BM - 1) / p.chunk_rows == q0;
+  uint16_t* const chunk_base = p.dst[q0] + (int64_t)(m0 - q0 * p.chunk_rows) * p.ldd;
   if (p.vec_out == 2 && m0 + BM <= p.m && n0 + TN <= p.n) {
     // interior tile, 16-byte aligned output rows: the rounded tile is staged
     // in LDS, then leaves in 16-byte stores that cover whole row segments of
@@ -111,24 +116,38 @@ __device__ __forceinline__ void store_tile(const AccT& acc, const Params& p, int
       }
     }
     __syncthreads();
-    // thread t stores chunk (t % CPR) of rows t / CPR + RPP i
+    // thread t stores chunk (t % CPR) of rows t / CPR + RPP i.  When the
+    // tile's rows lie in one chunk (always, if the chunk height is a
+    // multiple of the tile's), one base pointer serves every row: no
+    // division and no per-lane fetch of a chunk pointer before each store
+    const int c = (int)((unsigned)tid % CPR);
+    if (one_chunk) {
+      uint16_t* base = chunk_base + n0 + c * 8;
+#pragma unroll 8
+      for (int i = 0; i < BM / RPP; ++i) {
+        const int r = i * RPP + (int)((unsigned)tid / CPR);
+        const u32x4 v = *reinterpret_cast<const u32x4*>(st + r * pitch + ((c ^ (r & 15)) * 4));
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(base + (int64_t)r * p.ldd));
+      }
+    } else {
 #pragma unroll 4
-    for (int i = 0; i < BM / RPP; ++i) {
-      const int r = i * RPP + (int)((unsigned)tid / CPR);
-      const int gm = m0 + r;
-      const int q = gm / p.chunk_rows;
-      uint16_t* drow = p.dst[q] + (int64_t)(gm - q * p.chunk_rows) * p.ldd + n0;
-      const int c = (int)((unsigned)tid % CPR);
-      const u32x4 v = *reinterpret_cast<const u32x4*>(st + r * pitch + ((c ^ (r & 15)) * 4));
-      __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(drow + c * 8));
+      for (int i = 0; i < BM / RPP; ++i) {
+        const int r = i * RPP + (int)((unsigned)tid / CPR);
+        const int gm = m0 + r;
+        const int q = gm / p.chunk_rows;
+        uint16_t* drow = p.dst[q] + (int64_t)(gm - q * p.chunk_rows) * p.ldd + n0;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(st + r * pitch + ((c ^ (r & 15)) * 4));
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(drow + c * 8));
+      }
     }
   } else if (p.vec_out && m0 + BM <= p.m && n0 + TN <= p.n) {
     // interior tile: every element exists and every access is 8-byte aligned
 #pragma unroll
     for (int t = 0; t < NY; ++t) {
       const int gm = row0 + t * 16;
-      const int q = gm / p.chunk_rows;
-      uint16_t* drow = p.dst[q] + (int64_t)(gm - q * p.chunk_rows) * p.ldd + col0;
+      const int q = one_chunk ? 0 : gm / p.chunk_rows;
+      uint16_t* drow = (one_chunk ? chunk_base + (int64_t)(gm - m0) * p.ldd
+                                  : p.dst[q] + (int64_t)(gm - q * p.chunk_rows) * p.ldd) + col0;
       const uint16_t* crow = p.c ? p.c + (int64_t)gm * p.ldc + col0 : nullptr;
 #pragma unroll
       for (int s = 0; s < NX; ++s) {
