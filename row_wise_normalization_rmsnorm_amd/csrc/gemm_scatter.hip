@@ -17,12 +17,15 @@
 //     16-byte load-to-LDS forms, k steps of 64 in a ring of five 32 KiB
 //     operand slots, so every load has one and a half steps to land; each
 //     32-wide half step's products carry, one every four, the LDS reads of
-//     the next half's fragments and, one every eight, a load.  Measured on
-//     the 4096 x 8192 x 3584 bf16 product in one process: 179.0 us, against
-//     190.8 with two 64 KiB step buffers (loads one step ahead) and 209.1
-//     for the earlier eight-wave kernel (two waves per SIMD, 128 x 64
-//     blocks, loads staged through registers); the alternatives are in
-//     probe/gemm_probe.hip (bench.py --gemm-design-sweep).
+//     the next half's fragments and, one every eight, a load, with almost
+//     no address arithmetic in the loop.  Measured on the 4096 x 8192 x 3584
+//     bf16 product in one process with its predecessors: 168.0 us, against
+//     179.0 for the first ring (64-bit load addresses, per-read slot
+//     arithmetic), 190.8 with two 64 KiB step buffers (loads one step
+//     ahead) and 209.1 for the earlier eight-wave kernel (two waves per
+//     SIMD, 128 x 64 blocks, loads staged through registers); the
+//     alternatives are in probe/gemm_probe.hip (bench.py
+//     --gemm-design-sweep).
 //   - 256 x 128 tiles (gemm_narrow_kernel) for products whose 256 x 256
 //     tiles would leave much of the last round of workgroups idle (1024
 //     tokens: 128 tiles on 256 CUs): eight waves, two per SIMD, each a
