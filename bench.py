@@ -204,8 +204,7 @@ def gemm_bench(a, name: str) -> int:
                     for _ in range(w.world)]
         sets.append(s)
     tile_n = B.gemm_scatter_tile_n(w.m, w.n)
-    waves = 4 if tile_n == B.GEMM_SCATTER_TILE_N else 8
-    kernel = f"gemm_scatter<{w.dtype},256x{tile_n}x64,w{waves},mfma16x16x32>"
+    kernel = f"gemm_scatter<{w.dtype},256x{tile_n}x64,w4,mfma16x16x32>"
 
     def step(i):
         s = sets[i % nsets]
@@ -875,8 +874,7 @@ def gemm_design_sweep(a) -> int:
             return f
 
         tn = B.gemm_scatter_tile_n(w.m, w.n)
-        waves = 4 if tn == B.GEMM_SCATTER_TILE_N else 8
-        variants[(w.k, "library", f"gemm_scatter, 256x{tn} tiles, {waves} waves", -1, 0)] = (w, lib_step)
+        variants[(w.k, "library", f"gemm_scatter, 256x{tn} tiles, 4 waves", -1, 0)] = (w, lib_step)
         variants[(w.k, "hipBLASLt", "torch.matmul(a, b.t())", -1, 0)] = (w, blas_step)
         for mode in range(5):
             variants[(w.k, 2, GEMM_DESIGNS[2].format(nbuf=4), mode, 4)] = (w, pstep(2, mode, 4))

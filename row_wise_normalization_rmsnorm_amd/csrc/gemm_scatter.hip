@@ -28,9 +28,9 @@
 //     --gemm-design-sweep).
 //   - 256 x 128 tiles (gemm_narrow_kernel) for products whose 256 x 256
 //     tiles would leave much of the last round of workgroups idle (1024
-//     tokens: 128 tiles on 256 CUs): eight waves, two per SIMD, each a
-//     64 x 64 block of 4 x 4 products, loads through registers a whole k
-//     step ahead.  Both widths accumulate every output in the same k order,
+//     tokens: 128 tiles on 256 CUs): four waves too, each a 128 x 64 block
+//     of 4 x 8 products, the same operand path with a ring of three 48 KiB
+//     step slots.  Both widths accumulate every output in the same k order,
 //     so they give bitwise equal results.
 //   - The matrix-core operands are swapped (the weight rows feed the first
 //     operand, the activation rows the second), so each lane's four
@@ -200,200 +200,6 @@ __device__ __forceinline__ void store_tile(const AccT& acc, const Params& p, int
   }
 }
 
-// Tile shape of an eight-wave workgroup: 256 rows by TN columns (the
-// narrow kernel's 128).  The waves cover it as WAVES_M x WAVES_N blocks of
-// WR x WC outputs, each NY x NX products of 16 x 16; each thread loads NB
-// 16-byte chunks of B rows per k step (and four of A rows).
-template <int TN>
-struct Shape {
-  static constexpr int WAVES_N = TN == 256 ? 4 : 2;
-  static constexpr int WAVES_M = 8 / WAVES_N;
-  static constexpr int WR = BM / WAVES_M;  // 128 or 64 rows
-  static constexpr int WC = TN / WAVES_N;  // 64 columns
-  static constexpr int NY = WR / 16;
-  static constexpr int NX = WC / 16;
-  static constexpr int NB = TN / 64;       // B chunks per thread per k step
-  static constexpr int NLOAD = 4 + NB;     // global loads (and LDS writes) per thread per k step
-  static constexpr int PER = NX * NY / NLOAD;        // products placed after each load or write
-  static constexpr int REST = NX * NY - PER * NLOAD;  // products left after the last one
-  static constexpr int CPR = TN / 8;       // 16-byte chunks per staged output row
-  static constexpr int RPP = kThreads / CPR;  // staged rows stored per pass
-  static_assert(WC == 64 && NY * 16 == WR && CPR >= 16 && BM % RPP == 0, "tile mapping");
-};
-
-template <int DT>
-__global__ __launch_bounds__(kThreads) void gemm_narrow_kernel(Params p) {
-  using E = Elem<DT>;
-  constexpr int TN = BN_NARROW;
-  using S = Shape<TN>;
-  constexpr int NX = S::NX, NY = S::NY, NB = S::NB;
-  // per stage, [row * 8 + chunk] of the tile's BM rows of A, then of its TN
-  // rows of B
-  struct Stage {
-    u32x4 a[BM * kChunksPerRow];
-    u32x4 b[TN * kChunksPerRow];
-  };
-  __shared__ Stage lds[2];
-
-  const int tile = tile_at(position_of_wg((int)blockIdx.x, p.sched.tiles), p.sched);
-  const int m0 = (tile / p.sched.tiles_n) * BM;
-  const int n0 = (tile % p.sched.tiles_n) * TN;
-  const int tid = (int)threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  // wave block: WR rows x WC columns
-  const int wm = (int)((unsigned)wave / S::WAVES_N), wn = (int)((unsigned)wave % S::WAVES_N);
-
-  // global -> LDS: thread t moves logical chunk (t & 7) of rows (t >> 3) + 64 i
-  const int lrow = tid >> 3;
-  const int lchunk = tid & 7;
-
-  f32x4 acc[NX][NY];
-#pragma unroll
-  for (int s = 0; s < NX; ++s)
-#pragma unroll
-    for (int t = 0; t < NY; ++t) acc[s][t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-
-  u32x4 ra[4], rb[NB];
-  const int nk = (p.k + BK - 1) / BK;
-
-  // Operand loads are raw buffer loads over this tile's rows; the resource
-  // ends at the last element of the tile's last existing row.  Rows past m
-  // (n) only feed outputs that are never stored, so they re-read the
-  // thread's last existing row.  Chunks past k must read as zero: they take
-  // an offset beyond every resource, which the range check turns into zeros.
-  // Nothing is selected after a load, so the loads of the next k step stay
-  // in flight while the current one is multiplied.  The whole variable
-  // offset sits in the VGPR offset, which the range check covers.
-  const int a_tile_rows = p.m - m0 < BM ? p.m - m0 : BM;
-  const int b_tile_rows = p.n - n0 < TN ? p.n - n0 : TN;
-  const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(p.a + (int64_t)m0 * p.lda), (short)0,
-      (int)(((int64_t)(a_tile_rows - 1) * p.lda + p.k) * 2), kRsrcWord3);
-  const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(p.b + (int64_t)n0 * p.ldb), (short)0,
-      (int)(((int64_t)(b_tile_rows - 1) * p.ldb + p.k) * 2), kRsrcWord3);
-  // rows lrow + 64 i exist for i < a_rows (b_rows); the last one of them
-  const int a_rows = a_tile_rows > lrow ? (a_tile_rows - lrow + 63) / 64 : 0;
-  const int b_rows = b_tile_rows > lrow ? (b_tile_rows - lrow + 63) / 64 : 0;
-  const int a_last = a_rows > 0 ? lrow + 64 * (a_rows - 1) : a_tile_rows - 1;
-  const int b_last = b_rows > 0 ? lrow + 64 * (b_rows - 1) : b_tile_rows - 1;
-  const int a_off0 = (lrow * (int)p.lda + lchunk * 8) * 2;
-  const int b_off0 = (lrow * (int)p.ldb + lchunk * 8) * 2;
-  const int a_off_last = (a_last * (int)p.lda + lchunk * 8) * 2;
-  const int b_off_last = (b_last * (int)p.ldb + lchunk * 8) * 2;
-  const int a_row_step = 64 * (int)p.lda * 2, b_row_step = 64 * (int)p.ldb * 2;
-
-  auto lstore = [&](int stage) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = lrow + 64 * i;
-      const int at = r * kChunksPerRow + (lchunk ^ (r & 7));
-      lds[stage].a[at] = ra[i];
-      if (i < NB) lds[stage].b[at] = rb[i];
-    }
-  };
-
-  // Fragments of one 32-wide k half: lane l supplies row (l & 15) of each
-  // 16-row block and 16-byte chunk ks*4 + l/16 of the 64-wide k step.
-  auto read_frags = [&](int stage, int ks, u32x4 (&xf)[NX], u32x4 (&yf)[NY]) {
-    const int sw = (ks * 4 + (lane >> 4)) ^ (lane & 7);
-#pragma unroll
-    for (int s = 0; s < NX; ++s)
-      xf[s] = lds[stage].b[(wn * S::WC + s * 16 + (lane & 15)) * kChunksPerRow + sw];
-#pragma unroll
-    for (int t = 0; t < NY; ++t)
-      yf[t] = lds[stage].a[(wm * S::WR + t * 16 + (lane & 15)) * kChunksPerRow + sw];
-  };
-  auto mfmas = [&](const u32x4 (&xf)[NX], const u32x4 (&yf)[NY]) {
-#pragma unroll
-    for (int s = 0; s < NX; ++s)
-#pragma unroll
-      for (int t = 0; t < NY; ++t) acc[s][t] = E::mfma(xf[s], yf[t], acc[s][t]);
-  };
-
-  // A narrow tile has half the products per k step, too few to cover a
-  // load issued at the step's start (measured 98.8 -> 64.8 us on the
-  // 1024 x 8192 x 3584 bf16 product): the loads of step kt + 2 go out as
-  // soon as the LDS writes of step kt + 1 free their registers, a whole k
-  // step before they are needed.  The row offsets are fixed before the
-  // loop so that no load sits under a branch (a branch there makes the
-  // compiler wait for every load in flight).
-  int a_off[4], b_off[NB];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    a_off[i] = i < a_rows ? a_off0 + i * a_row_step : a_off_last;
-    if (i < NB) b_off[i] = i < b_rows ? b_off0 + i * b_row_step : b_off_last;
-  }
-  // Steps whose every chunk lies inside k load with plain global loads
-  // (measured 3-5% faster than buffer loads at 1024, 2560 and 3072 tokens);
-  // the partial last step takes the buffer form, whose range check reads
-  // zeros past k.  Rows past m (n) re-read the last existing row.
-  const int nk_full = p.k / BK;
-  const unsigned char* a_tile = reinterpret_cast<const unsigned char*>(p.a + (int64_t)m0 * p.lda);
-  const unsigned char* b_tile = reinterpret_cast<const unsigned char*>(p.b + (int64_t)n0 * p.ldb);
-  auto gload_early = [&](auto global, int kt) __attribute__((always_inline)) {
-    const int kb = kt * BK * 2;
-    if constexpr (decltype(global)::value) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        ra[i] = *reinterpret_cast<const u32x4*>(a_tile + a_off[i] + kb);
-        if (i < NB) rb[i] = *reinterpret_cast<const u32x4*>(b_tile + b_off[i] + kb);
-      }
-    } else {
-      const bool kin = kt * BK + lchunk * 8 < p.k;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        ra[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                              rsa, kin ? a_off[i] + kb : kOutOfRange, 0, 0));
-        if (i < NB)
-          rb[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                rsb, kin ? b_off[i] + kb : kOutOfRange, 0, 0));
-      }
-    }
-  };
-  auto gload_step = [&](int kt) __attribute__((always_inline)) {
-    if (kt < nk_full)
-      gload_early(std::true_type{}, kt);
-    else
-      gload_early(std::false_type{}, kt);
-  };
-  if (nk > 0) {
-    gload_step(0);
-    lstore(0);
-    gload_step(nk > 1 ? 1 : 0);
-  }
-  __syncthreads();
-  u32x4 xf[NX], yf[NY];
-  // step kt multiplies while step min(kt + 2, nk - 1) loads; two loops
-  // rather than a branch per step, which would split the registers'
-  // assignment between two copies of the step
-  auto step = [&](auto global, int kt) __attribute__((always_inline)) {
-    const int cur = kt & 1;
-    read_frags(cur, 0, xf, yf);
-    mfmas(xf, yf);
-    read_frags(cur, 1, xf, yf);
-    lstore(cur ^ 1);
-    gload_early(global, kt + 2 < nk ? kt + 2 : nk - 1);
-    mfmas(xf, yf);
-#pragma unroll
-    for (int i = 0; i < S::NLOAD; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);       // one LDS write
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);       // one global load
-      __builtin_amdgcn_sched_group_barrier(0x008, S::PER, 0);  // products
-    }
-    if constexpr (S::REST > 0) __builtin_amdgcn_sched_group_barrier(0x008, S::REST, 0);
-    __syncthreads();
-  };
-  int kt = 0;
-  for (; kt + 2 < nk_full; ++kt) step(std::true_type{}, kt);
-  for (; kt < nk; ++kt) step(std::false_type{}, kt);
-
-  store_tile<DT, TN, S::WR, S::WC, kThreads>(acc, p, tile, m0, n0, wm, wn, tid,
-                                            reinterpret_cast<uint32_t*>(&lds[0].a[0]));
-}
-
-
 // The 256 x 256 tile: four waves, one per SIMD, each a 128 x 128 block of
 // 8 x 8 products whose 256 fp32 accumulators stay in AGPRs.  Operand tiles
 // go straight from memory into LDS (gfx950's 16-byte load-to-LDS buffer
@@ -414,7 +220,6 @@ __global__ __launch_bounds__(kThreads) void gemm_narrow_kernel(Params p) {
 // are fixed for the kernel (fragments sit at immediate offsets), and a load
 // of a whole step takes its lane's row offset, fixed too, plus the step's
 // byte offset in a scalar register.
-constexpr int kWideThreads = 256;
 constexpr int kRowBytes = BK * 2;                 // LDS bytes per operand row (128)
 constexpr int kPartBytes = BM * kRowBytes;        // one operand of one k step: 32 KiB
 constexpr int kSlots = 5;                         // 160 KiB, the whole LDS
@@ -422,7 +227,7 @@ static_assert(BN == BM, "the wide tile is square");
 static_assert(kSlots * kPartBytes <= 160 * 1024, "gfx950 LDS per workgroup");
 
 template <int DT>
-__global__ __launch_bounds__(kWideThreads) void gemm_wide_kernel(Params p) {
+__global__ __launch_bounds__(kThreads) void gemm_wide_kernel(Params p) {
   __shared__ __attribute__((aligned(1024))) unsigned char lds[kSlots * kPartBytes];
   const int tile = tile_at(position_of_wg((int)blockIdx.x, p.sched.tiles), p.sched);
   const int m0 = (tile / p.sched.tiles_n) * BM;
@@ -574,8 +379,176 @@ __global__ __launch_bounds__(kWideThreads) void gemm_wide_kernel(Params p) {
   // results are staged in
   __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
   __builtin_amdgcn_s_barrier();
-  store_tile<DT, BN, 128, 128, kWideThreads>(acc, p, tile, m0, n0, wm, wn, tid,
+  store_tile<DT, BN, 128, 128, kThreads>(acc, p, tile, m0, n0, wm, wn, tid,
                                              reinterpret_cast<uint32_t*>(lds));
+}
+
+
+// The 256 x 128 tile, for products whose 256 x 256 tiles would leave much of
+// their last round of workgroups idle: four waves, one per SIMD, each a
+// 128 x 64 block of 4 x 8 products (128 accumulators in AGPRs).  The
+// operand path is the wide kernel's, scaled to the narrower tile: loads
+// straight into LDS, a ring of three 48 KiB step slots (A 32 KiB, B 16 KiB;
+// step kt loads step kt + 2 into the slot step kt - 1 freed, so every load
+// has one to two steps to land), whole steps loaded with the step in the
+// scalar offset, per-lane read bases fixed for the kernel.  Each 32-wide
+// half step's 32 products carry its 12 fragment reads and six of the step's
+// 12 loads.  Against the eight-wave kernel it replaced (4 x 2 blocks of
+// 64 x 64, loads staged through registers and written to LDS, two waves per
+// SIMD), in one process, bitwise equal: 60.7 against 63.1 us at 1024
+// tokens, 155.4 against 169.7 at 2560 (8192 x 3584 bf16 weights).
+constexpr int kNarrowStepBytes = (BM + BN_NARROW) * kRowBytes;   // 48 KiB
+constexpr int kNarrowSlots = 3;
+static_assert(kNarrowSlots * kNarrowStepBytes <= 160 * 1024, "gfx950 LDS per workgroup");
+
+template <int DT>
+__global__ __launch_bounds__(kThreads) void gemm_narrow_kernel(Params p) {
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[kNarrowSlots * kNarrowStepBytes];
+  const int tile = tile_at(position_of_wg((int)blockIdx.x, p.sched.tiles), p.sched);
+  const int m0 = (tile / p.sched.tiles_n) * BM;
+  const int n0 = (tile % p.sched.tiles_n) * BN_NARROW;
+  const int tid = (int)threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;   // wave block: rows wm * 128, columns wn * 64
+  const int nk = (p.k + BK - 1) / BK;
+  const int a_tile_rows = p.m - m0 < BM ? p.m - m0 : BM;
+  const int b_tile_rows = p.n - n0 < BN_NARROW ? p.n - n0 : BN_NARROW;
+  // buffer resources as in the wide kernel
+  const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.a + (int64_t)m0 * p.lda), (short)0,
+      (int)(((int64_t)(a_tile_rows - 1) * p.lda + p.k) * 2), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.b + (int64_t)n0 * p.ldb), (short)0,
+      (int)(((int64_t)(b_tile_rows - 1) * p.ldb + p.k) * 2), kRsrcWord3);
+  // loads 0..7 of a step move this wave's A rows 64 wave + 8 j + lane / 8,
+  // loads 8..11 its B rows 32 wave + 8 (j - 8) + lane / 8; LDS chunk
+  // position lane % 8 of a row holds global chunk (lane % 8) ^ (row % 8)
+  const int lr = lane >> 3, gchunk = (lane & 7) ^ lr;
+  int off[12];
+#pragma unroll
+  for (int j = 0; j < 12; ++j) {
+    if (j < 8) {
+      const int r = 64 * wave + 8 * j + lr;
+      off[j] = ((r < a_tile_rows ? r : a_tile_rows - 1) * (int)p.lda + gchunk * 8) * 2;
+    } else {
+      const int r = 32 * wave + 8 * (j - 8) + lr;
+      off[j] = ((r < b_tile_rows ? r : b_tile_rows - 1) * (int)p.ldb + gchunk * 8) * 2;
+    }
+  }
+  const int nk_full = p.k / BK;
+  // load j of step kt into slot `slot` (A rows first, then B rows)
+  auto load1 = [&](auto whole, int kt, int slot, int j) __attribute__((always_inline)) {
+    unsigned char* dst = lds + slot * kNarrowStepBytes +
+                         (j < 8 ? (64 * wave + 8 * j) * kRowBytes
+                                : BM * kRowBytes + (32 * wave + 8 * (j - 8)) * kRowBytes);
+    if constexpr (decltype(whole)::value) {
+      if (j < 8)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_ptr_t)dst, 16, off[j], kt * BK * 2, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_ptr_t)dst, 16, off[j], kt * BK * 2, 0, 0);
+    } else {
+      const bool kin = kt * BK + gchunk * 8 < p.k;
+      if (j < 8)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_ptr_t)dst, 16,
+                                                 kin ? off[j] + kt * BK * 2 : kOutOfRange, 0, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_ptr_t)dst, 16,
+                                                 kin ? off[j] + kt * BK * 2 : kOutOfRange, 0, 0, 0);
+    }
+  };
+  // per-lane byte offsets, inside a slot, of the first A and B fragment of
+  // each half step; fragment s lies 16 rows (2 KiB) further
+  uint32_t rd_a[2], rd_b[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int c = h * 4 + (lane >> 4);
+    const int ra = wm * 128 + (lane & 15), rb = wn * 64 + (lane & 15);
+    rd_a[h] = (uint32_t)(ra * kRowBytes + ((c ^ (ra & 7)) * 16));
+    rd_b[h] = (uint32_t)(BM * kRowBytes + rb * kRowBytes + ((c ^ (rb & 7)) * 16));
+  }
+  // fragment f (0..11) of half `half` of the step in `slot`, in the order
+  // the products use them (x 0, y 0..7, x 1..3)
+  auto read1 = [&](int slot, int half, int f, u32x4 (&xf)[4], u32x4 (&yf)[8])
+                   __attribute__((always_inline)) {
+    const unsigned char* base = lds + slot * kNarrowStepBytes;
+    if (f >= 1 && f <= 8) {
+      yf[f - 1] = *reinterpret_cast<const u32x4*>(base + rd_a[half] + (f - 1) * 16 * kRowBytes);
+    } else {
+      const int s = f == 0 ? 0 : f - 8;
+      xf[s] = *reinterpret_cast<const u32x4*>(base + rd_b[half] + s * 16 * kRowBytes);
+    }
+  };
+  f32x4 acc[4][8];
+  // one half step: the 32 products of (xc, yc), the 12 reads of half `half`
+  // of the step in `slot` into (xn, yn) spread between them, and with LOAD
+  // loads 6 PART .. 6 PART + 5 of step lkt into slot lslot, one every five
+  // products
+  auto half_step = [&](auto first, auto load, auto whole, auto part, const u32x4 (&xc)[4],
+                       const u32x4 (&yc)[8], u32x4 (&xn)[4], u32x4 (&yn)[8], int slot, int half,
+                       int lkt, int lslot) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      mma_agpr<DT, decltype(first)::value>(acc[i / 8][i % 8], xc[i / 8], yc[i % 8]);
+#pragma unroll
+      for (int f = 0; f < 12; ++f)
+        if (i == (f * 8) / 3) read1(slot, half, f, xn, yn);
+      if (decltype(load)::value && i % 5 == 3) load1(whole, lkt, lslot, decltype(part)::value * 6 + i / 5);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  using Yes = std::true_type;
+  using No = std::false_type;
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  auto wrap = [](int s) __attribute__((always_inline)) { return s >= kNarrowSlots ? s - kNarrowSlots : s; };
+  u32x4 xa[4], ya[8], xb[4], yb[8];
+  if (nk > 0) {
+    // steps 0..2 into slots 0..2 at once; the first barrier waits for step 0
+#pragma unroll
+    for (int t = 0; t < kNarrowSlots; ++t) {
+      if (t < nk_full) {
+#pragma unroll
+        for (int j = 0; j < 12; ++j) load1(Yes{}, t, t, j);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 12; ++j) load1(No{}, t, t, j);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt(24));   // loads complete in order
+    __builtin_amdgcn_s_barrier();
+#pragma unroll
+    for (int f = 0; f < 12; ++f) read1(0, 0, f, xa, ya);
+    half_step(Yes{}, No{}, No{}, P0{}, xa, ya, xb, yb, 0, 1, 0, 0);
+    // step kt is in slot s = kt mod 3 and loads step kt + 2 into slot s + 2
+    // (mod 3), which step kt - 1 used
+    auto step = [&](auto whole, int kt, int s) __attribute__((always_inline)) {
+      // step kt has landed for every wave (step kt + 1 may still be
+      // landing), and every wave is done reading step kt - 1
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      __builtin_amdgcn_s_waitcnt(wait_vmcnt(12));
+      __builtin_amdgcn_s_barrier();
+      const int ls = wrap(s + 2);
+      half_step(No{}, Yes{}, whole, P0{}, xb, yb, xa, ya, s, 0, kt + 2, ls);   // step kt - 1, second half
+      half_step(No{}, Yes{}, whole, P1{}, xa, ya, xb, yb, s, 1, kt + 2, ls);   // step kt, first half
+    };
+    int kt = 1, s = 1;
+    for (; kt + 2 < nk_full; ++kt, s = wrap(s + 1)) step(Yes{}, kt, s);   // loads of whole steps
+    for (; kt < nk; ++kt, s = wrap(s + 1)) step(No{}, kt, s);             // the partial step, past it
+#pragma unroll
+    for (int i = 0; i < 32; ++i) mma_agpr<DT, false>(acc[i / 8][i % 8], xb[i / 8], yb[i % 8]);
+    settle_agprs(acc);
+  } else {
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+#pragma unroll
+      for (int y = 0; y < 8; ++y) acc[x][y] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+  // the last loads (zeros past k) may still be landing in the LDS the
+  // results are staged in
+  __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+  __builtin_amdgcn_s_barrier();
+  store_tile<DT, BN_NARROW, 128, 64, kThreads>(acc, p, tile, m0, n0, wm, wn, tid,
+                                               reinterpret_cast<uint32_t*>(lds));
 }
 
 }  // namespace gsc
@@ -721,7 +694,7 @@ extern "C" int gemm_scatter_fwd(void* const* dst, int64_t ldd, int world, int ra
   hipStream_t st = (hipStream_t)stream;
   const dim3 grid((unsigned)tiles);
   if (tn == gsc::BN) {
-    const dim3 block(gsc::kWideThreads);
+    const dim3 block(gsc::kThreads);
     if (dtype == RMSN_BF16)
       hipLaunchKernelGGL((gsc::gemm_wide_kernel<RMSN_BF16>), grid, block, 0, st, p);
     else

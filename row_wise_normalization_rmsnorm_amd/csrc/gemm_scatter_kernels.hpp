@@ -16,7 +16,7 @@ constexpr int BM = GEMM_SCATTER_TILE_M;
 constexpr int BN = GEMM_SCATTER_TILE_N;            // wide tile
 constexpr int BN_NARROW = GEMM_SCATTER_TILE_N_NARROW;
 constexpr int BK = 64;                 // k elements per step (128 bytes of a row)
-constexpr int kThreads = 512;          // eight waves, two per SIMD
+constexpr int kThreads = 256;          // four waves, one per SIMD
 constexpr int kChunksPerRow = BK / 8;  // 16-byte chunks per LDS row
 constexpr int kXcds = 8;
 constexpr int kRoundPerXcd = 32;       // positions each XCD takes per round (one per CU)
@@ -25,7 +25,7 @@ constexpr int kGroupM = 8;             // tile-rows per schedule group
 // offset used for a chunk outside every operand's range.
 constexpr int kRsrcWord3 = 0x00020000;
 constexpr int kOutOfRange = 0x7FFFFFF0;
-static_assert(BM == 256 && BN == 256 && BN_NARROW == 128 && kThreads == 512,
+static_assert(BM == 256 && BN == 256 && BN_NARROW == 128 && kThreads == 256,
               "the thread mapping assumes these");
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -197,6 +197,20 @@ __device__ __forceinline__ void settle_agprs(f32x4 (&acc)[8][8]) {
                : GSC_PIN(48), GSC_PIN(49), GSC_PIN(50), GSC_PIN(51), GSC_PIN(52), GSC_PIN(53), GSC_PIN(54),
                  GSC_PIN(55), GSC_PIN(56), GSC_PIN(57), GSC_PIN(58), GSC_PIN(59), GSC_PIN(60), GSC_PIN(61),
                  GSC_PIN(62), GSC_PIN(63));
+#undef GSC_PIN
+}
+
+// The same for the 4 x 8 accumulators of a 128 x 64 wave block.
+__device__ __forceinline__ void settle_agprs(f32x4 (&acc)[4][8]) {
+#define GSC_PIN(I) "+a"(acc[I / 8][I % 8])
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+               : GSC_PIN(0), GSC_PIN(1), GSC_PIN(2), GSC_PIN(3), GSC_PIN(4), GSC_PIN(5), GSC_PIN(6),
+                 GSC_PIN(7), GSC_PIN(8), GSC_PIN(9), GSC_PIN(10), GSC_PIN(11), GSC_PIN(12), GSC_PIN(13),
+                 GSC_PIN(14), GSC_PIN(15));
+  asm volatile(""
+               : GSC_PIN(16), GSC_PIN(17), GSC_PIN(18), GSC_PIN(19), GSC_PIN(20), GSC_PIN(21), GSC_PIN(22),
+                 GSC_PIN(23), GSC_PIN(24), GSC_PIN(25), GSC_PIN(26), GSC_PIN(27), GSC_PIN(28), GSC_PIN(29),
+                 GSC_PIN(30), GSC_PIN(31));
 #undef GSC_PIN
 }
 
