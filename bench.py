@@ -204,7 +204,8 @@ def gemm_bench(a, name: str) -> int:
                     for _ in range(w.world)]
         sets.append(s)
     tile_n = B.gemm_scatter_tile_n(w.m, w.n)
-    kernel = f"gemm_scatter<{w.dtype},256x{tile_n}x64,w4,mfma16x16x32>"
+    tile_m = B.gemm_scatter_tile_m(w.m, w.n, tile_n)
+    kernel = f"gemm_scatter<{w.dtype},{tile_m}x{tile_n}x64,w4,mfma16x16x32>"
 
     def step(i):
         s = sets[i % nsets]
@@ -349,9 +350,16 @@ def gemm_shapes(a) -> int:
             return e0.elapsed_time(e1) / reps
 
         reps = max(20, min(200, int(2e5 / max(w.flops() / 1.2e12, 1.0))))
-        fns = {tn: (lambda i, tn=tn: B.gemm_scatter_fwd(sets[i % nsets][2], sets[i % nsets][0],
-                                                          sets[i % nsets][1], tile_n=tn))
-               for tn in (B.GEMM_SCATTER_TILE_N, B.GEMM_SCATTER_TILE_N_NARROW)}
+
+        def shaped(tm, tn):
+            def f(i):
+                with B.gemm_tile_m(tm if tn == B.GEMM_SCATTER_TILE_N else 0):
+                    B.gemm_scatter_fwd(sets[i % nsets][2], sets[i % nsets][0], sets[i % nsets][1], tile_n=tn)
+            return f
+
+        shapes = [(tm, B.GEMM_SCATTER_TILE_N) for tm in (256, 192, 160)] + \
+            [(B.GEMM_SCATTER_TILE_M, B.GEMM_SCATTER_TILE_N_NARROW)]
+        fns = {sh: shaped(*sh) for sh in shapes}
         fns["lib"] = lambda i: torch.matmul(sets[i % nsets][0], sets[i % nsets][1].t())
         # the GPU idles while the host builds a shape's inputs, and its clocks
         # take tens of milliseconds to rise again: warm up for 100 ms, then
@@ -366,17 +374,21 @@ def gemm_shapes(a) -> int:
         for _ in range(3):
             for key, f in fns.items():
                 runs[key].append(timed(f, reps))
-        by_width = {}
-        for tn in (B.GEMM_SCATTER_TILE_N, B.GEMM_SCATTER_TILE_N_NARROW):
-            t_ms = statistics.median(runs[tn])
-            by_width[tn] = {"tiles": B.gemm_scatter_tiles(m, n, tn), "us": round(t_ms * 1e3, 2),
-                            "tflops": round(w.flops() / (t_ms * 1e-3) / 1e12, 1)}
+        by_shape = {}
+        for tm, tn in shapes:
+            t_ms = statistics.median(runs[(tm, tn)])
+            with B.gemm_tile_m(tm if tn == B.GEMM_SCATTER_TILE_N else 0):
+                tiles = B.gemm_scatter_tiles(m, n, tn)
+            by_shape[(tm, tn)] = {"tiles": tiles, "us": round(t_ms * 1e3, 2),
+                                  "tflops": round(w.flops() / (t_ms * 1e-3) / 1e12, 1)}
         auto = B.gemm_scatter_tile_n(m, n)
+        auto_m = B.gemm_scatter_tile_m(m, n, auto)
+        a = by_shape[(auto_m, auto)]
         lib = statistics.median(runs["lib"])
         print(json.dumps({"workload": w.name, "m": m, "n": n, "k": k, "world": world,
-                          "tile_n": auto, "tiles": by_width[auto]["tiles"],
-                          "us": by_width[auto]["us"], "tflops": by_width[auto]["tflops"],
-                          "by_tile_n": {str(t): v for t, v in by_width.items()},
+                          "tile_n": auto, "tile_m": auto_m, "tiles": a["tiles"],
+                          "us": a["us"], "tflops": a["tflops"],
+                          "by_tile": {f"{tm}x{tn}": v for (tm, tn), v in by_shape.items()},
                           "library_us": round(lib * 1e3, 2),
                           "library_tflops": round(w.flops() / (lib * 1e-3) / 1e12, 1),
                           "rotating_sets": nsets, "launches": reps}), flush=True)
@@ -874,7 +886,8 @@ def gemm_design_sweep(a) -> int:
             return f
 
         tn = B.gemm_scatter_tile_n(w.m, w.n)
-        variants[(w.k, "library", f"gemm_scatter, 256x{tn} tiles, 4 waves", -1, 0)] = (w, lib_step)
+        tm = B.gemm_scatter_tile_m(w.m, w.n, tn)
+        variants[(w.k, "library", f"gemm_scatter, {tm}x{tn} tiles, 4 waves", -1, 0)] = (w, lib_step)
         variants[(w.k, "hipBLASLt", "torch.matmul(a, b.t())", -1, 0)] = (w, blas_step)
         for mode in range(5):
             variants[(w.k, 2, GEMM_DESIGNS[2].format(nbuf=4), mode, 4)] = (w, pstep(2, mode, 4))

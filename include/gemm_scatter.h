@@ -41,13 +41,17 @@
  *     2^29 (a tile's operand rows are addressed with 32-bit offsets).
  *   - tile_n: the output tile's width, GEMM_SCATTER_TILE_N (256) or
  *     GEMM_SCATTER_TILE_N_NARROW (128); 0 takes gemm_scatter_tile_n(m, n).
- *     Tiles are GEMM_SCATTER_TILE_M (256) rows high either way.
+ *     The 128-wide tiles are GEMM_SCATTER_TILE_M (256) rows high; the
+ *     256-wide ones 256, 192 or 160 rows, gemm_scatter_tile_m(m, n, tile_n)
+ *     (shorter tiles fill rounds of workgroups that 256-row tiles would
+ *     leave partly idle).  Every output is accumulated in the same k order
+ *     at every tile shape, so the results do not depend on it.
  *   - flags (nullable): gemm_scatter_tiles(m, n, tile_n) uint32 slots.  When
  *     given, the workgroup that computes tile t stores `epoch` to flags[t]
  *     after the tile's elements are written and made visible at system
  *     scope, so a consumer that reads flags[t] == epoch sees the whole tile.
- *     Tile t covers rows [(t / T) * GEMM_SCATTER_TILE_M, ...) and columns
- *     [(t % T) * W, ...), W the tile width used, T = ceil(n / W).
+ *     Tile t covers rows [(t / T) * H, ...) and columns [(t % T) * W, ...),
+ *     H and W the tile height and width used, T = ceil(n / W).
  *   - dst chunks must not overlap each other, a, b, c or flags.
  *   - The call enqueues one kernel on `stream` (NULL: the default stream),
  *     allocates nothing and does not synchronise.  Arguments are validated
@@ -94,10 +98,31 @@ int gemm_scatter_fwd(void* const* dst, int64_t ldd, int world, int rank, const v
  * rule beside GEMM_SCATTER_CUS; -1 if m or n is negative or too large. */
 int gemm_scatter_tile_n(int64_t m, int64_t n);
 
+/* gemm_scatter_tile_m -- the tile height a call with this m, n and tile_n
+ * (0: automatic width) uses: 256 for the 128-wide tiles; for the 256-wide
+ * ones the height set by gemm_scatter_tune, else the cheapest of 256, 192
+ * and 160 rows by an estimate of the rounds of workgroups each needs (a
+ * partial round counting 0.7 + 0.3 f of a full one, f the fraction of the
+ * CUS it keeps busy) times a round's cost (a fixed part plus a part in
+ * proportion to the rows; fitted on MI355X to 8192 x 3584 bf16 weights:
+ * 85.6, 68.3 and 62.5 us per full round), ties to the taller tile.  -1 if m
+ * or n is negative or too large, or tile_n is not 0, 128 or 256. */
+int gemm_scatter_tile_m(int64_t m, int64_t n, int tile_n);
+
 /* gemm_scatter_tiles -- number of output tiles (and flag slots) for m x n at
- * tile width tile_n (0: automatic); -1 if m or n is negative or too large,
- * or tile_n is not 0, 128 or 256. */
+ * tile width tile_n (0: automatic), at the height gemm_scatter_tile_m
+ * gives; -1 if m or n is negative or too large, or tile_n is not 0, 128 or
+ * 256. */
 int64_t gemm_scatter_tiles(int64_t m, int64_t n, int tile_n);
+
+/* gemm_scatter_tune -- for tuning and testing only.  From now on every call
+ * of this process (gemm_scatter_fwd, gemm_scatter_tile_m, gemm_scatter_tiles,
+ * gemm_scatter_schedule) makes the 256-wide tiles tile_m rows high (256,
+ * 192 or 160); 0 restores the automatic height.  Set it before the calls it
+ * should affect: it is not synchronised with calls running on other
+ * threads.  Returns RMSN_OK, or RMSN_ERR_SHAPE for another value (nothing is
+ * changed then). */
+int gemm_scatter_tune(int tile_m);
 
 /*
  * gemm_scatter_schedule -- the tile schedule of one launch (host only, no

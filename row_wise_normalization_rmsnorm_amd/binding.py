@@ -27,8 +27,8 @@ EXPORTS = ("rmsnorm_fwd", "add_rmsnorm_fwd", "rmsnorm_strerror", "rmsnorm_last_e
            "rmsnorm_plan_ag", "rmsnorm_variants_ag", "rmsnorm_tune")
 GATHER_MAX = 16
 BLOCK_SUM_EXPORTS = ("block_all_reduce_sum", "block_all_reduce_sum_noalloc", "block_sum_tune")
-GEMM_SCATTER_EXPORTS = ("gemm_scatter_fwd", "gemm_scatter_tile_n", "gemm_scatter_tiles",
-                        "gemm_scatter_schedule")
+GEMM_SCATTER_EXPORTS = ("gemm_scatter_fwd", "gemm_scatter_tile_n", "gemm_scatter_tile_m",
+                        "gemm_scatter_tiles", "gemm_scatter_schedule", "gemm_scatter_tune")
 
 # GEMM with a reduce-scatter epilogue (include/gemm_scatter.h)
 GEMM_SCATTER_WORLD_MAX = 16
@@ -115,6 +115,10 @@ def lib() -> ctypes.CDLL:
             l.gemm_scatter_fwd.restype = c_int
             l.gemm_scatter_tile_n.argtypes = [i64, i64]
             l.gemm_scatter_tile_n.restype = c_int
+            l.gemm_scatter_tile_m.argtypes = [i64, i64, c_int]
+            l.gemm_scatter_tile_m.restype = c_int
+            l.gemm_scatter_tune.argtypes = [c_int]
+            l.gemm_scatter_tune.restype = c_int
             l.gemm_scatter_tiles.argtypes = [i64, i64, c_int]
             l.gemm_scatter_tiles.restype = i64
             l.gemm_scatter_schedule.argtypes = [i64, i64, c_int, c_int, c_int,
@@ -449,8 +453,30 @@ def gemm_scatter_tile_n(m: int, n: int) -> int:
     return int(lib().gemm_scatter_tile_n(m, n))
 
 
+def gemm_scatter_tile_m(m: int, n: int, tile_n: int = 0) -> int:
+    """The output tile height a call with this m, n and tile width uses (256
+    for 128-wide tiles; 256, 192 or 160 for 256-wide ones)."""
+    return int(lib().gemm_scatter_tile_m(m, n, tile_n))
+
+
 def gemm_scatter_tiles(m: int, n: int, tile_n: int = 0) -> int:
     return int(lib().gemm_scatter_tiles(m, n, tile_n))
+
+
+def gemm_scatter_tune(tile_m: int = 0) -> None:
+    """For tuning and testing: force the 256-wide tiles' height (256, 192 or
+    160) for every later call; 0 restores the automatic choice."""
+    _check(lib().gemm_scatter_tune(tile_m))
+
+
+@contextlib.contextmanager
+def gemm_tile_m(tile_m: int):
+    """gemm_scatter_tune(tile_m) for the duration of a with-block."""
+    gemm_scatter_tune(tile_m)
+    try:
+        yield
+    finally:
+        gemm_scatter_tune(0)
 
 
 def gemm_scatter_schedule(m: int, n: int, world: int, rank: int, tile_n: int = 0):

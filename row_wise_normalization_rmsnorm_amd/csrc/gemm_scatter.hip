@@ -70,25 +70,25 @@ namespace gsc {
 // The results of one tile, alpha * D + beta * C, into the destination
 // chunks, then the tile's flag.  acc[s][t][r] is D[row m0 + wm*WR + t*16 +
 // (lane & 15)][col n0 + wn*WC + s*16 + 4*(lane >> 4) + r] for the THREADS / 64
-// waves' WR x WC blocks of a 256 x TN tile; staging: BM * TN * 2 bytes of LDS
+// waves' WR x WC blocks of a TM x TN tile; staging: TM * TN * 2 bytes of LDS
 // that no wave reads any more.
-template <int DT, int TN, int WR, int WC, int THREADS, typename AccT>
+template <int DT, int TM, int TN, int WR, int WC, int THREADS, typename AccT>
 __device__ __forceinline__ void store_tile(const AccT& acc, const Params& p, int tile, int m0, int n0,
                                            int wm, int wn, int tid, uint32_t* staging) {
   using E = Elem<DT>;
   constexpr int NX = WC / 16, NY = WR / 16;
   constexpr int CPR = TN / 8;          // 16-byte chunks per staged output row
   constexpr int RPP = THREADS / CPR;   // staged rows stored per pass
-  static_assert(CPR >= 16 && BM % RPP == 0, "staging layout");
+  static_assert(CPR >= 16 && TM % RPP == 0, "staging layout");
   const int lane = tid & 63;
   const int row0 = m0 + wm * WR + (lane & 15);
   const int col0 = n0 + wn * WC + 4 * (lane >> 4);
-  // interior tiles whose BM rows all belong to chunk q0 address every row
+  // interior tiles whose TM rows all belong to chunk q0 address every row
   // from that chunk's row m0
   const int q0 = m0 / p.chunk_rows;
-  const bool one_chunk = (m0 + BM - 1) / p.chunk_rows == q0;
+  const bool one_chunk = (m0 + TM - 1) / p.chunk_rows == q0;
   uint16_t* const chunk_base = p.dst[q0] + (int64_t)(m0 - q0 * p.chunk_rows) * p.ldd;
-  if (p.vec_out == 2 && m0 + BM <= p.m && n0 + TN <= p.n) {
+  if (p.vec_out == 2 && m0 + TM <= p.m && n0 + TN <= p.n) {
     // interior tile, 16-byte aligned output rows: the rounded tile is staged
     // in LDS, then leaves in 16-byte stores that cover whole row segments of
     // TN * 2 bytes (nontemporal: the output is not read back here).  The
@@ -127,14 +127,14 @@ __device__ __forceinline__ void store_tile(const AccT& acc, const Params& p, int
     if (one_chunk) {
       uint16_t* base = chunk_base + n0 + c * 8;
 #pragma unroll 8
-      for (int i = 0; i < BM / RPP; ++i) {
+      for (int i = 0; i < TM / RPP; ++i) {
         const int r = i * RPP + (int)((unsigned)tid / CPR);
         const u32x4 v = *reinterpret_cast<const u32x4*>(st + r * pitch + ((c ^ (r & 15)) * 4));
         __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(base + (int64_t)r * p.ldd));
       }
     } else {
 #pragma unroll 4
-      for (int i = 0; i < BM / RPP; ++i) {
+      for (int i = 0; i < TM / RPP; ++i) {
         const int r = i * RPP + (int)((unsigned)tid / CPR);
         const int gm = m0 + r;
         const int q = gm / p.chunk_rows;
@@ -143,7 +143,7 @@ __device__ __forceinline__ void store_tile(const AccT& acc, const Params& p, int
         __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(drow + c * 8));
       }
     }
-  } else if (p.vec_out && m0 + BM <= p.m && n0 + TN <= p.n) {
+  } else if (p.vec_out && m0 + TM <= p.m && n0 + TN <= p.n) {
     // interior tile: every element exists and every access is 8-byte aligned
 #pragma unroll
     for (int t = 0; t < NY; ++t) {
@@ -200,43 +200,51 @@ __device__ __forceinline__ void store_tile(const AccT& acc, const Params& p, int
   }
 }
 
-// The 256 x 256 tile: four waves, one per SIMD, each a 128 x 128 block of
-// 8 x 8 products whose 256 fp32 accumulators stay in AGPRs.  Operand tiles
-// go straight from memory into LDS (gfx950's 16-byte load-to-LDS buffer
-// form: no VGPR round trip, no LDS write instructions), k steps of 64.  The
-// LDS is a ring of five 32 KiB slots, one operand of one step each: A of
-// step t is part 2t and B part 2t + 1, in slot part % 5.  While step kt is
-// read, A of step kt + 1 has landed or is landing, and step kt issues B of
-// step kt + 1 and A of step kt + 2 into the two slots step kt - 1 freed:
-// every load has at least one and a half steps to land, against one with
-// two 64 KiB step buffers.  With one wave per SIMD nothing hides a stall,
-// so each 32-wide half step's 64 products carry, one every four, the 16 LDS
-// reads of the fragments the next half step multiplies, and one every eight
-// a load (B of the next step in the first half, A of the step after in the
-// second), in that order (a scheduling barrier after each product keeps the
-// compiler from bunching them): no wave holds the LDS queue or the memory
-// pipe for long, and the products keep issuing.  The loop carries almost no
-// address arithmetic: the slot is a scalar, each lane's four LDS read bases
-// are fixed for the kernel (fragments sit at immediate offsets), and a load
-// of a whole step takes its lane's row offset, fixed too, plus the step's
-// byte offset in a scalar register.
+// The TM x 256 tile (TM = 256, 192 or 160 rows): four waves, one per SIMD,
+// each a (TM / 2) x 128 block of 8 x NY products (NY = TM / 32) whose fp32
+// accumulators stay in AGPRs.  Operand tiles go straight from memory into
+// LDS (gfx950's 16-byte load-to-LDS buffer form: no VGPR round trip, no LDS
+// write instructions), k steps of 64.  The LDS is a ring of five 32 KiB
+// slots, one operand of one step each: A of step t is part 2t and B part
+// 2t + 1, in slot part % 5.  While step kt is read, A of step kt + 1 has
+// landed or is landing, and step kt issues B of step kt + 1 and A of step
+// kt + 2 into the two slots step kt - 1 freed: every load has at least one
+// and a half steps to land, against one with two 64 KiB step buffers.  With
+// one wave per SIMD nothing hides a stall, so each 32-wide half step's
+// products carry, evenly spaced, the LDS reads of the fragments the next
+// half step multiplies and the loads of one part (B of the next step in the
+// first half, A of the step after in the second), in that order (a
+// scheduling barrier after each product keeps the compiler from bunching
+// them): no wave holds the LDS queue or the memory pipe for long, and the
+// products keep issuing.  The loop carries almost no address arithmetic:
+// the slot is a scalar, each lane's four LDS read bases are fixed for the
+// kernel (fragments sit at immediate offsets), and a load of a whole step
+// takes its lane's row offset, fixed too, plus the step's byte offset in a
+// scalar register.  Tiles of 192 or 160 rows exist for products whose
+// 256-row tiles would leave much of a round of workgroups idle (1536 tokens:
+// one round of 192-row tiles; 2560: two of 160-row tiles).
 constexpr int kRowBytes = BK * 2;                 // LDS bytes per operand row (128)
 constexpr int kPartBytes = BM * kRowBytes;        // one operand of one k step: 32 KiB
 constexpr int kSlots = 5;                         // 160 KiB, the whole LDS
-static_assert(BN == BM, "the wide tile is square");
+static_assert(BN == BM, "the widest tile is square");
 static_assert(kSlots * kPartBytes <= 160 * 1024, "gfx950 LDS per workgroup");
 
-template <int DT>
-__global__ __launch_bounds__(kThreads) void gemm_wide_kernel(Params p) {
+template <int DT, int TM>
+__device__ __forceinline__ void wide_tile(const Params& p) {
+  constexpr int WR = TM / 2;    // rows of a wave block
+  constexpr int NY = WR / 16;   // its row fragments
+  constexpr int NA = TM / 32;   // A loads per wave and step
+  constexpr int NP = 8 * NY;    // products per half step
+  constexpr int NR = 8 + NY;    // fragment reads per half step
   __shared__ __attribute__((aligned(1024))) unsigned char lds[kSlots * kPartBytes];
   const int tile = tile_at(position_of_wg((int)blockIdx.x, p.sched.tiles), p.sched);
-  const int m0 = (tile / p.sched.tiles_n) * BM;
+  const int m0 = (tile / p.sched.tiles_n) * TM;
   const int n0 = (tile % p.sched.tiles_n) * BN;
   const int tid = (int)threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;   // wave block: rows wm * 128, columns wn * 128
+  const int wm = wave >> 1, wn = wave & 1;   // wave block: rows wm * WR, columns wn * 128
   const int nk = (p.k + BK - 1) / BK;
-  const int a_tile_rows = p.m - m0 < BM ? p.m - m0 : BM;
+  const int a_tile_rows = p.m - m0 < TM ? p.m - m0 : TM;
   const int b_tile_rows = p.n - n0 < BN ? p.n - n0 : BN;
   // buffer resources end at the last element of the tile's last existing
   // row; rows past m (n) re-read the last existing row (their outputs are
@@ -248,15 +256,20 @@ __global__ __launch_bounds__(kThreads) void gemm_wide_kernel(Params p) {
   const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(p.b + (int64_t)n0 * p.ldb), (short)0,
       (int)(((int64_t)(b_tile_rows - 1) * p.ldb + p.k) * 2), kRsrcWord3);
-  // load j (0..7) of a part moves this wave's tile rows 64 wave + 8 j +
-  // lane / 8; the 64 lanes fill 1 KiB of LDS in order, so LDS chunk position
-  // lane % 8 of a row holds global chunk (lane % 8) ^ (row % 8)
+  // A load j (0 .. NA - 1) moves this wave's tile rows (TM / 4) wave + 8 j +
+  // lane / 8, B load j (0..7) rows 64 wave + 8 j + lane / 8; the 64 lanes
+  // fill 1 KiB of LDS in order, so LDS chunk position lane % 8 of a row
+  // holds global chunk (lane % 8) ^ (row % 8)
   const int lr = lane >> 3, gchunk = (lane & 7) ^ lr;
-  int a_off[8], b_off[8];
+  int a_off[NA], b_off[8];
+#pragma unroll
+  for (int j = 0; j < NA; ++j) {
+    const int r = (TM / 4) * wave + 8 * j + lr;
+    a_off[j] = ((r < a_tile_rows ? r : a_tile_rows - 1) * (int)p.lda + gchunk * 8) * 2;
+  }
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int r = 64 * wave + 8 * j + lr;
-    a_off[j] = ((r < a_tile_rows ? r : a_tile_rows - 1) * (int)p.lda + gchunk * 8) * 2;
     b_off[j] = ((r < b_tile_rows ? r : b_tile_rows - 1) * (int)p.ldb + gchunk * 8) * 2;
   }
   // Steps whose every chunk lies inside k pass the step's byte offset as
@@ -265,17 +278,19 @@ __global__ __launch_bounds__(kThreads) void gemm_wide_kernel(Params p) {
   // The last, partial step and the steps past it put each chunk past k at
   // an offset outside the resource, which reads as zeros.
   const int nk_full = p.k / BK;
+  // load j of part q (A of step q / 2 for even q, B for odd q)
   auto load1 = [&](auto whole, int q, int slot, int j) __attribute__((always_inline)) {
     const int kt = q >> 1;
-    unsigned char* dst = lds + slot * kPartBytes + (64 * wave) * kRowBytes + j * 1024;
+    const bool is_a = (q & 1) == 0;
+    unsigned char* dst = lds + slot * kPartBytes + (is_a ? (TM / 4) * wave : 64 * wave) * kRowBytes + j * 1024;
     if constexpr (decltype(whole)::value) {
-      if ((q & 1) == 0)
+      if (is_a)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_ptr_t)dst, 16, a_off[j], kt * BK * 2, 0, 0);
       else
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_ptr_t)dst, 16, b_off[j], kt * BK * 2, 0, 0);
     } else {
       const bool kin = kt * BK + gchunk * 8 < p.k;
-      if ((q & 1) == 0)
+      if (is_a)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_ptr_t)dst, 16,
                                                  kin ? a_off[j] + kt * BK * 2 : kOutOfRange, 0, 0, 0);
       else
@@ -291,75 +306,91 @@ __global__ __launch_bounds__(kThreads) void gemm_wide_kernel(Params p) {
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int c = h * 4 + (lane >> 4);
-    const int ra = wm * 128 + (lane & 15), rb = wn * 128 + (lane & 15);
+    const int ra = wm * WR + (lane & 15), rb = wn * 128 + (lane & 15);
     rd_a[h] = (uint32_t)(ra * kRowBytes + ((c ^ (ra & 7)) * 16));
     rd_b[h] = (uint32_t)(rb * kRowBytes + ((c ^ (rb & 7)) * 16));
   }
-  // fragment f (0..15) of half `half` of the step whose A is in slot sa and
-  // B in slot sb, in the order the products use them (x 0, y 0..7, x 1..7)
-  auto read1 = [&](int sa, int sb, int half, int f, u32x4 (&xf)[8], u32x4 (&yf)[8])
+  // fragment f (0 .. NR - 1) of half `half` of the step whose A is in slot
+  // sa and B in slot sb, in the order the products use them (x 0, y 0 ..
+  // NY - 1, x 1..7)
+  auto read1 = [&](int sa, int sb, int half, int f, u32x4 (&xf)[8], u32x4 (&yf)[NY])
                    __attribute__((always_inline)) {
-    if (f >= 1 && f <= 8) {
+    if (f >= 1 && f <= NY) {
       const unsigned char* a = lds + sa * kPartBytes + rd_a[half];
       yf[f - 1] = *reinterpret_cast<const u32x4*>(a + (f - 1) * 16 * kRowBytes);
     } else {
-      const int s = f == 0 ? 0 : f - 8;
+      const int s = f == 0 ? 0 : f - NY;
       const unsigned char* b = lds + sb * kPartBytes + rd_b[half];
       xf[s] = *reinterpret_cast<const u32x4*>(b + s * 16 * kRowBytes);
     }
   };
-  f32x4 acc[8][8];
-  // one half step: the 64 products of (xc, yc) (x: B rows, y: A rows, so
-  // each lane's four results are four consecutive output columns), the 16
+  f32x4 acc[8][NY];
+  // one half step: the NP products of (xc, yc) (x: B rows, y: A rows, so
+  // each lane's four results are four consecutive output columns), the NR
   // reads of half `half` of the step in slots (sa, sb) into (xn, yn) and,
-  // with LOAD, the eight loads of part lq into slot lslot
-  auto half_step = [&](auto first, auto load, auto whole, const u32x4 (&xc)[8], const u32x4 (&yc)[8],
-                       u32x4 (&xn)[8], u32x4 (&yn)[8], int sa, int sb, int half, int lq, int lslot)
-                       __attribute__((always_inline)) {
+  // with LOAD, the NL loads of part lq into slot lslot.  Read f sits at
+  // product (f NP) / NR, load l at product (l NP) / NL + 2.
+  auto half_step = [&](auto first, auto load, auto whole, auto nl, const u32x4 (&xc)[8],
+                       const u32x4 (&yc)[NY], u32x4 (&xn)[8], u32x4 (&yn)[NY], int sa, int sb, int half,
+                       int lq, int lslot) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < 64; ++i) {
-      mma_agpr<DT, decltype(first)::value>(acc[i / 8][i % 8], xc[i / 8], yc[i % 8]);
-      if (i % 4 == 0) read1(sa, sb, half, i / 4, xn, yn);
-      if (decltype(load)::value && i % 8 == 2) load1(whole, lq, lslot, i / 8);
+    for (int i = 0; i < NP; ++i) {
+      mma_agpr<DT, decltype(first)::value>(acc[i / NY][i % NY], xc[i / NY], yc[i % NY]);
+      {
+        const int f = (i * NR + NP - 1) / NP;
+        if (f < NR && (f * NP) / NR == i) read1(sa, sb, half, f, xn, yn);
+      }
+      if constexpr (decltype(load)::value) {
+        constexpr int NL = decltype(nl)::value;
+        const int j = i - 2;
+        const int l = j < 0 ? NL : (j * NL + NP - 1) / NP;
+        if (l < NL && (l * NP) / NL == j) load1(whole, lq, lslot, l);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
   using Yes = std::true_type;
   using No = std::false_type;
+  using LoadsB = std::integral_constant<int, 8>;
+  using LoadsA = std::integral_constant<int, NA>;
   auto wrap = [](int s) __attribute__((always_inline)) { return s >= kSlots ? s - kSlots : s; };
-  u32x4 xa[8], ya[8], xb[8], yb[8];
+  u32x4 xa[8], ya[NY], xb[8], yb[NY];
   if (nk > 0) {
     // parts 0..4 (A0 B0 A1 B1 A2) at once, into slots 0..4; the first
     // barrier waits for A0 and B0 only
 #pragma unroll
     for (int q = 0; q < kSlots; ++q) {
+      const int nq = (q & 1) == 0 ? NA : 8;
       if ((q >> 1) < nk_full) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) load1(Yes{}, q, q, j);
+        for (int j = 0; j < 8; ++j)
+          if (j < nq) load1(Yes{}, q, q, j);
       } else {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) load1(No{}, q, q, j);
+        for (int j = 0; j < 8; ++j)
+          if (j < nq) load1(No{}, q, q, j);
       }
     }
-    __builtin_amdgcn_s_waitcnt(wait_vmcnt(24));   // loads complete in order
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt(2 * NA + 8));   // loads complete in order
     __builtin_amdgcn_s_barrier();
 #pragma unroll
-    for (int f = 0; f < 16; ++f) read1(0, 1, 0, f, xa, ya);
+    for (int f = 0; f < NR; ++f) read1(0, 1, 0, f, xa, ya);
     // step 0: its first half's products (from zero) carry the second half's
     // reads
-    half_step(Yes{}, No{}, No{}, xa, ya, xb, yb, 0, 1, 1, 0, 0);
+    half_step(Yes{}, No{}, No{}, LoadsB{}, xa, ya, xb, yb, 0, 1, 1, 0, 0);
     // step kt: A in slot sa (2 kt mod 5), B in sa + 1; B of step kt + 1 goes
     // to sa + 3 and A of step kt + 2 to sa + 4 (mod 5), the slots of step
     // kt - 1
     auto step = [&](auto whole, int kt, int sa) __attribute__((always_inline)) {
-      // A and B of step kt have landed for every wave (A of step kt + 1 may
-      // still be landing), and every wave is done reading step kt - 1
+      // A and B of step kt have landed for every wave (A of step kt + 1,
+      // the last NA loads, may still be landing), and every wave is done
+      // reading step kt - 1
       __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-      __builtin_amdgcn_s_waitcnt(wait_vmcnt(8));
+      __builtin_amdgcn_s_waitcnt(wait_vmcnt(NA));
       __builtin_amdgcn_s_barrier();
       const int sb = wrap(sa + 1);
-      half_step(No{}, Yes{}, whole, xb, yb, xa, ya, sa, sb, 0, 2 * kt + 3, wrap(sa + 3));  // kt - 1, 2nd half
-      half_step(No{}, Yes{}, whole, xa, ya, xb, yb, sa, sb, 1, 2 * kt + 4, wrap(sa + 4));  // kt, 1st half
+      half_step(No{}, Yes{}, whole, LoadsB{}, xb, yb, xa, ya, sa, sb, 0, 2 * kt + 3, wrap(sa + 3));  // kt - 1, 2nd half
+      half_step(No{}, Yes{}, whole, LoadsA{}, xa, ya, xb, yb, sa, sb, 1, 2 * kt + 4, wrap(sa + 4));  // kt, 1st half
     };
     // two loops rather than a branch per step, which would split the
     // registers' assignment between two copies of the products
@@ -367,22 +398,34 @@ __global__ __launch_bounds__(kThreads) void gemm_wide_kernel(Params p) {
     for (; kt + 2 < nk_full; ++kt, sa = wrap(sa + 2)) step(Yes{}, kt, sa);   // loads of whole steps
     for (; kt < nk; ++kt, sa = wrap(sa + 2)) step(No{}, kt, sa);             // the partial step, past it
 #pragma unroll
-    for (int i = 0; i < 64; ++i) mma_agpr<DT, false>(acc[i / 8][i % 8], xb[i / 8], yb[i % 8]);
-    settle_agprs(acc);
+    for (int i = 0; i < NP; ++i) mma_agpr<DT, false>(acc[i / NY][i % NY], xb[i / NY], yb[i % NY]);
+    settle_agprs_rows(acc);
   } else {
 #pragma unroll
-    for (int s = 0; s < 8; ++s)
+    for (int x = 0; x < 8; ++x)
 #pragma unroll
-      for (int t = 0; t < 8; ++t) acc[s][t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      for (int y = 0; y < NY; ++y) acc[x][y] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   }
   // the last loads (zeros past k) may still be landing in the LDS the
   // results are staged in
   __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
   __builtin_amdgcn_s_barrier();
-  store_tile<DT, BN, 128, 128, kThreads>(acc, p, tile, m0, n0, wm, wn, tid,
-                                             reinterpret_cast<uint32_t*>(lds));
+  store_tile<DT, TM, BN, WR, 128, kThreads>(acc, p, tile, m0, n0, wm, wn, tid,
+                                            reinterpret_cast<uint32_t*>(lds));
 }
 
+template <int DT>
+__global__ __launch_bounds__(kThreads) void gemm_wide_kernel(Params p) {
+  wide_tile<DT, 256>(p);
+}
+template <int DT>
+__global__ __launch_bounds__(kThreads) void gemm_wide192_kernel(Params p) {
+  wide_tile<DT, 192>(p);
+}
+template <int DT>
+__global__ __launch_bounds__(kThreads) void gemm_wide160_kernel(Params p) {
+  wide_tile<DT, 160>(p);
+}
 
 // The 256 x 128 tile, for products whose 256 x 256 tiles would leave much of
 // their last round of workgroups idle: four waves, one per SIMD, each a
@@ -547,7 +590,7 @@ __global__ __launch_bounds__(kThreads) void gemm_narrow_kernel(Params p) {
   // results are staged in
   __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
   __builtin_amdgcn_s_barrier();
-  store_tile<DT, BN_NARROW, 128, 64, kThreads>(acc, p, tile, m0, n0, wm, wn, tid,
+  store_tile<DT, BM, BN_NARROW, 128, 64, kThreads>(acc, p, tile, m0, n0, wm, wn, tid,
                                                reinterpret_cast<uint32_t*>(lds));
 }
 
@@ -584,6 +627,43 @@ int resolve_tile_n(int64_t m, int64_t n, int tile_n) {
   return wide > 0 && (narrow + cus - 1) / cus <= (wide + cus - 1) / cus ? gsc::BN_NARROW : gsc::BN;
 }
 
+// forced height of the 256-wide tiles (gemm_scatter_tune); 0: automatic
+int g_tile_m = 0;
+
+// Estimated time of the 256-wide tiles at height h, in arbitrary units:
+// rounds of workgroups, a partial round counting 0.7 + 0.3 f of a full one
+// (f the fraction of CUs it keeps busy: fewer tiles share the memory
+// system), times a round's cost, a fixed part plus a part in proportion to
+// the tile's rows.  Fitted to the 4096 x 8192 x 3584 bf16 product's rounds
+// on 8192 x 3584 weights: 85.6, 68.3 and 62.5 us per full round of 256-,
+// 192- and 160-row tiles, and 67.6 us for a quarter-full round of 256-row
+// tiles beside 85.6 for a full one.
+int64_t wide_cost(int64_t m, int64_t n, int h) {
+  const int64_t cus = GEMM_SCATTER_CUS;
+  const int64_t t = ((m + h - 1) / h) * ((n + gsc::BN - 1) / gsc::BN);
+  const int64_t full = t / cus, rem = t % cus;
+  const int64_t rounds = 1000 * full + (rem ? 700 + 300 * rem / cus : 0);
+  return rounds * (390 + 1000 * h / gsc::BM);
+}
+
+// tile height a call uses: 256 rows for the 128-wide tiles; for the 256-wide
+// ones the forced height, else the cheapest of 256, 192 and 160 rows by
+// wide_cost (ties to the taller tile)
+int resolve_tile_m(int64_t m, int64_t n, int tn) {
+  if (tn != gsc::BN) return gsc::BM;
+  if (g_tile_m) return g_tile_m;
+  int best = gsc::BM;
+  int64_t best_cost = wide_cost(m, n, gsc::BM);
+  for (int h : {192, 160}) {
+    const int64_t c = wide_cost(m, n, h);
+    if (c < best_cost) {
+      best = h;
+      best_cost = c;
+    }
+  }
+  return best;
+}
+
 }  // namespace
 
 extern "C" int gemm_scatter_tile_n(int64_t m, int64_t n) {
@@ -591,11 +671,25 @@ extern "C" int gemm_scatter_tile_n(int64_t m, int64_t n) {
   return resolve_tile_n(m, n, 0);
 }
 
+extern "C" int gemm_scatter_tile_m(int64_t m, int64_t n, int tile_n) {
+  if (m < 0 || n < 0 || m > kIntMax || n > kIntMax) return -1;
+  const int tn = resolve_tile_n(m, n, tile_n);
+  return tn < 0 ? -1 : resolve_tile_m(m, n, tn);
+}
+
+extern "C" int gemm_scatter_tune(int tile_m) {
+  if (tile_m != 0 && tile_m != 256 && tile_m != 192 && tile_m != 160)
+    return rmsn_set_error(RMSN_ERR_SHAPE, "gemm_scatter_tune: tile_m must be 0, 256, 192 or 160");
+  g_tile_m = tile_m;
+  return RMSN_OK;
+}
+
 extern "C" int64_t gemm_scatter_tiles(int64_t m, int64_t n, int tile_n) {
   if (m < 0 || n < 0 || m > kIntMax || n > kIntMax) return -1;
   const int tn = resolve_tile_n(m, n, tile_n);
   if (tn < 0) return -1;
-  const int64_t t = ((m + gsc::BM - 1) / gsc::BM) * ((n + tn - 1) / tn);
+  const int tm = resolve_tile_m(m, n, tn);
+  const int64_t t = ((m + tm - 1) / tm) * ((n + tn - 1) / tn);
   return t > kIntMax ? -1 : t;
 }
 
@@ -605,8 +699,8 @@ extern "C" int gemm_scatter_schedule(int64_t m, int64_t n, int world, int rank, 
   if (tiles < 0 || world < 1 || world > GEMM_SCATTER_WORLD_MAX || rank < 0 || rank >= world ||
       m % world != 0 || len < tiles)
     return rmsn_set_error(RMSN_ERR_SHAPE, "gemm_scatter_schedule: bad sizes, tile width, world or rank");
-  const gsc::Sched s =
-      gsc::make_sched((int)m, (int)n, resolve_tile_n(m, n, tile_n), world, rank);
+  const int tn = resolve_tile_n(m, n, tile_n);
+  const gsc::Sched s = gsc::make_sched((int)m, (int)n, resolve_tile_m(m, n, tn), tn, world, rank);
   for (int w = 0; w < s.tiles; ++w) {
     if (wg_tile) wg_tile[w] = gsc::tile_at(gsc::position_of_wg(w, s.tiles), s);
     if (pos_tile) pos_tile[w] = gsc::tile_at(w, s);
@@ -689,16 +783,24 @@ extern "C" int gemm_scatter_fwd(void* const* dst, int64_t ldd, int world, int ra
   p.alpha = alpha;
   p.beta = beta;
   p.vec_out = vec16 ? 2 : vec ? 1 : 0;
-  p.sched = gsc::make_sched((int)m, (int)n, tn, world, rank);
+  const int tm = resolve_tile_m(m, n, tn);
+  p.sched = gsc::make_sched((int)m, (int)n, tm, tn, world, rank);
 
   hipStream_t st = (hipStream_t)stream;
   const dim3 grid((unsigned)tiles);
   if (tn == gsc::BN) {
     const dim3 block(gsc::kThreads);
-    if (dtype == RMSN_BF16)
-      hipLaunchKernelGGL((gsc::gemm_wide_kernel<RMSN_BF16>), grid, block, 0, st, p);
-    else
-      hipLaunchKernelGGL((gsc::gemm_wide_kernel<RMSN_F16>), grid, block, 0, st, p);
+    const bool bf = dtype == RMSN_BF16;
+    if (tm == 192) {
+      if (bf) hipLaunchKernelGGL((gsc::gemm_wide192_kernel<RMSN_BF16>), grid, block, 0, st, p);
+      else hipLaunchKernelGGL((gsc::gemm_wide192_kernel<RMSN_F16>), grid, block, 0, st, p);
+    } else if (tm == 160) {
+      if (bf) hipLaunchKernelGGL((gsc::gemm_wide160_kernel<RMSN_BF16>), grid, block, 0, st, p);
+      else hipLaunchKernelGGL((gsc::gemm_wide160_kernel<RMSN_F16>), grid, block, 0, st, p);
+    } else {
+      if (bf) hipLaunchKernelGGL((gsc::gemm_wide_kernel<RMSN_BF16>), grid, block, 0, st, p);
+      else hipLaunchKernelGGL((gsc::gemm_wide_kernel<RMSN_F16>), grid, block, 0, st, p);
+    }
   } else {
     const dim3 block(gsc::kThreads);
     if (dtype == RMSN_BF16)

@@ -77,17 +77,17 @@ struct Sched {
   int local_group;   // tile-rows per group among the local chunk's
 };
 
-__host__ __device__ inline Sched make_sched(int m, int n, int tn, int world, int rank) {
+__host__ __device__ inline Sched make_sched(int m, int n, int tm, int tn, int world, int rank) {
   Sched s;
-  s.tiles_m = (m + BM - 1) / BM;
+  s.tiles_m = (m + tm - 1) / tm;
   s.tiles_n = (n + tn - 1) / tn;
   s.tiles = s.tiles_m * s.tiles_n;
   // A tile-row belongs to the chunk of its first row.  Rotated order starts
   // at the first tile-row of chunk rank + 1 (ring order), so the tile-rows
   // of the local chunk (rank) come last.
   const int64_t chunk_rows = world > 0 ? (int64_t)m / world : m;
-  const int64_t first_local = ((int64_t)rank * chunk_rows + BM - 1) / BM;
-  int64_t end_local = ((int64_t)(rank + 1) * chunk_rows + BM - 1) / BM;
+  const int64_t first_local = ((int64_t)rank * chunk_rows + tm - 1) / tm;
+  int64_t end_local = ((int64_t)(rank + 1) * chunk_rows + tm - 1) / tm;
   if (end_local > s.tiles_m) end_local = s.tiles_m;
   const int64_t local = end_local > first_local ? end_local - first_local : 0;
   s.tm_start = (int)(end_local >= s.tiles_m ? 0 : end_local);
@@ -199,6 +199,37 @@ __device__ __forceinline__ void settle_agprs(f32x4 (&acc)[8][8]) {
                  GSC_PIN(62), GSC_PIN(63));
 #undef GSC_PIN
 }
+
+// The same for the 8 x NY accumulators of a (16 NY) x 128 wave block, NY =
+// 8, 6 or 5 (tiles 256, 192 or 160 rows high).
+#define GSC_PIN(I) "+a"(acc[(I) / NY][(I) % NY])
+template <int NY>
+__device__ __forceinline__ void settle_agprs_rows(f32x4 (&acc)[8][NY]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+               : GSC_PIN(0), GSC_PIN(1), GSC_PIN(2), GSC_PIN(3), GSC_PIN(4), GSC_PIN(5), GSC_PIN(6),
+                 GSC_PIN(7), GSC_PIN(8), GSC_PIN(9), GSC_PIN(10), GSC_PIN(11), GSC_PIN(12), GSC_PIN(13),
+                 GSC_PIN(14), GSC_PIN(15));
+  asm volatile(""
+               : GSC_PIN(16), GSC_PIN(17), GSC_PIN(18), GSC_PIN(19), GSC_PIN(20), GSC_PIN(21), GSC_PIN(22),
+                 GSC_PIN(23), GSC_PIN(24), GSC_PIN(25), GSC_PIN(26), GSC_PIN(27), GSC_PIN(28), GSC_PIN(29),
+                 GSC_PIN(30), GSC_PIN(31));
+  if constexpr (NY == 5) {
+    asm volatile("" : GSC_PIN(32), GSC_PIN(33), GSC_PIN(34), GSC_PIN(35), GSC_PIN(36), GSC_PIN(37),
+                 GSC_PIN(38), GSC_PIN(39));
+  } else {
+    asm volatile(""
+                 : GSC_PIN(32), GSC_PIN(33), GSC_PIN(34), GSC_PIN(35), GSC_PIN(36), GSC_PIN(37), GSC_PIN(38),
+                   GSC_PIN(39), GSC_PIN(40), GSC_PIN(41), GSC_PIN(42), GSC_PIN(43), GSC_PIN(44), GSC_PIN(45),
+                   GSC_PIN(46), GSC_PIN(47));
+    if constexpr (NY == 8) {
+      asm volatile(""
+                   : GSC_PIN(48), GSC_PIN(49), GSC_PIN(50), GSC_PIN(51), GSC_PIN(52), GSC_PIN(53), GSC_PIN(54),
+                     GSC_PIN(55), GSC_PIN(56), GSC_PIN(57), GSC_PIN(58), GSC_PIN(59), GSC_PIN(60), GSC_PIN(61),
+                     GSC_PIN(62), GSC_PIN(63));
+    }
+  }
+}
+#undef GSC_PIN
 
 // The same for the 4 x 8 accumulators of a 128 x 64 wave block.
 __device__ __forceinline__ void settle_agprs(f32x4 (&acc)[4][8]) {

@@ -551,7 +551,7 @@ extern "C" int gemm_probe(int design, int mode, int nbuf, void* const* dst, int6
   p.alpha = 1.0f;
   p.beta = 0.0f;
   p.vec_out = vec16 ? 2 : vec8 ? 1 : 0;
-  p.sched = gsc::make_sched((int)m, (int)n, gsc::BN, world, 0);
+  p.sched = gsc::make_sched((int)m, (int)n, gsc::BM, gsc::BN, world, 0);
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)

@@ -491,22 +491,27 @@ def gemm_shapes_summary(argv) -> int:
     with open(md, "w") as f:
         f.write("# GEMM with the scatter epilogue across shapes (bf16)\n\n")
         f.write("Command: `python bench.py --gemm-shapes` (HIP events over back-to-back launches, "
-                "operands rotated over about 1 GiB; the library column is torch.matmul, i.e. "
-                "hipBLASLt's plain GEMM, on the same operands).  Output tiles of 256 rows by "
-                "256 or 128 columns, one workgroup each on 256 CUs; the automatic width takes "
-                "128-wide tiles only where they need no more rounds of 256 workgroups than "
-                "256-wide ones (include/gemm_scatter.h).\n\n")
-        f.write("| m | n | k | chunks | automatic width | tiles | kernel µs | TFLOP/s | "
-                "% of 2.5 PFLOP/s | 256-wide µs | 128-wide µs | hipBLASLt µs | "
-                "hipBLASLt TFLOP/s | kernel ÷ hipBLASLt |\n"
-                "|---|---|---|---|---|---|---|---|---|---|---|---|---|---|\n")
+                "operands rotated over about 1 GiB, 100 ms of warm-up, every tile shape and the "
+                "library timed round-robin over three rounds, median; the library column is "
+                "torch.matmul, i.e. hipBLASLt's plain GEMM, on the same operands).  One workgroup "
+                "per output tile on 256 CUs.  The automatic width takes 128-wide tiles only where "
+                "they need no more rounds of 256 workgroups than 256-wide ones; the 256-wide tiles "
+                "are 256, 192 or 160 rows high by an estimate of their rounds' cost "
+                "(include/gemm_scatter.h).  Every tile shape gives bitwise the same results.\n\n")
+        f.write("| m | n | k | chunks | automatic tile | tiles | kernel µs | TFLOP/s | "
+                "% of 2.5 PFLOP/s | 256x256 µs | 192x256 µs | 160x256 µs | 256x128 µs | "
+                "hipBLASLt µs | hipBLASLt TFLOP/s | kernel ÷ hipBLASLt |\n"
+                "|---|---|---|---|---|---|---|---|---|---|---|---|---|---|---|---|\n")
         for r in rows:
-            bw = r.get("by_tile_n", {})
-            wide = f"{bw['256']['us']:.1f}" if "256" in bw else "–"
-            narrow = f"{bw['128']['us']:.1f}" if "128" in bw else "–"
-            f.write(f"| {r['m']} | {r['n']} | {r['k']} | {r['world']} | {r.get('tile_n', 256)} | "
+            bt = r.get("by_tile", {})
+            if not bt and "by_tile_n" in r:   # lines of the earlier format (heights of 256 only)
+                bt = {f"256x{k}": v for k, v in r["by_tile_n"].items()}
+            cell = lambda key: f"{bt[key]['us']:.1f}" if key in bt else "–"
+            f.write(f"| {r['m']} | {r['n']} | {r['k']} | {r['world']} | "
+                    f"{r.get('tile_m', 256)}x{r.get('tile_n', 256)} | "
                     f"{r['tiles']} | {r['us']:.1f} | {r['tflops']:.0f} | "
-                    f"{100 * r['tflops'] / 2500:.1f} | {wide} | {narrow} | "
+                    f"{100 * r['tflops'] / 2500:.1f} | {cell('256x256')} | {cell('192x256')} | "
+                    f"{cell('160x256')} | {cell('256x128')} | "
                     f"{r['library_us']:.1f} | {r['library_tflops']:.0f} | "
                     f"{r['library_us'] / r['us']:.2f} |\n")
         f.write(f"\nKernel sources sha256: `{source_hash('gemm_scatter')}`\n")

@@ -3,7 +3,8 @@ exports what include/gemm_scatter.h declares, invalid arguments are rejected
 with the documented codes before any HIP call, and the tile schedule puts the
 other ranks' chunks first and the local chunk last (the order the oracle
 states), spreads each round of tiles over the eight XCDs in contiguous runs,
-and covers every tile exactly once, at either tile width."""
+and covers every tile exactly once, at either tile width and every tile
+height; the automatic width and height follow their documented rules."""
 from __future__ import annotations
 
 import ctypes
@@ -16,6 +17,7 @@ from tests.test_capi_cpu import FAKE, declared
 
 TM = B.GEMM_SCATTER_TILE_M
 WIDTHS = (B.GEMM_SCATTER_TILE_N, B.GEMM_SCATTER_TILE_N_NARROW)
+HEIGHTS = (256, 192, 160)   # of the 256-wide tiles
 
 
 def test_exports_every_declared_function():
@@ -29,10 +31,70 @@ def test_tile_count():
     f = B.lib().gemm_scatter_tiles
     assert f(4096, 8192, 256) == 16 * 32 and f(4096, 8192, 128) == 16 * 64
     assert f(4096, 8192, 0) == 16 * 32                  # 512 wide tiles: stays wide
-    assert f(1, 1, 256) == 1 and f(0, 5, 256) == 0 and f(257, 256, 256) == 2
-    assert f(256, 257, 256) == 2 and f(256, 257, 128) == 3 and f(256, 129, 128) == 2
+    assert f(256, 257, 128) == 3 and f(256, 129, 128) == 2
+    with B.gemm_tile_m(256):
+        assert f(1, 1, 256) == 1 and f(0, 5, 256) == 0 and f(257, 256, 256) == 2
+        assert f(256, 257, 256) == 2
+    with B.gemm_tile_m(160):
+        assert f(256, 257, 256) == 4 and f(320, 256, 256) == 2 and f(321, 256, 256) == 3
+        assert f(4096, 8192, 128) == 16 * 64            # the height applies to 256-wide tiles only
+    with B.gemm_tile_m(192):
+        assert f(1536, 8192, 256) == 8 * 32 and f(1537, 8192, 0) == 9 * 32
     assert f(-1, 4, 0) == -1 and f(4, 1 << 31, 0) == -1
     assert f(256, 256, 64) == -1 and f(256, 256, -1) == -1 and f(256, 256, 512) == -1
+
+
+def wide_cost(m: int, n: int, h: int) -> int:
+    """The header's estimate for 256-wide tiles h rows high, restated."""
+    t = -(-m // h) * -(-n // 256)
+    full, rem = divmod(t, 256)
+    rounds = 1000 * full + (700 + 300 * rem // 256 if rem else 0)
+    return rounds * (390 + 1000 * h // 256)
+
+
+def test_automatic_tile_height():
+    """256-wide tiles take the cheapest of 256, 192 and 160 rows by the
+    rounds estimate (ties to the taller tile); 128-wide tiles stay 256 rows.
+    The measured bf16 shapes (n = 8192, k = 3584) take the height that timed
+    fastest: 192 rows at 1536 and 3072 tokens, 160 at 2560, 256 elsewhere."""
+    h = B.gemm_scatter_tile_m
+    measured = {1536: 192, 2048: 256, 2560: 160, 3072: 192, 4096: 256, 5120: 256, 8192: 256,
+                16384: 256}
+    for m, height in measured.items():
+        assert B.gemm_scatter_tile_n(m, 8192) == 256 and h(m, 8192, 0) == height, m
+    assert h(1024, 8192, 0) == 256 and B.gemm_scatter_tile_n(1024, 8192) == 128
+    assert h(4096, 8192, 128) == 256 and h(4096, 4096, 0) == 256
+    assert h(-1, 5, 0) == -1 and h(5, 1 << 31, 0) == -1 and h(5, 5, 64) == -1
+
+    def rule(m, n):
+        costs = [(wide_cost(m, n, x), -x) for x in HEIGHTS]
+        return -min(costs)[1]
+
+    import random
+    rng = random.Random(6)
+    for _ in range(300):
+        m, n = rng.randint(1, 40000), rng.randint(1, 20000)
+        assert h(m, n, 256) == rule(m, n), (m, n)
+        t = h(m, n, 256)
+        assert B.gemm_scatter_tiles(m, n, 256) == -(-m // t) * -(-n // 256)
+
+
+def test_tune_forces_the_tile_height():
+    """gemm_scatter_tune(h) makes every later call use h-row 256-wide tiles
+    (queries, tile counts and schedules alike); 0 restores the automatic
+    height; other values are rejected and change nothing."""
+    try:
+        for x in HEIGHTS:
+            assert B.lib().gemm_scatter_tune(x) == 0
+            assert B.gemm_scatter_tile_m(4096, 8192, 0) == x
+            assert B.gemm_scatter_tile_m(1024, 8192, 0) == 256   # automatic width: 128-wide
+            assert B.gemm_scatter_tiles(4096, 8192, 256) == -(-4096 // x) * 32
+        assert B.lib().gemm_scatter_tune(128) == -2 and B.lib().gemm_scatter_tune(-1) == -2
+        assert B.gemm_scatter_tile_m(4096, 8192, 0) == 160           # unchanged by the rejected calls
+        assert B.lib().gemm_scatter_tune(0) == 0
+        assert B.gemm_scatter_tile_m(2560, 8192, 0) == 160 and B.gemm_scatter_tile_m(4096, 8192, 0) == 256
+    finally:
+        B.gemm_scatter_tune(0)
 
 
 def test_automatic_tile_width():
@@ -112,18 +174,25 @@ def test_error_codes():
 
 def tile_chunk(tile: int, m: int, n: int, world: int, width: int) -> int:
     tn = -(-n // width)
-    return ((tile // tn) * TM) // (m // world)
+    return ((tile // tn) * B.gemm_scatter_tile_m(m, n, width)) // (m // world)
 
 
 GROUP_ROWS = 8  # tile-rows per schedule group
 
 
-@pytest.mark.parametrize("width", WIDTHS)
+@pytest.mark.parametrize("shape", [(256, 256), (256, 128), (192, 256), (160, 256), (0, 256)],
+                         ids=lambda s: f"{s[0] or 'auto'}x{s[1]}")
 @pytest.mark.parametrize("m,n,world", [(4096, 8192, 8), (4096, 8192, 1), (8192, 4096, 8),
                                        (1024, 1024, 4), (777 * 8, 300, 8), (256, 256, 2),
                                        (2048, 2560, 16), (24576, 2048, 8), (4096, 8192, 2),
-                                       (1024, 8192, 8)])
-def test_schedule_is_remote_first_and_complete(m, n, world, width):
+                                       (1024, 8192, 8), (1536, 8192, 8), (2560, 8192, 8)])
+def test_schedule_is_remote_first_and_complete(m, n, world, shape):
+    height, width = shape
+    with B.gemm_tile_m(height):
+        check_schedule(m, n, world, width)
+
+
+def check_schedule(m, n, world, width):
     tiles = B.gemm_scatter_tiles(m, n, width)
     tn = -(-n // width)
     for rank in range(world):
@@ -149,10 +218,12 @@ def test_schedule_is_remote_first_and_complete(m, n, world, width):
             assert cols == sorted(cols)
 
 
-@pytest.mark.parametrize("width", WIDTHS)
-def test_workgroups_are_dealt_to_xcds_in_contiguous_runs(width):
+@pytest.mark.parametrize("shape", [(256, 256), (256, 128), (192, 256), (160, 256)],
+                         ids=lambda s: f"{s[0]}x{s[1]}")
+def test_workgroups_are_dealt_to_xcds_in_contiguous_runs(shape):
     m, n, world = 4096, 8192, 8
-    wg, pos = B.gemm_scatter_schedule(m, n, world, 3, width)
+    with B.gemm_tile_m(shape[0]):
+        wg, pos = B.gemm_scatter_schedule(m, n, world, 3, shape[1])
     at = {t: s for s, t in enumerate(pos)}
     positions = [at[t] for t in wg]
     rnd = 8 * 32
@@ -180,14 +251,19 @@ def test_schedule_random_shapes():
         n = rng.randint(1, 3000)
         rank = rng.randrange(world)
         width = rng.choice((0,) + WIDTHS)
-        tiles = B.gemm_scatter_tiles(m, n, width)
-        used = width or B.gemm_scatter_tile_n(m, n)
-        tn = -(-n // used)
-        wg, pos = B.gemm_scatter_schedule(m, n, world, rank, width)
+        B.gemm_scatter_tune(rng.choice((0,) + HEIGHTS))
+        try:
+            tiles = B.gemm_scatter_tiles(m, n, width)
+            used = width or B.gemm_scatter_tile_n(m, n)
+            tn = -(-n // used)
+            wg, pos = B.gemm_scatter_schedule(m, n, world, rank, width)
+            seq_chunks = [tile_chunk(t, m, n, world, used) for t in pos]
+        finally:
+            B.gemm_scatter_tune(0)
         assert sorted(wg) == list(range(tiles)) == sorted(pos)
         order = oracle.gemm_scatter_chunk_order(world, rank)
         rank_of = {q: i for i, q in enumerate(order)}
-        seq = [rank_of[tile_chunk(t, m, n, world, used)] for t in pos]
+        seq = [rank_of[q] for q in seq_chunks]
         local = [i for i, q in enumerate(seq) if q == world - 1]
         assert not local or local == list(range(tiles - len(local), tiles)), (m, n, world, rank)
         remote = seq[:tiles - len(local)]

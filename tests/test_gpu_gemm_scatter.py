@@ -38,6 +38,9 @@ P_BITS = {"bf16": 8, "f16": 11}
 TINY = {"bf16": 2.0 ** -126, "f16": 2.0 ** -14}
 GUARD = 0x7E5A  # a NaN pattern in both formats: never a computed value here
 WIDTHS = (B.GEMM_SCATTER_TILE_N, B.GEMM_SCATTER_TILE_N_NARROW)
+# every tile shape (rows, columns): the 256-wide tiles at each height, and
+# the 128-wide ones
+TILES = ((256, 256), (192, 256), (160, 256), (256, 128))
 
 
 def say(*a):
@@ -48,19 +51,22 @@ def st(t: torch.Tensor) -> np.ndarray:
     return I.to_storage(t)
 
 
-def run(a, b, c, alpha, beta, world, rank=0, ldd_pad=0, flags=None, epoch=0, col=4, tile_n=0):
+def run(a, b, c, alpha, beta, world, rank=0, ldd_pad=0, flags=None, epoch=0, col=4, tile_n=0,
+        tile_m=0):
     """Launch into guarded chunk buffers; returns (assembled [m, n] storage,
     the raw buffer).  Each chunk sits at column ``col`` of a [rows + 2,
     n + ldd_pad + 8 + col] block whose first and last rows and other columns
     are guards.  col = 8 with a row pitch that is a multiple of 8 elements
-    gives 16-byte aligned rows (the staged tile stores); col = 4, 8-byte."""
+    gives 16-byte aligned rows (the staged tile stores); col = 4, 8-byte.
+    tile_m forces the height of 256-wide tiles (0: automatic)."""
     m, n = a.shape[0], b.shape[0]
     rows = m // world
     width = n + ldd_pad + 8 + col
     buf = torch.full((world, rows + 2, width), GUARD, dtype=torch.int16, device=DEV)
     bufv = buf.view(a.dtype)
     dst = [bufv[q, 1:rows + 1, col:col + n] for q in range(world)]
-    B.gemm_scatter_fwd(dst, a, b, c, alpha, beta, rank, flags, epoch, tile_n=tile_n)
+    with B.gemm_tile_m(tile_m):
+        B.gemm_scatter_fwd(dst, a, b, c, alpha, beta, rank, flags, epoch, tile_n=tile_n)
     torch.cuda.synchronize()
     host = buf.cpu()
     inner = host[:, 1:rows + 1, col:col + n]
@@ -138,24 +144,24 @@ SHAPES = [  # m, n, k, world, with_c
 @pytest.mark.parametrize("shape", SHAPES, ids=[f"{s[0]}x{s[1]}x{s[2]}w{s[3]}{'c' if s[4] else ''}"
                                                for s in SHAPES])
 def test_parity(dtype, shape):
-    """Each shape at both tile widths, with 8-byte and with 16-byte aligned
-    output rows (the interior tiles of the latter take the LDS-staged
-    stores)."""
+    """Each shape at every tile shape (both widths, the 256-wide tiles at
+    each height), with 8-byte and with 16-byte aligned output rows (the
+    interior tiles of the latter take the LDS-staged stores)."""
     m, n, k, world, with_c = shape
     a, b, c = make(dtype, m, n, k, with_c, seed=m + n + k)
     alpha, beta = (0.5, -1.25) if with_c else (1.0, 0.0)
     want, y, mag = oracle_rows(a, b, c, alpha, beta, world, dtype)
     first = None
-    for tile_n in WIDTHS:
+    for tile_m, tile_n in TILES:
         for col, pad in ((4, 0), (8, (-(n + 16)) % 8)):
             say(f"[gpu] gemm_scatter {dtype} m={m} n={n} k={k} world={world} c={with_c} "
-                f"col={col} tile_n={tile_n}")
+                f"col={col} tile {tile_m}x{tile_n}")
             got, _ = run(a, b, c, alpha, beta, world, rank=world - 1, ldd_pad=pad, col=col,
-                         tile_n=tile_n)
-            compare(got, want, y, mag, k, dtype, f"{dtype} {shape} col {col} tile_n {tile_n}")
+                         tile_n=tile_n, tile_m=tile_m)
+            compare(got, want, y, mag, k, dtype, f"{dtype} {shape} col {col} tile {tile_m}x{tile_n}")
             if first is None:
                 first = got
-            assert np.array_equal(got, first), "tile widths or store paths differ"
+            assert np.array_equal(got, first), "tile shapes or store paths differ"
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
@@ -167,20 +173,21 @@ def test_k_around_whole_steps(dtype):
     The wide kernel loads up to two steps ahead into a ring of five operand
     slots, so k from one step to seven whole steps (and one past) covers
     every way the ring's prologue and its two loops split.  Ragged and whole
-    tiles, both widths against the oracle and bitwise equal to each other."""
+    tiles, every tile shape against the oracle and bitwise equal to each
+    other."""
     for m, n, world in ((264, 520, 2), (512, 512, 4)):
         for k in (8, 56, 64, 72, 120, 128, 136, 184, 192, 200, 256, 264, 320, 384, 448, 456):
             a, b, c = make(dtype, m, n, k, False, seed=k + m)
             want, y, mag = oracle_rows(a, b, c, 1.0, 0.0, world, dtype)
             first = None
-            for tile_n in WIDTHS:
-                say(f"[gpu] k steps {dtype} m={m} n={n} k={k} tile_n={tile_n}")
+            for tile_m, tile_n in TILES:
+                say(f"[gpu] k steps {dtype} m={m} n={n} k={k} tile {tile_m}x{tile_n}")
                 got, _ = run(a, b, c, 1.0, 0.0, world, ldd_pad=(-(n + 16)) % 8, col=8,
-                             tile_n=tile_n)
-                compare(got, want, y, mag, k, dtype, f"{dtype} {m}x{n}x{k} tile_n {tile_n}")
+                             tile_n=tile_n, tile_m=tile_m)
+                compare(got, want, y, mag, k, dtype, f"{dtype} {m}x{n}x{k} tile {tile_m}x{tile_n}")
                 if first is None:
                     first = got
-                assert np.array_equal(got, first), f"tile widths differ at k = {k}"
+                assert np.array_equal(got, first), f"tile shapes differ at k = {k}"
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
@@ -188,10 +195,11 @@ def test_strided_operands(dtype):
     """Row strides wider than the rows for A, B, C and the output (one odd,
     which takes the element-wise store path)."""
     m, n, k, world = 384, 264, 200, 4
-    for (ldd_pad, ldc_pad), tile_n in zip(((8, 3), (3, 8), (8, 8), (3, 3)), WIDTHS * 2):
-        say(f"[gpu] strided {dtype} ldd_pad={ldd_pad} ldc_pad={ldc_pad} tile_n={tile_n}")
+    for (ldd_pad, ldc_pad), (tile_m, tile_n) in zip(((8, 3), (3, 8), (8, 8), (3, 3)), TILES):
+        say(f"[gpu] strided {dtype} ldd_pad={ldd_pad} ldc_pad={ldc_pad} tile {tile_m}x{tile_n}")
         a, b, c = make(dtype, m, n, k, True, seed=7, lda_pad=8, ldb_pad=24, ldc_pad=ldc_pad)
-        got, _ = run(a, b, c, 1.5, 0.75, world, rank=1, ldd_pad=ldd_pad, tile_n=tile_n)
+        got, _ = run(a, b, c, 1.5, 0.75, world, rank=1, ldd_pad=ldd_pad, tile_n=tile_n,
+                     tile_m=tile_m)
         want, y, mag = oracle_rows(a, b, c, 1.5, 0.75, world, "bf16" if dtype == "bf16" else "f16")
         compare(got, want, y, mag, k, dtype, f"strided {dtype} {ldd_pad}/{ldc_pad}")
 
@@ -218,22 +226,24 @@ def test_k_zero_gives_beta_c():
     compare(got, want, y, mag, 0, "bf16", "k = 0", min_exact=1.0)
 
 
-@pytest.mark.parametrize("tile_n", (0,) + WIDTHS)
-def test_flags_epoch_and_rank_independence(tile_n):
+@pytest.mark.parametrize("tile_m,tile_n", ((0, 0),) + TILES, ids=lambda v: str(v))
+def test_flags_epoch_and_rank_independence(tile_m, tile_n):
     """Every tile's flag gets the epoch (slots past the tiles stay as they
     were), and the values do not depend on the rank (only the order of the
     tiles does)."""
     m, n, k, world = 1024, 768, 192, 8
     a, b, c = make("bf16", m, n, k, False, seed=11)
-    tiles = B.gemm_scatter_tiles(m, n, tile_n)
+    with B.gemm_tile_m(tile_m):
+        tiles = B.gemm_scatter_tiles(m, n, tile_n)
     flags = torch.full((tiles + 5,), 3, dtype=torch.int32, device=DEV)
-    say(f"[gpu] flags tile_n={tile_n} tiles={tiles}")
-    ref, _ = run(a, b, None, 1.0, 0.0, world, rank=0, flags=flags, epoch=41, tile_n=tile_n)
+    say(f"[gpu] flags tile {tile_m}x{tile_n} tiles={tiles}")
+    ref, _ = run(a, b, None, 1.0, 0.0, world, rank=0, flags=flags, epoch=41, tile_n=tile_n,
+                 tile_m=tile_m)
     f = flags.cpu()
     assert bool((f[:tiles] == 41).all()) and bool((f[tiles:] == 3).all())
     for rank in (3, 7):
         got, _ = run(a, b, None, 1.0, 0.0, world, rank=rank, flags=flags, epoch=42 + rank,
-                     tile_n=tile_n)
+                     tile_n=tile_n, tile_m=tile_m)
         assert np.array_equal(got, ref), rank
         assert bool((flags.cpu()[:tiles] == 42 + rank).all())
 
@@ -241,8 +251,8 @@ def test_flags_epoch_and_rank_independence(tile_n):
 @pytest.mark.parametrize("name", list(GEMM_WORKLOADS))
 def test_full_size_sampled(name):
     """The benchmark's workload at full size, in the benchmark's launch:
-    sampled rows of every chunk against the oracle, and a second launch
-    bitwise equal to the first."""
+    sampled rows of every chunk against the oracle, a second launch bitwise
+    equal to the first, and every other tile shape bitwise equal too."""
     w = GEMM_WORKLOADS[name]
     say(f"[gpu] full size {w.describe()} (tile width {B.gemm_scatter_tile_n(w.m, w.n)})")
     d = I.gemm_inputs(w)
@@ -253,9 +263,10 @@ def test_full_size_sampled(name):
     assert np.array_equal(got, again), "two launches differ"
     other, _ = run(a, b, c, w.alpha, w.beta, w.world, rank=w.rank, col=4)
     assert np.array_equal(got, other), "staged and direct stores differ"
-    for tile_n in WIDTHS:
-        wide, _ = run(a, b, c, w.alpha, w.beta, w.world, rank=w.rank, col=8, tile_n=tile_n)
-        assert np.array_equal(got, wide), f"tile width {tile_n} differs"
+    for tile_m, tile_n in TILES:
+        other, _ = run(a, b, c, w.alpha, w.beta, w.world, rank=w.rank, col=8, tile_n=tile_n,
+                       tile_m=tile_m)
+        assert np.array_equal(got, other), f"tile {tile_m}x{tile_n} differs"
     chunk = w.m // w.world
     rows = sorted({q * chunk + off for q in range(w.world) for off in (0, chunk // 2 + 3)}
                   | {w.m - 1, 255, 256})
@@ -367,9 +378,11 @@ def test_random_calls():
         col = int(rng.choice([4, 8]))
         pad = (-(n + 8 + col)) % 8 if col == 8 else int(rng.integers(0, 4))
         tile_n = int(rng.choice((0,) + WIDTHS))
+        tile_m = int(rng.choice((0, 256, 192, 160)))
         say(f"[gpu] random #{i}: {dtype} m={m} n={n} k={k} world={world} rank={rank} "
-            f"c={with_c} col={col} tile_n={tile_n}")
-        got, _ = run(a, b, c, alpha, beta, world, rank=rank, ldd_pad=pad, col=col, tile_n=tile_n)
+            f"c={with_c} col={col} tile_n={tile_n} tile_m={tile_m}")
+        got, _ = run(a, b, c, alpha, beta, world, rank=rank, ldd_pad=pad, col=col, tile_n=tile_n,
+                     tile_m=tile_m)
         want, y, mag = oracle_rows(a, b, c, alpha, beta, world, dtype)
         compare(got, want, y, mag, k, dtype, f"random #{i}", min_exact=0.6)
 
@@ -442,8 +455,8 @@ def test_graph_capture_gemm_then_add_rmsnorm():
 def test_operand_offsets_past_4gib():
     """A of 65536 x 33280 bf16 (4.36 GB, drawn on the device): rows whose
     byte offset passes 2^31 and 2^32, in every chunk, against the oracle row
-    by row (each row's values do not depend on the chunk split), at both tile
-    widths, which must agree bit for bit."""
+    by row (each row's values do not depend on the chunk split), at every
+    tile shape, which must agree bit for bit."""
     m, n, k, world = 65536, 264, 33280, 8
     chunk = m // world
     w = I.case("bf16", m, k, 1, seed=71, std=1.0)
@@ -452,11 +465,11 @@ def test_operand_offsets_past_4gib():
     assert a.numel() * 2 > 1 << 32
     say(f"[gpu] offsets past 4 GiB: A {tuple(a.shape)}, {a.numel() * 2 / 2**30:.2f} GiB")
     got = None
-    for tile_n in WIDTHS:
-        g, _ = run(a, b, None, 1.0, 0.0, world, rank=3, col=8, tile_n=tile_n)
+    for tile_m, tile_n in TILES:
+        g, _ = run(a, b, None, 1.0, 0.0, world, rank=3, col=8, tile_n=tile_n, tile_m=tile_m)
         if got is None:
             got = g
-        assert np.array_equal(g, got), f"tile width {tile_n} differs"
+        assert np.array_equal(g, got), f"tile {tile_m}x{tile_n} differs"
     row_bytes = k * 2
     rows = sorted({0, chunk - 1, chunk, (1 << 31) // row_bytes, (1 << 31) // row_bytes + 1,
                    (1 << 32) // row_bytes + 1, m - 2, m - 1})
