@@ -389,7 +389,8 @@ def test_random_calls():
 
 def test_graph_capture_gemm_then_add_rmsnorm():
     """The reduce-scatter pipeline captured in one HIP graph: four emulated
-    ranks' GEMMs (both tile widths, one with tile flags) scatter into receive
+    ranks' GEMMs (both tile widths and a forced height, one with tile flags)
+    scatter into receive
     buffers, then every receiving rank sums its four chunks with its residual
     and normalises (add_rmsnorm_fwd, K = 4).  Each replay, with eager resets
     and poisoning in between, equals the eager run bit for bit, flags
@@ -397,15 +398,16 @@ def test_graph_capture_gemm_then_add_rmsnorm():
     world, m, n, k = 4, 512, 1024, 256
     chunk = m // world
     ops = [make("bf16", m, n, k, False, seed=300 + r)[:2] for r in range(world)]
-    widths = [0, 256, 128, 0]
+    shapes = [(0, 0), (0, 256), (0, 128), (192, 256)]      # (tile height, tile width)
     res0 = I.matrix(31, I.RESIDUAL_ID, m, n, 1.0, "bf16").to(DEV)
     gam = I.matrix(31, I.GAMMA_ID, 1, n, 0.25, "bf16").reshape(n).to(DEV) + 1.0
-    tiles = B.gemm_scatter_tiles(m, n, widths[1])
+    tiles = B.gemm_scatter_tiles(m, n, shapes[1][1])
 
     def step(recv, res, out, flags):
-        for r, ((a, b), tn) in enumerate(zip(ops, widths)):
-            B.gemm_scatter_fwd([recv[q, r] for q in range(world)], a, b, rank=r, tile_n=tn,
-                               flags=flags if r == 1 else None, epoch=77)
+        for r, ((a, b), (tm, tn)) in enumerate(zip(ops, shapes)):
+            with B.gemm_tile_m(tm):
+                B.gemm_scatter_fwd([recv[q, r] for q in range(world)], a, b, rank=r, tile_n=tn,
+                                   flags=flags if r == 1 else None, epoch=77)
         for q in range(world):
             B.add_rmsnorm_fwd(out[q], res[q], [recv[q, r] for r in range(world)], gam, 1e-5)
 

@@ -51,7 +51,7 @@ def test_soak_rmsnorm():
 def test_soak_gemm_scatter():
     """GEMM with the scatter epilogue: dtype, ragged m, n and k (k from 0),
     world 1-16 and rank, alpha, beta, optional C, padded strides, both
-    output alignments and every tile width."""
+    output alignments, every tile width and every tile height."""
     rng = np.random.default_rng(GEMM_SEED)
     for i in range(GEMM_CASES):
         dtype = str(rng.choice(["bf16", "f16"]))
@@ -71,10 +71,12 @@ def test_soak_gemm_scatter():
         col = int(rng.choice([4, 8]))
         pad = (-(n + 8 + col)) % 8 if col == 8 else int(rng.integers(0, 4))
         tile_n = int(rng.choice((0,) + G.WIDTHS))
+        tile_m = int(rng.choice((0, 256, 192, 160)))
         what = (f"gemm soak #{i} ({dtype} m={m} n={n} k={k} world={world} rank={rank} "
-                f"c={with_c} col={col} tile_n={tile_n})")
+                f"c={with_c} col={col} tile_n={tile_n} tile_m={tile_m})")
         say(f"[gpu] {what}")
-        got, _ = G.run(a, b, c, alpha, beta, world, rank=rank, ldd_pad=pad, col=col, tile_n=tile_n)
+        got, _ = G.run(a, b, c, alpha, beta, world, rank=rank, ldd_pad=pad, col=col, tile_n=tile_n,
+                       tile_m=tile_m)
         want, y, mag = G.oracle_rows(a, b, c, alpha, beta, world, dtype)
         G.compare(got, want, y, mag, k, dtype, what, min_exact=0.5)
 
