@@ -437,15 +437,24 @@ def block_all_reduce_sum(x: torch.Tensor) -> torch.Tensor:
 
 # GEMM with a reduce-scatter epilogue -----------------------------------------
 
+def matrix_ld(shape, strides, what: str = "matrix") -> int:
+    """Row stride in elements of a 2-D [rows, cols] layout whose elements
+    are contiguous within a row.  The tensor's own stride is passed on as it
+    is, so that rows which overlap or repeat (a broadcast view has stride 0)
+    meet the library's check that a stride is at least a row long, instead of
+    being read as if they were distinct rows; a single row's stride does not
+    matter and is given as its length."""
+    if len(shape) != 2 or (shape[1] > 1 and strides[1] != 1):
+        raise RmsnormError(-2, f"{what} must be 2-D with contiguous rows")
+    return strides[0] if shape[0] > 1 else shape[1]
+
+
 def _matrix(t: torch.Tensor, what: str):
     """(pointer, row stride in elements) of a 2-D device tensor whose
     elements are contiguous within a row."""
     if not t.is_cuda:
         raise RmsnormError(-1, f"{what} must be a device tensor")
-    if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
-        raise RmsnormError(-2, f"{what} must be 2-D with contiguous rows")
-    ld = t.stride(0) if t.shape[0] > 1 else t.shape[1]
-    return t.data_ptr(), max(ld, t.shape[1])
+    return t.data_ptr(), matrix_ld(tuple(t.shape), t.stride(), what)
 
 
 def gemm_scatter_tile_n(m: int, n: int) -> int:
@@ -504,6 +513,8 @@ def gemm_scatter_fwd(dst: Sequence[torch.Tensor], a: torch.Tensor, b: torch.Tens
     per finished tile."""
     if a.dtype not in (torch.float16, torch.bfloat16):
         raise RmsnormError(-3, f"unsupported dtype {a.dtype}")
+    if a.dim() != 2:
+        raise RmsnormError(-2, "a must be 2-D")
     world = len(dst)
     m, k = a.shape
     n = b.shape[0]

@@ -57,6 +57,7 @@
 #include <stdio.h>
 #include <stdlib.h>
 
+#include <atomic>
 #include <type_traits>
 
 #include "../../include/gemm_scatter.h"
@@ -628,7 +629,7 @@ int resolve_tile_n(int64_t m, int64_t n, int tile_n) {
 }
 
 // forced height of the 256-wide tiles (gemm_scatter_tune); 0: automatic
-int g_tile_m = 0;
+std::atomic<int> g_tile_m{0};
 
 // Estimated time of the 256-wide tiles at height h, in arbitrary units:
 // rounds of workgroups, a partial round counting 0.7 + 0.3 f of a full one
@@ -651,7 +652,8 @@ int64_t wide_cost(int64_t m, int64_t n, int h) {
 // wide_cost (ties to the taller tile)
 int resolve_tile_m(int64_t m, int64_t n, int tn) {
   if (tn != gsc::BN) return gsc::BM;
-  if (g_tile_m) return g_tile_m;
+  const int forced = g_tile_m.load(std::memory_order_relaxed);
+  if (forced) return forced;
   int best = gsc::BM;
   int64_t best_cost = wide_cost(m, n, gsc::BM);
   for (int h : {192, 160}) {
@@ -680,7 +682,7 @@ extern "C" int gemm_scatter_tile_m(int64_t m, int64_t n, int tile_n) {
 extern "C" int gemm_scatter_tune(int tile_m) {
   if (tile_m != 0 && tile_m != 256 && tile_m != 192 && tile_m != 160)
     return rmsn_set_error(RMSN_ERR_SHAPE, "gemm_scatter_tune: tile_m must be 0, 256, 192 or 160");
-  g_tile_m = tile_m;
+  g_tile_m.store(tile_m, std::memory_order_relaxed);
   return RMSN_OK;
 }
 

@@ -240,6 +240,25 @@ def test_binding_checks_shapes_before_the_library():
         B.gemm_scatter_fwd([a[:4], a[4:]], a, a.to(torch.float16))
 
 
+def test_binding_passes_the_real_row_stride():
+    """A broadcast or overlapping operand keeps its short row stride, which
+    the library rejects, instead of being described as distinct rows."""
+    import torch
+    base = torch.empty(1, 64, dtype=torch.bfloat16)
+    assert B.matrix_ld(tuple(base.expand(128, 64).shape), base.expand(128, 64).stride()) == 0
+    assert B.matrix_ld((128, 64), (64, 1)) == 64
+    assert B.matrix_ld((128, 64), (72, 1)) == 72          # padded rows
+    assert B.matrix_ld((128, 64), (32, 1)) == 32          # overlapping rows, rejected below
+    assert B.matrix_ld((1, 64), (0, 1)) == 64             # one row: its own length
+    assert B.matrix_ld((128, 0), (1, 1)) == 1
+    for shape, strides in (((128, 64), (64, 2)), ((8, 8, 8), (64, 8, 1)), ((64,), (1,))):
+        with pytest.raises(B.RmsnormError):
+            B.matrix_ld(shape, strides)
+    # the library turns such strides away before any launch
+    assert call(lda=0) == -2 and call(ldb=0) == -2 and call(ldd=0) == -2
+    assert call(lda=32) == -2
+
+
 def test_schedule_random_shapes():
     """Seeded random shapes: every schedule is a permutation, the local chunk
     runs last, and the other chunks keep ring order group by group."""

@@ -218,6 +218,23 @@ def test_empty_products_launch_nothing():
     assert bool((sentinel == 7.0).all())
 
 
+def test_broadcast_operands_are_rejected():
+    """A broadcast operand (row stride 0) or output rows that overlap are
+    turned away before any launch; the output is untouched."""
+    row = torch.ones(1, 64, dtype=torch.bfloat16, device=DEV)
+    b = torch.ones(128, 64, dtype=torch.bfloat16, device=DEV)
+    sentinel = torch.full((64, 128), 7.0, dtype=torch.bfloat16, device=DEV)
+    dst = [sentinel[:32], sentinel[32:]]
+    for a_, b_ in ((row.expand(64, 64), b), (b[:64], row.expand(128, 64))):
+        with pytest.raises(B.RmsnormError):
+            B.gemm_scatter_fwd(dst, a_, b_)
+    out_row = torch.empty(1, 128, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(B.RmsnormError):
+        B.gemm_scatter_fwd([out_row.expand(32, 128)] * 2, b[:64], b)
+    torch.cuda.synchronize()
+    assert bool((sentinel == 7.0).all())
+
+
 def test_k_zero_gives_beta_c():
     a, b, c = make("bf16", 300, 200, 0, True, seed=3)
     say("[gpu] k = 0")
