@@ -372,7 +372,7 @@ def report_summary(argv) -> int:
         if gemm_rows:
             f.write("\nGEMM with the reduce-scatter epilogue (bound by the matrix cores; the "
                     "library column is hipBLASLt's plain GEMM on the same rotated operands; parity "
-                    "from `tests/test_gpu_gemm_scatter.py -k full_size`, sampled rows of every "
+                    "from `tests/test_gpu_gemm_scatter.py -k full_size`, every row of every "
                     "chunk):\n\n| workload | GPU µs/step | TFLOP/s | % of 2.5 PFLOP/s | hipBLASLt "
                     "µs | oracle TFLOP/s (cores) | oracle TFLOP/s, 1 core | GPU ÷ oracle | parity "
                     "|\n|---|---|---|---|---|---|---|---|---|\n")
@@ -383,7 +383,9 @@ def report_summary(argv) -> int:
                 st = stats.get(w, {})
                 par = (f"error / bound max {st['max_error_over_bound']:.2g}, "
                        f"{100 * st['min_equal_frac']:.2f}%+ equal to the oracle's rounding "
-                       f"({st['rows_checked']} rows)" if "max_error_over_bound" in st
+                       f"({st['rows_checked']} rows"
+                       + (f", {st['elements_checked']:,} elements)" if "elements_checked" in st else ")")
+                       if "max_error_over_bound" in st
                        else "see tests")
                 lib = r.get("library_context", {})
                 f.write(f"| {w} | {r['ms_per_step'] * 1e3:.2f} | {r['value']:.1f} | "
