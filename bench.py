@@ -696,7 +696,10 @@ DESIGN_NAMES = {0: "one row per workgroup, residual stored before the reduction"
                 1: "one row per workgroup, residual stored after the reduction",
                 2: "one row per workgroup, rows in contiguous eighths per XCD",
                 3: "persistent, next row's loads issued before this row's work",
-                4: "two rows per 1024-lane workgroup"}
+                4: "two rows per 1024-lane workgroup",
+                5: "phased: two rows per wave, all loads before any store",
+                6: "phased: four rows per wave, all loads before any store",
+                7: "phased: one row per wave, all loads before any store"}
 
 
 def design_sweep(a) -> int:
@@ -754,6 +757,10 @@ def design_sweep(a) -> int:
         for l, s_ in pols:
             if s_ in (2, 19):
                 variants[(3, DESIGN_NAMES[3], f"{l}/{s_}", grid)] = probe(3, l, s_, grid)
+    for d, per in ((5, 8), (6, 16), (7, 4)):
+        for l, s_ in pols:
+            grid = -(-rows // per)
+            variants[(d, DESIGN_NAMES[d], f"{l}/{s_}", grid)] = probe(d, l, s_, grid)
 
     def ulps(t):
         i = t.view(torch.int16).int()

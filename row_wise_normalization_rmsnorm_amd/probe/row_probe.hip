@@ -22,6 +22,13 @@
 //      next row's loads before it reduces and stores the current one (two
 //      register sets used in turn, so no load in flight is copied);
 //   4  two rows per 1024-lane workgroup.
+//   5, 6, 7  phased: each wave owns 2, 4 or 1 consecutive rows (256-lane
+//      workgroups, grid = rows / (4 * rows per wave)); lane l holds chunks
+//      l, l + 64, ..., l + 448 of each row.  The wave loads and sums all its
+//      rows, keeping the rounded residual in registers, before it stores
+//      any, so that when every wave of the launch is resident at once
+//      (8192 rows: 4096 waves at two rows, 16 per CU) nearly all of the
+//      launch's reads come before nearly all of its writes.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -188,6 +195,85 @@ __global__ __launch_bounds__(1024) void two_row_kernel(Args a) {
   }
 }
 
+// designs 5-7.  The loads run two steps ahead of the sums, S chunks of each
+// input per step (S = 1, 2, 4 for 1, 2, 4 rows per wave); scheduling
+// barriers keep the compiler from hoisting every load of the wave to the
+// top, which would need more registers than the wave count allows.
+template <int LP, int SP, int RPW>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RPW == 1 ? 8 : 8 / RPW)))
+void phased_kernel(Args a) {
+  constexpr int C = kChunks / 64;          // chunks of a row per lane
+  constexpr int S = RPW;                   // chunks per input per step
+  constexpr int T = RPW * C / S;           // steps
+  const int lane = threadIdx.x & 63;
+  const int64_t row0 =
+      ((int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) * RPW;
+  u32x4 rn[RPW][C];
+  float tot[RPW];
+  u32x4 xv[2][S], rv[2][S];
+  auto load = [&](int t) {
+    const int i = t * S / C, j0 = t * S % C;
+    const auto xr = row_of(a.x, row0 + i, a.rows), rr = row_of(a.r, row0 + i, a.rows);
+#pragma unroll
+    for (int q = 0; q < S; ++q) {
+      xv[t & 1][q] = ld<LP>(xr, lane + 64 * (j0 + q));
+      rv[t & 1][q] = ld<LP>(rr, lane + 64 * (j0 + q));
+    }
+  };
+  float ss = 0.0f;
+  load(0);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    if (t + 1 < T) load(t + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    const int i = t * S / C, j0 = t * S % C;
+#pragma unroll
+    for (int q = 0; q < S; ++q) {
+      IV::raw_t xw, rw;
+      xw.w[0] = xv[t & 1][q];
+      rw.w[0] = rv[t & 1][q];
+      float acc[8], u[8], v[8];
+      IV::unpack(xw, acc);
+      IV::unpack(rw, u);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += u[e];
+      const IV::raw_t p = IV::pack(acc);
+      rn[i][j0 + q] = p.w[0];
+      IV::unpack(p, v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(v[e], v[e], ss);
+    }
+    if (j0 + S == C) {
+      tot[i] = rmsn::wave_reduce(ss);
+      ss = 0.0f;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // The residual words pass through an empty asm statement so that the
+  // compiler re-expands them here instead of keeping the phase-1 fp32 copies
+  // (twice the registers) alive across the loads.
+#pragma unroll
+  for (int i = 0; i < RPW; ++i)
+#pragma unroll
+    for (int j = 0; j < C; ++j) asm volatile("" : "+v"(rn[i][j]));
+#pragma unroll
+  for (int i = 0; i < RPW; ++i) {
+    const float inv = rmsn::row_scale(tot[i], kHidden, a.eps);
+    const auto rr = row_of(a.r, row0 + i, a.rows), orr = row_of(a.out, row0 + i, a.rows);
+#pragma unroll
+    for (int j = 0; j < C; ++j) {
+      st<SP>(rr, lane + 64 * j, rn[i][j]);
+      float g[8], v[8];
+      IV::unpack(IV::load<false>(a.gamma, lane + 64 * j), g);
+      IV::raw_t w;
+      w.w[0] = rn[i][j];
+      IV::unpack(w, v);
+      st<SP>(orr, lane + 64 * j, normalise(v, inv, g));
+    }
+  }
+}
+
 template <int LP, int SP>
 int launch(int design, int grid, const Args& a, hipStream_t s) {
   switch (design) {
@@ -196,6 +282,9 @@ int launch(int design, int grid, const Args& a, hipStream_t s) {
     case 2: hipLaunchKernelGGL((one_row_kernel<LP, SP, false, true>), dim3(grid), dim3(512), 0, s, a); break;
     case 3: hipLaunchKernelGGL((persistent_kernel<LP, SP>), dim3(grid), dim3(512), 0, s, a); break;
     case 4: hipLaunchKernelGGL((two_row_kernel<LP, SP>), dim3(grid), dim3(1024), 0, s, a); break;
+    case 5: hipLaunchKernelGGL((phased_kernel<LP, SP, 2>), dim3(grid), dim3(256), 0, s, a); break;
+    case 6: hipLaunchKernelGGL((phased_kernel<LP, SP, 4>), dim3(grid), dim3(256), 0, s, a); break;
+    case 7: hipLaunchKernelGGL((phased_kernel<LP, SP, 1>), dim3(grid), dim3(256), 0, s, a); break;
     default: return -1;
   }
   return hipGetLastError() == hipSuccess ? 0 : -7;
@@ -215,8 +304,9 @@ extern "C" int row_probe_policies(int* loads, int* stores, int max) {
   return n;
 }
 
-// grid: workgroups (designs 0-2: rows; 4: rows / 2; 3: any).  rows must be a
-// multiple of 8 for design 2 and of 2 for design 4.  Returns 0, -1 for a
+// grid: workgroups (designs 0-2: rows; 4: rows / 2; 3: any; 5, 6, 7: rows /
+// 8, rows / 16, rows / 4, rounded up).  rows must be a multiple of 8 for
+// design 2 and of 2 for design 4.  Returns 0, -1 for a
 // design, policy or shape the probe does not have, -7 for a launch error.
 extern "C" int row_probe(int design, int load_cpol, int store_cpol, int grid, const void* x,
                          void* r, void* out, const void* gamma, int64_t rows, float eps,
@@ -225,6 +315,10 @@ extern "C" int row_probe(int design, int load_cpol, int store_cpol, int grid, co
   if ((design == 0 || design == 1 || design == 2) && grid != rows) return -1;
   if (design == 2 && rows % 8) return -1;
   if (design == 4 && (rows % 2 || grid != rows / 2)) return -1;
+  if (design >= 5 && design <= 7) {
+    const int64_t per = 4 * (design == 5 ? 2 : design == 6 ? 4 : 1);
+    if (grid != (rows + per - 1) / per) return -1;
+  }
   const Args a{static_cast<const __bf16*>(x), static_cast<__bf16*>(r), static_cast<__bf16*>(out),
                static_cast<const __bf16*>(gamma), rows, eps};
   const hipStream_t s = (hipStream_t)stream;

@@ -57,7 +57,8 @@ def test_row_probe_rejects_before_launch():
     def call(design=0, lp=2, sp=2, grid=64, rows=64, x=A, r=B, o=D0, g=D1):
         return lib.row_probe(design, lp, sp, grid, x, r, o, g, rows, 1e-6, None)
 
-    for kw in (dict(design=5), dict(lp=7), dict(sp=5), dict(grid=0), dict(rows=0),
+    for kw in (dict(design=8), dict(design=-1), dict(design=5, grid=64), dict(design=6, grid=5),
+               dict(design=7, grid=15), dict(lp=7), dict(sp=5), dict(grid=0), dict(rows=0),
                dict(grid=32), dict(design=2, rows=60, grid=60), dict(design=4, grid=64),
                dict(design=4, rows=63, grid=31), dict(x=None), dict(g=None)):
         assert call(**kw) == -1, kw
