@@ -149,16 +149,32 @@ _raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
 def _stream(t: torch.Tensor, stream) -> Optional[int]:
     """The HIP stream to launch on: the given one, else torch's current
     stream on the tensor's device."""
+    return _stream_on(t.get_device(), stream)
+
+
+def _stream_on(dev: int, stream) -> Optional[int]:
+    """The given stream, else torch's current stream on GPU ``dev``."""
     if stream is None:
         if _raw_stream is not None:
-            return _raw_stream(t.get_device())
-        stream = torch.cuda.current_stream(t.device)
+            return _raw_stream(dev)
+        stream = torch.cuda.current_stream(dev)
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
-def _dev_ptr(t: torch.Tensor, what: str) -> int:
-    if not t.is_cuda:
+def _device(t: torch.Tensor, what: str, dev: Optional[int] = None) -> int:
+    """The GPU index of a device tensor.  With ``dev`` given, the tensor must
+    be on that GPU: the kernels run on one GPU and address every tensor of
+    the call directly, so a tensor on another GPU is refused here."""
+    d = t.get_device()
+    if d < 0:
         raise RmsnormError(-1, f"{what} must be a device tensor")
+    if dev is not None and d != dev:
+        raise RmsnormError(-1, f"{what} is on cuda:{d}, the call's other tensors on cuda:{dev}")
+    return d
+
+
+def _dev_ptr(t: torch.Tensor, what: str, dev: Optional[int] = None) -> int:
+    _device(t, what, dev)
     if not t.is_contiguous():
         raise RmsnormError(-2, f"{what} must be contiguous")
     return t.data_ptr()
@@ -180,8 +196,9 @@ def rmsnorm_fwd(out: torch.Tensor, x: torch.Tensor, gamma: torch.Tensor, eps: fl
     code = DTYPE_CODE.get(x.dtype)
     if code is None or out.dtype != x.dtype or gamma.dtype != x.dtype:
         raise RmsnormError(-3, f"dtypes must match and be f32/f16/bf16")
-    args = (_dev_ptr(out, "out"), _dev_ptr(x, "x"), _dev_ptr(gamma, "gamma"), rows, hidden,
-            float(eps), code, _stream(x, stream))
+    dev = _device(x, "x")
+    args = (_dev_ptr(out, "out", dev), _dev_ptr(x, "x"), _dev_ptr(gamma, "gamma", dev), rows,
+            hidden, float(eps), code, _stream_on(dev, stream))
     l = _lib or lib()
     _check(_fast.rmsnorm_fwd(*args) if _fast else l.rmsnorm_fwd(*args))
 
@@ -198,9 +215,11 @@ def add_rmsnorm_fwd(out: torch.Tensor, residual: torch.Tensor, partials: Sequenc
     code = DTYPE_CODE.get(dt)
     if code is None or out.dtype != dt or gamma.dtype != dt or any(p.dtype != dt for p in partials):
         raise RmsnormError(-3, "dtypes must match and be f32/f16/bf16")
-    ptrs = [_dev_ptr(p, f"partials[{i}]") for i, p in enumerate(partials)]
-    o, r, g = _dev_ptr(out, "out"), _dev_ptr(residual, "residual"), _dev_ptr(gamma, "gamma")
-    st = _stream(residual, stream)
+    dev = _device(residual, "residual")
+    ptrs = [_dev_ptr(p, f"partials[{i}]", dev) for i, p in enumerate(partials)]
+    o, r = _dev_ptr(out, "out", dev), _dev_ptr(residual, "residual")
+    g = _dev_ptr(gamma, "gamma", dev)
+    st = _stream_on(dev, stream)
     l = _lib or lib()
     if _fast:
         _check(_fast.add_rmsnorm_fwd(o, r, ptrs, g, rows, hidden, float(eps), code, st))
@@ -223,11 +242,14 @@ def add_rmsnorm_ag_fwd(outs: Sequence[torch.Tensor], residual: torch.Tensor,
     if any(t.dtype != residual.dtype for t in [gamma, *outs, *partials]) or \
             residual.dtype not in DTYPE_CODE:
         raise RmsnormError(-3, "dtypes must match and be f32/f16/bf16")
-    arr = (ctypes.c_void_p * max(k, 1))(*[_dev_ptr(p, f"partials[{i}]") for i, p in enumerate(partials)])
-    oarr = (ctypes.c_void_p * max(nout, 1))(*[_dev_ptr(o, f"outs[{i}]") for i, o in enumerate(outs)])
+    dev = _device(residual, "residual")
+    arr = (ctypes.c_void_p * max(k, 1))(*[_dev_ptr(p, f"partials[{i}]", dev)
+                                          for i, p in enumerate(partials)])
+    oarr = (ctypes.c_void_p * max(nout, 1))(*[_dev_ptr(o, f"outs[{i}]", dev)
+                                              for i, o in enumerate(outs)])
     _check(lib().add_rmsnorm_ag_fwd(oarr, nout, _dev_ptr(residual, "residual"), arr, k,
-                                    _dev_ptr(gamma, "gamma"), rows, hidden, float(eps),
-                                    DTYPE_CODE[residual.dtype], _stream(residual, stream)))
+                                    _dev_ptr(gamma, "gamma", dev), rows, hidden, float(eps),
+                                    DTYPE_CODE[residual.dtype], _stream_on(dev, stream)))
 
 
 def rmsnorm_plan_ag(rows: int, hidden: int, k: int, dtype: str, align: int = 16) -> str:
@@ -270,10 +292,9 @@ def collapse_rows(shape, strides, what: str = "tensor"):
     return rows, hidden, lead[-1][1]
 
 
-def row_view(t: torch.Tensor, what: str):
-    """collapse_rows of a device tensor."""
-    if not t.is_cuda:
-        raise RmsnormError(-1, f"{what} must be a device tensor")
+def row_view(t: torch.Tensor, what: str, dev: Optional[int] = None):
+    """collapse_rows of a device tensor (on GPU ``dev`` when given)."""
+    _device(t, what, dev)
     return collapse_rows(tuple(t.shape), t.stride(), what)
 
 
@@ -283,8 +304,9 @@ def rmsnorm_fwd_ex(out: torch.Tensor, x: torch.Tensor, gamma: torch.Tensor, eps:
     are any [..., H] views with a contiguous last dimension (each with its
     own row stride), gamma is float32 or x's dtype, out any of the three
     dtypes."""
+    dev = _device(x, "x")
     rows, hidden, xs = row_view(x, "x")
-    orows, ohidden, os_ = row_view(out, "out")
+    orows, ohidden, os_ = row_view(out, "out", dev)
     if (orows, ohidden) != (rows, hidden) or gamma.numel() != hidden:
         raise RmsnormError(-2, f"shape mismatch: out {tuple(out.shape)} x {tuple(x.shape)} "
                                f"gamma {tuple(gamma.shape)}")
@@ -292,9 +314,9 @@ def rmsnorm_fwd_ex(out: torch.Tensor, x: torch.Tensor, gamma: torch.Tensor, eps:
         if t.dtype not in DTYPE_CODE:
             raise RmsnormError(-3, f"{n}: dtype {t.dtype} is not f32/f16/bf16")
     _check(lib().rmsnorm_fwd_ex(out.data_ptr(), os_, DTYPE_CODE[out.dtype], x.data_ptr(), xs,
-                                DTYPE_CODE[x.dtype], _dev_ptr(gamma, "gamma"),
+                                DTYPE_CODE[x.dtype], _dev_ptr(gamma, "gamma", dev),
                                 DTYPE_CODE[gamma.dtype], rows, hidden, float(eps),
-                                _stream(x, stream)))
+                                _stream_on(dev, stream)))
 
 
 def add_rmsnorm_fwd_ex(out: torch.Tensor, residual: torch.Tensor, partials: Sequence[torch.Tensor],
@@ -303,10 +325,11 @@ def add_rmsnorm_fwd_ex(out: torch.Tensor, residual: torch.Tensor, partials: Sequ
     place (in the residual's dtype, which the partials share); out =
     RMSNorm(residual) * gamma in out's dtype.  Every tensor may be a
     [..., H] view with its own row stride."""
+    dev = _device(residual, "residual")
     rows, hidden, rs = row_view(residual, "residual")
-    orows, ohidden, os_ = row_view(out, "out")
+    orows, ohidden, os_ = row_view(out, "out", dev)
     k = len(partials)
-    views = [row_view(p, f"partials[{i}]") for i, p in enumerate(partials)]
+    views = [row_view(p, f"partials[{i}]", dev) for i, p in enumerate(partials)]
     if (orows, ohidden) != (rows, hidden) or gamma.numel() != hidden or \
             any(v[:2] != (rows, hidden) for v in views):
         raise RmsnormError(-2, "shape mismatch between out, residual, partials and gamma")
@@ -317,9 +340,9 @@ def add_rmsnorm_fwd_ex(out: torch.Tensor, residual: torch.Tensor, partials: Sequ
     strides = (ctypes.c_int64 * max(k, 1))(*[v[2] for v in views])
     _check(lib().add_rmsnorm_fwd_ex(out.data_ptr(), os_, DTYPE_CODE[out.dtype],
                                     residual.data_ptr(), rs, arr, strides, k,
-                                    DTYPE_CODE[residual.dtype], _dev_ptr(gamma, "gamma"),
+                                    DTYPE_CODE[residual.dtype], _dev_ptr(gamma, "gamma", dev),
                                     DTYPE_CODE[gamma.dtype], rows, hidden, float(eps),
-                                    _stream(residual, stream)))
+                                    _stream_on(dev, stream)))
 
 
 def rmsnorm_plan_ex(rows: int, hidden: int, k: int, dtype: str, gamma_dtype: str,
@@ -384,11 +407,14 @@ def block_sum_workspace(device=None, stream=None) -> torch.Tensor:
     dev = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
     if dev.index is None:
         dev = torch.device("cuda", torch.cuda.current_device())
-    sid = _stream(torch.empty(0, device=dev), stream)
+    sid = _stream_on(dev.index, stream)
     with _ws_lock:
         ws = _workspaces.get((dev.index, sid))
         if ws is None:
             ws = torch.zeros(BRS_WORKSPACE_BYTES, dtype=torch.uint8, device=dev)
+            # the fill runs on torch's current stream, the sums on `sid`:
+            # finish it before a sum on another stream can read the counters
+            torch.cuda.current_stream(dev).synchronize()
             _workspaces[(dev.index, sid)] = ws
         return ws
 
@@ -401,12 +427,14 @@ def block_all_reduce_sum_fwd(out: torch.Tensor, x: torch.Tensor, workspace: Opti
     want = torch.int32 if x.dtype == torch.int8 else torch.float32
     if out.dtype != want or out.numel() != 1:
         raise RmsnormError(-2, f"out must be one {want}")
+    dev = _device(x, "x")
     if workspace is None:
         workspace = block_sum_workspace(x.device, stream)
-    _check(lib().block_all_reduce_sum(_dev_ptr(out, "out"), _dev_ptr(x, "x") if x.numel() else
-                                      x.data_ptr() or None, x.numel(), BRS_DTYPE_CODE[x.dtype],
-                                      _dev_ptr(workspace, "workspace"), workspace.numel(),
-                                      _stream(x, stream)))
+    _check(lib().block_all_reduce_sum(_dev_ptr(out, "out", dev), _dev_ptr(x, "x") if x.numel()
+                                      else x.data_ptr() or None, x.numel(),
+                                      BRS_DTYPE_CODE[x.dtype],
+                                      _dev_ptr(workspace, "workspace", dev), workspace.numel(),
+                                      _stream_on(dev, stream)))
 
 
 def block_all_reduce_sum_noalloc_fwd(out: torch.Tensor, x: torch.Tensor, stream=None) -> None:
@@ -417,9 +445,10 @@ def block_all_reduce_sum_noalloc_fwd(out: torch.Tensor, x: torch.Tensor, stream=
     want = torch.int32 if x.dtype == torch.int8 else torch.float32
     if out.dtype != want or out.numel() != 1:
         raise RmsnormError(-2, f"out must be one {want}")
-    _check(lib().block_all_reduce_sum_noalloc(_dev_ptr(out, "out"), _dev_ptr(x, "x") if x.numel()
-                                              else x.data_ptr() or None, x.numel(),
-                                              BRS_DTYPE_CODE[x.dtype], _stream(x, stream)))
+    dev = _device(x, "x")
+    _check(lib().block_all_reduce_sum_noalloc(_dev_ptr(out, "out", dev), _dev_ptr(x, "x")
+                                              if x.numel() else x.data_ptr() or None, x.numel(),
+                                              BRS_DTYPE_CODE[x.dtype], _stream_on(dev, stream)))
 
 
 def block_sum_tune(groups: int = 0) -> None:
@@ -449,11 +478,10 @@ def matrix_ld(shape, strides, what: str = "matrix") -> int:
     return strides[0] if shape[0] > 1 else shape[1]
 
 
-def _matrix(t: torch.Tensor, what: str):
-    """(pointer, row stride in elements) of a 2-D device tensor whose
-    elements are contiguous within a row."""
-    if not t.is_cuda:
-        raise RmsnormError(-1, f"{what} must be a device tensor")
+def _matrix(t: torch.Tensor, what: str, dev: Optional[int] = None):
+    """(pointer, row stride in elements) of a 2-D device tensor (on GPU
+    ``dev`` when given) whose elements are contiguous within a row."""
+    _device(t, what, dev)
     return t.data_ptr(), matrix_ld(tuple(t.shape), t.stride(), what)
 
 
@@ -525,30 +553,31 @@ def gemm_scatter_fwd(dst: Sequence[torch.Tensor], a: torch.Tensor, b: torch.Tens
             raise RmsnormError(-3, f"{what} dtype {t.dtype} differs from a's {a.dtype}")
     if world < 1 or world > GEMM_SCATTER_WORLD_MAX or m % world:
         raise RmsnormError(-2, "need 1 <= len(dst) <= 16 dividing m")
+    dev = _device(a, "a")
     ldd = None
     ptrs = []
     for d in dst:
         if tuple(d.shape) != (m // world, n):
             raise RmsnormError(-2, f"every dst chunk must be [{m // world}, {n}]")
-        p, ld = _matrix(d, "dst")
+        p, ld = _matrix(d, "dst", dev)
         if ldd is not None and ld != ldd:
             raise RmsnormError(-2, "dst chunks must share one row stride")
         ldd = ld
         ptrs.append(p)
     pa, lda = _matrix(a, "a")
-    pb, ldb = _matrix(b, "b")
-    pc, ldc = _matrix(c, "c") if c is not None else (None, 0)
+    pb, ldb = _matrix(b, "b", dev)
+    pc, ldc = _matrix(c, "c", dev) if c is not None else (None, 0)
     pf = None
     if flags is not None:
-        if flags.dtype not in (torch.int32, torch.uint32) or not flags.is_contiguous() or \
+        if flags.dtype not in (torch.int32, torch.uint32) or \
                 flags.numel() < gemm_scatter_tiles(m, n, tile_n):
             raise RmsnormError(-2, "flags must be a contiguous int32 tensor with one slot per tile")
-        pf = flags.data_ptr()
+        pf = _dev_ptr(flags, "flags", dev)
     arr = (ctypes.c_void_p * world)(*ptrs)
     _check(lib().gemm_scatter_fwd(arr, ldd, world, rank, pa, lda, pb, ldb, pc, ldc,
                                   ctypes.c_float(alpha), ctypes.c_float(beta), m, n, k,
                                   DTYPE_CODE[a.dtype], pf, ctypes.c_uint32(epoch & 0xFFFFFFFF),
-                                  tile_n, _stream(a, stream)))
+                                  tile_n, _stream_on(dev, stream)))
 
 
 def gemm_scatter(a: torch.Tensor, b: torch.Tensor, world: int, rank: int = 0,

@@ -393,6 +393,26 @@ def test_ag_binding_checks_before_the_library():
         B.add_rmsnorm_ag_fwd([torch.empty_like(r, dtype=torch.float16)], r, [r], g, 1e-6)
 
 
+def test_binding_refuses_tensors_on_two_devices():
+    """Every tensor of a call must be on the first tensor's GPU (a kernel on
+    one GPU addresses them all directly): the device check the binding runs
+    on each tensor, with stand-ins that report a device index."""
+    class OnDevice:
+        def __init__(self, d):
+            self.d = d
+
+        def get_device(self):
+            return self.d
+
+    assert B._device(OnDevice(0), "x") == 0 and B._device(OnDevice(3), "out", 3) == 3
+    with pytest.raises(B.RmsnormError, match="out is on cuda:1, the call's other tensors on cuda:0"):
+        B._device(OnDevice(1), "out", 0)
+    with pytest.raises(B.RmsnormError, match="must be a device tensor"):
+        B._device(OnDevice(-1), "gamma", 0)
+    with pytest.raises(B.RmsnormError, match="must be a device tensor"):
+        B._dev_ptr(OnDevice(-1), "x")
+
+
 def test_overlap_brute_force(tmp_path):
     """The aliasing test (rmsn_host::overlap in csrc/rmsnorm_span.hpp),
     compiled on the host, against brute force over the bytes of random

@@ -235,8 +235,14 @@ def test_broadcast_operands_are_rejected():
     out_row = torch.empty(1, 128, dtype=torch.bfloat16, device=DEV)
     with pytest.raises(B.RmsnormError):
         B.gemm_scatter_fwd([out_row.expand(32, 128)] * 2, b[:64], b)
+    # flags in host memory, or operands in host memory, are refused as well
+    host_flags = torch.zeros(B.gemm_scatter_tiles(64, 128), dtype=torch.int32)
+    with pytest.raises(B.RmsnormError, match="flags must be a device tensor"):
+        B.gemm_scatter_fwd(dst, b[:64], b, flags=host_flags, epoch=1)
+    with pytest.raises(B.RmsnormError, match="b must be a device tensor"):
+        B.gemm_scatter_fwd(dst, b[:64], b.cpu())
     torch.cuda.synchronize()
-    assert bool((sentinel == 7.0).all())
+    assert bool((sentinel == 7.0).all()) and bool((host_flags == 0).all())
 
 
 def test_k_zero_gives_beta_c():
