@@ -52,7 +52,8 @@
  *     scope, so a consumer that reads flags[t] == epoch sees the whole tile.
  *     Tile t covers rows [(t / T) * H, ...) and columns [(t % T) * W, ...),
  *     H and W the tile height and width used, T = ceil(n / W).
- *   - dst chunks must not overlap each other, a, b, c or flags.
+ *   - dst chunks must not overlap each other, a, b, c or flags, and flags
+ *     must not overlap a, b or c (RMSN_ERR_ALIAS otherwise).
  *   - The call enqueues one kernel on `stream` (NULL: the default stream),
  *     allocates nothing and does not synchronise.  Arguments are validated
  *     before the launch; on error nothing is launched.  m == 0 or n == 0

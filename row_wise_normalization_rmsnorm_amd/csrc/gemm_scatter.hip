@@ -766,6 +766,10 @@ extern "C" int gemm_scatter_fwd(void* const* dst, int64_t ldd, int world, int ra
       if (overlap(dst[q], dext, dst[r], dext))
         return rmsn_set_error(RMSN_ERR_ALIAS, "gemm_scatter: dst chunks overlap");
   }
+  // the flag stores must not land on operands other workgroups still read
+  if (overlap(flags, fext, a, aext) || overlap(flags, fext, b, bext) ||
+      overlap(flags, fext, c, cext))
+    return rmsn_set_error(RMSN_ERR_ALIAS, "gemm_scatter: flags overlap a, b or c");
 
   gsc::Params p{};
   p.a = static_cast<const uint16_t*>(a);

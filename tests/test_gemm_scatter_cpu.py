@@ -167,6 +167,9 @@ def test_error_codes():
     assert call(dst=[FAKE + (1 << 28), FAKE + (1 << 28) + 64]) == -5
     assert call(flags=FAKE + (1 << 28) + 16) == -5
     assert call(c=FAKE + (2 << 28), ldc=64) == -5
+    # flags over an operand: a, b, c
+    assert call(flags=FAKE + (1 << 32) + 64) == -5 and call(flags=FAKE + (2 << 32)) == -5
+    assert call(c=FAKE + (3 << 32), ldc=64, flags=FAKE + (3 << 32) + 1024) == -5
     # nothing to do: valid, and nothing launched
     assert call(m=0) == 0 and call(n=0) == 0
     assert call(m=0, tile_n=128) == 0 and call(n=0, tile_n=256) == 0
