@@ -807,6 +807,64 @@ def design_sweep(a) -> int:
     return 0
 
 
+def grid_cap_sweep(a) -> int:
+    """Time the dispatcher's kernel for a fused K = 1 workload (default the
+    8192 x 4096 one; --workload picks another) with its grid capped at
+    several workgroup counts (rmsnorm_tune's grid cap: the workgroups then
+    loop over the rows) beside the uncapped grid of one workgroup per row,
+    on buffers rotated over --rotate-bytes GiB.  Caps are timed round-robin
+    over --repeat rounds of --steps launches; the median is reported, one
+    JSON line each."""
+    import statistics
+    import torch
+    from row_wise_normalization_rmsnorm_amd import binding as B
+    from row_wise_normalization_rmsnorm_amd.workloads import WORKLOADS
+    w = WORKLOADS[a.workload or "add_rmsnorm_bf16_8192x4096_k1"]
+    if w.op != "add_rmsnorm" or w.k != 1 or w.dtype != "bf16":
+        raise SystemExit("--grid-cap-sweep takes a fused bf16 workload with one partial")
+    rows, H = a.rows or w.rows, w.hidden
+    dev = "cuda:0"
+    tb = rows * H * 2
+    nsets = max(1, int(-(-a.rotate_bytes * (1 << 30) // (3 * tb))))
+    gen = torch.Generator(device=dev).manual_seed(0)
+    g = (torch.rand(H, device=dev, generator=gen) + 0.5).to(torch.bfloat16)
+    sets = [(torch.randn(rows, H, device=dev, generator=gen).to(torch.bfloat16),
+             torch.randn(rows, H, device=dev, generator=gen).to(torch.bfloat16),
+             torch.empty(rows, H, device=dev, dtype=torch.bfloat16)) for _ in range(nsets)]
+    plan = B.rmsnorm_plan(rows, H, 1, "bf16")
+    caps = [0] + [c for c in (256, 512, 1024, 2048, 4096, 8192, 16384) if c < rows]
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        x, r, o = sets[i % nsets]
+        B.add_rmsnorm_fwd(o, r, [x], g, w.eps)
+
+    times = {c: [] for c in caps}
+    for rep in range(a.repeat):
+        for c in caps:
+            with B.forced(None, c):
+                for i in range(2 * nsets):
+                    step(i)
+                torch.cuda.synchronize()
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for i in range(a.steps):
+                    step(i)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                times[c].append(e0.elapsed_time(e1) / a.steps * 1e3)
+        print(f"[grid-cap] round {rep} done", file=sys.stderr, flush=True)
+    nbytes = rows * H * 2 * 4 + H * 2
+    for c, t in times.items():
+        us = statistics.median(t)
+        print(json.dumps({"workload": w.name if rows == w.rows else f"{w.name}_rows{rows}",
+                          "kernel": plan, "grid_cap": c or None, "us": round(us, 3),
+                          "gbs": round(nbytes / us / 1e3, 1), "rotating_sets": nsets,
+                          "runs_us": [round(x, 2) for x in t]}), flush=True)
+    return 0
+
+
 GEMM_DESIGNS = {0: "4 waves, 64-wide k stages in 2 LDS buffers, LDS reads and loads spread "
                     "between the products",
                  1: "4 waves, 64-wide k stages in 2 LDS buffers, LDS reads and loads in one "
@@ -972,6 +1030,9 @@ def main() -> int:
                          "|-separated substrings")
     ap.add_argument("--ceiling-policies", default="",
                     help="ceiling sweep: comma-separated cache policies (default: all)")
+    ap.add_argument("--grid-cap-sweep", action="store_true",
+                    help="time the fused K = 1 workload's kernel with its grid capped at "
+                         "256-16384 workgroups beside one workgroup per row")
     ap.add_argument("--design-sweep", action="store_true",
                     help="time the alternative row-kernel designs of librowprobe.so beside the "
                          "library's kernel (4096-wide bf16 rows, one partial) and exit")
@@ -1020,6 +1081,8 @@ def main() -> int:
                              rotate_gib=a.rotate_bytes)
     if a.design_sweep:
         return design_sweep(a)
+    if a.grid_cap_sweep:
+        return grid_cap_sweep(a)
 
     from row_wise_normalization_rmsnorm_amd.workloads import GEMM_WORKLOADS
     if a.gemm_design_sweep:

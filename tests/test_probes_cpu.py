@@ -83,3 +83,15 @@ def test_stream_probe_rejects_before_launch():
     for kw in (dict(nr=17), dict(nw=-1), dict(n16=-1), dict(sink=None), dict(grid=0),
                dict(policy=9), dict(policy=-1), dict(block=128), dict(unroll=3)):
         assert call(**kw) == -1, kw
+
+
+def test_grid_cap_sweep_takes_only_fused_single_partial_workloads():
+    """bench.py --grid-cap-sweep refuses, before touching a GPU, a workload
+    it does not time (plain RMSNorm, K = 8)."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    for wl in ("add_rmsnorm_bf16_4096x8192_k8", "rmsnorm_f32_512x2048"):
+        r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--grid-cap-sweep",
+                            "--workload", wl], capture_output=True, text=True, timeout=300)
+        assert r.returncode != 0 and "one partial" in r.stderr, (wl, r.stderr[-300:])
